@@ -1,0 +1,203 @@
+/*
+ * mxfp8.h -- C ABI of the MI355X (gfx950) MXFP8 library.
+ *
+ * MXFP8 as the page "End-to-End MXFP8 RL on Blackwell: What Matching Buys,
+ * When It Pays Off, and How It Fails" (verl blog) uses it, section "The
+ * pipeline", paragraph "The format": E4M3 elements in blocks of 32 along the
+ * reduction dimension, each block sharing one power-of-two E8M0 scale
+ * (8.25 bits per element), following the OCP Microscaling (MX) v1.0
+ * specification the paragraph cites.
+ *
+ * Conventions shared by every call
+ *  - All matrices are row-major.  BF16 inputs are raw 16-bit patterns.
+ *  - Device pointers (all tensors, the group offsets) must be device memory
+ *    that the stream's device can access, 16-byte aligned.
+ *  - The caller allocates and owns every buffer.  The library never
+ *    allocates, frees, copies to the host or synchronizes: every call only
+ *    validates its arguments on the host and enqueues kernels on `stream`
+ *    (0 = the legacy default stream), so calls are HIP-graph capturable.
+ *  - Arguments are validated before anything is enqueued; on a validation
+ *    error nothing is written and a non-zero status is returned.  A failed
+ *    launch returns MXFP8_ERR_HIP (mxfp8_last_hip_error() gives the HIP
+ *    code).  Faults inside a kernel surface at the caller's next
+ *    synchronization of the stream, as for any asynchronous HIP work.
+ *  - Calls are thread-safe; the library keeps no mutable global state
+ *    except the last HIP error code (per thread).
+ *  - Outputs are deterministic: the same inputs give the same bytes.
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXFP8_OK = 0,
+    MXFP8_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    MXFP8_ERR_SHAPE = 2,       /* a size <= 0 (or < 0 where 0 is allowed), a block
+                                  axis not a multiple of 32, or a size too large     */
+    MXFP8_ERR_AXIS = 3,        /* axis is not 0 or 1                                  */
+    MXFP8_ERR_DTYPE = 4,       /* unknown output dtype or B layout                    */
+    MXFP8_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                    */
+    MXFP8_ERR_HIP = 6,         /* a HIP launch or query failed                        */
+    MXFP8_ERR_UNSUPPORTED = 7  /* the current device is not gfx950                    */
+} mxfp8_status;
+
+typedef enum { MXFP8_F32 = 0, MXFP8_BF16 = 1 } mxfp8_dtype;
+
+typedef enum { MXFP8_CANONICAL = 0, MXFP8_PACKED = 1 } mxfp8_layout;
+
+/*
+ * mxfp8_quantize -- BF16 -> MXFP8 (E4M3 elements + one E8M0 scale per 32).
+ *
+ * Defined by the format paragraph above (blocks of 32 along the reduction
+ * axis) and, for axis 0, by the learner paragraph of the same section: the
+ * weight-gradient GEMM reduces over tokens, so some operands are blocked in
+ * 32s along the token dimension.
+ *
+ * Per block of 32 BF16 values x_i:
+ *   amax = max |x_i|; scale exponent s = floor(log2 amax) - 8 (OCP MX rule,
+ *   8 = largest exponent of E4M3), clamped to s >= -127; scale code = s+127.
+ *   An all-zero block has code 0; a block holding any NaN or +-Inf has
+ *   code 0xFF and all its elements 0x7F.  BF16 subnormals are not flushed.
+ *   q_i = x_i * 2^-s rounded to the nearest E4M3 value (ties to even),
+ *   saturated to +-448; the sign of zero is kept.
+ *
+ *   x      : BF16 [rows][cols]
+ *   axis 1 : blocks along cols.  cols % 32 == 0.
+ *            q[rows][cols], scales[rows][cols/32]
+ *   axis 0 : blocks along rows (tokens).  rows % 32 == 0.  The output is
+ *            TRANSPOSED so the block axis is contiguous (every GEMM operand
+ *            is then K-contiguous):  q[cols][rows], scales[cols][rows/32].
+ * rows, cols >= 1.  Bit-exact and deterministic.
+ */
+mxfp8_status mxfp8_quantize(const void *x_bf16, int64_t rows, int64_t cols,
+                            int axis, uint8_t *q, uint8_t *scales,
+                            hipStream_t stream);
+
+/*
+ * mxfp8_dequantize -- MXFP8 -> FP32 or BF16:  out = decode(q) * 2^(code-127).
+ *
+ * The high-precision reference that the page's post-sync self-check compares
+ * the MXFP8 kernel against is built from dequantized weights (section
+ * "Correctness: how it fails", "Post-sync self-check").
+ *
+ * q / scales are laid out as mxfp8_quantize writes them for `axis`; `out` is
+ * [rows][cols] in x's orientation.  FP32 output is exact (an E8M0 code above
+ * 246 can overflow to +-Inf); BF16 output is rounded to nearest even.  NaN
+ * codes (element 0x7F/0xFF or scale 0xFF) give NaN.
+ */
+mxfp8_status mxfp8_dequantize(const uint8_t *q, const uint8_t *scales,
+                              int64_t rows, int64_t cols, int axis, void *out,
+                              mxfp8_dtype out_dtype, hipStream_t stream);
+
+/*
+ * mxfp8_packed_bytes -- size in bytes of the packed weight buffers for
+ * `batch` matrices of [rows=N][cols=K]: which = 0 -> elements, 1 -> scales.
+ * Pure host function; returns 0 for invalid sizes (K % 32 != 0, N/K <= 0).
+ */
+size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which);
+
+/*
+ * mxfp8_repack -- canonical MXFP8 weights -> the GEMM's kernel layout.
+ *
+ * The page (section "The pipeline", sampler paragraph) notes that serving
+ * kernels rewrite weights and scales into kernel-specific layouts (swizzled
+ * scales, shuffled/interleaved experts, repacked weights), and that those
+ * derived layouts must be rebuilt from the synchronized canonical tensors
+ * after every weight update and written back into the storage the captured
+ * graphs use.  This call is that rebuild: run it after every update; it
+ * writes in place into the caller's packed buffers, so pointers captured by a
+ * HIP graph stay valid.
+ *
+ * In : q[batch][N][K], scales[batch][N][K/32] (axis-1 quantizer output of
+ *      weights [N][K]; K % 32 == 0, N >= 1, batch >= 1).
+ * Out: q_packed (mxfp8_packed_bytes(batch,N,K,0) bytes) and scales_packed
+ *      (mxfp8_packed_bytes(batch,N,K,1) bytes), with this layout:
+ *   NP = ceil(N/256) panels of 256 rows, KS = ceil(K/128) k-steps of 128,
+ *   KG = ceil(KS/4) groups of 4 k-steps.
+ *   elements [batch][NP][KS][256 rows][128 B]: the bytes k = 128*ks + 16c ..
+ *     + 15 of row r of the panel form chunk c (0..7), stored at chunk slot
+ *     c ^ f(r % 16), with f(t) = (t & 7) ^ (t >> 3) (a bank-conflict-free
+ *     swizzle of the GEMM's LDS image).  Rows >= N and k >= K hold 0x00.
+ *   scales [batch][NP*16 atoms of 16 rows][KG][64 lanes][4 B]: byte j of
+ *     lane l of (atom a, group g) is the scale of row 16a + (l % 16), block
+ *     4*(4g + j) + (l / 16).  Rows >= N or blocks >= K/32 hold 127 (1.0).
+ */
+mxfp8_status mxfp8_repack(const uint8_t *q, const uint8_t *scales,
+                          int64_t batch, int64_t rows, int64_t cols,
+                          uint8_t *q_packed, uint8_t *scales_packed,
+                          hipStream_t stream);
+
+/*
+ * mxfp8_gemm -- block-scaled GEMM  C[M][N] = A[M][K] * B[N][K]^T.
+ *
+ * The format paragraph (section "The pipeline") describes block scales fed
+ * to the matrix instruction as operands; here the scaled MFMA of gfx950
+ * consumes the E4M3 elements and E8M0 scales directly:
+ *   C[m][n] = sum_b 2^(sa[m][b] + sb[n][b] - 254) * sum_{k in block b} a[m][k] b[n][k]
+ * accumulated in fp32.  One A*B^T form serves the learner's three GEMMs:
+ * forward (X and W blocked along K), data gradient (dY blocked along N, W
+ * quantized with axis 0) and weight gradient (dY and X quantized with axis 0,
+ * blocked along tokens).
+ *
+ *   A (a_q, a_s): canonical K-contiguous MXFP8, q[M][K], s[M][K/32] (axis-1
+ *                 output, or axis-0 output, which is already transposed).
+ *   B (b_q, b_s): b_layout MXFP8_PACKED -> mxfp8_repack output for [N][K];
+ *                 MXFP8_CANONICAL -> q[N][K], s[N][K/32] like A.
+ *   C           : [M][N], FP32 or BF16 (round to nearest even).
+ * M, N >= 1; K >= 32, K % 32 == 0.  Deterministic (no split-K atomics).
+ */
+mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s,
+                        const uint8_t *b_q, const uint8_t *b_s,
+                        mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
+                        void *c, mxfp8_dtype c_dtype, hipStream_t stream);
+
+/*
+ * mxfp8_grouped_gemm -- MoE expert GEMM over groups of rows:
+ *   for g in 0..G-1:  C[o_g : o_{g+1}] = A[o_g : o_{g+1}] * B_g^T
+ *
+ * The page's MoE serving path runs its expert GEMMs in MXFP8 from weights
+ * stored "shuffled and interleaved" (section "The pipeline", sampler
+ * paragraph; section "Speed: when it pays off": expert GEMMs dominate MoE
+ * decode and FP8 halves their weight traffic).
+ *
+ *   A               : canonical MXFP8 q[M_total][K], s[M_total][K/32]; rows
+ *                     sorted by expert, each group padded to a multiple of 32.
+ *   B               : mxfp8_repack output for batch = G matrices [N][K].
+ *   d_group_offsets : DEVICE int32 [G+1], non-decreasing, o_0 >= 0,
+ *                     o_G <= M_total, every o_g % 32 == 0.  Read on the
+ *                     device (no host synchronization); offsets violating
+ *                     this are clamped to [0, M_total] and empty groups
+ *                     are skipped, never read out of bounds.
+ *   C               : [M_total][N]; rows outside [o_0, o_G) are not written.
+ * G >= 1, M_total >= 0 (0 enqueues nothing), M_total % 32 == 0, N >= 1,
+ * K >= 32, K % 32 == 0.
+ */
+mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s,
+                                const uint8_t *b_q_packed,
+                                const uint8_t *b_s_packed,
+                                const int32_t *d_group_offsets, int64_t G,
+                                int64_t M_total, int64_t N, int64_t K, void *c,
+                                mxfp8_dtype c_dtype, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *mxfp8_status_string(mxfp8_status status);
+
+/* The HIP error code of the calling thread's last MXFP8_ERR_HIP (0 if none). */
+int mxfp8_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *mxfp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H */

@@ -1,0 +1,261 @@
+"""MI355X (gfx950) MXFP8 library -- Python binding.
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libmxfp8.so`` through the C ABI declared in ``include/mxfp8.h``.  PyTorch
+supplies device memory and the current stream.  There is no fallback: if the
+library is not built, or the device is not gfx950, every call raises.
+
+    q, s   = quantize(x_bf16, axis)                  # E4M3 + E8M0
+    x'     = dequantize(q, s, rows, cols, axis, torch.float32 | torch.bfloat16)
+    w      = repack(q, s)                            # PackedWeight (kernel layout)
+    repack_(q, s, w)                                 # in place, after every update
+    c      = gemm(a_q, a_s, w_or_(b_q, b_s), out_dtype)
+    c      = grouped_gemm(a_q, a_s, w_experts, d_offsets, out_dtype)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+__all__ = ["lib", "quantize", "quantize_into", "dequantize", "packed_bytes", "PackedWeight",
+           "repack", "repack_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
+
+MXFP8_F32, MXFP8_BF16 = 0, 1
+MXFP8_CANONICAL, MXFP8_PACKED = 0, 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MXFP8Error(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libmxfp8.so (built in-tree by ``python -m mxfp8_block_scaled_05_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise MXFP8Error("libmxfp8.so is not built (%s); run "
+                             "`python -m mxfp8_block_scaled_05_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.mxfp8_quantize.argtypes = [P, I64, I64, I32, P, P, P]
+        L.mxfp8_dequantize.argtypes = [P, P, I64, I64, I32, P, I32, P]
+        L.mxfp8_packed_bytes.argtypes = [I64, I64, I64, I32]
+        L.mxfp8_packed_bytes.restype = ctypes.c_size_t
+        L.mxfp8_repack.argtypes = [P, P, I64, I64, I64, P, P, P]
+        L.mxfp8_gemm.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
+        L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
+                  "mxfp8_grouped_gemm"):
+            getattr(L, f).restype = I32
+        L.mxfp8_status_string.argtypes = [I32]
+        L.mxfp8_status_string.restype = ctypes.c_char_p
+        L.mxfp8_last_hip_error.restype = I32
+        L.mxfp8_version.restype = ctypes.c_char_p
+        _lib = L
+        return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        msg = L.mxfp8_status_string(status).decode()
+        if status == 6:
+            msg += " (hipError %d)" % L.mxfp8_last_hip_error()
+        raise MXFP8Error("%s: %s" % (what, msg))
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _out_code(dtype):
+    if dtype == torch.float32:
+        return MXFP8_F32
+    if dtype == torch.bfloat16:
+        return MXFP8_BF16
+    raise TypeError("output dtype must be torch.float32 or torch.bfloat16")
+
+
+# ------------------------------------------------------------------ quantize
+
+def quantize_into(x: torch.Tensor, axis: int, q: torch.Tensor, s: torch.Tensor) -> None:
+    _need(x, torch.bfloat16, "x")
+    _need(q, torch.uint8, "q")
+    _need(s, torch.uint8, "scales")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    want_q = (rows, cols) if axis == 1 else (cols, rows)
+    want_s = (rows, cols // 32) if axis == 1 else (cols, rows // 32)
+    if tuple(q.shape) != want_q or tuple(s.shape) != want_s:
+        raise ValueError("q/scales shapes %s/%s, expected %s/%s" % (tuple(q.shape), tuple(s.shape),
+                                                                  want_q, want_s))
+    _check(lib().mxfp8_quantize(_ptr(x), rows, cols, axis, _ptr(q), _ptr(s), _stream(x.device)),
+           "mxfp8_quantize")
+
+
+def quantize(x: torch.Tensor, axis: int = 1):
+    """BF16 [rows, cols] -> (q uint8, scales uint8).  axis=1: q[rows, cols],
+    s[rows, cols/32].  axis=0: transposed, q[cols, rows], s[cols, rows/32]."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if axis == 1:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        s = torch.empty((rows, max(cols // 32, 0)), dtype=torch.uint8, device=x.device)
+    elif axis == 0:
+        q = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+        s = torch.empty((cols, max(rows // 32, 0)), dtype=torch.uint8, device=x.device)
+    else:
+        raise ValueError("axis must be 0 or 1")
+    if (axis == 1 and cols % 32) or (axis == 0 and rows % 32):
+        raise ValueError("the block axis must be a multiple of 32")
+    quantize_into(x, axis, q, s)
+    return q, s
+
+
+def dequantize(q: torch.Tensor, s: torch.Tensor, rows: int, cols: int, axis: int = 1,
+               dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    _need(q, torch.uint8, "q")
+    _need(s, torch.uint8, "scales")
+    code = _out_code(dtype)
+    if q.numel() != rows * cols:
+        raise ValueError("q has %d elements, expected %d" % (q.numel(), rows * cols))
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=q.device)
+    else:
+        _need(out, dtype, "out")
+    _check(lib().mxfp8_dequantize(_ptr(q), _ptr(s), rows, cols, axis, _ptr(out), code,
+                                  _stream(q.device)), "mxfp8_dequantize")
+    return out
+
+
+# ------------------------------------------------------------------ repack
+
+def packed_bytes(batch: int, rows: int, cols: int, which: int) -> int:
+    return int(lib().mxfp8_packed_bytes(batch, rows, cols, which))
+
+
+@dataclass
+class PackedWeight:
+    """Weights [batch][N][K] in the GEMM's kernel layout (mxfp8_repack)."""
+    q: torch.Tensor
+    s: torch.Tensor
+    batch: int
+    N: int
+    K: int
+
+
+def repack_(q: torch.Tensor, s: torch.Tensor, w: PackedWeight) -> PackedWeight:
+    """Rebuild the kernel layout in place into w's storage (pointers stay valid)."""
+    _need(q, torch.uint8, "q")
+    _need(s, torch.uint8, "scales")
+    _need(w.q, torch.uint8, "q_packed")
+    _need(w.s, torch.uint8, "scales_packed")
+    if q.numel() != w.batch * w.N * w.K or s.numel() != w.batch * w.N * (w.K // 32):
+        raise ValueError("canonical q/scales do not match the packed weight's shape")
+    if w.q.numel() < packed_bytes(w.batch, w.N, w.K, 0) or w.s.numel() < packed_bytes(w.batch, w.N, w.K, 1):
+        raise ValueError("packed buffers too small")
+    _check(lib().mxfp8_repack(_ptr(q), _ptr(s), w.batch, w.N, w.K, _ptr(w.q), _ptr(w.s),
+                              _stream(q.device)), "mxfp8_repack")
+    return w
+
+
+def repack(q: torch.Tensor, s: torch.Tensor) -> PackedWeight:
+    """Canonical q[(batch,) N, K], s[(batch,) N, K/32] -> PackedWeight."""
+    if q.dim() == 2:
+        batch, (N, K) = 1, q.shape
+    elif q.dim() == 3:
+        batch, N, K = q.shape
+    else:
+        raise ValueError("q must be [N, K] or [batch, N, K]")
+    nq, ns = packed_bytes(batch, N, K, 0), packed_bytes(batch, N, K, 1)
+    if nq == 0:
+        raise ValueError("invalid weight shape for packing")
+    w = PackedWeight(torch.empty(nq, dtype=torch.uint8, device=q.device),
+                     torch.empty(ns, dtype=torch.uint8, device=q.device), batch, N, K)
+    return repack_(q, s, w)
+
+
+# ------------------------------------------------------------------ GEMMs
+
+def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b, out_dtype=torch.bfloat16,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = A[M, K] B[N, K]^T.  ``b`` is a PackedWeight (batch 1) or a
+    canonical (b_q[N, K], b_s[N, K/32]) pair."""
+    _need(a_q, torch.uint8, "a_q")
+    _need(a_s, torch.uint8, "a_s")
+    M, K = a_q.shape
+    if isinstance(b, PackedWeight):
+        if b.batch != 1 or b.K != K:
+            raise ValueError("packed B must be a single [N, K] matrix with K = %d" % K)
+        b_q, b_s, N, layout = b.q, b.s, b.N, MXFP8_PACKED
+    else:
+        b_q, b_s = b
+        _need(b_q, torch.uint8, "b_q")
+        _need(b_s, torch.uint8, "b_s")
+        N = b_q.shape[0]
+        if b_q.shape[1] != K or tuple(b_s.shape) != (N, K // 32):
+            raise ValueError("canonical B shapes do not match K = %d" % K)
+        layout = MXFP8_CANONICAL
+    if tuple(a_s.shape) != (M, K // 32):
+        raise ValueError("a_s must be [M, K/32]")
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_q.device)
+    else:
+        _need(out, out_dtype, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    _check(lib().mxfp8_gemm(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), layout, M, N, K,
+                            _ptr(out), code, _stream(a_q.device)), "mxfp8_gemm")
+    return out
+
+
+def grouped_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, offsets: torch.Tensor,
+                 out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-expert C[o_g:o_g+1] = A[o_g:o_g+1] B_g^T with device int32 offsets [G+1]."""
+    _need(a_q, torch.uint8, "a_q")
+    _need(a_s, torch.uint8, "a_s")
+    _need(offsets, torch.int32, "offsets")
+    M_total, K = a_q.shape
+    if w.K != K:
+        raise ValueError("K mismatch")
+    G = w.batch
+    if offsets.numel() != G + 1:
+        raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M_total, w.N), dtype=out_dtype, device=a_q.device)
+    else:
+        _need(out, out_dtype, "out")
+    _check(lib().mxfp8_grouped_gemm(_ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s), _ptr(offsets), G,
+                                    M_total, w.N, K, _ptr(out), code, _stream(a_q.device)),
+           "mxfp8_grouped_gemm")
+    return out

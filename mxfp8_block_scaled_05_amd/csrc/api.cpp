@@ -1,0 +1,189 @@
+// C ABI of the gfx950 MXFP8 library: argument validation and kernel dispatch.
+// The contract of every entry point is documented in include/mxfp8.h.
+#include "mxfp8.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "mx_launch.hpp"
+
+namespace mx {
+
+static thread_local int g_last_hip_error = 0;
+
+namespace {
+struct DeviceInfo {
+    bool valid = false;
+    bool gfx950 = false;
+    int cus = 0;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+const DeviceInfo *current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+        g_dev[dev].cus = prop.multiProcessorCount;
+        g_dev[dev].gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        g_dev[dev].valid = true;
+    });
+    return g_dev[dev].valid ? &g_dev[dev] : nullptr;
+}
+}  // namespace
+
+int device_cu_count() {
+    const DeviceInfo *d = current_device();
+    return (d && d->cus > 0) ? d->cus : 256;
+}
+
+// 1 if the current device is gfx950, 0 if not, -1 if it cannot be queried
+int device_arch_ok() {
+    const DeviceInfo *d = current_device();
+    if (!d) return -1;
+    return d->gfx950 ? 1 : 0;
+}
+
+}  // namespace mx
+
+using namespace mx;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;     // any single dimension
+constexpr int64_t kMaxK = (int64_t)1 << 22;       // 256 rows x K must stay < 2^31 B
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+mxfp8_status check_device() {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MXFP8_ERR_HIP;
+    }
+    const int arch = device_arch_ok();
+    if (arch < 0) return MXFP8_ERR_HIP;
+    return arch ? MXFP8_OK : MXFP8_ERR_UNSUPPORTED;
+}
+
+mxfp8_status finish(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return MXFP8_ERR_HIP;
+    }
+    return MXFP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mxfp8_version(void) { return "0.1.0"; }
+
+int mxfp8_last_hip_error(void) { return g_last_hip_error; }
+
+const char *mxfp8_status_string(mxfp8_status s) {
+    switch (s) {
+        case MXFP8_OK: return "MXFP8_OK";
+        case MXFP8_ERR_NULL: return "MXFP8_ERR_NULL: a required pointer is NULL";
+        case MXFP8_ERR_SHAPE: return "MXFP8_ERR_SHAPE: invalid or unsupported size";
+        case MXFP8_ERR_AXIS: return "MXFP8_ERR_AXIS: axis must be 0 or 1";
+        case MXFP8_ERR_DTYPE: return "MXFP8_ERR_DTYPE: unknown dtype or layout";
+        case MXFP8_ERR_ALIGN: return "MXFP8_ERR_ALIGN: pointer not 16-byte aligned";
+        case MXFP8_ERR_HIP: return "MXFP8_ERR_HIP: HIP launch or query failed";
+        case MXFP8_ERR_UNSUPPORTED: return "MXFP8_ERR_UNSUPPORTED: device is not gfx950";
+    }
+    return "MXFP8: unknown status";
+}
+
+mxfp8_status mxfp8_quantize(const void *x_bf16, int64_t rows, int64_t cols, int axis, uint8_t *q,
+                            uint8_t *scales, hipStream_t stream) {
+    if (!x_bf16 || !q || !scales) return MXFP8_ERR_NULL;
+    if (axis != 0 && axis != 1) return MXFP8_ERR_AXIS;
+    if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (axis == 1 && cols % 32) return MXFP8_ERR_SHAPE;
+    if (axis == 0 && (rows % 32 || (cols + 127) / 128 > 0x7FFFFFFF || (rows + 127) / 128 > 65535))
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q)) return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize(static_cast<const uint16_t *>(x_bf16), rows, cols, axis, q,
+                                  scales, stream));
+}
+
+mxfp8_status mxfp8_dequantize(const uint8_t *q, const uint8_t *scales, int64_t rows, int64_t cols,
+                              int axis, void *out, mxfp8_dtype out_dtype, hipStream_t stream) {
+    if (!q || !scales || !out) return MXFP8_ERR_NULL;
+    if (axis != 0 && axis != 1) return MXFP8_ERR_AXIS;
+    if (out_dtype != MXFP8_F32 && out_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (axis == 1 && cols % 32) return MXFP8_ERR_SHAPE;
+    if (axis == 0 && (rows % 32 || (rows + 63) / 64 > 65535)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(out)) return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_dequantize(q, scales, rows, cols, axis, out, out_dtype == MXFP8_BF16,
+                                    stream));
+}
+
+size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which) {
+    if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 32 || (which != 0 && which != 1)) return 0;
+    if (rows >= kMaxDim || cols > kMaxK || batch > 65535) return 0;
+    return (size_t)(which == 0 ? packed_q_bytes(batch, rows, cols) : packed_s_bytes(batch, rows, cols));
+}
+
+mxfp8_status mxfp8_repack(const uint8_t *q, const uint8_t *scales, int64_t batch, int64_t rows,
+                          int64_t cols, uint8_t *q_packed, uint8_t *scales_packed,
+                          hipStream_t stream) {
+    if (!q || !scales || !q_packed || !scales_packed) return MXFP8_ERR_NULL;
+    if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 32) return MXFP8_ERR_SHAPE;
+    if (rows >= kMaxDim || cols > kMaxK || batch > 65535 || packed_panels(rows) > 65535)
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(q_packed) || !aligned16(scales_packed)) return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_repack(q, scales, batch, rows, cols, q_packed, scales_packed, stream));
+}
+
+mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                        const uint8_t *b_s, mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
+                        void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
+    if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
+    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    // tile counts must fit the 1-D grid
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c)) return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_gemm(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
+                              c_dtype == MXFP8_BF16, stream));
+}
+
+mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q_packed,
+                                const uint8_t *b_s_packed, const int32_t *d_group_offsets,
+                                int64_t G, int64_t M_total, int64_t N, int64_t K, void *c,
+                                mxfp8_dtype c_dtype, hipStream_t stream) {
+    if (!a_q || !a_s || !b_q_packed || !b_s_packed || !d_group_offsets || !c) return MXFP8_ERR_NULL;
+    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (G < 1 || G > 65535 || M_total < 0 || M_total % 32 || M_total >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (N <= 0 || N >= kMaxDim || K < 32 || K % 32 || K > kMaxK) return MXFP8_ERR_SHAPE;
+    if ((ceil_div(M_total, 128) + G) * ceil_div(N, 256) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(b_q_packed) || !aligned16(b_s_packed) || !aligned16(c))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    if (M_total == 0) return MXFP8_OK;
+    return finish(launch_grouped_gemm(a_q, a_s, b_q_packed, b_s_packed, d_group_offsets, G,
+                                      M_total, N, K, c, c_dtype == MXFP8_BF16, stream));
+}
+
+}  // extern "C"

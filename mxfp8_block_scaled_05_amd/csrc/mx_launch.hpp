@@ -1,0 +1,48 @@
+// Host-side launchers of the gfx950 MXFP8 kernels (internal to the library;
+// the public C ABI is include/mxfp8.h).  Every launcher assumes its
+// arguments were validated by the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint8_t *q,
+                           uint8_t *scales, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t *q, const uint8_t *scales, int64_t rows, int64_t cols,
+                             int axis, void *out, bool out_bf16, hipStream_t stream);
+
+hipError_t launch_repack(const uint8_t *q, const uint8_t *scales, int64_t batch, int64_t N,
+                         int64_t K, uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                       const uint8_t *b_s, bool b_packed, int64_t M, int64_t N, int64_t K, void *c,
+                       bool c_bf16, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                               const uint8_t *b_s, const int32_t *offsets, int64_t G,
+                               int64_t M_total, int64_t N, int64_t K, void *c, bool c_bf16,
+                               hipStream_t stream);
+
+// Packed weight layout geometry (see mxfp8_repack in include/mxfp8.h).
+constexpr int64_t kPanelRows = 256;   // rows per packed panel
+constexpr int64_t kKStep = 128;       // K bytes per packed k-step (one MFMA K)
+constexpr int64_t kTileBytes = kPanelRows * kKStep;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t packed_panels(int64_t N) { return ceil_div(N, kPanelRows); }
+inline int64_t packed_ksteps(int64_t K) { return ceil_div(K, kKStep); }
+inline int64_t packed_kgroups(int64_t K) { return ceil_div(packed_ksteps(K), 4); }
+inline int64_t packed_q_bytes(int64_t batch, int64_t N, int64_t K) {
+    return batch * packed_panels(N) * packed_ksteps(K) * kTileBytes;
+}
+inline int64_t packed_s_bytes(int64_t batch, int64_t N, int64_t K) {
+    return batch * packed_panels(N) * 16 * packed_kgroups(K) * 256;
+}
+
+}  // namespace mx

@@ -18,3 +18,34 @@ def oracle_mod():
     import oracle
     oracle._load()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def mx():
+    """The HIP library's Python binding on cuda:0 (GPU tests only)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxfp8_block_scaled_05_amd as m
+    m.lib()
+    torch.cuda.set_device(0)
+    return m
+
+
+def to_dev(a):
+    """numpy array -> device tensor with the same bytes (uint16 -> bfloat16)."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def to_host(t):
+    import numpy as np
+    import torch
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

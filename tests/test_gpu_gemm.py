@@ -1,0 +1,361 @@
+"""GPU parity of mxfp8_repack, mxfp8_gemm and mxfp8_grouped_gemm against the oracle.
+
+Bars: repack bytes identical to the oracle's packing of the layout spec; GEMM
+results bit-identical where the exact result is representable in fp32 in any
+summation order (small-integer elements, narrow scales; one-hot blocks), and
+|C - C_ref| <= 1e-4 * sum_k |a_k b_k| per element otherwise (bf16 outputs add
+the bf16 rounding, 2^-8 |C_ref|).  Shapes span several tiles with ragged
+M/N/K tails, the Qwen3-8B qkv layer at full size (sampled rows), and MoE
+groups with empty and padded experts.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from conftest import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+E4M3_INT = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _quant_pair(oracle_mod, x):
+    return oracle_mod.quantize(x, 1)
+
+
+def _int_operand(rng, rows, K, lo=125, hi=130):
+    ints = rng.integers(-4, 5, size=(rows, K))
+    mag = np.vectorize(lambda v: E4M3_INT[abs(int(v))])(ints).astype(np.uint8)
+    codes = (mag | np.where(ints < 0, 0x80, 0)).astype(np.uint8)
+    scales = rng.integers(lo, hi, size=(rows, K // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def _hw_term(oracle_mod, aq, as_, bq, bs):
+    """Per element, sum over the 128-K steps of max_k |a_k b_k| within the step
+    (dequantized operands).  The MI355X FP8 matrix datapath sums each
+    instruction's products with about 12 bits relative to the largest product
+    (measured: at most 2^-10.8 of it per instruction), so on small-K,
+    outlier-dominated data the error can exceed 1e-4 * sum|ab|; adversarial
+    cases are checked against 1e-4 * sum|ab| + 2^-10 * this term."""
+    M, K = aq.shape
+    N = bq.shape[0]
+    A = np.abs(oracle_mod.dequantize(aq, as_, M, K, 1))
+    B = np.abs(oracle_mod.dequantize(bq, bs, N, K, 1))
+    H = np.zeros((M, N))
+    for k0 in range(0, K, 128):
+        step = np.zeros((M, N))
+        for k in range(k0, min(K, k0 + 128)):
+            np.maximum(step, np.outer(A[:, k], B[:, k]), out=step)
+        H += step
+    return H
+
+
+def _bound_with_hw(c, ref, sabs, H, out):
+    err = np.abs(np.asarray(c, np.float64) - ref)
+    allow = 1e-4 * sabs + 2.0 ** -10 * H
+    if out == "bf16":
+        allow = allow + 2.0 ** -8 * np.abs(ref)
+    return bool(np.all(err <= allow)), float(np.max(err / np.maximum(allow, 1e-300)))
+
+
+def _gemm_dev(mx, aq, as_, bq, bs, packed, out_dtype):
+    a_q, a_s = to_dev(aq), to_dev(as_)
+    if packed:
+        w = mx.repack(to_dev(bq), to_dev(bs))
+        c = mx.gemm(a_q, a_s, w, out_dtype)
+    else:
+        c = mx.gemm(a_q, a_s, (to_dev(bq), to_dev(bs)), out_dtype)
+    torch.cuda.synchronize()
+    return to_host(c.float()) if out_dtype == torch.bfloat16 else to_host(c)
+
+
+@pytest.mark.parametrize("batch,N,K", [(1, 256, 128), (1, 300, 320), (3, 17, 96), (2, 512, 768),
+                                       (1, 6144, 4096)])
+def test_repack_matches_oracle(mx, oracle_mod, batch, N, K):
+    _say("repack", batch, N, K)
+    rng = np.random.default_rng(batch * N + K)
+    q = rng.integers(0, 256, (batch, N, K)).astype(np.uint8)
+    s = rng.integers(0, 256, (batch, N, K // 32)).astype(np.uint8)
+    qp_ref, sp_ref = oracle_mod.pack(q, s, batch, N, K)
+    w = mx.repack(to_dev(q), to_dev(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(w.q), qp_ref)
+    assert np.array_equal(to_host(w.s), sp_ref)
+    q2, s2 = oracle_mod.unpack(to_host(w.q), to_host(w.s), batch, N, K)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_one_hot_blocks_exact(mx, oracle_mod, packed):
+    """Only block b* of each row is non-zero: C = 32 * 2^(sa + sb - 254) exactly.
+    Different b* per row / column pins the lane -> (row, K block, scale byte)
+    mapping of the scaled MFMA."""
+    M, N, K = 64, 48, 512
+    nb = K // 32
+    rng = np.random.default_rng(30)
+    aq = np.zeros((M, K), np.uint8)
+    bq = np.zeros((N, K), np.uint8)
+    as_ = rng.integers(100, 150, (M, nb)).astype(np.uint8)
+    bs = rng.integers(100, 150, (N, nb)).astype(np.uint8)
+    ab = np.arange(M) % nb
+    bb = (np.arange(N) * 5) % nb
+    for m in range(M):
+        aq[m, ab[m] * 32:(ab[m] + 1) * 32] = 0x38
+    for n in range(N):
+        bq[n, bb[n] * 32:(bb[n] + 1) * 32] = 0x38
+    # make rows and columns that share a block meet: duplicate a few b*
+    bb[:M % N] = ab[:M % N]
+    bq[:] = 0
+    for n in range(N):
+        bq[n, bb[n] * 32:(bb[n] + 1) * 32] = 0x38
+    _say("gemm one-hot", packed)
+    c = _gemm_dev(mx, aq, as_, bq, bs, packed, torch.float32)
+    ref, _ = oracle_mod.gemm(aq, as_, bq, bs)
+    expect = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            if ab[m] == bb[n]:
+                expect[m, n] = 32.0 * 2.0 ** (int(as_[m, ab[m]]) + int(bs[n, bb[n]]) - 254)
+    assert np.array_equal(ref, expect)
+    assert np.array_equal(c.astype(np.float64), expect)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 416), (256, 512, 1024),
+                                   (33, 17, 32), (513, 264, 4096)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_exact_integer_cases(mx, oracle_mod, M, N, K, packed):
+    rng = np.random.default_rng(M + N + K)
+    aq, as_ = _int_operand(rng, M, K)
+    bq, bs = _int_operand(rng, N, K)
+    _say("gemm exact", M, N, K, packed)
+    c = _gemm_dev(mx, aq, as_, bq, bs, packed, torch.float32)
+    ref, _ = oracle_mod.gemm(aq, as_, bq, bs)
+    bad = np.argwhere(c.astype(np.float64) != ref)
+    assert bad.size == 0, (bad[:5], c[tuple(bad[0])], ref[tuple(bad[0])])
+
+
+def test_gemm_tiny_config(mx, oracle_mod):
+    d = wl.tiny(0)
+    xq, xs = _quant_pair(oracle_mod, d["X"])
+    wq, ws = _quant_pair(oracle_mod, d["W"])
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+    for packed in (False, True):
+        _say("gemm tiny", packed)
+        c = _gemm_dev(mx, xq, xs, wq, ws, packed, torch.float32)
+        ok, worst = oracle_mod.gemm_bound_ok(c, ref, sabs, "f32")
+        assert ok, worst
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 300, 416), (64, 1000, 2080), (1000, 96, 160)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_random_ragged(mx, oracle_mod, M, N, K, out):
+    rng = np.random.default_rng(M * N + K)
+    X = wl.normal_bf16(rng, (M, K), outlier_frac=0.01)
+    W = wl.normal_bf16(rng, (N, K), std=0.02)
+    xq, xs = _quant_pair(oracle_mod, X)
+    wq, ws = _quant_pair(oracle_mod, W)
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+    H = _hw_term(oracle_mod, xq, xs, wq, ws)
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    cs = []
+    for packed in (False, True):
+        _say("gemm random", M, N, K, out, packed)
+        c = _gemm_dev(mx, xq, xs, wq, ws, packed, tdt)
+        ok, worst = _bound_with_hw(c, ref, sabs, H, out)
+        assert ok, (packed, worst)
+        cs.append(c)
+    # packed and canonical B run the same arithmetic in the same order
+    assert np.array_equal(cs[0], cs[1])
+
+
+def test_gemm_dgrad_wgrad_orientations(mx, oracle_mod):
+    """The learner's three GEMMs through one A*B^T: fprop (X, W along K),
+    dgrad (dY along N, W quantized with axis 0), wgrad (dY, X along tokens)."""
+    rng = np.random.default_rng(31)
+    T, H, O = 256, 192, 320
+    X = wl.normal_bf16(rng, (T, H))
+    W = wl.normal_bf16(rng, (O, H), std=0.02)
+    dY = wl.normal_bf16(rng, (T, O), std=2.0 ** -10)
+    cases = {
+        "fprop": (oracle_mod.quantize(X, 1), oracle_mod.quantize(W, 1)),     # [T,H] x [O,H]^T
+        "dgrad": (oracle_mod.quantize(dY, 1), oracle_mod.quantize(W, 0)),    # [T,O] x [H,O]^T
+        "wgrad": (oracle_mod.quantize(dY, 0), oracle_mod.quantize(X, 0)),    # [O,T] x [H,T]^T
+    }
+    for name, ((aq, as_), (bq, bs)) in cases.items():
+        _say("gemm", name)
+        ref, sabs = oracle_mod.gemm(aq, as_, bq, bs)
+        c = _gemm_dev(mx, aq, as_, bq, bs, False, torch.float32)
+        ok, worst = _bound_with_hw(c, ref, sabs, _hw_term(oracle_mod, aq, as_, bq, bs), "f32")
+        assert ok, (name, worst)
+
+
+def test_gemm_qkv_full_size_sampled(mx, oracle_mod):
+    d = wl.qkv(0)
+    xq, xs = _quant_pair(oracle_mod, d["X"])
+    wq, ws = _quant_pair(oracle_mod, d["W"])
+    rows = np.sort(np.random.default_rng(32).choice(xq.shape[0], 48, replace=False))
+    rows[0], rows[-1] = 0, xq.shape[0] - 1
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws, rows=rows)
+    _say("gemm qkv full size")
+    c = _gemm_dev(mx, xq, xs, wq, ws, True, torch.bfloat16)
+    ok, worst = oracle_mod.gemm_bound_ok(c[rows], ref, sabs, "bf16")
+    assert ok, worst
+    # the page's healthy-kernel error band for a dense layer: relative error
+    # of the MXFP8 layer against the high-precision GEMM on the BF16 inputs
+    from workloads import bf16_bits_to_f32
+    xf = bf16_bits_to_f32(d["X"][rows]).astype(np.float64)
+    wf = bf16_bits_to_f32(d["W"]).astype(np.float64)
+    y = xf @ wf.T
+    rel = np.linalg.norm(c[rows] - y) / np.linalg.norm(y)
+    assert 0.005 < rel < 0.25, rel
+
+
+def test_gemm_deterministic(mx, oracle_mod):
+    rng = np.random.default_rng(33)
+    xq, xs = _quant_pair(oracle_mod, wl.normal_bf16(rng, (512, 1024)))
+    wq, ws = _quant_pair(oracle_mod, wl.normal_bf16(rng, (768, 1024), std=0.02))
+    a_q, a_s = to_dev(xq), to_dev(xs)
+    w = mx.repack(to_dev(wq), to_dev(ws))
+    c0 = mx.gemm(a_q, a_s, w, torch.float32)
+    for _ in range(5):
+        assert torch.equal(mx.gemm(a_q, a_s, w, torch.float32), c0)
+
+
+def _moe_case(oracle_mod, G, N, K, tokens, topk, seed, empty=()):
+    rng = np.random.default_rng(seed)
+    route = wl.zipf_topk_routing(rng, tokens, G, topk)
+    for e in empty:
+        route[route == e] = (e + 1) % G
+    off, row_token, counts = wl.group_layout(route, G)
+    X = wl.normal_bf16(rng, (tokens, K))
+    A = np.zeros((row_token.size, K), np.uint16)
+    A[row_token >= 0] = X[row_token[row_token >= 0]]
+    aq, as_ = oracle_mod.quantize(A, 1)
+    W = wl.normal_bf16(rng, (G, N, K), std=0.02)
+    bq = np.empty((G, N, K), np.uint8)
+    bs = np.empty((G, N, K // 32), np.uint8)
+    for g in range(G):
+        bq[g], bs[g] = oracle_mod.quantize(W[g], 1)
+    return aq, as_, bq, bs, off, row_token
+
+
+@pytest.mark.parametrize("G,N,K,tokens,topk", [(8, 256, 256, 300, 2), (5, 200, 160, 97, 3),
+                                               (16, 512, 768, 1024, 4)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_grouped_gemm_small(mx, oracle_mod, G, N, K, tokens, topk, out):
+    aq, as_, bq, bs, off, row_token = _moe_case(oracle_mod, G, N, K, tokens, topk, G + N,
+                                                empty=(1,))
+    ref, sabs, grp = oracle_mod.grouped_gemm(aq, as_, bq, bs, off)
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    w = mx.repack(to_dev(bq), to_dev(bs))
+    M = aq.shape[0]
+    sentinel = torch.full((M + 64, N), 7.0, dtype=tdt, device="cuda")
+    _say("grouped", G, N, K, tokens, out)
+    c = mx.grouped_gemm(to_dev(aq), to_dev(as_), w, to_dev(off), tdt, out=sentinel[:M])
+    torch.cuda.synchronize()
+    ch = to_host(sentinel.float())
+    ok, worst = oracle_mod.gemm_bound_ok(ch[:M], ref, sabs, out)
+    assert ok, worst
+    assert np.all(ch[M:] == 7.0)                 # nothing written past M_total
+    assert np.all(ch[:M][row_token < 0] == 0.0)  # zero padding rows give zero rows
+    assert c.data_ptr() == sentinel.data_ptr()
+
+
+def test_grouped_gemm_untouched_rows_outside_groups(mx, oracle_mod):
+    G, N, K = 4, 128, 128
+    rng = np.random.default_rng(34)
+    M = 256
+    aq, as_ = oracle_mod.quantize(wl.normal_bf16(rng, (M, K)), 1)
+    W = wl.normal_bf16(rng, (G, N, K), std=0.02)
+    bq = np.stack([oracle_mod.quantize(W[g], 1)[0] for g in range(G)])
+    bs = np.stack([oracle_mod.quantize(W[g], 1)[1] for g in range(G)])
+    off = np.array([32, 64, 64, 160, 192], np.int32)      # rows [0,32) and [192,256) in no group
+    ref, sabs, grp = oracle_mod.grouped_gemm(aq, as_, bq, bs, off)
+    w = mx.repack(to_dev(bq), to_dev(bs))
+    out = torch.full((M, N), -3.0, dtype=torch.float32, device="cuda")
+    _say("grouped untouched rows")
+    mx.grouped_gemm(to_dev(aq), to_dev(as_), w, to_dev(off), torch.float32, out=out)
+    ch = to_host(out)
+    inside = grp >= 0
+    ok, worst = oracle_mod.gemm_bound_ok(ch[inside], ref[inside], sabs[inside], "f32")
+    assert ok, worst
+    assert np.all(ch[~inside] == -3.0)
+
+
+def test_grouped_gemm_moe_full_size_sampled(mx, oracle_mod):
+    d = wl.moe(0)
+    aq, as_ = oracle_mod.quantize(d["A_gu"], 1)
+    G, N, K = d["W_gu"].shape
+    bq = np.empty((G, N, K), np.uint8)
+    bs = np.empty((G, N, K // 32), np.uint8)
+    for g in range(G):
+        bq[g], bs[g] = oracle_mod.quantize(d["W_gu"][g], 1)
+    rng = np.random.default_rng(35)
+    rows = np.sort(rng.choice(aq.shape[0], 96, replace=False))
+    ref, sabs, grp = oracle_mod.grouped_gemm(aq, as_, bq, bs, d["offsets"], rows=rows)
+    w = mx.repack(to_dev(bq), to_dev(bs))
+    _say("grouped MoE full size")
+    c = mx.grouped_gemm(to_dev(aq), to_dev(as_), w, to_dev(d["offsets"]), torch.bfloat16)
+    ch = to_host(c.float())
+    ok, worst = oracle_mod.gemm_bound_ok(ch[rows], ref, sabs, "bf16")
+    assert ok, worst
+
+
+def test_mfma_accumulation_error_model(mx, oracle_mod):
+    """The hardware term used above, pinned on its own: over many random
+    128-K single-step products with outliers, |C - C_ref| stays within
+    2^-10 * max_k |a_k b_k| (and the pure spec bound holds whenever the
+    products are not dominated by a few terms)."""
+    rng = np.random.default_rng(36)
+    M, N, K = 512, 256, 128
+    X = wl.normal_bf16(rng, (M, K), outlier_frac=0.02)
+    W = wl.normal_bf16(rng, (N, K), std=0.02, outlier_frac=0.02)
+    xq, xs = _quant_pair(oracle_mod, X)
+    wq, ws = _quant_pair(oracle_mod, W)
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+    H = _hw_term(oracle_mod, xq, xs, wq, ws)
+    c = _gemm_dev(mx, xq, xs, wq, ws, True, torch.float32).astype(np.float64)
+    err = np.abs(c - ref)
+    ratio = err / np.maximum(H, 1e-300)
+    _say("mfma error / max|ab| (log2):", float(np.log2(ratio.max() + 1e-300)))
+    assert np.all(err <= 2.0 ** -10 * H)
+    spread = sabs >= 8 * H          # sums not dominated by a few products
+    assert np.all(err[spread] <= 1e-4 * sabs[spread])
+
+
+def test_gemm_mlp_step_full_size_sampled(mx, oracle_mod):
+    """Qwen3-8B MLP micro-batch of 8192 tokens: the six GEMMs of forward, data
+    gradient and weight gradient at full size, in the launch configuration the
+    library picks for them, checked on sampled output rows against the oracle
+    (operands quantized by the oracle) with the 1e-4 * sum|ab| bound."""
+    d = wl.mlp(0)
+    q = {}
+    for name, axis in (("X", 1), ("h", 1), ("W_gu", 1), ("W_d", 1), ("dY_gu", 1), ("dY_d", 1),
+                       ("W_gu", 0), ("W_d", 0), ("X", 0), ("h", 0), ("dY_gu", 0), ("dY_d", 0)):
+        q[(name, axis)] = oracle_mod.quantize(d[name], axis)
+    gemms = [
+        ("fprop gate_up", ("X", 1), ("W_gu", 1), True, "bf16"),
+        ("fprop down", ("h", 1), ("W_d", 1), True, "bf16"),
+        ("dgrad gate_up", ("dY_gu", 1), ("W_gu", 0), False, "bf16"),
+        ("dgrad down", ("dY_d", 1), ("W_d", 0), False, "bf16"),
+        ("wgrad gate_up", ("dY_gu", 0), ("X", 0), False, "f32"),
+        ("wgrad down", ("dY_d", 0), ("h", 0), False, "f32"),
+    ]
+    rng = np.random.default_rng(37)
+    for name, ka, kb, packed, out in gemms:
+        aq, as_ = q[ka]
+        bq, bs = q[kb]
+        rows = np.sort(rng.choice(aq.shape[0], 6, replace=False))
+        _say("mlp", name, aq.shape, bq.shape)
+        ref, sabs = oracle_mod.gemm(aq, as_, bq, bs, rows=rows)
+        tdt = torch.float32 if out == "f32" else torch.bfloat16
+        c = _gemm_dev(mx, aq, as_, bq, bs, packed, tdt)
+        ok, worst = oracle_mod.gemm_bound_ok(c[rows], ref, sabs, out)
+        assert ok, (name, worst)
+        del c
