@@ -20,8 +20,8 @@
 //    image, so their copy is linear.
 //  - Out-of-range rows and the K tail read as zeros through the buffer
 //    resource's range check (never a memory access out of bounds).
-//  - Waves form a 2x2 grid; each wave owns (BM/2) x (BN/2) of C as
-//    (BM/32) x (BN/32) MFMA tiles accumulated in fp32.
+//  - 8 waves (two per SIMD) form a 2x4 grid; each wave owns (BM/2) x (BN/4)
+//    of C as 16x16 MFMA tiles accumulated in fp32.
 //  - Tiles are mapped XCD-aware: the hardware deals workgroups round-robin to
 //    the 8 XCDs, so workgroup ids are renumbered to give each XCD a
 //    contiguous range of tiles, ordered in groups of GROUP_M tile-rows so
@@ -47,7 +47,46 @@ struct GemmParams {
 };
 
 constexpr int kGroupM = 8;
-constexpr int kThreads = 256;
+// s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at max
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Buffer descriptor in SGPRs for inline asm: base, stride 0, num_records =
+// bytes (range-checked: out-of-range lanes read zeros), 32-bit data format.
+__device__ __forceinline__ v4i make_srd(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    v4i r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// LDS byte address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 4 bytes per lane, global -> LDS at m0 + 4 * lane (one wave = 256 B).
+__device__ __forceinline__ void dma4(v4i srd, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(srd), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+// 16 bytes per lane, global -> LDS at m0 + 16 * lane (one wave = 1 KB).
+__device__ __forceinline__ void dma16(v4i srd, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(srd), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+// 8 waves (two per SIMD) in a 2 (M) x 4 (N) grid: while one wave of a SIMD
+// waits on LDS fragment reads or the barrier, the other keeps its MFMAs issuing.
+constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
 
 // Operand fragment of one 16-row x 128-K MFMA tile.  The scaled MFMA reads
 // lane group j = lane/16 as two 16-byte K slices, K = 16j..16j+15 (bytes 0-15)
@@ -120,15 +159,27 @@ __device__ int find_group(const int32_t *off, int G, int64_t M_total, int tm, in
     return -1;
 }
 
-template <int BM, int BN, bool BPACK, bool OUT_BF16, bool GROUPED>
+template <int BM, int BN, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-    constexpr int FM = BM / 32, FN = BN / 32;     // MFMA tiles per wave (rows, cols)
-    constexpr int STAGE = (BM + BN) * 128;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;   // wave tile
+    constexpr int FM = WTM / 16, FN = WTN / 16;            // MFMA tiles per wave (rows, cols)
+    // LDS: two stages of [A tile | B tile | A scales | canonical-B scales],
+    // then (packed B) two buffers of one k-group of B scales.  On the
+    // K % 128 == 0 path every scale byte arrives by the same asm copies as
+    // the tiles, so the loop has no compiler-visible global load to wait on.
+    constexpr int TILE = (BM + BN) * 128;
+    constexpr int SA_OFF = TILE;                                  // BM rows x 4 B
+    constexpr int SB_OFF = TILE + (KALIGN ? BM * 4 : 0);          // BN rows x 4 B (canonical)
+    constexpr int STAGE = SB_OFF + ((KALIGN && !BPACK) ? BN * 4 : 0);
+    constexpr int SBG_BYTES = (BN / 16) * 256;                    // one k-group, packed B
+    constexpr int SBG_OFF = 2 * STAGE;
+    constexpr int LDS_BYTES = 2 * STAGE + (BPACK ? 2 * SBG_BYTES : 0);
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int wm = w / kWavesN, wn = w % kWavesN;
 
     int tm, tn;
     grouped_order(xcd_logical(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, tm, tn);
@@ -153,79 +204,105 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int64_t n0 = (int64_t)tn * BN;
     const int rows_a = (int)min((int64_t)BM, m_end - m0);
 
-    // ---- operand resources
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_q + m0 * K, (uint32_t)(rows_a * K));
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
-    __amdgpu_buffer_rsrc_t rb, rsb;
+    // ---- operand descriptors (SGPRs, for the inline-asm copies): each one
+    //      spans exactly the rows of this tile, so out-of-range lanes read 0
+    const v4i ra = make_srd(p.a_q + m0 * K, (uint32_t)(rows_a * K));
+    const v4i rsa = make_srd(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
+    v4i rb, rsb;
     if constexpr (BPACK) {
         const int64_t panel = n0 / kPanelRows, prow = n0 % kPanelRows;
         const uint8_t *bt = p.b_q + ((g * p.NP + panel) * p.KS) * kTileBytes + prow * 128;
-        rb = make_rsrc(bt, (uint32_t)((int64_t)p.KS * kTileBytes));
+        // exactly the bytes left in this panel from row prow of k-step 0
+        rb = make_srd(bt, (uint32_t)((int64_t)p.KS * kTileBytes - prow * 128));
         const uint8_t *bs = p.b_s + ((g * p.NP * 16 + n0 / 16) * p.KG) * 256;
-        rsb = make_rsrc(bs, (uint32_t)((int64_t)FN * 2 * p.KG * 256));
+        rsb = make_srd(bs, (uint32_t)((int64_t)(BN / 16) * p.KG * 256));
     } else {
         const int rows_b = (int)min((int64_t)BN, N - n0);
-        rb = make_rsrc(p.b_q + n0 * K, (uint32_t)(rows_b * K));
-        rsb = make_rsrc(p.b_s + n0 * KB, (uint32_t)(rows_b * KB));
+        rb = make_srd(p.b_q + n0 * K, (uint32_t)(rows_b * K));
+        rsb = make_srd(p.b_s + n0 * KB, (uint32_t)(rows_b * KB));
     }
+    // the same ranges as compiler-visible resources, for the byte-granular
+    // scale loads of the K % 128 != 0 path
+    const __amdgpu_buffer_rsrc_t rsa_c = make_rsrc(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
+    const __amdgpu_buffer_rsrc_t rsb_c = BPACK ? make_rsrc(p.b_s, 0u)
+        : make_rsrc(p.b_s + n0 * KB, (uint32_t)(min((int64_t)BN, N - n0) * KB));
+    const int Ki = (int)K, KBi = (int)KB;
+    const uint32_t lds0 = lds_addr(smem);
 
-    // ---- issue the global->LDS copies of k-step ks into stage st
-    auto issue_tiles = [&](int ks, int st) {
-        uint8_t *sa = smem + st * STAGE;
-        uint8_t *sb = sa + BM * 128;
+    // ---- global -> LDS copies of k-step ks into stage st (inline asm; the
+    //      loop waits for them explicitly: vmcnt + barrier)
+    auto issue = [&](int ks, int st) {
+        const uint32_t sbase = lds0 + st * STAGE;
 #pragma unroll
-        for (int i = 0; i < BM / 32; ++i) {
-            const int seg = i * 4 + w;                 // 1 KB LDS segment = 8 rows
+        for (int i = 0; i < BM / (8 * kWaves); ++i) {
+            const int seg = i * kWaves + w;            // 1 KB LDS segment = 8 rows
             const int rr = seg * 8 + (lane >> 3);
             const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
-            const int64_t kk = (int64_t)ks * 128 + c * 16;
-            const uint32_t off = kk < K ? (uint32_t)(rr * K + kk) : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(sa + seg * 1024), 16, off, 0, 0, 0);
+            const int kk = ks * 128 + c * 16;
+            const uint32_t off = kk < Ki ? (uint32_t)(rr * Ki + kk) : kOOB;
+            dma16(ra, off, sbase + seg * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < BN / 32; ++i) {
-            const int seg = i * 4 + w;
+        for (int i = 0; i < BN / (8 * kWaves); ++i) {
+            const int seg = i * kWaves + w;
             uint32_t off;
             if constexpr (BPACK) {
                 off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
             } else {
                 const int rr = seg * 8 + (lane >> 3);
                 const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
-                const int64_t kk = (int64_t)ks * 128 + c * 16;
-                off = kk < K ? (uint32_t)(rr * K + kk) : kOOB;
+                const int kk = ks * 128 + c * 16;
+                off = kk < Ki ? (uint32_t)(rr * Ki + kk) : kOOB;
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + seg * 1024), 16, off, 0, 0, 0);
+            dma16(rb, off, sbase + BM * 128 + seg * 1024);
+        }
+        if constexpr (KALIGN) {
+            // A scales: the row's four block bytes of this step are one dword
+            if (w < BM / 64) {
+                const int rr = w * 64 + lane;
+                dma4(rsa, (uint32_t)(rr * KBi + ks * 4), sbase + SA_OFF + w * 256);
+            }
+            if constexpr (!BPACK) {
+                if (w < BN / 64) {
+                    const int rr = w * 64 + lane;
+                    dma4(rsb, (uint32_t)(rr * KBi + ks * 4), sbase + SB_OFF + w * 256);
+                }
+            }
+        }
+        if constexpr (BPACK) {
+            // packed B scales: one k-group (four steps) per copy, 256 B per atom
+            if ((ks & 3) == 0) {
+                const int grp = ks >> 2;
+                const uint32_t gbase = lds0 + SBG_OFF + (grp & 1) * SBG_BYTES;
+#pragma unroll
+                for (int a0 = 0; a0 < BN / 16; a0 += kWaves) {
+                    const int atom = a0 + w;
+                    if (BN / 16 >= kWaves || atom < BN / 16)
+                        dma4(rsb, (uint32_t)((atom * p.KG + grp) * 256 + lane * 4), gbase + atom * 256);
+                }
+            }
         }
     };
 
-    // ---- scale fetches: A (and canonical B) one byte per MFMA tile per step;
-    //      packed B one dword per MFMA tile per group of four steps
+    // ---- K % 128 != 0 path: scale bytes by compiler-visible loads, fetched
+    //      one step ahead (the K tail's blocks read as 0)
     const int lrow = lane & 15, lblk = lane >> 4;
-    auto fetch_sa = [&](int ks, int *dst) {
-        const int64_t blk = (int64_t)ks * 4 + lblk;
+    auto fetch_sa = [&](int ks, uint32_t *dst) {
+        const int blk = ks * 4 + lblk;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            const int rr = wm * (BM / 2) + i * 16 + lrow;
-            const uint32_t off = blk < KB ? (uint32_t)(rr * KB + blk) : kOOB;
-            dst[i] = __builtin_amdgcn_raw_buffer_load_b8(rsa, off, 0, 0);
+            const int rr = wm * WTM + i * 16 + lrow;
+            const uint32_t off = blk < KBi ? (uint32_t)(rr * KBi + blk) : kOOB;
+            dst[i] = __builtin_amdgcn_raw_buffer_load_b8(rsa_c, off, 0, 0);
         }
     };
-    auto fetch_sb = [&](int ks, int *dst) {
-        if constexpr (BPACK) {
+    auto fetch_sb = [&](int ks, uint32_t *dst) {
+        const int blk = ks * 4 + lblk;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int atom = wn * FN + j;
-                const uint32_t off = (uint32_t)((atom * p.KG + ks / 4) * 256 + lane * 4);
-                dst[j] = __builtin_amdgcn_raw_buffer_load_b32(rsb, off, 0, 0);
-            }
-        } else {
-            const int64_t blk = (int64_t)ks * 4 + lblk;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int rr = wn * (BN / 2) + j * 16 + lrow;
-                const uint32_t off = blk < KB ? (uint32_t)(rr * KB + blk) : kOOB;
-                dst[j] = __builtin_amdgcn_raw_buffer_load_b8(rsb, off, 0, 0);
-            }
+        for (int j = 0; j < FN; ++j) {
+            const int rr = wn * WTN + j * 16 + lrow;
+            const uint32_t off = blk < KBi ? (uint32_t)(rr * KBi + blk) : kOOB;
+            dst[j] = __builtin_amdgcn_raw_buffer_load_b8(rsb_c, off, 0, 0);
         }
     };
 
@@ -235,53 +312,65 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    int sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
+    uint32_t sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
     const int KS = p.KS;
-    issue_tiles(0, 0);
-    fetch_sa(0, sa_nxt);
-    fetch_sb(0, sb_nxt);
+    if constexpr (!KALIGN) {
+        fetch_sa(0, sa_nxt);
+        if constexpr (!BPACK) fetch_sb(0, sb_nxt);
+    }
+    issue(0, 0);
 
     for (int ks = 0; ks < KS; ++ks) {
         const int cur = ks & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // all copies of this step have landed (this wave's: vmcnt; everyone's:
+        // the barrier), and every wave is done reading the other stage
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
+        if constexpr (!KALIGN) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
-        if constexpr (BPACK) {
-            // the dword holds four steps; select this step's byte
-            if ((ks & 3) == 0) {
+            for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
+            if constexpr (!BPACK) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
-        }
-        if (ks + 1 < KS) {
-            issue_tiles(ks + 1, cur ^ 1);
-            fetch_sa(ks + 1, sa_nxt);
-            if constexpr (BPACK) {
-                if (((ks + 1) & 3) == 0) fetch_sb(ks + 1, sb_nxt);
-            } else {
-                fetch_sb(ks + 1, sb_nxt);
+            if (ks + 1 < KS) {
+                fetch_sa(ks + 1, sa_nxt);
+                if constexpr (!BPACK) fetch_sb(ks + 1, sb_nxt);
             }
         }
-        const uint8_t *sa = smem + cur * STAGE + wm * (BM / 2) * 128;
-        const uint8_t *sb = smem + cur * STAGE + BM * 128 + wn * (BN / 2) * 128;
-        v8i bf[FN];
-        int sbs[FN];
+        if (ks + 1 < KS) issue(ks + 1, cur ^ 1);
+
+        const uint8_t *st = smem + cur * STAGE;
+        const uint8_t *sa = st + wm * WTM * 128;
+        const uint8_t *sb = st + BM * 128 + wn * WTN * 128;
+        int sas[FM], sbs[FN];
+        // the MFMA reads bits [7:0] of each scale register (op_sel 0)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            if constexpr (KALIGN) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
+            else sas[i] = (int)(sa_cur[i] & 0xFFu);
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            bf[j] = lds_frag(sb + j * 16 * 128, lane);
-            sbs[j] = BPACK ? (int)((uint32_t)sb_cur[j] >> (8 * (ks & 3))) : sb_cur[j];
+            if constexpr (BPACK) {
+                const uint32_t *sg = reinterpret_cast<const uint32_t *>(smem + SBG_OFF + ((ks >> 2) & 1) * SBG_BYTES);
+                sbs[j] = (int)(sg[(wn * FN + j) * 64 + lane] >> (8 * (ks & 3)));
+            } else if constexpr (KALIGN) {
+                sbs[j] = st[SB_OFF + (wn * WTN + j * 16 + lrow) * 4 + lblk];
+            } else {
+                sbs[j] = (int)(sb_cur[j] & 0xFFu);
+            }
         }
+        v8i bf[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sb + j * 16 * 128, lane);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const v8i af = lds_frag(sa + i * 16 * 128, lane);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af, bf[j], acc[i][j], 0, 0, 0, sa_cur[i], 0, sbs[j]);
+                    af, bf[j], acc[i][j], 0, 0, 0, sas[i], 0, sbs[j]);
         }
     }
 
@@ -290,10 +379,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t col = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+            const int64_t col = n0 + wn * WTN + j * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + r;
+                const int64_t row = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
                 if (row < m_end && col < N) {
                     if constexpr (OUT_BF16)
                         static_cast<uint16_t *>(p.c)[row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
@@ -305,17 +394,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-template <int BM, int BN, bool GROUPED>
-static hipError_t launch_cfg(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
+template <int BM, int BN, bool GROUPED, bool KALIGN>
+static hipError_t launch_cfg2(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
     dim3 grid((unsigned)nwg), block(kThreads);
     if (b_packed) {
-        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true, GROUPED>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false, GROUPED>), grid, block, 0, s, p);
+        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true, GROUPED, KALIGN>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false, GROUPED, KALIGN>), grid, block, 0, s, p);
     } else {
-        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, false, true, GROUPED>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false, GROUPED>), grid, block, 0, s, p);
+        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, false, true, GROUPED, KALIGN>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false, GROUPED, KALIGN>), grid, block, 0, s, p);
     }
     return hipGetLastError();
+}
+
+template <int BM, int BN, bool GROUPED>
+static hipError_t launch_cfg(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
+    if (p.K % 128 == 0) return launch_cfg2<BM, BN, GROUPED, true>(p, b_packed, c_bf16, nwg, s);
+    return launch_cfg2<BM, BN, GROUPED, false>(p, b_packed, c_bf16, nwg, s);
 }
 
 hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
