@@ -33,10 +33,22 @@ BF16_PEAK_TFLOPS = 2500.0
 Q_BYTES_PER_ELT = 2 + 1 + 1 / 32     # quantize: BF16 in, E4M3 + E8M0 out
 REPACK_BYTES_PER_ELT = 2 * (1 + 1 / 32)
 
-# HBM traffic of the dominant kernel measured with rocprofv3 --pmc
-# (FETCH_SIZE / WRITE_SIZE per dispatch, scaled by the copy-kernel factor);
-# filled in from profiles/ once measured for the current kernel, else None.
-GEMM_QKV_TRAFFIC_BYTES = None
+def measured_gemm_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (scaled by the copy-kernel factors), if it was taken on
+    the GEMM source that is built now; None otherwise."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "qkv_step_hbm_traffic.md")
+    src = os.path.join(ROOT, "mxfp8_block_scaled_05_amd", "csrc", "gemm.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(path).read().splitlines() if ": " in line
+                      and line.split(": ", 1)[0] in ("traffic_bytes_per_launch", "gemm_source_sha256"))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields.get("gemm_source_sha256", "").strip() != sha:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def _bf16_dev(a, dev):
@@ -148,7 +160,7 @@ def bench_qkv(args, dev):
         "kernels": kern,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MXFP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP8_PEAK_TFLOPS, 4),
-                     "traffic": GEMM_QKV_TRAFFIC_BYTES},
+                     "traffic": measured_gemm_traffic()},
     }
     return out
 
@@ -158,12 +170,10 @@ def _bw(us, nbytes):
     return {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline_qkv(rows_small: int = 64, rows_large: int = 2048):
-    """The oracle (plain C, OpenMP) on a bounded sample of the qkv step: full
-    quantize of W and X, full pack of W, and the fp64 GEMM over the first
-    `rows_small` and `rows_large` rows of X; the GEMM time for all rows is the
-    straight line through those two points (the oracle dequantizes B once per
-    call, a fixed cost, then spends the same time on every row)."""
+def cpu_baseline_qkv():
+    """The oracle (plain C; OpenMP over independent output rows) on the same
+    qkv step at full size: quantize W and X, pack W, and the fp64 GEMM over
+    every row of X.  No extrapolation: the whole step is run once."""
     import oracle
     import workloads as wl
     oracle._load()
@@ -180,14 +190,9 @@ def cpu_baseline_qkv(rows_small: int = 64, rows_large: int = 2048):
     t0 = time.perf_counter()
     oracle.pack(wq, ws, 1, N, K)
     t["repack_W"] = time.perf_counter() - t0
-    tg = []
-    for r in (rows_small, rows_large):
-        t0 = time.perf_counter()
-        oracle.gemm(xq, xs, wq, ws, rows=np.arange(r, dtype=np.int64))
-        tg.append(time.perf_counter() - t0)
-    per_row = (tg[1] - tg[0]) / (rows_large - rows_small)
-    fixed = max(tg[0] - per_row * rows_small, 0.0)
-    t["gemm_extrapolated"] = fixed + per_row * M
+    t0 = time.perf_counter()
+    oracle.gemm(xq, xs, wq, ws)
+    t["gemm"] = time.perf_counter() - t0
     total = sum(t.values())
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {
@@ -195,11 +200,23 @@ def cpu_baseline_qkv(rows_small: int = 64, rows_large: int = 2048):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "qkv step: full quantize of W and X, full pack of W; fp64 GEMM timed on %d and "
-                  "%d of %d rows of X (%.2f s, %.2f s) and extrapolated linearly to all rows"
-                  % (rows_small, rows_large, M, tg[0], tg[1]),
+        "sample": "one full qkv step (quantize W[6144x4096] and X[4096x4096], pack W, "
+                  "fp64 GEMM of all 4096 rows) run once",
         "seconds": {k: round(v, 3) for k, v in t.items()},
     }
+
+
+def copy_calibration(dev, nbytes: int = 512 << 20, reps: int = 3):
+    """A plain device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters of a profiled run (reads nbytes, writes nbytes)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -209,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv", choices=["qkv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 512 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -222,6 +241,8 @@ def main():
     mx.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(dev)
     out = bench_qkv(args, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_qkv()

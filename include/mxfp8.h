@@ -120,15 +120,16 @@ size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which);
  *      weights [N][K]; K % 32 == 0, N >= 1, batch >= 1).
  * Out: q_packed (mxfp8_packed_bytes(batch,N,K,0) bytes) and scales_packed
  *      (mxfp8_packed_bytes(batch,N,K,1) bytes), with this layout:
- *   NP = ceil(N/256) panels of 256 rows, KS = ceil(K/128) k-steps of 128,
- *   KG = ceil(KS/4) groups of 4 k-steps.
+ *   NP = ceil(N/256) panels of 256 rows, KS = ceil(K/128) k-steps of 128.
  *   elements [batch][NP][KS][256 rows][128 B]: the bytes k = 128*ks + 16c ..
  *     + 15 of row r of the panel form chunk c (0..7), stored at chunk slot
  *     c ^ f(r % 16), with f(t) = (t & 7) ^ (t >> 3) (a bank-conflict-free
  *     swizzle of the GEMM's LDS image).  Rows >= N and k >= K hold 0x00.
- *   scales [batch][NP*16 atoms of 16 rows][KG][64 lanes][4 B]: byte j of
- *     lane l of (atom a, group g) is the scale of row 16a + (l % 16), block
- *     4*(4g + j) + (l / 16).  Rows >= N or blocks >= K/32 hold 127 (1.0).
+ *   scales [batch][NP][KS][16 atoms of 16 rows][64 lanes] bytes: byte
+ *     (panel, kstep, atom, lane) is the scale of row 256*panel + 16*atom +
+ *     (lane % 16), block 4*kstep + (lane / 16) (the byte the GEMM's MFMA lane
+ *     `lane` supplies for that 16-row atom).  Rows >= N or blocks >= K/32
+ *     hold 127 (1.0).
  */
 mxfp8_status mxfp8_repack(const uint8_t *q, const uint8_t *scales,
                           int64_t batch, int64_t rows, int64_t cols,

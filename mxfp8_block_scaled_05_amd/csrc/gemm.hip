@@ -9,10 +9,13 @@
 // lane group s (= lane / 16) applies to block s.  So the scales never leave
 // their byte form and no rescaling arithmetic runs outside the matrix core.
 //
-// Structure (one workgroup = 4 waves = one BM x BN output tile):
-//  - K advances in steps of 128.  A and B tiles of a step are staged in LDS
-//    with buffer_load_dwordx4 ... lds (global -> LDS, no VGPR round trip),
-//    double-buffered: step k+1 streams in while step k feeds the MFMAs.
+// Structure (one workgroup = 8 waves = one BM x BN output tile):
+//  - K advances in steps of 128.  The A and B tiles of a step and their
+//    scale bytes are staged in LDS with buffer_load ... lds (global -> LDS,
+//    no VGPR round trip) issued as inline asm, in an NST-stage ring: the
+//    copies for step k+NST-1 stream in while step k feeds the MFMAs.  Every
+//    wave issues the same number of copies per step, so one immediate
+//    s_waitcnt vmcnt(n) + barrier per step waits for exactly the step needed.
 //  - LDS rows are 128 B (one step); the 16-byte chunk c of row r sits at slot
 //    c ^ f(r % 16), which makes the ds_read_b128 of 16 rows at one chunk bank
 //    conflict free.  Canonical operands are swizzled by choosing each lane's
@@ -43,12 +46,13 @@ struct GemmParams {
     int tiles_m, tiles_n;   // grid tile counts (grouped: upper bound for m)
     const int32_t *offsets;  // grouped only
     int G;
-    int KS, KG, NP;          // k-steps, k-groups, packed panels of B
+    int KS, NP;              // k-steps, packed panels of B
 };
 
 constexpr int kGroupM = 8;
-// s_waitcnt immediate for gfx9: vmcnt(0), expcnt and lgkmcnt left at max
-constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate for gfx9 with expcnt and lgkmcnt left at their maximum:
+// vmcnt(n) for n < 64 (bits [3:0] and [15:14])
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Buffer descriptor in SGPRs for inline asm: base, stride 0, num_records =
 // bytes (range-checked: out-of-range lanes read zeros), 32-bit data format.
@@ -159,23 +163,27 @@ __device__ int find_group(const int32_t *off, int G, int64_t M_total, int tm, in
     return -1;
 }
 
-template <int BM, int BN, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN>
+template <int BM, int BN, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, int NST>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;   // wave tile
     constexpr int FM = WTM / 16, FN = WTN / 16;            // MFMA tiles per wave (rows, cols)
-    // LDS: two stages of [A tile | B tile | A scales | canonical-B scales],
-    // then (packed B) two buffers of one k-group of B scales.  On the
-    // K % 128 == 0 path every scale byte arrives by the same asm copies as
-    // the tiles, so the loop has no compiler-visible global load to wait on.
+    // LDS: NST stages of [A tile | B tile | A scales | B scales].  A scales
+    // (K % 128 == 0) are a dword per row per step; B scales are the packed
+    // layout's 64 bytes per 16-row atom per step, or (canonical B, K % 128
+    // == 0) a dword per row.  With K % 128 != 0, A (and canonical B) scale
+    // bytes come through registers instead (compiler-visible byte loads).
+    constexpr bool SA_LDS = KALIGN;
+    constexpr bool SB_LDS = BPACK || KALIGN;
     constexpr int TILE = (BM + BN) * 128;
-    constexpr int SA_OFF = TILE;                                  // BM rows x 4 B
-    constexpr int SB_OFF = TILE + (KALIGN ? BM * 4 : 0);          // BN rows x 4 B (canonical)
-    constexpr int STAGE = SB_OFF + ((KALIGN && !BPACK) ? BN * 4 : 0);
-    constexpr int SBG_BYTES = (BN / 16) * 256;                    // one k-group, packed B
-    constexpr int SBG_OFF = 2 * STAGE;
-    constexpr int LDS_BYTES = 2 * STAGE + (BPACK ? 2 * SBG_BYTES : 0);
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+    constexpr int SA_OFF = TILE;
+    constexpr int SB_OFF = SA_OFF + (SA_LDS ? BM * 4 : 0);
+    constexpr int STAGE = SB_OFF + (SB_LDS ? BN * 4 : 0);
+    static_assert(NST * STAGE <= 160 * 1024, "LDS budget");
+    static_assert(KALIGN || NST == 2, "register-fed scales are fetched one step ahead");
+    // copies per wave per step: tile segments plus one A- and one B-scale copy
+    constexpr int CPW = BM / (8 * kWaves) + BN / (8 * kWaves) + (SA_LDS ? 1 : 0) + (SB_LDS ? 1 : 0);
+    static_assert(CPW * (NST - 2) < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -205,17 +213,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int rows_a = (int)min((int64_t)BM, m_end - m0);
 
     // ---- operand descriptors (SGPRs, for the inline-asm copies): each one
-    //      spans exactly the rows of this tile, so out-of-range lanes read 0
+    //      spans exactly the bytes of this tile, so out-of-range lanes read 0
     const v4i ra = make_srd(p.a_q + m0 * K, (uint32_t)(rows_a * K));
     const v4i rsa = make_srd(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
     v4i rb, rsb;
     if constexpr (BPACK) {
         const int64_t panel = n0 / kPanelRows, prow = n0 % kPanelRows;
         const uint8_t *bt = p.b_q + ((g * p.NP + panel) * p.KS) * kTileBytes + prow * 128;
-        // exactly the bytes left in this panel from row prow of k-step 0
         rb = make_srd(bt, (uint32_t)((int64_t)p.KS * kTileBytes - prow * 128));
-        const uint8_t *bs = p.b_s + ((g * p.NP * 16 + n0 / 16) * p.KG) * 256;
-        rsb = make_srd(bs, (uint32_t)((int64_t)(BN / 16) * p.KG * 256));
+        const uint8_t *bs = p.b_s + ((g * p.NP + panel) * p.KS) * kScaleStepBytes + (prow / 16) * 64;
+        rsb = make_srd(bs, (uint32_t)((int64_t)p.KS * kScaleStepBytes - (prow / 16) * 64));
     } else {
         const int rows_b = (int)min((int64_t)BN, N - n0);
         rb = make_srd(p.b_q + n0 * K, (uint32_t)(rows_b * K));
@@ -224,13 +231,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // the same ranges as compiler-visible resources, for the byte-granular
     // scale loads of the K % 128 != 0 path
     const __amdgpu_buffer_rsrc_t rsa_c = make_rsrc(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
-    const __amdgpu_buffer_rsrc_t rsb_c = BPACK ? make_rsrc(p.b_s, 0u)
-        : make_rsrc(p.b_s + n0 * KB, (uint32_t)(min((int64_t)BN, N - n0) * KB));
+    const __amdgpu_buffer_rsrc_t rsb_c =
+        make_rsrc(p.b_s + (BPACK ? 0 : n0 * KB), BPACK ? 0u : (uint32_t)(min((int64_t)BN, N - n0) * KB));
     const int Ki = (int)K, KBi = (int)KB;
     const uint32_t lds0 = lds_addr(smem);
 
-    // ---- global -> LDS copies of k-step ks into stage st (inline asm; the
-    //      loop waits for them explicitly: vmcnt + barrier)
+    // ---- global -> LDS copies of k-step ks into stage st: CPW per wave
     auto issue = [&](int ks, int st) {
         const uint32_t sbase = lds0 + st * STAGE;
 #pragma unroll
@@ -256,36 +262,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             }
             dma16(rb, off, sbase + BM * 128 + seg * 1024);
         }
-        if constexpr (KALIGN) {
-            // A scales: the row's four block bytes of this step are one dword
-            if (w < BM / 64) {
-                const int rr = w * 64 + lane;
-                dma4(rsa, (uint32_t)(rr * KBi + ks * 4), sbase + SA_OFF + w * 256);
-            }
-            if constexpr (!BPACK) {
-                if (w < BN / 64) {
-                    const int rr = w * 64 + lane;
-                    dma4(rsb, (uint32_t)(rr * KBi + ks * 4), sbase + SB_OFF + w * 256);
-                }
+        // scale copies: 256 B segments.  With more than two stages every wave
+        // issues one of each (a wave beyond the segment count repeats one:
+        // identical bytes to the same place) so the per-wave count CPW, and
+        // with it the loop's vmcnt immediate, is uniform; with two stages
+        // (vmcnt(0)) only the waves with a segment of their own copy.
+        if constexpr (SA_LDS) {
+            if (NST > 2 || w < BM / 64) {
+                const int seg = w % (BM / 64);
+                const int rr = seg * 64 + lane;
+                dma4(rsa, (uint32_t)(rr * KBi + ks * 4), sbase + SA_OFF + seg * 256);
             }
         }
-        if constexpr (BPACK) {
-            // packed B scales: one k-group (four steps) per copy, 256 B per atom
-            if ((ks & 3) == 0) {
-                const int grp = ks >> 2;
-                const uint32_t gbase = lds0 + SBG_OFF + (grp & 1) * SBG_BYTES;
-#pragma unroll
-                for (int a0 = 0; a0 < BN / 16; a0 += kWaves) {
-                    const int atom = a0 + w;
-                    if (BN / 16 >= kWaves || atom < BN / 16)
-                        dma4(rsb, (uint32_t)((atom * p.KG + grp) * 256 + lane * 4), gbase + atom * 256);
-                }
+        if constexpr (SB_LDS) {
+            if (NST > 2 || w < BN / 64) {
+                const int seg = w % (BN / 64);
+                uint32_t off;
+                if constexpr (BPACK) off = (uint32_t)(ks * kScaleStepBytes + seg * 256 + lane * 4);
+                else off = (uint32_t)((seg * 64 + lane) * KBi + ks * 4);
+                dma4(rsb, off, sbase + SB_OFF + seg * 256);
             }
         }
     };
 
-    // ---- K % 128 != 0 path: scale bytes by compiler-visible loads, fetched
-    //      one step ahead (the K tail's blocks read as 0)
+    // ---- K % 128 != 0: A (and canonical B) scale bytes by compiler-visible
+    //      loads, one step ahead (the K tail's blocks read as 0)
     const int lrow = lane & 15, lblk = lane >> 4;
     auto fetch_sa = [&](int ks, uint32_t *dst) {
         const int blk = ks * 4 + lblk;
@@ -314,31 +315,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
     uint32_t sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
     const int KS = p.KS;
-    if constexpr (!KALIGN) {
-        fetch_sa(0, sa_nxt);
-        if constexpr (!BPACK) fetch_sb(0, sb_nxt);
-    }
-    issue(0, 0);
+    if constexpr (!SA_LDS) fetch_sa(0, sa_nxt);
+    if constexpr (!SB_LDS) fetch_sb(0, sb_nxt);
+#pragma unroll
+    for (int s0 = 0; s0 < NST - 1; ++s0)
+        if (s0 < KS) issue(s0, s0);
 
     for (int ks = 0; ks < KS; ++ks) {
-        const int cur = ks & 1;
-        // all copies of this step have landed (this wave's: vmcnt; everyone's:
-        // the barrier), and every wave is done reading the other stage
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        const int cur = ks % NST;
+        // this step's copies have landed (this wave's: vmcnt, letting the
+        // copies of later steps stay in flight; everyone's: the barrier), and
+        // every wave is done reading the stage the next issue overwrites
+        if constexpr (NST >= 3) {
+            if (ks + NST - 2 < KS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(CPW * (NST - 2)));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        } else {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
         __syncthreads();
-        if constexpr (!KALIGN) {
+        if constexpr (!SA_LDS || !SB_LDS) {
+            if constexpr (!SA_LDS) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
-            if constexpr (!BPACK) {
+                for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
+            }
+            if constexpr (!SB_LDS) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
             }
             if (ks + 1 < KS) {
-                fetch_sa(ks + 1, sa_nxt);
-                if constexpr (!BPACK) fetch_sb(ks + 1, sb_nxt);
+                if constexpr (!SA_LDS) fetch_sa(ks + 1, sa_nxt);
+                if constexpr (!SB_LDS) fetch_sb(ks + 1, sb_nxt);
             }
         }
-        if (ks + 1 < KS) issue(ks + 1, cur ^ 1);
+        if (ks + NST - 1 < KS) issue(ks + NST - 1, (ks + NST - 1) % NST);
 
         const uint8_t *st = smem + cur * STAGE;
         const uint8_t *sa = st + wm * WTM * 128;
@@ -347,19 +356,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         // the MFMA reads bits [7:0] of each scale register (op_sel 0)
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-            if constexpr (KALIGN) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
+            if constexpr (SA_LDS) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
             else sas[i] = (int)(sa_cur[i] & 0xFFu);
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            if constexpr (BPACK) {
-                const uint32_t *sg = reinterpret_cast<const uint32_t *>(smem + SBG_OFF + ((ks >> 2) & 1) * SBG_BYTES);
-                sbs[j] = (int)(sg[(wn * FN + j) * 64 + lane] >> (8 * (ks & 3)));
-            } else if constexpr (KALIGN) {
-                sbs[j] = st[SB_OFF + (wn * WTN + j * 16 + lrow) * 4 + lblk];
-            } else {
-                sbs[j] = (int)(sb_cur[j] & 0xFFu);
-            }
+            if constexpr (BPACK) sbs[j] = st[SB_OFF + (wn * FN + j) * 64 + lane];
+            else if constexpr (SB_LDS) sbs[j] = st[SB_OFF + (wn * WTN + j * 16 + lrow) * 4 + lblk];
+            else sbs[j] = (int)(sb_cur[j] & 0xFFu);
         }
         v8i bf[FN];
 #pragma unroll
@@ -394,23 +398,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-template <int BM, int BN, bool GROUPED, bool KALIGN>
+// Pipeline depth.  Two stages measured fastest on MI355X for every tile shape
+// here (a third stage keeps more copies in flight but did not shorten the
+// qkv GEMM); the NST > 2 path is kept for tuning.
+template <int BM, int BN>
+constexpr int stages_for() { return 2; }
+
+template <int BM, int BN, bool GROUPED, bool KALIGN, int NST>
 static hipError_t launch_cfg2(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
     dim3 grid((unsigned)nwg), block(kThreads);
     if (b_packed) {
-        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true, GROUPED, KALIGN>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false, GROUPED, KALIGN>), grid, block, 0, s, p);
+        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
     } else {
-        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, false, true, GROUPED, KALIGN>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false, GROUPED, KALIGN>), grid, block, 0, s, p);
+        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, false, true, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
     }
     return hipGetLastError();
 }
 
 template <int BM, int BN, bool GROUPED>
 static hipError_t launch_cfg(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
-    if (p.K % 128 == 0) return launch_cfg2<BM, BN, GROUPED, true>(p, b_packed, c_bf16, nwg, s);
-    return launch_cfg2<BM, BN, GROUPED, false>(p, b_packed, c_bf16, nwg, s);
+    if (p.K % 128 == 0) return launch_cfg2<BM, BN, GROUPED, true, stages_for<BM, BN>()>(p, b_packed, c_bf16, nwg, s);
+    return launch_cfg2<BM, BN, GROUPED, false, 2>(p, b_packed, c_bf16, nwg, s);
 }
 
 hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
@@ -420,13 +430,12 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = c;
     p.M = M; p.N = N; p.K = K;
     p.KS = (int)packed_ksteps(K);
-    p.KG = (int)packed_kgroups(K);
     p.NP = (int)packed_panels(N);
     p.G = 1;
     p.offsets = nullptr;
     const int cus = device_cu_count();
     // 256x256 tiles unless that leaves the last wave of tiles badly filled,
-    // then 256x128 (twice the tiles).
+    // then 256x128 (twice the tiles, and a three-stage pipeline).
     const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t waves256 = ceil_div(t256, cus);
     const double fill256 = (double)t256 / (double)(waves256 * cus);
@@ -448,7 +457,6 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uin
     p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = c;
     p.M = M_total; p.N = N; p.K = K;
     p.KS = (int)packed_ksteps(K);
-    p.KG = (int)packed_kgroups(K);
     p.NP = (int)packed_panels(N);
     p.G = (int)G;
     p.offsets = offsets;

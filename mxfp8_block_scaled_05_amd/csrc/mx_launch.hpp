@@ -37,12 +37,13 @@ constexpr int64_t kTileBytes = kPanelRows * kKStep;
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t packed_panels(int64_t N) { return ceil_div(N, kPanelRows); }
 inline int64_t packed_ksteps(int64_t K) { return ceil_div(K, kKStep); }
-inline int64_t packed_kgroups(int64_t K) { return ceil_div(packed_ksteps(K), 4); }
 inline int64_t packed_q_bytes(int64_t batch, int64_t N, int64_t K) {
     return batch * packed_panels(N) * packed_ksteps(K) * kTileBytes;
 }
+// scales: [batch][panel][k-step][16 atoms of 16 rows][64 lanes] bytes
+constexpr int64_t kScaleStepBytes = 16 * 64;
 inline int64_t packed_s_bytes(int64_t batch, int64_t N, int64_t K) {
-    return batch * packed_panels(N) * 16 * packed_kgroups(K) * 256;
+    return batch * packed_panels(N) * packed_ksteps(K) * kScaleStepBytes;
 }
 
 }  // namespace mx

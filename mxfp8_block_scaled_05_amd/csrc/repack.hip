@@ -10,9 +10,9 @@
 //   elements: [batch][panel of 256 rows][k-step of 128][256 rows][128 B], the
 //             16-byte chunk c of row r stored at slot c ^ f(r % 16) -- exactly
 //             the GEMM's LDS image of a B tile, so the GEMM copies it linearly.
-//   scales  : [batch][atom of 16 rows][group of 4 k-steps][64 lanes][4 B] --
-//             one dword per MFMA lane carries its scale byte for four
-//             consecutive k-steps.
+//   scales  : [batch][panel][k-step][16 atoms of 16 rows][64 lanes] bytes --
+//             one byte per MFMA lane per atom, 1 KB per panel and k-step, so
+//             the GEMM copies a tile's scales of one step as one block.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
@@ -39,28 +39,31 @@ __global__ __launch_bounds__(256) void repack_q_kernel(const uint8_t *__restrict
     }
 }
 
-// One thread per output dword (atom a, group g, lane l): byte j is the scale
-// of row 16a + l%16, block 4(4g + j) + l/16; padding holds 127.
+// One thread per output dword: bytes (panel, k-step, atom, lanes l..l+3) are
+// the scales of rows 256*panel + 16*atom + (l % 16) .. +3, block 4*kstep +
+// l/16 (four consecutive rows, one block); padding holds 127.
 __global__ __launch_bounds__(256) void repack_s_kernel(const uint8_t *__restrict__ s,
                                                        uint32_t *__restrict__ sp, int64_t batch,
-                                                       int64_t N, int64_t K, int64_t atoms,
-                                                       int64_t KG) {
-    const int64_t total = batch * atoms * KG * 64;
+                                                       int64_t N, int64_t K, int64_t NP,
+                                                       int64_t KS) {
+    const int64_t total = batch * NP * KS * (kScaleStepBytes / 4);
     const int64_t nb = K / 32;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t lane = i & 63;
-        const int64_t g = (i >> 6) % KG;
-        const int64_t a = (i / (64 * KG)) % atoms;
-        const int64_t b = i / (64 * KG * atoms);
-        const int64_t n = a * 16 + (lane & 15);
+        const int64_t lane0 = (i * 4) & 63;
+        const int64_t atom = (i >> 4) & 15;
+        const int64_t ks = (i >> 8) % KS;
+        const int64_t panel = (i >> 8) / KS % NP;
+        const int64_t b = (i >> 8) / (KS * NP);
+        const int64_t blk = 4 * ks + (lane0 >> 4);
+        const int64_t row0 = panel * kPanelRows + atom * 16 + (lane0 & 15);
         uint32_t word = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t blk = 4 * (4 * g + j) + (lane >> 4);
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = row0 + q;
             uint32_t v = 127u;
             if (n < N && blk < nb) v = s[(b * N + n) * nb + blk];
-            word |= v << (8 * j);
+            word |= v << (8 * q);
         }
         sp[i] = word;
     }
@@ -68,19 +71,18 @@ __global__ __launch_bounds__(256) void repack_s_kernel(const uint8_t *__restrict
 
 hipError_t launch_repack(const uint8_t *q, const uint8_t *scales, int64_t batch, int64_t N,
                          int64_t K, uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream) {
-    const int64_t NP = packed_panels(N), KS = packed_ksteps(K), KG = packed_kgroups(K);
+    const int64_t NP = packed_panels(N), KS = packed_ksteps(K);
     dim3 grid((unsigned)KS, (unsigned)NP, (unsigned)batch);
     hipLaunchKernelGGL(repack_q_kernel, grid, dim3(256), 0, stream, q, q_packed, N, K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t atoms = NP * 16;
-    const int64_t total = batch * atoms * KG * 64;
+    const int64_t total = batch * NP * KS * (kScaleStepBytes / 4);
     int64_t g = (total + 255) / 256;
     const int64_t cap = (int64_t)device_cu_count() * 16;
     if (g > cap) g = cap;
     if (g < 1) g = 1;
     hipLaunchKernelGGL(repack_s_kernel, dim3((unsigned)g), dim3(256), 0, stream, scales,
-                       reinterpret_cast<uint32_t *>(s_packed), batch, N, K, atoms, KG);
+                       reinterpret_cast<uint32_t *>(s_packed), batch, N, K, NP, KS);
     return hipGetLastError();
 }
 

@@ -329,17 +329,17 @@ int mxo_grouped_gemm_rows(const uint8_t *a_q, const uint8_t *a_s,
  *   elements: [b][panel][kstep][row 0..255][128 bytes]; inside a row the
  *     16-byte chunk c (k = kstep*128 + 16c .. +15) sits at chunk position
  *     c ^ f(row % 16), f(t) = (t & 7) ^ (t >> 3).  Rows >= N and k >= K are 0.
- *   scales: [b][atom = 16 rows, NP*16 atoms][kgroup = 4 ksteps][lane 0..63]
- *     [byte j 0..3]; byte (atom a, group g, lane l, j) is the scale of row
- *     16a + (l % 16), block 4(4g + j) + (l / 16).  Rows >= N or blocks >=
- *     K/32 hold 127 (the code of 1.0).
+ *   scales: [b][panel][kstep][atom 0..15 of 16 rows][lane 0..63] bytes; byte
+ *     (panel, kstep, atom, lane) is the scale of row 256*panel + 16*atom +
+ *     (lane % 16), block 4*kstep + (lane / 16).  Rows >= N or blocks >= K/32
+ *     hold 127 (the code of 1.0).
  */
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t mxo_packed_bytes(int64_t batch, int64_t N, int64_t K, int which) {
-    int64_t NP = ceil_div(N, 256), KS = ceil_div(K, 128), KG = ceil_div(KS, 4);
+    int64_t NP = ceil_div(N, 256), KS = ceil_div(K, 128);
     if (which == 0) return batch * NP * KS * 256 * 128;
-    return batch * NP * 16 * KG * 64 * 4;
+    return batch * NP * KS * 16 * 64;
 }
 
 static int64_t pk_elem_offset(int64_t N, int64_t K, int64_t b, int64_t n, int64_t k) {
@@ -351,10 +351,10 @@ static int64_t pk_elem_offset(int64_t N, int64_t K, int64_t b, int64_t n, int64_
 }
 
 static int64_t pk_scale_offset(int64_t N, int64_t K, int64_t b, int64_t n, int64_t blk) {
-    int64_t NP = ceil_div(N, 256), KS = ceil_div(K, 128), KG = ceil_div(KS, 4);
-    int64_t atom = n / 16, lane = (n % 16) + 16 * (blk % 4);
-    int64_t ks = blk / 4, g = ks / 4, j = ks % 4;
-    return (((b * NP * 16 + atom) * KG + g) * 64 + lane) * 4 + j;
+    int64_t NP = ceil_div(N, 256), KS = ceil_div(K, 128);
+    int64_t panel = n / 256, atom = (n % 256) / 16, lane = (n % 16) + 16 * (blk % 4);
+    int64_t ks = blk / 4;
+    return (((b * NP + panel) * KS + ks) * 16 + atom) * 64 + lane;
 }
 
 /* canonical -> packed (padding written as specified) */

@@ -34,7 +34,6 @@ def descriptors(M, N, K, BM, BN, packed, G=1, m0=0, m_end=None, n0=0, g=0):
     """(name, base_offset, num_records, buffer_size) of every descriptor of one tile."""
     KB = K // 32
     KS = ceil_div(K, KSTEP)
-    KG = ceil_div(KS, 4)
     NP = ceil_div(N, PANEL)
     m_end = M if m_end is None else m_end
     rows_a = min(BM, m_end - m0)
@@ -44,8 +43,10 @@ def descriptors(M, N, K, BM, BN, packed, G=1, m0=0, m_end=None, n0=0, g=0):
         panel, prow = n0 // PANEL, n0 % PANEL
         bt = ((g * NP + panel) * KS) * TILE_BYTES + prow * 128
         out.append(("b_q", bt, KS * TILE_BYTES - prow * 128, G * NP * KS * TILE_BYTES))
-        bs = ((g * NP * 16 + n0 // 16) * KG) * 256
-        out.append(("b_s", bs, (BN // 16) * KG * 256, G * NP * 16 * KG * 256))
+        bs = ((g * NP + panel) * KS) * 1024 + (prow // 16) * 64
+        out.append(("b_s", bs, KS * 1024 - (prow // 16) * 64, G * NP * KS * 1024))
+        # the per-step scale copies stay inside that range
+        assert (KS - 1) * 1024 + BN * 4 <= KS * 1024 - (prow // 16) * 64
     else:
         rows_b = min(BN, N - n0)
         out.append(("b_q", n0 * K, rows_b * K, N * K))
@@ -111,26 +112,38 @@ def test_grouped_descriptors_inside_buffers(G, N, K, offsets):
             check_tile(M_total, N, K, BM, BN, True, G=G, m0=m0, m_end=m_end, n0=tn * BN, g=g)
 
 
+def stages_for(BM, BN):
+    return 3 if (BM + BN) * 128 + (BM + BN) * 4 <= 52 * 1024 else 2
+
+
 @pytest.mark.parametrize("BM,BN", [(256, 256), (256, 128), (128, 256)])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("kalign", [False, True])
 def test_lds_footprint(BM, BN, packed, kalign):
-    """Two stages of [A tile | B tile | A scales | canonical-B scales] plus two
-    k-group buffers of packed B scales fit the 160 KB of LDS, and every copy
-    lands inside its region."""
+    """NST stages of [A tile | B tile | A scales | B scales] fit the 160 KB of
+    LDS, every copy lands inside its region, and each wave issues the same
+    number of copies per step (the loop's vmcnt immediate relies on it)."""
+    nst = stages_for(BM, BN) if kalign else 2
+    sa_lds, sb_lds = kalign, packed or kalign
     tile = (BM + BN) * 128
     sa_off = tile
-    sb_off = tile + (BM * 4 if kalign else 0)
-    stage = sb_off + (BN * 4 if (kalign and not packed) else 0)
-    sbg = (BN // 16) * 256
-    alloc = 2 * stage + (2 * sbg if packed else 0)
-    assert alloc <= 160 * 1024
+    sb_off = sa_off + (BM * 4 if sa_lds else 0)
+    stage = sb_off + (BN * 4 if sb_lds else 0)
+    assert nst * stage <= 160 * 1024
     segs_a, segs_b = BM // 8, BN // 8
     assert segs_a % WAVES == 0 and segs_b % WAVES == 0
     assert (segs_a + segs_b) * 1024 == tile                  # tile copies fill [0, tile)
-    if kalign:
-        assert BM // 64 <= WAVES and sa_off + (BM // 64) * 256 <= sb_off
-        if not packed:
-            assert sb_off + (BN // 64) * 256 <= stage
-    if packed:
-        assert 2 * stage + 2 * sbg <= alloc and (BN // 16) * 256 == sbg
+    per_wave = {w: 0 for w in range(WAVES)}
+    for w in range(WAVES):
+        per_wave[w] += segs_a // WAVES + segs_b // WAVES
+        if sa_lds:
+            seg = w % (BM // 64)
+            assert sa_off + seg * 256 + 256 <= sb_off
+            per_wave[w] += 1
+        if sb_lds:
+            seg = w % (BN // 64)
+            assert sb_off + seg * 256 + 256 <= stage
+            per_wave[w] += 1
+    assert len(set(per_wave.values())) == 1
+    cpw = per_wave[0]
+    assert cpw * (nst - 2) < 64
