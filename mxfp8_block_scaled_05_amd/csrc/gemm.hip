@@ -12,10 +12,10 @@
 // Structure (one workgroup = 8 waves = one BM x BN output tile):
 //  - K advances in steps of 128.  The A and B tiles of a step and their
 //    scale bytes are staged in LDS with buffer_load ... lds (global -> LDS,
-//    no VGPR round trip) issued as inline asm, in an NST-stage ring: the
-//    copies for step k+NST-1 stream in while step k feeds the MFMAs.  Every
-//    wave issues the same number of copies per step, so one immediate
-//    s_waitcnt vmcnt(n) + barrier per step waits for exactly the step needed.
+//    no VGPR round trip) issued as inline asm and awaited explicitly
+//    (s_waitcnt vmcnt + barrier), so the compiler never orders its own waits
+//    behind them.
+//  - A 2-stage ring with one barrier at the top of each step.
 //  - LDS rows are 128 B (one step); the 16-byte chunk c of row r sits at slot
 //    c ^ f(r % 16), which makes the ds_read_b128 of 16 rows at one chunk bank
 //    conflict free.  Canonical operands are swizzled by choosing each lane's
@@ -23,8 +23,8 @@
 //    image, so their copy is linear.
 //  - Out-of-range rows and the K tail read as zeros through the buffer
 //    resource's range check (never a memory access out of bounds).
-//  - 8 waves (two per SIMD) form a 2x4 grid; each wave owns (BM/2) x (BN/4)
-//    of C as 16x16 MFMA tiles accumulated in fp32.
+//  - 8 waves (two per SIMD) form a WM x (8/WM) grid; each wave owns a
+//    (BM/WM) x (BN/(8/WM)) block of C as 16x16 MFMA tiles accumulated in fp32.
 //  - Tiles are mapped XCD-aware: the hardware deals workgroups round-robin to
 //    the 8 XCDs, so workgroup ids are renumbered to give each XCD a
 //    contiguous range of tiles, ordered in groups of GROUP_M tile-rows so
@@ -86,10 +86,9 @@ __device__ __forceinline__ void dma16(v4i srd, uint32_t voff, uint32_t lds_base)
                  : "v"(voff), "s"(srd), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
-// 8 waves (two per SIMD) in a 2 (M) x 4 (N) grid: while one wave of a SIMD
-// waits on LDS fragment reads or the barrier, the other keeps its MFMAs issuing.
-constexpr int kWavesM = 2, kWavesN = 4;
-constexpr int kWaves = kWavesM * kWavesN;
+// 8 waves (two per SIMD): while one wave of a SIMD waits on LDS fragment
+// reads or a barrier, the other keeps its MFMAs issuing.
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
 // Operand fragment of one 16-row x 128-K MFMA tile.  The scaled MFMA reads
@@ -163,81 +162,65 @@ __device__ int find_group(const int32_t *off, int G, int64_t M_total, int tm, in
     return -1;
 }
 
-template <int BM, int BN, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, int NST>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-    constexpr int WTM = BM / kWavesM, WTN = BN / kWavesN;   // wave tile
-    constexpr int FM = WTM / 16, FN = WTN / 16;            // MFMA tiles per wave (rows, cols)
-    // LDS: NST stages of [A tile | B tile | A scales | B scales].  A scales
-    // (K % 128 == 0) are a dword per row per step; B scales are the packed
-    // layout's 64 bytes per 16-row atom per step, or (canonical B, K % 128
-    // == 0) a dword per row.  With K % 128 != 0, A (and canonical B) scale
-    // bytes come through registers instead (compiler-visible byte loads).
-    constexpr bool SA_LDS = KALIGN;
-    constexpr bool SB_LDS = BPACK || KALIGN;
-    constexpr int TILE = (BM + BN) * 128;
-    constexpr int SA_OFF = TILE;
-    constexpr int SB_OFF = SA_OFF + (SA_LDS ? BM * 4 : 0);
-    constexpr int STAGE = SB_OFF + (SB_LDS ? BN * 4 : 0);
-    static_assert(NST * STAGE <= 160 * 1024, "LDS budget");
-    static_assert(KALIGN || NST == 2, "register-fed scales are fetched one step ahead");
-    // copies per wave per step: tile segments plus one A- and one B-scale copy
-    constexpr int CPW = BM / (8 * kWaves) + BN / (8 * kWaves) + (SA_LDS ? 1 : 0) + (SB_LDS ? 1 : 0);
-    static_assert(CPW * (NST - 2) < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+// Per-tile state and the operations of one k-step, shared by both pipelines.
+template <int BM, int BN, int WM, bool BPACK, bool KALIGN>
+struct TileOps {
+    static constexpr int WN = kWaves / WM;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
+    static constexpr int FM = WTM / 16, FN = WTN / 16;      // MFMA tiles per wave
+    // LDS stage: [A tile | B tile | A scales | B scales].  A scales (K % 128
+    // == 0) are a dword per row per step; B scales are the packed layout's
+    // 64 bytes per 16-row atom per step, or (canonical B, K % 128 == 0) a
+    // dword per row.  With K % 128 != 0, A (and canonical B) scale bytes come
+    // through registers instead (compiler-visible byte loads).
+    static constexpr bool SA_LDS = KALIGN;
+    static constexpr bool SB_LDS = BPACK || KALIGN;
+    static constexpr int TILE = (BM + BN) * 128;
+    static constexpr int SA_OFF = TILE;
+    static constexpr int SB_OFF = SA_OFF + (SA_LDS ? BM * 4 : 0);
+    static constexpr int STAGE = SB_OFF + (SB_LDS ? BN * 4 : 0);
+    static_assert(FM >= 2 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "copy segments");
 
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int wm = w / kWavesN, wn = w % kWavesN;
+    v4i ra, rsa, rb, rsb;
+    __amdgpu_buffer_rsrc_t rsa_c, rsb_c;
+    int Ki, KBi, lane, w, wm, wn, lrow, lblk;
+    uint32_t lds0;
 
-    int tm, tn;
-    grouped_order(xcd_logical(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, tm, tn);
-    if (tm >= p.tiles_m || tn >= p.tiles_n) return;
-
-    const int64_t K = p.K, N = p.N;
-    const int64_t KB = K / 32;        // scale bytes per row
-    int64_t m0, m_end;
-    int64_t g = 0;
-    if constexpr (GROUPED) {
-        int64_t lo, hi;
-        int tig;
-        const int gg = find_group<BM>(p.offsets, p.G, p.M, tm, lane, lo, hi, tig);
-        if (gg < 0) return;
-        g = gg;
-        m0 = lo + (int64_t)tig * BM;
-        m_end = hi;
-    } else {
-        m0 = (int64_t)tm * BM;
-        m_end = p.M;
+    __device__ __forceinline__ void init(const GemmParams &p, int64_t m0, int64_t m_end, int64_t n0, int64_t g,
+                         const uint8_t *smem) {
+        const int64_t K = p.K, N = p.N, KB = K / 32;
+        lane = threadIdx.x & 63;
+        w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        wm = w / WN;
+        wn = w % WN;
+        lrow = lane & 15;
+        lblk = lane >> 4;
+        Ki = (int)K;
+        KBi = (int)KB;
+        lds0 = lds_addr(smem);
+        const int rows_a = (int)min((int64_t)BM, m_end - m0);
+        // each descriptor spans exactly this tile's bytes: out-of-range lanes read 0
+        ra = make_srd(p.a_q + m0 * K, (uint32_t)(rows_a * K));
+        rsa = make_srd(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
+        rsa_c = make_rsrc(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
+        if constexpr (BPACK) {
+            const int64_t panel = n0 / kPanelRows, prow = n0 % kPanelRows;
+            const uint8_t *bt = p.b_q + ((g * p.NP + panel) * p.KS) * kTileBytes + prow * 128;
+            rb = make_srd(bt, (uint32_t)((int64_t)p.KS * kTileBytes - prow * 128));
+            const uint8_t *bs = p.b_s + ((g * p.NP + panel) * p.KS) * kScaleStepBytes + (prow / 16) * 64;
+            rsb = make_srd(bs, (uint32_t)((int64_t)p.KS * kScaleStepBytes - (prow / 16) * 64));
+            rsb_c = make_rsrc(p.b_s, 0u);
+        } else {
+            const int rows_b = (int)min((int64_t)BN, N - n0);
+            rb = make_srd(p.b_q + n0 * K, (uint32_t)(rows_b * K));
+            rsb = make_srd(p.b_s + n0 * KB, (uint32_t)(rows_b * KB));
+            rsb_c = make_rsrc(p.b_s + n0 * KB, (uint32_t)(rows_b * KB));
+        }
     }
-    const int64_t n0 = (int64_t)tn * BN;
-    const int rows_a = (int)min((int64_t)BM, m_end - m0);
 
-    // ---- operand descriptors (SGPRs, for the inline-asm copies): each one
-    //      spans exactly the bytes of this tile, so out-of-range lanes read 0
-    const v4i ra = make_srd(p.a_q + m0 * K, (uint32_t)(rows_a * K));
-    const v4i rsa = make_srd(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
-    v4i rb, rsb;
-    if constexpr (BPACK) {
-        const int64_t panel = n0 / kPanelRows, prow = n0 % kPanelRows;
-        const uint8_t *bt = p.b_q + ((g * p.NP + panel) * p.KS) * kTileBytes + prow * 128;
-        rb = make_srd(bt, (uint32_t)((int64_t)p.KS * kTileBytes - prow * 128));
-        const uint8_t *bs = p.b_s + ((g * p.NP + panel) * p.KS) * kScaleStepBytes + (prow / 16) * 64;
-        rsb = make_srd(bs, (uint32_t)((int64_t)p.KS * kScaleStepBytes - (prow / 16) * 64));
-    } else {
-        const int rows_b = (int)min((int64_t)BN, N - n0);
-        rb = make_srd(p.b_q + n0 * K, (uint32_t)(rows_b * K));
-        rsb = make_srd(p.b_s + n0 * KB, (uint32_t)(rows_b * KB));
-    }
-    // the same ranges as compiler-visible resources, for the byte-granular
-    // scale loads of the K % 128 != 0 path
-    const __amdgpu_buffer_rsrc_t rsa_c = make_rsrc(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
-    const __amdgpu_buffer_rsrc_t rsb_c =
-        make_rsrc(p.b_s + (BPACK ? 0 : n0 * KB), BPACK ? 0u : (uint32_t)(min((int64_t)BN, N - n0) * KB));
-    const int Ki = (int)K, KBi = (int)KB;
-    const uint32_t lds0 = lds_addr(smem);
-
-    // ---- global -> LDS copies of k-step ks into stage st: CPW per wave
-    auto issue = [&](int ks, int st) {
+    // global -> LDS copies of k-step ks into stage st (this wave's share)
+    __device__ __forceinline__ void issue(int ks, int st) const {
         const uint32_t sbase = lds0 + st * STAGE;
 #pragma unroll
         for (int i = 0; i < BM / (8 * kWaves); ++i) {
@@ -262,33 +245,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             }
             dma16(rb, off, sbase + BM * 128 + seg * 1024);
         }
-        // scale copies: 256 B segments.  With more than two stages every wave
-        // issues one of each (a wave beyond the segment count repeats one:
-        // identical bytes to the same place) so the per-wave count CPW, and
-        // with it the loop's vmcnt immediate, is uniform; with two stages
-        // (vmcnt(0)) only the waves with a segment of their own copy.
+        // scale copies: 256 B segments, one per wave that owns one
         if constexpr (SA_LDS) {
-            if (NST > 2 || w < BM / 64) {
-                const int seg = w % (BM / 64);
-                const int rr = seg * 64 + lane;
-                dma4(rsa, (uint32_t)(rr * KBi + ks * 4), sbase + SA_OFF + seg * 256);
+            if (w < BM / 64) {
+                const int rr = w * 64 + lane;
+                dma4(rsa, (uint32_t)(rr * KBi + ks * 4), sbase + SA_OFF + w * 256);
             }
         }
         if constexpr (SB_LDS) {
-            if (NST > 2 || w < BN / 64) {
-                const int seg = w % (BN / 64);
+            if (w < BN / 64) {
                 uint32_t off;
-                if constexpr (BPACK) off = (uint32_t)(ks * kScaleStepBytes + seg * 256 + lane * 4);
-                else off = (uint32_t)((seg * 64 + lane) * KBi + ks * 4);
-                dma4(rsb, off, sbase + SB_OFF + seg * 256);
+                if constexpr (BPACK) off = (uint32_t)(ks * kScaleStepBytes + w * 256 + lane * 4);
+                else off = (uint32_t)((w * 64 + lane) * KBi + ks * 4);
+                dma4(rsb, off, sbase + SB_OFF + w * 256);
             }
         }
-    };
+    }
 
-    // ---- K % 128 != 0: A (and canonical B) scale bytes by compiler-visible
-    //      loads, one step ahead (the K tail's blocks read as 0)
-    const int lrow = lane & 15, lblk = lane >> 4;
-    auto fetch_sa = [&](int ks, uint32_t *dst) {
+    // K % 128 != 0: scale bytes by compiler-visible loads (K tail reads 0)
+    __device__ __forceinline__ void fetch_sa(int ks, uint32_t *dst) const {
         const int blk = ks * 4 + lblk;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -296,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             const uint32_t off = blk < KBi ? (uint32_t)(rr * KBi + blk) : kOOB;
             dst[i] = __builtin_amdgcn_raw_buffer_load_b8(rsa_c, off, 0, 0);
         }
-    };
-    auto fetch_sb = [&](int ks, uint32_t *dst) {
+    }
+    __device__ __forceinline__ void fetch_sb(int ks, uint32_t *dst) const {
         const int blk = ks * 4 + lblk;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -305,71 +280,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             const uint32_t off = blk < KBi ? (uint32_t)(rr * KBi + blk) : kOOB;
             dst[j] = __builtin_amdgcn_raw_buffer_load_b8(rsb_c, off, 0, 0);
         }
-    };
+    }
 
-    v4f acc[FM][FN];
+    // scale bytes of one step from LDS (the MFMA reads bits [7:0], op_sel 0)
+    __device__ __forceinline__ void lds_scales(const uint8_t *st, int *sas, int *sbs) const {
+        if constexpr (SA_LDS) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    uint32_t sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
-    const int KS = p.KS;
-    if constexpr (!SA_LDS) fetch_sa(0, sa_nxt);
-    if constexpr (!SB_LDS) fetch_sb(0, sb_nxt);
-#pragma unroll
-    for (int s0 = 0; s0 < NST - 1; ++s0)
-        if (s0 < KS) issue(s0, s0);
-
-    for (int ks = 0; ks < KS; ++ks) {
-        const int cur = ks % NST;
-        // this step's copies have landed (this wave's: vmcnt, letting the
-        // copies of later steps stay in flight; everyone's: the barrier), and
-        // every wave is done reading the stage the next issue overwrites
-        if constexpr (NST >= 3) {
-            if (ks + NST - 2 < KS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(CPW * (NST - 2)));
-            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        } else {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            for (int i = 0; i < FM; ++i) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
         }
-        __syncthreads();
-        if constexpr (!SA_LDS || !SB_LDS) {
-            if constexpr (!SA_LDS) {
+        if constexpr (SB_LDS) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
-            }
-            if constexpr (!SB_LDS) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
-            }
-            if (ks + 1 < KS) {
-                if constexpr (!SA_LDS) fetch_sa(ks + 1, sa_nxt);
-                if constexpr (!SB_LDS) fetch_sb(ks + 1, sb_nxt);
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (BPACK) sbs[j] = st[SB_OFF + (wn * FN + j) * 64 + lane];
+                else sbs[j] = st[SB_OFF + (wn * WTN + j * 16 + lrow) * 4 + lblk];
             }
         }
-        if (ks + NST - 1 < KS) issue(ks + NST - 1, (ks + NST - 1) % NST);
+    }
 
-        const uint8_t *st = smem + cur * STAGE;
-        const uint8_t *sa = st + wm * WTM * 128;
+    __device__ __forceinline__ void lds_bfrags(const uint8_t *st, v8i *bf) const {
         const uint8_t *sb = st + BM * 128 + wn * WTN * 128;
-        int sas[FM], sbs[FN];
-        // the MFMA reads bits [7:0] of each scale register (op_sel 0)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            if constexpr (SA_LDS) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
-            else sas[i] = (int)(sa_cur[i] & 0xFFu);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            if constexpr (BPACK) sbs[j] = st[SB_OFF + (wn * FN + j) * 64 + lane];
-            else if constexpr (SB_LDS) sbs[j] = st[SB_OFF + (wn * WTN + j * 16 + lrow) * 4 + lblk];
-            else sbs[j] = (int)(sb_cur[j] & 0xFFu);
-        }
-        v8i bf[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sb + j * 16 * 128, lane);
+    }
+
+    // MFMAs of A rows [i0, i1) of one step against the B fragments in registers
+    __device__ __forceinline__ void mma_rows(const uint8_t *st, int i0, int i1, const v8i *bf, const int *sas,
+                             const int *sbs, v4f (*acc)[FN]) const {
+        const uint8_t *sa = st + wm * WTM * 128;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int i = i0; i < i1; ++i) {
             const v8i af = lds_frag(sa + i * 16 * 128, lane);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
@@ -377,16 +316,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                     af, bf[j], acc[i][j], 0, 0, 0, sas[i], 0, sbs[j]);
         }
     }
+};
 
-    // ---- epilogue: lane holds C[4*(lane/16) + r][lane % 16] of each 16x16 tile
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+__device__ __forceinline__ void wait_copies_and_sync() {
+    // every copy this wave issued has landed (vmcnt; a builtin, so the
+    // compiler knows it too), then every wave's (barrier)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+}
+
+// Tile coordinates of this workgroup; false if it has no tile.
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ bool tile_of(const GemmParams &p, int64_t &m0, int64_t &m_end, int64_t &n0, int64_t &g) {
+    int tm, tn;
+    grouped_order(xcd_logical(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, tm, tn);
+    if (tm >= p.tiles_m || tn >= p.tiles_n) return false;
+    g = 0;
+    if constexpr (GROUPED) {
+        int64_t lo, hi;
+        int tig;
+        const int gg = find_group<BM>(p.offsets, p.G, p.M, tm, threadIdx.x & 63, lo, hi, tig);
+        if (gg < 0) return false;
+        g = gg;
+        m0 = lo + (int64_t)tig * BM;
+        m_end = hi;
+    } else {
+        m0 = (int64_t)tm * BM;
+        m_end = p.M;
+    }
+    n0 = (int64_t)tn * BN;
+    return true;
+}
+
+// C store, element by element: lane holds C[4*(lane/16) + r][lane % 16] of
+// each 16x16 tile (used for blocks that cross the matrix edge).
+template <int FM, int FN, bool OUT_BF16>
+__device__ __forceinline__ void store_tile_scalar(const GemmParams &p, int64_t row0, int64_t col0, int64_t m_end,
+                                  v4f (*acc)[FN], int lane) {
+    const int64_t N = p.N;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t col = n0 + wn * WTN + j * 16 + (lane & 15);
+            const int64_t col = col0 + j * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm * WTM + i * 16 + (lane >> 4) * 4 + r;
+                const int64_t row = row0 + i * 16 + (lane >> 4) * 4 + r;
                 if (row < m_end && col < N) {
                     if constexpr (OUT_BF16)
                         static_cast<uint16_t *>(p.c)[row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
@@ -398,29 +378,138 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-// Pipeline depth.  Two stages measured fastest on MI355X for every tile shape
-// here (a third stage keeps more copies in flight but did not shorten the
-// qkv GEMM); the NST > 2 path is kept for tuning.
-template <int BM, int BN>
-constexpr int stages_for() { return 2; }
-
-template <int BM, int BN, bool GROUPED, bool KALIGN, int NST>
-static hipError_t launch_cfg2(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
-    dim3 grid((unsigned)nwg), block(kThreads);
-    if (b_packed) {
-        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, true, true, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, true, false, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
-    } else {
-        if (c_bf16) hipLaunchKernelGGL((gemm_kernel<BM, BN, false, true, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((gemm_kernel<BM, BN, false, false, GROUPED, KALIGN, NST>), grid, block, 0, s, p);
+// C store through LDS: each wave writes its block into its own LDS region in
+// row-major order (rows padded by 16 B against bank conflicts), then reads it
+// back 16 bytes per lane so every global store is a whole 16-byte piece of a
+// contiguous row segment.  Rows go in passes of PR so the regions of all
+// waves fit the LDS the main loop used.  Callers sync before (the stages are
+// reused) and use this only for blocks fully inside C with 16-byte aligned
+// rows.
+template <int FM, int FN, bool OUT_BF16, int LDS_BYTES>
+__device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0, int64_t col0, v4f (*acc)[FN],
+                               int lane, int w, uint8_t *smem) {
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    constexpr int WTM = FM * 16, WTN = FN * 16;
+    constexpr int ROWB = WTN * ES + 16;                       // padded LDS row
+    constexpr int PR0 = LDS_BYTES / (kWaves * ROWB);          // rows per pass that fit
+    constexpr int PR = PR0 >= WTM ? WTM : (PR0 >= 64 ? 64 : (PR0 >= 32 ? 32 : 16));
+    static_assert(PR >= 16 && WTM % PR == 0 && kWaves * PR * ROWB <= LDS_BYTES, "epilogue LDS");
+    constexpr int LPR = WTN * ES / 16;                         // lanes per row (16 B each)
+    constexpr int RPI = 64 / LPR;                              // rows per store instruction
+    uint8_t *cw = smem + w * PR * ROWB;
+    const int64_t N = p.N;
+#pragma unroll
+    for (int pass = 0; pass < WTM / PR; ++pass) {
+        // scatter this pass's rows (16-row MFMA tiles i in [pass*PR/16, ...))
+#pragma unroll
+        for (int i = pass * (PR / 16); i < (pass + 1) * (PR / 16); ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rl = (i - pass * (PR / 16)) * 16 + (lane >> 4) * 4 + r;
+                    const int cl = j * 16 + (lane & 15);
+                    if constexpr (OUT_BF16)
+                        *reinterpret_cast<uint16_t *>(cw + rl * ROWB + cl * 2) =
+                            (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+                    else
+                        *reinterpret_cast<float *>(cw + rl * ROWB + cl * 4) = acc[i][j][r];
+                }
+            }
+        }
+        // gather 16 B per lane and store whole row segments
+#pragma unroll
+        for (int r0 = 0; r0 < PR; r0 += RPI) {
+            const int rl = r0 + lane / LPR;
+            const int cb = (lane % LPR) * 16;
+            const v4i v = *reinterpret_cast<const v4i *>(cw + rl * ROWB + cb);
+            uint8_t *dst = static_cast<uint8_t *>(p.c) + ((row0 + pass * PR + rl) * N + col0) * ES + cb;
+            *reinterpret_cast<v4i *>(dst) = v;
+        }
     }
-    return hipGetLastError();
 }
 
-template <int BM, int BN, bool GROUPED>
-static hipError_t launch_cfg(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
-    if (p.K % 128 == 0) return launch_cfg2<BM, BN, GROUPED, true, stages_for<BM, BN>()>(p, b_packed, c_bf16, nwg, s);
-    return launch_cfg2<BM, BN, GROUPED, false, 2>(p, b_packed, c_bf16, nwg, s);
+// ---------------------------------------------------------------- 2 stages
+// One barrier at the top of each step; copies of step k+1 overlap step k.
+template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+    using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
+    constexpr int FM = T::FM, FN = T::FN;
+    static_assert(2 * T::STAGE <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
+    int64_t m0, m_end, n0, g;
+    if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
+    T t;
+    t.init(p, m0, m_end, n0, g, smem);
+
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
+    const int KS = p.KS;
+    if constexpr (!T::SA_LDS) t.fetch_sa(0, sa_nxt);
+    if constexpr (!T::SB_LDS) t.fetch_sb(0, sb_nxt);
+    t.issue(0, 0);
+
+    for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;
+        wait_copies_and_sync();
+        if constexpr (!T::SA_LDS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
+            if (ks + 1 < KS) t.fetch_sa(ks + 1, sa_nxt);
+        }
+        if constexpr (!T::SB_LDS) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
+            if (ks + 1 < KS) t.fetch_sb(ks + 1, sb_nxt);
+        }
+        if (ks + 1 < KS) t.issue(ks + 1, cur ^ 1);
+
+        const uint8_t *st = smem + cur * T::STAGE;
+        int sas[FM], sbs[FN];
+        t.lds_scales(st, sas, sbs);
+        if constexpr (!T::SA_LDS) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sas[i] = (int)(sa_cur[i] & 0xFFu);
+        }
+        if constexpr (!T::SB_LDS) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sbs[j] = (int)(sb_cur[j] & 0xFFu);
+        }
+        v8i bf[FN];
+        t.lds_bfrags(st, bf);
+        t.mma_rows(st, 0, FM, bf, sas, sbs, acc);
+    }
+    const int64_t row0 = m0 + t.wm * T::WTM, col0 = n0 + t.wn * T::WTN;
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    // uniform over the workgroup: every wave's block inside C, rows 16 B aligned
+    const bool inside = m0 + BM <= m_end && n0 + BN <= p.N && (p.N * ES) % 16 == 0;
+    if (inside) {
+        __syncthreads();                    // every wave is done with the stages
+        store_tile_lds<FM, FN, OUT_BF16, 2 * T::STAGE>(p, row0, col0, acc, t.lane, t.w, smem);
+    } else {
+        store_tile_scalar<FM, FN, OUT_BF16>(p, row0, col0, m_end, acc, t.lane);
+    }
+}
+
+template <int BM, int BN, int WM, bool GROUPED>
+static hipError_t launch_tile(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
+    dim3 grid((unsigned)nwg), block(kThreads);
+    const bool kal = p.K % 128 == 0;
+#define MX_LAUNCH2(BP, BF, KA) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, GROUPED, KA>), grid, block, 0, s, p)
+    if (kal) {
+        if (b_packed) { if (c_bf16) MX_LAUNCH2(true, true, true); else MX_LAUNCH2(true, false, true); }
+        else { if (c_bf16) MX_LAUNCH2(false, true, true); else MX_LAUNCH2(false, false, true); }
+    } else {
+        if (b_packed) { if (c_bf16) MX_LAUNCH2(true, true, false); else MX_LAUNCH2(true, false, false); }
+        else { if (c_bf16) MX_LAUNCH2(false, true, false); else MX_LAUNCH2(false, false, false); }
+    }
+#undef MX_LAUNCH2
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
@@ -434,19 +523,19 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     p.G = 1;
     p.offsets = nullptr;
     const int cus = device_cu_count();
-    // 256x256 tiles unless that leaves the last wave of tiles badly filled,
-    // then 256x128 (twice the tiles, and a three-stage pipeline).
+    // 256x256 tiles (2 waves x 4, 128x64 per wave) unless that leaves the last
+    // wave of tiles badly filled; then 256x128 (4 x 2 waves, 64x64 each).
     const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t waves256 = ceil_div(t256, cus);
     const double fill256 = (double)t256 / (double)(waves256 * cus);
     if (fill256 >= 0.85 || N <= 128) {
         p.tiles_m = (int)ceil_div(M, 256);
         p.tiles_n = (int)ceil_div(N, 256);
-        return launch_cfg<256, 256, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
+        return launch_tile<256, 256, 2, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
     }
     p.tiles_m = (int)ceil_div(M, 256);
     p.tiles_n = (int)ceil_div(N, 128);
-    return launch_cfg<256, 128, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
+    return launch_tile<256, 128, 4, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
@@ -463,7 +552,7 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uin
     constexpr int BM = 128, BN = 256;
     p.tiles_m = (int)(ceil_div(M_total, BM) + G);
     p.tiles_n = (int)ceil_div(N, BN);
-    return launch_cfg<BM, BN, true>(p, true, c_bf16, p.tiles_m * p.tiles_n, stream);
+    return launch_tile<BM, BN, 2, true>(p, true, c_bf16, p.tiles_m * p.tiles_n, stream);
 }
 
 }  // namespace mx
