@@ -165,6 +165,343 @@ def bench_qkv(args, dev):
     return out
 
 
+def run_timed(ops, args):
+    """Run `ops` (a list of (name, fn)) as one step: W warmup steps, then K
+    timed steps bracketed by synchronizations; every op is bracketed by HIP
+    events.  Returns (ms per step from the host clock, {name: avg us})."""
+    import torch
+    timer = KernelTimer()
+    for _ in range(args.warmup):
+        for name, fn in ops:
+            timer.time(name, fn)
+    torch.cuda.synchronize()
+    timer.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for name, fn in ops:
+            timer.time(name, fn)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return 1e3 * wall / args.steps, timer.averages_us()
+
+
+def _line(metric, value, unit, args, ms, dtype, config, **extra):
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic (seeded; recipe in workloads/)", "config": config}
+    out.update(extra)
+    return out
+
+
+def _gemm_rate(us, M, N, K):
+    tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    return {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4)}
+
+
+def bench_mlp(args, dev):
+    """Qwen3-8B MLP learner micro-batch (8192 tokens): per step, quantize the
+    two weights along both axes and repack all four operands, quantize the four
+    activation/gradient tensors along both axes, and run the six GEMMs
+    (fprop, dgrad, wgrad for gate_up and down).  fprop/dgrad -> bf16, wgrad ->
+    fp32.  The working set (> 2.5 GB) is far larger than the Infinity Cache."""
+    import torch
+    import mxfp8_block_scaled_05_amd as mx
+    import workloads as wl
+
+    T = 8192
+    d = wl.mlp(0, tokens=T)
+    H, I2 = d["W_gu"].shape[1], d["W_gu"].shape[0]
+    I = d["W_d"].shape[1]
+    t = {k: _bf16_dev(v, dev) for k, v in d.items()}
+    del d
+
+    def qbuf(rows, cols, axis):
+        r, c = (rows, cols) if axis == 1 else (cols, rows)
+        return (torch.empty((r, c), dtype=torch.uint8, device=dev),
+                torch.empty((r, c // 32), dtype=torch.uint8, device=dev))
+
+    def pbuf(n, k):
+        return mx.PackedWeight(torch.empty(mx.packed_bytes(1, n, k, 0), dtype=torch.uint8, device=dev),
+                               torch.empty(mx.packed_bytes(1, n, k, 1), dtype=torch.uint8, device=dev),
+                               1, n, k)
+
+    Q = {}
+    for name, axes in (("W_gu", (1, 0)), ("W_d", (1, 0)), ("X", (1, 0)), ("h", (1, 0)),
+                       ("dY_gu", (1, 0)), ("dY_d", (1, 0))):
+        for ax in axes:
+            Q[name, ax] = qbuf(*t[name].shape, ax)
+    P = {"gu": pbuf(I2, H), "guT": pbuf(H, I2), "d": pbuf(H, I), "dT": pbuf(I, H)}
+    out = {"fprop_gu": torch.empty((T, I2), dtype=torch.bfloat16, device=dev),
+           "fprop_d": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+           "dgrad_d": torch.empty((T, I), dtype=torch.bfloat16, device=dev),
+           "dgrad_gu": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+           "wgrad_d": torch.empty((H, I), dtype=torch.float32, device=dev),
+           "wgrad_gu": torch.empty((I2, H), dtype=torch.float32, device=dev)}
+    ops = []
+    q_elts = {}
+    for (name, ax), (q, sc) in Q.items():
+        key = "quantize_%s_axis%d" % (name, ax)
+        ops.append((key, lambda x=t[name], a=ax, q=q, sc=sc: mx.quantize_into(x, a, q, sc)))
+        q_elts[key] = t[name].numel()
+    for key, src in (("repack_gu", ("W_gu", 1)), ("repack_guT", ("W_gu", 0)),
+                     ("repack_d", ("W_d", 1)), ("repack_dT", ("W_d", 0))):
+        pk = P[key.split("_", 1)[1]]
+        ops.append((key, lambda q=Q[src][0], sc=Q[src][1], w=pk: mx.repack_(q, sc, w)))
+    gemms = {  # name: (A, B, M, N, K, out dtype)
+        "fprop_gu": (Q["X", 1], P["gu"], T, I2, H, torch.bfloat16),
+        "fprop_d": (Q["h", 1], P["d"], T, H, I, torch.bfloat16),
+        "dgrad_d": (Q["dY_d", 1], P["dT"], T, I, H, torch.bfloat16),
+        "dgrad_gu": (Q["dY_gu", 1], P["guT"], T, H, I2, torch.bfloat16),
+        "wgrad_d": (Q["dY_d", 0], Q["h", 0], H, I, T, torch.float32),
+        "wgrad_gu": (Q["dY_gu", 0], Q["X", 0], I2, H, T, torch.float32),
+    }
+    for key, (A, B, M, N, K, dt) in gemms.items():
+        ops.append(("gemm_" + key, lambda A=A, B=B, dt=dt, o=out[key]: mx.gemm(A[0], A[1], B, dt, out=o)))
+    torch.cuda.synchronize()
+    ms, avg = run_timed(ops, args)
+    flops = sum(2.0 * M * N * K for (_, _, M, N, K, _) in gemms.values())
+    kern = {}
+    for key, n in q_elts.items():
+        kern[key] = _bw(avg[key], n * Q_BYTES_PER_ELT)
+    for key, src in (("repack_gu", (I2, H)), ("repack_guT", (H, I2)), ("repack_d", (H, I)), ("repack_dT", (I, H))):
+        kern[key] = _bw(avg[key], src[0] * src[1] * REPACK_BYTES_PER_ELT)
+    for key, (_, _, M, N, K, _) in gemms.items():
+        kern["gemm_" + key] = _gemm_rate(avg["gemm_" + key], M, N, K)
+    gemm_us = sum(avg["gemm_" + k] for k in gemms)
+    quant_us = sum(avg[k] for k in q_elts)
+    top = kern["gemm_fprop_gu"]
+    return _line("MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",
+                 round(flops / (ms * 1e-3) / 1e12, 2), "TFLOP/s", args, ms,
+                 "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out (fprop/dgrad), fp32 out (wgrad)",
+                 {"workload": "qwen3-8b MLP learner micro-batch, 8192 tokens: weight quantize (2 axes) "
+                              "+ repack, activation/gradient quantize (2 axes), 6 GEMMs",
+                  "tokens": T, "hidden": H, "inter": I},
+                 kernels=kern,
+                 summary={"gemm_us": round(gemm_us, 1),
+                          "gemm_TFLOP/s": round(flops / (gemm_us * 1e-6) / 1e12, 1),
+                          "quantize_us": round(quant_us, 1),
+                          "quantize_GB/s": round(sum(q_elts.values()) * Q_BYTES_PER_ELT / (quant_us * 1e-6) / 1e9, 1)},
+                 roofline={"bound": "mfma", "achieved": top["TFLOP/s"], "peak": MXFP8_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": top["frac_mxfp8_peak"], "traffic": None,
+                           "kernel": "gemm fprop gate_up 8192x24576x4096"})
+
+
+def bench_moe(args, dev):
+    """Qwen3-30B-A3B MoE layer forward (8192 tokens, 128 experts, Zipf(1.1)
+    top-8, groups padded to 32): quantize the gathered gate_up input, grouped
+    GEMM gate_up -> bf16, quantize the down input, grouped GEMM down -> bf16.
+    Expert weights are quantized and repacked beforehand (weight sync, timed
+    separately); offsets stay on the device."""
+    import torch
+    import mxfp8_block_scaled_05_amd as mx
+    import workloads as wl
+
+    d = wl.moe(0)
+    G, I2, H = d["W_gu"].shape
+    I = d["W_d"].shape[2]
+    Mt = int(d["offsets"][-1])
+    real = int(d["counts"].sum())
+    W_gu = _bf16_dev(d["W_gu"].reshape(G * I2, H), dev)
+    W_d = _bf16_dev(d["W_d"].reshape(G * H, I), dev)
+    A_gu = _bf16_dev(d["A_gu"], dev)
+    A_d = _bf16_dev(d["A_d"], dev)
+    offs = torch.from_numpy(d["offsets"]).to(dev)
+    del d
+    wgu_q = torch.empty((G * I2, H), dtype=torch.uint8, device=dev)
+    wgu_s = torch.empty((G * I2, H // 32), dtype=torch.uint8, device=dev)
+    wd_q = torch.empty((G * H, I), dtype=torch.uint8, device=dev)
+    wd_s = torch.empty((G * H, I // 32), dtype=torch.uint8, device=dev)
+    P_gu = mx.PackedWeight(torch.empty(mx.packed_bytes(G, I2, H, 0), dtype=torch.uint8, device=dev),
+                           torch.empty(mx.packed_bytes(G, I2, H, 1), dtype=torch.uint8, device=dev), G, I2, H)
+    P_d = mx.PackedWeight(torch.empty(mx.packed_bytes(G, H, I, 0), dtype=torch.uint8, device=dev),
+                          torch.empty(mx.packed_bytes(G, H, I, 1), dtype=torch.uint8, device=dev), G, H, I)
+    agu_q = torch.empty((Mt, H), dtype=torch.uint8, device=dev)
+    agu_s = torch.empty((Mt, H // 32), dtype=torch.uint8, device=dev)
+    ad_q = torch.empty((Mt, I), dtype=torch.uint8, device=dev)
+    ad_s = torch.empty((Mt, I // 32), dtype=torch.uint8, device=dev)
+    y_gu = torch.empty((Mt, I2), dtype=torch.bfloat16, device=dev)
+    y_d = torch.empty((Mt, H), dtype=torch.bfloat16, device=dev)
+    sync_ops = [
+        ("sync_quantize_W_gu", lambda: mx.quantize_into(W_gu, 1, wgu_q, wgu_s)),
+        ("sync_repack_W_gu", lambda: mx.repack_(wgu_q.view(G, I2, H), wgu_s.view(G, I2, H // 32), P_gu)),
+        ("sync_quantize_W_d", lambda: mx.quantize_into(W_d, 1, wd_q, wd_s)),
+        ("sync_repack_W_d", lambda: mx.repack_(wd_q.view(G, H, I), wd_s.view(G, H, I // 32), P_d)),
+    ]
+    ops = [
+        ("quantize_A_gu", lambda: mx.quantize_into(A_gu, 1, agu_q, agu_s)),
+        ("grouped_gemm_gate_up", lambda: mx.grouped_gemm(agu_q, agu_s, P_gu, offs, torch.bfloat16, out=y_gu)),
+        ("quantize_A_d", lambda: mx.quantize_into(A_d, 1, ad_q, ad_s)),
+        ("grouped_gemm_down", lambda: mx.grouped_gemm(ad_q, ad_s, P_d, offs, torch.bfloat16, out=y_d)),
+    ]
+    torch.cuda.synchronize()
+    sync_ms, sync_avg = run_timed(sync_ops, argparse.Namespace(steps=max(3, args.steps // 10), warmup=1))
+    ms, avg = run_timed(ops, args)
+    flops_gu = 2.0 * real * I2 * H
+    flops_d = 2.0 * real * H * I
+    eb = 1 + 1 / 32
+    bytes_gu = G * I2 * H * eb + Mt * H * eb + Mt * I2 * 2
+    bytes_d = G * H * I * eb + Mt * I * eb + Mt * H * 2
+    kern = {"quantize_A_gu": _bw(avg["quantize_A_gu"], Mt * H * Q_BYTES_PER_ELT),
+            "quantize_A_d": _bw(avg["quantize_A_d"], Mt * I * Q_BYTES_PER_ELT)}
+    for key, fl, by in (("grouped_gemm_gate_up", flops_gu, bytes_gu), ("grouped_gemm_down", flops_d, bytes_d)):
+        us = avg[key]
+        tf = fl / (us * 1e-6) / 1e12
+        gbs = by / (us * 1e-6) / 1e9
+        kern[key] = {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4),
+                     "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "roofline_us": round(max(fl / MXFP8_PEAK_TFLOPS / 1e12, by / HBM_PEAK_GBS / 1e9) * 1e6, 1)}
+    for key in ("sync_quantize_W_gu", "sync_quantize_W_d"):
+        n = G * I2 * H if key.endswith("gu") else G * H * I
+        kern[key] = _bw(sync_avg[key], n * Q_BYTES_PER_ELT)
+    for key in ("sync_repack_W_gu", "sync_repack_W_d"):
+        n = G * I2 * H if key.endswith("gu") else G * H * I
+        kern[key] = _bw(sync_avg[key], n * REPACK_BYTES_PER_ELT)
+    top = kern["grouped_gemm_gate_up"]
+    return _line("MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",
+                 round((flops_gu + flops_d) / (ms * 1e-3) / 1e12, 2), "TFLOP/s", args, ms,
+                 "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out",
+                 {"workload": "qwen3-30b-a3b MoE layer forward, 8192 tokens, 128 experts, Zipf(1.1) top-8, "
+                              "groups padded to 32: quantize + grouped GEMM gate_up, quantize + grouped GEMM down",
+                  "tokens": 8192, "experts": G, "rows_real": real, "rows_padded": Mt},
+                 kernels=kern, flops_basis="unpadded rows (padded FLOPs are %.1f%% more)" % (100.0 * (Mt / real - 1)),
+                 roofline={"bound": "mfma", "achieved": top["TFLOP/s"], "peak": MXFP8_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": top["frac_mxfp8_peak"], "traffic": None,
+                           "kernel": "grouped gemm gate_up", "hbm_frac": top["frac_hbm_peak"]})
+
+
+def bench_sync(args, dev):
+    """Shared-grid weight sync of Qwen3-8B: quantize along K and repack all 144
+    linear weights (36 layers x qkv, o, gate_up, down; 6.95e9 elements).  BF16
+    weights are drawn on the device (seeded Philox); one step = the whole sync."""
+    import torch
+    import mxfp8_block_scaled_05_amd as mx
+    import workloads as wl
+
+    layers = wl.QWEN3_8B["layers"]
+    tensors = []
+    for L in range(layers):
+        for j, (name, N, K) in enumerate(wl.sync_layer_shapes()):
+            W = wl.torch_normal_bf16((N, K), 0.02, seed=1000 + 4 * L + j, device=dev)
+            q = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            sc = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+            pk = mx.PackedWeight(torch.empty(mx.packed_bytes(1, N, K, 0), dtype=torch.uint8, device=dev),
+                                 torch.empty(mx.packed_bytes(1, N, K, 1), dtype=torch.uint8, device=dev), 1, N, K)
+            tensors.append((name, W, q, sc, pk))
+    n_elts = sum(W.numel() for _, W, _, _, _ in tensors)
+    ops = []
+    for name, W, q, sc, pk in tensors:
+        ops.append(("quantize_" + name, lambda W=W, q=q, sc=sc: mx.quantize_into(W, 1, q, sc)))
+        ops.append(("repack_" + name, lambda q=q, sc=sc, pk=pk: mx.repack_(q, sc, pk)))
+    torch.cuda.synchronize()
+    ms, avg = run_timed(ops, args)
+    by_q = n_elts * Q_BYTES_PER_ELT
+    by_r = n_elts * REPACK_BYTES_PER_ELT
+    kern = {}
+    for name, N, K in wl.sync_layer_shapes():
+        kern["quantize_" + name] = _bw(avg["quantize_" + name], N * K * Q_BYTES_PER_ELT)
+        kern["repack_" + name] = _bw(avg["repack_" + name], N * K * REPACK_BYTES_PER_ELT)
+    gbs = (by_q + by_r) / (ms * 1e-3) / 1e9
+    return _line("weight sync GB/s (% HBM): quantize + repack of all Qwen3-8B linears",
+                 round(gbs, 1), "GB/s", args, ms, "bf16 -> mxfp8-e4m3/e8m0",
+                 {"workload": "qwen3-8b weight sync: quantize along K + repack of 144 linears "
+                              "(36 layers x qkv, o, gate_up, down)", "elements": n_elts},
+                 kernels=kern,
+                 summary={"quantize_GB": round(by_q / 1e9, 2), "repack_GB": round(by_r / 1e9, 2),
+                          "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
+                 roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "whole sync (quantize + repack)"})
+
+
+def bench_sweep(args, dev):
+    """One Qwen3-8B decoder layer's four linears at M tokens, MXFP8 (quantize
+    the input along K + GEMM against packed weights, bf16 out) against BF16
+    (torch.nn.functional.linear -> hipBLASLt).  Fits t = F + c*M per arm, for
+    GPU time (events around the four linears) and for host wall time per layer
+    call, and reports the break-even M* = dF / dc if it lies in range."""
+    import torch
+    import torch.nn.functional as F_
+    import mxfp8_block_scaled_05_amd as mx
+    import workloads as wl
+
+    Ms = [512, 1024, 2048, 3072, 4096, 6144, 8192, 12288, 16384]
+    shapes = wl.sync_layer_shapes()
+    Wb, P = [], []
+    for j, (name, N, K) in enumerate(shapes):
+        W = wl.torch_normal_bf16((N, K), 0.02, seed=2000 + j, device=dev)
+        w = mx.repack(*mx.quantize(W, 1))
+        Wb.append(W)
+        P.append(w)
+    Xall = {K: wl.torch_normal_bf16((max(Ms), K), 1.0, seed=3000 + K, device=dev) for _, _, K in shapes}
+    rows = []
+    for M in Ms:
+        xs = [Xall[K][:M] for _, _, K in shapes]
+        qs = [(torch.empty((M, K), dtype=torch.uint8, device=dev),
+               torch.empty((M, K // 32), dtype=torch.uint8, device=dev)) for _, _, K in shapes]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N, _ in shapes]
+
+        def mx_layer():
+            for x, (q, sc), w, y in zip(xs, qs, P, ys):
+                mx.quantize_into(x, 1, q, sc)
+                mx.gemm(q, sc, w, torch.bfloat16, out=y)
+
+        def bf_layer():
+            for x, W, y in zip(xs, Wb, ys):
+                torch.mm(x, W.t(), out=y)
+
+        res = {"M": M}
+        for arm, fn in (("mxfp8", mx_layer), ("bf16", bf_layer)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            n = 20
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[arm + "_gpu_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+            # host wall time per layer call, no synchronization inside
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            host = time.perf_counter() - t0
+            torch.cuda.synchronize()
+            res[arm + "_host_us"] = round(host * 1e6 / n, 2)
+        rows.append(res)
+
+    def fit(key):
+        m = np.array([r["M"] for r in rows], np.float64)
+        t = np.array([r[key] for r in rows], np.float64)
+        c, f = np.polyfit(m, t, 1)
+        return f, c
+
+    fits = {}
+    for kind in ("gpu", "host"):
+        fm, cm = fit("mxfp8_%s_us" % kind)
+        fb, cb = fit("bf16_%s_us" % kind)
+        cross = None
+        if cb != cm:
+            x = (fm - fb) / (cb - cm)
+            cross = round(x, 0) if Ms[0] <= x <= Ms[-1] else None
+        fits[kind] = {"mxfp8_F_us": round(fm, 2), "mxfp8_c_ns_per_token": round(cm * 1e3, 3),
+                      "bf16_F_us": round(fb, 2), "bf16_c_ns_per_token": round(cb * 1e3, 3),
+                      "break_even_M": cross}
+    flops_tok = sum(2.0 * N * K for _, N, K in shapes)
+    big = rows[-1]
+    speedup = big["bf16_gpu_us"] / big["mxfp8_gpu_us"]
+    return _line("MXFP8 vs BF16 layer time over M (break-even tokens)", round(speedup, 3),
+                 "x speedup of MXFP8 over BF16 GPU time at M=16384", args, 0.0,
+                 "mxfp8-e4m3/e8m0 vs bf16, fp32 accumulate, bf16 out",
+                 {"workload": "qwen3-8b decoder layer linears (qkv, o, gate_up, down) at M in %s" % Ms,
+                  "flops_per_token": flops_tok},
+                 sweep=rows, fits=fits)
+
+
 def _bw(us, nbytes):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
@@ -224,7 +561,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qkv", choices=["qkv"])
+    ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "moe", "sync", "sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy (for scaling HBM counters)")
@@ -243,9 +580,12 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(dev)
-    out = bench_qkv(args, dev)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_qkv()
+    if args.workload == "qkv":
+        out = bench_qkv(args, dev)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_qkv()
+    else:
+        out = {"mlp": bench_mlp, "moe": bench_moe, "sync": bench_sync, "sweep": bench_sweep}[args.workload](args, dev)
     print(json.dumps(out), flush=True)
 
 

@@ -100,7 +100,8 @@ mxfp8_status mxfp8_dequantize(const uint8_t *q, const uint8_t *scales,
 /*
  * mxfp8_packed_bytes -- size in bytes of the packed weight buffers for
  * `batch` matrices of [rows=N][cols=K]: which = 0 -> elements, 1 -> scales.
- * Pure host function; returns 0 for invalid sizes (K % 32 != 0, N/K <= 0).
+ * Pure host function; returns 0 for sizes mxfp8_repack rejects (K % 32 != 0,
+ * a size <= 0, too many tiles).
  */
 size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which);
 
@@ -117,7 +118,8 @@ size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which);
  * HIP graph stay valid.
  *
  * In : q[batch][N][K], scales[batch][N][K/32] (axis-1 quantizer output of
- *      weights [N][K]; K % 32 == 0, N >= 1, batch >= 1).
+ *      weights [N][K]; K % 32 == 0, N >= 1, batch >= 1, and at most 2^24 - 1
+ *      tiles: batch * ceil(N/256) * ceil(K/128) < 2^24, else MXFP8_ERR_SHAPE).
  * Out: q_packed (mxfp8_packed_bytes(batch,N,K,0) bytes) and scales_packed
  *      (mxfp8_packed_bytes(batch,N,K,1) bytes), with this layout:
  *   NP = ceil(N/256) panels of 256 rows, KS = ceil(K/128) k-steps of 128.

@@ -80,6 +80,12 @@ mxfp8_status finish(hipError_t e) {
     return MXFP8_OK;
 }
 
+// repack runs one workgroup of 256 threads per (matrix, panel, k-step) tile on
+// a one-dimensional grid: keep the thread count below 2^32
+bool repack_tiles_ok(int64_t batch, int64_t rows, int64_t cols) {
+    return batch * packed_panels(rows) * packed_ksteps(cols) < ((int64_t)1 << 24);
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,7 +140,8 @@ mxfp8_status mxfp8_dequantize(const uint8_t *q, const uint8_t *scales, int64_t r
 
 size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which) {
     if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 32 || (which != 0 && which != 1)) return 0;
-    if (rows >= kMaxDim || cols > kMaxK || batch > 65535) return 0;
+    if (rows >= kMaxDim || cols > kMaxK || batch > 65535 || !repack_tiles_ok(batch, rows, cols))
+        return 0;
     return (size_t)(which == 0 ? packed_q_bytes(batch, rows, cols) : packed_s_bytes(batch, rows, cols));
 }
 
@@ -143,9 +150,10 @@ mxfp8_status mxfp8_repack(const uint8_t *q, const uint8_t *scales, int64_t batch
                           hipStream_t stream) {
     if (!q || !scales || !q_packed || !scales_packed) return MXFP8_ERR_NULL;
     if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 32) return MXFP8_ERR_SHAPE;
-    if (rows >= kMaxDim || cols > kMaxK || batch > 65535 || packed_panels(rows) > 65535)
+    if (rows >= kMaxDim || cols > kMaxK || batch > 65535 || !repack_tiles_ok(batch, rows, cols))
         return MXFP8_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(q_packed) || !aligned16(scales_packed)) return MXFP8_ERR_ALIGN;
+    if (!aligned16(q) || !aligned16(scales) || !aligned16(q_packed) || !aligned16(scales_packed))
+        return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
     return finish(launch_repack(q, scales, batch, rows, cols, q_packed, scales_packed, stream));

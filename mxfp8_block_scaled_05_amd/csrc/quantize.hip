@@ -6,18 +6,17 @@
 // HBM-bound (3.03 algorithmic bytes per element: 2 in, 1 + 1/32 out); the
 // design goal is full-width coalesced traffic with the arithmetic hidden.
 //
-//  - axis 1 (blocks along the contiguous axis): four lanes own one block,
-//    16 B (8 BF16) each, so every wave load is a contiguous 1 KB.  The block
-//    max is an integer max over BF16 magnitude bits, reduced across the four
-//    lanes with two DPP quad permutes (no LDS).  Elements are scaled by an
+//  - axis 1 (blocks along the contiguous axis): two lanes own one block,
+//    16 BF16 (32 B) each, so a wave's q store is a contiguous 1 KB.  The block
+//    max is an integer max over BF16 magnitude bits, completed across the
+//    lane pair with one DPP quad permute (no LDS).  Elements are scaled by an
 //    exact power of two, clamped to +-448 and converted with the hardware
-//    E4M3 conversion (round to nearest even).
+//    E4M3 conversion (round to nearest even).  A fixed set of waves walks the
+//    array with the next step's loads in flight.
 //  - axis 0 (blocks along rows, output transposed): a workgroup owns a
-//    128-row x 128-column tile; each lane walks one block (32 rows) of a
-//    column pair with dword loads, so each wave load is a contiguous 256 B row
-//    segment, and reduces its block entirely in registers.  The four waves
-//    write the four 32-byte block slices of each output row, which meet as
-//    whole 128-byte lines in the CU's L2.
+//    128-row x 128-column tile and transposes it through LDS, so global loads
+//    are 16-byte row reads and global stores whole 128-byte output lines;
+//    each lane reduces and converts its column's block in registers.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
@@ -52,14 +51,59 @@ __device__ __forceinline__ v2i convert8(const uint32_t *d, float inv) {
     return out;
 }
 
-// quad_perm DPP controls: [1,0,3,2] and [2,3,0,1]
+// quad_perm DPP control [1,0,3,2]: swap the lanes of each pair
 constexpr int kQuadSwap1 = 0xB1;
-constexpr int kQuadSwap2 = 0x4E;
+// resident waves per CU for the axis-1 quantizer's strided walk
+constexpr int kQuantWavesPerCu = 16;
 
 // ---------------------------------------------------------------- axis 1
-// One wave handles 64 consecutive blocks (4 KB of BF16) per step; the grid
-// strides over the flat array of blocks (rows * cols / 32 of them; a block
-// never straddles a row because cols % 32 == 0).
+// The flat array of blocks (rows * cols / 32 of them; a block never straddles
+// a row because cols % 32 == 0) is cut into wave-steps of 64 blocks (4 KB of
+// BF16): sub-step h in {0, 1} covers blocks 32h .. 32h+31, lane l the half
+// l % 2 of block 32h + l/2, loaded as two 16-byte pieces (d[2h], d[2h+1]).
+// Each wave walks a strided list of steps with the next step's loads in
+// flight while it converts the current one, so a wave pays the memory latency
+// once, not once per step.
+__device__ __forceinline__ void load_step(const uint16_t *__restrict__ x, int64_t b0,
+                                          int64_t nblocks, int lane, uint32_t (*d)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t blk = b0 + (u >> 1) * 32 + (lane >> 1);
+        if (blk < nblocks) {
+            const v4i v = *reinterpret_cast<const v4i *>(x + blk * 32 + (lane & 1) * 16 + (u & 1) * 8);
+            d[u][0] = v.x; d[u][1] = v.y; d[u][2] = v.z; d[u][3] = v.w;
+        } else {
+            d[u][0] = d[u][1] = d[u][2] = d[u][3] = 0;
+        }
+    }
+}
+
+__device__ __forceinline__ void convert_step(uint8_t *__restrict__ q, uint8_t *__restrict__ scales,
+                                             int64_t b0, int64_t nblocks, int lane,
+                                             uint32_t (*d)[4]) {
+    uint32_t code[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t m = max(max_mag(d[2 * h], 4), max_mag(d[2 * h + 1], 4));
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadSwap1, 0xF, 0xF, false));
+        code[h] = scale_code_from_amax_bits(m);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t blk = b0 + h * 32 + (lane >> 1);
+        const float inv = inv_scale_from_code(code[h]);
+        v2i o0 = convert8(d[2 * h], inv), o1 = convert8(d[2 * h + 1], inv);
+        v4i o = v4i{o0.x, o0.y, o1.x, o1.y};
+        if (code[h] == 255u) o = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+        if (blk < nblocks) *reinterpret_cast<v4i *>(q + blk * 32 + (lane & 1) * 16) = o;
+    }
+    // lane l stores the scale of block b0 + l, held by lane 2*(l%32) of sub-step l/32
+    const int src = (lane & 31) * 2;
+    const uint32_t s0 = __shfl(code[0], src), s1 = __shfl(code[1], src);
+    const uint32_t sc = lane < 32 ? s0 : s1;
+    if (b0 + lane < nblocks) scales[b0 + lane] = (uint8_t)sc;
+}
+
 __global__ __launch_bounds__(256) void quantize_axis1_kernel(const uint16_t *__restrict__ x,
                                                              uint8_t *__restrict__ q,
                                                              uint8_t *__restrict__ scales,
@@ -68,69 +112,76 @@ __global__ __launch_bounds__(256) void quantize_axis1_kernel(const uint16_t *__r
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     const int64_t nsteps = (nblocks + 63) / 64;
-    for (int64_t step = wave; step < nsteps; step += nwaves) {
-        const int64_t b0 = step * 64;
-        uint32_t d[4][4];
-        uint32_t code[4];
+    int64_t step = wave;
+    if (step >= nsteps) return;
+    uint32_t cur[4][4], nxt[4][4];
+    load_step(x, step * 64, nblocks, lane, cur);
+    for (; step < nsteps; step += nwaves) {
+        const bool more = step + nwaves < nsteps;
+        if (more) load_step(x, (step + nwaves) * 64, nblocks, lane, nxt);
+        convert_step(q, scales, step * 64, nblocks, lane, cur);
+        if (more) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t blk = b0 + u * 16 + (lane >> 2);
-            if (blk < nblocks) {
-                const v4i v = *reinterpret_cast<const v4i *>(x + blk * 32 + (lane & 3) * 8);
-                d[u][0] = v.x; d[u][1] = v.y; d[u][2] = v.z; d[u][3] = v.w;
-            } else {
-                d[u][0] = d[u][1] = d[u][2] = d[u][3] = 0;
-            }
-        }
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            uint32_t m = max_mag(d[u], 4);
-            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadSwap1, 0xF, 0xF, false));
-            m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadSwap2, 0xF, 0xF, false));
-            code[u] = scale_code_from_amax_bits(m);
+                for (int k = 0; k < 4; ++k) cur[u][k] = nxt[u][k];
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t blk = b0 + u * 16 + (lane >> 2);
-            v2i o = convert8(d[u], inv_scale_from_code(code[u]));
-            if (code[u] == 255u) { o.x = 0x7F7F7F7F; o.y = 0x7F7F7F7F; }
-            if (blk < nblocks) *reinterpret_cast<v2i *>(q + blk * 32 + (lane & 3) * 8) = o;
-        }
-        // lane l stores the scale of block b0 + l, held by lane 4*(l%16) of step l/16
-        const int src = (lane & 15) * 4;
-        uint32_t s0 = __shfl(code[0], src), s1 = __shfl(code[1], src);
-        uint32_t s2 = __shfl(code[2], src), s3 = __shfl(code[3], src);
-        const int sel = lane >> 4;
-        uint32_t s = sel == 0 ? s0 : sel == 1 ? s1 : sel == 2 ? s2 : s3;
-        if (b0 + lane < nblocks) scales[b0 + lane] = (uint8_t)s;
     }
 }
 
 // ---------------------------------------------------------------- axis 0
-// x[rows][cols] -> q[cols][rows], scales[cols][rows/32].  Workgroup = 4 waves
-// on a 128-row x 128-column tile; wave w takes rows [32w, 32w+32) of the tile,
-// lane l the column pair (2l, 2l+1).
+// x[rows][cols] -> q[cols][rows], scales[cols][rows/32].  A workgroup of four
+// waves owns a 128-row x 128-column tile and moves it through LDS twice:
+//   1. the BF16 tile is read with 16-byte row loads into LDS (row-major),
+//   2. wave w takes rows [32w, 32w+32), lane l the column pair (2l, 2l+1): it
+//      reads its two 32-element blocks as 32 dwords (one 256-byte LDS row per
+//      wave read, conflict-free) and quantizes them in registers,
+//   3. the E4M3 tile is written back to the same LDS as [128 columns][128 B]
+//      (padded rows) and stored to q as whole 128-byte lines.
+constexpr int kA0Tile = 128;
+constexpr int kA0OutPitch = 144;  // bytes per staged output column (16-byte aligned)
+
 __global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__restrict__ x,
                                                              uint8_t *__restrict__ q,
                                                              uint8_t *__restrict__ scales,
                                                              int64_t rows, int64_t cols) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int64_t r0 = (int64_t)blockIdx.y * 128 + w * 32;
-    const int64_t c = (int64_t)blockIdx.x * 128 + 2 * lane;
-    if (r0 >= rows || c >= cols) return;
-    const bool pair = c + 1 < cols;
-    const bool aligned_pair = pair && ((cols & 1) == 0);
-    uint32_t d[32];
-    const uint16_t *src = x + r0 * cols + c;
-    if (aligned_pair) {
+    __shared__ __attribute__((aligned(16))) uint32_t tile[kA0Tile * kA0Tile / 2];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    static_assert(kA0Tile * kA0OutPitch <= (int)sizeof(tile), "output stage fits the input stage");
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t R0 = (int64_t)blockIdx.y * kA0Tile, C0 = (int64_t)blockIdx.x * kA0Tile;
+
+    if ((cols & 7) == 0) {
+        // rows are 16-byte aligned: sixteen 16-byte chunks per tile row
+        const int ch = t & 15;
+        const int64_t c = C0 + ch * 8;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) d[r] = *reinterpret_cast<const uint32_t *>(src + r * cols);
+        for (int i = 0; i < 8; ++i) {
+            const int r = i * 16 + (t >> 4);
+            v4i v = v4i{0, 0, 0, 0};
+            if (R0 + r < rows && c < cols)
+                v = *reinterpret_cast<const v4i *>(x + (R0 + r) * cols + c);
+            *reinterpret_cast<v4i *>(&tile[r * 64 + ch * 4]) = v;
+        }
     } else {
-#pragma unroll
-        for (int r = 0; r < 32; ++r)
-            d[r] = (uint32_t)src[r * cols] | (pair ? ((uint32_t)src[r * cols + 1] << 16) : 0u);
+        for (int i = t; i < kA0Tile * 64; i += 256) {
+            const int r = i >> 6;
+            const int64_t row = R0 + r, c = C0 + 2 * (i & 63);
+            uint32_t v = 0;
+            if (row < rows) {
+                if (c < cols) v = x[row * cols + c];
+                if (c + 1 < cols) v |= (uint32_t)x[row * cols + c + 1] << 16;
+            }
+            tile[i] = v;
+        }
     }
+    __syncthreads();
+
+    uint32_t d[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) d[r] = tile[(32 * w + r) * 64 + lane];
+    __syncthreads();  // the tile is reused for the output below
+
     us2 m = as_us2(d[0] & 0x7FFF7FFFu);
 #pragma unroll
     for (int r = 1; r < 32; ++r) m = __builtin_elementwise_max(m, as_us2(d[r] & 0x7FFF7FFFu));
@@ -138,7 +189,7 @@ __global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__r
     const uint32_t code_hi = scale_code_from_amax_bits(m.y);
     const float inv_lo = inv_scale_from_code(code_lo);
     const float inv_hi = inv_scale_from_code(code_hi);
-    v4i lo[2], hi[2];
+    uint8_t *ob = reinterpret_cast<uint8_t *>(tile);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         int wl[4], wh[4];
@@ -154,21 +205,38 @@ __global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__r
             wh[k] = cvt2_e4m3<true>(bits_to_float(d[r + 2] & 0xFFFF0000u) * inv_hi,
                                     bits_to_float(d[r + 3] & 0xFFFF0000u) * inv_hi, b);
         }
-        lo[h] = v4i{wl[0], wl[1], wl[2], wl[3]};
-        hi[h] = v4i{wh[0], wh[1], wh[2], wh[3]};
-        if (code_lo == 255u) lo[h] = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
-        if (code_hi == 255u) hi[h] = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+        v4i lo = v4i{wl[0], wl[1], wl[2], wl[3]};
+        v4i hi = v4i{wh[0], wh[1], wh[2], wh[3]};
+        if (code_lo == 255u) lo = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+        if (code_hi == 255u) hi = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+        *reinterpret_cast<v4i *>(ob + (2 * lane) * kA0OutPitch + 32 * w + 16 * h) = lo;
+        *reinterpret_cast<v4i *>(ob + (2 * lane + 1) * kA0OutPitch + 32 * w + 16 * h) = hi;
+    }
+    stile[(2 * lane) * 4 + w] = (uint8_t)code_lo;
+    stile[(2 * lane + 1) * 4 + w] = (uint8_t)code_hi;
+    __syncthreads();
+
+    // eight lanes store one output column's 128-byte line; rows % 32 == 0, so a
+    // 16-byte chunk of the line is either wholly inside the matrix or outside
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int col = i * 32 + (t >> 3), j = t & 7;
+        const int64_t c = C0 + col, r = R0 + 16 * j;
+        if (c < cols && r < rows)
+            *reinterpret_cast<v4i *>(q + c * rows + r) =
+                *reinterpret_cast<const v4i *>(ob + col * kA0OutPitch + 16 * j);
     }
     const int64_t nb = rows / 32;
-    v4i *dst_lo = reinterpret_cast<v4i *>(q + c * rows + r0);
-    dst_lo[0] = lo[0];
-    dst_lo[1] = lo[1];
-    scales[c * nb + r0 / 32] = (uint8_t)code_lo;
-    if (pair) {
-        v4i *dst_hi = reinterpret_cast<v4i *>(q + (c + 1) * rows + r0);
-        dst_hi[0] = hi[0];
-        dst_hi[1] = hi[1];
-        scales[(c + 1) * nb + r0 / 32] = (uint8_t)code_hi;
+    if (t < kA0Tile && C0 + t < cols) {
+        uint8_t *srow = scales + (C0 + t) * nb + R0 / 32;
+        if ((nb & 3) == 0 && R0 + kA0Tile <= rows) {
+            // the tile's four scales of this column are one aligned dword
+            *reinterpret_cast<uint32_t *>(srow) = reinterpret_cast<const uint32_t *>(stile)[t];
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (R0 + 32 * b < rows) srow[b] = stile[t * 4 + b];
+        }
     }
 }
 
@@ -177,15 +245,16 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int ax
     if (axis == 1) {
         const int64_t nblocks = rows * (cols / 32);
         const int64_t nsteps = (nblocks + 63) / 64;
-        // enough waves to cover the chip several times; each wave loops
+        // kQuantWavesPerCu waves per CU, each walking several steps
         int64_t grid = (nsteps + 3) / 4;
-        const int64_t cap = (int64_t)device_cu_count() * 16;
+        const int64_t cap = (int64_t)device_cu_count() * (kQuantWavesPerCu / 4);
         if (grid > cap) grid = cap;
         if (grid < 1) grid = 1;
         hipLaunchKernelGGL(quantize_axis1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, q,
                            scales, nblocks);
     } else {
-        dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+        dim3 grid((unsigned)((cols + kA0Tile - 1) / kA0Tile),
+                  (unsigned)((rows + kA0Tile - 1) / kA0Tile));
         hipLaunchKernelGGL(quantize_axis0_kernel, grid, dim3(256), 0, stream, x, q, scales, rows,
                            cols);
     }

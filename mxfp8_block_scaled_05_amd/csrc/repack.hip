@@ -18,71 +18,77 @@
 
 namespace mx {
 
-// One workgroup per (k-step, panel, batch) tile of 32 KB.  Eight consecutive
-// lanes move one 128-byte row, so loads and stores are whole rows.
-__global__ __launch_bounds__(256) void repack_q_kernel(const uint8_t *__restrict__ q,
-                                                       uint8_t *__restrict__ qp, int64_t N,
-                                                       int64_t K) {
-    const int64_t ks = blockIdx.x, panel = blockIdx.y, b = blockIdx.z;
-    const int64_t KS = gridDim.x, NP = gridDim.y;
-    uint8_t *dst = qp + ((b * NP + panel) * KS + ks) * kTileBytes;
+// Workgroup index -> tile index such that each XCD (workgroups are dealt to
+// the eight XCDs round-robin) gets a contiguous range of tiles: all k-steps of
+// a panel then run under one L2, which serves the panel's scale rows to every
+// k-step after the first.
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t wg, int64_t nwg) {
+    const int64_t q = nwg / 8, r = nwg % 8, x = wg % 8;
+    return x * q + (x < r ? x : r) + wg / 8;
+}
+
+// One workgroup per (k-step, panel, batch) tile.
+//  - elements: 32 KB; eight consecutive lanes move one 128-byte row, so loads
+//    and stores are whole rows.
+//  - scales: the tile's 1 KB.  Thread t loads the four scale bytes (blocks
+//    4ks .. 4ks+3) of panel row t as one word, the words meet in LDS, and
+//    thread t then gathers its output word: rows 16*(t/16) + 4*(t%4) .. +3 of
+//    block 4ks + (t/4)%4, i.e. bytes (atom t/16, lanes 4*(t%16) .. +3).
+__global__ __launch_bounds__(256) void repack_kernel(const uint8_t *__restrict__ q,
+                                                     const uint8_t *__restrict__ s,
+                                                     uint8_t *__restrict__ qp,
+                                                     uint32_t *__restrict__ sp, int64_t N,
+                                                     int64_t K, int64_t KS, int64_t NP) {
+    __shared__ uint32_t rows_s[kPanelRows];
+    const int t = threadIdx.x;
+    const int64_t tile = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int64_t ks = tile % KS, panel = (tile / KS) % NP, b = tile / (KS * NP);
+    const int64_t tile_lin = (b * NP + panel) * KS + ks;
+
+    // scale word of row t: blocks 4ks .. 4ks+3, padding 127
+    const int64_t nb = K / 32, n = panel * kPanelRows + t, blk0 = 4 * ks;
+    uint32_t word = 0x7F7F7F7Fu;
+    if (n < N) {
+        const uint8_t *srow = s + (b * N + n) * nb;
+        if ((nb & 3) == 0) {
+            word = *reinterpret_cast<const uint32_t *>(srow + blk0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (blk0 + j < nb)
+                    word = (word & ~(0xFFu << (8 * j))) | ((uint32_t)srow[blk0 + j] << (8 * j));
+        }
+    }
+    rows_s[t] = word;
+
+    uint8_t *dst = qp + tile_lin * kTileBytes;
     const uint8_t *src = q + b * N * K;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-        const int ci = it * 256 + threadIdx.x;
+        const int ci = it * 256 + t;
         const int r = ci >> 3, c = ci & 7;
-        const int64_t n = panel * kPanelRows + r;
+        const int64_t nr = panel * kPanelRows + r;
         const int64_t k = ks * kKStep + c * 16;
         v4i v = v4i{0, 0, 0, 0};
-        if (n < N && k < K) v = *reinterpret_cast<const v4i *>(src + n * K + k);
+        if (nr < N && k < K) v = *reinterpret_cast<const v4i *>(src + nr * K + k);
         *reinterpret_cast<v4i *>(dst + r * 128 + ((c ^ (int)swz(r)) * 16)) = v;
     }
-}
 
-// One thread per output dword: bytes (panel, k-step, atom, lanes l..l+3) are
-// the scales of rows 256*panel + 16*atom + (l % 16) .. +3, block 4*kstep +
-// l/16 (four consecutive rows, one block); padding holds 127.
-__global__ __launch_bounds__(256) void repack_s_kernel(const uint8_t *__restrict__ s,
-                                                       uint32_t *__restrict__ sp, int64_t batch,
-                                                       int64_t N, int64_t K, int64_t NP,
-                                                       int64_t KS) {
-    const int64_t total = batch * NP * KS * (kScaleStepBytes / 4);
-    const int64_t nb = K / 32;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t lane0 = (i * 4) & 63;
-        const int64_t atom = (i >> 4) & 15;
-        const int64_t ks = (i >> 8) % KS;
-        const int64_t panel = (i >> 8) / KS % NP;
-        const int64_t b = (i >> 8) / (KS * NP);
-        const int64_t blk = 4 * ks + (lane0 >> 4);
-        const int64_t row0 = panel * kPanelRows + atom * 16 + (lane0 & 15);
-        uint32_t word = 0;
+    __syncthreads();
+    const uint8_t *bytes = reinterpret_cast<const uint8_t *>(rows_s);
+    const int row0 = 16 * (t >> 4) + 4 * (t & 3), j = (t >> 2) & 3;
+    uint32_t out = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t n = row0 + q;
-            uint32_t v = 127u;
-            if (n < N && blk < nb) v = s[(b * N + n) * nb + blk];
-            word |= v << (8 * q);
-        }
-        sp[i] = word;
-    }
+    for (int i = 0; i < 4; ++i) out |= (uint32_t)bytes[(row0 + i) * 4 + j] << (8 * i);
+    sp[tile_lin * (kScaleStepBytes / 4) + t] = out;
 }
 
 hipError_t launch_repack(const uint8_t *q, const uint8_t *scales, int64_t batch, int64_t N,
                          int64_t K, uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream) {
     const int64_t NP = packed_panels(N), KS = packed_ksteps(K);
-    dim3 grid((unsigned)KS, (unsigned)NP, (unsigned)batch);
-    hipLaunchKernelGGL(repack_q_kernel, grid, dim3(256), 0, stream, q, q_packed, N, K);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t total = batch * NP * KS * (kScaleStepBytes / 4);
-    int64_t g = (total + 255) / 256;
-    const int64_t cap = (int64_t)device_cu_count() * 16;
-    if (g > cap) g = cap;
-    if (g < 1) g = 1;
-    hipLaunchKernelGGL(repack_s_kernel, dim3((unsigned)g), dim3(256), 0, stream, scales,
-                       reinterpret_cast<uint32_t *>(s_packed), batch, N, K, NP, KS);
+    const int64_t tiles = batch * NP * KS;
+    hipLaunchKernelGGL(repack_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scales,
+                       q_packed, reinterpret_cast<uint32_t *>(s_packed), N, K, KS, NP);
     return hipGetLastError();
 }
 

@@ -44,6 +44,9 @@ def test_host_only_entry_points(libmx):
             assert libmx.mxfp8_packed_bytes(batch, N, K, which) == oracle.packed_bytes(batch, N, K, which)
     assert libmx.mxfp8_packed_bytes(1, 16, 48, 0) == 0      # K % 32 != 0
     assert libmx.mxfp8_packed_bytes(0, 16, 64, 0) == 0
+    # one repack workgroup per 256-row x 128-byte tile; 2^24 tiles are refused
+    assert libmx.mxfp8_packed_bytes(16, 1024 * 256, 1024 * 128, 0) == 0
+    assert libmx.mxfp8_packed_bytes(15, 1024 * 256, 1024 * 128, 0) == 15 * 2 ** 35
 
 
 def test_argument_errors_before_any_device_work(libmx):

@@ -76,7 +76,7 @@ def _gemm_dev(mx, aq, as_, bq, bs, packed, out_dtype):
 
 
 @pytest.mark.parametrize("batch,N,K", [(1, 256, 128), (1, 300, 320), (3, 17, 96), (2, 512, 768),
-                                       (1, 6144, 4096)])
+                                       (2, 300, 384), (5, 1000, 1056), (1, 6144, 4096)])
 def test_repack_matches_oracle(mx, oracle_mod, batch, N, K):
     _say("repack", batch, N, K)
     rng = np.random.default_rng(batch * N + K)
