@@ -395,7 +395,26 @@ def bench_sync(args, dev):
         ops.append(("quantize_" + name, lambda W=W, q=q, sc=sc: mx.quantize_into(W, 1, q, sc)))
         ops.append(("repack_" + name, lambda q=q, sc=sc, pk=pk: mx.repack_(q, sc, pk)))
     torch.cuda.synchronize()
-    ms, avg = run_timed(ops, args)
+    # eager: one host launch per call (host-bound: 288 launches per sync)
+    eager_ms, avg = run_timed(ops, argparse.Namespace(steps=max(2, args.steps // 5), warmup=1))
+    # captured: the 288 launches recorded once into a HIP graph and replayed,
+    # as a sampler replays its captured graphs after writing weights in place
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _, fn in ops:
+            fn()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    gpu_ms = e0.elapsed_time(e1) / args.steps
     by_q = n_elts * Q_BYTES_PER_ELT
     by_r = n_elts * REPACK_BYTES_PER_ELT
     kern = {}
@@ -406,9 +425,13 @@ def bench_sync(args, dev):
     return _line("weight sync GB/s (% HBM): quantize + repack of all Qwen3-8B linears",
                  round(gbs, 1), "GB/s", args, ms, "bf16 -> mxfp8-e4m3/e8m0",
                  {"workload": "qwen3-8b weight sync: quantize along K + repack of 144 linears "
-                              "(36 layers x qkv, o, gate_up, down)", "elements": n_elts},
-                 kernels=kern,
+                              "(36 layers x qkv, o, gate_up, down), replayed as one HIP graph",
+                  "elements": n_elts},
+                 kernels=kern, kernels_note="per-call HIP-event times from the eager run (they include "
+                                            "host launch gaps when the host falls behind)",
                  summary={"quantize_GB": round(by_q / 1e9, 2), "repack_GB": round(by_r / 1e9, 2),
+                          "graph_gpu_ms": round(gpu_ms, 3), "eager_ms_per_sync": round(eager_ms, 3),
+                          "eager_GB/s": round((by_q + by_r) / (eager_ms * 1e-3) / 1e9, 1),
                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
                  roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,

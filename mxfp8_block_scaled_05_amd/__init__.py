@@ -255,6 +255,10 @@ def grouped_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, offsets:
         out = torch.empty((M_total, w.N), dtype=out_dtype, device=a_q.device)
     else:
         _need(out, out_dtype, "out")
+        if tuple(out.shape) != (M_total, w.N):
+            raise ValueError("out must be [M_total, N]")
+    if tuple(a_s.shape) != (M_total, K // 32):
+        raise ValueError("a_s must be [M_total, K/32]")
     _check(lib().mxfp8_grouped_gemm(_ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s), _ptr(offsets), G,
                                     M_total, w.N, K, _ptr(out), code, _stream(a_q.device)),
            "mxfp8_grouped_gemm")

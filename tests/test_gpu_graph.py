@@ -1,0 +1,142 @@
+"""Library calls recorded into a HIP graph and replayed.
+
+The sampler of "End-to-End MXFP8 RL on Blackwell" (verl blog), section "The
+pipeline", sampler paragraph, rewrites its weights in place and replays
+captured graphs.  The library's calls allocate nothing and never synchronize,
+so a caller can record them once and replay them after every update.
+
+Bars: every replay equals an eager run of the same calls on the same inputs
+bit for bit (quantize and repack are exact; the GEMMs are deterministic), with
+eager work and synchronizations between the replays; the first replay is also
+checked against the oracle (quantize bit-exact, GEMM within 1e-4 * sum|ab| plus
+the bf16 rounding of the output).
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from conftest import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("graph case:", *a, flush=True)
+
+
+def test_graph_replay_dense_step_matches_eager(mx, oracle_mod):
+    import torch
+    M, N, K = 96, 300, 320
+    _say("dense", M, N, K)
+    dev = torch.device("cuda:0")
+    X = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    W = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+
+    def buffers():
+        return dict(xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                    xs=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+                    wq=torch.empty((N, K), dtype=torch.uint8, device=dev),
+                    ws=torch.empty((N, K // 32), dtype=torch.uint8, device=dev),
+                    w=mx.PackedWeight(torch.empty(mx.packed_bytes(1, N, K, 0), dtype=torch.uint8, device=dev),
+                                      torch.empty(mx.packed_bytes(1, N, K, 1), dtype=torch.uint8, device=dev),
+                                      1, N, K),
+                    y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                    y32=torch.empty((M, N), dtype=torch.float32, device=dev))
+
+    def step(b):
+        mx.quantize_into(W, 1, b["wq"], b["ws"])
+        mx.quantize_into(X, 1, b["xq"], b["xs"])
+        mx.repack_(b["wq"], b["ws"], b["w"])
+        mx.gemm(b["xq"], b["xs"], b["w"], torch.bfloat16, out=b["y"])
+        mx.gemm(b["xq"], b["xs"], (b["wq"], b["ws"]), torch.float32, out=b["y32"])
+
+    g_buf, e_buf = buffers(), buffers()
+    X.zero_()
+    W.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_buf)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        rng = np.random.default_rng(100 + rep)
+        x = wl.normal_bf16(rng, (M, K), outlier_frac=0.01)
+        w = wl.normal_bf16(rng, (N, K), std=0.02)
+        X.copy_(to_dev(x))          # new inputs written into the captured storage
+        W.copy_(to_dev(w))
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_buf)                 # eager reference on the same inputs
+        torch.cuda.synchronize()
+        for key in ("xq", "xs", "wq", "ws", "y", "y32"):
+            assert np.array_equal(to_host(g_buf[key]), to_host(e_buf[key])), (rep, key)
+        assert np.array_equal(to_host(g_buf["w"].q), to_host(e_buf["w"].q)), rep
+        assert np.array_equal(to_host(g_buf["w"].s), to_host(e_buf["w"].s)), rep
+        if rep == 0:
+            xq, xs = oracle_mod.quantize(x, 1)
+            wq, ws = oracle_mod.quantize(w, 1)
+            assert np.array_equal(to_host(g_buf["xq"]), xq) and np.array_equal(to_host(g_buf["xs"]), xs)
+            assert np.array_equal(to_host(g_buf["wq"]), wq) and np.array_equal(to_host(g_buf["ws"]), ws)
+            c_ref, c_abs = oracle_mod.gemm(xq, xs, wq, ws)
+            y = wl.bf16_bits_to_f32(to_host(g_buf["y"]))
+            ok, worst = oracle_mod.gemm_bound_ok(y, c_ref, c_abs, "bf16")
+            assert ok, worst
+            ok, worst = oracle_mod.gemm_bound_ok(to_host(g_buf["y32"]), c_ref, c_abs, "f32")
+            assert ok, worst
+
+
+def test_graph_replay_grouped_new_offsets_each_replay(mx, oracle_mod):
+    """The grouped GEMM reads its group offsets on the device, so one captured
+    graph serves every routing: new offsets are copied in before each replay."""
+    import torch
+    G, N, K, M_total = 5, 192, 256, 384
+    _say("grouped", G, N, K, M_total)
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7)
+    wb = wl.normal_bf16(rng, (G * N, K), std=0.02)
+    bq, bs = oracle_mod.quantize(wb, 1)
+    w = mx.repack(to_dev(bq.reshape(G, N, K)), to_dev(bs.reshape(G, N, K // 32)))
+    A = torch.empty((M_total, K), dtype=torch.bfloat16, device=dev)
+    offs = torch.zeros(G + 1, dtype=torch.int32, device=dev)
+
+    def buffers():
+        return dict(aq=torch.empty((M_total, K), dtype=torch.uint8, device=dev),
+                    as_=torch.empty((M_total, K // 32), dtype=torch.uint8, device=dev),
+                    y=torch.zeros((M_total, N), dtype=torch.float32, device=dev))
+
+    def step(b):
+        mx.quantize_into(A, 1, b["aq"], b["as_"])
+        mx.grouped_gemm(b["aq"], b["as_"], w, offs, torch.float32, out=b["y"])
+
+    g_buf, e_buf = buffers(), buffers()
+    A.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_buf)
+    torch.cuda.synchronize()
+
+    layouts = [[0, 32, 96, 96, 224, 384], [0, 0, 160, 192, 352, 384], [0, 64, 64, 64, 64, 320]]
+    for rep, lay in enumerate(layouts):
+        a = wl.normal_bf16(np.random.default_rng(200 + rep), (M_total, K))
+        A.copy_(to_dev(a))
+        offs.copy_(torch.tensor(lay, dtype=torch.int32))
+        g_buf["y"].zero_()
+        e_buf["y"].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_buf)
+        torch.cuda.synchronize()
+        yg = to_host(g_buf["y"])
+        assert np.array_equal(yg, to_host(e_buf["y"])), rep
+        aq, as_ = oracle_mod.quantize(a, 1)
+        assert np.array_equal(to_host(g_buf["aq"]), aq)
+        c_ref, c_abs, grp = oracle_mod.grouped_gemm(aq, as_, bq.reshape(G, N, K),
+                                                    bs.reshape(G, N, K // 32), np.array(lay, np.int32))
+        inside = grp >= 0
+        ok, worst = oracle_mod.gemm_bound_ok(yg[inside], c_ref[inside], c_abs[inside], "f32")
+        assert ok, (rep, worst)
+        # rows outside [o_0, o_G) are not written (zero from the fill above)
+        assert np.all(yg[~inside] == 0), rep
