@@ -441,11 +441,11 @@ __device__ __forceinline__ void store_tile_scalar(const GemmParams &p, int64_t r
 // back 16 bytes per lane so every global store is a whole 16-byte piece of a
 // contiguous row segment.  Rows go in passes of PR so the regions of all
 // waves fit the LDS the main loop used.  Callers sync before (the stages are
-// reused) and use this only for blocks fully inside C with 16-byte aligned
-// rows.
+// reused) and use this only for tiles whose columns are inside C with
+// 16-byte aligned rows; rows at or past m_end are not written.
 template <int FM, int FN, bool OUT_BF16, int LDS_BYTES>
-__device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0, int64_t col0, v4f (*acc)[FN],
-                               int lane, int w, uint8_t *smem) {
+__device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0, int64_t col0, int64_t m_end,
+                               v4f (*acc)[FN], int lane, int w, uint8_t *smem) {
     constexpr int ES = OUT_BF16 ? 2 : 4;
     constexpr int WTM = FM * 16, WTN = FN * 16;
     constexpr int ROWB = WTN * ES + 16;                       // padded LDS row
@@ -481,8 +481,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0
             const int rl = r0 + lane / LPR;
             const int cb = (lane % LPR) * 16;
             const v4i v = *reinterpret_cast<const v4i *>(cw + rl * ROWB + cb);
-            uint8_t *dst = static_cast<uint8_t *>(p.c) + ((row0 + pass * PR + rl) * N + col0) * ES + cb;
-            *reinterpret_cast<v4i *>(dst) = v;
+            const int64_t row = row0 + pass * PR + rl;
+            uint8_t *dst = static_cast<uint8_t *>(p.c) + (row * N + col0) * ES + cb;
+            if (row < m_end) *reinterpret_cast<v4i *>(dst) = v;
         }
     }
 }
@@ -544,11 +545,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
     const int64_t row0 = m0 + t.wm * T::WTM, col0 = n0 + t.wn * T::WTN;
     constexpr int ES = OUT_BF16 ? 2 : 4;
-    // uniform over the workgroup: every wave's block inside C, rows 16 B aligned
-    const bool inside = m0 + BM <= m_end && n0 + BN <= p.N && (p.N * ES) % 16 == 0;
+    // uniform over the workgroup: the tile's columns inside C, rows 16 B
+    // aligned (partial row ranges, e.g. the last tile of an expert, are masked)
+    const bool inside = n0 + BN <= p.N && (p.N * ES) % 16 == 0;
     if (inside) {
         __syncthreads();                    // every wave is done with the stages
-        store_tile_lds<FM, FN, OUT_BF16, 2 * T::STAGE>(p, row0, col0, acc, t.lane, t.w, smem);
+        store_tile_lds<FM, FN, OUT_BF16, 2 * T::STAGE>(p, row0, col0, m_end, acc, t.lane, t.w, smem);
     } else {
         store_tile_scalar<FM, FN, OUT_BF16>(p, row0, col0, m_end, acc, t.lane);
     }
