@@ -16,12 +16,11 @@
 //    (s_waitcnt vmcnt + barrier), so the compiler never orders its own waits
 //    behind them.
 //  - A 2-stage ring with one barrier at the top of each step.
-//  - LDS rows are 128 B (one step).  Packed weights (mxfp8_repack) are stored
-//    as their LDS image: the 16-byte chunk c of row r sits at slot c ^ f(r %
-//    16), which makes the ds_read_b128 of 16 rows at one chunk bank conflict
-//    free, and they are copied linearly.  Canonical operands are copied as
-//    whole 128-byte lines (every request a full line) into an interleaved,
-//    padded image (see lds_frag_il) that is bank-conflict free as well.
+//  - LDS rows are 128 B (one step); the 16-byte chunk c of row r sits at slot
+//    c ^ f(r % 16), which makes the ds_read_b128 of 16 rows at one chunk bank
+//    conflict free.  Canonical operands are swizzled by choosing each lane's
+//    source address; packed weights (mxfp8_repack) are already stored in this
+//    image, so their copy is linear.
 //  - Out-of-range rows and the K tail read as zeros through the buffer
 //    resource's range check (never a memory access out of bounds).
 //  - 8 waves (two per SIMD) form a WM x (8/WM) grid; each wave owns a
@@ -107,29 +106,6 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t *base, int lane) {
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
-// LDS image of a canonical (row-major, K-contiguous) operand, per k-step:
-// rows are copied as whole 128-byte lines (eight lanes per line, chunks in
-// order, so every request is a full line), 8 rows per 1 KB copy block, and a
-// 64-row group is 8 blocks, each followed by 16 bytes of padding.  Block i of
-// a group holds rows 16f + 2i + h (f = 0..3, h = 0..1) in slot 2f + h, so the
-// 16 rows of MFMA fragment f sit in 8 different blocks at two slot parities:
-// their byte offsets mod 256 (64 banks x 4 bytes) are 16i + 128h + 16 chunk,
-// all distinct, and a 16-lane fragment read is bank-conflict free.
-constexpr int kIlBlock = 1024 + 16;        // copy block + padding
-constexpr int kIlGroup = 8 * kIlBlock;     // 64 rows
-__host__ __device__ constexpr int il_bytes(int rows) { return rows / 64 * kIlGroup; }
-
-// Fragment (16 rows starting at a multiple of 16, `row0`) of an interleaved
-// image: lane group jj gets K chunks jj and 4 + jj of row row0 + (lane % 16).
-__device__ __forceinline__ v8i lds_frag_il(const uint8_t *img, int row0, int lane) {
-    const int q = lane & 15, jj = lane >> 4;
-    const int g = row0 >> 6, f = (row0 >> 4) & 3;
-    const uint8_t *r = img + g * kIlGroup + (q >> 1) * kIlBlock + (2 * f + (q & 1)) * 128;
-    const v4i lo = *reinterpret_cast<const v4i *>(r + jj * 16);
-    const v4i hi = *reinterpret_cast<const v4i *>(r + (4 + jj) * 16);
-    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
-
 // renumber so that each XCD (workgroup id mod 8) receives a contiguous range
 __device__ __forceinline__ int xcd_logical(int wg, int nwg) {
     const int q = nwg / 8, r = nwg % 8, x = wg % 8;
@@ -192,36 +168,24 @@ struct TileOps {
     static constexpr int WN = kWaves / WM;
     static constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
     static constexpr int FM = WTM / 16, FN = WTN / 16;      // MFMA tiles per wave
-    // LDS stage: [A image | B image | packed B scales].  Packed B scales are
-    // the packed layout's 64 bytes per 16-row atom per step; canonical A (and
-    // B) scales (K % 128 == 0) live in their own double buffer (below).  With
-    // K % 128 != 0, canonical scale bytes come through registers instead
-    // (compiler-visible byte loads).
+    // LDS stage: [A tile | B tile | A scales | B scales].  A scales (K % 128
+    // == 0) are a dword per row per step; B scales are the packed layout's
+    // 64 bytes per 16-row atom per step, or (canonical B, K % 128 == 0) a
+    // dword per row.  With K % 128 != 0, A (and canonical B) scale bytes come
+    // through registers instead (compiler-visible byte loads).
     static constexpr bool SA_LDS = KALIGN;
     static constexpr bool SB_LDS = BPACK || KALIGN;
-    static constexpr bool SB_CANON = KALIGN && !BPACK;   // canonical B scales in LDS
-    static constexpr int A_BYTES = il_bytes(BM);
-    static constexpr int B_BYTES = BPACK ? BN * 128 : il_bytes(BN);
-    static constexpr int TILE = A_BYTES + B_BYTES;
-    static constexpr int SB_OFF = TILE;                  // packed B scales, per stage
-    static constexpr int STAGE = SB_OFF + (BPACK ? BN * 4 : 0);
-    // Canonical scales come in groups of four k-steps (16 bytes of a row: one
-    // line request per row per four steps, not per step), double-buffered
-    // after the two stages: [buffer][row][16 B] when rows are 16-byte
-    // aligned (K % 512 == 0), else [buffer][step][row][4 B] filled per step.
-    static constexpr int SQA_OFF = 2 * STAGE;
-    static constexpr int SQB_OFF = SQA_OFF + (SA_LDS ? 2 * BM * 16 : 0);
-    static constexpr int LDS_TOTAL = SQB_OFF + (SB_CANON ? 2 * BN * 16 : 0);
+    static constexpr int TILE = (BM + BN) * 128;
+    static constexpr int SA_OFF = TILE;
+    static constexpr int SB_OFF = SA_OFF + (SA_LDS ? BM * 4 : 0);
+    static constexpr int STAGE = SB_OFF + (SB_LDS ? BN * 4 : 0);
     static_assert(FM >= 2 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0 && BM % 64 == 0 && BN % 64 == 0,
-                  "copy segments");
+    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "copy segments");
 
     v4i ra, rsa, rb, rsb;
     __amdgpu_buffer_rsrc_t rsa_c, rsb_c;
     int Ki, KBi, lane, w, wm, wn, lrow, lblk;
-    bool quad;                 // canonical scale rows 16-byte aligned
     uint32_t lds0;
-    const uint8_t *smem_p;
 
     __device__ __forceinline__ void init(const GemmParams &p, int64_t m0, int64_t m_end, int64_t n0, int64_t g,
                          const uint8_t *smem) {
@@ -234,9 +198,7 @@ struct TileOps {
         lblk = lane >> 4;
         Ki = (int)K;
         KBi = (int)KB;
-        quad = (KBi & 15) == 0;
         lds0 = lds_addr(smem);
-        smem_p = smem;
         const int rows_a = (int)min((int64_t)BM, m_end - m0);
         // each descriptor spans exactly this tile's bytes: out-of-range lanes read 0
         ra = make_srd(p.a_q + m0 * K, (uint32_t)(rows_a * K));
@@ -260,63 +222,44 @@ struct TileOps {
     // global -> LDS copies of k-step ks into stage st (this wave's share)
     __device__ __forceinline__ void issue(int ks, int st) const {
         const uint32_t sbase = lds0 + st * STAGE;
-        // interleaved image: copy block `seg` = (group seg / 8, block seg % 8);
-        // lane l moves chunk l % 8 of slot l / 8
-        const int slot = lane >> 3, c = lane & 7;
-        const int kk = ks * 128 + c * 16;
 #pragma unroll
         for (int i = 0; i < BM / (8 * kWaves); ++i) {
-            const int seg = i * kWaves + w;
-            const int rr = (seg >> 3) * 64 + (slot >> 1) * 16 + 2 * (seg & 7) + (slot & 1);
+            const int seg = i * kWaves + w;            // 1 KB LDS segment = 8 rows
+            const int rr = seg * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
+            const int kk = ks * 128 + c * 16;
             const uint32_t off = kk < Ki ? (uint32_t)(rr * Ki + kk) : kOOB;
-            dma16(ra, off, sbase + (seg >> 3) * kIlGroup + (seg & 7) * kIlBlock);
+            dma16(ra, off, sbase + seg * 1024);
         }
 #pragma unroll
         for (int i = 0; i < BN / (8 * kWaves); ++i) {
             const int seg = i * kWaves + w;
+            uint32_t off;
             if constexpr (BPACK) {
-                // packed weights are stored as their LDS image: a linear copy
-                const uint32_t off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
-                dma16(rb, off, sbase + A_BYTES + seg * 1024);
+                off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
             } else {
-                const int rr = (seg >> 3) * 64 + (slot >> 1) * 16 + 2 * (seg & 7) + (slot & 1);
-                const uint32_t off = kk < Ki ? (uint32_t)(rr * Ki + kk) : kOOB;
-                dma16(rb, off, sbase + A_BYTES + (seg >> 3) * kIlGroup + (seg & 7) * kIlBlock);
+                const int rr = seg * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
+                const int kk = ks * 128 + c * 16;
+                off = kk < Ki ? (uint32_t)(rr * Ki + kk) : kOOB;
+            }
+            dma16(rb, off, sbase + BM * 128 + seg * 1024);
+        }
+        // scale copies: 256 B segments, one per wave that owns one
+        if constexpr (SA_LDS) {
+            if (w < BM / 64) {
+                const int rr = w * 64 + lane;
+                dma4(rsa, (uint32_t)(rr * KBi + ks * 4), sbase + SA_OFF + w * 256);
             }
         }
-        // scale copies, one per wave that owns 64 rows
-        if constexpr (SA_LDS) {
-            if (w < BM / 64) scale_copy<BM>(rsa, ks, lds0 + SQA_OFF);
+        if constexpr (SB_LDS) {
+            if (w < BN / 64) {
+                uint32_t off;
+                if constexpr (BPACK) off = (uint32_t)(ks * kScaleStepBytes + w * 256 + lane * 4);
+                else off = (uint32_t)((w * 64 + lane) * KBi + ks * 4);
+                dma4(rsb, off, sbase + SB_OFF + w * 256);
+            }
         }
-        if constexpr (SB_CANON) {
-            if (w < BN / 64) scale_copy<BN>(rsb, ks, lds0 + SQB_OFF);
-        }
-        if constexpr (BPACK) {
-            if (w < BN / 64)
-                dma4(rsb, (uint32_t)(ks * kScaleStepBytes + w * 256 + lane * 4), sbase + SB_OFF + w * 256);
-        }
-    }
-
-    // canonical scales of rows [64w, 64w+64) for k-step ks into its buffer:
-    // the four steps' 16 bytes at the first step of a group, or this step's
-    // dword when rows are not 16-byte aligned
-    template <int ROWS>
-    __device__ __forceinline__ void scale_copy(v4i r, int ks, uint32_t base) const {
-        const int rr = w * 64 + lane;
-        const uint32_t buf = base + ((ks >> 2) & 1) * (ROWS * 16);
-        if (quad) {
-            if ((ks & 3) == 0) dma16(r, (uint32_t)(rr * KBi + ks * 4), buf + w * 1024);
-        } else {
-            dma4(r, (uint32_t)(rr * KBi + ks * 4), buf + (ks & 3) * (ROWS * 4) + w * 256);
-        }
-    }
-
-    // byte (row, block 4ks + lblk) of a canonical scale buffer
-    template <int ROWS>
-    __device__ __forceinline__ int scale_at(int off, int ks, int row) const {
-        const uint8_t *buf = smem_p + off + ((ks >> 2) & 1) * (ROWS * 16);
-        const int j = ks & 3;
-        return quad ? buf[row * 16 + j * 4 + lblk] : buf[j * (ROWS * 4) + row * 4 + lblk];
     }
 
     // K % 128 != 0: scale bytes by compiler-visible loads (K tail reads 0)
@@ -340,34 +283,33 @@ struct TileOps {
     }
 
     // scale bytes of one step from LDS (the MFMA reads bits [7:0], op_sel 0)
-    __device__ __forceinline__ void lds_scales(const uint8_t *st, int ks, int *sas, int *sbs) const {
+    __device__ __forceinline__ void lds_scales(const uint8_t *st, int *sas, int *sbs) const {
         if constexpr (SA_LDS) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) sas[i] = scale_at<BM>(SQA_OFF, ks, wm * WTM + i * 16 + lrow);
+            for (int i = 0; i < FM; ++i) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
         }
         if constexpr (SB_LDS) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 if constexpr (BPACK) sbs[j] = st[SB_OFF + (wn * FN + j) * 64 + lane];
-                else sbs[j] = scale_at<BN>(SQB_OFF, ks, wn * WTN + j * 16 + lrow);
+                else sbs[j] = st[SB_OFF + (wn * WTN + j * 16 + lrow) * 4 + lblk];
             }
         }
     }
 
     __device__ __forceinline__ void lds_bfrags(const uint8_t *st, v8i *bf) const {
+        const uint8_t *sb = st + BM * 128 + wn * WTN * 128;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            if constexpr (BPACK) bf[j] = lds_frag(st + A_BYTES + (wn * WTN + j * 16) * 128, lane);
-            else bf[j] = lds_frag_il(st + A_BYTES, wn * WTN + j * 16, lane);
-        }
+        for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sb + j * 16 * 128, lane);
     }
 
     // MFMAs of A rows [i0, i1) of one step against the B fragments in registers
     __device__ __forceinline__ void mma_rows(const uint8_t *st, int i0, int i1, const v8i *bf, const int *sas,
                              const int *sbs, v4f (*acc)[FN]) const {
+        const uint8_t *sa = st + wm * WTM * 128;
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
-            const v8i af = lds_frag_il(st, wm * WTM + i * 16, lane);
+            const v8i af = lds_frag(sa + i * 16 * 128, lane);
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -494,8 +436,8 @@ template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool 
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
     constexpr int FM = T::FM, FN = T::FN;
-    static_assert(T::LDS_TOTAL <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_TOTAL];
+    static_assert(2 * T::STAGE <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
     int64_t m0, m_end, n0, g;
     if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
     T t;
@@ -530,7 +472,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
         const uint8_t *st = smem + cur * T::STAGE;
         int sas[FM], sbs[FN];
-        t.lds_scales(st, ks, sas, sbs);
+        t.lds_scales(st, sas, sbs);
         if constexpr (!T::SA_LDS) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sas[i] = (int)(sa_cur[i] & 0xFFu);
