@@ -239,14 +239,33 @@ def bench_mlp(args, dev):
            "dgrad_gu": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
            "wgrad_d": torch.empty((H, I), dtype=torch.float32, device=dev),
            "wgrad_gu": torch.empty((I2, H), dtype=torch.float32, device=dev)}
-    ops = []
-    q_elts = {}
+    # unfused composition: every tensor quantized per axis, weights repacked
+    unfused = []
     for (name, ax), (q, sc) in Q.items():
         key = "quantize_%s_axis%d" % (name, ax)
-        ops.append((key, lambda x=t[name], a=ax, q=q, sc=sc: mx.quantize_into(x, a, q, sc)))
-        q_elts[key] = t[name].numel()
+        unfused.append((key, lambda x=t[name], a=ax, q=q, sc=sc: mx.quantize_into(x, a, q, sc)))
     for key, src in (("repack_gu", ("W_gu", 1)), ("repack_guT", ("W_gu", 0)),
                      ("repack_d", ("W_d", 1)), ("repack_dT", ("W_d", 0))):
+        pk = P[key.split("_", 1)[1]]
+        unfused.append((key, lambda q=Q[src][0], sc=Q[src][1], w=pk: mx.repack_(q, sc, w)))
+    # fused path (the step): activations and gradients quantized along both
+    # axes from one read; forward weights quantized straight into the packed
+    # layout; the transposed (data-gradient) weights quantized along N and
+    # repacked
+    ops = []
+    q_bytes = {}
+    for name in ("X", "h", "dY_gu", "dY_d"):
+        key = "quantize_dual_" + name
+        ops.append((key, lambda x=t[name], a=Q[name, 1], b=Q[name, 0]: mx.quantize_dual_into(x, a[0], a[1], b[0], b[1])))
+        q_bytes[key] = t[name].numel() * (2 + 2 * (1 + 1 / 32))
+    for name, pk in (("W_gu", "gu"), ("W_d", "d")):
+        key = "quantize_packed_" + name
+        ops.append((key, lambda x=t[name], w=P[pk]: mx.quantize_packed_(x, w)))
+        q_bytes[key] = t[name].numel() * Q_BYTES_PER_ELT
+        key = "quantize_%s_axis0" % name
+        ops.append((key, lambda x=t[name], q=Q[name, 0]: mx.quantize_into(x, 0, q[0], q[1])))
+        q_bytes[key] = t[name].numel() * Q_BYTES_PER_ELT
+    for key, src in (("repack_guT", ("W_gu", 0)), ("repack_dT", ("W_d", 0))):
         pk = P[key.split("_", 1)[1]]
         ops.append((key, lambda q=Q[src][0], sc=Q[src][1], w=pk: mx.repack_(q, sc, w)))
     gemms = {  # name: (A, B, M, N, K, out dtype)
@@ -261,28 +280,31 @@ def bench_mlp(args, dev):
         ops.append(("gemm_" + key, lambda A=A, B=B, dt=dt, o=out[key]: mx.gemm(A[0], A[1], B, dt, out=o)))
     torch.cuda.synchronize()
     ms, avg = run_timed(ops, args)
+    _, avg_unf = run_timed(unfused, argparse.Namespace(steps=max(2, args.steps // 2), warmup=1))
     flops = sum(2.0 * M * N * K for (_, _, M, N, K, _) in gemms.values())
     kern = {}
-    for key, n in q_elts.items():
-        kern[key] = _bw(avg[key], n * Q_BYTES_PER_ELT)
-    for key, src in (("repack_gu", (I2, H)), ("repack_guT", (H, I2)), ("repack_d", (H, I)), ("repack_dT", (I, H))):
+    for key, nbytes in q_bytes.items():
+        kern[key] = _bw(avg[key], nbytes)
+    for key, src in (("repack_guT", (H, I2)), ("repack_dT", (I, H))):
         kern[key] = _bw(avg[key], src[0] * src[1] * REPACK_BYTES_PER_ELT)
     for key, (_, _, M, N, K, _) in gemms.items():
         kern["gemm_" + key] = _gemm_rate(avg["gemm_" + key], M, N, K)
     gemm_us = sum(avg["gemm_" + k] for k in gemms)
-    quant_us = sum(avg[k] for k in q_elts)
+    quant_us = sum(avg[k] for k in avg if not k.startswith("gemm_"))
+    unfused_us = sum(avg_unf.values())
     top = kern["gemm_fprop_gu"]
     return _line("MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",
                  round(flops / (ms * 1e-3) / 1e12, 2), "TFLOP/s", args, ms,
                  "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out (fprop/dgrad), fp32 out (wgrad)",
-                 {"workload": "qwen3-8b MLP learner micro-batch, 8192 tokens: weight quantize (2 axes) "
-                              "+ repack, activation/gradient quantize (2 axes), 6 GEMMs",
+                 {"workload": "qwen3-8b MLP learner micro-batch, 8192 tokens: activation/gradient quantize "
+                              "(both axes, one read each), weight quantize (packed along K; along N + repack), "
+                              "6 GEMMs",
                   "tokens": T, "hidden": H, "inter": I},
                  kernels=kern,
                  summary={"gemm_us": round(gemm_us, 1),
                           "gemm_TFLOP/s": round(flops / (gemm_us * 1e-6) / 1e12, 1),
-                          "quantize_us": round(quant_us, 1),
-                          "quantize_GB/s": round(sum(q_elts.values()) * Q_BYTES_PER_ELT / (quant_us * 1e-6) / 1e9, 1)},
+                          "quantize_and_layout_us": round(quant_us, 1),
+                          "unfused_quantize_and_layout_us": round(unfused_us, 1)},
                  roofline={"bound": "mfma", "achieved": top["TFLOP/s"], "peak": MXFP8_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": top["frac_mxfp8_peak"], "traffic": None,
                            "kernel": "gemm fprop gate_up 8192x24576x4096"})
@@ -390,48 +412,58 @@ def bench_sync(args, dev):
                                  torch.empty(mx.packed_bytes(1, N, K, 1), dtype=torch.uint8, device=dev), 1, N, K)
             tensors.append((name, W, q, sc, pk))
     n_elts = sum(W.numel() for _, W, _, _, _ in tensors)
-    ops = []
+    # the sync: every weight quantized along K into its canonical grid (what a
+    # learner sends) and the GEMM's packed layout (what the sampler's graphs
+    # read) in one pass per weight
+    ops = [("quantize_packed_" + name, lambda W=W, q=q, sc=sc, pk=pk: mx.quantize_packed_(W, pk, q, sc))
+           for name, W, q, sc, pk in tensors]
+    # the same result by quantize + repack, for comparison
+    unfused = []
     for name, W, q, sc, pk in tensors:
-        ops.append(("quantize_" + name, lambda W=W, q=q, sc=sc: mx.quantize_into(W, 1, q, sc)))
-        ops.append(("repack_" + name, lambda q=q, sc=sc, pk=pk: mx.repack_(q, sc, pk)))
+        unfused.append(("quantize_" + name, lambda W=W, q=q, sc=sc: mx.quantize_into(W, 1, q, sc)))
+        unfused.append(("repack_" + name, lambda q=q, sc=sc, pk=pk: mx.repack_(q, sc, pk)))
     torch.cuda.synchronize()
-    # eager: one host launch per call (host-bound: 288 launches per sync)
+    # eager: one host launch per call (host-bound: 144 launches per sync)
     eager_ms, avg = run_timed(ops, argparse.Namespace(steps=max(2, args.steps // 5), warmup=1))
-    # captured: the 288 launches recorded once into a HIP graph and replayed,
-    # as a sampler replays its captured graphs after writing weights in place
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _, fn in ops:
-            fn()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = 1e3 * (time.perf_counter() - t0) / args.steps
-    gpu_ms = e0.elapsed_time(e1) / args.steps
-    by_q = n_elts * Q_BYTES_PER_ELT
-    by_r = n_elts * REPACK_BYTES_PER_ELT
+
+    def replayed(oplist, steps):
+        # recorded once into a HIP graph and replayed, as a sampler replays its
+        # captured graphs after writing weights in place
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _, fn in oplist:
+                fn()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / steps, e0.elapsed_time(e1) / steps
+
+    ms, gpu_ms = replayed(ops, args.steps)
+    unf_ms, unf_gpu_ms = replayed(unfused, max(2, args.steps // 2))
+    alg = n_elts * (2 + 2 * (1 + 1 / 32))          # bf16 in; canonical + packed out
     kern = {}
     for name, N, K in wl.sync_layer_shapes():
-        kern["quantize_" + name] = _bw(avg["quantize_" + name], N * K * Q_BYTES_PER_ELT)
-        kern["repack_" + name] = _bw(avg["repack_" + name], N * K * REPACK_BYTES_PER_ELT)
-    gbs = (by_q + by_r) / (ms * 1e-3) / 1e9
+        kern["quantize_packed_" + name] = _bw(avg["quantize_packed_" + name], N * K * (2 + 2 * (1 + 1 / 32)))
+    gbs = alg / (ms * 1e-3) / 1e9
     return _line("weight sync GB/s (% HBM): quantize + repack of all Qwen3-8B linears",
                  round(gbs, 1), "GB/s", args, ms, "bf16 -> mxfp8-e4m3/e8m0",
-                 {"workload": "qwen3-8b weight sync: quantize along K + repack of 144 linears "
-                              "(36 layers x qkv, o, gate_up, down), replayed as one HIP graph",
+                 {"workload": "qwen3-8b weight sync: every linear (36 layers x qkv, o, gate_up, down) quantized "
+                              "along K into its canonical grid and the packed GEMM layout in one pass, "
+                              "replayed as one HIP graph",
                   "elements": n_elts},
                  kernels=kern, kernels_note="per-call HIP-event times from the eager run (they include "
                                             "host launch gaps when the host falls behind)",
-                 summary={"quantize_GB": round(by_q / 1e9, 2), "repack_GB": round(by_r / 1e9, 2),
-                          "graph_gpu_ms": round(gpu_ms, 3), "eager_ms_per_sync": round(eager_ms, 3),
-                          "eager_GB/s": round((by_q + by_r) / (eager_ms * 1e-3) / 1e9, 1),
+                 summary={"algorithmic_GB": round(alg / 1e9, 2), "graph_gpu_ms": round(gpu_ms, 3),
+                          "eager_ms_per_sync": round(eager_ms, 3),
+                          "unfused_quantize_then_repack_ms": round(unf_ms, 3),
+                          "unfused_GB_moved": round(n_elts * (Q_BYTES_PER_ELT + REPACK_BYTES_PER_ELT) / 1e9, 2),
                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
                  roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,

@@ -82,6 +82,51 @@ mxfp8_status mxfp8_quantize(const void *x_bf16, int64_t rows, int64_t cols,
                             hipStream_t stream);
 
 /*
+ * mxfp8_quantize_dual -- one BF16 read, both operand grids of a learner tensor.
+ *
+ * The learner quantizes the operands of each linear layer's three GEMMs on
+ * the fly, and because the weight-gradient GEMM reduces over tokens some
+ * operands are blocked along tokens ("The pipeline", learner paragraph); the
+ * page counts the activation and gradient quantize launches per micro-batch
+ * among its added costs (section "Speed: when it pays off", "Where the time
+ * goes").  An activation or gradient feeds one GEMM blocked along its columns
+ * and another blocked along its rows; this call writes both from a single
+ * read (4.0625 instead of 6.0625 HBM bytes per element).
+ *
+ * Result: byte-for-byte mxfp8_quantize(x, axis=1) into (q_row, s_row) and
+ * mxfp8_quantize(x, axis=0) into (q_col, s_col):
+ *   q_row[rows][cols], s_row[rows][cols/32], q_col[cols][rows], s_col[cols][rows/32].
+ * rows % 32 == 0, cols % 32 == 0, rows, cols >= 32.  Bit-exact, deterministic.
+ */
+mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols,
+                                 uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
+                                 uint8_t *s_col, hipStream_t stream);
+
+/*
+ * mxfp8_quantize_packed -- weights BF16 -> MXFP8 straight into the GEMM's
+ * packed layout, optionally also the canonical grid.
+ *
+ * The weight synchronization passes every weight through the learner's
+ * forward-weight quantizer, and the sampler then rebuilds its kernel layouts
+ * from the result ("The pipeline", weight-synchronization and sampler
+ * paragraphs; writing cached weights' scales directly in the GEMM's layout is
+ * the remedy the page notes under "Speed: when it pays off", "Where the time
+ * goes").  This call is quantize(axis 1) followed by repack in one pass:
+ *   q_packed / scales_packed: exactly what mxfp8_repack writes for the
+ *     canonical result (sizes from mxfp8_packed_bytes);
+ *   q / scales (both NULL or both given): exactly mxfp8_quantize(w, axis=1),
+ *     q[batch][rows][cols], scales[batch][rows][cols/32].
+ * w is BF16 [batch][rows=N][cols=K]; the limits of mxfp8_repack apply.
+ * HBM bytes per element: 3.03125 packed only, 4.0625 with the canonical grid
+ * (quantize + repack: 5.09375).  Bit-exact, deterministic; writes in place,
+ * so graph-captured pointers stay valid.
+ */
+mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t rows,
+                                   int64_t cols, uint8_t *q, uint8_t *scales,
+                                   uint8_t *q_packed, uint8_t *scales_packed,
+                                   hipStream_t stream);
+
+/*
  * mxfp8_dequantize -- MXFP8 -> FP32 or BF16:  out = decode(q) * 2^(code-127).
  *
  * The high-precision reference that the page's post-sync self-check compares

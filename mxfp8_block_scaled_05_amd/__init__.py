@@ -55,8 +55,10 @@ def lib():
         L.mxfp8_repack.argtypes = [P, P, I64, I64, I64, P, P, P]
         L.mxfp8_gemm.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
         L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        L.mxfp8_quantize_dual.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
-                  "mxfp8_grouped_gemm"):
+                  "mxfp8_grouped_gemm", "mxfp8_quantize_dual", "mxfp8_quantize_packed"):
             getattr(L, f).restype = I32
         L.mxfp8_status_string.argtypes = [I32]
         L.mxfp8_status_string.restype = ctypes.c_char_p
@@ -140,6 +142,40 @@ def quantize(x: torch.Tensor, axis: int = 1):
     return q, s
 
 
+def quantize_dual_into(x: torch.Tensor, q_row: torch.Tensor, s_row: torch.Tensor,
+                       q_col: torch.Tensor, s_col: torch.Tensor) -> None:
+    """Both grids of x from one read: (q_row, s_row) = quantize(x, 1),
+    (q_col, s_col) = quantize(x, 0)."""
+    _need(x, torch.bfloat16, "x")
+    for t, n in ((q_row, "q_row"), (s_row, "s_row"), (q_col, "q_col"), (s_col, "s_col")):
+        _need(t, torch.uint8, n)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if rows % 32 or cols % 32:
+        raise ValueError("rows and cols must be multiples of 32")
+    want = ((rows, cols), (rows, cols // 32), (cols, rows), (cols, rows // 32))
+    got = tuple(tuple(t.shape) for t in (q_row, s_row, q_col, s_col))
+    if got != want:
+        raise ValueError("output shapes %s, expected %s" % (got, want))
+    _check(lib().mxfp8_quantize_dual(_ptr(x), rows, cols, _ptr(q_row), _ptr(s_row), _ptr(q_col),
+                                     _ptr(s_col), _stream(x.device)), "mxfp8_quantize_dual")
+
+
+def quantize_dual(x: torch.Tensor):
+    """BF16 [rows, cols] -> (q_row, s_row, q_col, s_col), the axis-1 and the
+    (transposed) axis-0 grids, from one read of x."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    out = (torch.empty((rows, cols), dtype=torch.uint8, device=x.device),
+           torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device),
+           torch.empty((cols, rows), dtype=torch.uint8, device=x.device),
+           torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device))
+    quantize_dual_into(x, *out)
+    return out
+
+
 def dequantize(q: torch.Tensor, s: torch.Tensor, rows: int, cols: int, axis: int = 1,
                dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
     _need(q, torch.uint8, "q")
@@ -201,6 +237,55 @@ def repack(q: torch.Tensor, s: torch.Tensor) -> PackedWeight:
     w = PackedWeight(torch.empty(nq, dtype=torch.uint8, device=q.device),
                      torch.empty(ns, dtype=torch.uint8, device=q.device), batch, N, K)
     return repack_(q, s, w)
+
+
+def quantize_packed_(w_bf16: torch.Tensor, out: PackedWeight, q: torch.Tensor | None = None,
+                     s: torch.Tensor | None = None) -> PackedWeight:
+    """Quantize weights [(batch,) N, K] along K straight into out's packed
+    storage (in place), and into the canonical (q, s) as well if given."""
+    _need(w_bf16, torch.bfloat16, "w")
+    _need(out.q, torch.uint8, "q_packed")
+    _need(out.s, torch.uint8, "scales_packed")
+    if w_bf16.numel() != out.batch * out.N * out.K:
+        raise ValueError("weights do not match the packed weight's shape")
+    if out.q.numel() < packed_bytes(out.batch, out.N, out.K, 0) or \
+            out.s.numel() < packed_bytes(out.batch, out.N, out.K, 1):
+        raise ValueError("packed buffers too small")
+    if (q is None) != (s is None):
+        raise ValueError("give both canonical q and scales, or neither")
+    if q is not None:
+        _need(q, torch.uint8, "q")
+        _need(s, torch.uint8, "scales")
+        if q.numel() != w_bf16.numel() or s.numel() != w_bf16.numel() // 32:
+            raise ValueError("canonical q/scales have the wrong size")
+    _check(lib().mxfp8_quantize_packed(_ptr(w_bf16), out.batch, out.N, out.K,
+                                       _ptr(q) if q is not None else None,
+                                       _ptr(s) if s is not None else None,
+                                       _ptr(out.q), _ptr(out.s), _stream(w_bf16.device)),
+           "mxfp8_quantize_packed")
+    return out
+
+
+def quantize_packed(w_bf16: torch.Tensor, canonical: bool = True):
+    """Weights [(batch,) N, K] -> (PackedWeight, q, s) in one pass; q and s
+    (the canonical grid) are None when canonical is False."""
+    if w_bf16.dim() == 2:
+        batch, (N, K) = 1, w_bf16.shape
+    elif w_bf16.dim() == 3:
+        batch, N, K = w_bf16.shape
+    else:
+        raise ValueError("weights must be [N, K] or [batch, N, K]")
+    nq, ns = packed_bytes(batch, N, K, 0), packed_bytes(batch, N, K, 1)
+    if nq == 0:
+        raise ValueError("invalid weight shape for packing")
+    out = PackedWeight(torch.empty(nq, dtype=torch.uint8, device=w_bf16.device),
+                       torch.empty(ns, dtype=torch.uint8, device=w_bf16.device), batch, N, K)
+    q = s = None
+    if canonical:
+        q = torch.empty(tuple(w_bf16.shape), dtype=torch.uint8, device=w_bf16.device)
+        s = torch.empty(tuple(w_bf16.shape[:-1]) + (K // 32,), dtype=torch.uint8, device=w_bf16.device)
+    quantize_packed_(w_bf16, out, q, s)
+    return out, q, s
 
 
 # ------------------------------------------------------------------ GEMMs

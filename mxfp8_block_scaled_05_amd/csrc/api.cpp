@@ -80,6 +80,12 @@ mxfp8_status finish(hipError_t e) {
     return MXFP8_OK;
 }
 
+// the axis-0 and dual quantizers run one workgroup per 128x128 tile on a
+// one-dimensional grid
+bool tile128_ok(int64_t rows, int64_t cols) {
+    return ((rows + 127) / 128) * ((cols + 127) / 128) <= 0x7FFFFFFF;
+}
+
 // repack runs one workgroup of 256 threads per (matrix, panel, k-step) tile on
 // a one-dimensional grid: keep the thread count below 2^32
 bool repack_tiles_ok(int64_t batch, int64_t rows, int64_t cols) {
@@ -114,13 +120,44 @@ mxfp8_status mxfp8_quantize(const void *x_bf16, int64_t rows, int64_t cols, int 
     if (axis != 0 && axis != 1) return MXFP8_ERR_AXIS;
     if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim) return MXFP8_ERR_SHAPE;
     if (axis == 1 && cols % 32) return MXFP8_ERR_SHAPE;
-    if (axis == 0 && (rows % 32 || (cols + 127) / 128 > 0x7FFFFFFF || (rows + 127) / 128 > 65535))
-        return MXFP8_ERR_SHAPE;
-    if (!aligned16(x_bf16) || !aligned16(q)) return MXFP8_ERR_ALIGN;
+    if (axis == 0 && (rows % 32 || !tile128_ok(rows, cols))) return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q) || !aligned16(scales)) return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
     return finish(launch_quantize(static_cast<const uint16_t *>(x_bf16), rows, cols, axis, q,
                                   scales, stream));
+}
+
+mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, uint8_t *q_row,
+                                 uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                                 hipStream_t stream) {
+    if (!x_bf16 || !q_row || !s_row || !q_col || !s_col) return MXFP8_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (rows % 32 || cols % 32 || !tile128_ok(rows, cols)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q_row) || !aligned16(s_row) || !aligned16(q_col) ||
+        !aligned16(s_col))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_dual(static_cast<const uint16_t *>(x_bf16), rows, cols, q_row,
+                                       s_row, q_col, s_col, stream));
+}
+
+mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols,
+                                   uint8_t *q, uint8_t *scales, uint8_t *q_packed,
+                                   uint8_t *scales_packed, hipStream_t stream) {
+    if (!w_bf16 || !q_packed || !scales_packed) return MXFP8_ERR_NULL;
+    if ((q == nullptr) != (scales == nullptr)) return MXFP8_ERR_NULL;
+    if (batch <= 0 || rows <= 0 || cols <= 0 || cols % 32) return MXFP8_ERR_SHAPE;
+    if (rows >= kMaxDim || cols > kMaxK || batch > 65535 || !repack_tiles_ok(batch, rows, cols))
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(w_bf16) || !aligned16(q_packed) || !aligned16(scales_packed) ||
+        (q && (!aligned16(q) || !aligned16(scales))))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_packed(static_cast<const uint16_t *>(w_bf16), batch, rows, cols,
+                                         q, scales, q_packed, scales_packed, stream));
 }
 
 mxfp8_status mxfp8_dequantize(const uint8_t *q, const uint8_t *scales, int64_t rows, int64_t cols,

@@ -14,6 +14,14 @@ int device_cu_count();
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint8_t *q,
                            uint8_t *scales, hipStream_t stream);
 
+hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
+                                uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream);
+
+// q / scales may be null (packed output only)
+hipError_t launch_quantize_packed(const uint16_t *w, int64_t batch, int64_t N, int64_t K,
+                                  uint8_t *q, uint8_t *scales, uint8_t *q_packed,
+                                  uint8_t *s_packed, hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t *q, const uint8_t *scales, int64_t rows, int64_t cols,
                              int axis, void *out, bool out_bf16, hipStream_t stream);
 

@@ -17,6 +17,8 @@
 //    128-row x 128-column tile and transposes it through LDS, so global loads
 //    are 16-byte row reads and global stores whole 128-byte output lines;
 //    each lane reduces and converts its column's block in registers.
+//  - both axes from one read (learner tensors), and weights quantized straight
+//    into the GEMM's packed layout (weight sync), share the LDS tile code.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
@@ -129,57 +131,85 @@ __global__ __launch_bounds__(256) void quantize_axis1_kernel(const uint16_t *__r
     }
 }
 
-// ---------------------------------------------------------------- axis 0
-// x[rows][cols] -> q[cols][rows], scales[cols][rows/32].  A workgroup of four
-// waves owns a 128-row x 128-column tile and moves it through LDS twice:
-//   1. the BF16 tile is read with 16-byte row loads into LDS (row-major),
-//   2. wave w takes rows [32w, 32w+32), lane l the column pair (2l, 2l+1): it
-//      reads its two 32-element blocks as 32 dwords (one 256-byte LDS row per
-//      wave read, conflict-free) and quantizes them in registers,
-//   3. the E4M3 tile is written back to the same LDS as [128 columns][128 B]
-//      (padded rows) and stored to q as whole 128-byte lines.
-constexpr int kA0Tile = 128;
-constexpr int kA0OutPitch = 144;  // bytes per staged output column (16-byte aligned)
+// ---------------------------------------------------------------- tiles in LDS
+// A 128-column BF16 tile in LDS: row r (256 B) holds its 16-byte chunk c at
+// slot c ^ (r % 16).  Column-pair dword reads (64 lanes over one row) and
+// block reads (a lane reads chunks 4b..4b+3 of its own row, 16 lanes over 4
+// rows x 4 blocks or 16 rows x 1 block) both hit 16 distinct chunk slots, so
+// neither has bank conflicts.
+__device__ __forceinline__ int tile_slot(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
-__global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__restrict__ x,
-                                                             uint8_t *__restrict__ q,
-                                                             uint8_t *__restrict__ scales,
-                                                             int64_t rows, int64_t cols) {
-    __shared__ __attribute__((aligned(16))) uint32_t tile[kA0Tile * kA0Tile / 2];
-    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
-    static_assert(kA0Tile * kA0OutPitch <= (int)sizeof(tile), "output stage fits the input stage");
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int64_t R0 = (int64_t)blockIdx.y * kA0Tile, C0 = (int64_t)blockIdx.x * kA0Tile;
-
+// BF16 rows [R0, R0 + nrows) x columns [C0, C0 + 128) of x[rows][cols] into the
+// tile (zeros outside the matrix).  256 threads.
+template <int NROWS>
+__device__ __forceinline__ void load_tile(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                                          int64_t R0, int64_t C0, uint8_t *tile, int t) {
     if ((cols & 7) == 0) {
         // rows are 16-byte aligned: sixteen 16-byte chunks per tile row
         const int ch = t & 15;
         const int64_t c = C0 + ch * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NROWS / 16; ++i) {
             const int r = i * 16 + (t >> 4);
             v4i v = v4i{0, 0, 0, 0};
-            if (R0 + r < rows && c < cols)
-                v = *reinterpret_cast<const v4i *>(x + (R0 + r) * cols + c);
-            *reinterpret_cast<v4i *>(&tile[r * 64 + ch * 4]) = v;
+            if (R0 + r < rows && c < cols) v = *reinterpret_cast<const v4i *>(x + (R0 + r) * cols + c);
+            *reinterpret_cast<v4i *>(tile + tile_slot(r, ch)) = v;
         }
     } else {
-        for (int i = t; i < kA0Tile * 64; i += 256) {
-            const int r = i >> 6;
-            const int64_t row = R0 + r, c = C0 + 2 * (i & 63);
+        for (int i = t; i < NROWS * 64; i += 256) {
+            const int r = i >> 6, cp = i & 63;
+            const int64_t row = R0 + r, c = C0 + 2 * cp;
             uint32_t v = 0;
             if (row < rows) {
                 if (c < cols) v = x[row * cols + c];
                 if (c + 1 < cols) v |= (uint32_t)x[row * cols + c + 1] << 16;
             }
-            tile[i] = v;
+            *reinterpret_cast<uint32_t *>(tile + tile_slot(r, cp >> 2) + (cp & 3) * 4) = v;
         }
     }
-    __syncthreads();
+}
 
+// Quantize block b (columns 32b .. 32b+31) of tile row r: scale code and the
+// 32 E4M3 bytes as 8 dwords (NaN/Inf blocks: code 0xFF, elements 0x7F).
+__device__ __forceinline__ uint32_t quantize_row_block(const uint8_t *tile, int r, int b, uint32_t *q8) {
+    uint32_t d[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const v4i v = *reinterpret_cast<const v4i *>(tile + tile_slot(r, 4 * b + j));
+        d[4 * j] = v.x; d[4 * j + 1] = v.y; d[4 * j + 2] = v.z; d[4 * j + 3] = v.w;
+    }
+    const uint32_t code = scale_code_from_amax_bits(max_mag(d, 16));
+    const float inv = inv_scale_from_code(code);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const v2i o = convert8(d + 4 * j, inv);
+        q8[2 * j] = code == 255u ? 0x7F7F7F7Fu : (uint32_t)o.x;
+        q8[2 * j + 1] = code == 255u ? 0x7F7F7F7Fu : (uint32_t)o.y;
+    }
+    return code;
+}
+
+// ---------------------------------------------------------------- axis 0
+// x[rows][cols] -> q[cols][rows], scales[cols][rows/32].  A workgroup of four
+// waves owns a 128-row x 128-column tile and moves it through LDS twice:
+//   1. the BF16 tile is read with 16-byte row loads into LDS,
+//   2. wave w takes rows [32w, 32w+32), lane l the column pair (2l, 2l+1): it
+//      reads its two 32-element blocks as 32 dwords and quantizes them in
+//      registers,
+//   3. the E4M3 tile is written back to the same LDS as [128 columns][128 B]
+//      (padded rows) and stored to q as whole 128-byte lines.
+constexpr int kA0Tile = 128;
+constexpr int kA0OutPitch = 144;  // bytes per staged output column (16-byte aligned)
+
+// Steps 2 and 3 for one tile already in LDS (`tile`, reused for the output).
+__device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, uint8_t *__restrict__ q,
+                                                uint8_t *__restrict__ scales, int64_t rows, int64_t cols,
+                                                int64_t R0, int64_t C0, int t) {
+    const int lane = t & 63, w = t >> 6;
     uint32_t d[32];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) d[r] = tile[(32 * w + r) * 64 + lane];
+    for (int r = 0; r < 32; ++r)
+        d[r] = *reinterpret_cast<const uint32_t *>(tile + tile_slot(32 * w + r, lane >> 2) + (lane & 3) * 4);
     __syncthreads();  // the tile is reused for the output below
 
     us2 m = as_us2(d[0] & 0x7FFF7FFFu);
@@ -189,7 +219,7 @@ __global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__r
     const uint32_t code_hi = scale_code_from_amax_bits(m.y);
     const float inv_lo = inv_scale_from_code(code_lo);
     const float inv_hi = inv_scale_from_code(code_hi);
-    uint8_t *ob = reinterpret_cast<uint8_t *>(tile);
+    uint8_t *ob = tile;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         int wl[4], wh[4];
@@ -240,6 +270,149 @@ __global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__r
     }
 }
 
+// one workgroup per tile; tiles numbered row-tile-major over a 1-D grid
+__device__ __forceinline__ void tile_origin(int64_t cols, int64_t &R0, int64_t &C0) {
+    const int64_t tiles_c = (cols + kA0Tile - 1) / kA0Tile;
+    R0 = (int64_t)(blockIdx.x / tiles_c) * kA0Tile;
+    C0 = (int64_t)(blockIdx.x % tiles_c) * kA0Tile;
+}
+
+__global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__restrict__ x,
+                                                             uint8_t *__restrict__ q,
+                                                             uint8_t *__restrict__ scales,
+                                                             int64_t rows, int64_t cols) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    static_assert(kA0Tile * kA0OutPitch <= (int)sizeof(tile), "output stage fits the input stage");
+    int64_t R0, C0;
+    tile_origin(cols, R0, C0);
+    load_tile<kA0Tile>(x, rows, cols, R0, C0, tile, threadIdx.x);
+    __syncthreads();
+    axis0_from_tile(tile, stile, q, scales, rows, cols, R0, C0, threadIdx.x);
+}
+
+// ---------------------------------------------------------------- both axes
+// One BF16 read, both operand grids of a learner tensor (rows % 32 == 0 and
+// cols % 32 == 0): the tile in LDS is first quantized along its rows (axis 1:
+// 512 blocks, two per thread, each lane's 32 output bytes part of a 128-byte
+// row segment), then along its columns exactly as the axis-0 kernel does.
+// 4.0625 algorithmic bytes per element instead of 2 x 3.03125.
+__global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t *__restrict__ x,
+                                                            uint8_t *__restrict__ q_row,
+                                                            uint8_t *__restrict__ s_row,
+                                                            uint8_t *__restrict__ q_col,
+                                                            uint8_t *__restrict__ s_col,
+                                                            int64_t rows, int64_t cols) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    const int t = threadIdx.x;
+    int64_t R0, C0;
+    tile_origin(cols, R0, C0);
+    load_tile<kA0Tile>(x, rows, cols, R0, C0, tile, t);
+    __syncthreads();
+    const int64_t nb = cols / 32;
+#pragma unroll
+    for (int u2 = 0; u2 < 2; ++u2) {
+        const int u = u2 * 256 + t, r = u >> 2, b = u & 3;
+        uint32_t q8[8];
+        const uint32_t code = quantize_row_block(tile, r, b, q8);
+        const int64_t row = R0 + r, c = C0 + 32 * b;
+        if (row < rows && c < cols) {
+            v4i *dst = reinterpret_cast<v4i *>(q_row + row * cols + c);
+            dst[0] = v4i{(int)q8[0], (int)q8[1], (int)q8[2], (int)q8[3]};
+            dst[1] = v4i{(int)q8[4], (int)q8[5], (int)q8[6], (int)q8[7]};
+            s_row[row * nb + c / 32] = (uint8_t)code;
+        }
+    }
+    axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
+}
+
+// ---------------------------------------------------------------- weights -> packed
+// Axis-1 quantization of weights [batch][N][K] written straight into the
+// GEMM's packed layout (and, if q/scales are given, the canonical grid too):
+// one workgroup per (k-step, panel) tile of 256 rows x 128 columns.  Eight
+// lanes share a row, lane l owning its 16-element output chunk l % 8 (half a
+// 32-block; the block max is completed across the lane pair with one DPP
+// swap).  A wave loads its 8 row-groups (8 rows x 256 B each) into registers
+// up front, then converts them, so its packed stores are 8 consecutive tile
+// rows = one contiguous 1 KB and its canonical stores whole 128-byte row
+// segments.  The tile's scale bytes are transposed through LDS into the
+// per-lane packed order.  Rows past N and blocks past K/32 hold element 0 and
+// scale 127, as repack writes them.
+__device__ __forceinline__ int64_t xcd_contiguous_tile(int64_t wg, int64_t nwg) {
+    const int64_t q = nwg / 8, r = nwg % 8, x = wg % 8;
+    return x * q + (x < r ? x : r) + wg / 8;
+}
+
+__global__ __launch_bounds__(256) void quantize_packed_kernel(const uint16_t *__restrict__ w,
+                                                              uint8_t *__restrict__ qc,
+                                                              uint8_t *__restrict__ sc,
+                                                              uint8_t *__restrict__ qp,
+                                                              uint32_t *__restrict__ sp, int64_t N,
+                                                              int64_t K, int64_t KS, int64_t NP) {
+    __shared__ uint32_t codes[kPanelRows];     // [row][block] bytes
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int64_t tidx = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+    const int64_t ks = tidx % KS, panel = (tidx / KS) % NP, b = tidx / (KS * NP);
+    const int64_t tile_lin = (b * NP + panel) * KS + ks;
+    const int64_t KB = K / 32;
+    const int c = lane & 7, blk = c >> 1;
+    const int64_t kb = ks * 4 + blk;
+    const int64_t k = ks * kKStep + 16 * c;
+    constexpr int IT = kPanelRows / 32;        // row-groups per wave
+
+    v4i dl[IT], dh[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int r = (it * 4 + wv) * 8 + (lane >> 3);
+        const int64_t n = panel * kPanelRows + r;
+        dl[it] = dh[it] = v4i{0, 0, 0, 0};
+        if (n < N && k < K) {
+            const uint16_t *src = w + (b * N + n) * K + k;
+            dl[it] = *reinterpret_cast<const v4i *>(src);
+            dh[it] = *reinterpret_cast<const v4i *>(src + 8);
+        }
+    }
+
+    uint8_t *code_bytes = reinterpret_cast<uint8_t *>(codes);
+    uint8_t *qtile = qp + tile_lin * kTileBytes;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int r = (it * 4 + wv) * 8 + (lane >> 3);
+        const uint32_t d[8] = {(uint32_t)dl[it].x, (uint32_t)dl[it].y, (uint32_t)dl[it].z, (uint32_t)dl[it].w,
+                               (uint32_t)dh[it].x, (uint32_t)dh[it].y, (uint32_t)dh[it].z, (uint32_t)dh[it].w};
+        uint32_t m = max_mag(d, 8);
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadSwap1, 0xF, 0xF, false));
+        uint32_t code = scale_code_from_amax_bits(m);
+        const int64_t n = panel * kPanelRows + r;
+        const bool valid = n < N && kb < KB;
+        v4i out;
+        if (!valid) {
+            code = 127u;
+            out = v4i{0, 0, 0, 0};
+        } else if (code == 255u) {
+            out = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+        } else {
+            const float inv = inv_scale_from_code(code);
+            const v2i o0 = convert8(d, inv), o1 = convert8(d + 4, inv);
+            out = v4i{o0.x, o0.y, o1.x, o1.y};
+        }
+        *reinterpret_cast<v4i *>(qtile + r * 128 + ((c ^ (int)swz((uint32_t)r)) << 4)) = out;
+        if (qc && valid) {
+            *reinterpret_cast<v4i *>(qc + (b * N + n) * K + k) = out;
+            if ((c & 1) == 0) sc[(b * N + n) * KB + kb] = (uint8_t)code;
+        }
+        if ((c & 1) == 0) code_bytes[r * 4 + blk] = (uint8_t)code;
+    }
+    __syncthreads();
+    // output word t: rows 16 (t/16) + 4 (t%4) .. +3 of block 4ks + (t/4)%4
+    const int row0 = 16 * (t >> 4) + 4 * (t & 3), j = (t >> 2) & 3;
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o |= (uint32_t)code_bytes[(row0 + i) * 4 + j] << (8 * i);
+    sp[tile_lin * (kScaleStepBytes / 4) + t] = o;
+}
+
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint8_t *q,
                            uint8_t *scales, hipStream_t stream) {
     if (axis == 1) {
@@ -253,11 +426,28 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int ax
         hipLaunchKernelGGL(quantize_axis1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, q,
                            scales, nblocks);
     } else {
-        dim3 grid((unsigned)((cols + kA0Tile - 1) / kA0Tile),
-                  (unsigned)((rows + kA0Tile - 1) / kA0Tile));
-        hipLaunchKernelGGL(quantize_axis0_kernel, grid, dim3(256), 0, stream, x, q, scales, rows,
-                           cols);
+        const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
+        hipLaunchKernelGGL(quantize_axis0_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x,
+                           q, scales, rows, cols);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
+                                uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream) {
+    const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
+    hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,
+                       s_row, q_col, s_col, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_packed(const uint16_t *w, int64_t batch, int64_t N, int64_t K,
+                                  uint8_t *q, uint8_t *scales, uint8_t *q_packed,
+                                  uint8_t *s_packed, hipStream_t stream) {
+    const int64_t NP = packed_panels(N), KS = packed_ksteps(K);
+    hipLaunchKernelGGL(quantize_packed_kernel, dim3((unsigned)(batch * NP * KS)), dim3(256), 0,
+                       stream, w, q, scales, q_packed, reinterpret_cast<uint32_t *>(s_packed), N,
+                       K, KS, NP);
     return hipGetLastError();
 }
 

@@ -67,3 +67,13 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_grouped_gemm(p, p, p, p, p, 2, 48, 4, 64, p, 0, NULL) == 2   # M_total % 32
     assert libmx.mxfp8_dequantize(p, p, 4, 32, 1, p, 5, NULL) == 4
     assert libmx.mxfp8_repack(p, p, 1, 4, 40, p, p, NULL) == 2
+    # fused quantizers
+    assert libmx.mxfp8_quantize_dual(p, 64, 64, p, p, NULL, p, NULL) == 1          # NULL output
+    assert libmx.mxfp8_quantize_dual(p, 48, 64, p, p, p, p, NULL) == 2             # rows % 32
+    assert libmx.mxfp8_quantize_dual(p, 64, 40, p, p, p, p, NULL) == 2             # cols % 32
+    assert libmx.mxfp8_quantize_dual(p, 64, 64, p, p, q, p, NULL) == 5             # alignment
+    assert libmx.mxfp8_quantize_packed(p, 1, 4, 64, p, NULL, p, p, NULL) == 1      # q without scales
+    assert libmx.mxfp8_quantize_packed(p, 1, 4, 40, NULL, NULL, p, p, NULL) == 2   # K % 32
+    assert libmx.mxfp8_quantize_packed(p, 0, 4, 64, NULL, NULL, p, p, NULL) == 2   # batch
+    assert libmx.mxfp8_quantize_packed(q, 1, 4, 64, NULL, NULL, p, p, NULL) == 5   # alignment
+    assert libmx.mxfp8_quantize(p, 32, 32, 1, p, q, NULL) == 5                     # scales alignment

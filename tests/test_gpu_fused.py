@@ -1,0 +1,105 @@
+"""GPU parity of the fused quantizers against the oracle, bit for bit.
+
+mxfp8_quantize_dual must equal the oracle's quantize along both axes, and
+mxfp8_quantize_packed must equal the oracle's packing of its axis-1 quantize
+(plus the canonical grid when requested) -- the definitions both calls state
+in include/mxfp8.h.  Shapes span several 128x128 (dual) or 256x128 (packed)
+tiles with ragged edges, the full learner and weight-sync shapes, and the
+special values (zero, subnormal, NaN and Inf blocks).
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from conftest import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("fused case:", *a, flush=True)
+
+
+def _specials(x, rng):
+    """Plant zero, subnormal, NaN, Inf and large-magnitude blocks into a BF16 array."""
+    x = x.copy()
+    flat = x.reshape(-1)
+    nblk = flat.size // 32
+    picks = rng.choice(nblk, size=min(nblk, 12), replace=False)
+    kinds = [0x0000, 0x0001, 0x7FC0, 0x7F80, 0xFF80, 0x7F7F, 0x8000, 0x0080]
+    for i, b in enumerate(picks):
+        kind = kinds[i % len(kinds)]
+        lo = b * 32
+        if kind in (0x0000, 0x8000):
+            flat[lo:lo + 32] = kind                              # all-zero block (signed)
+        elif kind in (0x0001, 0x0080):
+            flat[lo:lo + 32] = kind + rng.integers(0, 64, 32)   # subnormals / smallest normals
+        else:
+            flat[lo + int(rng.integers(0, 32))] = kind           # one NaN / Inf / max in the block
+    return x
+
+
+@pytest.mark.parametrize("rows,cols", [(32, 32), (64, 96), (160, 224), (256, 384), (96, 4160),
+                                       (4096, 4096)])
+def test_quantize_dual_matches_both_axes(mx, oracle_mod, rows, cols):
+    _say("dual", rows, cols)
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = wl.normal_bf16(rng, (rows, cols), outlier_frac=0.01)
+    if rows * cols <= 1 << 20:
+        x = _specials(x, rng)
+    q1, s1, q0, s0 = mx.quantize_dual(to_dev(x))
+    rq1, rs1 = oracle_mod.quantize(x, 1)
+    rq0, rs0 = oracle_mod.quantize(x, 0)
+    assert np.array_equal(to_host(q1), rq1) and np.array_equal(to_host(s1), rs1)
+    assert np.array_equal(to_host(q0), rq0) and np.array_equal(to_host(s0), rs0)
+
+
+def test_quantize_dual_mlp_gradient_full_size(mx, oracle_mod):
+    """dY_gu of the MLP micro-batch (8192 x 24576), the largest learner tensor."""
+    _say("dual mlp dY_gu")
+    rng = np.random.default_rng(11)
+    x = wl.normal_bf16(rng, (8192, 24576), std=2.0 ** -10)
+    q1, s1, q0, s0 = mx.quantize_dual(to_dev(x))
+    rq1, rs1 = oracle_mod.quantize(x, 1)
+    assert np.array_equal(to_host(q1), rq1) and np.array_equal(to_host(s1), rs1)
+    del rq1, rs1
+    rq0, rs0 = oracle_mod.quantize(x, 0)
+    assert np.array_equal(to_host(q0), rq0) and np.array_equal(to_host(s0), rs0)
+
+
+@pytest.mark.parametrize("batch,N,K", [(1, 256, 128), (1, 300, 320), (3, 17, 96), (2, 512, 768),
+                                       (5, 1000, 1056), (1, 6144, 4096), (16, 1536, 2048)])
+@pytest.mark.parametrize("canonical", [False, True])
+def test_quantize_packed_matches_quantize_then_pack(mx, oracle_mod, batch, N, K, canonical):
+    _say("packed", batch, N, K, canonical)
+    rng = np.random.default_rng(batch * 1000 + N + K)
+    w = wl.normal_bf16(rng, (batch * N, K), std=0.02)
+    if batch * N * K <= 1 << 21:
+        w = _specials(w, rng)
+    pw, q, s = mx.quantize_packed(to_dev(w.reshape(batch, N, K)), canonical=canonical)
+    rq, rs = oracle_mod.quantize(w, 1)
+    qp_ref, sp_ref = oracle_mod.pack(rq.reshape(batch, N, K), rs.reshape(batch, N, K // 32), batch, N, K)
+    assert np.array_equal(to_host(pw.q), qp_ref)
+    assert np.array_equal(to_host(pw.s), sp_ref)
+    if canonical:
+        assert np.array_equal(to_host(q).reshape(batch * N, K), rq)
+        assert np.array_equal(to_host(s).reshape(batch * N, K // 32), rs)
+    else:
+        assert q is None and s is None
+
+
+def test_quantize_packed_feeds_gemm_like_repack(mx, oracle_mod):
+    """The packed bytes are the repack bytes, so the GEMM result is identical."""
+    import torch
+    _say("packed gemm")
+    rng = np.random.default_rng(5)
+    M, N, K = 96, 300, 512
+    w = wl.normal_bf16(rng, (N, K), std=0.02)
+    x = wl.normal_bf16(rng, (M, K))
+    xq, xs = mx.quantize(to_dev(x), 1)
+    pw, q, s = mx.quantize_packed(to_dev(w))
+    ref = mx.repack(q, s)
+    y1 = mx.gemm(xq, xs, pw, torch.float32)
+    y2 = mx.gemm(xq, xs, ref, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(y1), to_host(y2))
