@@ -447,6 +447,13 @@ def bench_sync(args, dev):
 
     ms, gpu_ms = replayed(ops, args.steps)
     unf_ms, unf_gpu_ms = replayed(unfused, max(2, args.steps // 2))
+    # post-sync self-check of one synchronized layer (layer 0 qkv): serving
+    # GEMM on a 128-row N(0,1) probe against the dequantized grid
+    _, W0, q0, s0, pk0 = tensors[0]
+    mx.selfcheck_rel_err(q0, s0, pk0, seed=1)
+    t0 = time.perf_counter()
+    rel0 = mx.selfcheck_rel_err(q0, s0, pk0, seed=2)[0]
+    check_ms = 1e3 * (time.perf_counter() - t0)
     alg = n_elts * (2 + 2 * (1 + 1 / 32))          # bf16 in; canonical + packed out
     kern = {}
     for name, N, K in wl.sync_layer_shapes():
@@ -463,6 +470,7 @@ def bench_sync(args, dev):
                  summary={"algorithmic_GB": round(alg / 1e9, 2), "graph_gpu_ms": round(gpu_ms, 3),
                           "eager_ms_per_sync": round(eager_ms, 3),
                           "unfused_quantize_then_repack_ms": round(unf_ms, 3),
+                          "selfcheck_qkv_rel_err": round(rel0, 5), "selfcheck_ms": round(check_ms, 3),
                           "unfused_GB_moved": round(n_elts * (Q_BYTES_PER_ELT + REPACK_BYTES_PER_ELT) / 1e9, 2),
                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
                  roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -235,6 +235,40 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s,
                                 int64_t M_total, int64_t N, int64_t K, void *c,
                                 mxfp8_dtype c_dtype, hipStream_t stream);
 
+/*
+ * mxfp8_selfcheck -- post-sync check of one quantized layer's serving path.
+ *
+ * The page's post-sync self-check (section "Correctness: how it fails",
+ * run-time check C3): after every synchronization one quantized layer runs
+ * through the serving kernel on random input and is compared with a
+ * high-precision GEMM on the dequantized synchronized weights; healthy layers
+ * are a few percent off (about 0.027 dense, 0.049 expert on the page), stale
+ * derived layouts are off by order 1, and the page's tolerance is 0.25.
+ *
+ *   Y     = mxfp8_gemm(quantize(x, axis 1), packed weights)      (fp32 out)
+ *   Y_ref = x * W'^T in fp32, W' = dequantize(w_q, w_s)           (canonical)
+ *   d_result[0] = ||Y - Y_ref||_F / ||Y_ref||_F, d_result[1] = ||Y - Y_ref||^2,
+ *   d_result[2] = ||Y_ref||^2 (fp64); d_result[0] is NaN if either output is
+ *   not finite or Y_ref is zero.
+ *
+ * x: BF16 probe [M][K] (device; the caller draws it, e.g. N(0,1)), M <= 4096.
+ * w_q / w_s: the synchronized canonical grid [N][K], [N][K/32].
+ * w_q_packed / w_s_packed: the storage the serving GEMM reads (mxfp8_repack
+ *   layout, one matrix; for expert g of a batch pass the g-th matrix's
+ *   offsets, g * mxfp8_packed_bytes(1, N, K, which)).
+ * workspace: device, mxfp8_selfcheck_workspace_bytes(M, N, K) bytes, 16-byte
+ *   aligned, owned by the caller.  d_result: device, 3 doubles.
+ * Asynchronous like every call here: the verdict is read after the stream is
+ * synchronized (the Python binding applies the tolerance and the off / warn
+ * / error mode).  Deterministic.
+ */
+size_t mxfp8_selfcheck_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+mxfp8_status mxfp8_selfcheck(const void *x_bf16, int64_t M, int64_t N, int64_t K,
+                             const uint8_t *w_q, const uint8_t *w_s,
+                             const uint8_t *w_q_packed, const uint8_t *w_s_packed,
+                             void *workspace, double *d_result, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *mxfp8_status_string(mxfp8_status status);
 

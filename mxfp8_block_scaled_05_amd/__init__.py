@@ -55,6 +55,10 @@ def lib():
         L.mxfp8_repack.argtypes = [P, P, I64, I64, I64, P, P, P]
         L.mxfp8_gemm.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
         L.mxfp8_grouped_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        L.mxfp8_selfcheck_workspace_bytes.argtypes = [I64, I64, I64]
+        L.mxfp8_selfcheck_workspace_bytes.restype = ctypes.c_size_t
+        L.mxfp8_selfcheck.argtypes = [P, I64, I64, I64, P, P, P, P, P, P, P]
+        L.mxfp8_selfcheck.restype = I32
         L.mxfp8_quantize_dual.argtypes = [P, I64, I64, P, P, P, P, P]
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
@@ -348,3 +352,45 @@ def grouped_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, offsets:
                                     M_total, w.N, K, _ptr(out), code, _stream(a_q.device)),
            "mxfp8_grouped_gemm")
     return out
+
+
+# ------------------------------------------------------------------ self-check
+
+SELFCHECK_TOLERANCE = 0.25
+
+
+def selfcheck_rel_err(w_q: torch.Tensor, w_s: torch.Tensor, packed: PackedWeight, index: int = 0,
+                      probe_rows: int = 128, seed: int = 0, x: torch.Tensor | None = None):
+    """Relative Frobenius error of matrix `index` of `packed` served by the
+    MXFP8 GEMM on a random N(0,1) probe against an fp32 GEMM on the
+    dequantized canonical grid (w_q [N, K], w_s [N, K/32] of that matrix).
+    Returns (rel_err, sum_sq_err, sum_sq_ref); rel_err is NaN if an output is
+    not finite.  Synchronizes the current stream to read the verdict."""
+    N, K = packed.N, packed.K
+    _need(w_q, torch.uint8, "w_q")
+    _need(w_s, torch.uint8, "w_s")
+    if w_q.numel() != N * K or w_s.numel() != N * (K // 32):
+        raise ValueError("w_q/w_s must be one [N, K] canonical matrix")
+    if not 0 <= index < packed.batch:
+        raise ValueError("matrix index out of range")
+    dev = w_q.device
+    if x is None:
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        x = torch.randn((probe_rows, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    _need(x, torch.bfloat16, "x")
+    M = x.shape[0]
+    nbytes = int(lib().mxfp8_selfcheck_workspace_bytes(M, N, K))
+    if nbytes == 0:
+        raise ValueError("unsupported self-check size")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    res = torch.empty(3, dtype=torch.float64, device=dev)
+    oq = index * packed_bytes(1, N, K, 0)
+    os_ = index * packed_bytes(1, N, K, 1)
+    _check(lib().mxfp8_selfcheck(_ptr(x), M, N, K, _ptr(w_q), _ptr(w_s),
+                                 ctypes.c_void_p(packed.q.data_ptr() + oq),
+                                 ctypes.c_void_p(packed.s.data_ptr() + os_),
+                                 _ptr(ws), _ptr(res), _stream(dev)), "mxfp8_selfcheck")
+    torch.cuda.current_stream(dev).synchronize()
+    r = res.cpu().tolist()
+    return r[0], r[1], r[2]

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmxfp8.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "dequantize.hip", "repack.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "dequantize.hip", "repack.hip", "gemm.hip", "selfcheck.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -57,6 +57,7 @@ namespace {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;     // any single dimension
 constexpr int64_t kMaxK = (int64_t)1 << 22;       // 256 rows x K must stay < 2^31 B
+constexpr int64_t kMaxSelfcheckRows = 4096;       // probe rows of a self-check
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -158,6 +159,42 @@ mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t ro
     if (st != MXFP8_OK) return st;
     return finish(launch_quantize_packed(static_cast<const uint16_t *>(w_bf16), batch, rows, cols,
                                          q, scales, q_packed, scales_packed, stream));
+}
+
+size_t mxfp8_selfcheck_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 || M > kMaxSelfcheckRows || N >= kMaxDim || K > kMaxK)
+        return 0;
+    return (size_t)selfcheck_workspace(M, N, K).total;
+}
+
+mxfp8_status mxfp8_selfcheck(const void *x_bf16, int64_t M, int64_t N, int64_t K,
+                             const uint8_t *w_q, const uint8_t *w_s, const uint8_t *w_q_packed,
+                             const uint8_t *w_s_packed, void *workspace, double *d_result,
+                             hipStream_t stream) {
+    if (!x_bf16 || !w_q || !w_s || !w_q_packed || !w_s_packed || !workspace || !d_result)
+        return MXFP8_ERR_NULL;
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 || M > kMaxSelfcheckRows || N >= kMaxDim || K > kMaxK)
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(w_q) || !aligned16(w_s) || !aligned16(w_q_packed) ||
+        !aligned16(w_s_packed) || !aligned16(workspace) || ((uintptr_t)d_result & 7u))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    const SelfcheckWorkspace ws = selfcheck_workspace(M, N, K);
+    uint8_t *base = static_cast<uint8_t *>(workspace);
+    uint8_t *xq = base + ws.xq, *xs = base + ws.xs;
+    float *y = reinterpret_cast<float *>(base + ws.y);
+    float *yref = reinterpret_cast<float *>(base + ws.yref);
+    double *part = reinterpret_cast<double *>(base + ws.part);
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    // the serving path: quantize the probe, MXFP8 GEMM against the packed storage
+    hipError_t e = launch_quantize(x, M, K, 1, xq, xs, stream);
+    if (e == hipSuccess)
+        e = launch_gemm(xq, xs, w_q_packed, w_s_packed, true, M, N, K, y, false, stream);
+    // the reference from the canonical synchronized grid, then the error
+    if (e == hipSuccess) e = launch_selfcheck_ref(x, M, N, K, w_q, w_s, yref, stream);
+    if (e == hipSuccess) e = launch_selfcheck_error(y, yref, M * N, part, d_result, stream);
+    return finish(e);
 }
 
 mxfp8_status mxfp8_dequantize(const uint8_t *q, const uint8_t *scales, int64_t rows, int64_t cols,

@@ -37,6 +37,22 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uin
                                int64_t M_total, int64_t N, int64_t K, void *c, bool c_bf16,
                                hipStream_t stream);
 
+// Self-check workspace: byte offsets of its parts (256-byte aligned) and the
+// total size, for a probe of M rows against weights [N][K].
+struct SelfcheckWorkspace {
+    int64_t xq, xs, y, yref, part, total;
+};
+SelfcheckWorkspace selfcheck_workspace(int64_t M, int64_t N, int64_t K);
+
+// Reference Y_ref = X * dequant(W)^T in fp32 (X bf16 [M][K], W canonical [N][K]).
+hipError_t launch_selfcheck_ref(const uint16_t *x, int64_t M, int64_t N, int64_t K,
+                                const uint8_t *wq, const uint8_t *ws, float *yref,
+                                hipStream_t stream);
+
+// out[0] = ||y - yref|| / ||yref|| (NaN if not finite), out[1..2] the sums.
+hipError_t launch_selfcheck_error(const float *y, const float *yref, int64_t n, double *part,
+                                  double *out, hipStream_t stream);
+
 // Packed weight layout geometry (see mxfp8_repack in include/mxfp8.h).
 constexpr int64_t kPanelRows = 256;   // rows per packed panel
 constexpr int64_t kKStep = 128;       // K bytes per packed k-step (one MFMA K)
