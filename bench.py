@@ -281,6 +281,22 @@ def bench_mlp(args, dev):
     torch.cuda.synchronize()
     ms, avg = run_timed(ops, args)
     _, avg_unf = run_timed(unfused, argparse.Namespace(steps=max(2, args.steps // 2), warmup=1))
+    # the whole micro-batch (14 launches) captured once and replayed
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _, fn in ops:
+            fn()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(max(2, args.steps // 2)):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / max(2, args.steps // 2)
+    del graph
     flops = sum(2.0 * M * N * K for (_, _, M, N, K, _) in gemms.values())
     kern = {}
     for key, nbytes in q_bytes.items():
@@ -303,6 +319,7 @@ def bench_mlp(args, dev):
                  kernels=kern,
                  summary={"gemm_us": round(gemm_us, 1),
                           "gemm_TFLOP/s": round(flops / (gemm_us * 1e-6) / 1e12, 1),
+                          "graph_replay_ms_per_step": round(graph_ms, 4),
                           "quantize_and_layout_us": round(quant_us, 1),
                           "unfused_quantize_and_layout_us": round(unfused_us, 1)},
                  roofline={"bound": "mfma", "achieved": top["TFLOP/s"], "peak": MXFP8_PEAK_TFLOPS,
@@ -535,6 +552,21 @@ def bench_sweep(args, dev):
             host = time.perf_counter() - t0
             torch.cuda.synchronize()
             res[arm + "_host_us"] = round(host * 1e6 / n, 2)
+            # the layer's launches captured once as a HIP graph and replayed:
+            # GPU time without any per-launch host dispatch
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(n):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[arm + "_graph_us"] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+            del graph
         rows.append(res)
 
     def fit(key):
@@ -544,7 +576,7 @@ def bench_sweep(args, dev):
         return f, c
 
     fits = {}
-    for kind in ("gpu", "host"):
+    for kind in ("gpu", "graph", "host"):
         fm, cm = fit("mxfp8_%s_us" % kind)
         fb, cb = fit("bf16_%s_us" % kind)
         cross = None
