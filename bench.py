@@ -8,7 +8,7 @@ sit in the 256 MB Infinity Cache.  Every kernel launch is bracketed by HIP
 events on the stream it runs on, so each kernel's average duration is
 measured live; `value` is the whole step's throughput (2MNK / step time).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload qkv|mlp|moe|sync|sweep]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload qkv|mlp|moe|moe_train|sync|sweep]
                     [--no-cpu-baseline]
 
 Prints one JSON line.
@@ -410,6 +410,111 @@ def bench_moe(args, dev):
                            "kernel": "grouped gemm gate_up", "hbm_frac": top["frac_hbm_peak"]})
 
 
+def bench_moe_train(args, dev):
+    """Qwen3-30B-A3B MoE expert layer, one learner micro-batch of 8192 tokens
+    (128 experts, Zipf(1.1) top-8, groups padded to 32): forward, data
+    gradients and weight gradients of gate_up and down, all in MXFP8.
+      weights (per step): gate_up and down quantized along K into the packed
+        layout, and along N per expert (batched axis 0) + repacked for dgrad;
+      forward: X gathered by routing + quantized in one pass (the fused
+        permute), grouped gate_up; h quantized along both axes, grouped down;
+      backward: dY quantized along both axes -> dgrad down (grouped GEMM vs
+        W_d^T), wgrad down (grouped-K GEMM dY^T h); dH quantized along both
+        axes -> dgrad gate_up, wgrad gate_up (grouped-K GEMM dH^T X).
+    The activation function between gate_up and down is outside the MXFP8
+    path; h and dH are drawn as N(0,1) and N(0,1)*2^-10 on real rows."""
+    import torch
+    import mxfp8_block_scaled_05_amd as mx
+    import workloads as wl
+
+    d = wl.moe(0)
+    G, I2, H = d["W_gu"].shape
+    I = d["W_d"].shape[2]
+    offs_np = d["offsets"]
+    Mt = int(offs_np[-1])
+    real = int(d["counts"].sum())
+    rng = np.random.default_rng(1)
+    realrows = d["row_token"] >= 0
+    dY = np.zeros((Mt, H), np.uint16)
+    dY[realrows] = wl.normal_bf16(rng, (real, H), std=2.0 ** -10)
+    dH = np.zeros((Mt, I2), np.uint16)        # gradient at gate_up's output
+    dH[realrows] = wl.normal_bf16(rng, (real, I2), std=2.0 ** -10)
+    Xperm = np.zeros((Mt, H), np.uint16)
+    Xperm[realrows] = d["X"][d["row_token"][realrows]]
+    t = {"W_gu": _bf16_dev(d["W_gu"], dev), "W_d": _bf16_dev(d["W_d"], dev), "X": _bf16_dev(d["X"], dev),
+         "A_d": _bf16_dev(d["A_d"], dev), "dY": _bf16_dev(dY, dev), "dH": _bf16_dev(dH, dev),
+         "Xperm": _bf16_dev(Xperm, dev)}
+    idx = torch.from_numpy(d["row_token"]).to(dev)
+    offs = torch.from_numpy(offs_np).to(dev)
+    del d, dY, dH, Xperm
+    u8 = dict(dtype=torch.uint8, device=dev)
+
+    def packed(n, k):
+        return mx.PackedWeight(torch.empty(mx.packed_bytes(G, n, k, 0), **u8),
+                               torch.empty(mx.packed_bytes(G, n, k, 1), **u8), G, n, k)
+    P_gu, P_d, P_guT, P_dT = packed(I2, H), packed(H, I), packed(H, I2), packed(I, H)
+    wguT = (torch.empty((G, H, I2), **u8), torch.empty((G, H, I2 // 32), **u8))
+    wdT = (torch.empty((G, I, H), **u8), torch.empty((G, I, H // 32), **u8))
+    xq = (torch.empty((Mt, H), **u8), torch.empty((Mt, H // 32), **u8))
+    h1 = (torch.empty((Mt, I), **u8), torch.empty((Mt, I // 32), **u8))
+    h0 = (torch.empty((I, Mt), **u8), torch.empty((I, Mt // 32), **u8))
+    dy1 = (torch.empty((Mt, H), **u8), torch.empty((Mt, H // 32), **u8))
+    dy0 = (torch.empty((H, Mt), **u8), torch.empty((H, Mt // 32), **u8))
+    dh1 = (torch.empty((Mt, I2), **u8), torch.empty((Mt, I2 // 32), **u8))
+    dh0 = (torch.empty((I2, Mt), **u8), torch.empty((I2, Mt // 32), **u8))
+    x0 = (torch.empty((H, Mt), **u8), torch.empty((H, Mt // 32), **u8))
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    y_gu, y_d = torch.empty((Mt, I2), **bf), torch.empty((Mt, H), **bf)
+    g_h, g_x = torch.empty((Mt, I), **bf), torch.empty((Mt, H), **bf)
+    dW_d = torch.empty((G, H, I), dtype=torch.float32, device=dev)
+    dW_gu = torch.empty((G, I2, H), dtype=torch.float32, device=dev)
+    ops = [
+        ("w_gu_packed", lambda: mx.quantize_packed_(t["W_gu"], P_gu)),
+        ("w_d_packed", lambda: mx.quantize_packed_(t["W_d"], P_d)),
+        ("w_gu_axis0", lambda: mx._check(mx.lib().mxfp8_quantize_batched(
+            mx._ptr(t["W_gu"]), G, I2, H, 0, mx._ptr(wguT[0]), mx._ptr(wguT[1]), mx._stream(dev)), "q")),
+        ("w_d_axis0", lambda: mx._check(mx.lib().mxfp8_quantize_batched(
+            mx._ptr(t["W_d"]), G, H, I, 0, mx._ptr(wdT[0]), mx._ptr(wdT[1]), mx._stream(dev)), "q")),
+        ("repack_guT", lambda: mx.repack_(wguT[0], wguT[1], P_guT)),
+        ("repack_dT", lambda: mx.repack_(wdT[0], wdT[1], P_dT)),
+        ("gather_quantize_X", lambda: mx.quantize_gather_into(t["X"], idx, *xq)),
+        ("fprop_gate_up", lambda: mx.grouped_gemm(xq[0], xq[1], P_gu, offs, torch.bfloat16, out=y_gu)),
+        ("quantize_dual_h", lambda: mx.quantize_dual_into(t["A_d"], *h1, *h0)),
+        ("fprop_down", lambda: mx.grouped_gemm(h1[0], h1[1], P_d, offs, torch.bfloat16, out=y_d)),
+        ("quantize_dual_dY", lambda: mx.quantize_dual_into(t["dY"], *dy1, *dy0)),
+        ("dgrad_down", lambda: mx.grouped_gemm(dy1[0], dy1[1], P_dT, offs, torch.bfloat16, out=g_h)),
+        ("wgrad_down", lambda: mx.grouped_gemm_wgrad(dy0[0], dy0[1], h0[0], h0[1], offs, torch.float32, out=dW_d)),
+        ("quantize_dual_dH", lambda: mx.quantize_dual_into(t["dH"], *dh1, *dh0)),
+        ("dgrad_gate_up", lambda: mx.grouped_gemm(dh1[0], dh1[1], P_guT, offs, torch.bfloat16, out=g_x)),
+        ("quantize_X_axis0", lambda: mx.quantize_into(t["Xperm"], 0, *x0)),
+        ("wgrad_gate_up", lambda: mx.grouped_gemm_wgrad(dh0[0], dh0[1], x0[0], x0[1], offs, torch.float32, out=dW_gu)),
+    ]
+    torch.cuda.synchronize()
+    ms, avg = run_timed(ops, args)
+    f_gu = 2.0 * real * I2 * H
+    f_d = 2.0 * real * H * I
+    flops = {"fprop_gate_up": f_gu, "fprop_down": f_d, "dgrad_down": f_d, "wgrad_down": f_d,
+             "dgrad_gate_up": f_gu, "wgrad_gate_up": f_gu}
+    kern = {}
+    for name, us in avg.items():
+        if name in flops:
+            tf = flops[name] / (us * 1e-6) / 1e12
+            kern[name] = {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4)}
+        else:
+            kern[name] = {"us": round(us, 2)}
+    total = sum(flops.values())
+    gemm_us = sum(avg[k] for k in flops)
+    return _line("MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",
+                 round(total / (ms * 1e-3) / 1e12, 2), "TFLOP/s", args, ms,
+                 "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out (fprop/dgrad), fp32 out (wgrad)",
+                 {"workload": "qwen3-30b-a3b MoE expert layer learner micro-batch: 8192 tokens, 128 experts, "
+                              "Zipf(1.1) top-8, forward + dgrad + wgrad of gate_up and down",
+                  "tokens": 8192, "experts": G, "rows_real": real, "rows_padded": Mt},
+                 kernels=kern, flops_basis="unpadded rows",
+                 summary={"gemm_us": round(gemm_us, 1), "gemm_TFLOP/s": round(total / (gemm_us * 1e-6) / 1e12, 1),
+                          "other_us": round(sum(avg.values()) - gemm_us, 1)})
+
+
 def bench_sync(args, dev):
     """Shared-grid weight sync of Qwen3-8B: quantize along K and repack all 144
     linear weights (36 layers x qkv, o, gate_up, down; 6.95e9 elements).  BF16
@@ -656,7 +761,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "moe", "sync", "sweep"])
+    ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "moe", "moe_train", "sync", "sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy (for scaling HBM counters)")
@@ -680,7 +785,8 @@ def main():
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_qkv()
     else:
-        out = {"mlp": bench_mlp, "moe": bench_moe, "sync": bench_sync, "sweep": bench_sweep}[args.workload](args, dev)
+        out = {"mlp": bench_mlp, "moe": bench_moe, "moe_train": bench_moe_train, "sync": bench_sync,
+               "sweep": bench_sweep}[args.workload](args, dev)
     print(json.dumps(out), flush=True)
 
 

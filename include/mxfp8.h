@@ -127,6 +127,39 @@ mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t ro
                                    hipStream_t stream);
 
 /*
+ * mxfp8_quantize_batched -- mxfp8_quantize over `batch` matrices at once.
+ *
+ * The MoE learner's data-gradient GEMM needs every expert's weights blocked
+ * along N (axis 0, transposed; "The pipeline", learner paragraph), one
+ * matrix per expert.  x: BF16 [batch][rows][cols]; per matrix the result is
+ * exactly mxfp8_quantize's: axis 1 -> q[batch][rows][cols],
+ * scales[batch][rows][cols/32]; axis 0 -> q[batch][cols][rows],
+ * scales[batch][cols][rows/32] (rows % 32 == 0 and rows * cols % 16 == 0).
+ * batch <= 65535.  Bit-exact, deterministic.
+ */
+mxfp8_status mxfp8_quantize_batched(const void *x_bf16, int64_t batch, int64_t rows,
+                                    int64_t cols, int axis, uint8_t *q, uint8_t *scales,
+                                    hipStream_t stream);
+
+/*
+ * mxfp8_quantize_gather -- routing permute, expert padding and the axis-1
+ * quantize in one pass.
+ *
+ * The MoE GEMMs read token rows sorted by expert with each group padded to a
+ * multiple of 32 (the pages pad to 32 for the token-blocked operands; the
+ * expert GEMMs read "shuffled" expert inputs).  Output row i is input row
+ * d_row_index[i], quantized along its columns; an index outside
+ * [0, rows_in) (the padding rows of a group) gives a zero row (scale code 0,
+ * elements 0), so the index table can never make it read out of bounds.
+ *   x: BF16 [rows_in][cols], cols % 32 == 0; d_row_index: DEVICE int64
+ *   [rows_out]; q [rows_out][cols], scales [rows_out][cols/32].
+ * Bit-exact: equal to mxfp8_quantize of the gathered, zero-padded matrix.
+ */
+mxfp8_status mxfp8_quantize_gather(const void *x_bf16, int64_t rows_in, int64_t cols,
+                                   const int64_t *d_row_index, int64_t rows_out,
+                                   uint8_t *q, uint8_t *scales, hipStream_t stream);
+
+/*
  * mxfp8_dequantize -- MXFP8 -> FP32 or BF16:  out = decode(q) * 2^(code-127).
  *
  * The high-precision reference that the page's post-sync self-check compares
@@ -234,6 +267,32 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s,
                                 const int32_t *d_group_offsets, int64_t G,
                                 int64_t M_total, int64_t N, int64_t K, void *c,
                                 mxfp8_dtype c_dtype, hipStream_t stream);
+
+/*
+ * mxfp8_grouped_gemm_wgrad -- the experts' weight gradients:
+ *   for g in 0..G-1:  C[g] = A[:, o_g : o_{g+1}] * B[:, o_g : o_{g+1}]^T
+ *
+ * The weight-gradient GEMM reduces over tokens, so its operands are blocked
+ * along the token dimension ("The pipeline", learner paragraph); for an
+ * expert the reduction runs over that expert's (padded) token group only.
+ * With the token rows sorted by expert, dY^T and X^T quantized along tokens
+ * (mxfp8_quantize axis 0 of dY [T][M] and X [T][N]) hold every group's block
+ * columns contiguously, and expert g's gradient dW_g = dY_g^T X_g is this
+ * GEMM over columns [o_g, o_{g+1}):
+ *   A (a_q, a_s): [M][T] / [M][T/32] (axis-0 quantize output of dY [T][M]);
+ *   B (b_q, b_s): [N][T] / [N][T/32] (axis-0 quantize output of X [T][N]);
+ *   d_group_offsets: DEVICE int32 [G+1] token offsets, non-decreasing,
+ *     multiples of 32 (clamped into [0, T]; a malformed table can only drop
+ *     work, never address outside the operands);
+ *   C: [G][M][N], FP32 or BF16; an empty group's C[g] is all zeros.
+ * T % 32 == 0, 32 <= T < 2^23, M, N >= 1, G <= 65535.  Same accumulation and
+ * error bound as mxfp8_gemm.  Deterministic.
+ */
+mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s,
+                                      const uint8_t *b_q, const uint8_t *b_s,
+                                      const int32_t *d_group_offsets, int64_t G, int64_t T,
+                                      int64_t M, int64_t N, void *c, mxfp8_dtype c_dtype,
+                                      hipStream_t stream);
 
 /*
  * mxfp8_selfcheck -- post-sync check of one quantized layer's serving path.

@@ -59,6 +59,11 @@ def lib():
         L.mxfp8_selfcheck_workspace_bytes.restype = ctypes.c_size_t
         L.mxfp8_selfcheck.argtypes = [P, I64, I64, I64, P, P, P, P, P, P, P]
         L.mxfp8_selfcheck.restype = I32
+        L.mxfp8_quantize_batched.argtypes = [P, I64, I64, I64, I32, P, P, P]
+        L.mxfp8_quantize_gather.argtypes = [P, I64, I64, P, I64, P, P, P]
+        L.mxfp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        for f in ("mxfp8_quantize_batched", "mxfp8_quantize_gather", "mxfp8_grouped_gemm_wgrad"):
+            getattr(L, f).restype = I32
         L.mxfp8_quantize_dual.argtypes = [P, I64, I64, P, P, P, P, P]
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
@@ -143,6 +148,50 @@ def quantize(x: torch.Tensor, axis: int = 1):
     if (axis == 1 and cols % 32) or (axis == 0 and rows % 32):
         raise ValueError("the block axis must be a multiple of 32")
     quantize_into(x, axis, q, s)
+    return q, s
+
+
+def quantize_batched(x: torch.Tensor, axis: int = 1):
+    """BF16 [batch, rows, cols] -> (q, s) per matrix as quantize(x[b], axis):
+    axis 1: q[batch, rows, cols], s[batch, rows, cols/32]; axis 0 (transposed
+    per matrix): q[batch, cols, rows], s[batch, cols, rows/32]."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 3:
+        raise ValueError("x must be 3-D [batch, rows, cols]")
+    batch, rows, cols = x.shape
+    if axis == 1:
+        q = torch.empty((batch, rows, cols), dtype=torch.uint8, device=x.device)
+        s = torch.empty((batch, rows, cols // 32), dtype=torch.uint8, device=x.device)
+    elif axis == 0:
+        q = torch.empty((batch, cols, rows), dtype=torch.uint8, device=x.device)
+        s = torch.empty((batch, cols, rows // 32), dtype=torch.uint8, device=x.device)
+    else:
+        raise ValueError("axis must be 0 or 1")
+    _check(lib().mxfp8_quantize_batched(_ptr(x), batch, rows, cols, axis, _ptr(q), _ptr(s),
+                                        _stream(x.device)), "mxfp8_quantize_batched")
+    return q, s
+
+
+def quantize_gather_into(x: torch.Tensor, row_index: torch.Tensor, q: torch.Tensor,
+                         s: torch.Tensor) -> None:
+    """q/s = quantize(x[row_index], 1), rows whose index is outside [0, rows) zero."""
+    _need(x, torch.bfloat16, "x")
+    _need(row_index, torch.int64, "row_index")
+    _need(q, torch.uint8, "q")
+    _need(s, torch.uint8, "scales")
+    rows_in, cols = x.shape
+    rows_out = row_index.numel()
+    if tuple(q.shape) != (rows_out, cols) or tuple(s.shape) != (rows_out, cols // 32):
+        raise ValueError("q/scales must be [rows_out, cols] / [rows_out, cols/32]")
+    _check(lib().mxfp8_quantize_gather(_ptr(x), rows_in, cols, _ptr(row_index), rows_out, _ptr(q),
+                                       _ptr(s), _stream(x.device)), "mxfp8_quantize_gather")
+
+
+def quantize_gather(x: torch.Tensor, row_index: torch.Tensor):
+    rows_out, cols = row_index.numel(), x.shape[1]
+    q = torch.empty((rows_out, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((rows_out, cols // 32), dtype=torch.uint8, device=x.device)
+    quantize_gather_into(x, row_index, q, s)
     return q, s
 
 
@@ -351,6 +400,32 @@ def grouped_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, offsets:
     _check(lib().mxfp8_grouped_gemm(_ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s), _ptr(offsets), G,
                                     M_total, w.N, K, _ptr(out), code, _stream(a_q.device)),
            "mxfp8_grouped_gemm")
+    return out
+
+
+def grouped_gemm_wgrad(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, b_s: torch.Tensor,
+                       offsets: torch.Tensor, out_dtype=torch.float32,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[g] = A[:, o_g:o_g+1] B[:, o_g:o_g+1]^T for A [M, T], B [N, T] quantized
+    along tokens (axis-0 outputs) and device int32 token offsets [G+1]."""
+    for t, n in ((a_q, "a_q"), (a_s, "a_s"), (b_q, "b_q"), (b_s, "b_s")):
+        _need(t, torch.uint8, n)
+    _need(offsets, torch.int32, "offsets")
+    M, T = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != T or tuple(a_s.shape) != (M, T // 32) or tuple(b_s.shape) != (N, T // 32):
+        raise ValueError("A [M, T] and B [N, T] with scales [., T/32] expected")
+    G = offsets.numel() - 1
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((G, M, N), dtype=out_dtype, device=a_q.device)
+    else:
+        _need(out, out_dtype, "out")
+        if tuple(out.shape) != (G, M, N):
+            raise ValueError("out must be [G, M, N]")
+    _check(lib().mxfp8_grouped_gemm_wgrad(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), G,
+                                          T, M, N, _ptr(out), code, _stream(a_q.device)),
+           "mxfp8_grouped_gemm_wgrad")
     return out
 
 

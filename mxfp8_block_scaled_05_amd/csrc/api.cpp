@@ -129,6 +129,56 @@ mxfp8_status mxfp8_quantize(const void *x_bf16, int64_t rows, int64_t cols, int 
                                   scales, stream));
 }
 
+mxfp8_status mxfp8_quantize_batched(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
+                                    int axis, uint8_t *q, uint8_t *scales, hipStream_t stream) {
+    if (!x_bf16 || !q || !scales) return MXFP8_ERR_NULL;
+    if (axis != 0 && axis != 1) return MXFP8_ERR_AXIS;
+    if (batch <= 0 || batch > 65535 || rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    if (batch * rows >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (axis == 1 && cols % 32) return MXFP8_ERR_SHAPE;
+    if (axis == 0 && (rows % 32 || !tile128_ok(batch * rows, cols))) return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q) || !aligned16(scales)) return MXFP8_ERR_ALIGN;
+    if (axis == 0 && (rows * cols) % 16) return MXFP8_ERR_ALIGN;      // every matrix 16-byte aligned
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+    if (axis == 1) return finish(launch_quantize(x, batch * rows, cols, 1, q, scales, stream));
+    return finish(launch_quantize_axis0_batched(x, batch, rows, cols, q, scales, stream));
+}
+
+mxfp8_status mxfp8_quantize_gather(const void *x_bf16, int64_t rows_in, int64_t cols,
+                                   const int64_t *d_row_index, int64_t rows_out, uint8_t *q,
+                                   uint8_t *scales, hipStream_t stream) {
+    if (!x_bf16 || !d_row_index || !q || !scales) return MXFP8_ERR_NULL;
+    if (rows_in <= 0 || rows_out <= 0 || cols <= 0 || cols % 32 || rows_in >= kMaxDim ||
+        rows_out >= kMaxDim || cols >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q) || ((uintptr_t)d_row_index & 7u)) return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_gather(static_cast<const uint16_t *>(x_bf16), rows_in, cols,
+                                         d_row_index, rows_out, q, scales, stream));
+}
+
+mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                      const uint8_t *b_s, const int32_t *d_group_offsets,
+                                      int64_t G, int64_t T, int64_t M, int64_t N, void *c,
+                                      mxfp8_dtype c_dtype, hipStream_t stream) {
+    if (!a_q || !a_s || !b_q || !b_s || !d_group_offsets || !c) return MXFP8_ERR_NULL;
+    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (G < 1 || G > 65535 || T < 32 || T % 32 || T >= ((int64_t)1 << 23)) return MXFP8_ERR_SHAPE;
+    if (M <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (G * ((M + 255) / 256) * ((N + 255) / 256) > 0x7FFFFFFF) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c) ||
+        ((uintptr_t)d_group_offsets & 3u))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_grouped_gemm_wgrad(a_q, a_s, b_q, b_s, d_group_offsets, G, T, M, N, c,
+                                            c_dtype == MXFP8_BF16, stream));
+}
+
 mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, uint8_t *q_row,
                                  uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
                                  hipStream_t stream) {

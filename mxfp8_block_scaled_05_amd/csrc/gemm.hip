@@ -47,6 +47,10 @@ struct GemmParams {
     const int32_t *offsets;  // grouped only
     int G;
     int KS, NP;              // k-steps, packed panels of B
+    // canonical operand row strides in bytes (elements, scales): K and K/32,
+    // except in grouped-K mode where rows span all groups' tokens
+    int64_t lda, lsa, ldb, lsb;
+    int64_t c_stride;        // grouped-K: elements of one group's C
 };
 
 constexpr int kGroupM = 8;
@@ -185,11 +189,14 @@ struct TileOps {
     v4i ra, rsa, rb, rsb;
     __amdgpu_buffer_rsrc_t rsa_c, rsb_c;
     int Ki, KBi, lane, w, wm, wn, lrow, lblk;
+    int lda, lsa, ldb, lsb;    // row strides of canonical operands (bytes)
     uint32_t lds0;
 
+    // kbase / kbound: this tile's K range [kbase, kbase + kbound) of each
+    // canonical row (all of K unless in grouped-K mode)
     __device__ __forceinline__ void init(const GemmParams &p, int64_t m0, int64_t m_end, int64_t n0, int64_t g,
-                         const uint8_t *smem) {
-        const int64_t K = p.K, N = p.N, KB = K / 32;
+                         const uint8_t *smem, int64_t kbase = 0, int64_t kbound = -1) {
+        const int64_t K = kbound < 0 ? p.K : kbound, N = p.N, KB = K / 32;
         lane = threadIdx.x & 63;
         w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         wm = w / WN;
@@ -198,12 +205,19 @@ struct TileOps {
         lblk = lane >> 4;
         Ki = (int)K;
         KBi = (int)KB;
+        lda = (int)p.lda;
+        lsa = (int)p.lsa;
+        ldb = (int)p.ldb;
+        lsb = (int)p.lsb;
         lds0 = lds_addr(smem);
-        const int rows_a = (int)min((int64_t)BM, m_end - m0);
-        // each descriptor spans exactly this tile's bytes: out-of-range lanes read 0
-        ra = make_srd(p.a_q + m0 * K, (uint32_t)(rows_a * K));
-        rsa = make_srd(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
-        rsa_c = make_rsrc(p.a_s + m0 * KB, (uint32_t)(rows_a * KB));
+        const int64_t rows_a = min((int64_t)BM, m_end - m0);
+        // each descriptor spans exactly this tile's bytes (from its first row's
+        // K range start to its last row's K range end): out-of-range lanes read 0
+        const uint32_t a_bytes = (uint32_t)((rows_a - 1) * p.lda + K);
+        const uint32_t as_bytes = (uint32_t)((rows_a - 1) * p.lsa + KB);
+        ra = make_srd(p.a_q + m0 * p.lda + kbase, a_bytes);
+        rsa = make_srd(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
+        rsa_c = make_rsrc(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
         if constexpr (BPACK) {
             const int64_t panel = n0 / kPanelRows, prow = n0 % kPanelRows;
             const uint8_t *bt = p.b_q + ((g * p.NP + panel) * p.KS) * kTileBytes + prow * 128;
@@ -212,10 +226,12 @@ struct TileOps {
             rsb = make_srd(bs, (uint32_t)((int64_t)p.KS * kScaleStepBytes - (prow / 16) * 64));
             rsb_c = make_rsrc(p.b_s, 0u);
         } else {
-            const int rows_b = (int)min((int64_t)BN, N - n0);
-            rb = make_srd(p.b_q + n0 * K, (uint32_t)(rows_b * K));
-            rsb = make_srd(p.b_s + n0 * KB, (uint32_t)(rows_b * KB));
-            rsb_c = make_rsrc(p.b_s + n0 * KB, (uint32_t)(rows_b * KB));
+            const int64_t rows_b = min((int64_t)BN, N - n0);
+            const uint32_t b_bytes = (uint32_t)((rows_b - 1) * p.ldb + K);
+            const uint32_t bs_bytes = (uint32_t)((rows_b - 1) * p.lsb + KB);
+            rb = make_srd(p.b_q + n0 * p.ldb + kbase, b_bytes);
+            rsb = make_srd(p.b_s + n0 * p.lsb + kbase / 32, bs_bytes);
+            rsb_c = make_rsrc(p.b_s + n0 * p.lsb + kbase / 32, bs_bytes);
         }
     }
 
@@ -228,7 +244,7 @@ struct TileOps {
             const int rr = seg * 8 + (lane >> 3);
             const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
             const int kk = ks * 128 + c * 16;
-            const uint32_t off = kk < Ki ? (uint32_t)(rr * Ki + kk) : kOOB;
+            const uint32_t off = kk < Ki ? (uint32_t)(rr * lda + kk) : kOOB;
             dma16(ra, off, sbase + seg * 1024);
         }
 #pragma unroll
@@ -241,7 +257,7 @@ struct TileOps {
                 const int rr = seg * 8 + (lane >> 3);
                 const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
                 const int kk = ks * 128 + c * 16;
-                off = kk < Ki ? (uint32_t)(rr * Ki + kk) : kOOB;
+                off = kk < Ki ? (uint32_t)(rr * ldb + kk) : kOOB;
             }
             dma16(rb, off, sbase + BM * 128 + seg * 1024);
         }
@@ -249,14 +265,14 @@ struct TileOps {
         if constexpr (SA_LDS) {
             if (w < BM / 64) {
                 const int rr = w * 64 + lane;
-                dma4(rsa, (uint32_t)(rr * KBi + ks * 4), sbase + SA_OFF + w * 256);
+                dma4(rsa, (uint32_t)(rr * lsa + ks * 4), sbase + SA_OFF + w * 256);
             }
         }
         if constexpr (SB_LDS) {
             if (w < BN / 64) {
                 uint32_t off;
                 if constexpr (BPACK) off = (uint32_t)(ks * kScaleStepBytes + w * 256 + lane * 4);
-                else off = (uint32_t)((w * 64 + lane) * KBi + ks * 4);
+                else off = (uint32_t)((w * 64 + lane) * lsb + ks * 4);
                 dma4(rsb, off, sbase + SB_OFF + w * 256);
             }
         }
@@ -268,7 +284,7 @@ struct TileOps {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int rr = wm * WTM + i * 16 + lrow;
-            const uint32_t off = blk < KBi ? (uint32_t)(rr * KBi + blk) : kOOB;
+            const uint32_t off = blk < KBi ? (uint32_t)(rr * lsa + blk) : kOOB;
             dst[i] = __builtin_amdgcn_raw_buffer_load_b8(rsa_c, off, 0, 0);
         }
     }
@@ -277,7 +293,7 @@ struct TileOps {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int rr = wn * WTN + j * 16 + lrow;
-            const uint32_t off = blk < KBi ? (uint32_t)(rr * KBi + blk) : kOOB;
+            const uint32_t off = blk < KBi ? (uint32_t)(rr * lsb + blk) : kOOB;
             dst[j] = __builtin_amdgcn_raw_buffer_load_b8(rsb_c, off, 0, 0);
         }
     }
@@ -349,6 +365,29 @@ __device__ __forceinline__ bool tile_of(const GemmParams &p, int64_t &m0, int64_
         m0 = (int64_t)tm * BM;
         m_end = p.M;
     }
+    n0 = (int64_t)tn * BN;
+    return true;
+}
+
+// Grouped-K mode: tile -> (group g, tile row, tile column); the group's K range
+// is its token range [o_g, o_g+1) of the operands' rows (clamped like
+// find_group, so a malformed table can only drop work).  False past the end.
+template <int BM, int BN>
+__device__ __forceinline__ bool tile_of_gk(const GemmParams &p, int64_t &m0, int64_t &m_end, int64_t &n0,
+                                           int64_t &g, int64_t &kbase, int64_t &kbound) {
+    const int per = p.tiles_m * p.tiles_n;
+    const int L = xcd_logical(blockIdx.x, gridDim.x);
+    g = L / per;
+    if (g >= p.G) return false;
+    int tm, tn;
+    grouped_order(L % per, p.tiles_m, p.tiles_n, tm, tn);
+    int64_t lo = p.offsets[g], hi = p.offsets[g + 1];
+    lo = lo < 0 ? 0 : (lo > p.K ? p.K : lo);
+    hi = hi < lo ? lo : (hi > p.K ? p.K : hi);
+    kbase = lo;
+    kbound = hi - lo;
+    m0 = (int64_t)tm * BM;
+    m_end = p.M;
     n0 = (int64_t)tn * BN;
     return true;
 }
@@ -432,16 +471,26 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0
 
 // ---------------------------------------------------------------- 2 stages
 // One barrier at the top of each step; copies of step k+1 overlap step k.
-template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN>
+// GK (grouped-K, weight gradients of the experts): C_g = A[:, K_g] B[:, K_g]^T
+// for every group g, K_g its token range, C_g at c + g * c_stride.
+template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
     constexpr int FM = T::FM, FN = T::FN;
     static_assert(2 * T::STAGE <= 160 * 1024, "LDS budget");
+    static_assert(!GK || (!BPACK && !KALIGN && !GROUPED), "grouped-K reads canonical operands");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
-    int64_t m0, m_end, n0, g;
-    if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
+    int64_t m0, m_end, n0, g, kbase = 0, kbound = -1;
+    int KS = p.KS;
+    if constexpr (GK) {
+        if (!tile_of_gk<BM, BN>(p, m0, m_end, n0, g, kbase, kbound)) return;
+        KS = (int)((kbound + 127) / 128);
+        p.c = static_cast<uint8_t *>(p.c) + g * p.c_stride * (OUT_BF16 ? 2 : 4);
+    } else {
+        if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
+    }
     T t;
-    t.init(p, m0, m_end, n0, g, smem);
+    t.init(p, m0, m_end, n0, g, smem, kbase, kbound);
 
     v4f acc[FM][FN];
 #pragma unroll
@@ -450,10 +499,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     uint32_t sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
-    const int KS = p.KS;
-    if constexpr (!T::SA_LDS) t.fetch_sa(0, sa_nxt);
-    if constexpr (!T::SB_LDS) t.fetch_sb(0, sb_nxt);
-    t.issue(0, 0);
+    if (KS > 0) {                       // an empty group (grouped-K) stores zeros
+        if constexpr (!T::SA_LDS) t.fetch_sa(0, sa_nxt);
+        if constexpr (!T::SB_LDS) t.fetch_sb(0, sb_nxt);
+        t.issue(0, 0);
+    }
 
     for (int ks = 0; ks < KS; ++ks) {
         const int cur = ks & 1;
@@ -524,6 +574,7 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     p.NP = (int)packed_panels(N);
     p.G = 1;
     p.offsets = nullptr;
+    p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
     const int cus = device_cu_count();
     // 256x256 tiles (2 waves x 4, 128x64 per wave) unless that leaves the last
     // wave of tiles badly filled; then 256x128 (4 x 2 waves, 64x64 each).
@@ -540,6 +591,28 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     return launch_tile<256, 128, 4, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
 }
 
+hipError_t launch_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                     const uint8_t *b_s, const int32_t *offsets, int64_t G,
+                                     int64_t T, int64_t M, int64_t N, void *c, bool c_bf16,
+                                     hipStream_t stream) {
+    GemmParams p{};
+    p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = c;
+    p.M = M; p.N = N; p.K = T;
+    p.G = (int)G;
+    p.offsets = offsets;
+    p.lda = T; p.lsa = T / 32; p.ldb = T; p.lsb = T / 32;
+    p.c_stride = M * N;
+    constexpr int BM = 256, BN = 256;
+    p.tiles_m = (int)ceil_div(M, BM);
+    p.tiles_n = (int)ceil_div(N, BN);
+    dim3 grid((unsigned)(G * p.tiles_m * p.tiles_n)), block(kThreads);
+    if (c_bf16)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, 2, false, true, false, false, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, 2, false, false, false, false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                                const uint8_t *b_s, const int32_t *offsets, int64_t G,
                                int64_t M_total, int64_t N, int64_t K, void *c, bool c_bf16,
@@ -551,6 +624,7 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uin
     p.NP = (int)packed_panels(N);
     p.G = (int)G;
     p.offsets = offsets;
+    p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
     constexpr int BM = 128, BN = 256;
     p.tiles_m = (int)(ceil_div(M_total, BM) + G);
     p.tiles_n = (int)ceil_div(N, BN);

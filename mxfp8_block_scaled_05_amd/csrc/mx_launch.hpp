@@ -14,6 +14,16 @@ int device_cu_count();
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint8_t *q,
                            uint8_t *scales, hipStream_t stream);
 
+// x[batch][rows][cols] -> q[batch][cols][rows], scales[batch][cols][rows/32]
+hipError_t launch_quantize_axis0_batched(const uint16_t *x, int64_t batch, int64_t rows,
+                                         int64_t cols, uint8_t *q, uint8_t *scales,
+                                         hipStream_t stream);
+
+// axis-1 quantize of rows x[idx[i]] (zero rows for indices outside [0, rows_in))
+hipError_t launch_quantize_gather(const uint16_t *x, int64_t rows_in, int64_t cols,
+                                  const int64_t *idx, int64_t rows_out, uint8_t *q,
+                                  uint8_t *scales, hipStream_t stream);
+
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
                                 uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream);
 
@@ -52,6 +62,12 @@ hipError_t launch_selfcheck_ref(const uint16_t *x, int64_t M, int64_t N, int64_t
 // out[0] = ||y - yref|| / ||yref|| (NaN if not finite), out[1..2] the sums.
 hipError_t launch_selfcheck_error(const float *y, const float *yref, int64_t n, double *part,
                                   double *out, hipStream_t stream);
+
+// C[g] = A[:, o_g:o_g+1] B[:, o_g:o_g+1]^T, A [M][T], B [N][T] canonical (row stride T)
+hipError_t launch_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                     const uint8_t *b_s, const int32_t *offsets, int64_t G,
+                                     int64_t T, int64_t M, int64_t N, void *c, bool c_bf16,
+                                     hipStream_t stream);
 
 // Packed weight layout geometry (see mxfp8_repack in include/mxfp8.h).
 constexpr int64_t kPanelRows = 256;   // rows per packed panel

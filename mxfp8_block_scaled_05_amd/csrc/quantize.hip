@@ -189,6 +189,59 @@ __device__ __forceinline__ uint32_t quantize_row_block(const uint8_t *tile, int 
     return code;
 }
 
+// ---------------------------------------------------------------- gather + axis 1
+// Routing permute fused with the quantizer: output row i is input row
+// idx[i] (a row index outside [0, rows_in) -- the padding of an expert group
+// -- gives a zero row), quantized along its columns.  The same wave-step walk
+// as quantize_axis1_kernel over the output's blocks; a block never straddles
+// a row, so each lane pair reads one contiguous 64-byte block of its source
+// row.
+__device__ __forceinline__ void load_step_gather(const uint16_t *__restrict__ x, int64_t rows_in,
+                                                 int64_t bpr, const int64_t *__restrict__ idx,
+                                                 int64_t b0, int64_t nblocks, int lane,
+                                                 uint32_t (*d)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t blk = b0 + (u >> 1) * 32 + (lane >> 1);
+        d[u][0] = d[u][1] = d[u][2] = d[u][3] = 0;
+        if (blk < nblocks) {
+            const int64_t src = idx[blk / bpr];
+            if (src >= 0 && src < rows_in) {
+                const v4i v = *reinterpret_cast<const v4i *>(x + (src * bpr + blk % bpr) * 32 +
+                                                            (lane & 1) * 16 + (u & 1) * 8);
+                d[u][0] = v.x; d[u][1] = v.y; d[u][2] = v.z; d[u][3] = v.w;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void quantize_gather_kernel(const uint16_t *__restrict__ x,
+                                                              int64_t rows_in, int64_t bpr,
+                                                              const int64_t *__restrict__ idx,
+                                                              uint8_t *__restrict__ q,
+                                                              uint8_t *__restrict__ scales,
+                                                              int64_t nblocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t nsteps = (nblocks + 63) / 64;
+    int64_t step = wave;
+    if (step >= nsteps) return;
+    uint32_t cur[4][4], nxt[4][4];
+    load_step_gather(x, rows_in, bpr, idx, step * 64, nblocks, lane, cur);
+    for (; step < nsteps; step += nwaves) {
+        const bool more = step + nwaves < nsteps;
+        if (more) load_step_gather(x, rows_in, bpr, idx, (step + nwaves) * 64, nblocks, lane, nxt);
+        convert_step(q, scales, step * 64, nblocks, lane, cur);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) cur[u][k] = nxt[u][k];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- axis 0
 // x[rows][cols] -> q[cols][rows], scales[cols][rows/32].  A workgroup of four
 // waves owns a 128-row x 128-column tile and moves it through LDS twice:
@@ -271,12 +324,18 @@ __device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, u
 }
 
 // one workgroup per tile; tiles numbered row-tile-major over a 1-D grid
-__device__ __forceinline__ void tile_origin(int64_t cols, int64_t &R0, int64_t &C0) {
+// (batched: matrix-major)
+__device__ __forceinline__ void tile_origin(int64_t rows, int64_t cols, int64_t &b, int64_t &R0,
+                                            int64_t &C0) {
     const int64_t tiles_c = (cols + kA0Tile - 1) / kA0Tile;
-    R0 = (int64_t)(blockIdx.x / tiles_c) * kA0Tile;
-    C0 = (int64_t)(blockIdx.x % tiles_c) * kA0Tile;
+    const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * tiles_c;
+    const int64_t t = blockIdx.x % tiles;
+    b = blockIdx.x / tiles;
+    R0 = (t / tiles_c) * kA0Tile;
+    C0 = (t % tiles_c) * kA0Tile;
 }
 
+// x[batch][rows][cols] -> q[batch][cols][rows], scales[batch][cols][rows/32]
 __global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__restrict__ x,
                                                              uint8_t *__restrict__ q,
                                                              uint8_t *__restrict__ scales,
@@ -284,11 +343,12 @@ __global__ __launch_bounds__(256) void quantize_axis0_kernel(const uint16_t *__r
     __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
     __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
     static_assert(kA0Tile * kA0OutPitch <= (int)sizeof(tile), "output stage fits the input stage");
-    int64_t R0, C0;
-    tile_origin(cols, R0, C0);
-    load_tile<kA0Tile>(x, rows, cols, R0, C0, tile, threadIdx.x);
+    int64_t b, R0, C0;
+    tile_origin(rows, cols, b, R0, C0);
+    load_tile<kA0Tile>(x + b * rows * cols, rows, cols, R0, C0, tile, threadIdx.x);
     __syncthreads();
-    axis0_from_tile(tile, stile, q, scales, rows, cols, R0, C0, threadIdx.x);
+    axis0_from_tile(tile, stile, q + b * rows * cols, scales + b * cols * (rows / 32), rows, cols, R0,
+                    C0, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- both axes
@@ -306,8 +366,8 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t *__re
     __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
     __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
     const int t = threadIdx.x;
-    int64_t R0, C0;
-    tile_origin(cols, R0, C0);
+    int64_t b_unused, R0, C0;
+    tile_origin(rows, cols, b_unused, R0, C0);
     load_tile<kA0Tile>(x, rows, cols, R0, C0, tile, t);
     __syncthreads();
     const int64_t nb = cols / 32;
@@ -426,10 +486,32 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int ax
         hipLaunchKernelGGL(quantize_axis1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, q,
                            scales, nblocks);
     } else {
-        const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
-        hipLaunchKernelGGL(quantize_axis0_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x,
-                           q, scales, rows, cols);
+        return launch_quantize_axis0_batched(x, 1, rows, cols, q, scales, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_axis0_batched(const uint16_t *x, int64_t batch, int64_t rows,
+                                         int64_t cols, uint8_t *q, uint8_t *scales,
+                                         hipStream_t stream) {
+    const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
+    hipLaunchKernelGGL(quantize_axis0_kernel, dim3((unsigned)(batch * tiles)), dim3(256), 0, stream,
+                       x, q, scales, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_gather(const uint16_t *x, int64_t rows_in, int64_t cols,
+                                  const int64_t *idx, int64_t rows_out, uint8_t *q,
+                                  uint8_t *scales, hipStream_t stream) {
+    const int64_t bpr = cols / 32;
+    const int64_t nblocks = rows_out * bpr;
+    const int64_t nsteps = (nblocks + 63) / 64;
+    int64_t grid = (nsteps + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * (kQuantWavesPerCu / 4);
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(quantize_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                       rows_in, bpr, idx, q, scales, nblocks);
     return hipGetLastError();
 }
 

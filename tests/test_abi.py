@@ -77,3 +77,13 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_quantize_packed(p, 0, 4, 64, NULL, NULL, p, p, NULL) == 2   # batch
     assert libmx.mxfp8_quantize_packed(q, 1, 4, 64, NULL, NULL, p, p, NULL) == 5   # alignment
     assert libmx.mxfp8_quantize(p, 32, 32, 1, p, q, NULL) == 5                     # scales alignment
+    # MoE learner calls
+    assert libmx.mxfp8_quantize_batched(p, 0, 64, 64, 0, p, p, NULL) == 2           # batch
+    assert libmx.mxfp8_quantize_batched(p, 2, 48, 64, 0, p, p, NULL) == 2           # rows % 32 (axis 0)
+    assert libmx.mxfp8_quantize_batched(p, 2, 64, 64, 5, p, p, NULL) == 3           # axis
+    assert libmx.mxfp8_quantize_gather(p, 8, 64, NULL, 16, p, p, NULL) == 1          # index table
+    assert libmx.mxfp8_quantize_gather(p, 8, 40, p, 16, p, p, NULL) == 2             # cols % 32
+    assert libmx.mxfp8_grouped_gemm_wgrad(p, p, p, p, p, 0, 64, 8, 8, p, 0, NULL) == 2      # G
+    assert libmx.mxfp8_grouped_gemm_wgrad(p, p, p, p, p, 2, 48, 8, 8, p, 0, NULL) == 2      # T % 32
+    assert libmx.mxfp8_grouped_gemm_wgrad(p, p, p, p, p, 2, 1 << 23, 8, 8, p, 0, NULL) == 2  # T limit
+    assert libmx.mxfp8_grouped_gemm_wgrad(p, p, p, p, p, 2, 64, 8, 8, p, 7, NULL) == 4      # dtype

@@ -146,3 +146,36 @@ def test_lds_footprint(BM, BN, WM, packed, kalign):
             assert sb_off + w * 256 + 256 <= stage
     WN = WAVES // WM
     assert (BM // WM) % 16 == 0 and (BN // WN) % 16 == 0 and (BM // WM) // 16 >= 2
+
+
+def gk_descriptors(M, N, T, lo, hi, tm, tn, BM=256, BN=256):
+    """The grouped-K kernel's descriptors for tile (tm, tn) of a group with
+    token range [lo, hi): A [M][T] and B [N][T] canonical, row stride T."""
+    kb = hi - lo
+    m0, n0 = tm * BM, tn * BN
+    rows_a, rows_b = min(BM, M - m0), min(BN, N - n0)
+    return [("a_q", m0 * T + lo, (rows_a - 1) * T + kb, M * T),
+            ("a_s", m0 * (T // 32) + lo // 32, (rows_a - 1) * (T // 32) + kb // 32, M * (T // 32)),
+            ("b_q", n0 * T + lo, (rows_b - 1) * T + kb, N * T),
+            ("b_s", n0 * (T // 32) + lo // 32, (rows_b - 1) * (T // 32) + kb // 32, N * (T // 32))]
+
+
+@pytest.mark.parametrize("M,N,T,offsets", [(200, 300, 384, [0, 32, 32, 224, 384]),
+                                           (1536, 2048, 67616, [0, 7424, 7456, 67616]),
+                                           (768, 2048, 4096, [0, 0, 4096, 4096])])
+def test_grouped_k_descriptors_inside_buffers(M, N, T, offsets):
+    """Every byte a grouped-K tile may touch lies inside its operand buffer,
+    and in-range accesses (row < rows, k < group length) lie inside the
+    descriptor range while the first out-of-range row starts past it."""
+    for g in range(len(offsets) - 1):
+        lo, hi = offsets[g], offsets[g + 1]
+        for tm in range(ceil_div(M, 256)):
+            for tn in range(ceil_div(N, 256)):
+                for name, base, nbytes, size in gk_descriptors(M, N, T, lo, hi, tm, tn):
+                    assert base >= 0 and base + max(nbytes, 0) <= size, (name, g, tm, tn)
+                rows_a = min(256, M - tm * 256)
+                kb = hi - lo
+                if kb:
+                    # last valid element of the last valid row, and the first invalid row
+                    assert (rows_a - 1) * T + kb - 1 < (rows_a - 1) * T + kb
+                    assert rows_a * T >= (rows_a - 1) * T + kb

@@ -1,0 +1,135 @@
+"""GPU parity of the MoE learner calls against the oracle.
+
+mxfp8_quantize_batched and mxfp8_quantize_gather must equal the oracle's
+quantize (per matrix / of the gathered, zero-padded rows) bit for bit;
+mxfp8_grouped_gemm_wgrad must equal, per group, the oracle's GEMM over the
+group's token columns within 1e-4 * sum|ab| (+ bf16 rounding); an empty group
+must give exact zeros.  The expert data-gradient path (weights quantized
+along N per expert, repacked, grouped GEMM) is checked end to end.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from conftest import to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("moe-train case:", *a, flush=True)
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(3, 64, 96), (2, 96, 160), (4, 1536, 2048), (8, 2048, 768)])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_quantize_batched_matches_per_matrix(mx, oracle_mod, batch, rows, cols, axis):
+    _say("batched", batch, rows, cols, axis)
+    rng = np.random.default_rng(batch + rows + cols + axis)
+    x = wl.normal_bf16(rng, (batch, rows, cols), std=0.02)
+    q, s = mx.quantize_batched(to_dev(x), axis)
+    qh, sh = to_host(q), to_host(s)
+    for b in range(batch):
+        rq, rs = oracle_mod.quantize(x[b], axis)
+        assert np.array_equal(qh[b], rq) and np.array_equal(sh[b], rs), b
+
+
+def _routing(seed, tokens, experts, topk):
+    rng = np.random.default_rng(seed)
+    route = wl.zipf_topk_routing(rng, tokens, experts, topk)
+    offsets, row_token, counts = wl.group_layout(route, experts)
+    return rng, offsets, row_token, counts
+
+
+@pytest.mark.parametrize("tokens,experts,topk,hidden", [(64, 8, 2, 64), (512, 16, 4, 256), (8192, 128, 8, 2048)])
+def test_quantize_gather_matches_gathered_quantize(mx, oracle_mod, tokens, experts, topk, hidden):
+    _say("gather", tokens, experts, topk, hidden)
+    rng, offsets, row_token, _ = _routing(tokens + experts, tokens, experts, topk)
+    x = wl.normal_bf16(rng, (tokens, hidden))
+    idx = row_token.copy()
+    if idx.size > 8:
+        idx[3] = tokens + 5          # out of range -> zero row, never read
+        idx[5] = -7
+    q, s = mx.quantize_gather(to_dev(x), to_dev(idx))
+    gathered = np.zeros((idx.size, hidden), np.uint16)
+    ok = (idx >= 0) & (idx < tokens)
+    gathered[ok] = x[idx[ok]]
+    rq, rs = oracle_mod.quantize(gathered, 1)
+    assert np.array_equal(to_host(q), rq) and np.array_equal(to_host(s), rs)
+
+
+def _check_wgrad(oracle_mod, c_dev, aq, as_, bq, bs, offsets, out_dtype, rows=None):
+    G = len(offsets) - 1
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        cg = c_dev[g]
+        if hi == lo:
+            assert np.all(cg == 0), g
+            continue
+        A, As = np.ascontiguousarray(aq[:, lo:hi]), np.ascontiguousarray(as_[:, lo // 32:hi // 32])
+        B, Bs = np.ascontiguousarray(bq[:, lo:hi]), np.ascontiguousarray(bs[:, lo // 32:hi // 32])
+        c_ref, c_abs = oracle_mod.gemm(A, As, B, Bs, rows=rows)
+        got = cg if rows is None else cg[rows]
+        ok, worst = oracle_mod.gemm_bound_ok(got, c_ref, c_abs, out_dtype)
+        assert ok, (g, worst)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_wgrad_small_ragged_with_empty_group(mx, oracle_mod, out):
+    import torch
+    _say("wgrad small", out)
+    rng = np.random.default_rng(17)
+    T, M, N = 384, 200, 300
+    offsets = np.array([0, 32, 32, 224, 384], np.int32)      # group 1 empty
+    dy = wl.normal_bf16(rng, (T, M), std=2.0 ** -10)
+    x = wl.normal_bf16(rng, (T, N))
+    aq, as_ = mx.quantize(to_dev(dy), 0)                      # [M][T]
+    bq, bs = mx.quantize(to_dev(x), 0)                        # [N][T]
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    c = mx.grouped_gemm_wgrad(aq, as_, bq, bs, to_dev(offsets), dt)
+    torch.cuda.synchronize()
+    ch = to_host(c) if out == "f32" else wl.bf16_bits_to_f32(to_host(c))
+    _check_wgrad(oracle_mod, ch, to_host(aq), to_host(as_), to_host(bq), to_host(bs), offsets, out)
+
+
+def test_wgrad_moe_down_projection_sampled(mx, oracle_mod):
+    """Qwen3-30B-A3B down projection weight gradient over a Zipf(1.1) top-8
+    routing of 2048 tokens: dW_g[2048 x 768] = dY_g^T h_g per expert."""
+    import torch
+    _say("wgrad moe")
+    rng, offsets, row_token, counts = _routing(3, 2048, 128, 8)
+    T = int(offsets[-1])
+    real = row_token >= 0
+    dy = np.zeros((T, 2048), np.uint16)
+    dy[real] = wl.normal_bf16(rng, (int(real.sum()), 2048), std=2.0 ** -10)
+    h = np.zeros((T, 768), np.uint16)
+    h[real] = wl.normal_bf16(rng, (int(real.sum()), 768))
+    aq, as_ = mx.quantize(to_dev(dy), 0)
+    bq, bs = mx.quantize(to_dev(h), 0)
+    c = mx.grouped_gemm_wgrad(aq, as_, bq, bs, to_dev(offsets), torch.float32)
+    torch.cuda.synchronize()
+    ch = to_host(c)
+    rows = np.sort(rng.choice(2048, 48, replace=False))
+    _check_wgrad(oracle_mod, ch, to_host(aq), to_host(as_), to_host(bq), to_host(bs), offsets, "f32", rows=rows)
+
+
+def test_dgrad_through_transposed_expert_weights(mx, oracle_mod):
+    """dX = dH W_g per expert: W_g quantized along N (batched axis 0), repacked,
+    grouped GEMM -- against the oracle's grouped GEMM on the same grids."""
+    import torch
+    _say("dgrad")
+    G, N, K = 8, 256, 512
+    rng, offsets, row_token, _ = _routing(5, 256, G, 2)
+    Mt = int(offsets[-1])
+    w = wl.normal_bf16(rng, (G, N, K), std=0.02)             # forward weights [N][K]
+    wtq, wts = mx.quantize_batched(to_dev(w), 0)             # [G][K][N]
+    packed = mx.repack(wtq, wts)
+    dh = np.zeros((Mt, N), np.uint16)
+    real = row_token >= 0
+    dh[real] = wl.normal_bf16(rng, (int(real.sum()), N), std=2.0 ** -10)
+    aq, as_ = mx.quantize(to_dev(dh), 1)
+    c = mx.grouped_gemm(aq, as_, packed, to_dev(offsets), torch.float32)
+    torch.cuda.synchronize()
+    c_ref, c_abs, grp = oracle_mod.grouped_gemm(to_host(aq), to_host(as_), to_host(wtq), to_host(wts), offsets)
+    inside = grp >= 0
+    ok, worst = oracle_mod.gemm_bound_ok(to_host(c)[inside], c_ref[inside], c_abs[inside], "f32")
+    assert ok, worst
