@@ -53,7 +53,7 @@ struct GemmParams {
     int64_t c_stride;        // grouped-K: elements of one group's C
 };
 
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 4;
 // s_waitcnt immediate for gfx9 with expcnt and lgkmcnt left at their maximum:
 // vmcnt(n) for n < 64 (bits [3:0] and [15:14])
 constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
@@ -473,13 +473,33 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0
 // One barrier at the top of each step; copies of step k+1 overlap step k.
 // GK (grouped-K, weight gradients of the experts): C_g = A[:, K_g] B[:, K_g]^T
 // for every group g, K_g its token range, C_g at c + g * c_stride.
-template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false>
+// Copy instructions one wave issues per k-step (KALIGN: tiles and both scale
+// sets through LDS): its tile segments plus one scale copy per 64 rows it owns.
+template <int BM, int BN>
+__device__ __forceinline__ int copies_per_step(int w) {
+    return BM / (8 * kWaves) + BN / (8 * kWaves) + (w < BM / 64 ? 1 : 0) + (w < BN / 64 ? 1 : 0);
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [N0, N0 + 2]
+template <int N0>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+    if (n <= N0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(N0));
+    else if (n == N0 + 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(N0 + 1));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(N0 + 2));
+}
+
+// NST stages: the copies of step ks+NST-1 are issued at the top of step ks.
+// NST = 3 needs every copy to go through LDS (KALIGN) so that a wave's copy
+// count per step is fixed and the wait can leave the next steps in flight.
+template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false,
+          int NST = 2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
     constexpr int FM = T::FM, FN = T::FN;
-    static_assert(2 * T::STAGE <= 160 * 1024, "LDS budget");
+    static_assert(NST * T::STAGE <= 160 * 1024, "LDS budget");
     static_assert(!GK || (!BPACK && !KALIGN && !GROUPED), "grouped-K reads canonical operands");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
+    static_assert(NST == 2 || (NST == 3 && KALIGN), "three stages need all copies through LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * T::STAGE];
     int64_t m0, m_end, n0, g, kbase = 0, kbound = -1;
     int KS = p.KS;
     if constexpr (GK) {
@@ -503,11 +523,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         if constexpr (!T::SA_LDS) t.fetch_sa(0, sa_nxt);
         if constexpr (!T::SB_LDS) t.fetch_sb(0, sb_nxt);
         t.issue(0, 0);
+        if constexpr (NST == 3) {
+            if (KS > 1) t.issue(1, 1);
+        }
     }
+    const int ncopies = copies_per_step<BM, BN>(t.w);
 
+    int cur = 0;
     for (int ks = 0; ks < KS; ++ks) {
-        const int cur = ks & 1;
-        wait_copies_and_sync();
+        if constexpr (NST == 3) {
+            // this wave's copies of step ks have landed: only those of step
+            // ks+1 (issued after them, if any) may still be in flight
+            if (ks + 1 < KS) wait_vm_upto<BM / (8 * kWaves) + BN / (8 * kWaves)>(ncopies);
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            __syncthreads();
+        } else {
+            wait_copies_and_sync();
+        }
         if constexpr (!T::SA_LDS) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
@@ -518,7 +550,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
             if (ks + 1 < KS) t.fetch_sb(ks + 1, sb_nxt);
         }
-        if (ks + 1 < KS) t.issue(ks + 1, cur ^ 1);
+        if constexpr (NST == 3) {
+            // stage (cur + 2) % 3 held step ks-1, which every wave finished
+            // before the barrier above
+            if (ks + 2 < KS) t.issue(ks + 2, cur == 0 ? 2 : cur - 1);
+        } else {
+            if (ks + 1 < KS) t.issue(ks + 1, cur ^ 1);
+        }
 
         const uint8_t *st = smem + cur * T::STAGE;
         int sas[FM], sbs[FN];
@@ -534,7 +572,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         v8i bf[FN];
         t.lds_bfrags(st, bf);
         t.mma_rows(st, 0, FM, bf, sas, sbs, acc);
+        cur = cur + 1 == NST ? 0 : cur + 1;
     }
+    (void)ncopies;
     const int64_t row0 = m0 + t.wm * T::WTM, col0 = n0 + t.wn * T::WTN;
     constexpr int ES = OUT_BF16 ? 2 : 4;
     // uniform over the workgroup: the tile's columns inside C, rows 16 B
@@ -542,25 +582,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const bool inside = n0 + BN <= p.N && (p.N * ES) % 16 == 0;
     if (inside) {
         __syncthreads();                    // every wave is done with the stages
-        store_tile_lds<FM, FN, OUT_BF16, 2 * T::STAGE>(p, row0, col0, m_end, acc, t.lane, t.w, smem);
+        store_tile_lds<FM, FN, OUT_BF16, NST * T::STAGE>(p, row0, col0, m_end, acc, t.lane, t.w, smem);
     } else {
         store_tile_scalar<FM, FN, OUT_BF16>(p, row0, col0, m_end, acc, t.lane);
     }
 }
+
+// Pipeline depth.  Measured: a third stage (where it fits the LDS) speeds up
+// the grouped expert GEMMs (short K per tile: 443 -> 412 us and 315 -> 301 us
+// on the MoE layer) but slows the dense 256x128 qkv GEMM (127 -> 136 us), so
+// only grouped launches take it.
+template <int BM, int BN, int WM, bool BP, bool GROUPED>
+constexpr int kStages3 = GROUPED && 3 * TileOps<BM, BN, WM, BP, true>::STAGE <= 160 * 1024 ? 3 : 2;
 
 template <int BM, int BN, int WM, bool GROUPED>
 static hipError_t launch_tile(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
     dim3 grid((unsigned)nwg), block(kThreads);
     const bool kal = p.K % 128 == 0;
 #define MX_LAUNCH2(BP, BF, KA) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, GROUPED, KA>), grid, block, 0, s, p)
+#define MX_LAUNCH3(BP, BF) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, GROUPED, true, false, kStages3<BM, BN, WM, BP, GROUPED>>), grid, block, 0, s, p)
     if (kal) {
-        if (b_packed) { if (c_bf16) MX_LAUNCH2(true, true, true); else MX_LAUNCH2(true, false, true); }
-        else { if (c_bf16) MX_LAUNCH2(false, true, true); else MX_LAUNCH2(false, false, true); }
+        if (b_packed) { if (c_bf16) MX_LAUNCH3(true, true); else MX_LAUNCH3(true, false); }
+        else { if (c_bf16) MX_LAUNCH3(false, true); else MX_LAUNCH3(false, false); }
     } else {
         if (b_packed) { if (c_bf16) MX_LAUNCH2(true, true, false); else MX_LAUNCH2(true, false, false); }
         else { if (c_bf16) MX_LAUNCH2(false, true, false); else MX_LAUNCH2(false, false, false); }
     }
 #undef MX_LAUNCH2
+#undef MX_LAUNCH3
     return hipGetLastError();
 }
 
