@@ -51,6 +51,7 @@ struct GemmParams {
     // except in grouped-K mode where rows span all groups' tokens
     int64_t lda, lsa, ldb, lsb;
     int64_t c_stride;        // grouped-K: elements of one group's C
+    int mix_big, mix_big_cols;   // mixed dense launch: 256x256 tiles and their tile columns
 };
 
 constexpr int kGroupM = 4;
@@ -488,27 +489,17 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(N0 + 2));
 }
 
+// One BM x BN tile of C: k-loop over [kbase, kbase + kbound) of every row
+// (KS k-steps) and the store.  smem holds NST stages.
 // NST stages: the copies of step ks+NST-1 are issued at the top of step ks.
 // NST = 3 needs every copy to go through LDS (KALIGN) so that a wave's copy
 // count per step is fixed and the wait can leave the next steps in flight.
-template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false,
-          int NST = 2>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool KALIGN, int NST>
+__device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_end, int64_t n0, int64_t g,
+                                          int64_t kbase, int64_t kbound, int KS, uint8_t *smem) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
     constexpr int FM = T::FM, FN = T::FN;
-    static_assert(NST * T::STAGE <= 160 * 1024, "LDS budget");
-    static_assert(!GK || (!BPACK && !KALIGN && !GROUPED), "grouped-K reads canonical operands");
     static_assert(NST == 2 || (NST == 3 && KALIGN), "three stages need all copies through LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * T::STAGE];
-    int64_t m0, m_end, n0, g, kbase = 0, kbound = -1;
-    int KS = p.KS;
-    if constexpr (GK) {
-        if (!tile_of_gk<BM, BN>(p, m0, m_end, n0, g, kbase, kbound)) return;
-        KS = (int)((kbound + 127) / 128);
-        p.c = static_cast<uint8_t *>(p.c) + g * p.c_stride * (OUT_BF16 ? 2 : 4);
-    } else {
-        if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
-    }
     T t;
     t.init(p, m0, m_end, n0, g, smem, kbase, kbound);
 
@@ -588,6 +579,51 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
+template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false,
+          int NST = 2>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+    using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
+    static_assert(NST * T::STAGE <= 160 * 1024, "LDS budget");
+    static_assert(!GK || (!BPACK && !KALIGN && !GROUPED), "grouped-K reads canonical operands");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * T::STAGE];
+    int64_t m0, m_end, n0, g, kbase = 0, kbound = -1;
+    int KS = p.KS;
+    if constexpr (GK) {
+        if (!tile_of_gk<BM, BN>(p, m0, m_end, n0, g, kbase, kbound)) return;
+        KS = (int)((kbound + 127) / 128);
+        p.c = static_cast<uint8_t *>(p.c) + g * p.c_stride * (OUT_BF16 ? 2 : 4);
+    } else {
+        if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
+    }
+    gemm_tile<BM, BN, WM, BPACK, OUT_BF16, KALIGN, NST>(p, m0, m_end, n0, g, kbase, kbound, KS, smem);
+}
+
+// Dense C in two tile shapes in one launch: workgroups [0, mix_big) take the
+// 256x256 tiles of columns [0, 256 * mix_big_cols), the rest the 256x128
+// tiles of the remaining columns.  The large tiles come first in dispatch
+// order, so they fill the chip's first wave and the small ones the tail.
+// Each range is renumbered XCD-aware on its own (mix_big is a multiple of 8,
+// so a workgroup's XCD is its id mod 8 in both).
+template <bool BPACK, bool OUT_BF16, bool KALIGN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
+    constexpr int SB = TileOps<256, 256, 2, BPACK, KALIGN>::STAGE, SS = TileOps<256, 128, 4, BPACK, KALIGN>::STAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (SB > SS ? SB : SS)];
+    const int bid = blockIdx.x;
+    int tm, tn;
+    if (bid < p.mix_big) {
+        grouped_order(xcd_logical(bid, p.mix_big), p.tiles_m, p.mix_big_cols, tm, tn);
+        gemm_tile<256, 256, 2, BPACK, OUT_BF16, KALIGN, 2>(p, (int64_t)tm * 256, p.M, (int64_t)tn * 256, 0, 0,
+                                                           -1, p.KS, smem);
+    } else {
+        const int n_small = (int)gridDim.x - p.mix_big;
+        const int small_cols = n_small / p.tiles_m;
+        grouped_order(xcd_logical(bid - p.mix_big, n_small), p.tiles_m, small_cols, tm, tn);
+        gemm_tile<256, 128, 4, BPACK, OUT_BF16, KALIGN, 2>(p, (int64_t)tm * 256, p.M,
+                                                           (int64_t)p.mix_big_cols * 256 + (int64_t)tn * 128, 0,
+                                                           0, -1, p.KS, smem);
+    }
+}
+
 // Pipeline depth.  Measured: a third stage (where it fits the LDS) speeds up
 // the grouped expert GEMMs (short K per tile: 443 -> 412 us and 315 -> 301 us
 // on the MoE layer) but slows the dense 256x128 qkv GEMM (127 -> 136 us), so
@@ -613,6 +649,39 @@ static hipError_t launch_tile(const GemmParams &p, bool b_packed, bool c_bf16, i
     return hipGetLastError();
 }
 
+// Dense tile shapes.  A 256x256 tile moves 1.0 byte of operands per output
+// per k-step, a 256x128 tile 1.5, and the copy path from L2 into LDS is the
+// kernels' limit: measured per k-step, a 256x128 tile takes ~0.66 of a
+// 256x256 tile's time.  With one workgroup per CU, the launch takes as many
+// rounds of tiles as ceil(tiles / CUs); the choice minimises the estimated
+// total: all 256x256, all 256x128, or whole rounds of 256x256 tiles over
+// the leading columns followed by 256x128 tiles over the rest.
+DenseTiling dense_tiling(int64_t M, int64_t N, int cus) {
+    constexpr double kSmall = 0.66;
+    const int64_t tm = ceil_div(M, 256), tn_big = ceil_div(N, 256), tn_small = ceil_div(N, 128);
+    DenseTiling best{(int)tn_big, 0};
+    double best_t = (double)ceil_div(tm * tn_big, (int64_t)cus);
+    if (N <= 128) return best;
+    const double t_small = kSmall * (double)ceil_div(tm * tn_small, (int64_t)cus);
+    if (t_small < best_t) {
+        best = DenseTiling{0, (int)tn_small};
+        best_t = t_small;
+    }
+    // whole rounds of large tiles, whole tile columns, workgroup count a multiple of 8
+    for (int64_t rounds = 1; rounds * cus < tm * tn_big; ++rounds) {
+        int64_t cols = rounds * cus / tm;
+        while (cols > 0 && (tm * cols) % 8 != 0) --cols;
+        if (cols <= 0 || cols >= tn_big) continue;
+        const int64_t rest = ceil_div(N - cols * 256, 128);
+        const double t = (double)ceil_div(tm * cols, (int64_t)cus) + kSmall * (double)ceil_div(tm * rest, (int64_t)cus);
+        if (t < best_t - 1e-9) {
+            best = DenseTiling{(int)cols, (int)rest};
+            best_t = t;
+        }
+    }
+    return best;
+}
+
 hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                        const uint8_t *b_s, bool b_packed, int64_t M, int64_t N, int64_t K, void *c,
                        bool c_bf16, hipStream_t stream) {
@@ -625,18 +694,30 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     p.offsets = nullptr;
     p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
     const int cus = device_cu_count();
-    // 256x256 tiles (2 waves x 4, 128x64 per wave) unless that leaves the last
-    // wave of tiles badly filled; then 256x128 (4 x 2 waves, 64x64 each).
-    const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
-    const int64_t waves256 = ceil_div(t256, cus);
-    const double fill256 = (double)t256 / (double)(waves256 * cus);
-    if (fill256 >= 0.85 || N <= 128) {
-        p.tiles_m = (int)ceil_div(M, 256);
-        p.tiles_n = (int)ceil_div(N, 256);
+    const DenseTiling d = dense_tiling(M, N, cus);
+    p.tiles_m = (int)ceil_div(M, 256);
+    if (d.big_cols > 0 && d.small_cols > 0) {
+        p.tiles_n = d.big_cols + d.small_cols;
+        p.mix_big = p.tiles_m * d.big_cols;
+        p.mix_big_cols = d.big_cols;
+        dim3 grid((unsigned)(p.mix_big + p.tiles_m * d.small_cols)), block(kThreads);
+        const bool kal = K % 128 == 0;
+#define MX_MIXED(BP, BF, KA) hipLaunchKernelGGL((gemm_mixed_kernel<BP, BF, KA>), grid, block, 0, stream, p)
+        if (kal) {
+            if (b_packed) { if (c_bf16) MX_MIXED(true, true, true); else MX_MIXED(true, false, true); }
+            else { if (c_bf16) MX_MIXED(false, true, true); else MX_MIXED(false, false, true); }
+        } else {
+            if (b_packed) { if (c_bf16) MX_MIXED(true, true, false); else MX_MIXED(true, false, false); }
+            else { if (c_bf16) MX_MIXED(false, true, false); else MX_MIXED(false, false, false); }
+        }
+#undef MX_MIXED
+        return hipGetLastError();
+    }
+    if (d.big_cols > 0) {
+        p.tiles_n = d.big_cols;
         return launch_tile<256, 256, 2, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
     }
-    p.tiles_m = (int)ceil_div(M, 256);
-    p.tiles_n = (int)ceil_div(N, 128);
+    p.tiles_n = d.small_cols;
     return launch_tile<256, 128, 4, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
 }
 

@@ -11,6 +11,13 @@ namespace mx {
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Dense GEMM tiling: big_cols tile columns of 256x256 tiles over the leading
+// columns, then small_cols tile columns of 256x128 tiles (either may be 0).
+struct DenseTiling {
+    int big_cols, small_cols;
+};
+DenseTiling dense_tiling(int64_t M, int64_t N, int cus);
+
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint8_t *q,
                            uint8_t *scales, hipStream_t stream);
 

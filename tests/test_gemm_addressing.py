@@ -21,13 +21,58 @@ def ceil_div(a, b):
     return (a + b - 1) // b
 
 
-def dense_cfg(M, N, cus=256):
-    t256 = ceil_div(M, 256) * ceil_div(N, 256)
-    waves = ceil_div(t256, cus)
-    fill = t256 / (waves * cus)
-    if fill >= 0.85 or N <= 128:
-        return 256, 256
-    return 256, 128
+def dense_tiling(M, N, cus=256):
+    """Mirror of the launcher's dense tiling: (big_cols, small_cols) tile
+    columns of 256x256 tiles, then of 256x128 tiles, minimising the estimated
+    rounds of tiles (a 256x128 tile costs 0.66 of a 256x256 one)."""
+    small = 0.66
+    tm, tn_big, tn_small = ceil_div(M, 256), ceil_div(N, 256), ceil_div(N, 128)
+    best, best_t = (tn_big, 0), ceil_div(tm * tn_big, cus)
+    if N <= 128:
+        return best
+    t = small * ceil_div(tm * tn_small, cus)
+    if t < best_t:
+        best, best_t = (0, tn_small), t
+    rounds = 1
+    while rounds * cus < tm * tn_big:
+        cols = rounds * cus // tm
+        while cols > 0 and (tm * cols) % 8:
+            cols -= 1
+        if 0 < cols < tn_big:
+            rest = ceil_div(N - cols * 256, 128)
+            t = ceil_div(tm * cols, cus) + small * ceil_div(tm * rest, cus)
+            if t < best_t - 1e-9:
+                best, best_t = (cols, rest), t
+        rounds += 1
+    return best
+
+
+def dense_tiles(M, N):
+    """(m0, n0, BM, BN) of every tile of a dense launch."""
+    big, small = dense_tiling(M, N)
+    out = []
+    for tm in range(ceil_div(M, 256)):
+        out += [(tm * 256, tn * 256, 256, 256) for tn in range(big)]
+        out += [(tm * 256, big * 256 + tn * 128, 256, 128) for tn in range(small)]
+    return out
+
+
+def test_dense_tiling_covers_c_once():
+    """Every column of C lies in exactly one tile column, the mixed launch's
+    large-tile count is a multiple of 8, and the qkv layer takes the mixed form."""
+    for M, N, K in DENSE_SHAPES + [(500, 32968, 160), (512, 32768, 256)]:
+        big, small = dense_tiling(M, N)
+        assert big * 256 + small * 128 >= N                      # every column covered
+        if small:
+            assert big * 256 + (small - 1) * 128 < N             # no empty small column
+        else:
+            assert (big - 1) * 256 < N                           # no empty large column
+        if big and small:
+            assert (ceil_div(M, 256) * big) % 8 == 0
+    assert dense_tiling(4096, 6144) == (16, 16)
+    assert dense_tiling(500, 32968) == (128, 2)
+    assert dense_tiling(8192, 24576) == (96, 0)
+    assert dense_tiling(1024, 6144) == (0, 48)
 
 
 def descriptors(M, N, K, BM, BN, packed, G=1, m0=0, m_end=None, n0=0, g=0):
@@ -65,16 +110,15 @@ DENSE_SHAPES = [(64, 256, 256), (200, 300, 416), (256, 512, 1024), (33, 17, 32),
                 (64, 1000, 2080), (1000, 96, 160), (4096, 6144, 4096), (8192, 24576, 4096),
                 (8192, 4096, 12288), (8192, 4096, 24576), (8192, 12288, 4096),
                 (24576, 4096, 8192), (4096, 12288, 8192), (64, 48, 512), (512, 768, 1024),
-                (256, 320, 192), (512, 256, 128)]
+                (256, 320, 192), (512, 256, 128), (500, 32968, 160), (512, 32768, 256),
+                (2048, 12288, 4096), (3072, 6144, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_SHAPES)
 @pytest.mark.parametrize("packed", [False, True])
 def test_dense_descriptors_inside_buffers(M, N, K, packed):
-    BM, BN = dense_cfg(M, N)
-    for tm in range(ceil_div(M, BM)):
-        for tn in range(ceil_div(N, BN)):
-            check_tile(M, N, K, BM, BN, packed, m0=tm * BM, n0=tn * BN)
+    for m0, n0, BM, BN in dense_tiles(M, N):
+        check_tile(M, N, K, BM, BN, packed, m0=m0, n0=n0)
 
 
 def grouped_tiles(offsets, M_total, BM):
@@ -117,19 +161,21 @@ def stage_bytes(BM, BN, packed, kalign):
     return (BM + BN) * 128 + (BM * 4 if sa_lds else 0) + (BN * 4 if sb_lds else 0)
 
 
-def stages_for(BM, BN, kalign):
-    """the launcher's choice: three stages when K % 128 == 0 and they fit"""
+def stages_for(BM, BN, kalign, grouped):
+    """the launcher's choice: three stages for grouped launches when K % 128 == 0
+    and they fit, else two"""
     fits3 = all(3 * stage_bytes(BM, BN, pk, True) <= 160 * 1024 for pk in (False, True))
-    return 3 if (kalign and fits3) else 2
+    return 3 if (grouped and kalign and fits3) else 2
 
 
-@pytest.mark.parametrize("BM,BN,WM", [(256, 256, 2), (256, 128, 4), (128, 256, 2)])
+@pytest.mark.parametrize("BM,BN,WM,grouped", [(256, 256, 2, False), (256, 128, 4, False), (128, 256, 2, True)])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("kalign", [False, True])
-def test_lds_footprint(BM, BN, WM, packed, kalign):
+def test_lds_footprint(BM, BN, WM, grouped, packed, kalign):
     """NST stages of [A tile | B tile | A scales | B scales] fit the 160 KB of
-    LDS and every copy lands inside its region; the wave grid tiles the block."""
-    nst = stages_for(BM, BN, kalign)
+    LDS and every copy lands inside its region; the wave grid tiles the block.
+    (The mixed dense launch allocates two stages of its larger tile.)"""
+    nst = stages_for(BM, BN, kalign, grouped)
     sa_lds, sb_lds = kalign, packed or kalign
     tile = (BM + BN) * 128
     sa_off = tile

@@ -174,6 +174,29 @@ def test_gemm_random_ragged(mx, oracle_mod, M, N, K, out):
     assert np.array_equal(cs[0], cs[1])
 
 
+@pytest.mark.parametrize("M,N,K,out", [(500, 32968, 160, "f32"), (512, 32768, 256, "bf16")])
+def test_gemm_mixed_tiles_full_output(mx, oracle_mod, M, N, K, out):
+    """Shapes whose tile count leaves a partial round of 256x256 tiles launch
+    256x256 tiles over the leading columns and 256x128 tiles over the rest in
+    one grid (the qkv layer's launch form).  Every element is checked, with
+    ragged M and N tails and K either a multiple of 128 or not."""
+    rng = np.random.default_rng(M + N + K)
+    X = wl.normal_bf16(rng, (M, K))
+    W = wl.normal_bf16(rng, (N, K), std=0.02)
+    xq, xs = _quant_pair(oracle_mod, X)
+    wq, ws = _quant_pair(oracle_mod, W)
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    cs = []
+    for packed in (False, True):
+        _say("gemm mixed tiles", M, N, K, out, packed)
+        c = _gemm_dev(mx, xq, xs, wq, ws, packed, tdt)
+        ok, worst = oracle_mod.gemm_bound_ok(c, ref, sabs, out)
+        assert ok, (packed, worst)
+        cs.append(c)
+    assert np.array_equal(cs[0], cs[1])
+
+
 def test_gemm_dgrad_wgrad_orientations(mx, oracle_mod):
     """The learner's three GEMMs through one A*B^T: fprop (X, W along K),
     dgrad (dY along N, W quantized with axis 0), wgrad (dY, X along tokens)."""
