@@ -75,8 +75,24 @@ class KernelTimer:
     def averages_us(self):
         return {k: 1e3 * float(np.mean([s.elapsed_time(e) for s, e in v])) for k, v in self.pending.items()}
 
+    def medians_us(self):
+        return {k: 1e3 * float(np.median([s.elapsed_time(e) for s, e in v])) for k, v in self.pending.items()}
+
     def reset(self):
         self.pending = {}
+
+
+def host_description():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "omp_num_threads": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))}
 
 
 def bench_qkv(args, dev):
@@ -131,6 +147,7 @@ def bench_qkv(args, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     avg = timer.averages_us()
+    med = timer.medians_us()
     ms_per_step = 1e3 * wall / args.steps
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (avg["gemm"] * 1e-6) / 1e12
@@ -141,6 +158,8 @@ def bench_qkv(args, dev):
         "gemm": {"us": round(avg["gemm"], 2), "TFLOP/s": round(gemm_tflops, 1),
                  "frac_mxfp8_peak": round(gemm_tflops / MXFP8_PEAK_TFLOPS, 4)},
     }
+    for k in kern:
+        kern[k]["median_us"] = round(med[k], 2)
     out = {
         "metric": "MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
@@ -736,7 +755,10 @@ def cpu_baseline_qkv(min_seconds: float = 10.0):
         steps += 1
     total = sum(t.values())
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    one = _oracle_single_core()
     return {
+        "host": host_description(),
+        "single_core": one,
         "value": round(2.0 * M * N * K * steps / total / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": cores,
@@ -745,6 +767,48 @@ def cpu_baseline_qkv(min_seconds: float = 10.0):
                   "fp64 GEMM of all 4096 rows), %.1f s in total" % (steps, total),
         "seconds_per_step": {k: round(v / steps, 3) for k, v in t.items()},
     }
+
+
+def _oracle_single_core_sample():
+    """One host thread: the oracle's quantize of W and X and pack of W at full
+    size, and its fp64 GEMM over the first 64 rows of X (no extrapolation)."""
+    import oracle
+    import workloads as wl
+    oracle._load()
+    d = wl.qkv(0)
+    M, K = d["X"].shape
+    N = d["W"].shape[0]
+    t0 = time.perf_counter()
+    wq, ws = oracle.quantize(d["W"], 1)
+    xq, xs = oracle.quantize(d["X"], 1)
+    tq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.pack(wq, ws, 1, N, K)
+    tp = time.perf_counter() - t0
+    rows = np.arange(64)
+    t0 = time.perf_counter()
+    oracle.gemm(xq, xs, wq, ws, rows=rows)
+    tg = time.perf_counter() - t0
+    qbytes = (N * K + M * K) * Q_BYTES_PER_ELT
+    return {"quantize_GB/s": round(qbytes / tq / 1e9, 3),
+            "repack_GB/s": round(N * K * REPACK_BYTES_PER_ELT / tp / 1e9, 3),
+            "gemm_GFLOP/s": round(2.0 * rows.size * N * K / tg / 1e9, 3),
+            "sample": "quantize W[6144x4096] and X[4096x4096], pack W, fp64 GEMM of 64 rows x 6144 x 4096",
+            "seconds": round(tq + tp + tg, 3)}
+
+
+def _oracle_single_core():
+    """_oracle_single_core_sample in a child process limited to one OpenMP
+    thread (the child touches no GPU)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    code = "import json, bench; print(json.dumps(bench._oracle_single_core_sample()))"
+    try:
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                           timeout=300)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        return None
 
 
 def copy_calibration(dev, nbytes: int = 512 << 20, reps: int = 3):
