@@ -440,6 +440,10 @@ def bench_moe_train(args, dev):
       backward: dY quantized along both axes -> dgrad down (grouped GEMM vs
         W_d^T), wgrad down (grouped-K GEMM dY^T h); dH quantized along both
         axes -> dgrad gate_up, wgrad gate_up (grouped-K GEMM dH^T X).
+    The token-blocked (axis-0) grids that feed the weight gradients are
+    written regrouped, every expert's tokens starting on a multiple of 128
+    (mxfp8_quantize_dual_grouped), so the weight-gradient GEMMs run aligned;
+    the same GEMMs over the 32-padded grids are timed beside the step.
     The activation function between gate_up and down is outside the MXFP8
     path; h and dH are drawn as N(0,1) and N(0,1)*2^-10 on real rows."""
     import torch
@@ -465,6 +469,10 @@ def bench_moe_train(args, dev):
          "Xperm": _bf16_dev(Xperm, dev)}
     idx = torch.from_numpy(d["row_token"]).to(dev)
     offs = torch.from_numpy(offs_np).to(dev)
+    sizes = np.diff(offs_np.astype(np.int64))
+    offs128_np = np.concatenate([[0], np.cumsum(-(-sizes // 128) * 128)]).astype(np.int32)
+    T128 = int(offs128_np[-1])
+    offs128 = torch.from_numpy(offs128_np).to(dev)
     del d, dY, dH, Xperm
     u8 = dict(dtype=torch.uint8, device=dev)
 
@@ -476,12 +484,12 @@ def bench_moe_train(args, dev):
     wdT = (torch.empty((G, I, H), **u8), torch.empty((G, I, H // 32), **u8))
     xq = (torch.empty((Mt, H), **u8), torch.empty((Mt, H // 32), **u8))
     h1 = (torch.empty((Mt, I), **u8), torch.empty((Mt, I // 32), **u8))
-    h0 = (torch.empty((I, Mt), **u8), torch.empty((I, Mt // 32), **u8))
+    h0 = (torch.empty((I, T128), **u8), torch.empty((I, T128 // 32), **u8))
     dy1 = (torch.empty((Mt, H), **u8), torch.empty((Mt, H // 32), **u8))
-    dy0 = (torch.empty((H, Mt), **u8), torch.empty((H, Mt // 32), **u8))
+    dy0 = (torch.empty((H, T128), **u8), torch.empty((H, T128 // 32), **u8))
     dh1 = (torch.empty((Mt, I2), **u8), torch.empty((Mt, I2 // 32), **u8))
-    dh0 = (torch.empty((I2, Mt), **u8), torch.empty((I2, Mt // 32), **u8))
-    x0 = (torch.empty((H, Mt), **u8), torch.empty((H, Mt // 32), **u8))
+    dh0 = (torch.empty((I2, T128), **u8), torch.empty((I2, T128 // 32), **u8))
+    x0 = (torch.empty((H, T128), **u8), torch.empty((H, T128 // 32), **u8))
     bf = dict(dtype=torch.bfloat16, device=dev)
     y_gu, y_d = torch.empty((Mt, I2), **bf), torch.empty((Mt, H), **bf)
     g_h, g_x = torch.empty((Mt, I), **bf), torch.empty((Mt, H), **bf)
@@ -498,18 +506,31 @@ def bench_moe_train(args, dev):
         ("repack_dT", lambda: mx.repack_(wdT[0], wdT[1], P_dT)),
         ("gather_quantize_X", lambda: mx.quantize_gather_into(t["X"], idx, *xq)),
         ("fprop_gate_up", lambda: mx.grouped_gemm(xq[0], xq[1], P_gu, offs, torch.bfloat16, out=y_gu)),
-        ("quantize_dual_h", lambda: mx.quantize_dual_into(t["A_d"], *h1, *h0)),
+        ("quantize_dual_h", lambda: mx.quantize_dual_grouped_into(t["A_d"], offs, offs128, *h0, *h1)),
         ("fprop_down", lambda: mx.grouped_gemm(h1[0], h1[1], P_d, offs, torch.bfloat16, out=y_d)),
-        ("quantize_dual_dY", lambda: mx.quantize_dual_into(t["dY"], *dy1, *dy0)),
+        ("quantize_dual_dY", lambda: mx.quantize_dual_grouped_into(t["dY"], offs, offs128, *dy0, *dy1)),
         ("dgrad_down", lambda: mx.grouped_gemm(dy1[0], dy1[1], P_dT, offs, torch.bfloat16, out=g_h)),
-        ("wgrad_down", lambda: mx.grouped_gemm_wgrad(dy0[0], dy0[1], h0[0], h0[1], offs, torch.float32, out=dW_d)),
-        ("quantize_dual_dH", lambda: mx.quantize_dual_into(t["dH"], *dh1, *dh0)),
+        ("wgrad_down", lambda: mx.grouped_gemm_wgrad(dy0[0], dy0[1], h0[0], h0[1], offs128, torch.float32,
+                                                     out=dW_d)),
+        ("quantize_dual_dH", lambda: mx.quantize_dual_grouped_into(t["dH"], offs, offs128, *dh0, *dh1)),
         ("dgrad_gate_up", lambda: mx.grouped_gemm(dh1[0], dh1[1], P_guT, offs, torch.bfloat16, out=g_x)),
-        ("quantize_X_axis0", lambda: mx.quantize_into(t["Xperm"], 0, *x0)),
-        ("wgrad_gate_up", lambda: mx.grouped_gemm_wgrad(dh0[0], dh0[1], x0[0], x0[1], offs, torch.float32, out=dW_gu)),
+        ("quantize_X_axis0", lambda: mx.quantize_dual_grouped_into(t["Xperm"], offs, offs128, *x0)),
+        ("wgrad_gate_up", lambda: mx.grouped_gemm_wgrad(dh0[0], dh0[1], x0[0], x0[1], offs128, torch.float32,
+                                                        out=dW_gu)),
     ]
     torch.cuda.synchronize()
     ms, avg = run_timed(ops, args)
+    # the weight-gradient GEMMs over the 32-padded token grids, for comparison
+    # (operands quantized once, outside the timing)
+    p32 = {}
+    for name, src, cols in (("dY", t["dY"], H), ("h", t["A_d"], I), ("dH", t["dH"], I2), ("X", t["Xperm"], H)):
+        p32[name] = (torch.empty((cols, Mt), **u8), torch.empty((cols, Mt // 32), **u8))
+        mx.quantize_into(src, 0, *p32[name])
+    cmp_ops = [("wgrad_down_32", lambda: mx.grouped_gemm_wgrad(*p32["dY"], *p32["h"], offs, torch.float32, out=dW_d)),
+               ("wgrad_gate_up_32", lambda: mx.grouped_gemm_wgrad(*p32["dH"], *p32["X"], offs, torch.float32,
+                                                                   out=dW_gu))]
+    _, avg32 = run_timed(cmp_ops, argparse.Namespace(steps=max(5, args.steps // 4), warmup=2))
+    del p32
     f_gu = 2.0 * real * I2 * H
     f_d = 2.0 * real * H * I
     flops = {"fprop_gate_up": f_gu, "fprop_down": f_d, "dgrad_down": f_d, "wgrad_down": f_d,
@@ -521,6 +542,10 @@ def bench_moe_train(args, dev):
             kern[name] = {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4)}
         else:
             kern[name] = {"us": round(us, 2)}
+    for name, us in avg32.items():
+        tf = flops[name[:-3]] / (us * 1e-6) / 1e12
+        kern[name] = {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4),
+                      "note": "32-padded token grids, not part of the step"}
     total = sum(flops.values())
     gemm_us = sum(avg[k] for k in flops)
     return _line("MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",
@@ -528,7 +553,8 @@ def bench_moe_train(args, dev):
                  "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out (fprop/dgrad), fp32 out (wgrad)",
                  {"workload": "qwen3-30b-a3b MoE expert layer learner micro-batch: 8192 tokens, 128 experts, "
                               "Zipf(1.1) top-8, forward + dgrad + wgrad of gate_up and down",
-                  "tokens": 8192, "experts": G, "rows_real": real, "rows_padded": Mt},
+                  "tokens": 8192, "experts": G, "rows_real": real, "rows_padded": Mt,
+                  "wgrad_token_grid_rows": T128},
                  kernels=kern, flops_basis="unpadded rows",
                  summary={"gemm_us": round(gemm_us, 1), "gemm_TFLOP/s": round(total / (gemm_us * 1e-6) / 1e12, 1),
                           "other_us": round(sum(avg.values()) - gemm_us, 1)})

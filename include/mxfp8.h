@@ -103,6 +103,43 @@ mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols,
                                  uint8_t *s_col, hipStream_t stream);
 
 /*
+ * mxfp8_quantize_dual_grouped -- mxfp8_quantize_dual for token-sorted MoE
+ * tensors, with the token-blocked grid regrouped for the experts' weight
+ * gradients.
+ *
+ * The expert weight gradient reduces over each expert's own tokens ("The
+ * pipeline", learner paragraph: token-axis blocks, groups padded to 32).
+ * Giving every expert's token range in the token-blocked (axis-0) grid a
+ * start and a length that are multiples of 128 (one 128-deep k-step of the
+ * weight-gradient GEMM) lets that GEMM take its aligned path, so the extra
+ * padding lives only in this grid.
+ *
+ * x [rows][cols] BF16, rows sorted by group: group g owns source rows
+ * [src_offsets[g], src_offsets[g+1]).  Result:
+ *   (q_row, s_row), optional (both NULL or both given): exactly
+ *     mxfp8_quantize(x, axis=1);
+ *   (q_col, s_col) [cols][rows_out] / [cols][rows_out/32]: exactly
+ *     mxfp8_quantize(x', axis=0), where x' [rows_out][cols] holds group g's
+ *     source rows at rows [dst_offsets[g], dst_offsets[g] + len_g) and zero
+ *     rows everywhere else (so pad blocks have zero codes and scale code 0).
+ * src_offsets, dst_offsets: DEVICE int32 [G+1], read on the device (no host
+ * synchronization).  Well-formed tables: both non-decreasing, multiples of
+ * 32, dst_offsets[g+1] - dst_offsets[g] >= len_g, src within [0, rows], dst
+ * within [0, rows_out].  Others are clamped like mxfp8_grouped_gemm's
+ * (a group's block goes nowhere unless both of its starts are multiples of
+ * 32 and the block fits its destination range); they can leave bytes of
+ * q_col unspecified but never address outside the buffers.
+ * rows % 32 == 0, cols % 32 == 0, rows_out % 32 == 0, 1 <= G <= 65535.
+ * x, q_row, s_row and q_col 16-byte aligned, offsets 4-byte aligned.
+ * Bit-exact, deterministic for well-formed tables.
+ */
+mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64_t cols,
+                                         uint8_t *q_row, uint8_t *s_row, uint8_t *q_col,
+                                         uint8_t *s_col, const int32_t *src_offsets,
+                                         const int32_t *dst_offsets, int64_t G, int64_t rows_out,
+                                         hipStream_t stream);
+
+/*
  * mxfp8_quantize_packed -- weights BF16 -> MXFP8 straight into the GEMM's
  * packed layout, optionally also the canonical grid.
  *
@@ -287,6 +324,10 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s,
  *   C: [G][M][N], FP32 or BF16; an empty group's C[g] is all zeros.
  * T % 32 == 0, 32 <= T < 2^23, M, N >= 1, G <= 65535.  Same accumulation and
  * error bound as mxfp8_gemm.  Deterministic.
+ * Speed: with T % 128 == 0, a group whose range starts and ends on a multiple
+ * of 128 runs the aligned path (scale bytes copied as dwords with the tiles);
+ * other groups read scale bytes one per lane, several times slower.
+ * mxfp8_quantize_dual_grouped writes the operands in such a layout.
  */
 mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s,
                                       const uint8_t *b_q, const uint8_t *b_s,

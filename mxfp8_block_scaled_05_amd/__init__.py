@@ -65,9 +65,11 @@ def lib():
         for f in ("mxfp8_quantize_batched", "mxfp8_quantize_gather", "mxfp8_grouped_gemm_wgrad"):
             getattr(L, f).restype = I32
         L.mxfp8_quantize_dual.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.mxfp8_quantize_dual_grouped.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
-                  "mxfp8_grouped_gemm", "mxfp8_quantize_dual", "mxfp8_quantize_packed"):
+                  "mxfp8_grouped_gemm", "mxfp8_quantize_dual", "mxfp8_quantize_packed",
+                  "mxfp8_quantize_dual_grouped"):
             getattr(L, f).restype = I32
         L.mxfp8_status_string.argtypes = [I32]
         L.mxfp8_status_string.restype = ctypes.c_char_p
@@ -227,6 +229,57 @@ def quantize_dual(x: torch.Tensor):
            torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device))
     quantize_dual_into(x, *out)
     return out
+
+
+def quantize_dual_grouped_into(x: torch.Tensor, src_offsets: torch.Tensor, dst_offsets: torch.Tensor,
+                               q_col: torch.Tensor, s_col: torch.Tensor, q_row: torch.Tensor | None = None,
+                               s_row: torch.Tensor | None = None) -> None:
+    """(q_row, s_row) = quantize(x, 1) if given; (q_col, s_col) = quantize(x', 0)
+    where x' [rows_out, cols] holds group g's rows of x (src_offsets) at
+    dst_offsets[g] and zero rows elsewhere.  Offsets: int32 device tensors
+    [G+1]; rows_out = q_col.shape[1]."""
+    _need(x, torch.bfloat16, "x")
+    for t, n in ((q_col, "q_col"), (s_col, "s_col")):
+        _need(t, torch.uint8, n)
+    if (q_row is None) != (s_row is None):
+        raise ValueError("give both q_row and s_row or neither")
+    for t, n in ((src_offsets, "src_offsets"), (dst_offsets, "dst_offsets")):
+        _need(t, torch.int32, n)
+    if x.dim() != 2 or q_col.dim() != 2:
+        raise ValueError("x and q_col must be 2-D")
+    rows, cols = x.shape
+    rows_out = q_col.shape[1]
+    G = src_offsets.numel() - 1
+    if G < 1 or dst_offsets.numel() != G + 1:
+        raise ValueError("src_offsets and dst_offsets must both hold G+1 >= 2 entries")
+    if rows % 32 or cols % 32 or rows_out % 32:
+        raise ValueError("rows, cols and rows_out must be multiples of 32")
+    want = [((cols, rows_out), q_col), ((cols, rows_out // 32), s_col)]
+    if q_row is not None:
+        _need(q_row, torch.uint8, "q_row")
+        _need(s_row, torch.uint8, "s_row")
+        want += [((rows, cols), q_row), ((rows, cols // 32), s_row)]
+    for shape, t in want:
+        if tuple(t.shape) != shape:
+            raise ValueError("output shape %s, expected %s" % (tuple(t.shape), shape))
+    _check(lib().mxfp8_quantize_dual_grouped(
+        _ptr(x), rows, cols, _ptr(q_row) if q_row is not None else None,
+        _ptr(s_row) if s_row is not None else None, _ptr(q_col), _ptr(s_col), _ptr(src_offsets),
+        _ptr(dst_offsets), G, rows_out, _stream(x.device)), "mxfp8_quantize_dual_grouped")
+
+
+def quantize_dual_grouped(x: torch.Tensor, src_offsets: torch.Tensor, dst_offsets: torch.Tensor, rows_out: int,
+                          row_grid: bool = True):
+    """-> (q_row, s_row, q_col, s_col) (the first two None unless row_grid)."""
+    rows, cols = x.shape
+    q_col = torch.empty((cols, rows_out), dtype=torch.uint8, device=x.device)
+    s_col = torch.empty((cols, rows_out // 32), dtype=torch.uint8, device=x.device)
+    q_row = s_row = None
+    if row_grid:
+        q_row = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        s_row = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    quantize_dual_grouped_into(x, src_offsets, dst_offsets, q_col, s_col, q_row, s_row)
+    return q_row, s_row, q_col, s_col
 
 
 def dequantize(q: torch.Tensor, s: torch.Tensor, rows: int, cols: int, axis: int = 1,

@@ -194,6 +194,26 @@ mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols,
                                        s_row, q_col, s_col, stream));
 }
 
+mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64_t cols, uint8_t *q_row,
+                                         uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                                         const int32_t *src_offsets, const int32_t *dst_offsets, int64_t G,
+                                         int64_t rows_out, hipStream_t stream) {
+    if (!x_bf16 || !q_col || !s_col || !src_offsets || !dst_offsets) return MXFP8_ERR_NULL;
+    if ((q_row == nullptr) != (s_row == nullptr)) return MXFP8_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (rows % 32 || cols % 32 || !tile128_ok(rows, cols)) return MXFP8_ERR_SHAPE;
+    if (G < 1 || G > 65535 || rows_out <= 0 || rows_out % 32 || rows_out >= kMaxDim ||
+        rows_out / 32 > 0x7FFFFFFF)
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q_col) || (q_row && (!aligned16(q_row) || !aligned16(s_row))) ||
+        ((uintptr_t)src_offsets & 3u) || ((uintptr_t)dst_offsets & 3u))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_dual_grouped(static_cast<const uint16_t *>(x_bf16), rows, cols, q_row, s_row,
+                                               q_col, s_col, src_offsets, dst_offsets, G, rows_out, stream));
+}
+
 mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols,
                                    uint8_t *q, uint8_t *scales, uint8_t *q_packed,
                                    uint8_t *scales_packed, hipStream_t stream) {

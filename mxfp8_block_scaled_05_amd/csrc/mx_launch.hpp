@@ -34,6 +34,13 @@ hipError_t launch_quantize_gather(const uint16_t *x, int64_t rows_in, int64_t co
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
                                 uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream);
 
+// axis 1 (q_row / s_row may be null) and axis 0 regrouped by token offsets
+// into q_col[cols][rows_out], s_col[cols][rows_out/32], pads zeroed
+hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
+                                        uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                                        const int32_t *src_off, const int32_t *dst_off, int64_t G,
+                                        int64_t rows_out, hipStream_t stream);
+
 // q / scales may be null (packed output only)
 hipError_t launch_quantize_packed(const uint16_t *w, int64_t batch, int64_t N, int64_t K,
                                   uint8_t *q, uint8_t *scales, uint8_t *q_packed,

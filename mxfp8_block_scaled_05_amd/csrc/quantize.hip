@@ -255,9 +255,13 @@ constexpr int kA0Tile = 128;
 constexpr int kA0OutPitch = 144;  // bytes per staged output column (16-byte aligned)
 
 // Steps 2 and 3 for one tile already in LDS (`tile`, reused for the output).
+// dstb (optional, in LDS): destination 32-row block in an output of rows_out
+// rows for each of the tile's four source blocks (-1: not written); without
+// it block b goes to block R0/32 + b of an output of `rows` rows.
 __device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, uint8_t *__restrict__ q,
                                                 uint8_t *__restrict__ scales, int64_t rows, int64_t cols,
-                                                int64_t R0, int64_t C0, int t) {
+                                                int64_t R0, int64_t C0, int t, const int *dstb = nullptr,
+                                                int64_t rows_out = 0) {
     const int lane = t & 63, w = t >> 6;
     uint32_t d[32];
 #pragma unroll
@@ -299,6 +303,25 @@ __device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, u
     stile[(2 * lane + 1) * 4 + w] = (uint8_t)code_hi;
     __syncthreads();
 
+    if (dstb != nullptr) {
+        // regrouped output: each 16-byte chunk lies in one 32-row block
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int col = i * 32 + (t >> 3), j = t & 7;
+            const int64_t c = C0 + col;
+            const int d = dstb[j >> 1];
+            if (c < cols && d >= 0)
+                *reinterpret_cast<v4i *>(q + c * rows_out + (int64_t)d * 32 + 16 * (j & 1)) =
+                    *reinterpret_cast<const v4i *>(ob + col * kA0OutPitch + 16 * j);
+        }
+        if (t < kA0Tile && C0 + t < cols) {
+            uint8_t *srow = scales + (C0 + t) * (rows_out / 32);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (dstb[b] >= 0) srow[dstb[b]] = stile[t * 4 + b];
+        }
+        return;
+    }
     // eight lanes store one output column's 128-byte line; rows % 32 == 0, so a
     // 16-byte chunk of the line is either wholly inside the matrix or outside
 #pragma unroll
@@ -385,6 +408,144 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t *__re
         }
     }
     axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
+}
+
+// ---------------------------------------------------------------- regrouped axis 0
+// Row (token) regrouping of the axis-0 output: group g's source rows
+// [s_g, s_g+1) go to output rows [d_g, d_g + (s_g+1 - s_g)) of an output with
+// rows_out rows; the rest of [d_g, d_g+1) is zero (pad).  Offsets are read on
+// the device and clamped like the grouped GEMM's ([0, rows] and [0, rows_out],
+// each range at least empty), so a malformed table can only drop rows; a
+// source block goes nowhere unless its group's source and destination starts
+// are multiples of 32 and the block fits inside the group's destination range.
+
+// Wave-wide search: the first group g whose clamped source range holds row
+// `row`; returns g (or -1) and that group's clamped source start.
+__device__ int find_src_group(const int32_t *src_off, int G, int64_t rows, int64_t row, int lane, int64_t &lo) {
+    for (int g0 = 0; g0 < G; g0 += 64) {
+        const int g = g0 + lane;
+        int64_t l = 0, h = 0;
+        if (g < G) {
+            l = src_off[g];
+            h = src_off[g + 1];
+            l = l < 0 ? 0 : (l > rows ? rows : l);
+            h = h < l ? l : (h > rows ? rows : h);
+        }
+        const unsigned long long hit = __ballot(g < G && row >= l && row < h);
+        if (hit) {
+            const int src = __ffsll((long long)hit) - 1;
+            lo = __shfl(l, src);
+            return g0 + src;
+        }
+    }
+    return -1;
+}
+
+// destination block of the source block starting at row `row`, or -1
+__device__ int dst_block_of(const int32_t *src_off, const int32_t *dst_off, int G, int64_t rows,
+                            int64_t rows_out, int64_t row, int lane) {
+    if (row >= rows) return -1;
+    int64_t lo;
+    const int g = find_src_group(src_off, G, rows, row, lane, lo);
+    if (g < 0) return -1;
+    int64_t dlo = dst_off[g], dhi = dst_off[g + 1];
+    dlo = dlo < 0 ? 0 : (dlo > rows_out ? rows_out : dlo);
+    dhi = dhi < dlo ? dlo : (dhi > rows_out ? rows_out : dhi);
+    if ((lo & 31) || (dlo & 31)) return -1;
+    const int64_t d = dlo + (row - lo);
+    return d + 32 <= dhi ? (int)(d / 32) : -1;
+}
+
+// both axes of x[rows][cols]: axis 1 (optional) as quantize_dual_kernel, axis
+// 0 regrouped into q_col[cols][rows_out], s_col[cols][rows_out/32]
+__global__ __launch_bounds__(256) void quantize_dual_grouped_kernel(
+    const uint16_t *__restrict__ x, uint8_t *__restrict__ q_row, uint8_t *__restrict__ s_row,
+    uint8_t *__restrict__ q_col, uint8_t *__restrict__ s_col, int64_t rows, int64_t cols,
+    const int32_t *__restrict__ src_off, const int32_t *__restrict__ dst_off, int G, int64_t rows_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    __shared__ int dstb[4];
+    const int t = threadIdx.x;
+    int64_t b_unused, R0, C0;
+    tile_origin(rows, cols, b_unused, R0, C0);
+    {
+        // wave w finds the destination of the tile's source block w
+        const int w = t >> 6;
+        const int d = dst_block_of(src_off, dst_off, G, rows, rows_out, R0 + 32 * w, t & 63);
+        if ((t & 63) == 0) dstb[w] = d;
+    }
+    load_tile<kA0Tile>(x, rows, cols, R0, C0, tile, t);
+    __syncthreads();
+    if (q_row != nullptr) {
+        const int64_t nb = cols / 32;
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+            const int u = u2 * 256 + t, r = u >> 2, b = u & 3;
+            uint32_t q8[8];
+            const uint32_t code = quantize_row_block(tile, r, b, q8);
+            const int64_t row = R0 + r, c = C0 + 32 * b;
+            if (row < rows && c < cols) {
+                v4i *dst = reinterpret_cast<v4i *>(q_row + row * cols + c);
+                dst[0] = v4i{(int)q8[0], (int)q8[1], (int)q8[2], (int)q8[3]};
+                dst[1] = v4i{(int)q8[4], (int)q8[5], (int)q8[6], (int)q8[7]};
+                s_row[row * nb + c / 32] = (uint8_t)code;
+            }
+        }
+    }
+    axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t, dstb, rows_out);
+}
+
+// Zero codes and zero scale codes (the quantization of zero rows) for every
+// 32-row block of q_col / s_col that no source block fills: one workgroup per
+// destination block; wave 0 decides, all threads write.
+__global__ __launch_bounds__(256) void zero_dst_pads_kernel(uint8_t *__restrict__ q_col, uint8_t *__restrict__ s_col,
+                                                            int64_t rows, int64_t cols,
+                                                            const int32_t *__restrict__ src_off,
+                                                            const int32_t *__restrict__ dst_off, int G,
+                                                            int64_t rows_out) {
+    __shared__ int pad;
+    const int t = threadIdx.x;
+    const int64_t d0 = (int64_t)blockIdx.x * 32;
+    if (t < 64) {
+        // first group whose clamped destination range holds d0
+        int found = -1;
+        int64_t dlo_f = 0, dhi_f = 0, len_f = 0;
+        for (int g0 = 0; g0 < G && found < 0; g0 += 64) {
+            const int g = g0 + t;
+            int64_t dlo = 0, dhi = 0, lo = 0, hi = 0;
+            if (g < G) {
+                dlo = dst_off[g];
+                dhi = dst_off[g + 1];
+                dlo = dlo < 0 ? 0 : (dlo > rows_out ? rows_out : dlo);
+                dhi = dhi < dlo ? dlo : (dhi > rows_out ? rows_out : dhi);
+                lo = src_off[g];
+                hi = src_off[g + 1];
+                lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
+                hi = hi < lo ? lo : (hi > rows ? rows : hi);
+            }
+            const unsigned long long hit = __ballot(g < G && d0 >= dlo && d0 < dhi);
+            if (hit) {
+                const int src = __ffsll((long long)hit) - 1;
+                found = g0 + src;
+                dlo_f = __shfl(dlo, src);
+                dhi_f = __shfl(dhi, src);
+                len_f = __shfl(hi - lo, src);
+                // filled iff the group's source blocks reach this block (and the
+                // group is aligned, as dst_block_of requires)
+                const int64_t lo_f = __shfl(lo, src);
+                if ((lo_f & 31) || (dlo_f & 31)) len_f = 0;
+            }
+        }
+        if (t == 0) pad = !(found >= 0 && d0 - dlo_f < len_f && d0 + 32 <= dhi_f);
+    }
+    __syncthreads();
+    if (!pad) return;
+    const int64_t nbo = rows_out / 32;
+    for (int64_t i = t; i < cols * 2; i += 256) {
+        const int64_t c = i >> 1;
+        *reinterpret_cast<v4i *>(q_col + c * rows_out + d0 + 16 * (i & 1)) = v4i{0, 0, 0, 0};
+        if ((i & 1) == 0) s_col[c * nbo + blockIdx.x] = 0;
+    }
 }
 
 // ---------------------------------------------------------------- weights -> packed
@@ -520,6 +681,20 @@ hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, u
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
     hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,
                        s_row, q_col, s_col, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
+                                        uint8_t *s_row, uint8_t *q_col, uint8_t *s_col,
+                                        const int32_t *src_off, const int32_t *dst_off, int64_t G,
+                                        int64_t rows_out, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_dst_pads_kernel, dim3((unsigned)(rows_out / 32)), dim3(256), 0, stream, q_col,
+                       s_col, rows, cols, src_off, dst_off, (int)G, rows_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
+    hipLaunchKernelGGL(quantize_dual_grouped_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,
+                       s_row, q_col, s_col, rows, cols, src_off, dst_off, (int)G, rows_out);
     return hipGetLastError();
 }
 

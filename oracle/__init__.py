@@ -160,6 +160,30 @@ def quantize(x_bits: np.ndarray, axis: int):
     return q, s
 
 
+def regroup_rows(x_bits: np.ndarray, src_offsets, dst_offsets, rows_out: int) -> np.ndarray:
+    """x' [rows_out, cols]: group g's rows x[src[g]:src[g+1]] placed at rows
+    dst[g] .. dst[g] + len_g, zero rows everywhere else (well-formed tables:
+    non-decreasing, each destination range at least as long as its source)."""
+    x_bits = np.asarray(x_bits, np.uint16)
+    src = np.asarray(src_offsets, np.int64)
+    dst = np.asarray(dst_offsets, np.int64)
+    out = np.zeros((rows_out, x_bits.shape[1]), np.uint16)
+    for g in range(src.size - 1):
+        n = src[g + 1] - src[g]
+        assert n >= 0 and dst[g + 1] - dst[g] >= n and dst[g] + n <= rows_out
+        out[dst[g]:dst[g] + n] = x_bits[src[g]:src[g + 1]]
+    return out
+
+
+def quantize_grouped_axis0(x_bits: np.ndarray, src_offsets, dst_offsets, rows_out: int):
+    """The token-blocked grid of a token-sorted MoE tensor with every group
+    moved to its destination rows: quantize(regroup_rows(x, ...), axis=0)
+    (the pad rows are zero, so their blocks get zero codes and scale code 0).
+    Follows the learner paragraph of "The pipeline" (token-axis blocks for
+    the weight-gradient GEMM, per-expert groups)."""
+    return quantize(regroup_rows(x_bits, src_offsets, dst_offsets, rows_out), 0)
+
+
 def dequantize(q: np.ndarray, s: np.ndarray, rows: int, cols: int, axis: int,
                dtype: str = "f64") -> np.ndarray:
     """Inverse of ``quantize``: [rows, cols] in the original orientation.

@@ -87,3 +87,12 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_grouped_gemm_wgrad(p, p, p, p, p, 2, 48, 8, 8, p, 0, NULL) == 2      # T % 32
     assert libmx.mxfp8_grouped_gemm_wgrad(p, p, p, p, p, 2, 1 << 23, 8, 8, p, 0, NULL) == 2  # T limit
     assert libmx.mxfp8_grouped_gemm_wgrad(p, p, p, p, p, 2, 64, 8, 8, p, 7, NULL) == 4      # dtype
+    # regrouped dual quantize
+    assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, p, p, NULL, p, 2, 128, NULL) == 1  # offsets
+    assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, p, NULL, p, p, p, p, 2, 128, NULL) == 1     # q_row alone
+    assert libmx.mxfp8_quantize_dual_grouped(p, 48, 64, NULL, NULL, p, p, p, p, 2, 128, NULL) == 2  # rows % 32
+    assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, p, p, p, p, 2, 100, NULL) == 2  # rows_out % 32
+    assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, p, p, p, p, 0, 128, NULL) == 2  # G
+    assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, q, p, p, p, 2, 128, NULL) == 5  # alignment
+    r = ctypes.c_void_p(p.value + 2)
+    assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, p, p, r, p, 2, 128, NULL) == 5  # offsets align

@@ -133,3 +133,98 @@ def test_dgrad_through_transposed_expert_weights(mx, oracle_mod):
     inside = grp >= 0
     ok, worst = oracle_mod.gemm_bound_ok(to_host(c)[inside], c_ref[inside], c_abs[inside], "f32")
     assert ok, worst
+
+
+def _pad128(offsets):
+    sizes = np.diff(np.asarray(offsets, np.int64))
+    return np.concatenate([[0], np.cumsum(-(-sizes // 128) * 128)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("tokens,experts,topk,cols", [(64, 8, 2, 64), (512, 16, 4, 256), (8192, 128, 8, 768)])
+@pytest.mark.parametrize("row_grid", [True, False])
+def test_quantize_dual_grouped_matches_oracle(mx, oracle_mod, tokens, experts, topk, cols, row_grid):
+    """mxfp8_quantize_dual_grouped: the row grid equals quantize(x, 1) and the
+    regrouped token-blocked grid equals the oracle's quantize of the regrouped
+    matrix, pads included (the outputs are filled with 0xFF first, so pads must
+    be written), bit for bit."""
+    import torch
+    _say("dual grouped", tokens, experts, topk, cols, row_grid)
+    rng, offsets, row_token, _ = _routing(tokens + cols, tokens, experts, topk)
+    T = int(offsets[-1])
+    x = np.zeros((T, cols), np.uint16)
+    real = row_token >= 0
+    x[real] = wl.normal_bf16(rng, (int(real.sum()), cols), outlier_frac=0.01)
+    dst = _pad128(offsets)
+    rows_out = int(dst[-1]) + 64                       # trailing rows in no group
+    xd = to_dev(x)
+    q_col = torch.full((cols, rows_out), 0xFF, dtype=torch.uint8, device=xd.device)
+    s_col = torch.full((cols, rows_out // 32), 0xFF, dtype=torch.uint8, device=xd.device)
+    q_row = s_row = None
+    if row_grid:
+        q_row = torch.full((T, cols), 0xFF, dtype=torch.uint8, device=xd.device)
+        s_row = torch.full((T, cols // 32), 0xFF, dtype=torch.uint8, device=xd.device)
+    mx.quantize_dual_grouped_into(xd, to_dev(offsets), to_dev(dst), q_col, s_col, q_row, s_row)
+    torch.cuda.synchronize()
+    rq, rs = oracle_mod.quantize_grouped_axis0(x, offsets, dst, rows_out)
+    assert np.array_equal(to_host(q_col), rq) and np.array_equal(to_host(s_col), rs)
+    if row_grid:
+        rq1, rs1 = oracle_mod.quantize(x, 1)
+        assert np.array_equal(to_host(q_row), rq1) and np.array_equal(to_host(s_row), rs1)
+
+
+def test_quantize_dual_grouped_malformed_tables_stay_in_bounds(mx, oracle_mod):
+    """Misaligned, overlapping and out-of-range offsets are clamped on the
+    device: the call completes, the row grid is unaffected, and the blocks of
+    the well-formed groups land where the oracle puts them."""
+    import torch
+    _say("dual grouped malformed")
+    rng = np.random.default_rng(9)
+    x = wl.normal_bf16(rng, (256, 64))
+    # group 1 runs backwards (empty after clamping), group 2 starts off a block
+    # boundary, group 3's destination is misaligned, group 4 lies past the end;
+    # no destination range overlaps group 0's, whose result is therefore fixed
+    src = np.array([0, 64, 48, 160, 256, 10 ** 6], np.int32)
+    dst = np.array([0, 128, 100, 300, 2 ** 30, 7], np.int32)
+    rows_out = 512
+    q_row, s_row, q_col, s_col = mx.quantize_dual_grouped(to_dev(x), to_dev(src), to_dev(dst), rows_out)
+    torch.cuda.synchronize()
+    rq1, rs1 = oracle_mod.quantize(x, 1)
+    assert np.array_equal(to_host(q_row), rq1) and np.array_equal(to_host(s_row), rs1)
+    # group 0 (rows 0..63 -> 0..63) is well formed
+    rq0, rs0 = oracle_mod.quantize(x, 0)
+    assert np.array_equal(to_host(q_col)[:, 0:64], rq0[:, 0:64])
+    assert np.array_equal(to_host(s_col)[:, 0:2], rs0[:, 0:2])
+
+
+@pytest.mark.parametrize("tokens,experts,topk,M,N,out", [(512, 16, 4, 256, 320, "f32"),
+                                                        (2048, 128, 8, 2048, 768, "f32"),
+                                                        (512, 16, 4, 192, 256, "bf16")])
+def test_wgrad_aligned_groups_match_oracle(mx, oracle_mod, tokens, experts, topk, M, N, out):
+    """Weight gradients over the regrouped token-blocked grids (every group
+    starting and ending on a multiple of 128 tokens, T % 128 == 0): the GEMM's
+    aligned path against the oracle per group, and against the same gradients
+    computed over the 32-padded grids (same exact values: pads add zeros)."""
+    import torch
+    _say("wgrad aligned", tokens, experts, topk, M, N, out)
+    rng, offsets, row_token, _ = _routing(tokens + M, tokens, experts, topk)
+    T = int(offsets[-1])
+    real = row_token >= 0
+    dy = np.zeros((T, M), np.uint16)
+    dy[real] = wl.normal_bf16(rng, (int(real.sum()), M), std=2.0 ** -10)
+    h = np.zeros((T, N), np.uint16)
+    h[real] = wl.normal_bf16(rng, (int(real.sum()), N))
+    dst = _pad128(offsets)
+    T128 = int(dst[-1])
+    od, dd = to_dev(offsets), to_dev(dst)
+    _, _, aq, as_ = mx.quantize_dual_grouped(to_dev(dy), od, dd, T128, row_grid=False)
+    _, _, bq, bs = mx.quantize_dual_grouped(to_dev(h), od, dd, T128, row_grid=False)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    c = mx.grouped_gemm_wgrad(aq, as_, bq, bs, dd, dt)
+    torch.cuda.synchronize()
+    ch = to_host(c.float()) if out == "bf16" else to_host(c)
+    rows = None if M * N <= 256 * 320 else np.sort(rng.choice(M, 24, replace=False))
+    _check_wgrad(oracle_mod, ch, to_host(aq), to_host(as_), to_host(bq), to_host(bs), dst, out, rows=rows)
+    # the same gradients over the 32-padded grids, against one reference
+    a32, s32 = oracle_mod.quantize(dy, 0)
+    b32, t32 = oracle_mod.quantize(h, 0)
+    _check_wgrad(oracle_mod, ch, a32, s32, b32, t32, offsets, out, rows=rows)
