@@ -95,6 +95,30 @@ def host_description():
             "omp_num_threads": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))}
 
 
+def copy_reference_us(dev, nbytes: int, reps: int = 30) -> float:
+    """Median time of a plain device copy moving `nbytes` (half read, half
+    written), rotated over buffers so that it reads from HBM like the timed
+    kernels: the HBM rate reachable at that transfer size."""
+    import torch
+    half = nbytes // 2 // 4096 * 4096
+    R = max(3, int(700e6 // nbytes) + 1)
+    srcs = [torch.ones(half, dtype=torch.uint8, device=dev) for _ in range(R)]
+    dsts = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(R)]
+    for i in range(R):
+        dsts[i].copy_(srcs[i])
+    torch.cuda.synchronize()
+    ev = []
+    for it in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dsts[it % R].copy_(srcs[it % R])
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
 def bench_qkv(args, dev):
     import torch
     import mxfp8_block_scaled_05_amd as mx
@@ -160,6 +184,10 @@ def bench_qkv(args, dev):
     }
     for k in kern:
         kern[k]["median_us"] = round(med[k], 2)
+    # context for the HBM-bound kernels: a plain copy of the same bytes, cold
+    for k, nbytes in (("quantize_W", N * K * Q_BYTES_PER_ELT), ("quantize_X", M * K * Q_BYTES_PER_ELT),
+                      ("repack_W", N * K * REPACK_BYTES_PER_ELT)):
+        kern[k]["same_bytes_copy_us"] = round(copy_reference_us(dev, int(nbytes)), 2)
     out = {
         "metric": "MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),

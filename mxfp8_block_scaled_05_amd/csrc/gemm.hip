@@ -815,10 +815,18 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uin
     p.G = (int)G;
     p.offsets = offsets;
     p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
-    constexpr int BM = 128, BN = 256;
-    p.tiles_m = (int)(ceil_div(M_total, BM) + G);
-    p.tiles_n = (int)ceil_div(N, BN);
-    return launch_tile<BM, BN, 2, true>(p, true, c_bf16, p.tiles_m * p.tiles_n, stream);
+    // 256-row tiles move 1.0 operand byte per output per k-step against 1.5
+    // for 128-row ones, but pad each group to 256 rows: they win once groups
+    // average 256 rows (measured on the Qwen3-30B-A3B layer, 529 rows per
+    // expert: gate_up 374 -> 340 us, down 279 -> 234 us)
+    if (M_total >= 256 * G) {
+        p.tiles_m = (int)(ceil_div(M_total, 256) + G);
+        p.tiles_n = (int)ceil_div(N, 256);
+        return launch_tile<256, 256, 2, true>(p, true, c_bf16, p.tiles_m * p.tiles_n, stream);
+    }
+    p.tiles_m = (int)(ceil_div(M_total, 128) + G);
+    p.tiles_n = (int)ceil_div(N, 256);
+    return launch_tile<128, 256, 2, true>(p, true, c_bf16, p.tiles_m * p.tiles_n, stream);
 }
 
 }  // namespace mx

@@ -147,7 +147,7 @@ def test_grouped_descriptors_inside_buffers(G, N, K, offsets):
         offsets, _, _ = wl.group_layout(route, G)
     offsets = np.asarray(offsets, np.int64)
     M_total = max(32, int(min(max(offsets.max(), 0), 10 ** 5)) // 32 * 32)
-    BM, BN = 128, 256
+    BM, BN = (256 if M_total >= 256 * G else 128), 256     # the launcher's choice
     upper = ceil_div(M_total, BM) + G
     tiles = grouped_tiles(offsets, M_total, BM)
     assert len(tiles) <= upper        # the launch grid covers every real tile
@@ -168,7 +168,8 @@ def stages_for(BM, BN, kalign, grouped):
     return 3 if (grouped and kalign and fits3) else 2
 
 
-@pytest.mark.parametrize("BM,BN,WM,grouped", [(256, 256, 2, False), (256, 128, 4, False), (128, 256, 2, True)])
+@pytest.mark.parametrize("BM,BN,WM,grouped", [(256, 256, 2, False), (256, 128, 4, False), (128, 256, 2, True),
+                                               (256, 256, 2, True)])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("kalign", [False, True])
 def test_lds_footprint(BM, BN, WM, grouped, packed, kalign):
