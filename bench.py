@@ -757,13 +757,16 @@ def bench_sweep(args, dev):
     for kind in ("gpu", "graph", "host"):
         fm, cm = fit("mxfp8_%s_us" % kind)
         fb, cb = fit("bf16_%s_us" % kind)
-        cross = None
-        if cb != cm:
-            x = (fm - fb) / (cb - cm)
-            cross = round(x, 0) if Ms[0] <= x <= Ms[-1] else None
+        x = (fm - fb) / (cb - cm) if cb != cm else None
+        # measured: the sweep points between which the faster arm changes
+        faster = [r["mxfp8_%s_us" % kind] < r["bf16_%s_us" % kind] for r in rows]
+        measured = [[rows[i]["M"], rows[i + 1]["M"]] for i in range(len(rows) - 1) if faster[i] != faster[i + 1]]
         fits[kind] = {"mxfp8_F_us": round(fm, 2), "mxfp8_c_ns_per_token": round(cm * 1e3, 3),
                       "bf16_F_us": round(fb, 2), "bf16_c_ns_per_token": round(cb * 1e3, 3),
-                      "break_even_M": cross}
+                      "break_even_M": round(x, 0) if x is not None and Ms[0] <= x <= Ms[-1] else None,
+                      "fit_crossing_M": round(x, 0) if x is not None else None,
+                      "measured_crossings": measured,
+                      "mxfp8_faster_at": [r["M"] for r, f in zip(rows, faster) if f]}
     flops_tok = sum(2.0 * N * K for _, N, K in shapes)
     big = rows[-1]
     speedup = big["bf16_gpu_us"] / big["mxfp8_gpu_us"]
