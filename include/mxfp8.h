@@ -270,12 +270,42 @@ mxfp8_status mxfp8_repack(const uint8_t *q, const uint8_t *scales,
  *   B (b_q, b_s): b_layout MXFP8_PACKED -> mxfp8_repack output for [N][K];
  *                 MXFP8_CANONICAL -> q[N][K], s[N][K/32] like A.
  *   C           : [M][N], FP32 or BF16 (round to nearest even).
- * M, N >= 1; K >= 32, K % 32 == 0.  Deterministic (no split-K atomics).
+ * M, N >= 1; K >= 32, K % 32 == 0; a_q, a_s, b_q, b_s and c 16-byte aligned.
+ * Deterministic (no split-K atomics).
  */
 mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s,
                         const uint8_t *b_q, const uint8_t *b_s,
                         mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
                         void *c, mxfp8_dtype c_dtype, hipStream_t stream);
+
+/*
+ * mxfp8_gemm_splitk -- mxfp8_gemm for shapes with few output tiles (small M:
+ * the page's break-even analysis measures the MXFP8 layers over the tokens
+ * per micro-batch, section "Speed: when it pays off").
+ *
+ * Same operands, result and error bound as mxfp8_gemm; when the shape has
+ * too few 256x128 output tiles to fill the device, K is split into slices
+ * (multiples of 128, at least 4 k-steps each) whose fp32 partial tiles go to
+ * `workspace` and are then summed in slice order into C (deterministic; the
+ * summation order differs from mxfp8_gemm's, so results match it within the
+ * bound, not bit for bit).
+ *   workspace: DEVICE memory owned by the caller, 16-byte aligned, or NULL;
+ *     its contents on entry are ignored and on return unspecified.  With
+ *     workspace_bytes >= mxfp8_gemm_splitk_workspace_bytes(M, N, K) the full
+ *     split is used; with less, as many slices as fit (fewer than two: the
+ *     plain mxfp8_gemm path, no workspace touched).
+ * Argument errors as mxfp8_gemm.  Two kernels on `stream`, no allocation, no
+ * synchronization.
+ */
+mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s,
+                               const uint8_t *b_q, const uint8_t *b_s,
+                               mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
+                               void *c, mxfp8_dtype c_dtype, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes mxfp8_gemm_splitk uses for this shape on the current
+ * device (0: it would not split; also 0 for invalid shapes or no device). */
+size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * mxfp8_grouped_gemm -- MoE expert GEMM over groups of rows:

@@ -66,6 +66,10 @@ def lib():
             getattr(L, f).restype = I32
         L.mxfp8_quantize_dual.argtypes = [P, I64, I64, P, P, P, P, P]
         L.mxfp8_quantize_dual_grouped.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
+        L.mxfp8_gemm_splitk.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P, ctypes.c_size_t, P]
+        L.mxfp8_gemm_splitk.restype = I32
+        L.mxfp8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
+        L.mxfp8_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
                   "mxfp8_grouped_gemm", "mxfp8_quantize_dual", "mxfp8_quantize_packed",
@@ -396,10 +400,19 @@ def quantize_packed(w_bf16: torch.Tensor, canonical: bool = True):
 
 # ------------------------------------------------------------------ GEMMs
 
+def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes gemm_splitk uses for this shape on the current device (0: no split)."""
+    return int(lib().mxfp8_gemm_splitk_workspace_bytes(M, N, K))
+
+
 def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b, out_dtype=torch.bfloat16,
-         out: torch.Tensor | None = None) -> torch.Tensor:
+         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         split_k: bool = False) -> torch.Tensor:
     """C[M, N] = A[M, K] B[N, K]^T.  ``b`` is a PackedWeight (batch 1) or a
-    canonical (b_q[N, K], b_s[N, K/32]) pair."""
+    canonical (b_q[N, K], b_s[N, K/32]) pair.  With split_k (or a workspace
+    given) the call is mxfp8_gemm_splitk: K split over workgroups when the
+    shape has few output tiles, partials in ``workspace`` (a uint8 device
+    tensor; allocated here, through torch, when not given)."""
     _need(a_q, torch.uint8, "a_q")
     _need(a_s, torch.uint8, "a_s")
     M, K = a_q.shape
@@ -424,6 +437,17 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b, out_dtype=torch.bfloat16,
         _need(out, out_dtype, "out")
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be [M, N]")
+    if split_k or workspace is not None:
+        need = gemm_splitk_workspace_bytes(M, N, K)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=a_q.device)
+        if workspace is not None:
+            _need(workspace, torch.uint8, "workspace")
+        _check(lib().mxfp8_gemm_splitk(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), layout, M, N, K, _ptr(out),
+                                       code, _ptr(workspace) if workspace is not None else None,
+                                       workspace.numel() if workspace is not None else 0, _stream(a_q.device)),
+               "mxfp8_gemm_splitk")
+        return out
     _check(lib().mxfp8_gemm(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), layout, M, N, K,
                             _ptr(out), code, _stream(a_q.device)), "mxfp8_gemm")
     return out

@@ -313,11 +313,56 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b
         return MXFP8_ERR_SHAPE;
     // tile counts must fit the 1-D grid
     if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
-    if (!aligned16(a_q) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c)) return MXFP8_ERR_ALIGN;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c))
+        return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
     return finish(launch_gemm(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
                               c_dtype == MXFP8_BF16, stream));
+}
+
+size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim) return 0;
+    if (check_device() != MXFP8_OK) return 0;
+    const SplitPlan sp = splitk_plan(M, N, K, device_cu_count());
+    return sp.splits > 1 ? (size_t)sp.workspace_bytes : 0;
+}
+
+mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                               const uint8_t *b_s, mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
+                               void *c, mxfp8_dtype c_dtype, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
+    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c) ||
+        (workspace && !aligned16(workspace)))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    SplitPlan sp = splitk_plan(M, N, K, device_cu_count());
+    if (sp.splits > 1 && (!workspace || workspace_bytes < (size_t)sp.workspace_bytes)) {
+        // fewer slices, as many as the workspace holds
+        const int64_t slice = (M * N + 3) / 4 * 4 * 4;
+        const int64_t fit = workspace ? (int64_t)(workspace_bytes / (size_t)slice) : 0;
+        if (fit >= 2) {
+            const int64_t ks = ceil_div(K, 128);
+            const int64_t steps = ceil_div(ks, fit);
+            sp.split_steps = (int)steps;
+            sp.splits = (int)ceil_div(ks, steps);
+            sp.workspace_bytes = sp.splits * slice;
+        } else {
+            sp.splits = 1;
+        }
+    }
+    if (sp.splits <= 1)
+        return finish(launch_gemm(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
+                                  c_dtype == MXFP8_BF16, stream));
+    return finish(launch_gemm_splitk(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
+                                     c_dtype == MXFP8_BF16, sp, static_cast<float *>(workspace), stream));
 }
 
 mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q_packed,

@@ -34,6 +34,8 @@
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
+#include <algorithm>
+
 namespace mx {
 
 struct GemmParams {
@@ -52,6 +54,7 @@ struct GemmParams {
     int64_t lda, lsa, ldb, lsb;
     int64_t c_stride;        // grouped-K: elements of one group's C
     int mix_big, mix_big_cols;   // mixed dense launch: 256x256 tiles and their tile columns
+    int splits, split_steps;     // split-K: K slices and k-steps per slice
 };
 
 constexpr int kGroupM = 4;
@@ -241,11 +244,13 @@ struct TileOps {
         rsa = make_srd(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
         rsa_c = make_rsrc(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
         if constexpr (BPACK) {
-            const int64_t panel = n0 / kPanelRows, prow = n0 % kPanelRows;
-            const uint8_t *bt = p.b_q + ((g * p.NP + panel) * p.KS) * kTileBytes + prow * 128;
-            rb = make_srd(bt, (uint32_t)((int64_t)p.KS * kTileBytes - prow * 128));
-            const uint8_t *bs = p.b_s + ((g * p.NP + panel) * p.KS) * kScaleStepBytes + (prow / 16) * 64;
-            rsb = make_srd(bs, (uint32_t)((int64_t)p.KS * kScaleStepBytes - (prow / 16) * 64));
+            // packed B from k-step s0 = kbase / 128 of the panel on (kbase is a
+            // multiple of 128 whenever B is packed)
+            const int64_t panel = n0 / kPanelRows, prow = n0 % kPanelRows, s0 = kbase / 128;
+            const uint8_t *bt = p.b_q + ((g * p.NP + panel) * p.KS + s0) * kTileBytes + prow * 128;
+            rb = make_srd(bt, (uint32_t)((int64_t)(p.KS - s0) * kTileBytes - prow * 128));
+            const uint8_t *bs = p.b_s + ((g * p.NP + panel) * p.KS + s0) * kScaleStepBytes + (prow / 16) * 64;
+            rsb = make_srd(bs, (uint32_t)((int64_t)(p.KS - s0) * kScaleStepBytes - (prow / 16) * 64));
             rsb_c = make_rsrc(p.b_s, 0u);
         } else {
             const int64_t rows_b = min((int64_t)BN, N - n0);
@@ -654,6 +659,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_gk_aligned_kernel(GemmParams
         gemm_tile<256, 256, 2, false, OUT_BF16, false, 2>(p, m0, m_end, n0, g, kbase, kbound, KS, smem);
 }
 
+// Split-K (few output tiles): workgroup -> (slice s, tile); slice s covers
+// k-steps [s * split_steps, (s+1) * split_steps) and writes its fp32 partial
+// tile to p.c + s * c_stride (c_stride = M * N rounded up to 4 floats).  A slice ending before K % 128 (only the last,
+// when K % 128 != 0) takes the byte-scale path, the others the aligned one.
+template <bool BPACK>
+__global__ __launch_bounds__(kThreads, 1) void gemm_splitk_kernel(GemmParams p) {
+    constexpr int SA = TileOps<256, 128, 4, BPACK, true>::STAGE, SU = TileOps<256, 128, 4, BPACK, false>::STAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (SA > SU ? SA : SU)];
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int L = xcd_logical(blockIdx.x, gridDim.x);
+    const int sl = L / tiles;
+    if (sl >= p.splits) return;
+    int tm, tn;
+    grouped_order(L % tiles, p.tiles_m, p.tiles_n, tm, tn);
+    const int64_t kbase = (int64_t)sl * p.split_steps * 128;
+    if (kbase >= p.K) return;
+    const int64_t kbound = min((int64_t)p.split_steps * 128, p.K - kbase);
+    const int KS = (int)((kbound + 127) / 128);
+    p.c = static_cast<float *>(p.c) + (int64_t)sl * p.c_stride;
+    const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 128;
+    if ((kbound & 127) == 0)
+        gemm_tile<256, 128, 4, BPACK, false, true, 2>(p, m0, p.M, n0, 0, kbase, kbound, KS, smem);
+    else
+        gemm_tile<256, 128, 4, BPACK, false, false, 2>(p, m0, p.M, n0, 0, kbase, kbound, KS, smem);
+}
+
+// C[i] = sum over s of the fp32 partials ws[s * stride + i] in slice order
+// (deterministic), i < n; four elements per thread, grid-stride, and the
+// last n % 4 one by one.  stride % 4 == 0, ws 16-byte aligned; c 16-byte
+// aligned.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ ws, int splits, int64_t n,
+                                                            int64_t stride, void *__restrict__ c) {
+    const int64_t n4 = n / 4;
+    if (blockIdx.x == 0 && (int64_t)threadIdx.x < n - n4 * 4) {
+        const int64_t i = n4 * 4 + threadIdx.x;
+        float a = ws[i];
+        for (int sl = 1; sl < splits; ++sl) a += ws[(int64_t)sl * stride + i];
+        if constexpr (OUT_BF16) static_cast<uint16_t *>(c)[i] = (uint16_t)f32_to_bf16_rne(a);
+        else static_cast<float *>(c)[i] = a;
+    }
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        v4f a = reinterpret_cast<const v4f *>(ws)[i];
+        for (int sl = 1; sl < splits; ++sl) {
+            const v4f b = reinterpret_cast<const v4f *>(ws + (int64_t)sl * stride)[i];
+            a = v4f{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+        }
+        if constexpr (OUT_BF16) {
+            const uint32_t lo = f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16);
+            reinterpret_cast<uint2 *>(c)[i] = uint2{lo, hi};
+        } else {
+            reinterpret_cast<v4f *>(c)[i] = a;
+        }
+    }
+}
+
 // Dense C in two tile shapes in one launch: workgroups [0, mix_big) take the
 // 256x256 tiles of columns [0, 256 * mix_big_cols), the rest the 256x128
 // tiles of the remaining columns.  The large tiles come first in dispatch
@@ -775,6 +837,53 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     }
     p.tiles_n = d.small_cols;
     return launch_tile<256, 128, 4, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
+}
+
+// Split-K plan for a dense GEMM on `cus` CUs: 256x128 tiles, as many K
+// slices (each at least 4 k-steps) as keep tiles x slices within one round;
+// splits == 1 means no split.
+SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, int cus) {
+    SplitPlan sp{1, (int)packed_ksteps(K), 0};
+    const int64_t tiles = ceil_div(M, 256) * ceil_div(N, 128);
+    const int64_t ks = packed_ksteps(K);
+    if (tiles <= 0 || tiles * 2 > cus || ks < 8) return sp;
+    int64_t s = cus / tiles;
+    if (s > ks / 4) s = ks / 4;
+    if (s < 2) return sp;
+    const int64_t steps = ceil_div(ks, s);
+    sp.splits = (int)ceil_div(ks, steps);      // every slice non-empty
+    sp.split_steps = (int)steps;
+    sp.workspace_bytes = (int64_t)sp.splits * ((M * N + 3) / 4 * 4) * 4;
+    return sp;
+}
+
+hipError_t launch_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
+                              bool b_packed, int64_t M, int64_t N, int64_t K, void *c, bool c_bf16,
+                              const SplitPlan &sp, float *workspace, hipStream_t stream) {
+    GemmParams p{};
+    p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = workspace;
+    p.M = M; p.N = N; p.K = K;
+    p.KS = (int)packed_ksteps(K);
+    p.NP = (int)packed_panels(N);
+    p.G = 1;
+    p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
+    p.tiles_m = (int)ceil_div(M, 256);
+    p.tiles_n = (int)ceil_div(N, 128);
+    p.splits = sp.splits;
+    p.split_steps = sp.split_steps;
+    p.c_stride = (M * N + 3) / 4 * 4;
+    dim3 grid((unsigned)(p.tiles_m * p.tiles_n * sp.splits)), block(kThreads);
+    if (b_packed) hipLaunchKernelGGL(gemm_splitk_kernel<true>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(gemm_splitk_kernel<false>, grid, block, 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = M * N;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(n / 4, 256), 4096));
+    if (c_bf16) hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                                   workspace, sp.splits, n, p.c_stride, c);
+    else hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                            workspace, sp.splits, n, p.c_stride, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,

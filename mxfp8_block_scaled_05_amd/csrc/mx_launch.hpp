@@ -18,6 +18,18 @@ struct DenseTiling {
 };
 DenseTiling dense_tiling(int64_t M, int64_t N, int cus);
 
+// Split-K plan of a dense GEMM: K slices of split_steps k-steps, fp32
+// partials of splits * M * N floats (splits == 1: no split).
+struct SplitPlan {
+    int splits, split_steps;
+    int64_t workspace_bytes;
+};
+SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, int cus);
+// partial tiles into `workspace`, then C = their sum (slice order)
+hipError_t launch_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
+                              bool b_packed, int64_t M, int64_t N, int64_t K, void *c, bool c_bf16,
+                              const SplitPlan &plan, float *workspace, hipStream_t stream);
+
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint8_t *q,
                            uint8_t *scales, hipStream_t stream);
 

@@ -226,3 +226,55 @@ def test_grouped_k_descriptors_inside_buffers(M, N, T, offsets):
                     # last valid element of the last valid row, and the first invalid row
                     assert (rows_a - 1) * T + kb - 1 < (rows_a - 1) * T + kb
                     assert rows_a * T >= (rows_a - 1) * T + kb
+
+
+def splitk_plan(M, N, K, cus=256):
+    """Mirror of the split-K plan: (splits, k-steps per slice); 256x128 tiles."""
+    tiles = ceil_div(M, 256) * ceil_div(N, 128)
+    ks = ceil_div(K, KSTEP)
+    if tiles * 2 > cus or ks < 8:
+        return 1, ks
+    s = min(cus // tiles, ks // 4)
+    if s < 2:
+        return 1, ks
+    steps = ceil_div(ks, s)
+    return ceil_div(ks, steps), steps
+
+
+SPLITK_SHAPES = [(64, 256, 1024), (200, 300, 2080), (512, 6144, 4096), (1000, 96, 4128), (32, 4096, 12288),
+                 (512, 4096, 4096), (256, 24576, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLITK_SHAPES)
+@pytest.mark.parametrize("packed", [False, True])
+def test_splitk_slices_cover_k_and_stay_inside(M, N, K, packed):
+    """Every slice is non-empty, the slices tile [0, K) exactly, the grid fits
+    one round, and every descriptor of every (slice, tile) -- A from its
+    slice's first column, packed B from its slice's first k-step -- lies
+    inside its buffer."""
+    splits, steps = splitk_plan(M, N, K)
+    KB, KS, NP = K // 32, ceil_div(K, KSTEP), ceil_div(N, PANEL)
+    bounds = [(s * steps * KSTEP, min(steps * KSTEP, K - s * steps * KSTEP)) for s in range(splits)]
+    assert all(kb > 0 for _, kb in bounds) and bounds[0][0] == 0
+    assert sum(kb for _, kb in bounds) == K
+    assert all(k0 % KSTEP == 0 for k0, _ in bounds)
+    if splits > 1:
+        assert ceil_div(M, 256) * ceil_div(N, 128) * splits <= 256
+    for k0, kb in bounds:
+        s0 = k0 // KSTEP
+        for tm in range(ceil_div(M, 256)):
+            m0 = tm * 256
+            rows_a = min(256, M - m0)
+            assert m0 * K + k0 + (rows_a - 1) * K + kb <= M * K
+            assert m0 * KB + k0 // 32 + (rows_a - 1) * KB + kb // 32 <= M * KB
+            for tn in range(ceil_div(N, 128)):
+                n0 = tn * 128
+                if packed:
+                    panel, prow = n0 // PANEL, n0 % PANEL
+                    base = (panel * KS + s0) * TILE_BYTES + prow * 128
+                    assert base + (KS - s0) * TILE_BYTES - prow * 128 <= NP * KS * TILE_BYTES
+                    sbase = (panel * KS + s0) * 1024 + (prow // 16) * 64
+                    assert sbase + (KS - s0) * 1024 - (prow // 16) * 64 <= NP * KS * 1024
+                else:
+                    rows_b = min(128, N - n0)
+                    assert n0 * K + k0 + (rows_b - 1) * K + kb <= N * K

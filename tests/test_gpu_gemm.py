@@ -382,3 +382,45 @@ def test_gemm_mlp_step_full_size_sampled(mx, oracle_mod):
         ok, worst = oracle_mod.gemm_bound_ok(c[rows], ref, sabs, out)
         assert ok, (name, worst)
         del c
+
+
+@pytest.mark.parametrize("M,N,K,out", [(64, 256, 1024, "bf16"), (200, 300, 2080, "f32"), (1000, 96, 4128, "bf16"),
+                                       (32, 4096, 12288, "f32"), (512, 6144, 4096, "bf16")])
+def test_gemm_splitk_matches_oracle(mx, oracle_mod, M, N, K, out):
+    """mxfp8_gemm_splitk: K split over workgroups for shapes with few tiles,
+    partials summed in slice order.  Every element within the GEMM bound, for
+    packed and canonical B (identical bits: same arithmetic), the last slice
+    unaligned when K % 128 != 0; two calls give the same bits; a workspace too
+    small for the full split still gives a correct result, and no workspace
+    gives exactly mxfp8_gemm's result."""
+    import torch
+    _say("gemm splitk", M, N, K, out, mx.gemm_splitk_workspace_bytes(M, N, K))
+    assert mx.gemm_splitk_workspace_bytes(M, N, K) > 0
+    rng = np.random.default_rng(M + N + K)
+    X = wl.normal_bf16(rng, (M, K))
+    W = wl.normal_bf16(rng, (N, K), std=0.02)
+    xq, xs = _quant_pair(oracle_mod, X)
+    wq, ws = _quant_pair(oracle_mod, W)
+    rows = None if M * N <= 1 << 20 else np.sort(rng.choice(M, 48, replace=False))
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws, rows=rows)
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    a_q, a_s = to_dev(xq), to_dev(xs)
+    packed = mx.repack(to_dev(wq), to_dev(ws))
+    canon = (to_dev(wq), to_dev(ws))
+
+    def host(c):
+        torch.cuda.synchronize()
+        return to_host(c.float()) if out == "bf16" else to_host(c)
+
+    c1 = host(mx.gemm(a_q, a_s, packed, tdt, split_k=True))
+    sel = c1 if rows is None else c1[rows]
+    ok, worst = oracle_mod.gemm_bound_ok(sel, ref, sabs, out)
+    assert ok, worst
+    assert np.array_equal(c1, host(mx.gemm(a_q, a_s, canon, tdt, split_k=True)))
+    assert np.array_equal(c1, host(mx.gemm(a_q, a_s, packed, tdt, split_k=True)))
+    half = torch.empty(mx.gemm_splitk_workspace_bytes(M, N, K) // 2 + 16, dtype=torch.uint8, device=a_q.device)
+    c2 = host(mx.gemm(a_q, a_s, packed, tdt, workspace=half))
+    ok, worst = oracle_mod.gemm_bound_ok(c2 if rows is None else c2[rows], ref, sabs, out)
+    assert ok, worst
+    none = torch.empty(0, dtype=torch.uint8, device=a_q.device)
+    assert np.array_equal(host(mx.gemm(a_q, a_s, packed, tdt, workspace=none)), host(mx.gemm(a_q, a_s, packed, tdt)))
