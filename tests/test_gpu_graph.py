@@ -140,3 +140,77 @@ def test_graph_replay_grouped_new_offsets_each_replay(mx, oracle_mod):
         assert ok, (rep, worst)
         # rows outside [o_0, o_G) are not written (zero from the fill above)
         assert np.all(yg[~inside] == 0), rep
+
+
+def test_graph_replay_splitk_and_regrouped_wgrad(mx, oracle_mod):
+    """Split-K GEMM (workspace reused across replays) and the MoE weight-
+    gradient path (regrouped quantize with its pad pass, aligned grouped-K
+    GEMM) recorded once and replayed with new inputs and new group offsets;
+    every replay equals an eager run bit for bit, and the first is checked
+    against the oracle."""
+    import torch
+    _say("splitk + regrouped wgrad")
+    dev = torch.device("cuda:0")
+    M, N, K = 64, 512, 4096                           # few tiles: split-K applies
+    X = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    W = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    wsb = mx.gemm_splitk_workspace_bytes(M, N, K)
+    assert wsb > 0
+    G, T, C1, C2 = 4, 512, 256, 192
+    T128 = T + 128 * G
+    dy = torch.empty((T, C1), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((T, C2), dtype=torch.bfloat16, device=dev)
+    src = torch.zeros(G + 1, dtype=torch.int32, device=dev)
+    dst = torch.zeros(G + 1, dtype=torch.int32, device=dev)
+
+    def buffers():
+        u8 = dict(dtype=torch.uint8, device=dev)
+        return dict(xq=torch.empty((M, K), **u8), xs=torch.empty((M, K // 32), **u8),
+                    wq=torch.empty((N, K), **u8), ws=torch.empty((N, K // 32), **u8),
+                    wk=torch.empty(wsb, **u8), y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                    aq=torch.empty((C1, T128), **u8), as_=torch.empty((C1, T128 // 32), **u8),
+                    bq=torch.empty((C2, T128), **u8), bs=torch.empty((C2, T128 // 32), **u8),
+                    dw=torch.empty((G, C1, C2), dtype=torch.float32, device=dev))
+
+    def step(b):
+        mx.quantize_into(X, 1, b["xq"], b["xs"])
+        mx.quantize_into(W, 1, b["wq"], b["ws"])
+        mx.gemm(b["xq"], b["xs"], (b["wq"], b["ws"]), torch.bfloat16, out=b["y"], workspace=b["wk"])
+        mx.quantize_dual_grouped_into(dy, src, dst, b["aq"], b["as_"])
+        mx.quantize_dual_grouped_into(h, src, dst, b["bq"], b["bs"])
+        mx.grouped_gemm_wgrad(b["aq"], b["as_"], b["bq"], b["bs"], dst, torch.float32, out=b["dw"])
+
+    g_buf, e_buf = buffers(), buffers()
+    for t in (X, W, dy, h):
+        t.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_buf)
+    torch.cuda.synchronize()
+    layouts = [[0, 96, 96, 352, 512], [0, 256, 288, 288, 512], [0, 32, 64, 96, 512]]
+    for rep, lay in enumerate(layouts):
+        rng = np.random.default_rng(300 + rep)
+        x, w = wl.normal_bf16(rng, (M, K)), wl.normal_bf16(rng, (N, K), std=0.02)
+        dyh, hh = wl.normal_bf16(rng, (T, C1), std=2.0 ** -10), wl.normal_bf16(rng, (T, C2))
+        sizes = np.diff(lay)
+        dlay = np.concatenate([[0], np.cumsum(-(-sizes // 128) * 128)]).astype(np.int32)
+        for t, v in ((X, x), (W, w), (dy, dyh), (h, hh)):
+            t.copy_(to_dev(v))
+        src.copy_(torch.tensor(lay, dtype=torch.int32))
+        dst.copy_(torch.from_numpy(dlay))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_buf)
+        torch.cuda.synchronize()
+        for key in ("xq", "xs", "y", "aq", "as_", "bq", "bs", "dw"):
+            assert np.array_equal(to_host(g_buf[key]), to_host(e_buf[key])), (rep, key)
+        if rep == 0:
+            xq, xs = oracle_mod.quantize(x, 1)
+            wq, ws = oracle_mod.quantize(w, 1)
+            c_ref, c_abs = oracle_mod.gemm(xq, xs, wq, ws)
+            ok, worst = oracle_mod.gemm_bound_ok(wl.bf16_bits_to_f32(to_host(g_buf["y"])), c_ref, c_abs, "bf16")
+            assert ok, worst
+            rq, rs = oracle_mod.quantize_grouped_axis0(dyh, lay, dlay, T128)
+            assert np.array_equal(to_host(g_buf["aq"]), rq) and np.array_equal(to_host(g_buf["as_"]), rs)
