@@ -240,8 +240,9 @@ size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which);
  *   NP = ceil(N/256) panels of 256 rows, KS = ceil(K/128) k-steps of 128.
  *   elements [batch][NP][KS][256 rows][128 B]: the bytes k = 128*ks + 16c ..
  *     + 15 of row r of the panel form chunk c (0..7), stored at chunk slot
- *     c ^ f(r % 16), with f(t) = (t & 7) ^ (t >> 3) (a bank-conflict-free
- *     swizzle of the GEMM's LDS image).  Rows >= N and k >= K hold 0x00.
+ *     c ^ (r % 8) (the GEMM's LDS image, whose 16-byte fragment reads of 16
+ *     rows at one chunk are then bank-conflict free).  Rows >= N and k >= K
+ *     hold 0x00.
  *   scales [batch][NP][KS][16 atoms of 16 rows][64 lanes] bytes: byte
  *     (panel, kstep, atom, lane) is the scale of row 256*panel + 16*atom +
  *     (lane % 16), block 4*kstep + (lane / 16) (the byte the GEMM's MFMA lane

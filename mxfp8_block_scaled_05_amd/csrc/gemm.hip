@@ -17,8 +17,8 @@
 //    behind them.
 //  - A 2-stage ring with one barrier at the top of each step.
 //  - LDS rows are 128 B (one step); the 16-byte chunk c of row r sits at slot
-//    c ^ f(r % 16), which makes the ds_read_b128 of 16 rows at one chunk bank
-//    conflict free.  Canonical operands are swizzled by choosing each lane's
+//    c ^ (r % 8), which makes the ds_read_b128 of 16 rows at one chunk bank
+//    conflict free (swz).  Canonical operands are swizzled by choosing each lane's
 //    source address; packed weights (mxfp8_repack) are already stored in this
 //    image, so their copy is linear.
 //  - Out-of-range rows and the K tail read as zeros through the buffer

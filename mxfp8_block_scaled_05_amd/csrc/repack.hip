@@ -8,7 +8,7 @@
 // 2.0625 algorithmic bytes per element.  The layout is specified in
 // include/mxfp8.h (mxfp8_repack):
 //   elements: [batch][panel of 256 rows][k-step of 128][256 rows][128 B], the
-//             16-byte chunk c of row r stored at slot c ^ f(r % 16) -- exactly
+//             16-byte chunk c of row r stored at slot c ^ (r % 8) -- exactly
 //             the GEMM's LDS image of a B tile, so the GEMM copies it linearly.
 //   scales  : [batch][panel][k-step][16 atoms of 16 rows][64 lanes] bytes --
 //             one byte per MFMA lane per atom, 1 KB per panel and k-step, so

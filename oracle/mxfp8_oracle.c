@@ -328,7 +328,7 @@ int mxo_grouped_gemm_rows(const uint8_t *a_q, const uint8_t *a_s,
  *   panels of 256 rows (NP = ceil(N/256)), k-steps of 128 (KS = ceil(K/128)).
  *   elements: [b][panel][kstep][row 0..255][128 bytes]; inside a row the
  *     16-byte chunk c (k = kstep*128 + 16c .. +15) sits at chunk position
- *     c ^ f(row % 16), f(t) = (t & 7) ^ (t >> 3).  Rows >= N and k >= K are 0.
+ *     c ^ (row % 8).  Rows >= N and k >= K are 0.
  *   scales: [b][panel][kstep][atom 0..15 of 16 rows][lane 0..63] bytes; byte
  *     (panel, kstep, atom, lane) is the scale of row 256*panel + 16*atom +
  *     (lane % 16), block 4*kstep + (lane / 16).  Rows >= N or blocks >= K/32
@@ -345,8 +345,7 @@ int64_t mxo_packed_bytes(int64_t batch, int64_t N, int64_t K, int which) {
 static int64_t pk_elem_offset(int64_t N, int64_t K, int64_t b, int64_t n, int64_t k) {
     int64_t NP = ceil_div(N, 256), KS = ceil_div(K, 128);
     int64_t panel = n / 256, row = n % 256, ks = k / 128, kin = k % 128;
-    int64_t c = kin / 16, t = row % 16;
-    int64_t f = (t & 7) ^ (t >> 3);
+    int64_t c = kin / 16, f = row % 8;
     return (((b * NP + panel) * KS + ks) * 256 + row) * 128 + ((c ^ f) * 16) + kin % 16;
 }
 

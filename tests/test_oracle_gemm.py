@@ -119,16 +119,16 @@ def test_packed_layout_hand_offsets(oracle_mod):
     N, K = 300, 320
     q = np.zeros((1, N, K), np.uint8)
     s = np.full((1, N, K // 32), 127, np.uint8)
-    q[0, 17, 130] = 0xAB          # panel 0, kstep 1, row 17, chunk 0 -> slot 0^f(1)=1
+    q[0, 17, 130] = 0xAB          # panel 0, kstep 1, row 17, chunk 0 -> slot 0^(17%8)=1
     s[0, 17, 5] = 0x42            # panel 0, kstep 1, atom 1, lane 1+16*1=17
     s[0, 299, 9] = 0x43           # panel 1, kstep 2, atom 2 (row 43), lane 11+16*1=27
-    q[0, 299, 319] = 0xCD         # panel 1, row 43, kstep 2, chunk 3 -> slot 3^f(11)=3^(3^1)=1
+    q[0, 299, 319] = 0xCD         # panel 1, row 43, kstep 2, chunk 3 -> slot 3^(43%8)=3^3=0
     qp, sp = oracle_mod.pack(q, s, 1, N, K)
     assert qp.size == 2 * 3 * 256 * 128 and sp.size == 2 * 3 * 16 * 64
     assert qp[(1 * 256 + 17) * 128 + 16 + 2] == 0xAB
     assert sp[((0 * 3 + 1) * 16 + 1) * 64 + 17] == 0x42
     assert sp[((1 * 3 + 2) * 16 + 2) * 64 + 27] == 0x43
-    off = ((1 * 3 + 2) * 256 + 43) * 128 + 1 * 16 + 15
+    off = ((1 * 3 + 2) * 256 + 43) * 128 + 0 * 16 + 15
     assert qp[off] == 0xCD
     assert int((qp != 0).sum()) == 2
     # padding: rows >= N zero, k >= K zero; padded scale slots hold 127
