@@ -16,6 +16,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -54,6 +55,26 @@ def measured_gemm_traffic():
 def _bf16_dev(a, dev):
     import torch
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def settle(step, seconds):
+    """Run `step()` (untimed) until `seconds` of wall time have passed: the
+    GPU's clocks ramp for tens of milliseconds after it leaves idle (measured:
+    the qkv GEMM takes ~114 us on average over its first 50 launches and
+    ~102 us once settled), so the warm-up ends in steady state whatever W is.
+    Returns the seconds spent."""
+    import torch
+    if seconds <= 0:
+        return 0.0
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return time.perf_counter() - t0
 
 
 class KernelTimer:
@@ -159,6 +180,8 @@ def bench_qkv(args, dev):
             mx.repack_(wq, ws, w)
             mx.gemm(xq, xs, w, torch.bfloat16, out=y)
 
+    settled = settle(lambda: step(0, False), args.settle_s)
+    gc.disable()   # no collector pauses between the timing events
     for i in range(args.warmup):
         step(i, True)
     torch.cuda.synchronize()
@@ -170,6 +193,7 @@ def bench_qkv(args, dev):
         step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     avg = timer.averages_us()
     med = timer.medians_us()
     ms_per_step = 1e3 * wall / args.steps
@@ -195,6 +219,7 @@ def bench_qkv(args, dev):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": round(settled, 3),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -218,6 +243,12 @@ def run_timed(ops, args):
     events.  Returns (ms per step from the host clock, {name: avg us})."""
     import torch
     timer = KernelTimer()
+
+    def plain():
+        for _, fn in ops:
+            fn()
+    settle(plain, getattr(args, "settle_s", 0.0))
+    gc.disable()
     for _ in range(args.warmup):
         for name, fn in ops:
             timer.time(name, fn)
@@ -230,6 +261,7 @@ def run_timed(ops, args):
             timer.time(name, fn)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     return 1e3 * wall / args.steps, timer.averages_us()
 
 
@@ -890,8 +922,10 @@ def copy_calibration(dev, nbytes: int = 512 << 20, reps: int = 3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed seconds of the step before the W warm-up steps (clock ramp)")
     ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "moe", "moe_train", "sync", "sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
