@@ -55,8 +55,19 @@ __device__ __forceinline__ v2i convert8(const uint32_t *d, float inv) {
 
 // quad_perm DPP control [1,0,3,2]: swap the lanes of each pair
 constexpr int kQuadSwap1 = 0xB1;
-// resident waves per CU for the axis-1 quantizer's strided walk
-constexpr int kQuantWavesPerCu = 16;
+// The axis-1 quantizer's strided walk: resident waves per CU, and the input
+// size from which its loads and stores are nontemporal.  Measured on MI355X
+// (settled clocks, medians): 32 waves per CU instead of 16 take 6144x4096
+// from 16.5 to 16.0 us and 4096x4096 from 12.3 to 11.5 us (more bytes in
+// flight while the launch ramps up); nontemporal accesses take 8192x24576 and
+// 16384x16384 from 5.2-5.35 to 5.46 TB/s but slow the tensors that fit the
+// 256 MB Infinity Cache (6144x4096: 16.5 -> 18.1 us), so only inputs of at
+// least that size use them, with 16 waves per CU.
+constexpr int kQuantWavesPerCu = 32;
+constexpr int kQuantWavesPerCuLarge = 16;
+constexpr int64_t kQuantNontemporalBytes = 256ll << 20;
+// resident waves per CU of the gather quantizer (the axis-1 walk over gathered rows)
+constexpr int kGatherWavesPerCu = 16;
 
 // ---------------------------------------------------------------- axis 1
 // The flat array of blocks (rows * cols / 32 of them; a block never straddles
@@ -66,13 +77,15 @@ constexpr int kQuantWavesPerCu = 16;
 // Each wave walks a strided list of steps with the next step's loads in
 // flight while it converts the current one, so a wave pays the memory latency
 // once, not once per step.
+template <bool NT = false>
 __device__ __forceinline__ void load_step(const uint16_t *__restrict__ x, int64_t b0,
                                           int64_t nblocks, int lane, uint32_t (*d)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int64_t blk = b0 + (u >> 1) * 32 + (lane >> 1);
         if (blk < nblocks) {
-            const v4i v = *reinterpret_cast<const v4i *>(x + blk * 32 + (lane & 1) * 16 + (u & 1) * 8);
+            const v4i *p = reinterpret_cast<const v4i *>(x + blk * 32 + (lane & 1) * 16 + (u & 1) * 8);
+            const v4i v = NT ? __builtin_nontemporal_load(p) : *p;
             d[u][0] = v.x; d[u][1] = v.y; d[u][2] = v.z; d[u][3] = v.w;
         } else {
             d[u][0] = d[u][1] = d[u][2] = d[u][3] = 0;
@@ -80,6 +93,7 @@ __device__ __forceinline__ void load_step(const uint16_t *__restrict__ x, int64_
     }
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void convert_step(uint8_t *__restrict__ q, uint8_t *__restrict__ scales,
                                              int64_t b0, int64_t nblocks, int lane,
                                              uint32_t (*d)[4]) {
@@ -97,7 +111,11 @@ __device__ __forceinline__ void convert_step(uint8_t *__restrict__ q, uint8_t *_
         v2i o0 = convert8(d[2 * h], inv), o1 = convert8(d[2 * h + 1], inv);
         v4i o = v4i{o0.x, o0.y, o1.x, o1.y};
         if (code[h] == 255u) o = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
-        if (blk < nblocks) *reinterpret_cast<v4i *>(q + blk * 32 + (lane & 1) * 16) = o;
+        if (blk < nblocks) {
+            v4i *p = reinterpret_cast<v4i *>(q + blk * 32 + (lane & 1) * 16);
+            if constexpr (NT) __builtin_nontemporal_store(o, p);
+            else *p = o;
+        }
     }
     // lane l stores the scale of block b0 + l, held by lane 2*(l%32) of sub-step l/32
     const int src = (lane & 31) * 2;
@@ -106,6 +124,7 @@ __device__ __forceinline__ void convert_step(uint8_t *__restrict__ q, uint8_t *_
     if (b0 + lane < nblocks) scales[b0 + lane] = (uint8_t)sc;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(256) void quantize_axis1_kernel(const uint16_t *__restrict__ x,
                                                              uint8_t *__restrict__ q,
                                                              uint8_t *__restrict__ scales,
@@ -117,11 +136,11 @@ __global__ __launch_bounds__(256) void quantize_axis1_kernel(const uint16_t *__r
     int64_t step = wave;
     if (step >= nsteps) return;
     uint32_t cur[4][4], nxt[4][4];
-    load_step(x, step * 64, nblocks, lane, cur);
+    load_step<NT>(x, step * 64, nblocks, lane, cur);
     for (; step < nsteps; step += nwaves) {
         const bool more = step + nwaves < nsteps;
-        if (more) load_step(x, (step + nwaves) * 64, nblocks, lane, nxt);
-        convert_step(q, scales, step * 64, nblocks, lane, cur);
+        if (more) load_step<NT>(x, (step + nwaves) * 64, nblocks, lane, nxt);
+        convert_step<NT>(q, scales, step * 64, nblocks, lane, cur);
         if (more) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -639,13 +658,18 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int ax
     if (axis == 1) {
         const int64_t nblocks = rows * (cols / 32);
         const int64_t nsteps = (nblocks + 63) / 64;
-        // kQuantWavesPerCu waves per CU, each walking several steps
+        // a fixed number of waves per CU, each walking several steps
+        const bool nt = rows * cols * 2 >= kQuantNontemporalBytes;
         int64_t grid = (nsteps + 3) / 4;
-        const int64_t cap = (int64_t)device_cu_count() * (kQuantWavesPerCu / 4);
+        const int64_t cap = (int64_t)device_cu_count() * ((nt ? kQuantWavesPerCuLarge : kQuantWavesPerCu) / 4);
         if (grid > cap) grid = cap;
         if (grid < 1) grid = 1;
-        hipLaunchKernelGGL(quantize_axis1_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, q,
-                           scales, nblocks);
+        if (nt)
+            hipLaunchKernelGGL(quantize_axis1_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x, q,
+                               scales, nblocks);
+        else
+            hipLaunchKernelGGL(quantize_axis1_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, x, q,
+                               scales, nblocks);
     } else {
         return launch_quantize_axis0_batched(x, 1, rows, cols, q, scales, stream);
     }
@@ -668,7 +692,7 @@ hipError_t launch_quantize_gather(const uint16_t *x, int64_t rows_in, int64_t co
     const int64_t nblocks = rows_out * bpr;
     const int64_t nsteps = (nblocks + 63) / 64;
     int64_t grid = (nsteps + 3) / 4;
-    const int64_t cap = (int64_t)device_cu_count() * (kQuantWavesPerCu / 4);
+    const int64_t cap = (int64_t)device_cu_count() * (kGatherWavesPerCu / 4);
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(quantize_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x,
