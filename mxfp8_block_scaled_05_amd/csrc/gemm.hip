@@ -192,7 +192,7 @@ __device__ int find_group(const int32_t *off, int G, int64_t M_total, int tm, in
 }
 
 // Per-tile state and the operations of one k-step, shared by both pipelines.
-template <int BM, int BN, int WM, bool BPACK, bool KALIGN>
+template <int BM, int BN, int WM, bool BPACK, bool KALIGN, bool SAC = false>
 struct TileOps {
     static constexpr int WN = kWaves / WM;
     static constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
@@ -201,8 +201,14 @@ struct TileOps {
     // == 0) are a dword per row per step; B scales are the packed layout's
     // 64 bytes per 16-row atom per step, or (canonical B, K % 128 == 0) a
     // dword per row.  With K % 128 != 0, A (and canonical B) scale bytes come
-    // through registers instead (compiler-visible byte loads).
-    static constexpr bool SA_LDS = KALIGN;
+    // through registers instead (compiler-visible byte loads).  SAC: the A
+    // scales come instead from a chunk buffer outside the stage ring that
+    // holds 8 k-steps of them (32 bytes per row), copied once per 8 steps.
+    static_assert(!SAC || KALIGN, "chunked A scales need K % 128 == 0");
+    static constexpr bool SA_LDS = KALIGN && !SAC;
+    static constexpr bool SA_REG = !KALIGN;
+    static constexpr int kChunkSteps = 8;
+    static constexpr int CHUNK = BM * 4 * kChunkSteps;     // bytes of one chunk buffer
     static constexpr bool SB_LDS = BPACK || KALIGN;
     static constexpr int TILE = (BM + BN) * 128;
     static constexpr int SA_OFF = TILE;
@@ -325,11 +331,28 @@ struct TileOps {
         }
     }
 
-    // scale bytes of one step from LDS (the MFMA reads bits [7:0], op_sel 0)
-    __device__ __forceinline__ void lds_scales(const uint8_t *st, int *sas, int *sbs) const {
+    // SAC: A scale bytes of k-steps [8c, 8c + 8) of every tile row, 32 bytes
+    // per row, into the chunk buffer at LDS address cbase (row r at r * 32):
+    // two lanes per row, 16 bytes each, each wave a 32-row share.  Rows past
+    // the operand's end read zero; bytes past a row's K range are never read.
+    __device__ __forceinline__ void issue_sa_chunk(int c, uint32_t cbase) const {
+        static_assert(BM == 8 * 32, "eight waves of 32 rows");
+        const int rr = w * 32 + (lane >> 1);
+        dma16(rsa, (uint32_t)(rr * lsa + c * 32 + (lane & 1) * 16), cbase + w * 1024);
+    }
+
+    // scale bytes of one step from LDS (the MFMA reads bits [7:0], op_sel 0);
+    // chunk: the SAC chunk buffer holding step ks
+    __device__ __forceinline__ void lds_scales(const uint8_t *st, int *sas, int *sbs, const uint8_t *chunk = nullptr,
+                                               int ks = 0) const {
         if constexpr (SA_LDS) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
+        }
+        if constexpr (SAC) {
+            const int kb = (ks % kChunkSteps) * 4 + lblk;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sas[i] = chunk[(wm * WTM + i * 16 + lrow) * 32 + kb];
         }
         if constexpr (SB_LDS) {
 #pragma unroll
@@ -535,10 +558,13 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 // NST stages: the copies of step ks+NST-1 are issued at the top of step ks.
 // NST = 3 needs every copy to go through LDS (KALIGN) so that a wave's copy
 // count per step is fixed and the wait can leave the next steps in flight.
-template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool KALIGN, int NST>
+template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool KALIGN, int NST, bool SAC = false>
 __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_end, int64_t n0, int64_t g,
                                           int64_t kbase, int64_t kbound, int KS, uint8_t *smem) {
-    using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
+    using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
+    static_assert(!SAC || NST == 2, "chunked A scales with the two-stage ring");
+    // SAC chunk buffers (two) after the stage ring
+    uint8_t *chunks = smem + NST * T::STAGE;
     constexpr int FM = T::FM, FN = T::FN;
     static_assert(NST == 2 || (NST == 3 && KALIGN), "three stages need all copies through LDS");
     T t;
@@ -552,7 +578,8 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
 
     uint32_t sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
     if (KS > 0) {                       // an empty group (grouped-K) stores zeros
-        if constexpr (!T::SA_LDS) t.fetch_sa(0, sa_nxt);
+        if constexpr (SAC) t.issue_sa_chunk(0, t.lds0 + NST * T::STAGE);
+        if constexpr (T::SA_REG) t.fetch_sa(0, sa_nxt);
         if constexpr (!T::SB_LDS) t.fetch_sb(0, sb_nxt);
         t.issue(0, 0);
         if constexpr (NST == 3) {
@@ -572,7 +599,15 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
         } else {
             wait_copies_and_sync();
         }
-        if constexpr (!T::SA_LDS) {
+        if constexpr (SAC) {
+            // at the first step of chunk c every wave is past chunk c-1's
+            // steps: its buffer takes chunk c+1 (awaited at the next step's
+            // top with everything else)
+            const int c = ks / T::kChunkSteps;
+            if (ks % T::kChunkSteps == 0 && (c + 1) * T::kChunkSteps < KS)
+                t.issue_sa_chunk(c + 1, t.lds0 + NST * T::STAGE + ((c + 1) & 1) * T::CHUNK);
+        }
+        if constexpr (T::SA_REG) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
             if (ks + 1 < KS) t.fetch_sa(ks + 1, sa_nxt);
@@ -592,8 +627,8 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
 
         const uint8_t *st = smem + cur * T::STAGE;
         int sas[FM], sbs[FN];
-        t.lds_scales(st, sas, sbs);
-        if constexpr (!T::SA_LDS) {
+        t.lds_scales(st, sas, sbs, chunks + ((ks / T::kChunkSteps) & 1) * T::CHUNK, ks);
+        if constexpr (T::SA_REG) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sas[i] = (int)(sa_cur[i] & 0xFFu);
         }
@@ -607,6 +642,7 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
         cur = cur + 1 == NST ? 0 : cur + 1;
     }
     (void)ncopies;
+    (void)chunks;
     const int64_t row0 = m0 + t.wm * T::WTM, col0 = n0 + t.wn * T::WTN;
     constexpr int ES = OUT_BF16 ? 2 : 4;
     // uniform over the workgroup: the tile's columns inside C, rows 16 B
@@ -621,12 +657,13 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
 }
 
 template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false,
-          int NST = 2>
+          int NST = 2, bool SAC = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-    using T = TileOps<BM, BN, WM, BPACK, KALIGN>;
-    static_assert(NST * T::STAGE <= 160 * 1024, "LDS budget");
+    using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
+    constexpr int LDS = NST * T::STAGE + (SAC ? 2 * T::CHUNK : 0);
+    static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(!GK || (!BPACK && !KALIGN && !GROUPED), "grouped-K reads canonical operands");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * T::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
     int64_t m0, m_end, n0, g, kbase = 0, kbound = -1;
     int KS = p.KS;
     if constexpr (GK) {
@@ -636,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     } else {
         if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
     }
-    gemm_tile<BM, BN, WM, BPACK, OUT_BF16, KALIGN, NST>(p, m0, m_end, n0, g, kbase, kbound, KS, smem);
+    gemm_tile<BM, BN, WM, BPACK, OUT_BF16, KALIGN, NST, SAC>(p, m0, m_end, n0, g, kbase, kbound, KS, smem);
 }
 
 // Grouped-K (expert weight gradients) with T % 128 == 0: a tile whose token
@@ -722,23 +759,26 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // order, so they fill the chip's first wave and the small ones the tail.
 // Each range is renumbered XCD-aware on its own (mix_big is a multiple of 8,
 // so a workgroup's XCD is its id mod 8 in both).
-template <bool BPACK, bool OUT_BF16, bool KALIGN>
+template <bool BPACK, bool OUT_BF16, bool KALIGN, bool SAC = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
-    constexpr int SB = TileOps<256, 256, 2, BPACK, KALIGN>::STAGE, SS = TileOps<256, 128, 4, BPACK, KALIGN>::STAGE;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (SB > SS ? SB : SS)];
+    constexpr int SB = TileOps<256, 256, 2, BPACK, KALIGN, SAC>::STAGE;
+    constexpr int SS = TileOps<256, 128, 4, BPACK, KALIGN, SAC>::STAGE;
+    constexpr int CH = SAC ? 2 * TileOps<256, 256, 2, BPACK, KALIGN, SAC>::CHUNK : 0;
+    static_assert(2 * (SB > SS ? SB : SS) + CH <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (SB > SS ? SB : SS) + CH];
     const int bid = blockIdx.x;
     int tm, tn;
     if (bid < p.mix_big) {
         grouped_order(xcd_logical(bid, p.mix_big), p.tiles_m, p.mix_big_cols, tm, tn);
-        gemm_tile<256, 256, 2, BPACK, OUT_BF16, KALIGN, 2>(p, (int64_t)tm * 256, p.M, (int64_t)tn * 256, 0, 0,
-                                                           -1, p.KS, smem);
+        gemm_tile<256, 256, 2, BPACK, OUT_BF16, KALIGN, 2, SAC>(p, (int64_t)tm * 256, p.M, (int64_t)tn * 256, 0,
+                                                                0, -1, p.KS, smem);
     } else {
         const int n_small = (int)gridDim.x - p.mix_big;
         const int small_cols = n_small / p.tiles_m;
         grouped_order(xcd_logical(bid - p.mix_big, n_small), p.tiles_m, small_cols, tm, tn);
-        gemm_tile<256, 128, 4, BPACK, OUT_BF16, KALIGN, 2>(p, (int64_t)tm * 256, p.M,
-                                                           (int64_t)p.mix_big_cols * 256 + (int64_t)tn * 128, 0,
-                                                           0, -1, p.KS, smem);
+        gemm_tile<256, 128, 4, BPACK, OUT_BF16, KALIGN, 2, SAC>(p, (int64_t)tm * 256, p.M,
+                                                                (int64_t)p.mix_big_cols * 256 + (int64_t)tn * 128,
+                                                                0, 0, -1, p.KS, smem);
     }
 }
 
@@ -749,10 +789,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
 template <int BM, int BN, int WM, bool BP, bool GROUPED>
 constexpr int kStages3 = GROUPED && 3 * TileOps<BM, BN, WM, BP, true>::STAGE <= 160 * 1024 ? 3 : 2;
 
+// Dense launches with K % 512 == 0 (A scale rows a multiple of 16 bytes, so
+// every 16-byte piece of a chunk lies wholly inside or wholly past its row)
+// copy the A scales in chunks of 8 k-steps instead of a dword per row per
+// step.  Each per-step copy touches one 128-byte line per row, as many line
+// requests as the step's whole A tile; measured on MI355X the chunked copy
+// takes 8192x24576x4096 from 782 to 743 us, 8192x4096x12288 from 362 to
+// 347 us and the canonical-B 24576x4096x8192 from 775 to 749 us.
+static bool chunked_a_scales(int64_t K) { return K % 512 == 0; }
+
 template <int BM, int BN, int WM, bool GROUPED>
 static hipError_t launch_tile(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
     dim3 grid((unsigned)nwg), block(kThreads);
     const bool kal = p.K % 128 == 0;
+    if constexpr (!GROUPED) {
+        if (chunked_a_scales(p.K)) {
+#define MX_LAUNCHC(BP, BF) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, false, true, false, 2, true>), grid, block, 0, s, p)
+            if (b_packed) { if (c_bf16) MX_LAUNCHC(true, true); else MX_LAUNCHC(true, false); }
+            else { if (c_bf16) MX_LAUNCHC(false, true); else MX_LAUNCHC(false, false); }
+#undef MX_LAUNCHC
+            return hipGetLastError();
+        }
+    }
 #define MX_LAUNCH2(BP, BF, KA) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, GROUPED, KA>), grid, block, 0, s, p)
 #define MX_LAUNCH3(BP, BF) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, GROUPED, true, false, kStages3<BM, BN, WM, BP, GROUPED>>), grid, block, 0, s, p)
     if (kal) {
@@ -821,7 +879,11 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
         dim3 grid((unsigned)(p.mix_big + p.tiles_m * d.small_cols)), block(kThreads);
         const bool kal = K % 128 == 0;
 #define MX_MIXED(BP, BF, KA) hipLaunchKernelGGL((gemm_mixed_kernel<BP, BF, KA>), grid, block, 0, stream, p)
-        if (kal) {
+#define MX_MIXEDC(BP, BF) hipLaunchKernelGGL((gemm_mixed_kernel<BP, BF, true, true>), grid, block, 0, stream, p)
+        if (chunked_a_scales(K)) {
+            if (b_packed) { if (c_bf16) MX_MIXEDC(true, true); else MX_MIXEDC(true, false); }
+            else { if (c_bf16) MX_MIXEDC(false, true); else MX_MIXEDC(false, false); }
+        } else if (kal) {
             if (b_packed) { if (c_bf16) MX_MIXED(true, true, true); else MX_MIXED(true, false, true); }
             else { if (c_bf16) MX_MIXED(false, true, true); else MX_MIXED(false, false, true); }
         } else {
@@ -829,6 +891,7 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
             else { if (c_bf16) MX_MIXED(false, true, false); else MX_MIXED(false, false, false); }
         }
 #undef MX_MIXED
+#undef MX_MIXEDC
         return hipGetLastError();
     }
     if (d.big_cols > 0) {

@@ -195,6 +195,41 @@ def test_lds_footprint(BM, BN, WM, grouped, packed, kalign):
     assert (BM // WM) % 16 == 0 and (BN // WN) % 16 == 0 and (BM // WM) // 16 >= 2
 
 
+CHUNK_STEPS = 8
+
+
+@pytest.mark.parametrize("M,N,K", [s for s in DENSE_SHAPES if s[2] % 512 == 0] + [(300, 520, 1536), (77, 256, 512)])
+def test_chunked_a_scale_copies(M, N, K):
+    """Dense launches with K % 512 == 0 copy each tile's A scales in chunks of
+    8 k-steps: wave w, lane l copies the 16 bytes at offset
+    row * KB + 32c + 16 (l % 2) of the tile's A-scale descriptor, row =
+    32w + l // 2.  Every piece must be wholly inside the descriptor's range
+    (and so inside a_s) or wholly past it (read as zero, never partly), and
+    the pieces that carry scales of real k-steps must be inside.  Mirrors
+    gemm.hip's chunked A-scale path; also checks the LDS budget of the
+    two chunk buffers beside the two stages."""
+    KB, KS = K // 32, ceil_div(K, KSTEP)
+    assert K % 512 == 0 and KB % 16 == 0
+    chunks = ceil_div(KS, CHUNK_STEPS)
+    for m0, n0, BM, BN in dense_tiles(M, N):
+        rows_a = min(BM, M - m0)
+        base, num = m0 * KB, (rows_a - 1) * KB + KB
+        assert base + num <= M * KB
+        for w in range(WAVES):
+            for lane in range(64):
+                row = 32 * w + lane // 2
+                for c in range(chunks):
+                    off = row * KB + 32 * c + 16 * (lane % 2)
+                    inside = off + 16 <= num
+                    assert inside or off >= num, (M, N, K, m0, row, c)
+                    if row < rows_a and 32 * c + 16 * (lane % 2) < KB:
+                        assert inside                      # real scales arrive
+    # LDS: two stages without per-step A scales plus two 8 KB chunk buffers
+    for BM, BN, packed in ((256, 256, True), (256, 256, False), (256, 128, True), (256, 128, False)):
+        stage = (BM + BN) * 128 + BN * 4
+        assert 2 * max(stage, (256 + 256) * 128 + 256 * 4) + 2 * BM * 32 <= 160 * 1024
+
+
 def gk_descriptors(M, N, T, lo, hi, tm, tn, BM=256, BN=256):
     """The grouped-K kernel's descriptors for tile (tm, tn) of a group with
     token range [lo, hi): A [M][T] and B [N][T] canonical, row stride T."""
