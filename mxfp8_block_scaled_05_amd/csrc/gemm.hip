@@ -802,9 +802,11 @@ template <int BM, int BN, int WM, bool GROUPED>
 static hipError_t launch_tile(const GemmParams &p, bool b_packed, bool c_bf16, int nwg, hipStream_t s) {
     dim3 grid((unsigned)nwg), block(kThreads);
     const bool kal = p.K % 128 == 0;
-    if constexpr (!GROUPED) {
+    // (dense tiles, and grouped 256-row tiles, which keep the two-stage ring)
+    if constexpr (!GROUPED || (BM == 256 && kStages3<BM, BN, WM, true, GROUPED> == 2 &&
+                               kStages3<BM, BN, WM, false, GROUPED> == 2)) {
         if (chunked_a_scales(p.K)) {
-#define MX_LAUNCHC(BP, BF) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, false, true, false, 2, true>), grid, block, 0, s, p)
+#define MX_LAUNCHC(BP, BF) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, BP, BF, GROUPED, true, false, 2, true>), grid, block, 0, s, p)
             if (b_packed) { if (c_bf16) MX_LAUNCHC(true, true); else MX_LAUNCHC(true, false); }
             else { if (c_bf16) MX_LAUNCHC(false, true); else MX_LAUNCHC(false, false); }
 #undef MX_LAUNCHC

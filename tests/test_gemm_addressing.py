@@ -198,6 +198,40 @@ def test_lds_footprint(BM, BN, WM, grouped, packed, kalign):
 CHUNK_STEPS = 8
 
 
+def check_chunk_copies(M, K, tiles):
+    """tiles: (m0, m_end) of 256-row tiles over an A of M rows"""
+    KB, KS = K // 32, ceil_div(K, KSTEP)
+    assert K % 512 == 0 and KB % 16 == 0
+    chunks = ceil_div(KS, CHUNK_STEPS)
+    for m0, m_end in tiles:
+        rows_a = min(256, m_end - m0)
+        base, num = m0 * KB, (rows_a - 1) * KB + KB
+        assert base + num <= M * KB
+        for w in range(WAVES):
+            for lane in range(64):
+                row = 32 * w + lane // 2
+                for c in range(chunks):
+                    off = row * KB + 32 * c + 16 * (lane % 2)
+                    inside = off + 16 <= num
+                    assert inside or off >= num, (M, K, m0, row, c)
+                    if row < rows_a and 32 * c + 16 * (lane % 2) < KB:
+                        assert inside                      # real scales arrive
+
+
+def test_chunked_a_scale_copies_grouped():
+    """The grouped GEMM's 256-row tiles (groups averaging 256 rows or more)
+    take the same chunked A-scale copies when K % 512 == 0."""
+    import workloads as wl
+    rng = np.random.default_rng(7)
+    for G, K, tokens in ((128, 2048, 8192), (16, 512, 2048)):
+        route = wl.zipf_topk_routing(rng, tokens, G, 8)
+        offsets, _, _ = wl.group_layout(route, G)
+        M_total = int(offsets[-1])
+        assert M_total >= 256 * G                   # the launcher takes 256-row tiles
+        tiles = [(m0, m_end) for g, m0, m_end in grouped_tiles(offsets, M_total, 256)]
+        check_chunk_copies(M_total, K, tiles)
+
+
 @pytest.mark.parametrize("M,N,K", [s for s in DENSE_SHAPES if s[2] % 512 == 0] + [(300, 520, 1536), (77, 256, 512)])
 def test_chunked_a_scale_copies(M, N, K):
     """Dense launches with K % 512 == 0 copy each tile's A scales in chunks of
@@ -208,22 +242,7 @@ def test_chunked_a_scale_copies(M, N, K):
     the pieces that carry scales of real k-steps must be inside.  Mirrors
     gemm.hip's chunked A-scale path; also checks the LDS budget of the
     two chunk buffers beside the two stages."""
-    KB, KS = K // 32, ceil_div(K, KSTEP)
-    assert K % 512 == 0 and KB % 16 == 0
-    chunks = ceil_div(KS, CHUNK_STEPS)
-    for m0, n0, BM, BN in dense_tiles(M, N):
-        rows_a = min(BM, M - m0)
-        base, num = m0 * KB, (rows_a - 1) * KB + KB
-        assert base + num <= M * KB
-        for w in range(WAVES):
-            for lane in range(64):
-                row = 32 * w + lane // 2
-                for c in range(chunks):
-                    off = row * KB + 32 * c + 16 * (lane % 2)
-                    inside = off + 16 <= num
-                    assert inside or off >= num, (M, N, K, m0, row, c)
-                    if row < rows_a and 32 * c + 16 * (lane % 2) < KB:
-                        assert inside                      # real scales arrive
+    check_chunk_copies(M, K, [(m0, M) for m0, n0, BM, BN in dense_tiles(M, N) if BM == 256])
     # LDS: two stages without per-step A scales plus two 8 KB chunk buffers
     for BM, BN, packed in ((256, 256, True), (256, 256, False), (256, 128, True), (256, 128, False)):
         stage = (BM + BN) * 128 + BN * 4
