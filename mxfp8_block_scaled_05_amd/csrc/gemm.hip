@@ -209,7 +209,11 @@ struct TileOps {
     static constexpr bool SA_REG = !KALIGN;
     static constexpr int kChunkSteps = 8;
     static constexpr int CHUNK = BM * 4 * kChunkSteps;     // bytes of one chunk buffer
-    static constexpr bool SB_LDS = BPACK || KALIGN;
+    // SBC: canonical B scales of 256-row B tiles chunked the same way
+    static constexpr bool SBC = SAC && !BPACK && BN == 256;
+    static constexpr bool SB_LDS = BPACK || (KALIGN && !SBC);
+    static constexpr bool SB_REG = !BPACK && !KALIGN;
+    static constexpr int CHUNK_B = SBC ? BN * 4 * kChunkSteps : 0;
     static constexpr int TILE = (BM + BN) * 128;
     static constexpr int SA_OFF = TILE;
     static constexpr int SB_OFF = SA_OFF + (SA_LDS ? BM * 4 : 0);
@@ -340,11 +344,22 @@ struct TileOps {
         const int rr = w * 32 + (lane >> 1);
         dma16(rsa, (uint32_t)(rr * lsa + c * 32 + (lane & 1) * 16), cbase + w * 1024);
     }
+    // SBC: the same for the canonical B tile's scales
+    __device__ __forceinline__ void issue_sb_chunk(int c, uint32_t cbase) const {
+        static_assert(BN == 8 * 32, "eight waves of 32 rows");
+        const int rr = w * 32 + (lane >> 1);
+        dma16(rsb, (uint32_t)(rr * lsb + c * 32 + (lane & 1) * 16), cbase + w * 1024);
+    }
 
     // scale bytes of one step from LDS (the MFMA reads bits [7:0], op_sel 0);
     // chunk: the SAC chunk buffer holding step ks
     __device__ __forceinline__ void lds_scales(const uint8_t *st, int *sas, int *sbs, const uint8_t *chunk = nullptr,
-                                               int ks = 0) const {
+                                               int ks = 0, const uint8_t *chunk_b = nullptr) const {
+        if constexpr (SBC) {
+            const int kb = (ks % kChunkSteps) * 4 + lblk;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sbs[j] = chunk_b[(wn * WTN + j * 16 + lrow) * 32 + kb];
+        }
         if constexpr (SA_LDS) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
@@ -563,8 +578,9 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
                                           int64_t kbase, int64_t kbound, int KS, uint8_t *smem) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
     static_assert(!SAC || NST == 2, "chunked A scales with the two-stage ring");
-    // SAC chunk buffers (two) after the stage ring
+    // SAC chunk buffers (two) after the stage ring, then (SBC) two for B
     uint8_t *chunks = smem + NST * T::STAGE;
+    uint8_t *chunks_b = chunks + 2 * T::CHUNK;
     constexpr int FM = T::FM, FN = T::FN;
     static_assert(NST == 2 || (NST == 3 && KALIGN), "three stages need all copies through LDS");
     T t;
@@ -579,8 +595,9 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
     uint32_t sa_cur[FM], sa_nxt[FM], sb_cur[FN], sb_nxt[FN];
     if (KS > 0) {                       // an empty group (grouped-K) stores zeros
         if constexpr (SAC) t.issue_sa_chunk(0, t.lds0 + NST * T::STAGE);
+        if constexpr (T::SBC) t.issue_sb_chunk(0, t.lds0 + NST * T::STAGE + 2 * T::CHUNK);
         if constexpr (T::SA_REG) t.fetch_sa(0, sa_nxt);
-        if constexpr (!T::SB_LDS) t.fetch_sb(0, sb_nxt);
+        if constexpr (T::SB_REG) t.fetch_sb(0, sb_nxt);
         t.issue(0, 0);
         if constexpr (NST == 3) {
             if (KS > 1) t.issue(1, 1);
@@ -604,15 +621,18 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
             // steps: its buffer takes chunk c+1 (awaited at the next step's
             // top with everything else)
             const int c = ks / T::kChunkSteps;
-            if (ks % T::kChunkSteps == 0 && (c + 1) * T::kChunkSteps < KS)
+            if (ks % T::kChunkSteps == 0 && (c + 1) * T::kChunkSteps < KS) {
                 t.issue_sa_chunk(c + 1, t.lds0 + NST * T::STAGE + ((c + 1) & 1) * T::CHUNK);
+                if constexpr (T::SBC)
+                    t.issue_sb_chunk(c + 1, t.lds0 + NST * T::STAGE + 2 * T::CHUNK + ((c + 1) & 1) * T::CHUNK_B);
+            }
         }
         if constexpr (T::SA_REG) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
             if (ks + 1 < KS) t.fetch_sa(ks + 1, sa_nxt);
         }
-        if constexpr (!T::SB_LDS) {
+        if constexpr (T::SB_REG) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
             if (ks + 1 < KS) t.fetch_sb(ks + 1, sb_nxt);
@@ -627,12 +647,13 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
 
         const uint8_t *st = smem + cur * T::STAGE;
         int sas[FM], sbs[FN];
-        t.lds_scales(st, sas, sbs, chunks + ((ks / T::kChunkSteps) & 1) * T::CHUNK, ks);
+        t.lds_scales(st, sas, sbs, chunks + ((ks / T::kChunkSteps) & 1) * T::CHUNK, ks,
+                     chunks_b + ((ks / T::kChunkSteps) & 1) * T::CHUNK_B);
         if constexpr (T::SA_REG) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sas[i] = (int)(sa_cur[i] & 0xFFu);
         }
-        if constexpr (!T::SB_LDS) {
+        if constexpr (T::SB_REG) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) sbs[j] = (int)(sb_cur[j] & 0xFFu);
         }
@@ -643,6 +664,7 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
     }
     (void)ncopies;
     (void)chunks;
+    (void)chunks_b;
     const int64_t row0 = m0 + t.wm * T::WTM, col0 = n0 + t.wn * T::WTN;
     constexpr int ES = OUT_BF16 ? 2 : 4;
     // uniform over the workgroup: the tile's columns inside C, rows 16 B
@@ -660,7 +682,7 @@ template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool 
           int NST = 2, bool SAC = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
-    constexpr int LDS = NST * T::STAGE + (SAC ? 2 * T::CHUNK : 0);
+    constexpr int LDS = NST * T::STAGE + (SAC ? 2 * T::CHUNK + 2 * T::CHUNK_B : 0);
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(!GK || (!BPACK && !KALIGN && !GROUPED), "grouped-K reads canonical operands");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
@@ -763,7 +785,8 @@ template <bool BPACK, bool OUT_BF16, bool KALIGN, bool SAC = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
     constexpr int SB = TileOps<256, 256, 2, BPACK, KALIGN, SAC>::STAGE;
     constexpr int SS = TileOps<256, 128, 4, BPACK, KALIGN, SAC>::STAGE;
-    constexpr int CH = SAC ? 2 * TileOps<256, 256, 2, BPACK, KALIGN, SAC>::CHUNK : 0;
+    constexpr int CH = SAC ? 2 * TileOps<256, 256, 2, BPACK, KALIGN, SAC>::CHUNK +
+                                 2 * TileOps<256, 256, 2, BPACK, KALIGN, SAC>::CHUNK_B : 0;
     static_assert(2 * (SB > SS ? SB : SS) + CH <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (SB > SS ? SB : SS) + CH];
     const int bid = blockIdx.x;

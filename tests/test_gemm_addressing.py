@@ -199,7 +199,7 @@ CHUNK_STEPS = 8
 
 
 def check_chunk_copies(M, K, tiles):
-    """tiles: (m0, m_end) of 256-row tiles over an A of M rows"""
+    """tiles: (r0, r_end) of 256-row operand tiles over an operand of M rows"""
     KB, KS = K // 32, ceil_div(K, KSTEP)
     assert K % 512 == 0 and KB % 16 == 0
     chunks = ceil_div(KS, CHUNK_STEPS)
@@ -242,11 +242,18 @@ def test_chunked_a_scale_copies(M, N, K):
     the pieces that carry scales of real k-steps must be inside.  Mirrors
     gemm.hip's chunked A-scale path; also checks the LDS budget of the
     two chunk buffers beside the two stages."""
-    check_chunk_copies(M, K, [(m0, M) for m0, n0, BM, BN in dense_tiles(M, N) if BM == 256])
-    # LDS: two stages without per-step A scales plus two 8 KB chunk buffers
+    tiles = dense_tiles(M, N)
+    check_chunk_copies(M, K, [(m0, M) for m0, n0, BM, BN in tiles if BM == 256])
+    # canonical B: the 256-row B tiles' scales are chunked the same way
+    check_chunk_copies(N, K, [(n0, N) for m0, n0, BM, BN in tiles if BN == 256])
+    # LDS: two stages without per-step A scales plus two 8 KB chunk buffers,
+    # and (canonical B, 256-row B tiles) without per-step B scales plus two more
     for BM, BN, packed in ((256, 256, True), (256, 256, False), (256, 128, True), (256, 128, False)):
-        stage = (BM + BN) * 128 + BN * 4
-        assert 2 * max(stage, (256 + 256) * 128 + 256 * 4) + 2 * BM * 32 <= 160 * 1024
+        sbc = not packed and BN == 256
+        stage = (BM + BN) * 128 + (0 if sbc else BN * 4)
+        big = (256 + 256) * 128 + (0 if not packed else 256 * 4)
+        chunks = 2 * BM * 32 + (2 * 256 * 32 if not packed else 0)
+        assert 2 * max(stage, big) + chunks <= 160 * 1024
 
 
 def gk_descriptors(M, N, T, lo, hi, tm, tn, BM=256, BN=256):
