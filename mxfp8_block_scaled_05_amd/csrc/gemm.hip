@@ -336,19 +336,25 @@ struct TileOps {
     }
 
     // SAC: A scale bytes of k-steps [8c, 8c + 8) of every tile row, 32 bytes
-    // per row, into the chunk buffer at LDS address cbase (row r at r * 32):
-    // two lanes per row, 16 bytes each, each wave a 32-row share.  Rows past
-    // the operand's end read zero; bytes past a row's K range are never read.
+    // per row, into the chunk buffer at LDS address cbase: two lanes per row,
+    // 16 bytes each, each wave a 32-row share; row r's 16-byte half h sits at
+    // r * 32 + 16 * (h ^ (r / 8 % 2)) so that the byte reads of 16
+    // consecutive rows (one per lane) fall in distinct banks.  Rows past the
+    // operand's end read zero; bytes past a row's K range are never read.
     __device__ __forceinline__ void issue_sa_chunk(int c, uint32_t cbase) const {
         static_assert(BM == 8 * 32, "eight waves of 32 rows");
-        const int rr = w * 32 + (lane >> 1);
-        dma16(rsa, (uint32_t)(rr * lsa + c * 32 + (lane & 1) * 16), cbase + w * 1024);
+        const int rr = w * 32 + (lane >> 1), h = (lane & 1) ^ ((rr >> 3) & 1);
+        dma16(rsa, (uint32_t)(rr * lsa + c * 32 + h * 16), cbase + w * 1024);
     }
     // SBC: the same for the canonical B tile's scales
     __device__ __forceinline__ void issue_sb_chunk(int c, uint32_t cbase) const {
         static_assert(BN == 8 * 32, "eight waves of 32 rows");
-        const int rr = w * 32 + (lane >> 1);
-        dma16(rsb, (uint32_t)(rr * lsb + c * 32 + (lane & 1) * 16), cbase + w * 1024);
+        const int rr = w * 32 + (lane >> 1), h = (lane & 1) ^ ((rr >> 3) & 1);
+        dma16(rsb, (uint32_t)(rr * lsb + c * 32 + h * 16), cbase + w * 1024);
+    }
+    // byte kb (0..31) of row r in a chunk buffer
+    __device__ __forceinline__ static int chunk_byte(int r, int kb) {
+        return r * 32 + (((kb >> 4) ^ ((r >> 3) & 1)) << 4) + (kb & 15);
     }
 
     // scale bytes of one step from LDS (the MFMA reads bits [7:0], op_sel 0);
@@ -358,7 +364,7 @@ struct TileOps {
         if constexpr (SBC) {
             const int kb = (ks % kChunkSteps) * 4 + lblk;
 #pragma unroll
-            for (int j = 0; j < FN; ++j) sbs[j] = chunk_b[(wn * WTN + j * 16 + lrow) * 32 + kb];
+            for (int j = 0; j < FN; ++j) sbs[j] = chunk_b[chunk_byte(wn * WTN + j * 16 + lrow, kb)];
         }
         if constexpr (SA_LDS) {
 #pragma unroll
@@ -367,7 +373,7 @@ struct TileOps {
         if constexpr (SAC) {
             const int kb = (ks % kChunkSteps) * 4 + lblk;
 #pragma unroll
-            for (int i = 0; i < FM; ++i) sas[i] = chunk[(wm * WTM + i * 16 + lrow) * 32 + kb];
+            for (int i = 0; i < FM; ++i) sas[i] = chunk[chunk_byte(wm * WTM + i * 16 + lrow, kb)];
         }
         if constexpr (SB_LDS) {
 #pragma unroll

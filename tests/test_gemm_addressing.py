@@ -210,11 +210,12 @@ def check_chunk_copies(M, K, tiles):
         for w in range(WAVES):
             for lane in range(64):
                 row = 32 * w + lane // 2
+                h = (lane % 2) ^ (row // 8 % 2)
                 for c in range(chunks):
-                    off = row * KB + 32 * c + 16 * (lane % 2)
+                    off = row * KB + 32 * c + 16 * h
                     inside = off + 16 <= num
                     assert inside or off >= num, (M, K, m0, row, c)
-                    if row < rows_a and 32 * c + 16 * (lane % 2) < KB:
+                    if row < rows_a and 32 * c + 16 * h < KB:
                         assert inside                      # real scales arrive
 
 
@@ -236,8 +237,8 @@ def test_chunked_a_scale_copies_grouped():
 def test_chunked_a_scale_copies(M, N, K):
     """Dense launches with K % 512 == 0 copy each tile's A scales in chunks of
     8 k-steps: wave w, lane l copies the 16 bytes at offset
-    row * KB + 32c + 16 (l % 2) of the tile's A-scale descriptor, row =
-    32w + l // 2.  Every piece must be wholly inside the descriptor's range
+    row * KB + 32c + 16 ((l % 2) ^ (row // 8 % 2)) of the tile's A-scale
+    descriptor, row = 32w + l // 2.  Every piece must be wholly inside the descriptor's range
     (and so inside a_s) or wholly past it (read as zero, never partly), and
     the pieces that carry scales of real k-steps must be inside.  Mirrors
     gemm.hip's chunked A-scale path; also checks the LDS budget of the
