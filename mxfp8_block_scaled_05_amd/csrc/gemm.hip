@@ -390,7 +390,11 @@ struct TileOps {
         for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sb + j * 16 * 128, lane);
     }
 
-    // MFMAs of A rows [i0, i1) of one step against the B fragments in registers
+    // MFMAs of A rows [i0, i1) of one step against the B fragments in
+    // registers.  The B fragment is the first operand, so each 16x16 result
+    // is C^T: lane l accumulates C[16i + l % 16][16j + 4 (l / 16) + r],
+    // r = 0..3 -- four consecutive columns of one row, which the epilogue
+    // moves as one 8-byte (bf16) or 16-byte (fp32) piece.
     __device__ __forceinline__ void mma_rows(const uint8_t *st, int i0, int i1, const v8i *bf, const int *sas,
                              const int *sbs, v4f (*acc)[FN]) const {
         const uint8_t *sa = st + wm * WTM * 128;
@@ -400,7 +404,7 @@ struct TileOps {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af, bf[j], acc[i][j], 0, 0, 0, sas[i], 0, sbs[j]);
+                    bf[j], af, acc[i][j], 0, 0, 0, sbs[j], 0, sas[i]);
         }
     }
 };
@@ -478,8 +482,8 @@ __device__ __forceinline__ bool tile_of_gk(const GemmParams &p, int64_t &m0, int
     return true;
 }
 
-// C store, element by element: lane holds C[4*(lane/16) + r][lane % 16] of
-// each 16x16 tile (used for blocks that cross the matrix edge).
+// C store, element by element: lane holds C[lane % 16][4*(lane/16) + r] of
+// each 16x16 tile (C^T fragments; used for blocks that cross the matrix edge).
 template <int FM, int FN, bool OUT_BF16>
 __device__ __forceinline__ void store_tile_scalar(const GemmParams &p, int64_t row0, int64_t col0, int64_t m_end,
                                   v4f (*acc)[FN], int lane) {
@@ -488,10 +492,10 @@ __device__ __forceinline__ void store_tile_scalar(const GemmParams &p, int64_t r
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int64_t col = col0 + j * 16 + (lane & 15);
+            const int64_t row = row0 + i * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = row0 + i * 16 + (lane >> 4) * 4 + r;
+                const int64_t col = col0 + j * 16 + (lane >> 4) * 4 + r;
                 if (row < m_end && col < N) {
                     if constexpr (OUT_BF16)
                         static_cast<uint16_t *>(p.c)[row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
@@ -525,20 +529,20 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0
     const int64_t N = p.N;
 #pragma unroll
     for (int pass = 0; pass < WTM / PR; ++pass) {
-        // scatter this pass's rows (16-row MFMA tiles i in [pass*PR/16, ...))
+        // scatter this pass's rows (16-row MFMA tiles i in [pass*PR/16, ...)):
+        // each lane's four consecutive columns of one row as one LDS write
 #pragma unroll
         for (int i = pass * (PR / 16); i < (pass + 1) * (PR / 16); ++i) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int rl = (i - pass * (PR / 16)) * 16 + (lane >> 4) * 4 + r;
-                    const int cl = j * 16 + (lane & 15);
-                    if constexpr (OUT_BF16)
-                        *reinterpret_cast<uint16_t *>(cw + rl * ROWB + cl * 2) =
-                            (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-                    else
-                        *reinterpret_cast<float *>(cw + rl * ROWB + cl * 4) = acc[i][j][r];
+                const int rl = (i - pass * (PR / 16)) * 16 + (lane & 15);
+                const int cl = j * 16 + (lane >> 4) * 4;
+                if constexpr (OUT_BF16) {
+                    const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+                    const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+                    *reinterpret_cast<v2i *>(cw + rl * ROWB + cl * 2) = v2i{(int)lo, (int)hi};
+                } else {
+                    *reinterpret_cast<v4f *>(cw + rl * ROWB + cl * 4) = acc[i][j];
                 }
             }
         }
