@@ -367,14 +367,41 @@ __device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, u
 
 // one workgroup per tile; tiles numbered row-tile-major over a 1-D grid
 // (batched: matrix-major)
-__device__ __forceinline__ void tile_origin(int64_t rows, int64_t cols, int64_t &b, int64_t &R0,
-                                            int64_t &C0) {
+__device__ __forceinline__ void tile_origin_of(int64_t idx, int64_t rows, int64_t cols, int64_t &b, int64_t &R0,
+                                               int64_t &C0) {
     const int64_t tiles_c = (cols + kA0Tile - 1) / kA0Tile;
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * tiles_c;
-    const int64_t t = blockIdx.x % tiles;
-    b = blockIdx.x / tiles;
+    const int64_t t = idx % tiles;
+    b = idx / tiles;
     R0 = (t / tiles_c) * kA0Tile;
     C0 = (t % tiles_c) * kA0Tile;
+}
+__device__ __forceinline__ void tile_origin(int64_t rows, int64_t cols, int64_t &b, int64_t &R0,
+                                            int64_t &C0) {
+    tile_origin_of(blockIdx.x, rows, cols, b, R0, C0);
+}
+
+// The tile walk used when cols % 8 == 0: a workgroup takes tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ... and keeps the next tile's sixteen-byte loads in
+// registers (in flight) while it quantizes the current one out of LDS, so the
+// load latency of a tile overlaps the previous tile's work.
+constexpr int kA0Loads = kA0Tile / 16;     // 16-byte loads per thread per tile
+__device__ __forceinline__ void load_tile_regs(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                                               int64_t R0, int64_t C0, int t, v4i *v) {
+    const int ch = t & 15;
+    const int64_t c = C0 + ch * 8;
+#pragma unroll
+    for (int i = 0; i < kA0Loads; ++i) {
+        const int r = i * 16 + (t >> 4);
+        v[i] = v4i{0, 0, 0, 0};
+        if (R0 + r < rows && c < cols) v[i] = *reinterpret_cast<const v4i *>(x + (R0 + r) * cols + c);
+    }
+}
+__device__ __forceinline__ void store_tile_regs(uint8_t *tile, int t, const v4i *v) {
+    const int ch = t & 15;
+#pragma unroll
+    for (int i = 0; i < kA0Loads; ++i)
+        *reinterpret_cast<v4i *>(tile + tile_slot(i * 16 + (t >> 4), ch)) = v[i];
 }
 
 // x[batch][rows][cols] -> q[batch][cols][rows], scales[batch][cols][rows/32]
@@ -653,6 +680,89 @@ __global__ __launch_bounds__(256) void quantize_packed_kernel(const uint16_t *__
     sp[tile_lin * (kScaleStepBytes / 4) + t] = o;
 }
 
+// axis 0 over a tile walk (cols % 8 == 0); batch matrices x[batch][rows][cols]
+__global__ __launch_bounds__(256) void quantize_axis0_walk_kernel(const uint16_t *__restrict__ x,
+                                                                  uint8_t *__restrict__ q,
+                                                                  uint8_t *__restrict__ scales, int64_t rows,
+                                                                  int64_t cols, int64_t ntiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    const int t = threadIdx.x;
+    int64_t idx = blockIdx.x;
+    if (idx >= ntiles) return;
+    int64_t b, R0, C0;
+    tile_origin_of(idx, rows, cols, b, R0, C0);
+    v4i v[kA0Loads];
+    load_tile_regs(x + b * rows * cols, rows, cols, R0, C0, t, v);
+    for (; idx < ntiles; idx += gridDim.x) {
+        store_tile_regs(tile, t, v);
+        __syncthreads();
+        const int64_t nxt = idx + gridDim.x;
+        int64_t b2 = b, R2 = R0, C2 = C0;
+        if (nxt < ntiles) {
+            tile_origin_of(nxt, rows, cols, b2, R2, C2);
+            load_tile_regs(x + b2 * rows * cols, rows, cols, R2, C2, t, v);
+        }
+        axis0_from_tile(tile, stile, q + b * rows * cols, scales + b * cols * (rows / 32), rows, cols, R0, C0, t);
+        __syncthreads();          // every thread's stores have read the tile
+        b = b2;
+        R0 = R2;
+        C0 = C2;
+    }
+}
+
+// both axes over a tile walk (cols % 8 == 0)
+__global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t *__restrict__ x,
+                                                                 uint8_t *__restrict__ q_row,
+                                                                 uint8_t *__restrict__ s_row,
+                                                                 uint8_t *__restrict__ q_col,
+                                                                 uint8_t *__restrict__ s_col, int64_t rows,
+                                                                 int64_t cols, int64_t ntiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    const int t = threadIdx.x;
+    int64_t idx = blockIdx.x;
+    if (idx >= ntiles) return;
+    int64_t b_unused, R0, C0;
+    tile_origin_of(idx, rows, cols, b_unused, R0, C0);
+    v4i v[kA0Loads];
+    load_tile_regs(x, rows, cols, R0, C0, t, v);
+    const int64_t nb = cols / 32;
+    for (; idx < ntiles; idx += gridDim.x) {
+        store_tile_regs(tile, t, v);
+        __syncthreads();
+        const int64_t nxt = idx + gridDim.x;
+        int64_t R2 = R0, C2 = C0;
+        if (nxt < ntiles) {
+            tile_origin_of(nxt, rows, cols, b_unused, R2, C2);
+            load_tile_regs(x, rows, cols, R2, C2, t, v);
+        }
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+            const int u = u2 * 256 + t, r = u >> 2, bb = u & 3;
+            uint32_t q8[8];
+            const uint32_t code = quantize_row_block(tile, r, bb, q8);
+            const int64_t row = R0 + r, c = C0 + 32 * bb;
+            if (row < rows && c < cols) {
+                v4i *dst = reinterpret_cast<v4i *>(q_row + row * cols + c);
+                dst[0] = v4i{(int)q8[0], (int)q8[1], (int)q8[2], (int)q8[3]};
+                dst[1] = v4i{(int)q8[4], (int)q8[5], (int)q8[6], (int)q8[7]};
+                s_row[row * nb + c / 32] = (uint8_t)code;
+            }
+        }
+        axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
+        __syncthreads();
+        R0 = R2;
+        C0 = C2;
+    }
+}
+
+// workgroups of a tile walk: four per CU (the LDS tile), at most one per tile
+static int64_t walk_grid(int64_t ntiles) {
+    const int64_t cap = (int64_t)device_cu_count() * 4;
+    return ntiles < cap ? ntiles : cap;
+}
+
 hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint8_t *q,
                            uint8_t *scales, hipStream_t stream) {
     if (axis == 1) {
@@ -680,6 +790,11 @@ hipError_t launch_quantize_axis0_batched(const uint16_t *x, int64_t batch, int64
                                          int64_t cols, uint8_t *q, uint8_t *scales,
                                          hipStream_t stream) {
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
+    if (cols % 8 == 0) {
+        hipLaunchKernelGGL(quantize_axis0_walk_kernel, dim3((unsigned)walk_grid(batch * tiles)), dim3(256), 0,
+                           stream, x, q, scales, rows, cols, batch * tiles);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(quantize_axis0_kernel, dim3((unsigned)(batch * tiles)), dim3(256), 0, stream,
                        x, q, scales, rows, cols);
     return hipGetLastError();
@@ -703,6 +818,11 @@ hipError_t launch_quantize_gather(const uint16_t *x, int64_t rows_in, int64_t co
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
                                 uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream) {
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
+    if (cols % 8 == 0) {
+        hipLaunchKernelGGL(quantize_dual_walk_kernel, dim3((unsigned)walk_grid(tiles)), dim3(256), 0, stream, x,
+                           q_row, s_row, q_col, s_col, rows, cols, tiles);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,
                        s_row, q_col, s_col, rows, cols);
     return hipGetLastError();
