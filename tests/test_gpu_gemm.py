@@ -92,11 +92,12 @@ def test_repack_matches_oracle(mx, oracle_mod, batch, N, K):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-def test_gemm_one_hot_blocks_exact(mx, oracle_mod, packed):
+@pytest.mark.parametrize("M,N,K", [(64, 48, 512), (300, 272, 4096)])
+def test_gemm_one_hot_blocks_exact(mx, oracle_mod, packed, M, N, K):
     """Only block b* of each row is non-zero: C = 32 * 2^(sa + sb - 254) exactly.
     Different b* per row / column pins the lane -> (row, K block, scale byte)
-    mapping of the scaled MFMA."""
-    M, N, K = 64, 48, 512
+    mapping of the scaled MFMA; K = 4096 spans four 8-step scale chunks and
+    two row tiles of A and of B."""
     nb = K // 32
     rng = np.random.default_rng(30)
     aq = np.zeros((M, K), np.uint8)
@@ -114,7 +115,7 @@ def test_gemm_one_hot_blocks_exact(mx, oracle_mod, packed):
     bq[:] = 0
     for n in range(N):
         bq[n, bb[n] * 32:(bb[n] + 1) * 32] = 0x38
-    _say("gemm one-hot", packed)
+    _say("gemm one-hot", M, N, K, packed)
     c = _gemm_dev(mx, aq, as_, bq, bs, packed, torch.float32)
     ref, _ = oracle_mod.gemm(aq, as_, bq, bs)
     expect = np.zeros((M, N))
