@@ -257,6 +257,36 @@ def test_chunked_a_scale_copies(M, N, K):
         assert 2 * max(stage, big) + chunks <= 160 * 1024
 
 
+def test_pair_kernel_lds_regions():
+    """The paired launch (a 256x256 tile, then a 256x128 tile, per
+    workgroup): before the first tile's epilogue, the second tile's step-0
+    copies and scale chunk 0 go into the stage and chunk buffer the first
+    tile's last step did not read, and the epilogue stages C only in the
+    other stage; every region stays inside the allocation.  Mirrors
+    gemm_pair_kernel's choice of F = KS % 2 and Lc = ((KS - 1) / 8) % 2."""
+    SB = (256 + 256) * 128 + 256 * 4            # large-tile stage (packed B scales, chunked A)
+    SS = (256 + 128) * 128 + 128 * 4            # small-tile stage
+    CHUNK = 256 * 32
+    total = 2 * SB + 2 * CHUNK
+    assert total <= 160 * 1024 and SS <= SB
+    for KS in range(1, 50):
+        last_stage = (KS - 1) % 2
+        last_chunk = ((KS - 1) // 8) % 2
+        F, Lc = KS % 2, ((KS - 1) // 8) % 2
+        assert F != last_stage and Lc == last_chunk
+        small0 = (F * SB, F * SB + SS)                       # second tile's step 0
+        epi = ((1 - F) * SB, (1 - F) * SB + SB)              # first tile's C staging
+        chunk0 = (2 * SB + (1 - Lc) * CHUNK, 2 * SB + (2 - Lc) * CHUNK)
+        in_use = [(last_stage * SB, last_stage * SB + SB), (2 * SB + Lc * CHUNK, 2 * SB + (Lc + 1) * CHUNK)]
+        for a, b in (small0, chunk0):
+            assert 0 <= a < b <= total
+            for c, d in in_use:                               # nothing the last step reads
+                assert b <= c or a >= d
+            assert b <= epi[0] or a >= epi[1]                 # nor the staging area
+        # C staging of the 256x256 tile fits one stage: 8 waves x 32 rows x (64 x 2 + 16) B
+        assert 8 * 32 * (64 * 2 + 16) <= SB and 8 * 16 * (64 * 4 + 16) <= SB
+
+
 def gk_descriptors(M, N, T, lo, hi, tm, tn, BM=256, BN=256):
     """The grouped-K kernel's descriptors for tile (tm, tn) of a group with
     token range [lo, hi): A [M][T] and B [N][T] canonical, row stride T."""

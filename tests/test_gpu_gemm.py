@@ -175,12 +175,16 @@ def test_gemm_random_ragged(mx, oracle_mod, M, N, K, out):
     assert np.array_equal(cs[0], cs[1])
 
 
-@pytest.mark.parametrize("M,N,K,out", [(500, 32968, 160, "f32"), (512, 32768, 256, "bf16")])
+@pytest.mark.parametrize("M,N,K,out", [(500, 32968, 160, "f32"), (512, 32768, 256, "bf16"),
+                                       (4000, 6100, 512, "bf16"), (4096, 6144, 1024, "f32")])
 def test_gemm_mixed_tiles_full_output(mx, oracle_mod, M, N, K, out):
     """Shapes whose tile count leaves a partial round of 256x256 tiles launch
     256x256 tiles over the leading columns and 256x128 tiles over the rest in
     one grid (the qkv layer's launch form).  Every element is checked, with
-    ragged M and N tails and K either a multiple of 128 or not."""
+    ragged M and N tails and K either a multiple of 128 or not.  With as many
+    small tiles as large ones, packed B and K % 512 == 0 (the last two
+    shapes) a workgroup computes one tile of each kind; its output must equal
+    the one-tile-per-workgroup launch of canonical B bit for bit."""
     rng = np.random.default_rng(M + N + K)
     X = wl.normal_bf16(rng, (M, K))
     W = wl.normal_bf16(rng, (N, K), std=0.02)
