@@ -77,41 +77,6 @@ def settle(step, seconds):
                 return time.perf_counter() - t0
 
 
-def clocks_under_load(step, max_s=3.0):
-    """Shader and memory clocks (MHz) read by rocm-smi while `step()` runs
-    untimed on the GPU (after the timed region); None where rocm-smi is not
-    available or prints no clock."""
-    import re
-    import subprocess
-    import torch
-    try:
-        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
-                                stderr=subprocess.DEVNULL, text=True)
-    except OSError:
-        return None
-    t0 = time.perf_counter()
-    n = 0
-    while proc.poll() is None and time.perf_counter() - t0 < max_s:
-        step()
-        n += 1
-        if n % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    try:
-        out, _ = proc.communicate(timeout=10)
-        card = next(iter(json.loads(out).values()))
-    except Exception:
-        proc.kill()
-        return None
-    res = {"source": "rocm-smi --showclocks during an untimed run of the step"}
-    for key, name in (("sclk", "sclk_mhz"), ("mclk", "mclk_mhz")):
-        for k, v in card.items():
-            m = re.search(r"(\d+)\s*Mhz", str(v))
-            if k.startswith(key) and "speed" in k and m:
-                res[name] = int(m.group(1))
-    return res
-
-
 class KernelTimer:
     """HIP events around each launch, on the current stream."""
 
@@ -229,7 +194,6 @@ def bench_qkv(args, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
-    clocks = clocks_under_load(lambda: step(0, False))
     avg = timer.averages_us()
     med = timer.medians_us()
     ms_per_step = 1e3 * wall / args.steps
@@ -266,7 +230,6 @@ def bench_qkv(args, dev):
                                "repack W, MXFP8 GEMM -> bf16",
                    "M": M, "N": N, "K": K, "rotated_sets": R},
         "kernels": kern,
-        "clocks": clocks,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MXFP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP8_PEAK_TFLOPS, 4),
                      "traffic": measured_gemm_traffic()},
