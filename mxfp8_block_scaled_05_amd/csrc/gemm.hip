@@ -821,18 +821,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
 // the two chunk buffers at ch_off, chunk c in buffer (c + ch_par) & 1.  Step
 // 0's copies and chunk 0 are issued by the caller (into st_off[0] and buffer
 // ch_par); the loop issues everything after them.
-template <int BM, int BN, int WM>
-__device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, true> &t, int KS, uint8_t *smem,
+template <int BM, int BN, int WM, bool SAC = true>
+__device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, SAC> &t, int KS, uint8_t *smem,
                                           const uint32_t *st_off, uint32_t ch_off, int ch_par,
-                                          v4f (*acc)[TileOps<BM, BN, WM, true, true, true>::FN]) {
-    using T = TileOps<BM, BN, WM, true, true, true>;
+                                          v4f (*acc)[TileOps<BM, BN, WM, true, true, SAC>::FN]) {
+    using T = TileOps<BM, BN, WM, true, true, SAC>;
     constexpr int FM = T::FM, FN = T::FN;
     int cur = 0;
     for (int ks = 0; ks < KS; ++ks) {
         wait_copies_and_sync();
         const int c = ks / T::kChunkSteps;
-        if (ks % T::kChunkSteps == 0 && (c + 1) * T::kChunkSteps < KS)
-            t.issue_sa_chunk(c + 1, t.lds0 + ch_off + ((c + 1 + ch_par) & 1) * T::CHUNK);
+        if constexpr (SAC) {
+            if (ks % T::kChunkSteps == 0 && (c + 1) * T::kChunkSteps < KS)
+                t.issue_sa_chunk(c + 1, t.lds0 + ch_off + ((c + 1 + ch_par) & 1) * T::CHUNK);
+        }
         if (ks + 1 < KS) t.issue_at(ks + 1, t.lds0 + st_off[cur ^ 1]);
         const uint8_t *st = smem + st_off[cur];
         int sas[FM], sbs[FN];
@@ -918,6 +920,95 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
         } else {
             store_tile_scalar<TS::FM, TS::FN, OUT_BF16>(p, row0, col0, p.M, acc2, ts.lane);
         }
+    }
+}
+
+// Grouped (MoE) GEMM with 256x256 tiles as a persistent launch: one
+// workgroup per CU walks tiles; each XCD (workgroup id mod 8) takes a
+// contiguous eighth of the tiles that exist, dealt over its workgroups.
+// Between two tiles the next tile's first copies (and scale chunk) go into
+// the stage and chunk buffer the finished tile's last step did not read,
+// before its epilogue, which stages C in the other stage only -- the same
+// hand-over as gemm_pair_kernel.  Packed B, K % 128 == 0; SAC: K % 512 == 0.
+template <bool OUT_BF16, bool SAC>
+__global__ __launch_bounds__(kThreads, 1) void gemm_grouped_persist_kernel(GemmParams p) {
+    using T = TileOps<256, 256, 2, true, true, SAC>;
+    constexpr uint32_t SB = T::STAGE, CH = 2 * T::STAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE + (SAC ? 2 * T::CHUNK : 0)];
+    const int lane = threadIdx.x & 63;
+    const int tiles_m = count_group_tiles<256>(p.offsets, p.G, p.M, lane);
+    const int n = tiles_m * p.tiles_n;
+    // this workgroup's tiles: XCD x = blockIdx % 8 owns [lo_x, hi_x), its
+    // workgroups (blockIdx / 8 = j of nj) take lo_x + j, lo_x + j + nj, ...
+    const int G8 = (int)gridDim.x;
+    const int x = blockIdx.x % 8, j = blockIdx.x / 8, nj = (G8 - x + 7) / 8;
+    const int lo = (int)((int64_t)n * x / 8), hi = (int)((int64_t)n * (x + 1) / 8);
+    int L = lo + j;
+    if (L >= hi) return;
+    const int KS = p.KS;
+
+    auto coords = [&](int Lt, int64_t &m0, int64_t &m_end, int64_t &n0, int64_t &g) -> bool {
+        int tm, tn;
+        grouped_order(Lt, tiles_m, p.tiles_n, tm, tn);
+        int64_t glo, ghi;
+        int tig;
+        const int gg = find_group<256>(p.offsets, p.G, p.M, tm, lane, glo, ghi, tig);
+        if (gg < 0) return false;
+        g = gg;
+        m0 = glo + (int64_t)tig * 256;
+        m_end = ghi;
+        n0 = (int64_t)tn * 256;
+        return true;
+    };
+    int64_t m0, m_end, n0, g;
+    if (!coords(L, m0, m_end, n0, g)) return;
+    T t;
+    t.init(p, m0, m_end, n0, g, smem);
+    if constexpr (SAC) t.issue_sa_chunk(0, t.lds0 + CH);
+    t.issue_at(0, t.lds0);
+    uint32_t st[2] = {0u, SB};
+    int ch_par = 0;
+    while (true) {
+        v4f acc[T::FM][T::FN];
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < T::FN; ++jj) acc[i][jj] = v4f{0.f, 0.f, 0.f, 0.f};
+        pair_loop<256, 256, 2, SAC>(t, KS, smem, st, CH, ch_par, acc);
+        // the last step read st[(KS-1)&1] and chunk buffer
+        // ((KS-1)/8 + ch_par)&1; the other stage and buffer are free
+        const uint32_t st_free = st[KS & 1], st_busy = st[(KS - 1) & 1];
+        const int c_free = 1 - ((((KS - 1) / T::kChunkSteps) + ch_par) & 1);
+        const int64_t row0 = m0 + t.wm * T::WTM, col0 = n0 + t.wn * T::WTN, mend = m_end;
+        const int wm = t.wm;
+        (void)wm;
+        L += nj;
+        int64_t nm0 = 0, nm_end = 0, nn0 = 0, ng = 0;
+        // uniform over the workgroup (the coordinates come from wave-wide
+        // scans), said so the descriptors stay scalar through the loop
+        const bool more = __builtin_amdgcn_readfirstlane((int)(L < hi && coords(L, nm0, nm_end, nn0, ng))) != 0;
+        T t2;
+        if (more) {
+            t2.init(p, nm0, nm_end, nn0, ng, smem);
+            if constexpr (SAC) t2.issue_sa_chunk(0, t2.lds0 + CH + c_free * T::CHUNK);
+            t2.issue_at(0, t2.lds0 + st_free);
+        }
+        __syncthreads();                     // every wave is done with the finished tile's stages
+        {
+            constexpr int ES = OUT_BF16 ? 2 : 4;
+            if (n0 + 256 <= p.N && (p.N * ES) % 16 == 0)
+                store_tile_lds<T::FM, T::FN, OUT_BF16, (int)SB>(p, row0, col0, mend, acc, t.lane, t.w,
+                                                               smem + st_busy);
+            else
+                store_tile_scalar<T::FM, T::FN, OUT_BF16>(p, row0, col0, mend, acc, t.lane);
+        }
+        if (!more) break;
+        __syncthreads();                     // the staging stage is free again
+        t = t2;
+        m0 = nm0; m_end = nm_end; n0 = nn0; g = ng;
+        st[0] = st_free;
+        st[1] = st_busy;
+        ch_par = c_free;
     }
 }
 
@@ -1142,6 +1233,20 @@ hipError_t launch_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uin
     if (M_total >= 256 * G) {
         p.tiles_m = (int)(ceil_div(M_total, 256) + G);
         p.tiles_n = (int)ceil_div(N, 256);
+        // persistent launch (measured on the Qwen3-30B-A3B layer: gate_up
+        // 297 -> 282 us, down 214 -> 192 us against one workgroup per tile)
+        if (K % 128 == 0) {
+            dim3 grid((unsigned)device_cu_count()), block(kThreads);
+            const bool sac = chunked_a_scales(K);
+            if (sac) {
+                if (c_bf16) hipLaunchKernelGGL((gemm_grouped_persist_kernel<true, true>), grid, block, 0, stream, p);
+                else hipLaunchKernelGGL((gemm_grouped_persist_kernel<false, true>), grid, block, 0, stream, p);
+            } else {
+                if (c_bf16) hipLaunchKernelGGL((gemm_grouped_persist_kernel<true, false>), grid, block, 0, stream, p);
+                else hipLaunchKernelGGL((gemm_grouped_persist_kernel<false, false>), grid, block, 0, stream, p);
+            }
+            return hipGetLastError();
+        }
         return launch_tile<256, 256, 2, true>(p, true, c_bf16, p.tiles_m * p.tiles_n, stream);
     }
     p.tiles_m = (int)(ceil_div(M_total, 128) + G);

@@ -287,6 +287,44 @@ def test_pair_kernel_lds_regions():
         assert 8 * 32 * (64 * 2 + 16) <= SB and 8 * 16 * (64 * 4 + 16) <= SB
 
 
+@pytest.mark.parametrize("n", [1, 7, 8, 255, 256, 257, 1000, 3091])
+@pytest.mark.parametrize("grid", [256, 80])
+def test_grouped_persistent_tile_assignment(n, grid):
+    """The persistent grouped launch: XCD x = workgroup % 8 owns tiles
+    [n x / 8, n (x+1) / 8), its workgroups j = workgroup / 8 (nj of them)
+    take lo + j, lo + j + nj, ...  Every tile exactly once."""
+    seen = []
+    for b in range(grid):
+        x, j = b % 8, b // 8
+        nj = (grid - x + 7) // 8
+        lo, hi = n * x // 8, n * (x + 1) // 8
+        seen += list(range(lo + j, hi, nj))
+    assert sorted(seen) == list(range(n))
+
+
+def test_grouped_persistent_lds_handover():
+    """Between two tiles the persistent grouped launch issues the next tile's
+    step 0 into the stage the finished tile's last step did not read and its
+    scale chunk 0 into the chunk buffer that step did not read; C is staged
+    in the other stage.  Mirrors st_free / c_free over tile sequences."""
+    for sac in (False, True):
+        SB = (256 + 256) * 128 + (0 if sac else 256 * 4) + 256 * 4
+        CHUNK = 256 * 32
+        total = 2 * SB + (2 * CHUNK if sac else 0)
+        assert total <= 160 * 1024
+        for KS in range(1, 40):
+            st, ch_par = [0, SB], 0
+            for _ in range(5):                                  # five tiles in a row
+                last_stage = st[(KS - 1) % 2]
+                last_chunk = ((KS - 1) // 8 + ch_par) % 2
+                st_free, c_free = st[KS % 2], 1 - last_chunk
+                assert st_free != last_stage and c_free != last_chunk
+                assert st_free + SB <= 2 * SB and last_stage + SB <= 2 * SB
+                # C staging (8 waves x 32 rows x 144 B) fits the busy stage
+                assert 8 * 32 * (64 * 2 + 16) <= SB and 8 * 16 * (64 * 4 + 16) <= SB
+                st, ch_par = [st_free, last_stage], c_free
+
+
 def gk_descriptors(M, N, T, lo, hi, tm, tn, BM=256, BN=256):
     """The grouped-K kernel's descriptors for tile (tm, tn) of a group with
     token range [lo, hi): A [M][T] and B [N][T] canonical, row stride T."""

@@ -274,7 +274,10 @@ def _moe_case(oracle_mod, G, N, K, tokens, topk, seed, empty=()):
 
 
 @pytest.mark.parametrize("G,N,K,tokens,topk", [(8, 256, 256, 300, 2), (5, 200, 160, 97, 3),
-                                               (16, 512, 768, 1024, 4)])
+                                               (16, 512, 768, 1024, 4),
+                                               # groups of 256+ rows: the persistent launch, more
+                                               # tiles than CUs (K % 512 != 0 and == 0)
+                                               (8, 1024, 768, 8192, 2), (8, 1024, 1024, 8192, 2)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_grouped_gemm_small(mx, oracle_mod, G, N, K, tokens, topk, out):
     aq, as_, bq, bs, off, row_token = _moe_case(oracle_mod, G, N, K, tokens, topk, G + N,
