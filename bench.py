@@ -644,6 +644,10 @@ def bench_sync(args, dev):
     # read) in one pass per weight
     ops = [("quantize_packed_" + name, lambda W=W, q=q, sc=sc, pk=pk: mx.quantize_packed_(W, pk, q, sc))
            for name, W, q, sc, pk in tensors]
+    # the same, up to 32 weights per launch (mxfp8_quantize_packed_many)
+    jobs = [(W, pk, q, sc) for _, W, q, sc, pk in tensors]
+    many = [("quantize_packed_many_%d" % i, lambda c=jobs[i:i + mx.PACKED_JOBS_MAX]: mx.quantize_packed_many_(c))
+            for i in range(0, len(jobs), mx.PACKED_JOBS_MAX)]
     # the same result by quantize + repack, for comparison
     unfused = []
     for name, W, q, sc, pk in tensors:
@@ -672,7 +676,8 @@ def bench_sync(args, dev):
         torch.cuda.synchronize()
         return 1e3 * (time.perf_counter() - t0) / steps, e0.elapsed_time(e1) / steps
 
-    ms, gpu_ms = replayed(ops, args.steps)
+    ms, gpu_ms = replayed(many, args.steps)
+    one_ms, one_gpu_ms = replayed(ops, args.steps)
     unf_ms, unf_gpu_ms = replayed(unfused, max(2, args.steps // 2))
     # post-sync self-check of one synchronized layer (layer 0 qkv): serving
     # GEMM on a 128-row N(0,1) probe against the dequantized grid
@@ -690,11 +695,13 @@ def bench_sync(args, dev):
                  round(gbs, 1), "GB/s", args, ms, "bf16 -> mxfp8-e4m3/e8m0",
                  {"workload": "qwen3-8b weight sync: every linear (36 layers x qkv, o, gate_up, down) quantized "
                               "along K into its canonical grid and the packed GEMM layout in one pass, "
-                              "replayed as one HIP graph",
+                              "32 weights per launch, replayed as one HIP graph",
                   "elements": n_elts},
-                 kernels=kern, kernels_note="per-call HIP-event times from the eager run (they include "
+                 kernels=kern, kernels_note="one launch per weight (mxfp8_quantize_packed): per-call HIP-event times from the eager run (they include "
                                             "host launch gaps when the host falls behind)",
                  summary={"algorithmic_GB": round(alg / 1e9, 2), "graph_gpu_ms": round(gpu_ms, 3),
+                          "launches_per_sync": len(many),
+                          "one_launch_per_weight_graph_ms": round(one_ms, 3),
                           "eager_ms_per_sync": round(eager_ms, 3),
                           "unfused_quantize_then_repack_ms": round(unf_ms, 3),
                           "selfcheck_qkv_rel_err": round(rel0, 5), "selfcheck_ms": round(check_ms, 3),

@@ -163,6 +163,36 @@ mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t ro
                                    uint8_t *q_packed, uint8_t *scales_packed,
                                    hipStream_t stream);
 
+/* One weight of an mxfp8_quantize_packed_many call: the arguments of
+ * mxfp8_quantize_packed for that weight. */
+typedef struct {
+    const void *w_bf16;        /* BF16 [batch][rows][cols]                         */
+    int64_t batch, rows, cols;
+    uint8_t *q, *scales;       /* canonical grid, or both NULL                     */
+    uint8_t *q_packed, *scales_packed;
+} mxfp8_packed_job;
+
+#define MXFP8_PACKED_JOBS_MAX 32
+
+/*
+ * mxfp8_quantize_packed_many -- mxfp8_quantize_packed over a list of weights
+ * in one launch.
+ *
+ * A weight synchronization quantizes every linear of the model ("The
+ * pipeline", weight-synchronization paragraph); one launch per weight pays a
+ * launch ramp and tail per weight, which costs most on the smaller
+ * projections.  jobs: HOST array of `count` entries (1 <= count <=
+ * MXFP8_PACKED_JOBS_MAX), each validated as mxfp8_quantize_packed validates
+ * its arguments; the tiles of all entries together must stay below 2^24
+ * (batch * ceil(rows/256) * ceil(cols/128) summed over the list).  The output
+ * of every entry is exactly what mxfp8_quantize_packed writes for it; entries
+ * must not overlap in memory.  The array is read during the call only (its
+ * contents are passed by value to the kernel, so a captured graph keeps
+ * them).  Bit-exact, deterministic.
+ */
+mxfp8_status mxfp8_quantize_packed_many(const mxfp8_packed_job *jobs, int64_t count,
+                                        hipStream_t stream);
+
 /*
  * mxfp8_quantize_batched -- mxfp8_quantize over `batch` matrices at once.
  *

@@ -22,7 +22,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["lib", "quantize", "quantize_into", "dequantize", "packed_bytes", "PackedWeight",
-           "repack", "repack_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
+           "repack", "repack_", "quantize_packed_many_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
 
@@ -71,6 +71,8 @@ def lib():
         L.mxfp8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
         L.mxfp8_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+        L.mxfp8_quantize_packed_many.argtypes = [ctypes.POINTER(PackedJob), I64, P]
+        L.mxfp8_quantize_packed_many.restype = I32
         for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
                   "mxfp8_grouped_gemm", "mxfp8_quantize_dual", "mxfp8_quantize_packed",
                   "mxfp8_quantize_dual_grouped"):
@@ -81,6 +83,16 @@ def lib():
         L.mxfp8_version.restype = ctypes.c_char_p
         _lib = L
         return L
+
+
+class PackedJob(ctypes.Structure):
+    """One entry of mxfp8_quantize_packed_many's host array (mxfp8_packed_job)."""
+    _fields_ = [("w_bf16", ctypes.c_void_p), ("batch", ctypes.c_int64), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("q", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("q_packed", ctypes.c_void_p), ("scales_packed", ctypes.c_void_p)]
+
+
+PACKED_JOBS_MAX = 32
 
 
 def _check(status: int, what: str):
@@ -374,6 +386,43 @@ def quantize_packed_(w_bf16: torch.Tensor, out: PackedWeight, q: torch.Tensor | 
                                        _ptr(out.q), _ptr(out.s), _stream(w_bf16.device)),
            "mxfp8_quantize_packed")
     return out
+
+
+def quantize_packed_many_(items) -> None:
+    """quantize_packed_ over a list of (w_bf16, PackedWeight, q or None, s or
+    None) in launches of up to PACKED_JOBS_MAX weights (mxfp8_quantize_packed_many),
+    all on the current stream of the first weight's device."""
+    items = list(items)
+    jobs = []
+    for w_bf16, out, q, s in items:
+        _need(w_bf16, torch.bfloat16, "w")
+        _need(out.q, torch.uint8, "q_packed")
+        _need(out.s, torch.uint8, "scales_packed")
+        if w_bf16.numel() != out.batch * out.N * out.K:
+            raise ValueError("weights do not match the packed weight's shape")
+        if out.q.numel() < packed_bytes(out.batch, out.N, out.K, 0) or \
+                out.s.numel() < packed_bytes(out.batch, out.N, out.K, 1):
+            raise ValueError("packed buffers too small")
+        if (q is None) != (s is None):
+            raise ValueError("give both canonical q and scales, or neither")
+        if q is not None:
+            _need(q, torch.uint8, "q")
+            _need(s, torch.uint8, "scales")
+            if q.numel() != w_bf16.numel() or s.numel() != w_bf16.numel() // 32:
+                raise ValueError("canonical q/scales have the wrong size")
+        if w_bf16.device != items[0][0].device:
+            raise ValueError("all weights must be on one device")
+        jobs.append(PackedJob(w_bf16.data_ptr(), out.batch, out.N, out.K,
+                              q.data_ptr() if q is not None else None,
+                              s.data_ptr() if s is not None else None,
+                              out.q.data_ptr(), out.s.data_ptr()))
+    if not jobs:
+        return
+    stream = _stream(items[0][0].device)
+    for i in range(0, len(jobs), PACKED_JOBS_MAX):
+        chunk = jobs[i:i + PACKED_JOBS_MAX]
+        arr = (PackedJob * len(chunk))(*chunk)
+        _check(lib().mxfp8_quantize_packed_many(arr, len(chunk), stream), "mxfp8_quantize_packed_many")
 
 
 def quantize_packed(w_bf16: torch.Tensor, canonical: bool = True):

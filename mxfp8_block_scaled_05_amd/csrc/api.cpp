@@ -231,6 +231,41 @@ mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t ro
                                          q, scales, q_packed, scales_packed, stream));
 }
 
+mxfp8_status mxfp8_quantize_packed_many(const mxfp8_packed_job *jobs, int64_t count,
+                                        hipStream_t stream) {
+    if (!jobs) return MXFP8_ERR_NULL;
+    if (count < 1 || count > MXFP8_PACKED_JOBS_MAX) return MXFP8_ERR_SHAPE;
+    static_assert(MXFP8_PACKED_JOBS_MAX == kPackedJobsMax, "job table size");
+    PackedJobs t = {};
+    int64_t tiles = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        const mxfp8_packed_job &j = jobs[i];
+        if (!j.w_bf16 || !j.q_packed || !j.scales_packed) return MXFP8_ERR_NULL;
+        if ((j.q == nullptr) != (j.scales == nullptr)) return MXFP8_ERR_NULL;
+        if (j.batch <= 0 || j.rows <= 0 || j.cols <= 0 || j.cols % 32) return MXFP8_ERR_SHAPE;
+        if (j.rows >= kMaxDim || j.cols > kMaxK || j.batch > 65535 ||
+            !repack_tiles_ok(j.batch, j.rows, j.cols))
+            return MXFP8_ERR_SHAPE;
+        if (!aligned16(j.w_bf16) || !aligned16(j.q_packed) || !aligned16(j.scales_packed) ||
+            (j.q && (!aligned16(j.q) || !aligned16(j.scales))))
+            return MXFP8_ERR_ALIGN;
+        tiles += j.batch * packed_panels(j.rows) * packed_ksteps(j.cols);
+        if (tiles >= ((int64_t)1 << 24)) return MXFP8_ERR_SHAPE;
+        t.w[i] = static_cast<const uint16_t *>(j.w_bf16);
+        t.qc[i] = j.q;
+        t.sc[i] = j.scales;
+        t.qp[i] = j.q_packed;
+        t.sp[i] = reinterpret_cast<uint32_t *>(j.scales_packed);
+        t.N[i] = j.rows;
+        t.K[i] = j.cols;
+        t.tile_end[i] = tiles;
+    }
+    t.count = (int)count;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_packed_jobs(t, stream));
+}
+
 size_t mxfp8_selfcheck_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K < 32 || K % 32 || M > kMaxSelfcheckRows || N >= kMaxDim || K > kMaxK)
         return 0;

@@ -53,6 +53,23 @@ hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t
                                         const int32_t *src_off, const int32_t *dst_off, int64_t G,
                                         int64_t rows_out, hipStream_t stream);
 
+// A list of weights quantized into the packed layout in one launch.  Weight i
+// is BF16 [batch_i][N[i]][K[i]]; its tiles are tile_end[i-1] .. tile_end[i]-1
+// of the launch (tile_end[i] - tile_end[i-1] = batch_i * panels * k-steps).
+constexpr int kPackedJobsMax = 32;
+struct PackedJobs {
+    const uint16_t *w[kPackedJobsMax];
+    uint8_t *qc[kPackedJobsMax];      // canonical q, or null
+    uint8_t *sc[kPackedJobsMax];      // canonical scales, or null
+    uint8_t *qp[kPackedJobsMax];
+    uint32_t *sp[kPackedJobsMax];
+    int64_t N[kPackedJobsMax];
+    int64_t K[kPackedJobsMax];
+    int64_t tile_end[kPackedJobsMax];
+    int count;
+};
+hipError_t launch_quantize_packed_jobs(const PackedJobs &jobs, hipStream_t stream);
+
 // q / scales may be null (packed output only)
 hipError_t launch_quantize_packed(const uint16_t *w, int64_t batch, int64_t N, int64_t K,
                                   uint8_t *q, uint8_t *scales, uint8_t *q_packed,

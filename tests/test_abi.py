@@ -77,6 +77,22 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_quantize_packed(p, 0, 4, 64, NULL, NULL, p, p, NULL) == 2   # batch
     assert libmx.mxfp8_quantize_packed(q, 1, 4, 64, NULL, NULL, p, p, NULL) == 5   # alignment
     assert libmx.mxfp8_quantize(p, 32, 32, 1, p, q, NULL) == 5                     # scales alignment
+    # multi-weight packed quantize: the host table is validated entry by entry
+    from mxfp8_block_scaled_05_amd import PackedJob
+    good = PackedJob(p.value, 1, 4, 64, None, None, p.value, p.value)
+    arr = (PackedJob * 33)(*([good] * 33))
+    assert libmx.mxfp8_quantize_packed_many(None, 1, NULL) == 1                     # NULL table
+    assert libmx.mxfp8_quantize_packed_many(arr, 0, NULL) == 2                      # empty list
+    assert libmx.mxfp8_quantize_packed_many(arr, 33, NULL) == 2                     # more than 32
+    arr[1] = PackedJob(p.value, 1, 4, 40, None, None, p.value, p.value)
+    assert libmx.mxfp8_quantize_packed_many(arr, 2, NULL) == 2                      # K % 32 in entry 1
+    arr[1] = PackedJob(p.value, 1, 4, 64, p.value, None, p.value, p.value)
+    assert libmx.mxfp8_quantize_packed_many(arr, 2, NULL) == 1                      # q without scales
+    arr[1] = PackedJob(q.value, 1, 4, 64, None, None, p.value, p.value)
+    assert libmx.mxfp8_quantize_packed_many(arr, 2, NULL) == 5                      # alignment
+    arr[1] = PackedJob(p.value, 1, 1 << 20, 1 << 18, None, None, p.value, p.value)   # 2^23 tiles
+    arr[2] = arr[1]
+    assert libmx.mxfp8_quantize_packed_many(arr, 3, NULL) == 2                      # 2^24 tiles in total
     # MoE learner calls
     assert libmx.mxfp8_quantize_batched(p, 0, 64, 64, 0, p, p, NULL) == 2           # batch
     assert libmx.mxfp8_quantize_batched(p, 2, 48, 64, 0, p, p, NULL) == 2           # rows % 32 (axis 0)

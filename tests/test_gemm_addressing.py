@@ -408,3 +408,41 @@ def test_splitk_slices_cover_k_and_stay_inside(M, N, K, packed):
                 else:
                     rows_b = min(128, N - n0)
                     assert n0 * K + k0 + (rows_b - 1) * K + kb <= N * K
+
+
+def xcd_contiguous_tile(wg, nwg):
+    q, r, x = nwg // 8, nwg % 8, wg % 8
+    return x * q + min(x, r) + wg // 8
+
+
+@pytest.mark.parametrize("shapes", [[(1, 256, 128)], [(1, 6144, 4096), (1, 4096, 4096), (1, 24576, 4096),
+                                                       (1, 4096, 12288)],
+                                    [(3, 17, 96), (1, 1, 32), (2, 300, 320)] * 10 + [(1, 513, 4160)]])
+def test_packed_many_job_select(shapes):
+    """CPU mirror of quantize_packed_kernel's job lookup: every workgroup of the
+    launch lands on exactly one tile of exactly one weight, inside that
+    weight's tile range, and every tile of every weight is taken once."""
+    JMAX = 32
+    assert len(shapes) <= JMAX
+    tile_end, tot = [], 0
+    for batch, N, K in shapes:
+        tot += batch * ceil_div(N, 256) * ceil_div(K, 128)
+        tile_end.append(tot)
+    count = len(shapes)
+    tile_end += [0] * (JMAX - count)               # unused table slots are zero
+    seen = [set() for _ in shapes]
+    for wg in range(tot):
+        tidx = xcd_contiguous_tile(wg, tot)
+        assert 0 <= tidx < tot
+        j = 0
+        for i in range(JMAX - 1):
+            if i < count - 1 and tidx >= tile_end[i]:
+                j = i + 1
+        start = tile_end[j - 1] if j else 0
+        local = tidx - start
+        batch, N, K = shapes[j]
+        assert 0 <= local < batch * ceil_div(N, 256) * ceil_div(K, 128)
+        assert local not in seen[j]
+        seen[j].add(local)
+    for (batch, N, K), s in zip(shapes, seen):
+        assert len(s) == batch * ceil_div(N, 256) * ceil_div(K, 128)

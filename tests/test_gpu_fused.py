@@ -103,3 +103,76 @@ def test_quantize_packed_feeds_gemm_like_repack(mx, oracle_mod):
     y2 = mx.gemm(xq, xs, ref, torch.float32)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(y1), to_host(y2))
+
+
+def _packed_out(mx, batch, N, K, canonical, dev):
+    """Output buffers of one weight, filled with 0xEE so an unwritten byte shows."""
+    import torch
+    pw = mx.PackedWeight(torch.full((mx.packed_bytes(batch, N, K, 0),), 0xEE, dtype=torch.uint8, device=dev),
+                         torch.full((mx.packed_bytes(batch, N, K, 1),), 0xEE, dtype=torch.uint8, device=dev),
+                         batch, N, K)
+    q = s = None
+    if canonical:
+        q = torch.full((batch, N, K), 0xEE, dtype=torch.uint8, device=dev)
+        s = torch.full((batch, N, K // 32), 0xEE, dtype=torch.uint8, device=dev)
+    return pw, q, s
+
+
+def test_quantize_packed_many_matches_oracle(mx, oracle_mod):
+    """34 ragged weights (two launches: 32 + 2), canonical grid on every other
+    one: each equals the oracle's quantize + pack."""
+    import torch
+    shapes = [(1, 256, 128), (1, 300, 320), (3, 17, 96), (2, 512, 768), (1, 40, 4160), (1, 513, 96),
+              (1, 1, 32), (2, 257, 160), (1, 1024, 256), (1, 96, 1056), (4, 33, 64), (1, 768, 512),
+              (1, 255, 384), (1, 64, 2048), (2, 130, 224), (1, 2048, 128), (1, 7, 4096), (3, 300, 96)]
+    shapes = shapes + shapes[:16]
+    _say("packed many", len(shapes))
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(77)
+    items, refs = [], []
+    for i, (batch, N, K) in enumerate(shapes):
+        w = wl.normal_bf16(rng, (batch * N, K), std=0.02 * (1 + i))
+        w = _specials(w, rng)
+        pw, q, s = _packed_out(mx, batch, N, K, i % 2 == 0, dev)
+        items.append((to_dev(w.reshape(batch, N, K)), pw, q, s))
+        refs.append(w)
+    mx.quantize_packed_many_(items)
+    torch.cuda.synchronize()
+    for (batch, N, K), w, (_, pw, q, s) in zip(shapes, refs, items):
+        rq, rs = oracle_mod.quantize(w, 1)
+        qp_ref, sp_ref = oracle_mod.pack(rq.reshape(batch, N, K), rs.reshape(batch, N, K // 32), batch, N, K)
+        assert np.array_equal(to_host(pw.q), qp_ref), (batch, N, K)
+        assert np.array_equal(to_host(pw.s), sp_ref), (batch, N, K)
+        if q is not None:
+            assert np.array_equal(to_host(q).reshape(batch * N, K), rq), (batch, N, K)
+            assert np.array_equal(to_host(s).reshape(batch * N, K // 32), rs), (batch, N, K)
+
+
+def test_quantize_packed_many_sync_layer(mx, oracle_mod):
+    """One Qwen3-8B layer's four linears in one launch (its input is above the
+    nontemporal threshold) equal the per-weight calls byte for byte, and the
+    qkv and down weights equal the oracle."""
+    import torch
+    _say("packed many, qwen3-8b layer")
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(78)
+    items, singles, hosts = [], [], {}
+    for name, N, K in wl.sync_layer_shapes():
+        w = wl.normal_bf16(rng, (N, K), std=0.02)
+        wd = to_dev(w)
+        if name in ("qkv", "down"):
+            hosts[name] = w
+        items.append((wd,) + _packed_out(mx, 1, N, K, True, dev))
+        singles.append(mx.quantize_packed(wd, canonical=True))
+    mx.quantize_packed_many_(items)
+    torch.cuda.synchronize()
+    for (name, N, K), (_, pw, q, s), (pw1, q1, s1) in zip(wl.sync_layer_shapes(), items, singles):
+        assert torch.equal(pw.q, pw1.q) and torch.equal(pw.s, pw1.s), name
+        assert torch.equal(q.view(N, K), q1) and torch.equal(s.view(N, K // 32), s1), name
+        if name in hosts:
+            rq, rs = oracle_mod.quantize(hosts[name], 1)
+            assert np.array_equal(to_host(q).reshape(N, K), rq), name
+            assert np.array_equal(to_host(s).reshape(N, K // 32), rs), name
+            qp_ref, sp_ref = oracle_mod.pack(rq.reshape(1, N, K), rs.reshape(1, N, K // 32), 1, N, K)
+            assert np.array_equal(to_host(pw.q), qp_ref), name
+            assert np.array_equal(to_host(pw.s), sp_ref), name
