@@ -214,3 +214,56 @@ def test_graph_replay_splitk_and_regrouped_wgrad(mx, oracle_mod):
             assert ok, worst
             rq, rs = oracle_mod.quantize_grouped_axis0(dyh, lay, dlay, T128)
             assert np.array_equal(to_host(g_buf["aq"]), rq) and np.array_equal(to_host(g_buf["as_"]), rs)
+
+
+def test_graph_replay_packed_many_weight_sync(mx, oracle_mod):
+    """A weight sync recorded once (mxfp8_quantize_packed_many, 34 weights: two
+    launches) and replayed after new weights are written in place: every
+    replay equals the eager call, and the first equals the oracle.  The job
+    table is passed by value, so the recorded launches keep it after the host
+    array is gone."""
+    import torch
+    shapes = [(1, 300, 320), (2, 256, 128), (1, 40, 4160), (3, 17, 96)] * 8 + [(1, 513, 96), (1, 1, 32)]
+    _say("packed many", len(shapes))
+    dev = torch.device("cuda:0")
+    Ws = [torch.zeros((b, N, K), dtype=torch.bfloat16, device=dev) for b, N, K in shapes]
+
+    def buffers():
+        out = []
+        for i, (b, N, K) in enumerate(shapes):
+            pw = mx.PackedWeight(torch.empty(mx.packed_bytes(b, N, K, 0), dtype=torch.uint8, device=dev),
+                                 torch.empty(mx.packed_bytes(b, N, K, 1), dtype=torch.uint8, device=dev), b, N, K)
+            q = s = None
+            if i % 3 != 1:
+                q = torch.empty((b, N, K), dtype=torch.uint8, device=dev)
+                s = torch.empty((b, N, K // 32), dtype=torch.uint8, device=dev)
+            out.append((pw, q, s))
+        return out
+
+    g_buf, e_buf = buffers(), buffers()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mx.quantize_packed_many_([(W,) + o for W, o in zip(Ws, g_buf)])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        rng = np.random.default_rng(400 + rep)
+        hosts = [wl.normal_bf16(rng, (b * N, K), std=0.02 * (rep + 1)) for b, N, K in shapes]
+        for W, w in zip(Ws, hosts):
+            W.copy_(to_dev(w).view(W.shape))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        mx.quantize_packed_many_([(W,) + o for W, o in zip(Ws, e_buf)])
+        torch.cuda.synchronize()
+        for i, ((pg, qg, sg), (pe, qe, se)) in enumerate(zip(g_buf, e_buf)):
+            assert torch.equal(pg.q, pe.q) and torch.equal(pg.s, pe.s), (rep, i)
+            if qg is not None:
+                assert torch.equal(qg, qe) and torch.equal(sg, se), (rep, i)
+        if rep == 0:
+            for (b, N, K), w, (pg, qg, sg) in zip(shapes, hosts, g_buf):
+                rq, rs = oracle_mod.quantize(w, 1)
+                qp_ref, sp_ref = oracle_mod.pack(rq.reshape(b, N, K), rs.reshape(b, N, K // 32), b, N, K)
+                assert np.array_equal(to_host(pg.q), qp_ref) and np.array_equal(to_host(pg.s), sp_ref)
+                if qg is not None:
+                    assert np.array_equal(to_host(qg).reshape(b * N, K), rq)
