@@ -255,32 +255,48 @@ def bench_qkv(args, dev):
     return out
 
 
-def run_timed(ops, args):
+def run_timed(ops, args, live=()):
     """Run `ops` (a list of (name, fn)) as one step: W warmup steps, then K
-    timed steps bracketed by synchronizations; every op is bracketed by HIP
-    events.  Returns (ms per step from the host clock, {name: avg us})."""
+    timed steps bracketed by synchronizations, with HIP events only around
+    the ops named in `live` (an event record costs GPU time between kernels);
+    then a pass of min(K, 50) steps with events around every op.  Returns (ms
+    per step from the host clock over the timed steps, {name: avg us}), the
+    averages of `live` ops from the timed steps, the others from that pass."""
     import torch
     timer = KernelTimer()
 
     def plain():
         for _, fn in ops:
             fn()
+
+    def one(names):
+        for name, fn in ops:
+            if name in names:
+                timer.time(name, fn)
+            else:
+                fn()
     settle(plain, getattr(args, "settle_s", 0.0))
     gc.disable()
     for _ in range(args.warmup):
-        for name, fn in ops:
-            timer.time(name, fn)
+        one(live)
     torch.cuda.synchronize()
     timer.reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        for name, fn in ops:
-            timer.time(name, fn)
+        one(live)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    avg_live = timer.averages_us()
+    timer.reset()
+    every = {name for name, _ in ops}
+    for _ in range(min(args.steps, 50)):
+        one(every)
+    torch.cuda.synchronize()
     gc.enable()
-    return 1e3 * wall / args.steps, timer.averages_us()
+    avg = timer.averages_us()
+    avg.update(avg_live)
+    return 1e3 * wall / args.steps, avg
 
 
 def _line(metric, value, unit, args, ms, dtype, config, **extra):
@@ -376,7 +392,7 @@ def bench_mlp(args, dev):
     for key, (A, B, M, N, K, dt) in gemms.items():
         ops.append(("gemm_" + key, lambda A=A, B=B, dt=dt, o=out[key]: mx.gemm(A[0], A[1], B, dt, out=o)))
     torch.cuda.synchronize()
-    ms, avg = run_timed(ops, args)
+    ms, avg = run_timed(ops, args, live=("gemm_fprop_gu",))
     _, avg_unf = run_timed(unfused, argparse.Namespace(steps=max(2, args.steps // 2), warmup=1))
     # the whole micro-batch (14 launches) captured once and replayed
     graph = torch.cuda.CUDAGraph()
@@ -473,7 +489,7 @@ def bench_moe(args, dev):
     ]
     torch.cuda.synchronize()
     sync_ms, sync_avg = run_timed(sync_ops, argparse.Namespace(steps=max(3, args.steps // 10), warmup=1))
-    ms, avg = run_timed(ops, args)
+    ms, avg = run_timed(ops, args, live=("grouped_gemm_gate_up",))
     flops_gu = 2.0 * real * I2 * H
     flops_d = 2.0 * real * H * I
     eb = 1 + 1 / 32
@@ -597,7 +613,7 @@ def bench_moe_train(args, dev):
                                                         out=dW_gu)),
     ]
     torch.cuda.synchronize()
-    ms, avg = run_timed(ops, args)
+    ms, avg = run_timed(ops, args, live=("wgrad_gate_up",))
     # the weight-gradient GEMMs over the 32-padded token grids, for comparison
     # (operands quantized once, outside the timing)
     p32 = {}
