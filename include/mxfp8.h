@@ -163,6 +163,32 @@ mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t ro
                                    uint8_t *q_packed, uint8_t *scales_packed,
                                    hipStream_t stream);
 
+/* One tensor of an mxfp8_quantize_many call: the arguments of
+ * mxfp8_quantize(x, rows, cols, axis = 1, q, scales) for that tensor. */
+typedef struct {
+    const void *x_bf16;        /* BF16 [rows][cols]                                */
+    int64_t rows, cols;
+    uint8_t *q, *scales;       /* q[rows][cols], scales[rows][cols/32]             */
+} mxfp8_quant_job;
+
+#define MXFP8_QUANT_JOBS_MAX 8
+
+/*
+ * mxfp8_quantize_many -- mxfp8_quantize along axis 1 over a list of tensors
+ * in one launch.
+ *
+ * A linear layer's forward quantizes its weights and its activations along
+ * the reduction axis (format paragraph of "The pipeline"); one launch for
+ * both pays one launch ramp and tail instead of two.  jobs: HOST array of
+ * `count` entries (1 <= count <= MXFP8_QUANT_JOBS_MAX), each validated as
+ * mxfp8_quantize(axis = 1) validates its arguments; the wave-steps of all
+ * entries together (ceil(rows * cols / 2048) each) must stay below 2^40.
+ * The output of every entry is exactly what mxfp8_quantize(axis = 1) writes
+ * for it; entries must not overlap in memory.  The array is read during the
+ * call only (passed by value to the kernel).  Bit-exact, deterministic.
+ */
+mxfp8_status mxfp8_quantize_many(const mxfp8_quant_job *jobs, int64_t count, hipStream_t stream);
+
 /* One weight of an mxfp8_quantize_packed_many call: the arguments of
  * mxfp8_quantize_packed for that weight. */
 typedef struct {

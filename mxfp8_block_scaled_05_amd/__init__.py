@@ -22,7 +22,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["lib", "quantize", "quantize_into", "dequantize", "packed_bytes", "PackedWeight",
-           "repack", "repack_", "quantize_packed_many_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
+           "repack", "repack_", "quantize_many_", "quantize_packed_many_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
 
@@ -71,6 +71,8 @@ def lib():
         L.mxfp8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
         L.mxfp8_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+        L.mxfp8_quantize_many.argtypes = [ctypes.POINTER(QuantJob), I64, P]
+        L.mxfp8_quantize_many.restype = I32
         L.mxfp8_quantize_packed_many.argtypes = [ctypes.POINTER(PackedJob), I64, P]
         L.mxfp8_quantize_packed_many.restype = I32
         for f in ("mxfp8_quantize", "mxfp8_dequantize", "mxfp8_repack", "mxfp8_gemm",
@@ -83,6 +85,15 @@ def lib():
         L.mxfp8_version.restype = ctypes.c_char_p
         _lib = L
         return L
+
+
+class QuantJob(ctypes.Structure):
+    """One entry of mxfp8_quantize_many's host array (mxfp8_quant_job)."""
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+QUANT_JOBS_MAX = 8
 
 
 class PackedJob(ctypes.Structure):
@@ -386,6 +397,34 @@ def quantize_packed_(w_bf16: torch.Tensor, out: PackedWeight, q: torch.Tensor | 
                                        _ptr(out.q), _ptr(out.s), _stream(w_bf16.device)),
            "mxfp8_quantize_packed")
     return out
+
+
+def quantize_many_(items) -> None:
+    """quantize_into(x, 1, q, s) over a list of (x_bf16, q, s) in launches of
+    up to QUANT_JOBS_MAX tensors (mxfp8_quantize_many), on the current stream
+    of the first tensor's device."""
+    items = list(items)
+    jobs = []
+    for x, q, s in items:
+        _need(x, torch.bfloat16, "x")
+        _need(q, torch.uint8, "q")
+        _need(s, torch.uint8, "scales")
+        if x.dim() != 2:
+            raise ValueError("x must be 2-D [rows, cols]")
+        rows, cols = x.shape
+        if tuple(q.shape) != (rows, cols) or tuple(s.shape) != (rows, cols // 32):
+            raise ValueError("q/scales shapes %s/%s, expected %s/%s" % (tuple(q.shape), tuple(s.shape),
+                                                                      (rows, cols), (rows, cols // 32)))
+        if x.device != items[0][0].device:
+            raise ValueError("all tensors must be on one device")
+        jobs.append(QuantJob(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr()))
+    if not jobs:
+        return
+    stream = _stream(items[0][0].device)
+    for i in range(0, len(jobs), QUANT_JOBS_MAX):
+        chunk = jobs[i:i + QUANT_JOBS_MAX]
+        arr = (QuantJob * len(chunk))(*chunk)
+        _check(lib().mxfp8_quantize_many(arr, len(chunk), stream), "mxfp8_quantize_many")
 
 
 def quantize_packed_many_(items) -> None:

@@ -231,6 +231,33 @@ mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t ro
                                          q, scales, q_packed, scales_packed, stream));
 }
 
+mxfp8_status mxfp8_quantize_many(const mxfp8_quant_job *jobs, int64_t count, hipStream_t stream) {
+    if (!jobs) return MXFP8_ERR_NULL;
+    if (count < 1 || count > MXFP8_QUANT_JOBS_MAX) return MXFP8_ERR_SHAPE;
+    static_assert(MXFP8_QUANT_JOBS_MAX == kQuantJobsMax, "job table size");
+    QuantJobs t = {};
+    int64_t steps = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        const mxfp8_quant_job &j = jobs[i];
+        if (!j.x_bf16 || !j.q || !j.scales) return MXFP8_ERR_NULL;
+        if (j.rows <= 0 || j.cols <= 0 || j.rows >= kMaxDim || j.cols >= kMaxDim || j.cols % 32)
+            return MXFP8_ERR_SHAPE;
+        if (!aligned16(j.x_bf16) || !aligned16(j.q) || !aligned16(j.scales)) return MXFP8_ERR_ALIGN;
+        const int64_t nblocks = j.rows * (j.cols / 32);
+        steps += (nblocks + 63) / 64;
+        if (steps >= ((int64_t)1 << 40)) return MXFP8_ERR_SHAPE;
+        t.x[i] = static_cast<const uint16_t *>(j.x_bf16);
+        t.q[i] = j.q;
+        t.s[i] = j.scales;
+        t.nblocks[i] = nblocks;
+        t.step_end[i] = steps;
+    }
+    t.count = (int)count;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_many(t, stream));
+}
+
 mxfp8_status mxfp8_quantize_packed_many(const mxfp8_packed_job *jobs, int64_t count,
                                         hipStream_t stream) {
     if (!jobs) return MXFP8_ERR_NULL;

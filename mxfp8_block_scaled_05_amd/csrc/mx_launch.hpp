@@ -53,6 +53,20 @@ hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t
                                         const int32_t *src_off, const int32_t *dst_off, int64_t G,
                                         int64_t rows_out, hipStream_t stream);
 
+// Several tensors quantized along axis 1 in one launch.  Tensor i has
+// nblocks[i] = rows * cols / 32 blocks and ceil(nblocks[i] / 64) wave-steps,
+// which are steps step_end[i-1] .. step_end[i]-1 of the launch.
+constexpr int kQuantJobsMax = 8;
+struct QuantJobs {
+    const uint16_t *x[kQuantJobsMax];
+    uint8_t *q[kQuantJobsMax];
+    uint8_t *s[kQuantJobsMax];
+    int64_t nblocks[kQuantJobsMax];
+    int64_t step_end[kQuantJobsMax];
+    int count;
+};
+hipError_t launch_quantize_many(const QuantJobs &jobs, hipStream_t stream);
+
 // A list of weights quantized into the packed layout in one launch.  Weight i
 // is BF16 [batch_i][N[i]][K[i]]; its tiles are tile_end[i-1] .. tile_end[i]-1
 // of the launch (tile_end[i] - tile_end[i-1] = batch_i * panels * k-steps).

@@ -150,6 +150,48 @@ __global__ __launch_bounds__(256) void quantize_axis1_kernel(const uint16_t *__r
     }
 }
 
+// Several tensors in one launch: the wave-steps of tensor i are
+// step_end[i-1] .. step_end[i]-1 of one index space that the waves walk as
+// above; each step finds its tensor from the running step totals (uniform over
+// the wave, so the table is read by scalar loads).
+__device__ __forceinline__ int quant_job_of(const QuantJobs &jobs, int64_t step) {
+    int j = 0;
+#pragma unroll
+    for (int i = 0; i < kQuantJobsMax - 1; ++i)
+        if (i < jobs.count - 1 && step >= jobs.step_end[i]) j = i + 1;
+    return j;
+}
+
+__global__ __launch_bounds__(256) void quantize_axis1_many_kernel(QuantJobs jobs) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t nsteps = jobs.step_end[jobs.count - 1];
+    int64_t step = wave;
+    if (step >= nsteps) return;
+    uint32_t cur[4][4], nxt[4][4];
+    int j = quant_job_of(jobs, step);
+    load_step(jobs.x[j], (step - (j ? jobs.step_end[j - 1] : 0)) * 64, jobs.nblocks[j], lane, cur);
+    for (; step < nsteps; step += nwaves) {
+        const bool more = step + nwaves < nsteps;
+        int jn = j;
+        if (more) {
+            jn = quant_job_of(jobs, step + nwaves);
+            load_step(jobs.x[jn], (step + nwaves - (jn ? jobs.step_end[jn - 1] : 0)) * 64, jobs.nblocks[jn],
+                      lane, nxt);
+        }
+        convert_step(jobs.q[j], jobs.s[j], (step - (j ? jobs.step_end[j - 1] : 0)) * 64, jobs.nblocks[j],
+                     lane, cur);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) cur[u][k] = nxt[u][k];
+        }
+        j = jn;
+    }
+}
+
 // ---------------------------------------------------------------- tiles in LDS
 // A 128-column BF16 tile in LDS: row r (256 B) holds its 16-byte chunk c at
 // slot c ^ (r % 16).  Column-pair dword reads (64 lanes over one row) and
@@ -837,6 +879,16 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int ax
     } else {
         return launch_quantize_axis0_batched(x, 1, rows, cols, q, scales, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_many(const QuantJobs &jobs, hipStream_t stream) {
+    const int64_t nsteps = jobs.step_end[jobs.count - 1];
+    int64_t grid = (nsteps + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * (kQuantWavesPerCu / 4);
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(quantize_axis1_many_kernel, dim3((unsigned)grid), dim3(256), 0, stream, jobs);
     return hipGetLastError();
 }
 

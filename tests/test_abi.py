@@ -77,6 +77,21 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_quantize_packed(p, 0, 4, 64, NULL, NULL, p, p, NULL) == 2   # batch
     assert libmx.mxfp8_quantize_packed(q, 1, 4, 64, NULL, NULL, p, p, NULL) == 5   # alignment
     assert libmx.mxfp8_quantize(p, 32, 32, 1, p, q, NULL) == 5                     # scales alignment
+    # multi-tensor axis-1 quantize: the host table is validated entry by entry
+    from mxfp8_block_scaled_05_amd import QuantJob
+    qgood = QuantJob(p.value, 4, 64, p.value, p.value)
+    qarr = (QuantJob * 9)(*([qgood] * 9))
+    assert libmx.mxfp8_quantize_many(None, 1, NULL) == 1                            # NULL table
+    assert libmx.mxfp8_quantize_many(qarr, 0, NULL) == 2                            # empty list
+    assert libmx.mxfp8_quantize_many(qarr, 9, NULL) == 2                            # more than 8
+    qarr[1] = QuantJob(p.value, 4, 40, p.value, p.value)
+    assert libmx.mxfp8_quantize_many(qarr, 2, NULL) == 2                            # cols % 32 in entry 1
+    qarr[1] = QuantJob(p.value, 0, 64, p.value, p.value)
+    assert libmx.mxfp8_quantize_many(qarr, 2, NULL) == 2                            # rows
+    qarr[1] = QuantJob(p.value, 4, 64, None, p.value)
+    assert libmx.mxfp8_quantize_many(qarr, 2, NULL) == 1                            # NULL q
+    qarr[1] = QuantJob(p.value, 4, 64, q.value, p.value)
+    assert libmx.mxfp8_quantize_many(qarr, 2, NULL) == 5                            # alignment
     # multi-weight packed quantize: the host table is validated entry by entry
     from mxfp8_block_scaled_05_amd import PackedJob
     good = PackedJob(p.value, 1, 4, 64, None, None, p.value, p.value)

@@ -446,3 +446,44 @@ def test_packed_many_job_select(shapes):
         seen[j].add(local)
     for (batch, N, K), s in zip(shapes, seen):
         assert len(s) == batch * ceil_div(N, 256) * ceil_div(K, 128)
+
+
+@pytest.mark.parametrize("shapes", [[(4096, 4096), (6144, 4096)], [(1, 32), (3, 96), (5, 4160), (64, 64)],
+                                    [(7, 2048), (1, 32)] * 4])
+def test_quantize_many_step_walk(shapes):
+    """CPU mirror of quantize_axis1_many_kernel's walk: the waves of the launch
+    visit every wave-step once; each step's tensor and local block range come
+    from the running step totals; the blocks a step writes (block < nblocks
+    of its tensor) cover every block of every tensor exactly once."""
+    JMAX = 8
+    assert len(shapes) <= JMAX
+    nblocks = [r * c // 32 for r, c in shapes]
+    step_end, tot = [], 0
+    for nb in nblocks:
+        tot += -(-nb // 64)
+        step_end.append(tot)
+    count = len(shapes)
+    step_end += [0] * (JMAX - count)
+    cus = 256
+    grid = max(1, min(-(-tot // 4), cus * 32 // 4))
+    nwaves = grid * 4
+    covered = [np.zeros(nb, np.int32) for nb in nblocks]
+    visited = np.zeros(tot, np.int32)
+    for wave in range(nwaves):
+        step = wave
+        while step < tot:
+            j = 0
+            for i in range(JMAX - 1):
+                if i < count - 1 and step >= step_end[i]:
+                    j = i + 1
+            local = step - (step_end[j - 1] if j else 0)
+            assert 0 <= local < -(-nblocks[j] // 64)
+            visited[step] += 1
+            for lane in range(64):
+                blk = local * 64 + lane
+                if blk < nblocks[j]:
+                    covered[j][blk] += 1
+            step += nwaves
+    assert np.all(visited == 1)
+    for c in covered:
+        assert np.all(c == 1)

@@ -176,3 +176,45 @@ def test_dequantize_axis0_and_axis1(mx, oracle_mod, rows, cols):
             ref = oracle_mod.dequantize(q, s, rows, cols, axis, dt)
             got = to_host(mx.dequantize(to_dev(q), to_dev(s), rows, cols, axis, tdt))
             assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), (axis, dt)
+
+
+def test_quantize_many_matches_oracle(mx, oracle_mod):
+    """mxfp8_quantize_many over 11 tensors (two launches: 8 + 3), ragged block
+    counts (steps of 64 blocks that end inside a tensor), the special blocks
+    and the exhaustive sweep among them: every output equals the oracle's
+    axis-1 quantize, bit for bit."""
+    rng = np.random.default_rng(91)
+    xs = [wl.normal_bf16(rng, (r, c), outlier_frac=0.02) for r, c in
+          [(1, 32), (3, 96), (33, 64), (96, 4128), (160, 224), (7, 2048), (2, 32)]]
+    xs.insert(2, _special_blocks())
+    xs.insert(5, np.ascontiguousarray(_sweep_matrix()[:50000]))
+    xs += [wl.normal_bf16(rng, (513, 1056)), wl.normal_bf16(rng, (64, 64), std=1e-30)]
+    _say("quantize many", len(xs))
+    items = []
+    for x in xs:
+        r, c = x.shape
+        items.append((to_dev(x), torch.full((r, c), 0xEE, dtype=torch.uint8, device="cuda"),
+                      torch.full((r, c // 32), 0xEE, dtype=torch.uint8, device="cuda")))
+    mx.quantize_many_(items)
+    torch.cuda.synchronize()
+    for i, (x, (_, q, s)) in enumerate(zip(xs, items)):
+        q_ref, s_ref = oracle_mod.quantize(x, 1)
+        assert np.array_equal(to_host(s), s_ref), i
+        assert np.array_equal(to_host(q), q_ref), i
+
+
+def test_quantize_many_qkv_pair(mx, oracle_mod):
+    """The qkv layer's weight and activations in one launch equal the oracle."""
+    d = wl.qkv(0)
+    _say("quantize many qkv")
+    items = []
+    for name in ("W", "X"):
+        r, c = d[name].shape
+        items.append((to_dev(d[name]), torch.empty((r, c), dtype=torch.uint8, device="cuda"),
+                      torch.empty((r, c // 32), dtype=torch.uint8, device="cuda")))
+    mx.quantize_many_(items)
+    torch.cuda.synchronize()
+    for name, (_, q, s) in zip(("W", "X"), items):
+        q_ref, s_ref = oracle_mod.quantize(d[name], 1)
+        assert np.array_equal(to_host(s), s_ref), name
+        assert np.array_equal(to_host(q), q_ref), name
