@@ -315,7 +315,8 @@ def _gemm_rate(us, M, N, K):
 
 def bench_mlp(args, dev):
     """Qwen3-8B MLP learner micro-batch (8192 tokens): per step, quantize the
-    two weights along both axes and repack all four operands, quantize the four
+    two weights along both axes straight into the GEMMs' packed layouts
+    (blocked along K for fprop, along N for dgrad), quantize the four
     activation/gradient tensors along both axes, and run the six GEMMs
     (fprop, dgrad, wgrad for gate_up and down).  fprop/dgrad -> bf16, wgrad ->
     fp32.  The working set (> 2.5 GB) is far larger than the Infinity Cache."""
@@ -363,8 +364,8 @@ def bench_mlp(args, dev):
         unfused.append((key, lambda q=Q[src][0], sc=Q[src][1], w=pk: mx.repack_(q, sc, w)))
     # fused path (the step): activations and gradients quantized along both
     # axes from one read; forward weights quantized straight into the packed
-    # layout; the transposed (data-gradient) weights quantized along N and
-    # repacked
+    # layout; the transposed (data-gradient) weights quantized along N
+    # straight into their packed layout
     ops = []
     q_bytes = {}
     for name in ("X", "h", "dY_gu", "dY_d"):
@@ -375,12 +376,9 @@ def bench_mlp(args, dev):
         key = "quantize_packed_" + name
         ops.append((key, lambda x=t[name], w=P[pk]: mx.quantize_packed_(x, w)))
         q_bytes[key] = t[name].numel() * Q_BYTES_PER_ELT
-        key = "quantize_%s_axis0" % name
-        ops.append((key, lambda x=t[name], q=Q[name, 0]: mx.quantize_into(x, 0, q[0], q[1])))
+        key = "quantize_packed_axis0_%s" % name
+        ops.append((key, lambda x=t[name], w=P[pk + "T"]: mx.quantize_packed_axis0_(x, w)))
         q_bytes[key] = t[name].numel() * Q_BYTES_PER_ELT
-    for key, src in (("repack_guT", ("W_gu", 0)), ("repack_dT", ("W_d", 0))):
-        pk = P[key.split("_", 1)[1]]
-        ops.append((key, lambda q=Q[src][0], sc=Q[src][1], w=pk: mx.repack_(q, sc, w)))
     gemms = {  # name: (A, B, M, N, K, out dtype)
         "fprop_gu": (Q["X", 1], P["gu"], T, I2, H, torch.bfloat16),
         "fprop_d": (Q["h", 1], P["d"], T, H, I, torch.bfloat16),
@@ -414,8 +412,6 @@ def bench_mlp(args, dev):
     kern = {}
     for key, nbytes in q_bytes.items():
         kern[key] = _bw(avg[key], nbytes)
-    for key, src in (("repack_guT", (H, I2)), ("repack_dT", (I, H))):
-        kern[key] = _bw(avg[key], src[0] * src[1] * REPACK_BYTES_PER_ELT)
     for key, (_, _, M, N, K, _) in gemms.items():
         kern["gemm_" + key] = _gemm_rate(avg["gemm_" + key], M, N, K)
     gemm_us = sum(avg["gemm_" + k] for k in gemms)
@@ -426,7 +422,7 @@ def bench_mlp(args, dev):
                  round(flops / (ms * 1e-3) / 1e12, 2), "TFLOP/s", args, ms,
                  "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out (fprop/dgrad), fp32 out (wgrad)",
                  {"workload": "qwen3-8b MLP learner micro-batch, 8192 tokens: activation/gradient quantize "
-                              "(both axes, one read each), weight quantize (packed along K; along N + repack), "
+                              "(both axes, one read each), weight quantize (packed along K; packed along N), "
                               "6 GEMMs",
                   "tokens": T, "hidden": H, "inter": I},
                  kernels=kern,
@@ -528,7 +524,8 @@ def bench_moe_train(args, dev):
     (128 experts, Zipf(1.1) top-8, groups padded to 32): forward, data
     gradients and weight gradients of gate_up and down, all in MXFP8.
       weights (per step): gate_up and down quantized along K into the packed
-        layout, and along N per expert (batched axis 0) + repacked for dgrad;
+        layout, and along N per expert straight into the packed layout of
+        the transposed weights (for dgrad);
       forward: X gathered by routing + quantized in one pass (the fused
         permute), grouped gate_up; h quantized along both axes, grouped down;
       backward: dY quantized along both axes -> dgrad down (grouped GEMM vs
@@ -574,8 +571,6 @@ def bench_moe_train(args, dev):
         return mx.PackedWeight(torch.empty(mx.packed_bytes(G, n, k, 0), **u8),
                                torch.empty(mx.packed_bytes(G, n, k, 1), **u8), G, n, k)
     P_gu, P_d, P_guT, P_dT = packed(I2, H), packed(H, I), packed(H, I2), packed(I, H)
-    wguT = (torch.empty((G, H, I2), **u8), torch.empty((G, H, I2 // 32), **u8))
-    wdT = (torch.empty((G, I, H), **u8), torch.empty((G, I, H // 32), **u8))
     xq = (torch.empty((Mt, H), **u8), torch.empty((Mt, H // 32), **u8))
     h1 = (torch.empty((Mt, I), **u8), torch.empty((Mt, I // 32), **u8))
     h0 = (torch.empty((I, T128), **u8), torch.empty((I, T128 // 32), **u8))
@@ -592,12 +587,8 @@ def bench_moe_train(args, dev):
     ops = [
         ("w_gu_packed", lambda: mx.quantize_packed_(t["W_gu"], P_gu)),
         ("w_d_packed", lambda: mx.quantize_packed_(t["W_d"], P_d)),
-        ("w_gu_axis0", lambda: mx._check(mx.lib().mxfp8_quantize_batched(
-            mx._ptr(t["W_gu"]), G, I2, H, 0, mx._ptr(wguT[0]), mx._ptr(wguT[1]), mx._stream(dev)), "q")),
-        ("w_d_axis0", lambda: mx._check(mx.lib().mxfp8_quantize_batched(
-            mx._ptr(t["W_d"]), G, H, I, 0, mx._ptr(wdT[0]), mx._ptr(wdT[1]), mx._stream(dev)), "q")),
-        ("repack_guT", lambda: mx.repack_(wguT[0], wguT[1], P_guT)),
-        ("repack_dT", lambda: mx.repack_(wdT[0], wdT[1], P_dT)),
+        ("w_gu_packed_axis0", lambda: mx.quantize_packed_axis0_(t["W_gu"], P_guT)),
+        ("w_d_packed_axis0", lambda: mx.quantize_packed_axis0_(t["W_d"], P_dT)),
         ("gather_quantize_X", lambda: mx.quantize_gather_into(t["X"], idx, *xq)),
         ("fprop_gate_up", lambda: mx.grouped_gemm(xq[0], xq[1], P_gu, offs, torch.bfloat16, out=y_gu)),
         ("quantize_dual_h", lambda: mx.quantize_dual_grouped_into(t["A_d"], offs, offs128, *h0, *h1)),

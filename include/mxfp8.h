@@ -220,6 +220,28 @@ mxfp8_status mxfp8_quantize_packed_many(const mxfp8_packed_job *jobs, int64_t co
                                         hipStream_t stream);
 
 /*
+ * mxfp8_quantize_packed_axis0 -- weights BF16 -> MXFP8 blocked along their
+ * rows (axis 0), straight into the GEMM's packed layout of the transposed
+ * grid.
+ *
+ * The data-gradient GEMM of the learner multiplies by the transposed weights,
+ * blocked along the weights' output dimension ("The pipeline", learner
+ * paragraph), and the sampler-side layouts are rebuilt after every update;
+ * this call is mxfp8_quantize_batched(x, axis = 0) followed by mxfp8_repack of
+ * its result (N = cols, K = rows) in one pass:
+ *   x: BF16 [batch][rows][cols], rows % 32 == 0, cols % 8 == 0;
+ *   q_packed / scales_packed: exactly what mxfp8_repack writes for
+ *     q[batch][cols][rows], scales[batch][cols][rows/32] (sizes from
+ *     mxfp8_packed_bytes(batch, cols, rows, which)), padding included.
+ * The limits of mxfp8_repack apply with N = cols, K = rows; batch <= 65535.
+ * HBM bytes per element: 3.03125 (quantize along axis 0 + repack: 5.09375).
+ * Bit-exact, deterministic; writes in place.
+ */
+mxfp8_status mxfp8_quantize_packed_axis0(const void *x_bf16, int64_t batch, int64_t rows,
+                                         int64_t cols, uint8_t *q_packed, uint8_t *scales_packed,
+                                         hipStream_t stream);
+
+/*
  * mxfp8_quantize_batched -- mxfp8_quantize over `batch` matrices at once.
  *
  * The MoE learner's data-gradient GEMM needs every expert's weights blocked

@@ -22,7 +22,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["lib", "quantize", "quantize_into", "dequantize", "packed_bytes", "PackedWeight",
-           "repack", "repack_", "quantize_many_", "quantize_packed_many_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
+           "repack", "repack_", "quantize_packed_axis0_", "quantize_many_", "quantize_packed_many_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
 
@@ -71,6 +71,8 @@ def lib():
         L.mxfp8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
         L.mxfp8_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
+        L.mxfp8_quantize_packed_axis0.argtypes = [P, I64, I64, I64, P, P, P]
+        L.mxfp8_quantize_packed_axis0.restype = I32
         L.mxfp8_quantize_many.argtypes = [ctypes.POINTER(QuantJob), I64, P]
         L.mxfp8_quantize_many.restype = I32
         L.mxfp8_quantize_packed_many.argtypes = [ctypes.POINTER(PackedJob), I64, P]
@@ -396,6 +398,28 @@ def quantize_packed_(w_bf16: torch.Tensor, out: PackedWeight, q: torch.Tensor | 
                                        _ptr(s) if s is not None else None,
                                        _ptr(out.q), _ptr(out.s), _stream(w_bf16.device)),
            "mxfp8_quantize_packed")
+    return out
+
+
+def quantize_packed_axis0_(x_bf16: torch.Tensor, out: PackedWeight) -> PackedWeight:
+    """x [(batch,) rows, cols] quantized along rows (axis 0) straight into the
+    packed layout of its transposed grid: out is PackedWeight(batch, N=cols,
+    K=rows), equal to repack(quantize_batched(x, 0))."""
+    _need(x_bf16, torch.bfloat16, "x")
+    _need(out.q, torch.uint8, "q_packed")
+    _need(out.s, torch.uint8, "scales_packed")
+    if x_bf16.dim() == 2:
+        batch, (rows, cols) = 1, x_bf16.shape
+    elif x_bf16.dim() == 3:
+        batch, rows, cols = x_bf16.shape
+    else:
+        raise ValueError("x must be [rows, cols] or [batch, rows, cols]")
+    if (out.batch, out.N, out.K) != (batch, cols, rows):
+        raise ValueError("packed weight must be (batch, N=cols, K=rows) = %s" % ((batch, cols, rows),))
+    if out.q.numel() < packed_bytes(batch, cols, rows, 0) or out.s.numel() < packed_bytes(batch, cols, rows, 1):
+        raise ValueError("packed buffers too small")
+    _check(lib().mxfp8_quantize_packed_axis0(_ptr(x_bf16), batch, rows, cols, _ptr(out.q), _ptr(out.s),
+                                             _stream(x_bf16.device)), "mxfp8_quantize_packed_axis0")
     return out
 
 

@@ -231,6 +231,19 @@ mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t ro
                                          q, scales, q_packed, scales_packed, stream));
 }
 
+mxfp8_status mxfp8_quantize_packed_axis0(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
+                                         uint8_t *q_packed, uint8_t *scales_packed, hipStream_t stream) {
+    if (!x_bf16 || !q_packed || !scales_packed) return MXFP8_ERR_NULL;
+    if (batch <= 0 || rows <= 0 || cols <= 0 || rows % 32 || cols % 8) return MXFP8_ERR_SHAPE;
+    if (cols >= kMaxDim || rows > kMaxK || batch > 65535 || !repack_tiles_ok(batch, cols, rows))
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q_packed) || !aligned16(scales_packed)) return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_axis0_packed(static_cast<const uint16_t *>(x_bf16), batch, rows, cols,
+                                               q_packed, scales_packed, stream));
+}
+
 mxfp8_status mxfp8_quantize_many(const mxfp8_quant_job *jobs, int64_t count, hipStream_t stream) {
     if (!jobs) return MXFP8_ERR_NULL;
     if (count < 1 || count > MXFP8_QUANT_JOBS_MAX) return MXFP8_ERR_SHAPE;

@@ -53,6 +53,12 @@ hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t
                                         const int32_t *src_off, const int32_t *dst_off, int64_t G,
                                         int64_t rows_out, hipStream_t stream);
 
+// x[batch][rows][cols] along axis 0 into the packed layout of the transposed
+// grid (what repack writes for q[batch][cols][rows]); rows % 32 == 0,
+// cols % 8 == 0
+hipError_t launch_quantize_axis0_packed(const uint16_t *x, int64_t batch, int64_t rows, int64_t cols,
+                                        uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream);
+
 // Several tensors quantized along axis 1 in one launch.  Tensor i has
 // nblocks[i] = rows * cols / 32 blocks and ceil(nblocks[i] / 64) wave-steps,
 // which are steps step_end[i-1] .. step_end[i]-1 of the launch.

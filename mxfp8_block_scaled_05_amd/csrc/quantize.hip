@@ -315,14 +315,11 @@ __global__ __launch_bounds__(256) void quantize_gather_kernel(const uint16_t *__
 constexpr int kA0Tile = 128;
 constexpr int kA0OutPitch = 144;  // bytes per staged output column (16-byte aligned)
 
-// Steps 2 and 3 for one tile already in LDS (`tile`, reused for the output).
-// dstb (optional, in LDS): destination 32-row block in an output of rows_out
-// rows for each of the tile's four source blocks (-1: not written); without
-// it block b goes to block R0/32 + b of an output of `rows` rows.
-__device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, uint8_t *__restrict__ q,
-                                                uint8_t *__restrict__ scales, int64_t rows, int64_t cols,
-                                                int64_t R0, int64_t C0, int t, const int *dstb = nullptr,
-                                                int64_t rows_out = 0) {
+// Step 2: the tile's 128 columns quantized along its rows into the staging
+// area: column c's 128 codes at tile + c * kA0OutPitch (16-byte chunk j holds
+// rows 16j..16j+15), its four scale codes at stile[c * 4 + b] (block b = rows
+// 32b..32b+31).  Ends with a barrier; the staged tile is then ready to store.
+__device__ __forceinline__ void axis0_stage_tile(uint8_t *tile, uint8_t *stile, int t) {
     const int lane = t & 63, w = t >> 6;
     uint32_t d[32];
 #pragma unroll
@@ -363,7 +360,18 @@ __device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, u
     stile[(2 * lane) * 4 + w] = (uint8_t)code_lo;
     stile[(2 * lane + 1) * 4 + w] = (uint8_t)code_hi;
     __syncthreads();
+}
 
+// Steps 2 and 3 for one tile already in LDS (`tile`, reused for the output).
+// dstb (optional, in LDS): destination 32-row block in an output of rows_out
+// rows for each of the tile's four source blocks (-1: not written); without
+// it block b goes to block R0/32 + b of an output of `rows` rows.
+__device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, uint8_t *__restrict__ q,
+                                                uint8_t *__restrict__ scales, int64_t rows, int64_t cols,
+                                                int64_t R0, int64_t C0, int t, const int *dstb = nullptr,
+                                                int64_t rows_out = 0) {
+    axis0_stage_tile(tile, stile, t);
+    const uint8_t *ob = tile;
     if (dstb != nullptr) {
         // regrouped output: each 16-byte chunk lies in one 32-row block
 #pragma unroll
@@ -853,9 +861,97 @@ __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t 
     }
 }
 
-// workgroups of a tile walk: four per CU (the LDS tile), at most one per tile
+// Axis 0 straight into the packed layout of the transposed grid: x[batch]
+// [rows][cols] quantized along rows (as the axis-0 kernel) and written as
+// mxfp8_repack lays out q[batch][cols][rows] (N' = cols, K' = rows).  A
+// 128x128 tile is one k-step (its 128 rows) of one half-panel (its 128
+// columns), so the tile list covers two halves of every panel, and a half
+// beyond cols writes the panel's padding (zero codes, scale code 127), as do
+// the blocks beyond rows.  Walks tiles as quantize_axis0_walk_kernel does.
+__device__ __forceinline__ void packed_t_tile_origin(int64_t idx, int64_t KS, int64_t NP2, int64_t &b,
+                                                     int64_t &R0, int64_t &C0) {
+    const int64_t per = KS * NP2, t = idx % per;
+    b = idx / per;
+    R0 = (t / NP2) * kA0Tile;
+    C0 = (t % NP2) * kA0Tile;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(256) void quantize_axis0_packed_kernel(const uint16_t *__restrict__ x,
+                                                                    uint8_t *__restrict__ qp,
+                                                                    uint32_t *__restrict__ sp, int64_t rows,
+                                                                    int64_t cols, int64_t ntiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    const int t = threadIdx.x;
+    const int64_t KS = (rows + kKStep - 1) / kKStep, NP = (cols + kPanelRows - 1) / kPanelRows;
+    int64_t idx = blockIdx.x;
+    if (idx >= ntiles) return;
+    int64_t b, R0, C0;
+    packed_t_tile_origin(idx, KS, 2 * NP, b, R0, C0);
+    v4i v[kA0Loads];
+    load_tile_regs<NT>(x + b * rows * cols, rows, cols, R0, C0, t, v);
+    for (; idx < ntiles; idx += gridDim.x) {
+        store_tile_regs(tile, t, v);
+        __syncthreads();
+        const int64_t nxt = idx + gridDim.x;
+        int64_t b2 = b, R2 = R0, C2 = C0;
+        if (nxt < ntiles) {
+            packed_t_tile_origin(nxt, KS, 2 * NP, b2, R2, C2);
+            load_tile_regs<NT>(x + b2 * rows * cols, rows, cols, R2, C2, t, v);
+        }
+        axis0_stage_tile(tile, stile, t);
+        // codes: output row o = C0 + col is row o % 256 of panel o / 256 in
+        // k-step R0 / 128; chunk j (input rows R0 + 16j ..) at slot j ^ (o % 8).
+        // Loads beyond rows or cols were zero, so those codes are zero.
+        const int64_t ks = R0 / kKStep, h = (C0 / kA0Tile) & 1;
+        const int64_t tile_lin = (b * NP + C0 / kPanelRows) * KS + ks;
+        uint8_t *qt = qp + tile_lin * kTileBytes + h * (kA0Tile * kKStep);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int col = i * 32 + (t >> 3), j = t & 7;
+            *reinterpret_cast<v4i *>(qt + col * kKStep + ((j ^ (col & 7)) << 4)) =
+                *reinterpret_cast<const v4i *>(tile + col * kA0OutPitch + 16 * j);
+        }
+        // scales: words h*128 .. h*128+127 of the k-step's 1 KB scale tile; word
+        // w holds rows 16(w/16) + 4(w%4) .. +3 (of the panel) of block (w/4) % 4
+        if (t < kA0Tile) {
+            const int jb = (t >> 2) & 3;
+            uint32_t o = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int lc = 16 * (t >> 4) + 4 * (t & 3) + i;
+                const uint32_t code =
+                    (C0 + lc < cols && R0 + 32 * jb < rows) ? (uint32_t)stile[lc * 4 + jb] : 127u;
+                o |= code << (8 * i);
+            }
+            sp[tile_lin * (kScaleStepBytes / 4) + h * kA0Tile + t] = o;
+        }
+        __syncthreads();          // every thread's stores have read the staged tile
+        b = b2;
+        R0 = R2;
+        C0 = C2;
+    }
+}
+
+// Workgroups of a tile walk: as many per CU as can be resident at once, at
+// most one per tile.  The LDS tile would allow four per CU, but the walks'
+// 130-145 registers per lane leave room for three 256-thread workgroups; with
+// four per CU in the grid the fourth waits for a whole walk to end (measured
+// on MI355X, three instead of four: axis 0 on 24576x4096 4.82 -> 5.33 TB/s,
+// 16384x16384 5.24 -> 5.44; both axes level or up to 8% faster).  The count
+// comes from the runtime's occupancy query for each kernel, once.
+template <auto Kernel>
 static int64_t walk_grid(int64_t ntiles) {
-    const int64_t cap = (int64_t)device_cu_count() * 4;
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(Kernel), 256, 0) !=
+                hipSuccess ||
+            n < 1)
+            n = 1;
+        return n;
+    }();
+    const int64_t cap = (int64_t)device_cu_count() * per_cu;
     return ntiles < cap ? ntiles : cap;
 }
 
@@ -897,12 +993,29 @@ hipError_t launch_quantize_axis0_batched(const uint16_t *x, int64_t batch, int64
                                          hipStream_t stream) {
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
     if (cols % 8 == 0) {
-        hipLaunchKernelGGL(quantize_axis0_walk_kernel<true>, dim3((unsigned)walk_grid(batch * tiles)), dim3(256),
+        const int64_t grid = walk_grid<quantize_axis0_walk_kernel<true>>(batch * tiles);
+        hipLaunchKernelGGL(quantize_axis0_walk_kernel<true>, dim3((unsigned)grid), dim3(256),
                            0, stream, x, q, scales, rows, cols, batch * tiles);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(quantize_axis0_kernel, dim3((unsigned)(batch * tiles)), dim3(256), 0, stream,
                        x, q, scales, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_axis0_packed(const uint16_t *x, int64_t batch, int64_t rows, int64_t cols,
+                                        uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream) {
+    const int64_t ntiles = batch * packed_ksteps(rows) * 2 * packed_panels(cols);
+    uint32_t *sp = reinterpret_cast<uint32_t *>(s_packed);
+    if (batch * rows * cols * 2 >= kQuantNontemporalBytes) {
+        const int64_t grid = walk_grid<quantize_axis0_packed_kernel<true>>(ntiles);
+        hipLaunchKernelGGL(quantize_axis0_packed_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                           q_packed, sp, rows, cols, ntiles);
+    } else {
+        const int64_t grid = walk_grid<quantize_axis0_packed_kernel<false>>(ntiles);
+        hipLaunchKernelGGL(quantize_axis0_packed_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                           q_packed, sp, rows, cols, ntiles);
+    }
     return hipGetLastError();
 }
 
@@ -925,12 +1038,15 @@ hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, u
                                 uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream) {
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
     if (cols % 8 == 0) {
-        if (rows * cols * 2 >= kQuantNontemporalBytes)
-            hipLaunchKernelGGL(quantize_dual_walk_kernel<true>, dim3((unsigned)walk_grid(tiles)), dim3(256), 0,
-                               stream, x, q_row, s_row, q_col, s_col, rows, cols, tiles);
-        else
-            hipLaunchKernelGGL(quantize_dual_walk_kernel<false>, dim3((unsigned)walk_grid(tiles)), dim3(256), 0,
-                               stream, x, q_row, s_row, q_col, s_col, rows, cols, tiles);
+        if (rows * cols * 2 >= kQuantNontemporalBytes) {
+            const int64_t grid = walk_grid<quantize_dual_walk_kernel<true>>(tiles);
+            hipLaunchKernelGGL(quantize_dual_walk_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                               q_row, s_row, q_col, s_col, rows, cols, tiles);
+        } else {
+            const int64_t grid = walk_grid<quantize_dual_walk_kernel<false>>(tiles);
+            hipLaunchKernelGGL(quantize_dual_walk_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                               q_row, s_row, q_col, s_col, rows, cols, tiles);
+        }
         return hipGetLastError();
     }
     hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,

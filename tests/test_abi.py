@@ -77,6 +77,11 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_quantize_packed(p, 0, 4, 64, NULL, NULL, p, p, NULL) == 2   # batch
     assert libmx.mxfp8_quantize_packed(q, 1, 4, 64, NULL, NULL, p, p, NULL) == 5   # alignment
     assert libmx.mxfp8_quantize(p, 32, 32, 1, p, q, NULL) == 5                     # scales alignment
+    assert libmx.mxfp8_quantize_packed_axis0(p, 1, 48, 64, p, p, NULL) == 2          # rows % 32
+    assert libmx.mxfp8_quantize_packed_axis0(p, 1, 64, 12, p, p, NULL) == 2          # cols % 8
+    assert libmx.mxfp8_quantize_packed_axis0(p, 0, 64, 64, p, p, NULL) == 2          # batch
+    assert libmx.mxfp8_quantize_packed_axis0(p, 1, 64, 64, None, p, NULL) == 1       # NULL output
+    assert libmx.mxfp8_quantize_packed_axis0(q, 1, 64, 64, p, p, NULL) == 5          # alignment
     # multi-tensor axis-1 quantize: the host table is validated entry by entry
     from mxfp8_block_scaled_05_amd import QuantJob
     qgood = QuantJob(p.value, 4, 64, p.value, p.value)

@@ -487,3 +487,31 @@ def test_quantize_many_step_walk(shapes):
     assert np.all(visited == 1)
     for c in covered:
         assert np.all(c == 1)
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(1, 128, 256), (1, 96, 40), (3, 64, 296), (2, 320, 520),
+                                             (1, 32, 8)])
+def test_quantize_packed_axis0_writes_every_byte_once(batch, rows, cols):
+    """CPU mirror of quantize_axis0_packed_kernel's stores: over the tile list
+    (batch x k-steps x two halves per panel) every 16-byte code chunk and every
+    scale word of the packed buffers is written exactly once, inside them."""
+    KS, NP = ceil_div(rows, 128), ceil_div(cols, 256)
+    q_chunks = np.zeros(batch * NP * KS * 256 * 8, np.int32)     # 16-byte chunks of q_packed
+    s_words = np.zeros(batch * NP * KS * 256, np.int32)          # 4-byte words of scales_packed
+    ntiles = batch * KS * 2 * NP
+    for idx in range(ntiles):
+        per = KS * 2 * NP
+        b, t = idx // per, idx % per
+        R0, C0 = (t // (2 * NP)) * 128, (t % (2 * NP)) * 128
+        ks, h = R0 // 128, (C0 // 128) & 1
+        tile_lin = (b * NP + C0 // 256) * KS + ks
+        base = tile_lin * 256 * 128 + h * 128 * 128
+        for th in range(256):
+            for i in range(4):
+                col, j = i * 32 + (th >> 3), th & 7
+                off = base + col * 128 + ((j ^ (col & 7)) << 4)
+                assert off % 16 == 0
+                q_chunks[off // 16] += 1
+            if th < 128:
+                s_words[tile_lin * 256 + h * 128 + th] += 1
+    assert np.all(q_chunks == 1) and np.all(s_words == 1)

@@ -176,3 +176,43 @@ def test_quantize_packed_many_sync_layer(mx, oracle_mod):
             qp_ref, sp_ref = oracle_mod.pack(rq.reshape(1, N, K), rs.reshape(1, N, K // 32), 1, N, K)
             assert np.array_equal(to_host(pw.q), qp_ref), name
             assert np.array_equal(to_host(pw.s), sp_ref), name
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(1, 128, 256), (1, 96, 40), (3, 64, 296), (2, 320, 520),
+                                             (1, 32, 8), (4, 1536, 2048), (2, 2048, 768)])
+def test_quantize_packed_axis0_matches_quantize_then_pack(mx, oracle_mod, batch, rows, cols):
+    """mxfp8_quantize_packed_axis0 equals the oracle's axis-0 quantize of each
+    matrix packed as the transposed grid (N = cols, K = rows), padding
+    included; half-panels beyond cols and k-steps beyond rows are covered."""
+    import torch
+    _say("packed axis0", batch, rows, cols)
+    rng = np.random.default_rng(batch * 7 + rows * 3 + cols)
+    x = wl.normal_bf16(rng, (batch * rows, cols), std=0.02)
+    if batch * rows * cols <= 1 << 21:
+        x = _specials(x, rng)
+    dev = torch.device("cuda:0")
+    pw = _packed_out(mx, batch, cols, rows, False, dev)[0]
+    mx.quantize_packed_axis0_(to_dev(x.reshape(batch, rows, cols)), pw)
+    torch.cuda.synchronize()
+    q0 = np.empty((batch, cols, rows), np.uint8)
+    s0 = np.empty((batch, cols, rows // 32), np.uint8)
+    for b in range(batch):
+        q0[b], s0[b] = oracle_mod.quantize(np.ascontiguousarray(x[b * rows:(b + 1) * rows]), 0)
+    qp_ref, sp_ref = oracle_mod.pack(q0, s0, batch, cols, rows)
+    assert np.array_equal(to_host(pw.q), qp_ref)
+    assert np.array_equal(to_host(pw.s), sp_ref)
+
+
+def test_quantize_packed_axis0_mlp_weight_full_size(mx):
+    """The MLP gate_up weight [24576 x 4096] (input above the nontemporal
+    threshold): equal to quantize(axis 0) + repack on the device, byte for byte."""
+    import torch
+    _say("packed axis0 mlp W_gu")
+    dev = torch.device("cuda:0")
+    W = wl.torch_normal_bf16((24576, 4096), 0.02, seed=5, device=dev)
+    pw = _packed_out(mx, 1, 4096, 24576, False, dev)[0]
+    mx.quantize_packed_axis0_(W, pw)
+    q0, s0 = mx.quantize(W, 0)
+    ref = mx.repack(q0, s0)
+    torch.cuda.synchronize()
+    assert torch.equal(pw.q, ref.q) and torch.equal(pw.s, ref.s)
