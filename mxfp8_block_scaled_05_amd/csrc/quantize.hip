@@ -814,16 +814,24 @@ __global__ __launch_bounds__(256) void quantize_axis0_walk_kernel(const uint16_t
     }
 }
 
-// both axes over a tile walk (cols % 8 == 0)
-template <bool NT>
+// both axes over a tile walk (cols % 8 == 0).  GROUPED: the axis-0 grid is
+// regrouped as quantize_dual_grouped_kernel does (each tile's destination
+// blocks found at the top of its iteration; q_row may be null).  Looking the
+// next tile's up beside its loads instead (double-buffered) measured no
+// faster on the MoE learner's tensors.
+template <bool NT, bool GROUPED = false>
 __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t *__restrict__ x,
                                                                  uint8_t *__restrict__ q_row,
                                                                  uint8_t *__restrict__ s_row,
                                                                  uint8_t *__restrict__ q_col,
                                                                  uint8_t *__restrict__ s_col, int64_t rows,
-                                                                 int64_t cols, int64_t ntiles) {
+                                                                 int64_t cols, int64_t ntiles,
+                                                                 const int32_t *__restrict__ src_off = nullptr,
+                                                                 const int32_t *__restrict__ dst_off = nullptr,
+                                                                 int G = 0, int64_t rows_out = 0) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
     __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    __shared__ int dstb[4];
     const int t = threadIdx.x;
     int64_t idx = blockIdx.x;
     if (idx >= ntiles) return;
@@ -833,6 +841,14 @@ __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t 
     load_tile_regs<NT>(x, rows, cols, R0, C0, t, v);
     const int64_t nb = cols / 32;
     for (; idx < ntiles; idx += gridDim.x) {
+        if constexpr (GROUPED) {
+            // wave w finds the destination of the tile's source block w (read
+            // after the barriers below; the previous tile's readers ended at
+            // the barrier closing the last iteration)
+            const int w = t >> 6;
+            const int d = dst_block_of(src_off, dst_off, G, rows, rows_out, R0 + 32 * w, t & 63);
+            if ((t & 63) == 0) dstb[w] = d;
+        }
         store_tile_regs(tile, t, v);
         __syncthreads();
         const int64_t nxt = idx + gridDim.x;
@@ -841,20 +857,25 @@ __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t 
             tile_origin_of(nxt, rows, cols, b_unused, R2, C2);
             load_tile_regs<NT>(x, rows, cols, R2, C2, t, v);
         }
+        if (!GROUPED || q_row != nullptr) {
 #pragma unroll
-        for (int u2 = 0; u2 < 2; ++u2) {
-            const int u = u2 * 256 + t, r = u >> 2, bb = u & 3;
-            uint32_t q8[8];
-            const uint32_t code = quantize_row_block(tile, r, bb, q8);
-            const int64_t row = R0 + r, c = C0 + 32 * bb;
-            if (row < rows && c < cols) {
-                v4i *dst = reinterpret_cast<v4i *>(q_row + row * cols + c);
-                dst[0] = v4i{(int)q8[0], (int)q8[1], (int)q8[2], (int)q8[3]};
-                dst[1] = v4i{(int)q8[4], (int)q8[5], (int)q8[6], (int)q8[7]};
-                s_row[row * nb + c / 32] = (uint8_t)code;
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int u = u2 * 256 + t, r = u >> 2, bb = u & 3;
+                uint32_t q8[8];
+                const uint32_t code = quantize_row_block(tile, r, bb, q8);
+                const int64_t row = R0 + r, c = C0 + 32 * bb;
+                if (row < rows && c < cols) {
+                    v4i *dst = reinterpret_cast<v4i *>(q_row + row * cols + c);
+                    dst[0] = v4i{(int)q8[0], (int)q8[1], (int)q8[2], (int)q8[3]};
+                    dst[1] = v4i{(int)q8[4], (int)q8[5], (int)q8[6], (int)q8[7]};
+                    s_row[row * nb + c / 32] = (uint8_t)code;
+                }
             }
         }
-        axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
+        if constexpr (GROUPED)
+            axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t, dstb, rows_out);
+        else
+            axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
         __syncthreads();
         R0 = R2;
         C0 = C2;
@@ -1063,6 +1084,12 @@ hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
+    if (cols % 8 == 0) {
+        const int64_t grid = walk_grid<quantize_dual_walk_kernel<false, true>>(tiles);
+        hipLaunchKernelGGL((quantize_dual_walk_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0, stream, x,
+                           q_row, s_row, q_col, s_col, rows, cols, tiles, src_off, dst_off, (int)G, rows_out);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(quantize_dual_grouped_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,
                        s_row, q_col, s_col, rows, cols, src_off, dst_off, (int)G, rows_out);
     return hipGetLastError();
