@@ -267,3 +267,58 @@ def test_graph_replay_packed_many_weight_sync(mx, oracle_mod):
                 assert np.array_equal(to_host(pg.q), qp_ref) and np.array_equal(to_host(pg.s), sp_ref)
                 if qg is not None:
                     assert np.array_equal(to_host(qg).reshape(b * N, K), rq)
+
+
+def test_graph_replay_quantize_many_and_packed_axis0(mx, oracle_mod):
+    """The list quantizer (weight and activations along K in one launch) and
+    the transposed-weight packed quantizer, recorded once and replayed after
+    in-place input updates: every replay equals the eager calls; the first
+    also equals the oracle."""
+    import torch
+    _say("quantize many + packed axis0")
+    dev = torch.device("cuda:0")
+    N, K, M = 320, 288, 96
+    W = torch.zeros((N, K), dtype=torch.bfloat16, device=dev)
+    X = torch.zeros((M, K), dtype=torch.bfloat16, device=dev)
+
+    def buffers():
+        return dict(wq=torch.empty((N, K), dtype=torch.uint8, device=dev),
+                    ws=torch.empty((N, K // 32), dtype=torch.uint8, device=dev),
+                    xq=torch.empty((M, K), dtype=torch.uint8, device=dev),
+                    xs=torch.empty((M, K // 32), dtype=torch.uint8, device=dev),
+                    wt=mx.PackedWeight(torch.empty(mx.packed_bytes(1, K, N, 0), dtype=torch.uint8, device=dev),
+                                       torch.empty(mx.packed_bytes(1, K, N, 1), dtype=torch.uint8, device=dev),
+                                       1, K, N))
+
+    def step(b):
+        mx.quantize_many_([(W, b["wq"], b["ws"]), (X, b["xq"], b["xs"])])
+        mx.quantize_packed_axis0_(W, b["wt"])
+
+    g_buf, e_buf = buffers(), buffers()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_buf)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        rng = np.random.default_rng(500 + rep)
+        w = wl.normal_bf16(rng, (N, K), std=0.02)
+        x = wl.normal_bf16(rng, (M, K), outlier_frac=0.01)
+        W.copy_(to_dev(w))
+        X.copy_(to_dev(x))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_buf)
+        torch.cuda.synchronize()
+        for key in ("wq", "ws", "xq", "xs"):
+            assert torch.equal(g_buf[key], e_buf[key]), (rep, key)
+        assert torch.equal(g_buf["wt"].q, e_buf["wt"].q) and torch.equal(g_buf["wt"].s, e_buf["wt"].s), rep
+        if rep == 0:
+            rq, rs = oracle_mod.quantize(w, 1)
+            assert np.array_equal(to_host(g_buf["wq"]), rq) and np.array_equal(to_host(g_buf["ws"]), rs)
+            rq, rs = oracle_mod.quantize(x, 1)
+            assert np.array_equal(to_host(g_buf["xq"]), rq) and np.array_equal(to_host(g_buf["xs"]), rs)
+            q0, s0 = oracle_mod.quantize(w, 0)
+            qp, sp = oracle_mod.pack(q0.reshape(1, K, N), s0.reshape(1, K, N // 32), 1, K, N)
+            assert np.array_equal(to_host(g_buf["wt"].q), qp) and np.array_equal(to_host(g_buf["wt"].s), sp)
