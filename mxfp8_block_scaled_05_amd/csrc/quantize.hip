@@ -1085,6 +1085,16 @@ hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t
     if (e != hipSuccess) return e;
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
     if (cols % 8 == 0) {
+        // nontemporal loads from inputs of the Infinity Cache's size, as the
+        // plain dual walk (measured: the MoE learner's dY 65536x2048 162 -> 144
+        // us, X 122 -> 117 us)
+        if (rows * cols * 2 >= kQuantNontemporalBytes) {
+            const int64_t grid = walk_grid<quantize_dual_walk_kernel<true, true>>(tiles);
+            hipLaunchKernelGGL((quantize_dual_walk_kernel<true, true>), dim3((unsigned)grid), dim3(256), 0, stream,
+                               x, q_row, s_row, q_col, s_col, rows, cols, tiles, src_off, dst_off, (int)G,
+                               rows_out);
+            return hipGetLastError();
+        }
         const int64_t grid = walk_grid<quantize_dual_walk_kernel<false, true>>(tiles);
         hipLaunchKernelGGL((quantize_dual_walk_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0, stream, x,
                            q_row, s_row, q_col, s_col, rows, cols, tiles, src_off, dst_off, (int)G, rows_out);

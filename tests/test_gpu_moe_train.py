@@ -140,7 +140,9 @@ def _pad128(offsets):
     return np.concatenate([[0], np.cumsum(-(-sizes // 128) * 128)]).astype(np.int32)
 
 
-@pytest.mark.parametrize("tokens,experts,topk,cols", [(64, 8, 2, 64), (512, 16, 4, 256), (8192, 128, 8, 768)])
+# (8192, 128, 8, 2048): the MoE learner's dY, an input above the nontemporal-load threshold
+@pytest.mark.parametrize("tokens,experts,topk,cols", [(64, 8, 2, 64), (512, 16, 4, 256), (8192, 128, 8, 768),
+                                                      (8192, 128, 8, 2048)])
 @pytest.mark.parametrize("row_grid", [True, False])
 def test_quantize_dual_grouped_matches_oracle(mx, oracle_mod, tokens, experts, topk, cols, row_grid):
     """mxfp8_quantize_dual_grouped: the row grid equals quantize(x, 1) and the
