@@ -1,12 +1,13 @@
 /*
  * mxfp8.h -- C ABI of the MI355X (gfx950) MXFP8 library.
  *
- * MXFP8 as the page "End-to-End MXFP8 RL on Blackwell: What Matching Buys,
- * When It Pays Off, and How It Fails" (verl blog) uses it, section "The
- * pipeline", paragraph "The format": E4M3 elements in blocks of 32 along the
- * reduction dimension, each block sharing one power-of-two E8M0 scale
- * (8.25 bits per element), following the OCP Microscaling (MX) v1.0
- * specification the paragraph cites.
+ * The number format is the one described on the page "End-to-End MXFP8 RL on
+ * Blackwell: What Matching Buys, When It Pays Off, and How It Fails" (verl
+ * blog), section "The pipeline", paragraph "The format", which follows the
+ * OCP Microscaling (MX) v1.0 specification: every run of 32 consecutive
+ * values along the axis a GEMM sums over is stored as 32 one-byte E4M3
+ * codes plus a single one-byte E8M0 power-of-two multiplier, so a tensor
+ * costs 8 + 8/32 bits per value.
  *
  * Conventions shared by every call
  *  - All matrices are row-major.  BF16 inputs are raw 16-bit patterns.
@@ -261,8 +262,8 @@ mxfp8_status mxfp8_quantize_batched(const void *x_bf16, int64_t batch, int64_t r
  * quantize in one pass.
  *
  * The MoE GEMMs read token rows sorted by expert with each group padded to a
- * multiple of 32 (the pages pad to 32 for the token-blocked operands; the
- * expert GEMMs read "shuffled" expert inputs).  Output row i is input row
+ * multiple of 32 (the pages pad to 32 for the token-blocked operands, and the
+ * expert GEMMs consume their inputs reordered by expert).  Output row i is input row
  * d_row_index[i], quantized along its columns; an index outside
  * [0, rows_in) (the padding rows of a group) gives a zero row (scale code 0,
  * elements 0), so the index table can never make it read out of bounds.
@@ -301,12 +302,12 @@ size_t mxfp8_packed_bytes(int64_t batch, int64_t rows, int64_t cols, int which);
 /*
  * mxfp8_repack -- canonical MXFP8 weights -> the GEMM's kernel layout.
  *
- * The page (section "The pipeline", sampler paragraph) notes that serving
- * kernels rewrite weights and scales into kernel-specific layouts (swizzled
- * scales, shuffled/interleaved experts, repacked weights), and that those
- * derived layouts must be rebuilt from the synchronized canonical tensors
- * after every weight update and written back into the storage the captured
- * graphs use.  This call is that rebuild: run it after every update; it
+ * Per the page (section "The pipeline", sampler paragraph), the serving
+ * kernels do not read the canonical grid itself but their own rearranged
+ * copies of it (reordered scale bytes, expert weights in a kernel order),
+ * and those copies go stale whenever the weights change: they have to be
+ * regenerated from the freshly synchronized canonical tensors each time and
+ * stored into the same buffers the recorded graphs point at.  This call is that rebuild: run it after every update; it
  * writes in place into the caller's packed buffers, so pointers captured by a
  * HIP graph stay valid.
  *
@@ -391,7 +392,7 @@ size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   for g in 0..G-1:  C[o_g : o_{g+1}] = A[o_g : o_{g+1}] * B_g^T
  *
  * The page's MoE serving path runs its expert GEMMs in MXFP8 from weights
- * stored "shuffled and interleaved" (section "The pipeline", sampler
+ * stored in a kernel-specific order (section "The pipeline", sampler
  * paragraph; section "Speed: when it pays off": expert GEMMs dominate MoE
  * decode and FP8 halves their weight traffic).
  *

@@ -449,7 +449,8 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const ui
     if (G < 1 || G > 65535 || M_total < 0 || M_total % 32 || M_total >= kMaxDim) return MXFP8_ERR_SHAPE;
     if (N <= 0 || N >= kMaxDim || K < 32 || K % 32 || K > kMaxK) return MXFP8_ERR_SHAPE;
     if ((ceil_div(M_total, 128) + G) * ceil_div(N, 256) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
-    if (!aligned16(a_q) || !aligned16(b_q_packed) || !aligned16(b_s_packed) || !aligned16(c))
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q_packed) || !aligned16(b_s_packed) ||
+        !aligned16(c))
         return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;

@@ -3,8 +3,8 @@
 // The page's sampler rebuilds its kernel-specific weight and scale layouts
 // from the canonical tensors after every weight synchronization ("End-to-End
 // MXFP8 RL on Blackwell" (verl blog), section "The pipeline", sampler
-// paragraph: swizzled scales, shuffled experts, repacked weights); this is
-// that rebuild for the gfx950 GEMM.  Pure byte permutation, HBM-bound at
+// paragraph: the serving kernels read rearranged copies of weights and
+// scales, regenerated at every update); this is that rebuild for the gfx950 GEMM.  Pure byte permutation, HBM-bound at
 // 2.0625 algorithmic bytes per element.  The layout is specified in
 // include/mxfp8.h (mxfp8_repack):
 //   elements: [batch][panel of 256 rows][k-step of 128][256 rows][128 B], the

@@ -10,8 +10,8 @@
  * What it follows:
  *  - "End-to-End MXFP8 RL on Blackwell: What Matching Buys, When It Pays Off,
  *    and How It Fails" (verl blog), section "The pipeline", paragraph "The
- *    format": E4M3 elements in blocks of 32 along the reduction dimension,
- *    each block sharing one power-of-two (E8M0) scale, 8.25 bits per element.
+ *    format": along the summed axis, every 32 consecutive values become 32
+ *    E4M3 codes and one E8M0 power-of-two scale byte (8 + 8/32 bits each).
  *  - same page, section "The pipeline", paragraph on the learner: the
  *    weight-gradient GEMM reduces over tokens, so some operands are blocked
  *    in 32s along the token dimension (axis 0 here).

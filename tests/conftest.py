@@ -49,3 +49,27 @@ def to_host(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def sample_rows(n_rows, tile, count, seed, groups=None):
+    """Sorted, distinct row indices of an [n_rows x N] output for sampled
+    parity: one random row from every `tile`-row tile (or, with `groups` =
+    offsets of row groups, one from every non-empty group), the first and last
+    row, then random rows until `count` are drawn (all rows if count >=
+    n_rows)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    if count >= n_rows:
+        return np.arange(n_rows, dtype=np.int64)
+    pick = {0, n_rows - 1}
+    if groups is not None:
+        off = np.asarray(groups, np.int64)
+        for lo, hi in zip(off[:-1], off[1:]):
+            if hi > lo:
+                pick.add(int(rng.integers(lo, hi)))
+    else:
+        for t0 in range(0, n_rows, tile):
+            pick.add(int(rng.integers(t0, min(n_rows, t0 + tile))))
+    while len(pick) < count:
+        pick.add(int(rng.integers(0, n_rows)))
+    return np.array(sorted(pick), dtype=np.int64)

@@ -65,6 +65,15 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_gemm(p, p, p, p, 0, 4, 4, 64, p, 9, NULL) == 4  # dtype
     assert libmx.mxfp8_grouped_gemm(p, p, p, p, p, 0, 64, 4, 64, p, 0, NULL) == 2   # G
     assert libmx.mxfp8_grouped_gemm(p, p, p, p, p, 2, 48, 4, 64, p, 0, NULL) == 2   # M_total % 32
+    for i in range(5):                                                             # each pointer's alignment
+        args = [p, p, p, p, p]
+        args[i] = q
+        assert libmx.mxfp8_grouped_gemm(args[0], args[1], args[2], args[3], p, 2, 64, 4, 64, args[4], 0,
+                                        NULL) == 5, i
+    for i in range(5):
+        args = [p, p, p, p, p]
+        args[i] = q
+        assert libmx.mxfp8_gemm(args[0], args[1], args[2], args[3], 1, 4, 4, 64, args[4], 0, NULL) == 5, i
     assert libmx.mxfp8_dequantize(p, p, 4, 32, 1, p, 5, NULL) == 4
     assert libmx.mxfp8_repack(p, p, 1, 4, 40, p, p, NULL) == 2
     # fused quantizers

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads as wl
-from conftest import to_dev, to_host
+from conftest import sample_rows, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,14 @@ def _hw_term(oracle_mod, aq, as_, bq, bs):
             np.maximum(step, np.outer(A[:, k], B[:, k]), out=step)
         H += step
     return H
+
+
+# Cap on the ratio of |C - C_ref| to the pure allowance 1e-4 * sum|ab| (+ bf16
+# rounding) for the scaled-MFMA path on the adversarial inputs below.  Measured
+# on MI355X: 1.013 on the 1000 x 96 x 160 fp32 case (1% x20 outliers, 5
+# k-steps), 0.32-0.94 on the other ragged cases, 0.09-0.11 on the learner
+# orientations; every configured workload stays below 1.
+PURE_RATIO_MAX = 1.25
 
 
 def _bound_with_hw(c, ref, sabs, H, out):
@@ -169,7 +177,10 @@ def test_gemm_random_ragged(mx, oracle_mod, M, N, K, out):
         _say("gemm random", M, N, K, out, packed)
         c = _gemm_dev(mx, xq, xs, wq, ws, packed, tdt)
         ok, worst = _bound_with_hw(c, ref, sabs, H, out)
+        _, pure = oracle_mod.gemm_bound_ok(c, ref, sabs, out)
+        _say("  worst error / (pure bound + hardware term) %.3f, error / pure bound %.3f" % (worst, pure))
         assert ok, (packed, worst)
+        assert pure <= PURE_RATIO_MAX, (packed, pure)
         cs.append(c)
     # packed and canonical B run the same arithmetic in the same order
     assert np.array_equal(cs[0], cs[1])
@@ -220,22 +231,27 @@ def test_gemm_dgrad_wgrad_orientations(mx, oracle_mod):
         ref, sabs = oracle_mod.gemm(aq, as_, bq, bs)
         c = _gemm_dev(mx, aq, as_, bq, bs, False, torch.float32)
         ok, worst = _bound_with_hw(c, ref, sabs, _hw_term(oracle_mod, aq, as_, bq, bs), "f32")
+        _, pure = oracle_mod.gemm_bound_ok(c, ref, sabs, "f32")
+        _say("  worst error / (pure bound + hardware term) %.3f, error / pure bound %.3f" % (worst, pure))
         assert ok, (name, worst)
+        assert pure <= PURE_RATIO_MAX, (name, pure)
 
 
-def test_gemm_qkv_full_size_sampled(mx, oracle_mod):
+def test_gemm_qkv_full_output(mx, oracle_mod):
+    """The Qwen3-8B qkv layer (4096 x 6144 x 4096, bf16 out) in the launch the
+    bench times: every one of the 25.2M outputs against the oracle."""
     d = wl.qkv(0)
     xq, xs = _quant_pair(oracle_mod, d["X"])
     wq, ws = _quant_pair(oracle_mod, d["W"])
-    rows = np.sort(np.random.default_rng(32).choice(xq.shape[0], 48, replace=False))
-    rows[0], rows[-1] = 0, xq.shape[0] - 1
-    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws, rows=rows)
-    _say("gemm qkv full size")
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+    _say("gemm qkv full output")
     c = _gemm_dev(mx, xq, xs, wq, ws, True, torch.bfloat16)
-    ok, worst = oracle_mod.gemm_bound_ok(c[rows], ref, sabs, "bf16")
+    ok, worst = oracle_mod.gemm_bound_ok(c, ref, sabs, "bf16")
+    _say("qkv worst error / allowance", worst)
     assert ok, worst
     # the page's healthy-kernel error band for a dense layer: relative error
     # of the MXFP8 layer against the high-precision GEMM on the BF16 inputs
+    rows = sample_rows(xq.shape[0], 256, 256, 32)
     from workloads import bf16_bits_to_f32
     xf = bf16_bits_to_f32(d["X"][rows]).astype(np.float64)
     wf = bf16_bits_to_f32(d["W"]).astype(np.float64)
@@ -251,7 +267,7 @@ def test_gemm_deterministic(mx, oracle_mod):
     a_q, a_s = to_dev(xq), to_dev(xs)
     w = mx.repack(to_dev(wq), to_dev(ws))
     c0 = mx.gemm(a_q, a_s, w, torch.float32)
-    for _ in range(5):
+    for _ in range(10):
         assert torch.equal(mx.gemm(a_q, a_s, w, torch.float32), c0)
 
 
@@ -319,22 +335,32 @@ def test_grouped_gemm_untouched_rows_outside_groups(mx, oracle_mod):
     assert np.all(ch[~inside] == -3.0)
 
 
-def test_grouped_gemm_moe_full_size_sampled(mx, oracle_mod):
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_grouped_gemm_moe_full_size_sampled(mx, oracle_mod, proj):
+    """The Qwen3-30B-A3B expert GEMMs at full size (8192 tokens, top-8
+    Zipf(1.1) routing, 128 experts, groups padded to 32): gate_up
+    [67616 x 1536 x 2048] and down [67616 x 2048 x 768] in the launch the
+    bench times, checked on 512 rows that include one row of every
+    non-empty expert."""
     d = wl.moe(0)
-    aq, as_ = oracle_mod.quantize(d["A_gu"], 1)
-    G, N, K = d["W_gu"].shape
+    A = d["A_gu"] if proj == "gate_up" else d["A_d"]
+    Wt = d["W_gu"] if proj == "gate_up" else d["W_d"]
+    aq, as_ = oracle_mod.quantize(A, 1)
+    G, N, K = Wt.shape
     bq = np.empty((G, N, K), np.uint8)
     bs = np.empty((G, N, K // 32), np.uint8)
     for g in range(G):
-        bq[g], bs[g] = oracle_mod.quantize(d["W_gu"][g], 1)
-    rng = np.random.default_rng(35)
-    rows = np.sort(rng.choice(aq.shape[0], 96, replace=False))
+        bq[g], bs[g] = oracle_mod.quantize(Wt[g], 1)
+    rows = sample_rows(aq.shape[0], 256, 512, 35, groups=d["offsets"])
     ref, sabs, grp = oracle_mod.grouped_gemm(aq, as_, bq, bs, d["offsets"], rows=rows)
+    assert np.all(grp >= 0)
+    assert np.unique(grp).size == int(np.count_nonzero(np.diff(d["offsets"])))
     w = mx.repack(to_dev(bq), to_dev(bs))
-    _say("grouped MoE full size")
+    _say("grouped MoE full size", proj, aq.shape, N)
     c = mx.grouped_gemm(to_dev(aq), to_dev(as_), w, to_dev(d["offsets"]), torch.bfloat16)
     ch = to_host(c.float())
     ok, worst = oracle_mod.gemm_bound_ok(ch[rows], ref, sabs, "bf16")
+    _say("moe", proj, "worst error / allowance", worst)
     assert ok, worst
 
 
@@ -363,8 +389,9 @@ def test_mfma_accumulation_error_model(mx, oracle_mod):
 def test_gemm_mlp_step_full_size_sampled(mx, oracle_mod):
     """Qwen3-8B MLP micro-batch of 8192 tokens: the six GEMMs of forward, data
     gradient and weight gradient at full size, in the launch configuration the
-    library picks for them, checked on sampled output rows against the oracle
-    (operands quantized by the oracle) with the 1e-4 * sum|ab| bound."""
+    library picks for them, each checked on 256 sampled output rows (one in
+    every 256-row tile) against the oracle (operands quantized by the oracle)
+    with the 1e-4 * sum|ab| bound."""
     d = wl.mlp(0)
     q = {}
     for name, axis in (("X", 1), ("h", 1), ("W_gu", 1), ("W_d", 1), ("dY_gu", 1), ("dY_d", 1),
@@ -378,16 +405,16 @@ def test_gemm_mlp_step_full_size_sampled(mx, oracle_mod):
         ("wgrad gate_up", ("dY_gu", 0), ("X", 0), False, "f32"),
         ("wgrad down", ("dY_d", 0), ("h", 0), False, "f32"),
     ]
-    rng = np.random.default_rng(37)
-    for name, ka, kb, packed, out in gemms:
+    for i, (name, ka, kb, packed, out) in enumerate(gemms):
         aq, as_ = q[ka]
         bq, bs = q[kb]
-        rows = np.sort(rng.choice(aq.shape[0], 6, replace=False))
+        rows = sample_rows(aq.shape[0], 256, 256, 37 + i)
         _say("mlp", name, aq.shape, bq.shape)
         ref, sabs = oracle_mod.gemm(aq, as_, bq, bs, rows=rows)
         tdt = torch.float32 if out == "f32" else torch.bfloat16
         c = _gemm_dev(mx, aq, as_, bq, bs, packed, tdt)
         ok, worst = oracle_mod.gemm_bound_ok(c[rows], ref, sabs, out)
+        _say("mlp", name, "rows", rows.size, "worst error / allowance", worst)
         assert ok, (name, worst)
         del c
 

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from conftest import to_dev, to_host
+from conftest import sample_rows, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -91,24 +91,29 @@ def test_wgrad_small_ragged_with_empty_group(mx, oracle_mod, out):
     _check_wgrad(oracle_mod, ch, to_host(aq), to_host(as_), to_host(bq), to_host(bs), offsets, out)
 
 
-def test_wgrad_moe_down_projection_sampled(mx, oracle_mod):
-    """Qwen3-30B-A3B down projection weight gradient over a Zipf(1.1) top-8
-    routing of 2048 tokens: dW_g[2048 x 768] = dY_g^T h_g per expert."""
+@pytest.mark.parametrize("proj,M,N", [("down", 2048, 768), ("gate_up", 1536, 2048)])
+def test_wgrad_moe_full_config_sampled(mx, oracle_mod, proj, M, N):
+    """The Qwen3-30B-A3B experts' weight gradients at the MoE config's size:
+    8192 tokens, Zipf(1.1) top-8 routing over 128 experts, groups padded to
+    32 (T = 67,616 token rows).  down: dW_g[2048 x 768] = dY_g^T h_g;
+    gate_up: dW_g[1536 x 2048] = dY_g^T X_g.  Every expert's gradient is
+    checked on 256 of its M rows (one in every 256-row tile)."""
     import torch
-    _say("wgrad moe")
-    rng, offsets, row_token, counts = _routing(3, 2048, 128, 8)
+    _say("wgrad moe", proj)
+    rng, offsets, row_token, counts = _routing(3, 8192, 128, 8)
     T = int(offsets[-1])
     real = row_token >= 0
-    dy = np.zeros((T, 2048), np.uint16)
-    dy[real] = wl.normal_bf16(rng, (int(real.sum()), 2048), std=2.0 ** -10)
-    h = np.zeros((T, 768), np.uint16)
-    h[real] = wl.normal_bf16(rng, (int(real.sum()), 768))
+    dy = np.zeros((T, M), np.uint16)
+    dy[real] = wl.normal_bf16(rng, (int(real.sum()), M), std=2.0 ** -10)
+    h = np.zeros((T, N), np.uint16)
+    h[real] = wl.normal_bf16(rng, (int(real.sum()), N))
     aq, as_ = mx.quantize(to_dev(dy), 0)
     bq, bs = mx.quantize(to_dev(h), 0)
     c = mx.grouped_gemm_wgrad(aq, as_, bq, bs, to_dev(offsets), torch.float32)
     torch.cuda.synchronize()
     ch = to_host(c)
-    rows = np.sort(rng.choice(2048, 48, replace=False))
+    del c
+    rows = sample_rows(M, 256, 256, 38)
     _check_wgrad(oracle_mod, ch, to_host(aq), to_host(as_), to_host(bq), to_host(bs), offsets, "f32", rows=rows)
 
 

@@ -86,6 +86,19 @@ def _special_blocks():
     sp[5, 0] = 0x4370; sp[5, 1:] = 0x3F80                   # 240 (significand 1.875) saturates
     sp[6, 0] = 0x4380; sp[6, 1] = 0x3F88; sp[6, 2] = 0x3F98  # ties at the E4M3 grid
     out.append(sp)
+    # blocks whose max is a BF16 normal with exponent field 1..7 (below
+    # 2^-119): floor(log2 amax) - 8 < -127, so the scale clamps to code 0
+    # and the elements are not all below 448 * 2^-127 -- eight blocks per
+    # field, the rest of each block drawn from every smaller magnitude
+    lo = np.zeros((56, 32), np.uint16)
+    for i, E in enumerate(range(1, 8)):
+        for r in range(8):
+            row = i * 8 + r
+            mx_bits = (E << 7) | int(rng.integers(0, 128))
+            lo[row, :] = rng.integers(0, mx_bits + 1, 32)
+            lo[row, int(rng.integers(0, 32))] = mx_bits
+            lo[row] |= (rng.integers(0, 2, 32) << 15).astype(np.uint16)
+    out.append(lo)
     return np.concatenate(out)
 
 
