@@ -388,6 +388,29 @@ mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s,
 size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * mxfp8_gemm_splitk_noalloc -- mxfp8_gemm_splitk with no caller workspace and
+ * no allocation, for callers that cannot allocate device memory (code under
+ * HIP-graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operands, result, error bound and launches as mxfp8_gemm_splitk given
+ * a workspace of mxfp8_gemm_splitk_workspace_bytes(M, N, K) bytes (the same
+ * bits); the fp32 partial tiles go to a static device array inside the
+ * library of 32 MiB + 4 KiB per device (held by every device the library
+ * runs on until the process ends; every split plan on a 256-CU device fits
+ * it).  A plan that would need more returns MXFP8_ERR_SHAPE and enqueues
+ * nothing; a shape that does not split runs mxfp8_gemm and touches no
+ * scratch.  The array is shared by every call on a device and keeps the last
+ * call's partials: calls that overlap on one device (different streams or
+ * threads) race on it and must be serialized by the caller.  No allocation,
+ * no memset, no synchronization; the first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) once.
+ */
+mxfp8_status mxfp8_gemm_splitk_noalloc(const uint8_t *a_q, const uint8_t *a_s,
+                                       const uint8_t *b_q, const uint8_t *b_s,
+                                       mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
+                                       void *c, mxfp8_dtype c_dtype, hipStream_t stream);
+
+/*
  * mxfp8_grouped_gemm -- MoE expert GEMM over groups of rows:
  *   for g in 0..G-1:  C[o_g : o_{g+1}] = A[o_g : o_{g+1}] * B_g^T
  *

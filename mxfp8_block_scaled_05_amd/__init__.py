@@ -68,6 +68,8 @@ def lib():
         L.mxfp8_quantize_dual_grouped.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
         L.mxfp8_gemm_splitk.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P, ctypes.c_size_t, P]
         L.mxfp8_gemm_splitk.restype = I32
+        L.mxfp8_gemm_splitk_noalloc.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
+        L.mxfp8_gemm_splitk_noalloc.restype = I32
         L.mxfp8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
         L.mxfp8_gemm_splitk_workspace_bytes.restype = ctypes.c_size_t
         L.mxfp8_quantize_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]

@@ -440,6 +440,32 @@ mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uin
                                      c_dtype == MXFP8_BF16, sp, static_cast<float *>(workspace), stream));
 }
 
+mxfp8_status mxfp8_gemm_splitk_noalloc(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                       const uint8_t *b_s, mxfp8_layout b_layout, int64_t M, int64_t N,
+                                       int64_t K, void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
+    if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
+    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    const SplitPlan sp = splitk_plan(M, N, K, device_cu_count());
+    if (sp.splits <= 1)
+        return finish(launch_gemm(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
+                                  c_dtype == MXFP8_BF16, stream));
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    const hipError_t e = splitk_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess) return finish(e);
+    if ((size_t)sp.workspace_bytes > ws_bytes) return MXFP8_ERR_SHAPE;   // plan exceeds the static scratch
+    return finish(launch_gemm_splitk(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
+                                     c_dtype == MXFP8_BF16, sp, static_cast<float *>(ws), stream));
+}
+
 mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q_packed,
                                 const uint8_t *b_s_packed, const int32_t *d_group_offsets,
                                 int64_t G, int64_t M_total, int64_t N, int64_t K, void *c,

@@ -35,8 +35,46 @@
 #include "mx_launch.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace mx {
+
+// Device scratch of the allocation-free split-K call: the fp32 partial tiles
+// of every K slice.  A split plan keeps slices x tiles within one round of
+// the CUs and each tile covers at most 256 x 128 outputs, so on a 256-CU
+// device a plan needs at most 256 x 32768 x 4 bytes plus the per-slice
+// rounding to 16 bytes.  Each device the library runs on holds its own copy
+// of this array until the process ends.
+constexpr size_t kSplitScratchBytes = ((size_t)32 << 20) + 4096;
+static __device__ __align__(256) uint8_t scratch[kSplitScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void *g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+}  // namespace
+
+// The device address of `scratch` on the current device.  In host code the
+// array's name is only a host-side stand-in, so its address is looked up once
+// per device (with that device current) and the looked-up pointer is what
+// kernels receive.
+hipError_t splitk_scratch(void **ptr, size_t *bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void *p = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_err[dev] = r;
+        g_scratch_ptr[dev] = r == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    *bytes = kSplitScratchBytes;
+    return hipSuccess;
+}
 
 struct GemmParams {
     const uint8_t *a_q;
