@@ -359,6 +359,31 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s,
                         void *c, mxfp8_dtype c_dtype, hipStream_t stream);
 
 /*
+ * mxfp8_gemm_accurate -- mxfp8_gemm with every product exact and the sums
+ * carried at fp32 accuracy, so |C - C_ref| <= 1e-4 * sum_k |a_k b_k| holds
+ * element by element on every input, outlier-dominated rows included.
+ *
+ * Same operands, layouts, result definition and argument errors as
+ * mxfp8_gemm.  Why it exists: the scaled FP8 matrix instruction that
+ * mxfp8_gemm uses adds the products of one instruction (128 K values) with
+ * about 12 bits relative to its largest product (measured on MI355X: at most
+ * 2^-10.8 of it), which exceeds the 1e-4 * sum|ab| bound on rows whose sum
+ * is dominated by a few products (1% of x20 outliers at K = 160: 1.013x the
+ * bound).  This call instead converts each E4M3 element times its block
+ * scale to BF16 (exact for scale codes 3..246; a step whose operands hold a
+ * code outside that range takes unscaled BF16 products per block, scaled by
+ * 2^(sa + sb - 254) in fp32) and runs the BF16 matrix instruction, whose
+ * sums carry fp32 accuracy (measured: at most 2^-20 of the largest product).
+ * About half the speed of mxfp8_gemm (the BF16 matrix rate is half the FP8
+ * rate).  Limits shared with any fp32 result: products or sums outside
+ * fp32's range over- or underflow.  Deterministic.
+ */
+mxfp8_status mxfp8_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s,
+                                 const uint8_t *b_q, const uint8_t *b_s,
+                                 mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
+                                 void *c, mxfp8_dtype c_dtype, hipStream_t stream);
+
+/*
  * mxfp8_gemm_splitk -- mxfp8_gemm for shapes with few output tiles (small M:
  * the page's break-even analysis measures the MXFP8 layers over the tokens
  * per micro-batch, section "Speed: when it pays off").

@@ -68,6 +68,8 @@ def lib():
         L.mxfp8_quantize_dual_grouped.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
         L.mxfp8_gemm_splitk.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P, ctypes.c_size_t, P]
         L.mxfp8_gemm_splitk.restype = I32
+        L.mxfp8_gemm_accurate.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
+        L.mxfp8_gemm_accurate.restype = I32
         L.mxfp8_gemm_splitk_noalloc.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
         L.mxfp8_gemm_splitk_noalloc.restype = I32
         L.mxfp8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
@@ -521,12 +523,13 @@ def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:
 
 def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b, out_dtype=torch.bfloat16,
          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-         split_k: bool = False) -> torch.Tensor:
+         split_k: bool = False, accurate: bool = False) -> torch.Tensor:
     """C[M, N] = A[M, K] B[N, K]^T.  ``b`` is a PackedWeight (batch 1) or a
     canonical (b_q[N, K], b_s[N, K/32]) pair.  With split_k (or a workspace
     given) the call is mxfp8_gemm_splitk: K split over workgroups when the
     shape has few output tiles, partials in ``workspace`` (a uint8 device
-    tensor; allocated here, through torch, when not given)."""
+    tensor; allocated here, through torch, when not given).  With accurate
+    the call is mxfp8_gemm_accurate (exact products, fp32-accurate sums)."""
     _need(a_q, torch.uint8, "a_q")
     _need(a_s, torch.uint8, "a_s")
     M, K = a_q.shape
@@ -551,6 +554,12 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b, out_dtype=torch.bfloat16,
         _need(out, out_dtype, "out")
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be [M, N]")
+    if accurate:
+        if split_k or workspace is not None:
+            raise ValueError("accurate and split_k are separate calls")
+        _check(lib().mxfp8_gemm_accurate(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), layout, M, N, K,
+                                         _ptr(out), code, _stream(a_q.device)), "mxfp8_gemm_accurate")
+        return out
     if split_k or workspace is not None:
         need = gemm_splitk_workspace_bytes(M, N, K)
         if workspace is None and need:

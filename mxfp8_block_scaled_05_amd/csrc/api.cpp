@@ -396,6 +396,23 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b
                               c_dtype == MXFP8_BF16, stream));
 }
 
+mxfp8_status mxfp8_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                 const uint8_t *b_s, mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
+                                 void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
+    if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
+    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_gemm_accurate(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
+                                       c_dtype == MXFP8_BF16, stream));
+}
+
 size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim) return 0;
     if (check_device() != MXFP8_OK) return 0;

@@ -262,6 +262,7 @@ struct TileOps {
     v4i ra, rsa, rb, rsb;
     __amdgpu_buffer_rsrc_t rsa_c, rsb_c;
     int Ki, KBi, lane, w, wm, wn, lrow, lblk;
+    int rows_a, rows_b;        // rows of the A and B tiles inside the operands
     int lda, lsa, ldb, lsb;    // row strides of canonical operands (bytes)
     uint32_t lds0;
 
@@ -284,6 +285,8 @@ struct TileOps {
         lsb = (int)p.lsb;
         lds0 = lds_addr(smem);
         const int64_t rows_a = min((int64_t)BM, m_end - m0);
+        this->rows_a = (int)rows_a;
+        this->rows_b = (int)min((int64_t)BN, N - n0);
         // each descriptor spans exactly this tile's bytes (from its first row's
         // K range start to its last row's K range end): out-of-range lanes read 0
         const uint32_t a_bytes = (uint32_t)((rows_a - 1) * p.lda + K);
@@ -444,6 +447,173 @@ struct TileOps {
             for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     bf[j], af, acc[i][j], 0, 0, 0, sbs[j], 0, sas[i]);
+        }
+    }
+
+    // ---- accurate path (mxfp8_gemm_accurate): BF16 MFMA on operands
+    // converted exactly.  Every E4M3 element times its block's scale is a
+    // 4-bit significand with an exponent inside BF16's range whenever the
+    // scale code lies in [3, 246], so the conversion is exact, every product
+    // of two such BF16 values is exact in fp32, and the BF16 matrix
+    // instruction adds them with fp32 accuracy (measured: at most 2^-20 of
+    // the largest product), far inside 1e-4 * sum|ab|.
+
+    // The four block scales of step ks (byte t: block 4 ks + t) of the
+    // lane's row in A atom i and B atom j.  Rows outside the operands and
+    // blocks past K (whose elements are all zero) read as 127, whatever the
+    // layout stores there, so packed and canonical B take the same path.
+    __device__ __forceinline__ void acc_scales(const uint8_t *st, int ks, const uint8_t *chunk,
+                                               const uint8_t *chunk_b, uint32_t *sa4, uint32_t *sb4) const {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int r = wm * WTM + i * 16 + lrow;
+            if constexpr (SA_LDS) {
+                sa4[i] = *reinterpret_cast<const uint32_t *>(st + SA_OFF + r * 4);
+            } else if constexpr (SAC) {
+                sa4[i] = *reinterpret_cast<const uint32_t *>(chunk + chunk_byte(r, (ks % kChunkSteps) * 4));
+            } else {
+                uint32_t v = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int blk = ks * 4 + t;
+                    const uint32_t off = blk < KBi ? (uint32_t)(r * lsa + blk) : kOOB;
+                    v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsa_c, off, 0, 0) << (8 * t);
+                }
+                sa4[i] = v;
+            }
+            sa4[i] = neutral_outside(sa4[i], r < rows_a, ks);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int r = wn * WTN + j * 16 + lrow;
+            if constexpr (BPACK) {
+                const uint8_t *p = st + SB_OFF + (wn * FN + j) * 64 + lrow;
+                sb4[j] = (uint32_t)p[0] | ((uint32_t)p[16] << 8) | ((uint32_t)p[32] << 16) | ((uint32_t)p[48] << 24);
+            } else if constexpr (SBC) {
+                sb4[j] = *reinterpret_cast<const uint32_t *>(chunk_b + chunk_byte(r, (ks % kChunkSteps) * 4));
+            } else if constexpr (SB_LDS) {
+                sb4[j] = *reinterpret_cast<const uint32_t *>(st + SB_OFF + r * 4);
+            } else {
+                uint32_t v = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int blk = ks * 4 + t;
+                    const uint32_t off = blk < KBi ? (uint32_t)(r * lsb + blk) : kOOB;
+                    v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rsb_c, off, 0, 0) << (8 * t);
+                }
+                sb4[j] = v;
+            }
+            sb4[j] = neutral_outside(sb4[j], r < rows_b, ks);
+        }
+    }
+
+    // 127 in every byte of a row outside the operand, and in the bytes of
+    // blocks at or past K/32
+    __device__ __forceinline__ uint32_t neutral_outside(uint32_t v, bool row_in, int ks) const {
+        if (!row_in) return 0x7F7F7F7Fu;
+        const int valid = KBi - ks * 4;                 // blocks of this step inside K
+        if (valid >= 4) return v;
+        const uint32_t keep = valid <= 0 ? 0u : (1u << (8 * valid)) - 1u;
+        return (v & keep) | (0x7F7F7F7Fu & ~keep);
+    }
+
+    // 8 E4M3 bytes of the lane's row of a 16-row atom: K = 32 t + 8 (lane / 16)
+    // .. + 7 of the step (the K slice a lane supplies to the 16x16x32 BF16
+    // MFMA), from the swizzled 128-byte LDS rows
+    __device__ __forceinline__ v2i lds_k8(const uint8_t *atom, int t) const {
+        const int g = lane >> 4;
+        const int c = 2 * t + (g >> 1);
+        return *reinterpret_cast<const v2i *>(atom + lrow * 128 + (int)((c ^ (int)swz((uint32_t)lrow)) * 16) +
+                                              (g & 1) * 8);
+    }
+
+    // the BF16 fragment of those 8 elements times 2^(code - 127)
+    __device__ __forceinline__ static v8bf cvt8(v2i v, uint32_t code) {
+        const float s = code == 0 ? bits_to_float(0x00400000u) : bits_to_float(code << 23);
+        const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v.x, s, false);
+        const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v.x, s, true);
+        const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v.y, s, false);
+        const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v.y, s, true);
+        return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    }
+
+    // true if every scale byte of the step lies in [3, 246] (exact folded
+    // conversion), the same in every lane of the wave
+    __device__ __forceinline__ static bool scales_foldable(const uint32_t *sa4, const uint32_t *sb4) {
+        uint32_t bad = 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t c = (sa4[i] >> (8 * t)) & 0xFFu;
+                bad |= (uint32_t)(c < 3u || c > 246u);
+            }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t c = (sb4[j] >> (8 * t)) & 0xFFu;
+                bad |= (uint32_t)(c < 3u || c > 246u);
+            }
+        return __ballot(bad != 0) == 0;
+    }
+
+    // One k-step on the accurate path.  Folded: the scales ride the
+    // conversions and the four 32-K MFMAs per tile accumulate straight into
+    // acc.  Otherwise (a scale outside [3, 246] somewhere in the wave's
+    // operands): unscaled BF16 products per block, each block's 16x16 sum
+    // scaled by 2^(sa + sb - 254) with ldexp and added in fp32.
+    __device__ __forceinline__ void acc_step(const uint8_t *st, int ks, const uint8_t *chunk,
+                                             const uint8_t *chunk_b, v4f (*acc)[FN]) const {
+        uint32_t sa4[FM], sb4[FN];
+        acc_scales(st, ks, chunk, chunk_b, sa4, sb4);
+        const uint8_t *sa = st + wm * WTM * 128;
+        const uint8_t *sb = st + BM * 128 + wn * WTN * 128;
+        if (scales_foldable(sa4, sb4)) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v8bf bf[FN];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) bf[j] = cvt8(lds_k8(sb + j * 16 * 128, t), (sb4[j] >> (8 * t)) & 0xFFu);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const v8bf af = cvt8(lds_k8(sa + i * 16 * 128, t), (sa4[i] >> (8 * t)) & 0xFFu);
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);
+                }
+            }
+            return;
+        }
+        // lane l holds C[row l % 16][cols 4 (l / 16) + r]: the column scales
+        // are the B scale words of lanes 4 (l / 16) + r
+        uint32_t sbc[FN][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sbc[j][r] = (uint32_t)__shfl((int)sb4[j], 4 * (lane >> 4) + r);
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            v8bf bf[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = cvt8(lds_k8(sb + j * 16 * 128, t), 127u);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const v8bf af = cvt8(lds_k8(sa + i * 16 * 128, t), 127u);
+                const int ca = (int)((sa4[i] >> (8 * t)) & 0xFFu);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const v4f p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, zero, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int cb = (int)((sbc[j][r] >> (8 * t)) & 0xFFu);
+                        float v = __builtin_ldexpf(p[r], ca + cb - 254);
+                        if (ca == 255 || cb == 255) v = __builtin_nanf("");
+                        acc[i][j][r] += v;
+                    }
+                }
+            }
         }
     }
 };
@@ -622,7 +792,8 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 // NST stages: the copies of step ks+NST-1 are issued at the top of step ks.
 // NST = 3 needs every copy to go through LDS (KALIGN) so that a wave's copy
 // count per step is fixed and the wait can leave the next steps in flight.
-template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool KALIGN, int NST, bool SAC = false>
+template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool KALIGN, int NST, bool SAC = false,
+          bool ACC = false>
 __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_end, int64_t n0, int64_t g,
                                           int64_t kbase, int64_t kbound, int KS, uint8_t *smem) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
@@ -645,8 +816,8 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
     if (KS > 0) {                       // an empty group (grouped-K) stores zeros
         if constexpr (SAC) t.issue_sa_chunk(0, t.lds0 + NST * T::STAGE);
         if constexpr (T::SBC) t.issue_sb_chunk(0, t.lds0 + NST * T::STAGE + 2 * T::CHUNK);
-        if constexpr (T::SA_REG) t.fetch_sa(0, sa_nxt);
-        if constexpr (T::SB_REG) t.fetch_sb(0, sb_nxt);
+        if constexpr (T::SA_REG && !ACC) t.fetch_sa(0, sa_nxt);
+        if constexpr (T::SB_REG && !ACC) t.fetch_sb(0, sb_nxt);
         t.issue(0, 0);
         if constexpr (NST == 3) {
             if (KS > 1) t.issue(1, 1);
@@ -676,12 +847,12 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
                     t.issue_sb_chunk(c + 1, t.lds0 + NST * T::STAGE + 2 * T::CHUNK + ((c + 1) & 1) * T::CHUNK_B);
             }
         }
-        if constexpr (T::SA_REG) {
+        if constexpr (T::SA_REG && !ACC) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sa_cur[i] = sa_nxt[i];
             if (ks + 1 < KS) t.fetch_sa(ks + 1, sa_nxt);
         }
-        if constexpr (T::SB_REG) {
+        if constexpr (T::SB_REG && !ACC) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) sb_cur[j] = sb_nxt[j];
             if (ks + 1 < KS) t.fetch_sb(ks + 1, sb_nxt);
@@ -695,6 +866,12 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
         }
 
         const uint8_t *st = smem + cur * T::STAGE;
+        if constexpr (ACC) {
+            t.acc_step(st, ks, chunks + ((ks / T::kChunkSteps) & 1) * T::CHUNK,
+                       chunks_b + ((ks / T::kChunkSteps) & 1) * T::CHUNK_B, acc);
+            cur = cur + 1 == NST ? 0 : cur + 1;
+            continue;
+        }
         int sas[FM], sbs[FN];
         t.lds_scales(st, sas, sbs, chunks + ((ks / T::kChunkSteps) & 1) * T::CHUNK, ks,
                      chunks_b + ((ks / T::kChunkSteps) & 1) * T::CHUNK_B);
@@ -728,7 +905,7 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
 }
 
 template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false,
-          int NST = 2, bool SAC = false>
+          int NST = 2, bool SAC = false, bool ACC = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
     constexpr int LDS = NST * T::STAGE + (SAC ? 2 * T::CHUNK + 2 * T::CHUNK_B : 0);
@@ -744,7 +921,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     } else {
         if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
     }
-    gemm_tile<BM, BN, WM, BPACK, OUT_BF16, KALIGN, NST, SAC>(p, m0, m_end, n0, g, kbase, kbound, KS, smem);
+    gemm_tile<BM, BN, WM, BPACK, OUT_BF16, KALIGN, NST, SAC, ACC>(p, m0, m_end, n0, g, kbase, kbound, KS, smem);
 }
 
 // Grouped-K (expert weight gradients) with T % 128 == 0: a tile whose token
@@ -1177,6 +1354,35 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     }
     p.tiles_n = d.small_cols;
     return launch_tile<256, 128, 4, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
+}
+
+// Accurate path: 256x128 tiles (dense, XCD-aware order), both operands
+// staged in LDS as for mxfp8_gemm, each k-step computed by
+// TileOps::acc_step.
+hipError_t launch_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                const uint8_t *b_s, bool b_packed, int64_t M, int64_t N, int64_t K, void *c,
+                                bool c_bf16, hipStream_t stream) {
+    GemmParams p{};
+    p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = c;
+    p.M = M; p.N = N; p.K = K;
+    p.KS = (int)packed_ksteps(K);
+    p.NP = (int)packed_panels(N);
+    p.G = 1;
+    p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
+    p.tiles_m = (int)ceil_div(M, 256);
+    p.tiles_n = (int)ceil_div(N, 128);
+    dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(kThreads);
+#define MX_ACC(BP, BF, KA) hipLaunchKernelGGL((gemm_kernel<256, 128, 4, BP, BF, false, KA, false, 2, false, true>), \
+                                             grid, block, 0, stream, p)
+    if (K % 128 == 0) {
+        if (b_packed) { if (c_bf16) MX_ACC(true, true, true); else MX_ACC(true, false, true); }
+        else { if (c_bf16) MX_ACC(false, true, true); else MX_ACC(false, false, true); }
+    } else {
+        if (b_packed) { if (c_bf16) MX_ACC(true, true, false); else MX_ACC(true, false, false); }
+        else { if (c_bf16) MX_ACC(false, true, false); else MX_ACC(false, false, false); }
+    }
+#undef MX_ACC
+    return hipGetLastError();
 }
 
 // Split-K plan for a dense GEMM on `cus` CUs: 256x128 tiles, as many K

@@ -26,6 +26,10 @@ struct SplitPlan {
 };
 SplitPlan splitk_plan(int64_t M, int64_t N, int64_t K, int cus);
 // partial tiles into `workspace`, then C = their sum (slice order)
+// mxfp8_gemm_accurate: BF16 MFMA on exactly converted operands
+hipError_t launch_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                const uint8_t *b_s, bool b_packed, int64_t M, int64_t N, int64_t K, void *c,
+                                bool c_bf16, hipStream_t stream);
 // device address and size of the static split-K scratch on the current device
 hipError_t splitk_scratch(void **ptr, size_t *bytes);
 hipError_t launch_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,

@@ -72,13 +72,13 @@ def _bound_with_hw(c, ref, sabs, H, out):
     return bool(np.all(err <= allow)), float(np.max(err / np.maximum(allow, 1e-300)))
 
 
-def _gemm_dev(mx, aq, as_, bq, bs, packed, out_dtype):
+def _gemm_dev(mx, aq, as_, bq, bs, packed, out_dtype, accurate=False):
     a_q, a_s = to_dev(aq), to_dev(as_)
     if packed:
         w = mx.repack(to_dev(bq), to_dev(bs))
-        c = mx.gemm(a_q, a_s, w, out_dtype)
+        c = mx.gemm(a_q, a_s, w, out_dtype, accurate=accurate)
     else:
-        c = mx.gemm(a_q, a_s, (to_dev(bq), to_dev(bs)), out_dtype)
+        c = mx.gemm(a_q, a_s, (to_dev(bq), to_dev(bs)), out_dtype, accurate=accurate)
     torch.cuda.synchronize()
     return to_host(c.float()) if out_dtype == torch.bfloat16 else to_host(c)
 
@@ -186,6 +186,80 @@ def test_gemm_random_ragged(mx, oracle_mod, M, N, K, out):
     assert np.array_equal(cs[0], cs[1])
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 300, 416), (64, 1000, 2080), (1000, 96, 160), (513, 264, 4096)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_accurate_pure_bound(mx, oracle_mod, M, N, K, out):
+    """mxfp8_gemm_accurate on the adversarial ragged inputs (1% x20 outliers,
+    small K): every element within the pure bound 1e-4 * sum|ab| (+ bf16
+    rounding), no hardware term; packed and canonical B give the same bits."""
+    rng = np.random.default_rng(M * N + K)
+    X = wl.normal_bf16(rng, (M, K), outlier_frac=0.01)
+    W = wl.normal_bf16(rng, (N, K), std=0.02)
+    xq, xs = _quant_pair(oracle_mod, X)
+    wq, ws = _quant_pair(oracle_mod, W)
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    cs = []
+    for packed in (False, True):
+        _say("gemm accurate", M, N, K, out, packed)
+        c = _gemm_dev(mx, xq, xs, wq, ws, packed, tdt, accurate=True)
+        ok, worst = oracle_mod.gemm_bound_ok(c, ref, sabs, out)
+        _say("  error / pure bound %.4f" % worst)
+        assert ok, (packed, worst)
+        cs.append(c)
+    assert np.array_equal(cs[0], cs[1])
+
+
+def test_gemm_accurate_outlier_products(mx, oracle_mod):
+    """Single-step products dominated by outliers on both operands (2% x20
+    each): the scaled-MFMA path errs by up to 2^-10 max|ab| there; the
+    accurate path stays within the pure bound on every element, and its
+    error is far below 2^-16 max|ab|."""
+    rng = np.random.default_rng(36)
+    M, N, K = 512, 256, 128
+    X = wl.normal_bf16(rng, (M, K), outlier_frac=0.02)
+    W = wl.normal_bf16(rng, (N, K), std=0.02, outlier_frac=0.02)
+    xq, xs = _quant_pair(oracle_mod, X)
+    wq, ws = _quant_pair(oracle_mod, W)
+    ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+    H = _hw_term(oracle_mod, xq, xs, wq, ws)
+    c = _gemm_dev(mx, xq, xs, wq, ws, True, torch.float32, accurate=True).astype(np.float64)
+    ok, worst = oracle_mod.gemm_bound_ok(c, ref, sabs, "f32")
+    _say("accurate: error / pure bound %.4f, log2 max error / max|ab| %.2f"
+         % (worst, float(np.log2(np.max(np.abs(c - ref) / np.maximum(H, 1e-300)) + 1e-300))))
+    assert ok, worst
+    assert np.all(np.abs(c - ref) <= 2.0 ** -16 * H)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 416), (513, 264, 4096)])
+def test_gemm_accurate_exact_cases(mx, oracle_mod, M, N, K, packed):
+    """Exact results compare bit for bit on both paths: small-integer elements
+    with narrow scales (the folded conversion), and with scale codes at the
+    ends of the E8M0 range (A in {0, 1, 2, 250, 251, 252}, B chosen so that
+    every block's combined exponent stays within [-8, 8]: the accurate path's
+    per-block fallback for codes outside [3, 246]; the result is exact in
+    fp32 either way)."""
+    rng = np.random.default_rng(M + N + K + 7)
+    aq, as_ = _int_operand(rng, M, K)
+    bq, bs = _int_operand(rng, N, K)
+    _say("gemm accurate exact", M, N, K, packed)
+    ref, _ = oracle_mod.gemm(aq, as_, bq, bs)
+    c = _gemm_dev(mx, aq, as_, bq, bs, packed, torch.float32, accurate=True)
+    assert np.array_equal(c.astype(np.float64), ref)
+    # end-of-range scale codes: per block, A low and B high, or A high and B low
+    nb = K // 32
+    lowhi = rng.integers(0, 2, size=nb).astype(bool)
+    as2 = np.where(lowhi[None, :], rng.integers(0, 3, size=(M, nb)), rng.integers(250, 253, size=(M, nb)))
+    bs2 = np.where(lowhi[None, :], rng.integers(250, 253, size=(N, nb)), rng.integers(3, 6, size=(N, nb)))
+    as2, bs2 = as2.astype(np.uint8), bs2.astype(np.uint8)
+    ref2, _ = oracle_mod.gemm(aq, as2, bq, bs2)
+    c2 = _gemm_dev(mx, aq, as2, bq, bs2, packed, torch.float32, accurate=True)
+    assert np.array_equal(c2.astype(np.float64), ref2)
+    c3 = _gemm_dev(mx, aq, as2, bq, bs2, packed, torch.float32)
+    assert np.array_equal(c3.astype(np.float64), ref2)
+
+
 @pytest.mark.parametrize("M,N,K,out", [(500, 32968, 160, "f32"), (512, 32768, 256, "bf16"),
                                        (4000, 6100, 512, "bf16"), (4096, 6144, 1024, "f32")])
 def test_gemm_mixed_tiles_full_output(mx, oracle_mod, M, N, K, out):
@@ -249,6 +323,12 @@ def test_gemm_qkv_full_output(mx, oracle_mod):
     ok, worst = oracle_mod.gemm_bound_ok(c, ref, sabs, "bf16")
     _say("qkv worst error / allowance", worst)
     assert ok, worst
+    _say("gemm qkv full output, accurate path")
+    ca = _gemm_dev(mx, xq, xs, wq, ws, True, torch.bfloat16, accurate=True)
+    ok, worst_a = oracle_mod.gemm_bound_ok(ca, ref, sabs, "bf16")
+    _say("qkv accurate worst error / allowance", worst_a)
+    assert ok, worst_a
+    del ca
     # the page's healthy-kernel error band for a dense layer: relative error
     # of the MXFP8 layer against the high-precision GEMM on the BF16 inputs
     rows = sample_rows(xq.shape[0], 256, 256, 32)
