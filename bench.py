@@ -186,7 +186,14 @@ def bench_qkv(args, dev):
         else:
             mx.gemm(xq, xs, w, torch.bfloat16, out=y)
 
-    settled = settle(lambda: step(0, ()), args.settle_s)
+    # the settle phase rotates the input sets like the timed steps, so every
+    # launch a kernel trace of this command averages reads from HBM
+    rot = [0]
+
+    def settle_step():
+        step(rot[0], ())
+        rot[0] += 1
+    settled = settle(settle_step, args.settle_s)
     gc.disable()   # no collector pauses between the timing events
     for i in range(args.warmup):
         step(i, ("gemm",))
@@ -211,6 +218,14 @@ def bench_qkv(args, dev):
     med_all = timer.medians_us()
     for k in ("quantize_W", "quantize_X", "repack_W"):
         avg[k], med[k] = avg_all[k], med_all[k]
+    # the accurate GEMM (mxfp8_gemm_accurate: BF16 matrix instructions on
+    # exactly converted operands) on the same rotated inputs, its own pass
+    timer.reset()
+    for i in range(min(args.steps, 20)):
+        X, W, xq, xs, wq, ws, w, y = sets[i % R]
+        timer.time("gemm_accurate", lambda: mx.gemm(xq, xs, w, torch.bfloat16, out=y, accurate=True))
+    torch.cuda.synchronize()
+    acc_us = timer.averages_us()["gemm_accurate"]
     ms_per_step = 1e3 * wall / args.steps
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (avg["gemm"] * 1e-6) / 1e12
@@ -222,7 +237,8 @@ def bench_qkv(args, dev):
                  "frac_mxfp8_peak": round(gemm_tflops / MXFP8_PEAK_TFLOPS, 4),
                  "us_with_events_around_every_op": round(avg_all["gemm"], 2)},
     }
-    for k in kern:
+    kern["gemm_accurate"] = _gemm_rate(acc_us, M, N, K)
+    for k in ("quantize_W", "quantize_X", "repack_W", "gemm"):
         kern[k]["median_us"] = round(med[k], 2)
     # context for the HBM-bound kernels: a plain copy of the same bytes, cold
     for k, nbytes in (("quantize_W", N * K * Q_BYTES_PER_ELT), ("quantize_X", M * K * Q_BYTES_PER_ELT),
@@ -247,7 +263,8 @@ def bench_qkv(args, dev):
                    "M": M, "N": N, "K": K, "rotated_sets": R},
         "kernels": kern,
         "kernels_note": "gemm: HIP events around every GEMM launch of the timed steps; quantize and "
-                        "repack: HIP events around every op in a separate pass of min(steps, 100) steps",
+                        "repack: HIP events around every op in a separate pass of min(steps, 100) steps; "
+                        "gemm_accurate: mxfp8_gemm_accurate in a pass of its own",
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MXFP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP8_PEAK_TFLOPS, 4),
                      "traffic": measured_gemm_traffic()},
@@ -412,6 +429,10 @@ def bench_mlp(args, dev):
     kern = {}
     for key, nbytes in q_bytes.items():
         kern[key] = _bw(avg[key], nbytes)
+    # the largest tensor quantized along each axis on its own (unfused pass)
+    for ax in (1, 0):
+        key = "quantize_dY_gu_axis%d" % ax
+        kern[key + "_unfused"] = _bw(avg_unf[key], t["dY_gu"].numel() * Q_BYTES_PER_ELT)
     for key, (_, _, M, N, K, _) in gemms.items():
         kern["gemm_" + key] = _gemm_rate(avg["gemm_" + key], M, N, K)
     gemm_us = sum(avg["gemm_" + k] for k in gemms)
@@ -938,6 +959,46 @@ def _oracle_single_core():
         return None
 
 
+def secondary_workloads(args, dev):
+    """Compact figures of the other configurations, run after the default
+    step with few steps each (a few seconds in all): the Qwen3-8B weight sync
+    (all 144 linears quantized into the canonical grid and the packed layout),
+    the Qwen3-8B MLP learner micro-batch (8192 tokens), and the Qwen3-30B-A3B
+    MoE layer forward.  Each is the same code as its --workload line."""
+    import torch
+    sub = argparse.Namespace(steps=min(args.steps, 10), warmup=min(args.warmup, 2), settle_s=0.1)
+    res = {}
+    s = bench_sync(sub, dev)
+    res["weight_sync"] = {"ms": s["summary"]["graph_gpu_ms"], "GB/s": s["value"],
+                          "frac_hbm_peak": s["summary"]["frac_hbm_peak"],
+                          "algorithmic_GB": s["summary"]["algorithmic_GB"],
+                          "one_launch_per_weight_graph_ms": s["summary"]["one_launch_per_weight_graph_ms"],
+                          "what": s["config"]["workload"]}
+    gc.collect()
+    torch.cuda.empty_cache()
+    m = bench_mlp(sub, dev)
+    k = m["kernels"]
+    res["mlp_step"] = {"ms_per_step": m["ms_per_step"], "TFLOP/s": m["value"],
+                       "gemm_TFLOP/s": m["summary"]["gemm_TFLOP/s"],
+                       "graph_replay_ms_per_step": m["summary"]["graph_replay_ms_per_step"],
+                       "gemms": {g: k[g] for g in k if g.startswith("gemm_")},
+                       "quantize": {q: k[q] for q in k if q.startswith("quantize_")},
+                       "what": m["config"]["workload"]}
+    gc.collect()
+    torch.cuda.empty_cache()
+    e = bench_moe(sub, dev)
+    k = e["kernels"]
+    res["moe_forward"] = {"ms_per_step": e["ms_per_step"], "TFLOP/s": e["value"],
+                          "grouped_gemm_gate_up": k["grouped_gemm_gate_up"],
+                          "grouped_gemm_down": k["grouped_gemm_down"],
+                          "what": e["config"]["workload"]}
+    gc.collect()
+    torch.cuda.empty_cache()
+    res["note"] = "steps=%d warmup=%d per workload; HIP-event kernel times as in each --workload line" % (
+        sub.steps, sub.warmup)
+    return res
+
+
 def copy_calibration(dev, nbytes: int = 512 << 20, reps: int = 3):
     """A plain device copy of known size, for scaling the FETCH_SIZE /
     WRITE_SIZE counters of a profiled run (reads nbytes, writes nbytes)."""
@@ -960,6 +1021,8 @@ def main():
                     help="untimed seconds of the step before the W warm-up steps (clock ramp)")
     ap.add_argument("--workload", default="qkv", choices=["qkv", "mlp", "moe", "moe_train", "sync", "sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="default workload only: skip the compact weight-sync / MLP / MoE figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -979,6 +1042,8 @@ def main():
         copy_calibration(dev)
     if args.workload == "qkv":
         out = bench_qkv(args, dev)
+        if not args.no_secondary:
+            out["secondary"] = secondary_workloads(args, dev)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_qkv()
     else:
