@@ -61,6 +61,17 @@ constexpr int64_t kMaxSelfcheckRows = 4096;       // probe rows of a self-check
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The integer a caller passed for an enum parameter.  C callers may pass any
+// int; reading such a value through the enum type is undefined in C++ (the
+// host UBSan build flags it), so enum arguments are validated on their bytes.
+template <class E>
+int raw(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+    int v = 0;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+
 mxfp8_status check_device() {
     int dev = 0;
     const hipError_t e = hipGetDevice(&dev);
@@ -166,7 +177,7 @@ mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, co
                                       int64_t G, int64_t T, int64_t M, int64_t N, void *c,
                                       mxfp8_dtype c_dtype, hipStream_t stream) {
     if (!a_q || !a_s || !b_q || !b_s || !d_group_offsets || !c) return MXFP8_ERR_NULL;
-    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
     if (G < 1 || G > 65535 || T < 32 || T % 32 || T >= ((int64_t)1 << 23)) return MXFP8_ERR_SHAPE;
     if (M <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim) return MXFP8_ERR_SHAPE;
     if (G * ((M + 255) / 256) * ((N + 255) / 256) > 0x7FFFFFFF) return MXFP8_ERR_SHAPE;
@@ -176,7 +187,7 @@ mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, co
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
     return finish(launch_grouped_gemm_wgrad(a_q, a_s, b_q, b_s, d_group_offsets, G, T, M, N, c,
-                                            c_dtype == MXFP8_BF16, stream));
+                                            raw(c_dtype) == MXFP8_BF16, stream));
 }
 
 mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols, uint8_t *q_row,
@@ -346,14 +357,14 @@ mxfp8_status mxfp8_dequantize(const uint8_t *q, const uint8_t *scales, int64_t r
                               int axis, void *out, mxfp8_dtype out_dtype, hipStream_t stream) {
     if (!q || !scales || !out) return MXFP8_ERR_NULL;
     if (axis != 0 && axis != 1) return MXFP8_ERR_AXIS;
-    if (out_dtype != MXFP8_F32 && out_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (raw(out_dtype) != MXFP8_F32 && raw(out_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
     if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim) return MXFP8_ERR_SHAPE;
     if (axis == 1 && cols % 32) return MXFP8_ERR_SHAPE;
     if (axis == 0 && (rows % 32 || (rows + 63) / 64 > 65535)) return MXFP8_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(out)) return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
-    return finish(launch_dequantize(q, scales, rows, cols, axis, out, out_dtype == MXFP8_BF16,
+    return finish(launch_dequantize(q, scales, rows, cols, axis, out, raw(out_dtype) == MXFP8_BF16,
                                     stream));
 }
 
@@ -382,8 +393,8 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b
                         const uint8_t *b_s, mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
                         void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
     if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
-    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
-    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (raw(b_layout) != MXFP8_CANONICAL && raw(b_layout) != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
     if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
         return MXFP8_ERR_SHAPE;
     // tile counts must fit the 1-D grid
@@ -392,16 +403,16 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b
         return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
-    return finish(launch_gemm(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
-                              c_dtype == MXFP8_BF16, stream));
+    return finish(launch_gemm(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
+                              raw(c_dtype) == MXFP8_BF16, stream));
 }
 
 mxfp8_status mxfp8_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                                  const uint8_t *b_s, mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
                                  void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
     if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
-    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
-    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (raw(b_layout) != MXFP8_CANONICAL && raw(b_layout) != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
     if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
         return MXFP8_ERR_SHAPE;
     if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
@@ -409,8 +420,8 @@ mxfp8_status mxfp8_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s, const u
         return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
-    return finish(launch_gemm_accurate(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
-                                       c_dtype == MXFP8_BF16, stream));
+    return finish(launch_gemm_accurate(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
+                                       raw(c_dtype) == MXFP8_BF16, stream));
 }
 
 size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -425,8 +436,8 @@ mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uin
                                void *c, mxfp8_dtype c_dtype, void *workspace, size_t workspace_bytes,
                                hipStream_t stream) {
     if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
-    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
-    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (raw(b_layout) != MXFP8_CANONICAL && raw(b_layout) != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
     if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
         return MXFP8_ERR_SHAPE;
     if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
@@ -451,18 +462,18 @@ mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uin
         }
     }
     if (sp.splits <= 1)
-        return finish(launch_gemm(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
-                                  c_dtype == MXFP8_BF16, stream));
-    return finish(launch_gemm_splitk(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
-                                     c_dtype == MXFP8_BF16, sp, static_cast<float *>(workspace), stream));
+        return finish(launch_gemm(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
+                                  raw(c_dtype) == MXFP8_BF16, stream));
+    return finish(launch_gemm_splitk(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
+                                     raw(c_dtype) == MXFP8_BF16, sp, static_cast<float *>(workspace), stream));
 }
 
 mxfp8_status mxfp8_gemm_splitk_noalloc(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                                        const uint8_t *b_s, mxfp8_layout b_layout, int64_t M, int64_t N,
                                        int64_t K, void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
     if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
-    if (b_layout != MXFP8_CANONICAL && b_layout != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
-    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (raw(b_layout) != MXFP8_CANONICAL && raw(b_layout) != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
     if (M <= 0 || N <= 0 || K < 32 || K % 32 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
         return MXFP8_ERR_SHAPE;
     if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
@@ -472,15 +483,15 @@ mxfp8_status mxfp8_gemm_splitk_noalloc(const uint8_t *a_q, const uint8_t *a_s, c
     if (st != MXFP8_OK) return st;
     const SplitPlan sp = splitk_plan(M, N, K, device_cu_count());
     if (sp.splits <= 1)
-        return finish(launch_gemm(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
-                                  c_dtype == MXFP8_BF16, stream));
+        return finish(launch_gemm(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
+                                  raw(c_dtype) == MXFP8_BF16, stream));
     void *ws = nullptr;
     size_t ws_bytes = 0;
     const hipError_t e = splitk_scratch(&ws, &ws_bytes);
     if (e != hipSuccess) return finish(e);
     if ((size_t)sp.workspace_bytes > ws_bytes) return MXFP8_ERR_SHAPE;   // plan exceeds the static scratch
-    return finish(launch_gemm_splitk(a_q, a_s, b_q, b_s, b_layout == MXFP8_PACKED, M, N, K, c,
-                                     c_dtype == MXFP8_BF16, sp, static_cast<float *>(ws), stream));
+    return finish(launch_gemm_splitk(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
+                                     raw(c_dtype) == MXFP8_BF16, sp, static_cast<float *>(ws), stream));
 }
 
 mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q_packed,
@@ -488,7 +499,7 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const ui
                                 int64_t G, int64_t M_total, int64_t N, int64_t K, void *c,
                                 mxfp8_dtype c_dtype, hipStream_t stream) {
     if (!a_q || !a_s || !b_q_packed || !b_s_packed || !d_group_offsets || !c) return MXFP8_ERR_NULL;
-    if (c_dtype != MXFP8_F32 && c_dtype != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
     if (G < 1 || G > 65535 || M_total < 0 || M_total % 32 || M_total >= kMaxDim) return MXFP8_ERR_SHAPE;
     if (N <= 0 || N >= kMaxDim || K < 32 || K % 32 || K > kMaxK) return MXFP8_ERR_SHAPE;
     if ((ceil_div(M_total, 128) + G) * ceil_div(N, 256) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
@@ -499,7 +510,7 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const ui
     if (st != MXFP8_OK) return st;
     if (M_total == 0) return MXFP8_OK;
     return finish(launch_grouped_gemm(a_q, a_s, b_q_packed, b_s_packed, d_group_offsets, G,
-                                      M_total, N, K, c, c_dtype == MXFP8_BF16, stream));
+                                      M_total, N, K, c, raw(c_dtype) == MXFP8_BF16, stream));
 }
 
 }  // extern "C"
