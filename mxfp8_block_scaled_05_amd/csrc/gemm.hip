@@ -570,18 +570,35 @@ struct TileOps {
         const uint8_t *sa = st + wm * WTM * 128;
         const uint8_t *sb = st + BM * 128 + wn * WTN * 128;
         if (scales_foldable(sa4, sb4)) {
+            // Folded: every element carries its own scale, so the K slots of
+            // the four 16x16x32 MFMAs may be any split of the step's 128 K
+            // that A and B share.  The lane's 32-byte fragment of the scaled
+            // FP8 MFMA (K 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15,
+            // g = lane / 16; conflict-free 16-byte LDS reads) is cut into
+            // four 8-byte slices, slice v feeding MFMA v; slices 0-1 belong
+            // to block g / 2, slices 2-3 to block 2 + g / 2.
+            const int b0 = lblk >> 1, b1 = 2 + (lblk >> 1);
+            v8bf bf[FN][4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v8bf bf[FN];
+            for (int j = 0; j < FN; ++j) {
+                const v8i f = lds_frag(sb + j * 16 * 128, lane);
+                const uint32_t c0 = (sb4[j] >> (8 * b0)) & 0xFFu, c1 = (sb4[j] >> (8 * b1)) & 0xFFu;
+                bf[j][0] = cvt8(v2i{f[0], f[1]}, c0);
+                bf[j][1] = cvt8(v2i{f[2], f[3]}, c0);
+                bf[j][2] = cvt8(v2i{f[4], f[5]}, c1);
+                bf[j][3] = cvt8(v2i{f[6], f[7]}, c1);
+            }
 #pragma unroll
-                for (int j = 0; j < FN; ++j) bf[j] = cvt8(lds_k8(sb + j * 16 * 128, t), (sb4[j] >> (8 * t)) & 0xFFu);
+            for (int i = 0; i < FM; ++i) {
+                const v8i f = lds_frag(sa + i * 16 * 128, lane);
+                const uint32_t c0 = (sa4[i] >> (8 * b0)) & 0xFFu, c1 = (sa4[i] >> (8 * b1)) & 0xFFu;
+                const v8bf af[4] = {cvt8(v2i{f[0], f[1]}, c0), cvt8(v2i{f[2], f[3]}, c0),
+                                    cvt8(v2i{f[4], f[5]}, c1), cvt8(v2i{f[6], f[7]}, c1)};
 #pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    const v8bf af = cvt8(lds_k8(sa + i * 16 * 128, t), (sa4[i] >> (8 * t)) & 0xFFu);
+                for (int v = 0; v < 4; ++v)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af, acc[i][j], 0, 0, 0);
-                }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j][v], af[v], acc[i][j], 0, 0, 0);
             }
             return;
         }
