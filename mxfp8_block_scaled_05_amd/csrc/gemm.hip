@@ -315,7 +315,58 @@ struct TileOps {
 
     // global -> LDS copies of k-step ks into stage st (this wave's share)
     __device__ __forceinline__ void issue(int ks, int st) const { issue_at(ks, lds0 + st * STAGE); }
-    // the same into the stage at LDS byte address sbase
+    // The copies of a 256-row tile with the two-stage ring are issued by
+    // waves 0-3 only (one per SIMD; waves w and w + 4 share a SIMD): issuing
+    // a step's 48-64 KB of copies stalls the issuing wave for ~1300-1900
+    // clocks while the address unit drains, and this way the other wave of
+    // each SIMD starts its MFMAs at once instead of both stalling.
+    // Measured (MI355X, 8192x24576x4096 / 8192x4096x12288): 746 -> 716 us
+    // and 367 -> 353 us, bit-identical.  (Even waves as copiers, i.e. both
+    // waves of two SIMDs: slower.)  Three-stage rings keep every wave's
+    // share, since their waits count each wave's own copies.
+    static constexpr bool kCopiers = BM == 256 && (BN == 256 || BN == 128);
+    __device__ __forceinline__ void issue_copiers(int ks, uint32_t sbase) const {
+        if (w >= 4) return;
+        const int cw = w;
+#pragma unroll
+        for (int i = 0; i < BM / 32; ++i) {
+            const int seg = i * 4 + cw;
+            const int rr = seg * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
+            const int kk = ks * 128 + c * 16;
+            const uint32_t off = kk < Ki ? (uint32_t)(rr * lda + kk) : kOOB;
+            dma16(ra, off, sbase + seg * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < BN / 32; ++i) {
+            const int seg = i * 4 + cw;
+            uint32_t off;
+            if constexpr (BPACK) {
+                off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
+            } else {
+                const int rr = seg * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
+                const int kk = ks * 128 + c * 16;
+                off = kk < Ki ? (uint32_t)(rr * ldb + kk) : kOOB;
+            }
+            dma16(rb, off, sbase + BM * 128 + seg * 1024);
+        }
+        if constexpr (SA_LDS) dma4(rsa, (uint32_t)((cw * 64 + lane) * lsa + ks * 4), sbase + SA_OFF + cw * 256);
+        if constexpr (SB_LDS) {
+            if (cw < BN / 64) {
+                uint32_t off;
+                if constexpr (BPACK) off = (uint32_t)(ks * kScaleStepBytes + cw * 256 + lane * 4);
+                else off = (uint32_t)((cw * 64 + lane) * lsb + ks * 4);
+                dma4(rsb, off, sbase + SB_OFF + cw * 256);
+            }
+        }
+    }
+    // copies of a step for the two-stage rings (whose waits are vmcnt(0))
+    __device__ __forceinline__ void issue2(int ks, uint32_t sbase) const {
+        if constexpr (kCopiers) issue_copiers(ks, sbase);
+        else issue_at(ks, sbase);
+    }
+    // the same into the stage at LDS byte address sbase, each wave its share
     __device__ __forceinline__ void issue_at(int ks, uint32_t sbase) const {
 #pragma unroll
         for (int i = 0; i < BM / (8 * kWaves); ++i) {
@@ -835,7 +886,8 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
         if constexpr (T::SBC) t.issue_sb_chunk(0, t.lds0 + NST * T::STAGE + 2 * T::CHUNK);
         if constexpr (T::SA_REG && !ACC) t.fetch_sa(0, sa_nxt);
         if constexpr (T::SB_REG && !ACC) t.fetch_sb(0, sb_nxt);
-        t.issue(0, 0);
+        if constexpr (NST == 2) t.issue2(0, t.lds0);
+        else t.issue(0, 0);
         if constexpr (NST == 3) {
             if (KS > 1) t.issue(1, 1);
         }
@@ -879,7 +931,7 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
             // before the barrier above
             if (ks + 2 < KS) t.issue(ks + 2, cur == 0 ? 2 : cur - 1);
         } else {
-            if (ks + 1 < KS) t.issue(ks + 1, cur ^ 1);
+            if (ks + 1 < KS) t.issue2(ks + 1, t.lds0 + (cur ^ 1) * T::STAGE);
         }
 
         const uint8_t *st = smem + cur * T::STAGE;
@@ -1067,7 +1119,7 @@ __device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, SAC> &
             if (ks % T::kChunkSteps == 0 && (c + 1) * T::kChunkSteps < KS)
                 t.issue_sa_chunk(c + 1, t.lds0 + ch_off + ((c + 1 + ch_par) & 1) * T::CHUNK);
         }
-        if (ks + 1 < KS) t.issue_at(ks + 1, t.lds0 + st_off[cur ^ 1]);
+        if (ks + 1 < KS) t.issue2(ks + 1, t.lds0 + st_off[cur ^ 1]);
         const uint8_t *st = smem + st_off[cur];
         int sas[FM], sbs[FN];
         t.lds_scales(st, sas, sbs, smem + ch_off + ((c + ch_par) & 1) * T::CHUNK, ks);
@@ -1111,7 +1163,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TB::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     tb.issue_sa_chunk(0, tb.lds0 + CH);
-    tb.issue_at(0, tb.lds0);
+    tb.issue2(0, tb.lds0);
     const uint32_t st_b[2] = {0u, SB};
     pair_loop<256, 256, 2>(tb, KS, smem, st_b, CH, 0, acc);
 
@@ -1121,7 +1173,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
     TS ts;
     ts.init(p, m2, p.M, n2, 0, smem);
     ts.issue_sa_chunk(0, ts.lds0 + CH + (1 - Lc) * TB::CHUNK);
-    ts.issue_at(0, ts.lds0 + F * SB);
+    ts.issue2(0, ts.lds0 + F * SB);
 
     __syncthreads();                         // every wave is done with the first tile's stages
     {
@@ -1197,7 +1249,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_persist_kernel(GemmP
     T t;
     t.init(p, m0, m_end, n0, g, smem);
     if constexpr (SAC) t.issue_sa_chunk(0, t.lds0 + CH);
-    t.issue_at(0, t.lds0);
+    t.issue2(0, t.lds0);
     uint32_t st[2] = {0u, SB};
     int ch_par = 0;
     while (true) {
@@ -1223,7 +1275,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_persist_kernel(GemmP
         if (more) {
             t2.init(p, nm0, nm_end, nn0, ng, smem);
             if constexpr (SAC) t2.issue_sa_chunk(0, t2.lds0 + CH + c_free * T::CHUNK);
-            t2.issue_at(0, t2.lds0 + st_free);
+            t2.issue2(0, t2.lds0 + st_free);
         }
         __syncthreads();                     // every wave is done with the finished tile's stages
         {
