@@ -791,19 +791,40 @@ __device__ __forceinline__ void store_tile_scalar(const GemmParams &p, int64_t r
 // waves fit the LDS the main loop used.  Callers sync before (the stages are
 // reused) and use this only for tiles whose columns are inside C with
 // 16-byte aligned rows; rows at or past m_end are not written.
-template <int FM, int FN, bool OUT_BF16, int LDS_BYTES>
-__device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0, int64_t col0, int64_t m_end,
+//
+// The stores are buffer stores over this wave's rows of C that exist (rows
+// at or past m_end fall outside the descriptor and are dropped), so every
+// wave issues exactly store_tile_lds_count() of them whatever m_end is, and
+// a caller may wait for VMEM operations issued before them with
+// vmcnt(count) (vector memory operations complete in issue order), leaving
+// the stores to drain behind its next work.  Returns false (pointer stores,
+// count not exact) when the wave's block spans 4 GiB or more of C.
+template <int FM, int FN, bool OUT_BF16, int LDS_BYTES, int NW = kWaves>
+struct EpilogueShape {
+    static constexpr int ES = OUT_BF16 ? 2 : 4;
+    static constexpr int WTM = FM * 16, WTN = FN * 16;
+    static constexpr int ROWB = WTN * ES + 16;                       // padded LDS row
+    static constexpr int PR0 = LDS_BYTES / (NW * ROWB);              // rows per pass that fit
+    static constexpr int PR = PR0 >= WTM ? WTM : (PR0 >= 64 ? 64 : (PR0 >= 32 ? 32 : 16));
+    static_assert(PR >= 16 && WTM % PR == 0 && NW * PR * ROWB <= LDS_BYTES, "epilogue LDS");
+    static constexpr int LPR = WTN * ES / 16;                         // lanes per row (16 B each)
+    static constexpr int RPI = 64 / LPR;                              // rows per store instruction
+    static constexpr int kStores = WTM / RPI;                         // store instructions per wave
+};
+template <int FM, int FN, bool OUT_BF16, int LDS_BYTES, int NW = kWaves>
+__device__ __forceinline__ bool store_tile_lds(const GemmParams &p, int64_t row0, int64_t col0, int64_t m_end,
                                v4f (*acc)[FN], int lane, int w, uint8_t *smem) {
-    constexpr int ES = OUT_BF16 ? 2 : 4;
-    constexpr int WTM = FM * 16, WTN = FN * 16;
-    constexpr int ROWB = WTN * ES + 16;                       // padded LDS row
-    constexpr int PR0 = LDS_BYTES / (kWaves * ROWB);          // rows per pass that fit
-    constexpr int PR = PR0 >= WTM ? WTM : (PR0 >= 64 ? 64 : (PR0 >= 32 ? 32 : 16));
-    static_assert(PR >= 16 && WTM % PR == 0 && kWaves * PR * ROWB <= LDS_BYTES, "epilogue LDS");
-    constexpr int LPR = WTN * ES / 16;                         // lanes per row (16 B each)
-    constexpr int RPI = 64 / LPR;                              // rows per store instruction
+    using E = EpilogueShape<FM, FN, OUT_BF16, LDS_BYTES, NW>;
+    constexpr int ES = E::ES, WTN = E::WTN, WTM = E::WTM, ROWB = E::ROWB, PR = E::PR, LPR = E::LPR,
+                  RPI = E::RPI;
     uint8_t *cw = smem + w * PR * ROWB;
     const int64_t N = p.N;
+    const bool counted = (int64_t)WTM * N * ES <= 0xFFFFFFFFll;
+    const int64_t rows_here = m_end - row0;
+    const uint32_t range = rows_here <= 0 ? 0u
+                           : (uint32_t)((min(rows_here, (int64_t)WTM) - 1) * N * ES + WTN * ES);
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc(static_cast<uint8_t *>(p.c) + (rows_here > 0 ? (row0 * N + col0) * ES : 0), range);
 #pragma unroll
     for (int pass = 0; pass < WTM / PR; ++pass) {
         // scatter this pass's rows (16-row MFMA tiles i in [pass*PR/16, ...)):
@@ -829,11 +850,17 @@ __device__ __forceinline__ void store_tile_lds(const GemmParams &p, int64_t row0
             const int rl = r0 + lane / LPR;
             const int cb = (lane % LPR) * 16;
             const v4i v = *reinterpret_cast<const v4i *>(cw + rl * ROWB + cb);
-            const int64_t row = row0 + pass * PR + rl;
-            uint8_t *dst = static_cast<uint8_t *>(p.c) + (row * N + col0) * ES + cb;
-            if (row < m_end) *reinterpret_cast<v4i *>(dst) = v;
+            if (counted) {
+                const uint32_t off = (uint32_t)(pass * PR + rl) * (uint32_t)(N * ES) + (uint32_t)cb;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, 0);
+            } else {
+                const int64_t row = row0 + pass * PR + rl;
+                uint8_t *dst = static_cast<uint8_t *>(p.c) + (row * N + col0) * ES + cb;
+                if (row < m_end) *reinterpret_cast<v4i *>(dst) = v;
+            }
         }
     }
+    return counted;
 }
 
 // ---------------------------------------------------------------- 2 stages
@@ -1104,7 +1131,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
 // offsets st_off[0..1] of smem, chunked A scales (K % 512 == 0, packed B) in
 // the two chunk buffers at ch_off, chunk c in buffer (c + ch_par) & 1.  Step
 // 0's copies and chunk 0 are issued by the caller (into st_off[0] and buffer
-// ch_par); the loop issues everything after them.
+// ch_par), which also waits for them and syncs before the call; the loop
+// issues and waits for everything after them.
 template <int BM, int BN, int WM, bool SAC = true>
 __device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, SAC> &t, int KS, uint8_t *smem,
                                           const uint32_t *st_off, uint32_t ch_off, int ch_par,
@@ -1113,7 +1141,7 @@ __device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, SAC> &
     constexpr int FM = T::FM, FN = T::FN;
     int cur = 0;
     for (int ks = 0; ks < KS; ++ks) {
-        wait_copies_and_sync();
+        if (ks) wait_copies_and_sync();    // step ks's copies (step 0: the caller's wait)
         const int c = ks / T::kChunkSteps;
         if constexpr (SAC) {
             if (ks % T::kChunkSteps == 0 && (c + 1) * T::kChunkSteps < KS)
@@ -1164,6 +1192,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
         for (int j = 0; j < TB::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     tb.issue_sa_chunk(0, tb.lds0 + CH);
     tb.issue2(0, tb.lds0);
+    wait_copies_and_sync();
     const uint32_t st_b[2] = {0u, SB};
     pair_loop<256, 256, 2>(tb, KS, smem, st_b, CH, 0, acc);
 
@@ -1179,13 +1208,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
     {
         const int64_t row0 = m0 + tb.wm * TB::WTM, col0 = n0 + tb.wn * TB::WTN;
         constexpr int ES = OUT_BF16 ? 2 : 4;
+        bool counted = false;
         if (n0 + 256 <= p.N && (p.N * ES) % 16 == 0)
-            store_tile_lds<TB::FM, TB::FN, OUT_BF16, (int)SB>(p, row0, col0, p.M, acc, tb.lane, tb.w,
-                                                              smem + (1 - F) * SB);
+            counted = store_tile_lds<TB::FM, TB::FN, OUT_BF16, (int)SB>(p, row0, col0, p.M, acc, tb.lane, tb.w,
+                                                                        smem + (1 - F) * SB);
         else
             store_tile_scalar<TB::FM, TB::FN, OUT_BF16>(p, row0, col0, p.M, acc, tb.lane);
+        // the second tile's first copies have landed; the stores issued after
+        // them may still be in flight
+        if (counted) __builtin_amdgcn_s_waitcnt(waitcnt_vm(EpilogueShape<TB::FM, TB::FN, OUT_BF16, (int)SB>::kStores));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     }
-    __syncthreads();                         // the staging area is free again
+    __syncthreads();                         // the staging area is free again, step 0 visible
 
     // second tile: step 0 in stage F (issued), step 1 into the other stage
     v4f acc2[TS::FM][TS::FN];
@@ -1250,6 +1284,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_persist_kernel(GemmP
     t.init(p, m0, m_end, n0, g, smem);
     if constexpr (SAC) t.issue_sa_chunk(0, t.lds0 + CH);
     t.issue2(0, t.lds0);
+    wait_copies_and_sync();
     uint32_t st[2] = {0u, SB};
     int ch_par = 0;
     while (true) {
@@ -1278,16 +1313,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_persist_kernel(GemmP
             t2.issue2(0, t2.lds0 + st_free);
         }
         __syncthreads();                     // every wave is done with the finished tile's stages
+        bool counted = false;
         {
             constexpr int ES = OUT_BF16 ? 2 : 4;
             if (n0 + 256 <= p.N && (p.N * ES) % 16 == 0)
-                store_tile_lds<T::FM, T::FN, OUT_BF16, (int)SB>(p, row0, col0, mend, acc, t.lane, t.w,
-                                                               smem + st_busy);
+                counted = store_tile_lds<T::FM, T::FN, OUT_BF16, (int)SB>(p, row0, col0, mend, acc, t.lane,
+                                                                         t.w, smem + st_busy);
             else
                 store_tile_scalar<T::FM, T::FN, OUT_BF16>(p, row0, col0, mend, acc, t.lane);
         }
         if (!more) break;
-        __syncthreads();                     // the staging stage is free again
+        // the next tile's first copies have landed; the finished tile's
+        // stores, issued after them, drain behind the next tile's steps
+        if (counted) __builtin_amdgcn_s_waitcnt(waitcnt_vm(EpilogueShape<T::FM, T::FN, OUT_BF16, (int)SB>::kStores));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();                     // the staging stage is free again, step 0 visible
         t = t2;
         m0 = nm0; m_end = nm_end; n0 = nn0; g = ng;
         st[0] = st_free;

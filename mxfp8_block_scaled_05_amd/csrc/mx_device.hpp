@@ -60,12 +60,15 @@ __device__ __forceinline__ int cvt2_e4m3(float a, float b, int old) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
-// fp32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.  Both
+// results are computed and one selected: written with an early return, the
+// NaN test became a branch around every conversion (exec-mask juggling per
+// element), which made the GEMM epilogues several times slower.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = float_to_bits(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    const uint32_t u = float_to_bits(f);
+    const uint32_t rne = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t qnan = ((u >> 16) | 0x40u) & 0xFFFFu;
+    return (u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rne;
 }
 
 // XOR swizzle of the 16-byte chunk slots inside a 128-byte LDS row: chunk c

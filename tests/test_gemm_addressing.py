@@ -156,6 +156,53 @@ def test_grouped_descriptors_inside_buffers(G, N, K, offsets):
             check_tile(M_total, N, K, BM, BN, True, G=G, m0=m0, m_end=m_end, n0=tn * BN, g=g)
 
 
+def check_epilogue_stores(M, N, BM, BN, WM, m0, m_end, n0, es):
+    """Mirror of store_tile_lds's buffer stores: each wave's descriptor starts
+    at its first row of C and spans its rows below m_end; every store of a
+    row below m_end lies inside it, every store of a row at or past m_end lies
+    past it (dropped), and the descriptor lies inside C (M x N elements)."""
+    WN = WAVES // WM
+    WTM, WTN = BM // WM, BN // WN
+    if not (n0 + BN <= N and (N * es) % 16 == 0):
+        return                                  # the element-by-element path
+    if WTM * N * es > 0xFFFFFFFF:
+        return                                  # pointer stores (count not exact)
+    lpr = WTN * es // 16
+    for w in range(WAVES):
+        row0, col0 = m0 + (w // WN) * WTM, n0 + (w % WN) * WTN
+        rows_here = m_end - row0
+        if rows_here <= 0:
+            continue                            # range 0: every store dropped
+        base = (row0 * N + col0) * es
+        rng = (min(rows_here, WTM) - 1) * N * es + WTN * es
+        assert 0 <= base and base + rng <= M * N * es, (M, N, m0, m_end, n0, w)
+        # offsets grow with the row and the lane: the extreme stores decide
+        last = min(rows_here, WTM) - 1                 # last row below m_end
+        assert last * N * es + (lpr - 1) * 16 + 16 <= rng
+        assert (WTM - 1) * N * es + (lpr - 1) * 16 < 2 ** 32
+        if rows_here < WTM:                            # first row at m_end: dropped
+            assert rows_here * N * es >= rng
+
+
+@pytest.mark.parametrize("M,N,K", DENSE_SHAPES[:12])
+@pytest.mark.parametrize("es", [2, 4])
+def test_epilogue_store_descriptors(M, N, K, es):
+    for m0, n0, BM, BN in dense_tiles(M, N):
+        check_epilogue_stores(M, N, BM, BN, 2 if BN == 256 else 4, m0, M, n0, es)
+
+
+def test_epilogue_store_descriptors_grouped():
+    import workloads as wl
+    rng = np.random.default_rng(7)
+    route = wl.zipf_topk_routing(rng, 4096, 128, 8)
+    offsets, _, _ = wl.group_layout(route, 128)
+    M_total = int(offsets[-1])
+    for N in (1536, 2048):
+        for g, m0, m_end in grouped_tiles(offsets, M_total, 256):
+            for tn in range(ceil_div(N, 256)):
+                check_epilogue_stores(M_total, N, 256, 256, 2, m0, m_end, tn * 256, 2)
+
+
 def stage_bytes(BM, BN, packed, kalign):
     sa_lds, sb_lds = kalign, packed or kalign
     return (BM + BN) * 128 + (BM * 4 if sa_lds else 0) + (BN * 4 if sb_lds else 0)
