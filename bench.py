@@ -150,7 +150,7 @@ def bench_qkv(args, dev):
     M, K = 4096, wl.QWEN3_8B["hidden"]
     N = wl.QWEN3_8B["qkv"]
     d = wl.qkv(0, tokens=M)
-    per_set = (N * K + M * K) * 2 + (N * K + M * K) + N * K + M * N * 2
+    per_set = (N * K + M * K) * 2 + (N * K + M * K) + N * K + M * K + M * N * 2
     # 8 sets (1.6 GB): each op's inputs over the sets exceed the 256 MB
     # Infinity Cache, so back-to-back launches of one op over the sets read HBM
     R = max(8, int(np.ceil(600e6 / per_set)))
@@ -166,8 +166,12 @@ def bench_qkv(args, dev):
         w = mx.PackedWeight(torch.empty(mx.packed_bytes(1, N, K, 0), dtype=torch.uint8, device=dev),
                             torch.empty(mx.packed_bytes(1, N, K, 1), dtype=torch.uint8, device=dev),
                             1, N, K)
+        # X quantized straight into the GEMM's packed operand layout
+        a = mx.PackedWeight(torch.empty(mx.packed_bytes(1, M, K, 0), dtype=torch.uint8, device=dev),
+                            torch.empty(mx.packed_bytes(1, M, K, 1), dtype=torch.uint8, device=dev),
+                            1, M, K)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        sets.append((X, W, xq, xs, wq, ws, w, y))
+        sets.append((X, W, xq, xs, wq, ws, w, a, y))
     torch.cuda.synchronize()
     timer = KernelTimer()
 
@@ -178,15 +182,16 @@ def bench_qkv(args, dev):
         # around the GEMM only, 133 us with none), so the timed steps bracket
         # only the GEMM, whose live duration the roofline needs; the HBM-bound
         # kernels are timed in a pass of their own after the timed region.
-        X, W, xq, xs, wq, ws, w, y = sets[i % R]
+        X, W, xq, xs, wq, ws, w, a, y = sets[i % R]
         t = timer.time if "all" in timed else (lambda name, fn: fn())
-        # W and X quantized along K in one launch (mxfp8_quantize_many)
-        t("quantize_WX", lambda: mx.quantize_many_([(W, wq, ws), (X, xq, xs)]))
+        # W along K into its canonical grid and X along K straight into the
+        # GEMM's packed operand layout, one launch (mxfp8_quantize_many_layouts)
+        t("quantize_WX", lambda: mx.quantize_many_layouts_([(W, (wq, ws)), (X, a)]))
         t("repack_W", lambda: mx.repack_(wq, ws, w))
         if timed:
-            timer.time("gemm", lambda: mx.gemm(xq, xs, w, torch.bfloat16, out=y))
+            timer.time("gemm", lambda: mx.gemm_packed(a, w, torch.bfloat16, out=y))
         else:
-            mx.gemm(xq, xs, w, torch.bfloat16, out=y)
+            mx.gemm_packed(a, w, torch.bfloat16, out=y)
 
     # the settle phase rotates the input sets like the timed steps, so every
     # launch a kernel trace of this command averages reads from HBM
@@ -228,7 +233,7 @@ def bench_qkv(args, dev):
         mx.quantize_into(s[1], 1, s[4], s[5])
 
     def qwx(s):
-        mx.quantize_many_([(s[1], s[4], s[5]), (s[0], s[2], s[3])])
+        mx.quantize_many_layouts_([(s[1], (s[4], s[5])), (s[0], s[7])])
 
     def rp(s):
         mx.repack_(s[4], s[5], s[6])
@@ -254,11 +259,22 @@ def bench_qkv(args, dev):
     # the accurate GEMM (mxfp8_gemm_accurate: BF16 matrix instructions on
     # exactly converted operands) on the same rotated inputs, its own pass
     timer.reset()
+    for i in range(R):          # canonical X grids for the reference GEMM passes
+        X, W, xq, xs, wq, ws, w, a, y = sets[i]
+        mx.quantize_into(X, 1, xq, xs)
     for i in range(min(args.steps, 20)):
-        X, W, xq, xs, wq, ws, w, y = sets[i % R]
+        X, W, xq, xs, wq, ws, w, a, y = sets[i % R]
         timer.time("gemm_accurate", lambda: mx.gemm(xq, xs, w, torch.bfloat16, out=y, accurate=True))
+    # the step as it would be with X's canonical grid (mxfp8_quantize_many,
+    # mxfp8_gemm): events around the GEMM only, its inputs as fresh as above
+    for i in range(max(args.steps, 20)):
+        X, W, xq, xs, wq, ws, w, a, y = sets[i % R]
+        mx.quantize_many_([(W, wq, ws), (X, xq, xs)])
+        mx.repack_(wq, ws, w)
+        timer.time("gemm_canonical_A", lambda: mx.gemm(xq, xs, w, torch.bfloat16, out=y))
     torch.cuda.synchronize()
     acc_us = timer.averages_us()["gemm_accurate"]
+    can_us = timer.averages_us()["gemm_canonical_A"]
     ms_per_step = 1e3 * wall / args.steps
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (avg["gemm"] * 1e-6) / 1e12
@@ -272,11 +288,14 @@ def bench_qkv(args, dev):
                  "us_with_events_around_every_op": round(avg_all["gemm"], 2)},
     }
     kern["gemm_accurate"] = _gemm_rate(acc_us, M, N, K)
+    kern["gemm_canonical_A"] = _gemm_rate(can_us, M, N, K)
+    kern["gemm_canonical_A"]["note"] = ("mxfp8_gemm on X's canonical grid (its copies gather 8 rows per "
+                                        "instruction) in the same step with mxfp8_quantize_many, for reference")
     kern["gemm"]["median_us"] = round(med["gemm"], 2)
     for k in ("quantize_WX", "repack_W"):
         kern[k]["us_events_around_each_launch"] = round(avg_all[k], 2)
     kern["quantize_W"]["note"] = kern["quantize_X"]["note"] = \
-        "one tensor per launch (mxfp8_quantize), for reference; the step quantizes both in one launch"
+        "one tensor per launch into its canonical grid (mxfp8_quantize), for reference; the step quantizes both in one launch"
     kern["repack_W"]["us_cold_input"] = round(batch["repack_W_cold"], 2)
     # context for the HBM-bound kernels: a plain copy of the same bytes, cold
     for k, nbytes in (("quantize_WX", (N + M) * K * Q_BYTES_PER_ELT), ("quantize_W", N * K * Q_BYTES_PER_ELT),
@@ -296,8 +315,9 @@ def bench_qkv(args, dev):
         "vs_baseline": None,
         "dtype": "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out",
         "data": "synthetic (seeded N(0,1) activations with 1% x20 outliers, N(0,0.02) weights)",
-        "config": {"workload": "qwen3-8b qkv_proj: quantize W[6144x4096] + X[4096x4096] along K (one "
-                               "mxfp8_quantize_many launch), repack W, MXFP8 GEMM -> bf16",
+        "config": {"workload": "qwen3-8b qkv_proj: quantize W[6144x4096] (canonical grid) + X[4096x4096] (the "
+                               "GEMM's packed operand layout) along K in one mxfp8_quantize_many_layouts launch, "
+                               "repack W, MXFP8 GEMM (mxfp8_gemm_packed) -> bf16",
                    "M": M, "N": N, "K": K, "rotated_sets": R},
         "kernels": kern,
         "kernels_note": "gemm: HIP events around every GEMM launch of the timed steps; quantize and "
@@ -305,7 +325,7 @@ def bench_qkv(args, dev):
                         "events, per launch (repack_W: a batch of quantize_WX + repack_W pairs less the "
                         "quantize_WX batch, since in the step repack reads the grid just written; "
                         "us_events_around_each_launch: events around every op of min(steps, 100) steps); "
-                        "gemm_accurate: mxfp8_gemm_accurate in a pass of its own" % (4 * R, R),
+                        "gemm_accurate, gemm_canonical_A: passes of their own" % (4 * R, R),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": MXFP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / MXFP8_PEAK_TFLOPS, 4),
                      "traffic": measured_gemm_traffic()},

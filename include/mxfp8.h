@@ -190,13 +190,46 @@ typedef struct {
  */
 mxfp8_status mxfp8_quantize_many(const mxfp8_quant_job *jobs, int64_t count, hipStream_t stream);
 
+/* One tensor of an mxfp8_quantize_many_layouts call: BF16 [rows][cols]
+ * quantized along its columns (axis 1) into the given layout. */
+typedef struct {
+    const void *x_bf16;        /* BF16 [rows][cols]                                */
+    int64_t rows, cols;
+    mxfp8_layout layout;       /* MXFP8_CANONICAL or MXFP8_PACKED                  */
+    uint8_t *q, *scales;       /* canonical: q[rows][cols], scales[rows][cols/32];
+                                  packed: the mxfp8_repack layout of that grid
+                                  (mxfp8_packed_bytes(1, rows, cols, 0 / 1) bytes) */
+} mxfp8_quant_layout_job;
+
+/*
+ * mxfp8_quantize_many_layouts -- mxfp8_quantize_many with a layout per
+ * tensor.
+ *
+ * A canonical entry writes exactly what mxfp8_quantize(axis = 1) writes; a
+ * packed entry writes exactly the bytes mxfp8_repack writes for that
+ * canonical grid (padding rows and blocks included).  Why: a linear layer's
+ * activations quantized straight into the GEMM's operand layout for
+ * mxfp8_gemm_packed, in the same launch as its weights' canonical grid.  The
+ * packed entries are walked in steps of 16 rows x 128 columns, so each
+ * step's codes land as 2 KB of one packed tile and its scales as one 64-byte
+ * record.  jobs: HOST array of `count` entries (1 <= count <=
+ * MXFP8_QUANT_JOBS_MAX), each validated as mxfp8_quantize(axis = 1)
+ * validates its arguments, plus: layout one of the two values
+ * (MXFP8_ERR_DTYPE), a packed entry's tiles as mxfp8_repack limits them and
+ * its steps (ceil(rows / 256) * 16 * ceil(cols / 128)) below 2^31.
+ * Entries must not overlap in memory.  The array is read during the call
+ * only.  Bit-exact, deterministic.
+ */
+mxfp8_status mxfp8_quantize_many_layouts(const mxfp8_quant_layout_job *jobs, int64_t count,
+                                         hipStream_t stream);
+
 /* One weight of an mxfp8_quantize_packed_many call: the arguments of
  * mxfp8_quantize_packed for that weight. */
 typedef struct {
     const void *w_bf16;        /* BF16 [batch][rows][cols]                         */
     int64_t batch, rows, cols;
     uint8_t *q, *scales;       /* canonical grid, or both NULL                     */
-    uint8_t *q_packed, *scales_packed;
+    uint8_t *q_packed, *scales_packed;   /* packed layout, or both NULL            */
 } mxfp8_packed_job;
 
 #define MXFP8_PACKED_JOBS_MAX 32
@@ -210,9 +243,12 @@ typedef struct {
  * launch ramp and tail per weight, which costs most on the smaller
  * projections.  jobs: HOST array of `count` entries (1 <= count <=
  * MXFP8_PACKED_JOBS_MAX), each validated as mxfp8_quantize_packed validates
- * its arguments; the tiles of all entries together must stay below 2^24
- * (batch * ceil(rows/256) * ceil(cols/128) summed over the list).  The output
- * of every entry is exactly what mxfp8_quantize_packed writes for it; entries
+ * its arguments, except that an entry may leave both packed pointers NULL
+ * when it gives the canonical grid (then it writes that grid only; an entry
+ * with neither output is MXFP8_ERR_NULL); the tiles of all entries together
+ * must stay below 2^24 (batch * ceil(rows/256) * ceil(cols/128) summed over
+ * the list).  The output of every entry is exactly what mxfp8_quantize_packed
+ * (or, canonical only, mxfp8_quantize(axis = 1)) writes for it; entries
  * must not overlap in memory.  The array is read during the call only (its
  * contents are passed by value to the kernel, so a captured graph keeps
  * them).  Bit-exact, deterministic.
@@ -357,6 +393,28 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s,
                         const uint8_t *b_q, const uint8_t *b_s,
                         mxfp8_layout b_layout, int64_t M, int64_t N, int64_t K,
                         void *c, mxfp8_dtype c_dtype, hipStream_t stream);
+
+/*
+ * mxfp8_gemm_packed -- mxfp8_gemm with A in the packed layout as well.
+ *
+ * Same result definition as mxfp8_gemm (bit-identical output for the same
+ * operands).  A (a_q, a_s) is the packed layout of q[M][K], s[M][K/32]
+ * (the layout mxfp8_repack describes, with M in place of N): written by
+ * mxfp8_quantize_packed straight from BF16 activations, or by mxfp8_repack
+ * of a canonical grid.  B (b_q, b_s) is packed as for mxfp8_gemm.  Why: the
+ * GEMM copies each k-step's operand tiles into LDS 1 KB per instruction; a
+ * canonical A tile is gathered 128 bytes from each of 8 rows K bytes apart,
+ * which the address unit issues at about half the rate of a contiguous 1 KB
+ * (measured on MI355X: 64 KB of such copies per CU take ~1920 clocks to
+ * issue against ~920), while every packed copy is contiguous.  Measured:
+ * 4096x6144x4096 101-114 -> 92-98 us, 8192x4096x12288 333-343 -> 312-320 us.
+ * M, N >= 1; K >= 128, K % 128 == 0; the five pointers 16-byte aligned.
+ * MXFP8_ERR_SHAPE otherwise (K % 128 != 0 included).  Deterministic.
+ */
+mxfp8_status mxfp8_gemm_packed(const uint8_t *a_q, const uint8_t *a_s,
+                               const uint8_t *b_q, const uint8_t *b_s,
+                               int64_t M, int64_t N, int64_t K,
+                               void *c, mxfp8_dtype c_dtype, hipStream_t stream);
 
 /*
  * mxfp8_gemm_accurate -- mxfp8_gemm with every product exact and the sums

@@ -70,6 +70,10 @@ def lib():
         L.mxfp8_gemm_splitk.restype = I32
         L.mxfp8_gemm_accurate.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
         L.mxfp8_gemm_accurate.restype = I32
+        L.mxfp8_gemm_packed.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
+        L.mxfp8_gemm_packed.restype = I32
+        L.mxfp8_quantize_many_layouts.argtypes = [P, I64, P]
+        L.mxfp8_quantize_many_layouts.restype = I32
         L.mxfp8_gemm_splitk_noalloc.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
         L.mxfp8_gemm_splitk_noalloc.restype = I32
         L.mxfp8_gemm_splitk_workspace_bytes.argtypes = [I64, I64, I64]
@@ -100,6 +104,12 @@ class QuantJob(ctypes.Structure):
 
 
 QUANT_JOBS_MAX = 8
+
+
+class QuantLayoutJob(ctypes.Structure):
+    """mxfp8_quant_layout_job"""
+    _fields_ = [("x_bf16", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("layout", ctypes.c_int32), ("q", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
 class PackedJob(ctypes.Structure):
@@ -455,21 +465,68 @@ def quantize_many_(items) -> None:
         _check(lib().mxfp8_quantize_many(arr, len(chunk), stream), "mxfp8_quantize_many")
 
 
+def quantize_many_layouts_(items) -> None:
+    """Axis-1 quantize of a list of (x_bf16 [rows, cols], target) in one launch
+    (mxfp8_quantize_many_layouts, up to QUANT_JOBS_MAX entries): target is a
+    canonical (q, s) pair, or a PackedWeight (batch 1, N = rows, K = cols)
+    that receives the packed layout (the operand layout of gemm_packed)."""
+    items = list(items)
+    if not items or len(items) > QUANT_JOBS_MAX:
+        raise ValueError("1 to %d entries" % QUANT_JOBS_MAX)
+    jobs = []
+    for x, target in items:
+        _need(x, torch.bfloat16, "x")
+        if x.dim() != 2:
+            raise ValueError("x must be 2-D [rows, cols]")
+        rows, cols = x.shape
+        if x.device != items[0][0].device:
+            raise ValueError("all tensors must be on one device")
+        if isinstance(target, PackedWeight):
+            _need(target.q, torch.uint8, "q_packed")
+            _need(target.s, torch.uint8, "scales_packed")
+            if (target.batch, target.N, target.K) != (1, rows, cols):
+                raise ValueError("packed target must be PackedWeight(batch 1, N = rows, K = cols)")
+            if target.q.numel() < packed_bytes(1, rows, cols, 0) or target.s.numel() < packed_bytes(1, rows, cols, 1):
+                raise ValueError("packed buffers too small")
+            jobs.append(QuantLayoutJob(x.data_ptr(), rows, cols, MXFP8_PACKED, target.q.data_ptr(),
+                                       target.s.data_ptr()))
+        else:
+            q, s = target
+            _need(q, torch.uint8, "q")
+            _need(s, torch.uint8, "scales")
+            if tuple(q.shape) != (rows, cols) or tuple(s.shape) != (rows, cols // 32):
+                raise ValueError("q/scales shapes do not match x")
+            jobs.append(QuantLayoutJob(x.data_ptr(), rows, cols, MXFP8_CANONICAL, q.data_ptr(), s.data_ptr()))
+    arr = (QuantLayoutJob * len(jobs))(*jobs)
+    _check(lib().mxfp8_quantize_many_layouts(arr, len(jobs), _stream(items[0][0].device)),
+           "mxfp8_quantize_many_layouts")
+
+
 def quantize_packed_many_(items) -> None:
-    """quantize_packed_ over a list of (w_bf16, PackedWeight, q or None, s or
-    None) in launches of up to PACKED_JOBS_MAX weights (mxfp8_quantize_packed_many),
-    all on the current stream of the first weight's device."""
+    """quantize_packed_ over a list of (w_bf16, PackedWeight or None, q or
+    None, s or None) in launches of up to PACKED_JOBS_MAX weights
+    (mxfp8_quantize_packed_many), all on the current stream of the first
+    weight's device.  An entry without a PackedWeight writes only its
+    canonical grid (q and s given)."""
     items = list(items)
     jobs = []
     for w_bf16, out, q, s in items:
         _need(w_bf16, torch.bfloat16, "w")
-        _need(out.q, torch.uint8, "q_packed")
-        _need(out.s, torch.uint8, "scales_packed")
-        if w_bf16.numel() != out.batch * out.N * out.K:
-            raise ValueError("weights do not match the packed weight's shape")
-        if out.q.numel() < packed_bytes(out.batch, out.N, out.K, 0) or \
-                out.s.numel() < packed_bytes(out.batch, out.N, out.K, 1):
-            raise ValueError("packed buffers too small")
+        if out is None:
+            if q is None:
+                raise ValueError("an entry needs the packed layout, the canonical grid, or both")
+            shape = tuple(w_bf16.shape)
+            if len(shape) not in (2, 3):
+                raise ValueError("weights must be [N, K] or [batch, N, K]")
+            batch, (N, K) = (1, shape) if len(shape) == 2 else (shape[0], shape[1:])
+        else:
+            _need(out.q, torch.uint8, "q_packed")
+            _need(out.s, torch.uint8, "scales_packed")
+            batch, N, K = out.batch, out.N, out.K
+            if w_bf16.numel() != batch * N * K:
+                raise ValueError("weights do not match the packed weight's shape")
+            if out.q.numel() < packed_bytes(batch, N, K, 0) or out.s.numel() < packed_bytes(batch, N, K, 1):
+                raise ValueError("packed buffers too small")
         if (q is None) != (s is None):
             raise ValueError("give both canonical q and scales, or neither")
         if q is not None:
@@ -479,10 +536,11 @@ def quantize_packed_many_(items) -> None:
                 raise ValueError("canonical q/scales have the wrong size")
         if w_bf16.device != items[0][0].device:
             raise ValueError("all weights must be on one device")
-        jobs.append(PackedJob(w_bf16.data_ptr(), out.batch, out.N, out.K,
+        jobs.append(PackedJob(w_bf16.data_ptr(), batch, N, K,
                               q.data_ptr() if q is not None else None,
                               s.data_ptr() if s is not None else None,
-                              out.q.data_ptr(), out.s.data_ptr()))
+                              out.q.data_ptr() if out is not None else None,
+                              out.s.data_ptr() if out is not None else None))
     if not jobs:
         return
     stream = _stream(items[0][0].device)
@@ -573,6 +631,31 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b, out_dtype=torch.bfloat16,
         return out
     _check(lib().mxfp8_gemm(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), layout, M, N, K,
                             _ptr(out), code, _stream(a_q.device)), "mxfp8_gemm")
+    return out
+
+
+def gemm_packed(a: PackedWeight, b: PackedWeight, out_dtype=torch.bfloat16,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = A[M, K] B[N, K]^T with both operands in the packed layout
+    (mxfp8_gemm_packed): A from quantize_packed / repack of [M, K] (a.N = M),
+    B a packed weight.  K % 128 == 0."""
+    for name, w in (("a", a), ("b", b)):
+        if not isinstance(w, PackedWeight) or w.batch != 1:
+            raise ValueError("%s must be a single packed [rows, K] matrix" % name)
+        _need(w.q, torch.uint8, name + ".q")
+        _need(w.s, torch.uint8, name + ".s")
+    if a.K != b.K:
+        raise ValueError("A and B must share K")
+    M, N, K = a.N, b.N, a.K
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.q.device)
+    else:
+        _need(out, out_dtype, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    _check(lib().mxfp8_gemm_packed(_ptr(a.q), _ptr(a.s), _ptr(b.q), _ptr(b.s), M, N, K, _ptr(out), code,
+                                   _stream(a.q.device)), "mxfp8_gemm_packed")
     return out
 
 

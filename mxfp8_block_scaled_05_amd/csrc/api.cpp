@@ -282,6 +282,46 @@ mxfp8_status mxfp8_quantize_many(const mxfp8_quant_job *jobs, int64_t count, hip
     return finish(launch_quantize_many(t, stream));
 }
 
+mxfp8_status mxfp8_quantize_many_layouts(const mxfp8_quant_layout_job *jobs, int64_t count,
+                                         hipStream_t stream) {
+    if (!jobs) return MXFP8_ERR_NULL;
+    if (count < 1 || count > MXFP8_QUANT_JOBS_MAX) return MXFP8_ERR_SHAPE;
+    QuantJobs t = {};
+    int64_t steps = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        const mxfp8_quant_layout_job &j = jobs[i];
+        if (!j.x_bf16 || !j.q || !j.scales) return MXFP8_ERR_NULL;
+        const int lay = raw(j.layout);
+        if (lay != MXFP8_CANONICAL && lay != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+        if (j.rows <= 0 || j.cols <= 0 || j.rows >= kMaxDim || j.cols >= kMaxDim || j.cols % 32)
+            return MXFP8_ERR_SHAPE;
+        if (!aligned16(j.x_bf16) || !aligned16(j.q) || !aligned16(j.scales)) return MXFP8_ERR_ALIGN;
+        const int64_t nblocks = j.rows * (j.cols / 32);
+        int64_t s;
+        if (lay == MXFP8_PACKED) {
+            if (j.cols > kMaxK || !repack_tiles_ok(1, j.rows, j.cols)) return MXFP8_ERR_SHAPE;
+            s = packed_panels(j.rows) * 16 * packed_ksteps(j.cols);
+            if (s >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+        } else {
+            s = (nblocks + 63) / 64;
+        }
+        steps += s;
+        if (steps >= ((int64_t)1 << 40)) return MXFP8_ERR_SHAPE;
+        t.x[i] = static_cast<const uint16_t *>(j.x_bf16);
+        t.q[i] = j.q;
+        t.s[i] = j.scales;
+        t.nblocks[i] = nblocks;
+        t.step_end[i] = steps;
+        t.rows[i] = j.rows;
+        t.cols[i] = j.cols;
+        t.packed[i] = lay == MXFP8_PACKED;
+    }
+    t.count = (int)count;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_many(t, stream));
+}
+
 mxfp8_status mxfp8_quantize_packed_many(const mxfp8_packed_job *jobs, int64_t count,
                                         hipStream_t stream) {
     if (!jobs) return MXFP8_ERR_NULL;
@@ -291,13 +331,15 @@ mxfp8_status mxfp8_quantize_packed_many(const mxfp8_packed_job *jobs, int64_t co
     int64_t tiles = 0;
     for (int64_t i = 0; i < count; ++i) {
         const mxfp8_packed_job &j = jobs[i];
-        if (!j.w_bf16 || !j.q_packed || !j.scales_packed) return MXFP8_ERR_NULL;
+        if (!j.w_bf16) return MXFP8_ERR_NULL;
         if ((j.q == nullptr) != (j.scales == nullptr)) return MXFP8_ERR_NULL;
+        if ((j.q_packed == nullptr) != (j.scales_packed == nullptr)) return MXFP8_ERR_NULL;
+        if (!j.q && !j.q_packed) return MXFP8_ERR_NULL;        // no output at all
         if (j.batch <= 0 || j.rows <= 0 || j.cols <= 0 || j.cols % 32) return MXFP8_ERR_SHAPE;
         if (j.rows >= kMaxDim || j.cols > kMaxK || j.batch > 65535 ||
             !repack_tiles_ok(j.batch, j.rows, j.cols))
             return MXFP8_ERR_SHAPE;
-        if (!aligned16(j.w_bf16) || !aligned16(j.q_packed) || !aligned16(j.scales_packed) ||
+        if (!aligned16(j.w_bf16) || (j.q_packed && (!aligned16(j.q_packed) || !aligned16(j.scales_packed))) ||
             (j.q && (!aligned16(j.q) || !aligned16(j.scales))))
             return MXFP8_ERR_ALIGN;
         tiles += j.batch * packed_panels(j.rows) * packed_ksteps(j.cols);
@@ -405,6 +447,21 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b
     if (st != MXFP8_OK) return st;
     return finish(launch_gemm(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
                               raw(c_dtype) == MXFP8_BF16, stream));
+}
+
+mxfp8_status mxfp8_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
+                               int64_t M, int64_t N, int64_t K, void *c, mxfp8_dtype c_dtype,
+                               hipStream_t stream) {
+    if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K < 128 || K % 128 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_gemm_packed(a_q, a_s, b_q, b_s, M, N, K, c, raw(c_dtype) == MXFP8_BF16, stream));
 }
 
 mxfp8_status mxfp8_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,

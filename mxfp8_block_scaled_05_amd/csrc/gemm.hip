@@ -230,7 +230,7 @@ __device__ int find_group(const int32_t *off, int G, int64_t M_total, int tm, in
 }
 
 // Per-tile state and the operations of one k-step, shared by both pipelines.
-template <int BM, int BN, int WM, bool BPACK, bool KALIGN, bool SAC = false>
+template <int BM, int BN, int WM, bool BPACK, bool KALIGN, bool SAC = false, bool APACK = false>
 struct TileOps {
     static constexpr int WN = kWaves / WM;
     static constexpr int WTM = BM / WM, WTN = BN / WN;       // wave tile
@@ -243,6 +243,10 @@ struct TileOps {
     // scales come instead from a chunk buffer outside the stage ring that
     // holds 8 k-steps of them (32 bytes per row), copied once per 8 steps.
     static_assert(!SAC || KALIGN, "chunked A scales need K % 128 == 0");
+    // APACK: A in the packed layout too (panels of 256 rows, each k-step's
+    // 32 KB tile contiguous, rows' 16-byte chunks already in their LDS slots;
+    // the step's scales a 1 KB per-lane tile), copied exactly as packed B
+    static_assert(!APACK || (BPACK && KALIGN && !SAC && BM == 256), "packed A: packed B, K % 128 == 0, 256-row tiles");
     static constexpr bool SA_LDS = KALIGN && !SAC;
     static constexpr bool SA_REG = !KALIGN;
     static constexpr int kChunkSteps = 8;
@@ -291,9 +295,20 @@ struct TileOps {
         // K range start to its last row's K range end): out-of-range lanes read 0
         const uint32_t a_bytes = (uint32_t)((rows_a - 1) * p.lda + K);
         const uint32_t as_bytes = (uint32_t)((rows_a - 1) * p.lsa + KB);
-        ra = make_srd(p.a_q + m0 * p.lda + kbase, a_bytes);
-        rsa = make_srd(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
-        rsa_c = make_rsrc(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
+        if constexpr (APACK) {
+            // A's panel m0 / 256 from k-step s0 on (m0 % 256 == 0: dense tiles)
+            const int64_t pa = m0 / kPanelRows, s0 = kbase / 128;
+            ra = make_srd(p.a_q + (pa * p.KS + s0) * kTileBytes, (uint32_t)((int64_t)(p.KS - s0) * kTileBytes));
+            rsa = make_srd(p.a_s + (pa * p.KS + s0) * kScaleStepBytes,
+                           (uint32_t)((int64_t)(p.KS - s0) * kScaleStepBytes));
+            rsa_c = make_rsrc(p.a_s, 0u);
+            (void)a_bytes;
+            (void)as_bytes;
+        } else {
+            ra = make_srd(p.a_q + m0 * p.lda + kbase, a_bytes);
+            rsa = make_srd(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
+            rsa_c = make_rsrc(p.a_s + m0 * p.lsa + kbase / 32, as_bytes);
+        }
         if constexpr (BPACK) {
             // packed B from k-step s0 = kbase / 128 of the panel on (kbase is a
             // multiple of 128 whenever B is packed)
@@ -331,10 +346,15 @@ struct TileOps {
 #pragma unroll
         for (int i = 0; i < BM / 32; ++i) {
             const int seg = i * 4 + cw;
-            const int rr = seg * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
-            const int kk = ks * 128 + c * 16;
-            const uint32_t off = kk < Ki ? (uint32_t)(rr * lda + kk) : kOOB;
+            uint32_t off;
+            if constexpr (APACK) {
+                off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
+            } else {
+                const int rr = seg * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
+                const int kk = ks * 128 + c * 16;
+                off = kk < Ki ? (uint32_t)(rr * lda + kk) : kOOB;
+            }
             dma16(ra, off, sbase + seg * 1024);
         }
 #pragma unroll
@@ -351,7 +371,8 @@ struct TileOps {
             }
             dma16(rb, off, sbase + BM * 128 + seg * 1024);
         }
-        if constexpr (SA_LDS) dma4(rsa, (uint32_t)((cw * 64 + lane) * lsa + ks * 4), sbase + SA_OFF + cw * 256);
+        if constexpr (APACK) dma4(rsa, (uint32_t)(ks * kScaleStepBytes + cw * 256 + lane * 4), sbase + SA_OFF + cw * 256);
+        else if constexpr (SA_LDS) dma4(rsa, (uint32_t)((cw * 64 + lane) * lsa + ks * 4), sbase + SA_OFF + cw * 256);
         if constexpr (SB_LDS) {
             if (cw < BN / 64) {
                 uint32_t off;
@@ -371,10 +392,15 @@ struct TileOps {
 #pragma unroll
         for (int i = 0; i < BM / (8 * kWaves); ++i) {
             const int seg = i * kWaves + w;            // 1 KB LDS segment = 8 rows
-            const int rr = seg * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
-            const int kk = ks * 128 + c * 16;
-            const uint32_t off = kk < Ki ? (uint32_t)(rr * lda + kk) : kOOB;
+            uint32_t off;
+            if constexpr (APACK) {
+                off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
+            } else {
+                const int rr = seg * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
+                const int kk = ks * 128 + c * 16;
+                off = kk < Ki ? (uint32_t)(rr * lda + kk) : kOOB;
+            }
             dma16(ra, off, sbase + seg * 1024);
         }
 #pragma unroll
@@ -395,7 +421,8 @@ struct TileOps {
         if constexpr (SA_LDS) {
             if (w < BM / 64) {
                 const int rr = w * 64 + lane;
-                dma4(rsa, (uint32_t)(rr * lsa + ks * 4), sbase + SA_OFF + w * 256);
+                if constexpr (APACK) dma4(rsa, (uint32_t)(ks * kScaleStepBytes + w * 256 + lane * 4), sbase + SA_OFF + w * 256);
+                else dma4(rsa, (uint32_t)(rr * lsa + ks * 4), sbase + SA_OFF + w * 256);
             }
         }
         if constexpr (SB_LDS) {
@@ -459,7 +486,10 @@ struct TileOps {
 #pragma unroll
             for (int j = 0; j < FN; ++j) sbs[j] = chunk_b[chunk_byte(wn * WTN + j * 16 + lrow, kb)];
         }
-        if constexpr (SA_LDS) {
+        if constexpr (APACK) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sas[i] = st[SA_OFF + (wm * FM + i) * 64 + lane];
+        } else if constexpr (SA_LDS) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) sas[i] = st[SA_OFF + (wm * WTM + i * 16 + lrow) * 4 + lblk];
         }
@@ -888,10 +918,11 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 // NST = 3 needs every copy to go through LDS (KALIGN) so that a wave's copy
 // count per step is fixed and the wait can leave the next steps in flight.
 template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool KALIGN, int NST, bool SAC = false,
-          bool ACC = false>
+          bool ACC = false, bool APACK = false>
 __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_end, int64_t n0, int64_t g,
                                           int64_t kbase, int64_t kbound, int KS, uint8_t *smem) {
-    using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
+    using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC, APACK>;
+    static_assert(!(APACK && ACC), "packed A on the fast path only");
     static_assert(!SAC || NST == 2, "chunked A scales with the two-stage ring");
     // SAC chunk buffers (two) after the stage ring, then (SBC) two for B
     uint8_t *chunks = smem + NST * T::STAGE;
@@ -1001,9 +1032,9 @@ __device__ __forceinline__ void gemm_tile(GemmParams &p, int64_t m0, int64_t m_e
 }
 
 template <int BM, int BN, int WM, bool BPACK, bool OUT_BF16, bool GROUPED, bool KALIGN, bool GK = false,
-          int NST = 2, bool SAC = false, bool ACC = false>
+          int NST = 2, bool SAC = false, bool ACC = false, bool APACK = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-    using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC>;
+    using T = TileOps<BM, BN, WM, BPACK, KALIGN, SAC, APACK>;
     constexpr int LDS = NST * T::STAGE + (SAC ? 2 * T::CHUNK + 2 * T::CHUNK_B : 0);
     static_assert(LDS <= 160 * 1024, "LDS budget");
     static_assert(!GK || (!BPACK && !KALIGN && !GROUPED), "grouped-K reads canonical operands");
@@ -1017,7 +1048,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     } else {
         if (!tile_of<BM, BN, GROUPED>(p, m0, m_end, n0, g)) return;
     }
-    gemm_tile<BM, BN, WM, BPACK, OUT_BF16, KALIGN, NST, SAC, ACC>(p, m0, m_end, n0, g, kbase, kbound, KS, smem);
+    gemm_tile<BM, BN, WM, BPACK, OUT_BF16, KALIGN, NST, SAC, ACC, APACK>(p, m0, m_end, n0, g, kbase, kbound, KS,
+                                                                          smem);
 }
 
 // Grouped-K (expert weight gradients) with T % 128 == 0: a tile whose token
@@ -1103,10 +1135,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // order, so they fill the chip's first wave and the small ones the tail.
 // Each range is renumbered XCD-aware on its own (mix_big is a multiple of 8,
 // so a workgroup's XCD is its id mod 8 in both).
-template <bool BPACK, bool OUT_BF16, bool KALIGN, bool SAC = false>
+template <bool BPACK, bool OUT_BF16, bool KALIGN, bool SAC = false, bool APACK = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
-    constexpr int SB = TileOps<256, 256, 2, BPACK, KALIGN, SAC>::STAGE;
-    constexpr int SS = TileOps<256, 128, 4, BPACK, KALIGN, SAC>::STAGE;
+    constexpr int SB = TileOps<256, 256, 2, BPACK, KALIGN, SAC, APACK>::STAGE;
+    constexpr int SS = TileOps<256, 128, 4, BPACK, KALIGN, SAC, APACK>::STAGE;
     constexpr int CH = SAC ? 2 * TileOps<256, 256, 2, BPACK, KALIGN, SAC>::CHUNK +
                                  2 * TileOps<256, 256, 2, BPACK, KALIGN, SAC>::CHUNK_B : 0;
     static_assert(2 * (SB > SS ? SB : SS) + CH <= 160 * 1024, "LDS budget");
@@ -1115,13 +1147,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
     int tm, tn;
     if (bid < p.mix_big) {
         grouped_order(xcd_logical(bid, p.mix_big), p.tiles_m, p.mix_big_cols, tm, tn);
-        gemm_tile<256, 256, 2, BPACK, OUT_BF16, KALIGN, 2, SAC>(p, (int64_t)tm * 256, p.M, (int64_t)tn * 256, 0,
-                                                                0, -1, p.KS, smem);
+        gemm_tile<256, 256, 2, BPACK, OUT_BF16, KALIGN, 2, SAC, false, APACK>(p, (int64_t)tm * 256, p.M,
+                                                                              (int64_t)tn * 256, 0, 0, -1, p.KS,
+                                                                              smem);
     } else {
         const int n_small = (int)gridDim.x - p.mix_big;
         const int small_cols = n_small / p.tiles_m;
         grouped_order(xcd_logical(bid - p.mix_big, n_small), p.tiles_m, small_cols, tm, tn);
-        gemm_tile<256, 128, 4, BPACK, OUT_BF16, KALIGN, 2, SAC>(p, (int64_t)tm * 256, p.M,
+        gemm_tile<256, 128, 4, BPACK, OUT_BF16, KALIGN, 2, SAC, false, APACK>(p, (int64_t)tm * 256, p.M,
                                                                 (int64_t)p.mix_big_cols * 256 + (int64_t)tn * 128,
                                                                 0, 0, -1, p.KS, smem);
     }
@@ -1133,11 +1166,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mixed_kernel(GemmParams p) {
 // 0's copies and chunk 0 are issued by the caller (into st_off[0] and buffer
 // ch_par), which also waits for them and syncs before the call; the loop
 // issues and waits for everything after them.
-template <int BM, int BN, int WM, bool SAC = true>
-__device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, SAC> &t, int KS, uint8_t *smem,
+template <int BM, int BN, int WM, bool SAC = true, bool APACK = false>
+__device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, SAC, APACK> &t, int KS, uint8_t *smem,
                                           const uint32_t *st_off, uint32_t ch_off, int ch_par,
-                                          v4f (*acc)[TileOps<BM, BN, WM, true, true, SAC>::FN]) {
-    using T = TileOps<BM, BN, WM, true, true, SAC>;
+                                          v4f (*acc)[TileOps<BM, BN, WM, true, true, SAC, APACK>::FN]) {
+    using T = TileOps<BM, BN, WM, true, true, SAC, APACK>;
     constexpr int FM = T::FM, FN = T::FN;
     int cur = 0;
     for (int ks = 0; ks < KS; ++ks) {
@@ -1166,10 +1199,12 @@ __device__ __forceinline__ void pair_loop(TileOps<BM, BN, WM, true, true, SAC> &
 // the epilogue stages C in the other stage only.  The second tile's loads
 // are then in flight while the first tile's C is written, instead of
 // starting after it as with one workgroup per tile.
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool APACK = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
-    using TB = TileOps<256, 256, 2, true, true, true>;
-    using TS = TileOps<256, 128, 4, true, true, true>;
+    // chunked A scales, or (APACK) A packed with its per-step scale tiles
+    constexpr bool SAC = !APACK;
+    using TB = TileOps<256, 256, 2, true, true, SAC, APACK>;
+    using TS = TileOps<256, 128, 4, true, true, SAC, APACK>;
     static_assert(TS::STAGE <= TB::STAGE && TS::CHUNK == TB::CHUNK, "small tile inside the large tile's regions");
     constexpr uint32_t SB = TB::STAGE, CH = 2 * TB::STAGE;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * TB::STAGE + 2 * TB::CHUNK];
@@ -1190,18 +1225,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
     for (int i = 0; i < TB::FM; ++i)
 #pragma unroll
         for (int j = 0; j < TB::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    tb.issue_sa_chunk(0, tb.lds0 + CH);
+    if constexpr (SAC) tb.issue_sa_chunk(0, tb.lds0 + CH);
     tb.issue2(0, tb.lds0);
     wait_copies_and_sync();
     const uint32_t st_b[2] = {0u, SB};
-    pair_loop<256, 256, 2>(tb, KS, smem, st_b, CH, 0, acc);
+    pair_loop<256, 256, 2, SAC, APACK>(tb, KS, smem, st_b, CH, 0, acc);
 
     // its last step read stage (KS-1)%2 and chunk buffer ((KS-1)/8)%2; the
     // other stage and buffer are free since the barrier of that step
     const int F = KS & 1, Lc = ((KS - 1) / TB::kChunkSteps) & 1;
     TS ts;
     ts.init(p, m2, p.M, n2, 0, smem);
-    ts.issue_sa_chunk(0, ts.lds0 + CH + (1 - Lc) * TB::CHUNK);
+    if constexpr (SAC) ts.issue_sa_chunk(0, ts.lds0 + CH + (1 - Lc) * TB::CHUNK);
     ts.issue2(0, ts.lds0 + F * SB);
 
     __syncthreads();                         // every wave is done with the first tile's stages
@@ -1228,7 +1263,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < TS::FN; ++j) acc2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     const uint32_t st_s[2] = {(uint32_t)F * SB, (uint32_t)(1 - F) * SB};
-    pair_loop<256, 128, 4>(ts, KS, smem, st_s, CH, 1 - Lc, acc2);
+    pair_loop<256, 128, 4, SAC, APACK>(ts, KS, smem, st_s, CH, 1 - Lc, acc2);
     {
         const int64_t row0 = m2 + ts.wm * TS::WTM, col0 = n2 + ts.wn * TS::WTN;
         constexpr int ES = OUT_BF16 ? 2 : 4;
@@ -1463,6 +1498,61 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     }
     p.tiles_n = d.small_cols;
     return launch_tile<256, 128, 4, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
+}
+
+// Both operands in the packed layout (A quantized straight into it, or
+// repacked): every copy of a k-step reads one contiguous 1 KB, where a
+// canonical A segment gathers 8 rows K bytes apart.  K % 128 == 0.  The same
+// tilings as launch_gemm.
+hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
+                              int64_t M, int64_t N, int64_t K, void *c, bool c_bf16, hipStream_t stream) {
+    GemmParams p{};
+    p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = c;
+    p.M = M; p.N = N; p.K = K;
+    p.KS = (int)packed_ksteps(K);
+    p.NP = (int)packed_panels(N);
+    p.G = 1;
+    p.offsets = nullptr;
+    p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
+    const int cus = device_cu_count();
+    const DenseTiling d = dense_tiling(M, N, cus);
+    p.tiles_m = (int)ceil_div(M, 256);
+    dim3 block(kThreads);
+    if (d.big_cols > 0 && d.small_cols > 0) {
+        p.tiles_n = d.big_cols + d.small_cols;
+        p.mix_big = p.tiles_m * d.big_cols;
+        p.mix_big_cols = d.big_cols;
+        if (d.small_cols == d.big_cols) {
+            dim3 grid((unsigned)p.mix_big);
+            if (c_bf16) hipLaunchKernelGGL((gemm_pair_kernel<true, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_pair_kernel<false, true>), grid, block, 0, stream, p);
+        } else {
+            dim3 grid((unsigned)(p.mix_big + p.tiles_m * d.small_cols));
+            if (c_bf16) hipLaunchKernelGGL((gemm_mixed_kernel<true, true, true, false, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_mixed_kernel<true, false, true, false, true>), grid, block, 0, stream, p);
+        }
+        return hipGetLastError();
+    }
+    if (d.big_cols > 0) {
+        p.tiles_n = d.big_cols;
+        dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+        if (c_bf16)
+            hipLaunchKernelGGL((gemm_kernel<256, 256, 2, true, true, false, true, false, 2, false, false, true>), grid,
+                               block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_kernel<256, 256, 2, true, false, false, true, false, 2, false, false, true>), grid,
+                               block, 0, stream, p);
+        return hipGetLastError();
+    }
+    p.tiles_n = d.small_cols;
+    dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    if (c_bf16)
+        hipLaunchKernelGGL((gemm_kernel<256, 128, 4, true, true, false, true, false, 2, false, false, true>), grid,
+                           block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<256, 128, 4, true, false, false, true, false, 2, false, false, true>), grid,
+                           block, 0, stream, p);
+    return hipGetLastError();
 }
 
 // Accurate path: 256x128 tiles (dense, XCD-aware order), both operands

@@ -75,6 +75,11 @@ struct QuantJobs {
     uint8_t *s[kQuantJobsMax];
     int64_t nblocks[kQuantJobsMax];
     int64_t step_end[kQuantJobsMax];
+    // packed[i]: q/s of job i are the packed layout of its grid; its steps are
+    // (16-row atom, k-step) pairs over ceil(rows / 256) * 16 atoms
+    int64_t rows[kQuantJobsMax];
+    int64_t cols[kQuantJobsMax];
+    int32_t packed[kQuantJobsMax];
     int count;
 };
 hipError_t launch_quantize_many(const QuantJobs &jobs, hipStream_t stream);
@@ -107,6 +112,8 @@ hipError_t launch_dequantize(const uint8_t *q, const uint8_t *scales, int64_t ro
 hipError_t launch_repack(const uint8_t *q, const uint8_t *scales, int64_t batch, int64_t N,
                          int64_t K, uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream);
 
+hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
+                              int64_t M, int64_t N, int64_t K, void *c, bool c_bf16, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                        const uint8_t *b_s, bool b_packed, int64_t M, int64_t N, int64_t K, void *c,
                        bool c_bf16, hipStream_t stream);

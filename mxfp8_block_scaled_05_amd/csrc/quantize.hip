@@ -150,6 +150,68 @@ __global__ __launch_bounds__(256) void quantize_axis1_kernel(const uint16_t *__r
     }
 }
 
+// The same walk writing the packed layout (the GEMM's operand layout, as
+// mxfp8_repack defines it): a step is one 16-row atom x one 128-column k-step
+// (64 blocks, 4 KB of BF16 as above), atom-major, over every atom of every
+// 256-row panel.  Sub-step h covers the atom's rows 8h .. 8h+7: lane l holds
+// half l % 2 of block (l / 2) % 4 of row 8h + l / 8, loaded as two 16-byte
+// pieces.  The step's codes are 16 rows x 128 bytes of one packed tile (each
+// row's 16-byte chunk c at slot c ^ (row % 8)), its 64 scale bytes the atom's
+// 64-byte per-lane record of that k-step; rows past `rows` and blocks past
+// cols / 32 are written as the layout's padding (codes 0, scale 127).
+// (steps of a packed job < 2^31, so the step index math is 32-bit)
+__device__ __forceinline__ void load_step_packed(const uint16_t *__restrict__ x, int64_t rows, int64_t cols,
+                                                 int KS, int st, int lane, uint32_t (*d)[4]) {
+    const int atom = st / KS, ks = st - atom * KS;
+    const int bl = lane >> 1, half = lane & 1, i = bl >> 2, kb4 = bl & 3;
+    const int kcol = ks * (int)kKStep + kb4 * 32 + half * 16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t r = (int64_t)atom * 16 + (u >> 1) * 8 + i;
+        const int k = kcol + (u & 1) * 8;
+        if (r < rows && k < cols) {
+            const v4i v = *reinterpret_cast<const v4i *>(x + r * cols + k);
+            d[u][0] = v.x; d[u][1] = v.y; d[u][2] = v.z; d[u][3] = v.w;
+        } else {
+            d[u][0] = d[u][1] = d[u][2] = d[u][3] = 0;
+        }
+    }
+}
+
+__device__ __forceinline__ void convert_step_packed(uint8_t *__restrict__ qp, uint8_t *__restrict__ sp,
+                                                    int64_t rows, int64_t cols, int KS, int st,
+                                                    int lane, uint32_t (*d)[4]) {
+    const int atom = st / KS, ks = st - atom * KS;
+    const int bl = lane >> 1, half = lane & 1, i = bl >> 2, kb4 = bl & 3;
+    const bool kvalid = ks * 4 + kb4 < (int)(cols / 32);
+    const int64_t tile_lin = (int64_t)(atom >> 4) * KS + ks;
+    const int arow0 = (atom & 15) * 16;
+    uint32_t code[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t m = max(max_mag(d[2 * h], 4), max_mag(d[2 * h + 1], 4));
+        m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, kQuadSwap1, 0xF, 0xF, false));
+        const bool valid = kvalid && (int64_t)atom * 16 + h * 8 + i < rows;
+        code[h] = valid ? scale_code_from_amax_bits(m) : 127u;
+    }
+    uint8_t *qtile = qp + tile_lin * kTileBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float inv = inv_scale_from_code(code[h]);
+        v2i o0 = convert8(d[2 * h], inv), o1 = convert8(d[2 * h + 1], inv);
+        v4i o = v4i{o0.x, o0.y, o1.x, o1.y};
+        if (code[h] == 255u) o = v4i{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+        const int rp = arow0 + h * 8 + i;              // row inside the panel
+        const int c = kb4 * 2 + half;                  // 16-byte chunk of the row's 128 bytes
+        *reinterpret_cast<v4i *>(qtile + rp * 128 + ((c ^ (int)swz((uint32_t)rp)) << 4)) = o;
+    }
+    // lane l stores the scale of row l % 16, block l / 16 of the step: held by
+    // lane 2 * (4 * (row % 8) + block) of sub-step row / 8
+    const int rr = lane & 15, src = 2 * ((rr & 7) * 4 + (lane >> 4));
+    const uint32_t s0 = __shfl(code[0], src), s1 = __shfl(code[1], src);
+    sp[tile_lin * kScaleStepBytes + (atom & 15) * 64 + lane] = (uint8_t)(rr < 8 ? s0 : s1);
+}
+
 // Several tensors in one launch: the wave-steps of tensor i are
 // step_end[i-1] .. step_end[i]-1 of one index space that the waves walk as
 // above; each step finds its tensor from the running step totals (uniform over
@@ -162,6 +224,10 @@ __device__ __forceinline__ int quant_job_of(const QuantJobs &jobs, int64_t step)
     return j;
 }
 
+// PACKED: some jobs write the packed layout.  That step needs about 18 more
+// registers, so it is a variant of its own, launched with 6 workgroups per CU;
+// a list of canonical jobs only keeps the leaner variant at 8 per CU.
+template <bool PACKED>
 __global__ __launch_bounds__(256) void quantize_axis1_many_kernel(QuantJobs jobs) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -170,18 +236,30 @@ __global__ __launch_bounds__(256) void quantize_axis1_many_kernel(QuantJobs jobs
     int64_t step = wave;
     if (step >= nsteps) return;
     uint32_t cur[4][4], nxt[4][4];
+    // a step of job jj, local index st, into registers d (the job is uniform
+    // over the wave, so the branch on its layout is too)
+    auto load = [&](int jj, int64_t st, uint32_t (*d)[4]) {
+        if (PACKED && jobs.packed[jj])
+            load_step_packed(jobs.x[jj], jobs.rows[jj], jobs.cols[jj], (int)((jobs.cols[jj] + kKStep - 1) / kKStep),
+                             (int)st, lane, d);
+        else
+            load_step(jobs.x[jj], st * 64, jobs.nblocks[jj], lane, d);
+    };
     int j = quant_job_of(jobs, step);
-    load_step(jobs.x[j], (step - (j ? jobs.step_end[j - 1] : 0)) * 64, jobs.nblocks[j], lane, cur);
+    load(j, step - (j ? jobs.step_end[j - 1] : 0), cur);
     for (; step < nsteps; step += nwaves) {
         const bool more = step + nwaves < nsteps;
         int jn = j;
         if (more) {
             jn = quant_job_of(jobs, step + nwaves);
-            load_step(jobs.x[jn], (step + nwaves - (jn ? jobs.step_end[jn - 1] : 0)) * 64, jobs.nblocks[jn],
-                      lane, nxt);
+            load(jn, step + nwaves - (jn ? jobs.step_end[jn - 1] : 0), nxt);
         }
-        convert_step(jobs.q[j], jobs.s[j], (step - (j ? jobs.step_end[j - 1] : 0)) * 64, jobs.nblocks[j],
-                     lane, cur);
+        const int64_t st = step - (j ? jobs.step_end[j - 1] : 0);
+        if (PACKED && jobs.packed[j])
+            convert_step_packed(jobs.q[j], jobs.s[j], jobs.rows[j], jobs.cols[j],
+                                (int)((jobs.cols[j] + kKStep - 1) / kKStep), (int)st, lane, cur);
+        else
+            convert_step(jobs.q[j], jobs.s[j], st * 64, jobs.nblocks[j], lane, cur);
         if (more) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -735,9 +813,11 @@ __device__ __forceinline__ void quantize_packed_tile(const uint16_t *__restrict_
             const v2i o0 = convert8(d, inv), o1 = convert8(d + 4, inv);
             out = v4i{o0.x, o0.y, o1.x, o1.y};
         }
-        v4i *pdst = reinterpret_cast<v4i *>(qtile + r * 128 + ((c ^ (int)swz((uint32_t)r)) << 4));
-        if constexpr (NT) __builtin_nontemporal_store(out, pdst);
-        else *pdst = out;
+        if (qp) {                          // uniform: a job without the packed layout skips it
+            v4i *pdst = reinterpret_cast<v4i *>(qtile + r * 128 + ((c ^ (int)swz((uint32_t)r)) << 4));
+            if constexpr (NT) __builtin_nontemporal_store(out, pdst);
+            else *pdst = out;
+        }
         if (qc && valid) {
             v4i *cdst = reinterpret_cast<v4i *>(qc + (b * N + n) * K + k);
             if constexpr (NT) __builtin_nontemporal_store(out, cdst);
@@ -748,7 +828,7 @@ __device__ __forceinline__ void quantize_packed_tile(const uint16_t *__restrict_
     }
     __syncthreads();
     // output word t: rows 16 (t/16) + 4 (t%4) .. +3 of block 4ks + (t/4)%4
-    if (t < kPanelRows) {
+    if (sp && t < kPanelRows) {
         const int row0 = 16 * (t >> 4) + 4 * (t & 3), j = (t >> 2) & 3;
         uint32_t o = 0;
 #pragma unroll
@@ -1010,11 +1090,15 @@ hipError_t launch_quantize(const uint16_t *x, int64_t rows, int64_t cols, int ax
 
 hipError_t launch_quantize_many(const QuantJobs &jobs, hipStream_t stream) {
     const int64_t nsteps = jobs.step_end[jobs.count - 1];
+    bool packed = false;
+    for (int i = 0; i < jobs.count; ++i) packed = packed || jobs.packed[i];
     int64_t grid = (nsteps + 3) / 4;
-    const int64_t cap = (int64_t)device_cu_count() * (kQuantWavesPerCu / 4);
+    // workgroups of 4 waves resident per CU: 8 (<= 64 registers), 6 with packed jobs (<= 80)
+    const int64_t cap = (int64_t)device_cu_count() * (packed ? 6 : kQuantWavesPerCu / 4);
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(quantize_axis1_many_kernel, dim3((unsigned)grid), dim3(256), 0, stream, jobs);
+    if (packed) hipLaunchKernelGGL(quantize_axis1_many_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, jobs);
+    else hipLaunchKernelGGL(quantize_axis1_many_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, jobs);
     return hipGetLastError();
 }
 

@@ -74,6 +74,15 @@ def test_argument_errors_before_any_device_work(libmx):
         args = [p, p, p, p, p]
         args[i] = q
         assert libmx.mxfp8_gemm(args[0], args[1], args[2], args[3], 1, 4, 4, 64, args[4], 0, NULL) == 5, i
+    # both operands packed: K a multiple of 128
+    assert libmx.mxfp8_gemm_packed(p, p, p, p, 4, 4, 64, p, 0, NULL) == 2          # K % 128
+    assert libmx.mxfp8_gemm_packed(p, p, p, p, 0, 4, 128, p, 0, NULL) == 2         # M
+    assert libmx.mxfp8_gemm_packed(p, p, p, p, 4, 4, 128, p, 9, NULL) == 4         # dtype
+    assert libmx.mxfp8_gemm_packed(NULL, p, p, p, 4, 4, 128, p, 0, NULL) == 1      # NULL
+    for i in range(5):
+        args = [p, p, p, p, p]
+        args[i] = q
+        assert libmx.mxfp8_gemm_packed(args[0], args[1], args[2], args[3], 4, 4, 128, args[4], 0, NULL) == 5, i
     assert libmx.mxfp8_dequantize(p, p, 4, 32, 1, p, 5, NULL) == 4
     assert libmx.mxfp8_repack(p, p, 1, 4, 40, p, p, NULL) == 2
     # fused quantizers
@@ -106,10 +115,32 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_quantize_many(qarr, 2, NULL) == 1                            # NULL q
     qarr[1] = QuantJob(p.value, 4, 64, q.value, p.value)
     assert libmx.mxfp8_quantize_many(qarr, 2, NULL) == 5                            # alignment
+    # multi-tensor axis-1 quantize with a layout per entry
+    from mxfp8_block_scaled_05_amd import QuantLayoutJob
+    lgood = QuantLayoutJob(p.value, 4, 64, 1, p.value, p.value)
+    larr = (QuantLayoutJob * 9)(*([lgood] * 9))
+    assert libmx.mxfp8_quantize_many_layouts(None, 1, NULL) == 1                    # NULL table
+    assert libmx.mxfp8_quantize_many_layouts(larr, 0, NULL) == 2                    # empty list
+    assert libmx.mxfp8_quantize_many_layouts(larr, 9, NULL) == 2                    # more than 8
+    larr[1] = QuantLayoutJob(p.value, 4, 64, 7, p.value, p.value)
+    assert libmx.mxfp8_quantize_many_layouts(larr, 2, NULL) == 4                    # layout value
+    larr[1] = QuantLayoutJob(p.value, 4, 40, 1, p.value, p.value)
+    assert libmx.mxfp8_quantize_many_layouts(larr, 2, NULL) == 2                    # cols % 32
+    larr[1] = QuantLayoutJob(p.value, 4, 64, 0, None, p.value)
+    assert libmx.mxfp8_quantize_many_layouts(larr, 2, NULL) == 1                    # NULL q
+    larr[1] = QuantLayoutJob(p.value, 4, 64, 1, p.value, q.value)
+    assert libmx.mxfp8_quantize_many_layouts(larr, 2, NULL) == 5                    # alignment
+    larr[1] = QuantLayoutJob(p.value, 1 << 21, 1 << 18, 1, p.value, p.value)      # 2^24 packed tiles
+    assert libmx.mxfp8_quantize_many_layouts(larr, 2, NULL) == 2
     # multi-weight packed quantize: the host table is validated entry by entry
     from mxfp8_block_scaled_05_amd import PackedJob
     good = PackedJob(p.value, 1, 4, 64, None, None, p.value, p.value)
     arr = (PackedJob * 33)(*([good] * 33))
+    arr[1] = PackedJob(p.value, 1, 4, 64, None, None, None, None)
+    assert libmx.mxfp8_quantize_packed_many(arr, 2, NULL) == 1                      # no output at all
+    arr[1] = PackedJob(p.value, 1, 4, 64, None, None, p.value, None)
+    assert libmx.mxfp8_quantize_packed_many(arr, 2, NULL) == 1                      # packed q without scales
+    arr[1] = good
     assert libmx.mxfp8_quantize_packed_many(None, 1, NULL) == 1                     # NULL table
     assert libmx.mxfp8_quantize_packed_many(arr, 0, NULL) == 2                      # empty list
     assert libmx.mxfp8_quantize_packed_many(arr, 33, NULL) == 2                     # more than 32

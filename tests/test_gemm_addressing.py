@@ -99,6 +99,32 @@ def descriptors(M, N, K, BM, BN, packed, G=1, m0=0, m_end=None, n0=0, g=0):
     return out
 
 
+def packed_a_descriptors(M, K, m0):
+    """mxfp8_gemm_packed's A descriptors for a tile at row m0 (m0 % 256 == 0):
+    panel m0 / 256 from k-step 0, its KS tiles and KS scale tiles."""
+    KS = ceil_div(K, KSTEP)
+    MP = ceil_div(M, PANEL)
+    assert m0 % PANEL == 0
+    pa = m0 // PANEL
+    return [("a_q", pa * KS * TILE_BYTES, KS * TILE_BYTES, MP * KS * TILE_BYTES),
+            ("a_s", pa * KS * 1024, KS * 1024, MP * KS * 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 512), (1000, 96, 1024), (513, 264, 4096),
+                                   (2048, 9216, 512), (512, 32768, 256), (4096, 6144, 4096),
+                                   (8192, 24576, 4096), (8192, 4096, 12288)])
+def test_packed_a_descriptors_inside_buffers(M, N, K):
+    for m0, n0, BM, BN in dense_tiles(M, N):
+        for name, base, num, size in packed_a_descriptors(M, K, m0) + \
+                [d for d in descriptors(M, N, K, BM, BN, True, m0=m0, n0=n0) if d[0].startswith("b")]:
+            assert base >= 0 and num > 0 and base + num <= size, (name, M, N, K, m0)
+            assert num < 2 ** 31
+        # every step's copies (32 KB tile, 1 KB of scales) stay inside the ranges
+        KS = ceil_div(K, KSTEP)
+        assert (KS - 1) * TILE_BYTES + BM * 128 <= KS * TILE_BYTES
+        assert (KS - 1) * 1024 + BM * 4 <= KS * 1024
+
+
 def check_tile(*args, **kw):
     for name, base, num, size in descriptors(*args, **kw):
         assert base >= 0 and num > 0, (name, base, num)
@@ -562,3 +588,40 @@ def test_quantize_packed_axis0_writes_every_byte_once(batch, rows, cols):
             if th < 128:
                 s_words[tile_lin * 256 + h * 128 + th] += 1
     assert np.all(q_chunks == 1) and np.all(s_words == 1)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (17, 4128), (300, 320), (513, 1056), (256, 128), (4096, 4096)])
+def test_quantize_many_packed_steps_write_every_byte_once(rows, cols):
+    """Mirror of the list quantizer's packed steps (mxfp8_quantize_many_layouts):
+    step = (16-row atom, k-step); lane l holds half l % 2 of block (l / 2) % 4
+    of row 8h + l / 8 in sub-step h.  Every byte of the packed codes and
+    scales is written exactly once; each code chunk lands at its row's slot
+    c ^ (row % 8); each scale byte comes from the lane that holds that row's
+    block (the shuffle source)."""
+    KS = ceil_div(cols, KSTEP)
+    atoms = ceil_div(rows, PANEL) * 16
+    st = np.arange(atoms * KS)
+    atom, ks = st // KS, st % KS
+    lane = np.arange(64)
+    bl, half = lane >> 1, lane & 1
+    i, kb4 = bl >> 2, bl & 3
+    tile_lin = (atom // 16) * KS + ks
+    qcount = np.zeros(ceil_div(rows, PANEL) * KS * TILE_BYTES // 16, np.int64)
+    for h in (0, 1):
+        rp = (atom[:, None] % 16) * 16 + h * 8 + i[None, :]
+        c = kb4 * 2 + half
+        off = tile_lin[:, None] * TILE_BYTES + rp * 128 + ((c[None, :] ^ (rp & 7)) << 4)
+        assert np.all(off % 16 == 0)
+        np.add.at(qcount, (off // 16).ravel(), 1)
+        # the chunk holds K bytes 32 kb4 + 16 half .. +15 of row rp: chunk c
+        assert np.all(((kb4 * 32 + half * 16) // 16) == c)
+    assert np.all(qcount == 1)
+    soff = tile_lin[:, None] * 1024 + (atom[:, None] % 16) * 64 + lane[None, :]
+    scount = np.bincount(soff.ravel(), minlength=ceil_div(rows, PANEL) * KS * 1024)
+    assert np.all(scount == 1)
+    # scale byte l: row l % 16 (sub-step row // 8), block l // 16; its code is
+    # held by lane 2 * (4 * (row % 8) + block), which owns that row and block
+    rr = lane & 15
+    src = 2 * ((rr & 7) * 4 + (lane >> 4))
+    assert np.all(((src >> 1) >> 2) == (rr & 7)) and np.all(((src >> 1) & 3) == (lane >> 4))
+

@@ -120,7 +120,8 @@ def _packed_out(mx, batch, N, K, canonical, dev):
 
 def test_quantize_packed_many_matches_oracle(mx, oracle_mod):
     """34 ragged weights (two launches: 32 + 2), canonical grid on every other
-    one: each equals the oracle's quantize + pack."""
+    one and only the canonical grid on every sixth: each equals the oracle's
+    quantize + pack."""
     import torch
     shapes = [(1, 256, 128), (1, 300, 320), (3, 17, 96), (2, 512, 768), (1, 40, 4160), (1, 513, 96),
               (1, 1, 32), (2, 257, 160), (1, 1024, 256), (1, 96, 1056), (4, 33, 64), (1, 768, 512),
@@ -134,6 +135,8 @@ def test_quantize_packed_many_matches_oracle(mx, oracle_mod):
         w = wl.normal_bf16(rng, (batch * N, K), std=0.02 * (1 + i))
         w = _specials(w, rng)
         pw, q, s = _packed_out(mx, batch, N, K, i % 2 == 0, dev)
+        if i % 6 == 4:
+            pw = None
         items.append((to_dev(w.reshape(batch, N, K)), pw, q, s))
         refs.append(w)
     mx.quantize_packed_many_(items)
@@ -141,8 +144,9 @@ def test_quantize_packed_many_matches_oracle(mx, oracle_mod):
     for (batch, N, K), w, (_, pw, q, s) in zip(shapes, refs, items):
         rq, rs = oracle_mod.quantize(w, 1)
         qp_ref, sp_ref = oracle_mod.pack(rq.reshape(batch, N, K), rs.reshape(batch, N, K // 32), batch, N, K)
-        assert np.array_equal(to_host(pw.q), qp_ref), (batch, N, K)
-        assert np.array_equal(to_host(pw.s), sp_ref), (batch, N, K)
+        if pw is not None:
+            assert np.array_equal(to_host(pw.q), qp_ref), (batch, N, K)
+            assert np.array_equal(to_host(pw.s), sp_ref), (batch, N, K)
         if q is not None:
             assert np.array_equal(to_host(q).reshape(batch * N, K), rq), (batch, N, K)
             assert np.array_equal(to_host(s).reshape(batch * N, K // 32), rs), (batch, N, K)

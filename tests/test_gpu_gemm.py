@@ -329,6 +329,14 @@ def test_gemm_qkv_full_output(mx, oracle_mod):
     _say("qkv accurate worst error / allowance", worst_a)
     assert ok, worst_a
     del ca
+    # both operands packed, A quantized straight from the BF16 activations:
+    # the same bits as the canonical-A launch above
+    _say("gemm qkv full output, packed A")
+    Aq, _, _ = mx.quantize_packed(to_dev(d["X"]).view(torch.bfloat16), canonical=False)
+    P = mx.repack(to_dev(wq), to_dev(ws))
+    cp = to_host(mx.gemm_packed(Aq, P, torch.bfloat16).float())
+    assert np.array_equal(cp, c)
+    del cp
     # the page's healthy-kernel error band for a dense layer: relative error
     # of the MXFP8 layer against the high-precision GEMM on the BF16 inputs
     rows = sample_rows(xq.shape[0], 256, 256, 32)
@@ -338,6 +346,38 @@ def test_gemm_qkv_full_output(mx, oracle_mod):
     y = xf @ wf.T
     rel = np.linalg.norm(c[rows] - y) / np.linalg.norm(y)
     assert 0.005 < rel < 0.25, rel
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 512), (1000, 96, 1024), (513, 264, 4096),
+                                   (2048, 9216, 512), (512, 32768, 256)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_packed_a_matches_canonical(mx, oracle_mod, M, N, K, out):
+    """mxfp8_gemm_packed: A quantized straight into the packed layout
+    (mxfp8_quantize_packed) gives the same bytes as repacking the canonical
+    grid, and the GEMM over it is bit-identical to mxfp8_gemm with canonical
+    A, over every tiling the launcher picks (256x128 tiles, 256x256 tiles,
+    the mixed launch 2048x9216: 32 large + 8 small tile columns); the smaller
+    cases also against the oracle."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = wl.normal_bf16(rng, (M, K))
+    w = wl.normal_bf16(rng, (N, K), std=0.02)
+    xq, xs = _quant_pair(oracle_mod, x)
+    wq, ws = _quant_pair(oracle_mod, w)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    _say("gemm packed A", M, N, K, out)
+    P = mx.repack(to_dev(wq), to_dev(ws))
+    c0 = mx.gemm(to_dev(xq), to_dev(xs), P, dt)
+    Ar = mx.repack(to_dev(xq), to_dev(xs))
+    Aq, _, _ = mx.quantize_packed(to_dev(x).view(torch.bfloat16), canonical=False)
+    assert torch.equal(Ar.q, Aq.q) and torch.equal(Ar.s, Aq.s)
+    c1 = mx.gemm_packed(Aq, P, dt)
+    torch.cuda.synchronize()
+    iv = torch.int32 if out == "f32" else torch.int16
+    assert torch.equal(c0.view(iv), c1.view(iv))
+    if M * N * K <= 2 ** 28:
+        ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+        ok, worst = oracle_mod.gemm_bound_ok(to_host(c1.float()) if out == "bf16" else to_host(c1), ref, sabs, out)
+        assert ok, worst
 
 
 def test_gemm_deterministic(mx, oracle_mod):

@@ -216,6 +216,63 @@ def test_quantize_many_matches_oracle(mx, oracle_mod):
         assert np.array_equal(to_host(q), q_ref), i
 
 
+def _layout_target(mx, r, c, packed):
+    if packed:
+        return mx.PackedWeight(torch.full((mx.packed_bytes(1, r, c, 0),), 0xEE, dtype=torch.uint8, device="cuda"),
+                               torch.full((mx.packed_bytes(1, r, c, 1),), 0xEE, dtype=torch.uint8, device="cuda"),
+                               1, r, c)
+    return (torch.full((r, c), 0xEE, dtype=torch.uint8, device="cuda"),
+            torch.full((r, c // 32), 0xEE, dtype=torch.uint8, device="cuda"))
+
+
+def _check_layout_target(mx, oracle_mod, x, target, what):
+    r, c = x.shape
+    q_ref, s_ref = oracle_mod.quantize(x, 1)
+    if isinstance(target, mx.PackedWeight):
+        qp_ref, sp_ref = oracle_mod.pack(q_ref.reshape(1, r, c), s_ref.reshape(1, r, c // 32), 1, r, c)
+        assert np.array_equal(to_host(target.q), qp_ref), what
+        assert np.array_equal(to_host(target.s), sp_ref), what
+    else:
+        assert np.array_equal(to_host(target[1]), s_ref), what
+        assert np.array_equal(to_host(target[0]), q_ref), what
+
+
+def test_quantize_many_layouts_matches_oracle(mx, oracle_mod):
+    """mxfp8_quantize_many_layouts over 8 tensors, canonical and packed
+    targets alternating, rows that are not multiples of 16 or 256, columns
+    that are not multiples of 128, the special blocks and the exhaustive sweep
+    among them: canonical entries equal the oracle's axis-1 quantize, packed
+    entries the oracle's packing of it (padding rows and blocks included), bit
+    for bit; buffers start as 0xEE so every byte must be written."""
+    rng = np.random.default_rng(92)
+    xs = [wl.normal_bf16(rng, (1, 32)), _special_blocks(), wl.normal_bf16(rng, (33, 64), outlier_frac=0.02),
+          np.ascontiguousarray(_sweep_matrix()[:20000]), wl.normal_bf16(rng, (300, 320)),
+          wl.normal_bf16(rng, (513, 1056)), wl.normal_bf16(rng, (17, 4128)), wl.normal_bf16(rng, (256, 128))]
+    for first_packed in (True, False):
+        _say("quantize many layouts, first packed", first_packed)
+        items = []
+        for i, x in enumerate(xs):
+            r, c = x.shape
+            items.append((to_dev(x), _layout_target(mx, r, c, (i % 2 == 0) == first_packed)))
+        mx.quantize_many_layouts_(items)
+        torch.cuda.synchronize()
+        for i, (x, (_, target)) in enumerate(zip(xs, items)):
+            _check_layout_target(mx, oracle_mod, x, target, (i, first_packed))
+
+
+def test_quantize_many_layouts_qkv(mx, oracle_mod):
+    """The qkv layer's weight into its canonical grid and its activations into
+    the packed layout in one launch (the default bench step)."""
+    d = wl.qkv(0)
+    _say("quantize many layouts qkv")
+    items = [(to_dev(d["W"]), _layout_target(mx, *d["W"].shape, False)),
+             (to_dev(d["X"]), _layout_target(mx, *d["X"].shape, True))]
+    mx.quantize_many_layouts_(items)
+    torch.cuda.synchronize()
+    for name, (_, target) in zip(("W", "X"), items):
+        _check_layout_target(mx, oracle_mod, d[name], target, name)
+
+
 def test_quantize_many_qkv_pair(mx, oracle_mod):
     """The qkv layer's weight and activations in one launch equal the oracle."""
     d = wl.qkv(0)
