@@ -39,7 +39,7 @@ __device__ __forceinline__ void store16(void *out, int64_t idx, const float *v, 
     if (bf16) {
         uint32_t p[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = f32_to_bf16_rne(v[2 * i]) | (f32_to_bf16_rne(v[2 * i + 1]) << 16);
+        for (int i = 0; i < 8; ++i) p[i] = bf16x2_rne(v[2 * i], v[2 * i + 1]);
         v4i *dst = reinterpret_cast<v4i *>(static_cast<uint16_t *>(out) + idx);
         dst[0] = v4i{(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
         dst[1] = v4i{(int)p[4], (int)p[5], (int)p[6], (int)p[7]};

@@ -866,8 +866,8 @@ __device__ __forceinline__ bool store_tile_lds(const GemmParams &p, int64_t row0
                 const int rl = (i - pass * (PR / 16)) * 16 + (lane & 15);
                 const int cl = j * 16 + (lane >> 4) * 4;
                 if constexpr (OUT_BF16) {
-                    const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-                    const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+                    const uint32_t lo = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+                    const uint32_t hi = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
                     *reinterpret_cast<v2i *>(cw + rl * ROWB + cl * 2) = v2i{(int)lo, (int)hi};
                 } else {
                     *reinterpret_cast<v4f *>(cw + rl * ROWB + cl * 4) = acc[i][j];
@@ -1120,8 +1120,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
             a = v4f{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
         }
         if constexpr (OUT_BF16) {
-            const uint32_t lo = f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16);
+            const uint32_t lo = bf16x2_rne(a[0], a[1]);
+            const uint32_t hi = bf16x2_rne(a[2], a[3]);
             reinterpret_cast<uint2 *>(c)[i] = uint2{lo, hi};
         } else {
             reinterpret_cast<v4f *>(c)[i] = a;
@@ -1272,6 +1272,220 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
             store_tile_lds<TS::FM, TS::FN, OUT_BF16, 2 * (int)SB>(p, row0, col0, p.M, acc2, ts.lane, ts.w, smem);
         } else {
             store_tile_scalar<TS::FM, TS::FN, OUT_BF16>(p, row0, col0, p.M, acc2, ts.lane);
+        }
+    }
+}
+
+// ------------------------------------------------- copy waves + MFMA waves
+// Dense C with both operands packed (K % 128 == 0) as a persistent launch of
+// 256x128 tiles whose waves split the work: waves 0-3 (one per SIMD) only
+// compute, each a 128x64 block of the tile; waves 4-7 (the other wave of
+// each SIMD) only copy, each a quarter of every k-step's A and B tiles and
+// scale tiles.  Measured in the two-stage kernels above: the wave that issues
+// a step's copies is held in the issue for most of the step while the memory
+// pipeline drains, and a step's copies land ~1000 clocks after the last one
+// is issued, so copy issue plus the issuing wave's own MFMAs set the step.
+// Here no computing wave ever issues a copy, and three 49.5 KB stages form a
+// ring that runs on across tile boundaries, so two steps of copies are in
+// flight while one is computed (a 256x256 tile's three stages would not fit
+// the LDS).  One barrier per step g: before it, the computing waves have
+// finished step g and the copying waves have seen step g+1's copies land;
+// after it, step g+1 is computed and the copies of step g+3 go into the stage
+// step g used.  C leaves straight from the accumulators (8 bytes of bf16 or
+// 16 of fp32 per lane and 16x16 tile, through a descriptor spanning this
+// wave's block of C); the stores drain while the next tile's steps run, since
+// the computing waves never wait on vector memory.
+struct WsLayout {
+    static constexpr int BM = 256, BN = 128, NST = 3;
+    static constexpr int A_OFF = 0, B_OFF = BM * 128;            // 32 KB of A rows, 16 KB of B rows
+    static constexpr int SA_OFF = B_OFF + BN * 128;              // the A panel's 1 KB scale tile
+    static constexpr int SB_OFF = SA_OFF + BM * 4;               // 512 B: the B half panel's 8 atoms
+    static constexpr int STAGE = SB_OFF + BN * 4;
+    static constexpr int FM = 8, FN = 4;                         // 128x64 per computing wave
+};
+
+// Cache policy of the C stores (sc0 | nt: streamed, not kept in the L2 that
+// holds the operands).  Measured against the default policy: the qkv shape
+// 92.6 -> 89.4 us, 2048x4096x4096 34.9 -> 30.6 us, the others within 2%.
+constexpr int kStoreStream = 3;
+
+// copy instructions one copying wave (0..3) issues per k-step
+__device__ __forceinline__ constexpr int ws_copies(int pw) { return 8 + 4 + 1 + (pw < 2 ? 1 : 0); }
+
+// the tiles of workgroup `wg`: each XCD (wg % 8) owns a contiguous share of
+// the tile order in proportion to its workgroups, dealt over them; returns
+// the first tile, the stride and the count
+__device__ __forceinline__ void ws_tiles(int wg, int nwg, int T, int &first, int &stride, int &count) {
+    const int q = nwg / 8, r = nwg % 8, x = wg % 8, j = wg / 8;
+    const int nx = q + (x < r ? 1 : 0);
+    const int before = x * q + (x < r ? x : r);                  // workgroups on XCDs < x
+    const int lo = (int)((int64_t)T * before / nwg), hi = (int)((int64_t)T * (before + nx) / nwg);
+    first = lo + j;
+    stride = nx;
+    count = first < hi ? (hi - first + nx - 1) / nx : 0;
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
+    using Lw = WsLayout;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Lw::NST * Lw::STAGE];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KS = p.KS;
+    int first, stride, ntile;
+    ws_tiles(blockIdx.x, gridDim.x, p.tiles_m * p.tiles_n, first, stride, ntile);
+    const int total = ntile * KS;                                // k-steps of this workgroup
+    const uint32_t lds0 = lds_addr(smem);
+
+    if (w >= 4) {
+        // ---- copying wave pw: segments pw, pw + 4, ... of each step
+        const int pw = w - 4;
+        const int nc = ws_copies(pw);
+        int it = 0, ks = 0, st = 0;                              // next step to issue
+        v4i ra = {}, rsa = {}, rb = {}, rsb = {};
+        auto set_tile = [&](int i) {
+            int tm, tn;
+            grouped_order(first + i * stride, p.tiles_m, p.tiles_n, tm, tn);
+            const int64_t pa = tm, pb = ((int64_t)tn * Lw::BN) / kPanelRows, prow = ((int64_t)tn * Lw::BN) % kPanelRows;
+            ra = make_srd(p.a_q + pa * KS * kTileBytes, (uint32_t)((int64_t)KS * kTileBytes));
+            rsa = make_srd(p.a_s + pa * KS * kScaleStepBytes, (uint32_t)((int64_t)KS * kScaleStepBytes));
+            rb = make_srd(p.b_q + pb * KS * kTileBytes + prow * 128,
+                          (uint32_t)((int64_t)KS * kTileBytes - prow * 128));
+            rsb = make_srd(p.b_s + pb * KS * kScaleStepBytes + (prow / 16) * 64,
+                           (uint32_t)((int64_t)KS * kScaleStepBytes - (prow / 16) * 64));
+        };
+        auto issue_next = [&]() {
+            if (ks == 0) set_tile(it);
+            const uint32_t sbase = lds0 + st * Lw::STAGE;
+            const uint32_t k0 = (uint32_t)ks * (uint32_t)kTileBytes;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int seg = i * 4 + pw;
+                dma16(ra, k0 + seg * 1024 + lane * 16, sbase + Lw::A_OFF + seg * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int seg = i * 4 + pw;
+                dma16(rb, k0 + seg * 1024 + lane * 16, sbase + Lw::B_OFF + seg * 1024);
+            }
+            const uint32_t s0 = (uint32_t)ks * (uint32_t)kScaleStepBytes + pw * 256 + lane * 4;
+            dma4(rsa, s0, sbase + Lw::SA_OFF + pw * 256);
+            if (pw < 2) dma4(rsb, s0, sbase + Lw::SB_OFF + pw * 256);
+            st = st == Lw::NST - 1 ? 0 : st + 1;
+            if (++ks == KS) { ks = 0; ++it; }
+        };
+        auto wait_all_but_last = [&]() {
+            if (nc == 14) __builtin_amdgcn_s_waitcnt(waitcnt_vm(14));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(13));
+        };
+        if (total > 0) issue_next();
+        if (total > 1) { issue_next(); wait_all_but_last(); }
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();                                         // step 0 has landed
+        for (int g = 0; g < total; ++g) {
+            if (g + 2 < total) {
+                issue_next();                                    // into the stage step g - 1 used
+                wait_all_but_last();                             // step g + 1 has landed
+            } else {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---- computing wave: rows wm * 128.., columns wn * 64.. of the tile
+    const int wm = w >> 1, wn = w & 1;
+    constexpr int FM = Lw::FM, FN = Lw::FN;
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    const int g16 = lane >> 4;                                   // lane group: columns 4 g16 .. 4 g16 + 3
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();                                             // step 0 has landed
+    int st = 0;
+    for (int it = 0; it < ntile; ++it) {
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint8_t *sp = smem + st * Lw::STAGE;
+            const uint8_t *sa = sp + Lw::A_OFF + wm * 128 * 128;
+            int sas[FM], sbs[FN];
+            v8i bf[FN], af[2];
+            // the B fragments and scales, then row 0's A fragment; each later
+            // A fragment is read while the previous row's MFMAs run (with one
+            // computing wave per SIMD nothing else hides the LDS latency)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sp + Lw::B_OFF + (wn * 64 + j * 16) * 128, lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sbs[j] = sp[Lw::SB_OFF + (wn * FN + j) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sas[i] = sp[Lw::SA_OFF + (wm * FM + i) * 64 + lane];
+            af[0] = lds_frag(sa, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                if (i + 1 < FM) af[(i + 1) & 1] = lds_frag(sa + (i + 1) * 16 * 128, lane);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i & 1], acc[i][j], 0, 0,
+                                                                                 0, sbs[j], 0, sas[i]);
+                __builtin_amdgcn_sched_barrier(0);      // keep the read of row i + 1 ahead of row i's MFMAs
+            }
+            st = st == Lw::NST - 1 ? 0 : st + 1;
+            if (ks == KS - 1) {
+                // the tile's C: this wave's rows and columns that lie inside C
+                int tm, tn;
+                grouped_order(first + it * stride, p.tiles_m, p.tiles_n, tm, tn);
+                const int64_t row0 = (int64_t)tm * Lw::BM + wm * 128, col0 = (int64_t)tn * Lw::BN + wn * 64;
+                const int64_t rows_here = p.M - row0, cols_here = p.N - col0;
+                if (rows_here > 0 && cols_here > 0) {
+                    const int rh = (int)min(rows_here, (int64_t)128), chh = (int)min(cols_here, (int64_t)64);
+                    const uint32_t range = (uint32_t)(((int64_t)(rh - 1) * p.N + chh) * ES);
+                    const __amdgpu_buffer_rsrc_t rc =
+                        make_rsrc(static_cast<uint8_t *>(p.c) + (row0 * p.N + col0) * ES, range);
+                    const int r0 = lane & 15;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        const int r = i * 16 + r0;
+                        if constexpr (OUT_BF16) {
+                            // tiles 2q and 2q + 1 as 16-byte pieces: lane groups
+                            // 2h and 2h + 1 swap halves, so the even one holds
+                            // columns 8h .. 8h + 7 of tile 2q, the odd one those
+                            // of tile 2q + 1
+#pragma unroll
+                            for (int q = 0; q < FN / 2; ++q) {
+                                const v4f &e = acc[i][2 * q], &o = acc[i][2 * q + 1];
+                                const uint32_t e0 = bf16x2_rne(e[0], e[1]), e1 = bf16x2_rne(e[2], e[3]);
+                                const uint32_t o0 = bf16x2_rne(o[0], o[1]), o1 = bf16x2_rne(o[2], o[3]);
+                                const bool even = (g16 & 1) == 0;
+                                const uint32_t s0 = even ? o0 : e0, s1 = even ? o1 : e1;
+                                const uint32_t x0 = (uint32_t)__shfl_xor((int)s0, 16), x1 = (uint32_t)__shfl_xor((int)s1, 16);
+                                const v4i v = even ? v4i{(int)e0, (int)e1, (int)x0, (int)x1}
+                                                   : v4i{(int)x0, (int)x1, (int)o0, (int)o1};
+                                const int cl = (2 * q + (even ? 0 : 1)) * 16 + (g16 >> 1) * 8;
+                                const uint32_t off = (r < rh && cl < chh) ? (uint32_t)(((int64_t)r * p.N + cl) * ES) : kOOB;
+                                __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, kStoreStream);
+                            }
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < FN; ++j) {
+                                const int cl = j * 16 + g16 * 4;
+                                const uint32_t off = (r < rh && cl < chh) ? (uint32_t)(((int64_t)r * p.N + cl) * ES) : kOOB;
+                                __builtin_amdgcn_raw_buffer_store_b128(
+                                    v4i{(int)float_to_bits(acc[i][j][0]), (int)float_to_bits(acc[i][j][1]),
+                                        (int)float_to_bits(acc[i][j][2]), (int)float_to_bits(acc[i][j][3])},
+                                    rc, (int)off, 0, kStoreStream);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+            __syncthreads();
         }
     }
 }
@@ -1515,9 +1729,23 @@ hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint
     p.offsets = nullptr;
     p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
     const int cus = device_cu_count();
-    const DenseTiling d = dense_tiling(M, N, cus);
     p.tiles_m = (int)ceil_div(M, 256);
     dim3 block(kThreads);
+    // the copying / computing split of gemm_ws_kernel where its 256x128 tiles
+    // make at most three rounds over the CUs (a persistent walk hides each
+    // tile's prologue; on more rounds the 256x256 tiles' lower copy volume
+    // per output wins)
+    const int64_t ws_cols = ceil_div(N, 128), ws_count = (int64_t)p.tiles_m * ws_cols;
+    if (N % (c_bf16 ? 8 : 4) == 0 && (int64_t)128 * N * (c_bf16 ? 2 : 4) < ((int64_t)1 << 31) &&
+        ws_count <= (int64_t)3 * cus) {
+        p.tiles_n = (int)ws_cols;
+        const int64_t tiles = ws_count;
+        dim3 grid((unsigned)std::min<int64_t>(tiles, cus));
+        if (c_bf16) hipLaunchKernelGGL((gemm_ws_kernel<true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((gemm_ws_kernel<false>), grid, block, 0, stream, p);
+        return hipGetLastError();
+    }
+    const DenseTiling d = dense_tiling(M, N, cus);
     if (d.big_cols > 0 && d.small_cols > 0) {
         p.tiles_n = d.big_cols + d.small_cols;
         p.mix_big = p.tiles_m * d.big_cols;

@@ -625,3 +625,121 @@ def test_quantize_many_packed_steps_write_every_byte_once(rows, cols):
     src = 2 * ((rr & 7) * 4 + (lane >> 4))
     assert np.all(((src >> 1) >> 2) == (rr & 7)) and np.all(((src >> 1) & 3) == (lane >> 4))
 
+
+
+# ---- gemm_ws_kernel (packed A and B, 256x128 tiles, copying and computing waves)
+
+WS_STAGE = 256 * 128 + 128 * 128 + 256 * 4 + 128 * 4       # A rows | B rows | A scales | B scales
+
+
+def grouped_order(L, tiles_m, tiles_n, group_m=4):
+    per = group_m * tiles_n
+    gid, inn = L // per, L % per
+    first = gid * group_m
+    gsz = min(tiles_m - first, group_m)
+    return first + inn % gsz, inn // gsz
+
+
+def ws_tiles(wg, nwg, T):
+    """Mirror of ws_tiles: (first, stride, count) of workgroup wg."""
+    q, r, x, j = nwg // 8, nwg % 8, wg % 8, wg // 8
+    nx = q + (1 if x < r else 0)
+    before = x * q + min(x, r)
+    lo, hi = T * before // nwg, T * (before + nx) // nwg
+    first = lo + j
+    return first, nx, (hi - first + nx - 1) // nx if first < hi else 0
+
+
+@pytest.mark.parametrize("T", [1, 3, 7, 8, 9, 255, 256, 257, 768, 1000, 6144])
+def test_ws_tile_assignment(T):
+    """Every tile exactly once, for grids of min(T, CUs) workgroups (also
+    grids smaller than 8, which leave XCDs without workgroups)."""
+    for cus in (256, 80, 304):
+        nwg = min(T, cus)
+        seen = []
+        for wg in range(nwg):
+            first, stride, count = ws_tiles(wg, nwg, T)
+            seen += [first + i * stride for i in range(count)]
+        assert sorted(seen) == list(range(T)), (T, cus)
+        counts = [ws_tiles(wg, nwg, T)[2] for wg in range(nwg)]
+        assert max(counts) - min(counts) <= 2, (T, cus)
+
+
+WS_SHAPES = [(64, 256, 256), (200, 300, 512), (1000, 96, 1024), (513, 264, 4096), (2048, 9216, 512),
+             (512, 32768, 256), (4096, 6144, 4096), (8192, 24576, 4096), (8192, 4096, 12288), (33, 4, 128),
+             (300, 132, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", WS_SHAPES)
+def test_ws_copies_inside_buffers(M, N, K):
+    """The copying waves' descriptors (A panel, B half panel and their scale
+    tiles from k-step 0) lie inside the packed buffers, every copy of every
+    step lies inside its descriptor, and every LDS target inside its stage."""
+    assert 3 * WS_STAGE <= 160 * 1024
+    KS, MP, NP = ceil_div(K, KSTEP), ceil_div(M, PANEL), ceil_div(N, PANEL)
+    tiles_m, tiles_n = ceil_div(M, 256), ceil_div(N, 128)
+    for L in range(tiles_m * tiles_n):
+        tm, tn = grouped_order(L, tiles_m, tiles_n)
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        pa, pb, prow = tm, tn * 128 // PANEL, tn * 128 % PANEL
+        descs = [(pa * KS * TILE_BYTES, KS * TILE_BYTES, MP * KS * TILE_BYTES),
+                 (pa * KS * 1024, KS * 1024, MP * KS * 1024),
+                 (pb * KS * TILE_BYTES + prow * 128, KS * TILE_BYTES - prow * 128, NP * KS * TILE_BYTES),
+                 (pb * KS * 1024 + prow // 16 * 64, KS * 1024 - prow // 16 * 64, NP * KS * 1024)]
+        for base, num, size in descs:
+            assert base >= 0 and 0 < num < 2 ** 32 and base + num <= size, (M, N, K, tm, tn)
+        last = (KS - 1) * TILE_BYTES
+        for pw in range(4):
+            a_end = max(last + (i * 4 + pw) * 1024 + 63 * 16 + 16 for i in range(8))
+            b_end = max(last + (i * 4 + pw) * 1024 + 63 * 16 + 16 for i in range(4))
+            s_end = (KS - 1) * 1024 + pw * 256 + 63 * 4 + 4
+            assert a_end <= descs[0][1] and b_end <= descs[2][1] and s_end <= descs[1][1]
+            if pw < 2:
+                assert s_end <= descs[3][1]
+            # LDS targets: A segments, B segments, scale dwords, inside one stage
+            assert max((i * 4 + pw) * 1024 + 1024 for i in range(8)) <= 256 * 128
+            assert 256 * 128 + max((i * 4 + pw) * 1024 + 1024 for i in range(4)) <= 256 * 128 + 128 * 128
+            assert 256 * 128 + 128 * 128 + pw * 256 + 256 <= 256 * 128 + 128 * 128 + 1024
+        assert 256 * 128 + 128 * 128 + 1024 + 2 * 256 == WS_STAGE
+
+
+@pytest.mark.parametrize("M,N", [(64, 256), (200, 304), (1000, 96), (513, 264), (33, 4), (300, 132),
+                                 (256, 128), (4096, 6144), (40, 72)])
+@pytest.mark.parametrize("es", [2, 4])
+def test_ws_stores_cover_c_once(M, N, es):
+    """Each computing wave's stores through a descriptor spanning its block
+    of C (fp32: one 4-column piece per lane and 16x16 tile; bf16: one
+    8-column piece per lane and pair of tiles): every piece inside the range,
+    every element of C written exactly once."""
+    if N % (8 if es == 2 else 4):
+        pytest.skip("the launcher takes this kernel only for N % 8 == 0 (bf16) or N % 4 == 0 (fp32)")
+    tiles_m, tiles_n = ceil_div(M, 256), ceil_div(N, 128)
+    hits = np.zeros(M * N, np.int32)
+    lane = np.arange(64)
+    for L in range(tiles_m * tiles_n):
+        tm, tn = grouped_order(L, tiles_m, tiles_n)
+        for w in range(4):
+            wm, wn = w >> 1, w & 1
+            row0, col0 = tm * 256 + wm * 128, tn * 128 + wn * 64
+            rows_here, cols_here = M - row0, N - col0
+            if rows_here <= 0 or cols_here <= 0:
+                continue
+            rh, chh = min(rows_here, 128), min(cols_here, 64)
+            rng = ((rh - 1) * N + chh) * es
+            base = (row0 * N + col0) * es
+            assert base + rng <= M * N * es and rng < 2 ** 31
+            g = lane >> 4
+            if es == 2:        # tiles 2q, 2q + 1: even lane groups tile 2q, odd ones tile 2q + 1
+                pieces = [(q * 32 + (g & 1) * 16 + (g >> 1) * 8, 8) for q in range(2)]
+            else:
+                pieces = [(j * 16 + g * 4, 4) for j in range(4)]
+            for i in range(8):
+                for cl, width in pieces:
+                    r = i * 16 + (lane & 15)
+                    ok = (r < rh) & (cl < chh)
+                    off = (r * N + cl) * es
+                    assert np.all(off[ok] + width * es <= rng)
+                    assert 0x80000000 >= rng
+                    for c in range(width):
+                        np.add.at(hits, (row0 + r[ok]) * N + col0 + cl[ok] + c, 1)
+    assert np.all(hits == 1), (M, N)

@@ -349,15 +349,19 @@ def test_gemm_qkv_full_output(mx, oracle_mod):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 512), (1000, 96, 1024), (513, 264, 4096),
-                                   (2048, 9216, 512), (512, 32768, 256)])
+                                   (2048, 9216, 512), (512, 32768, 256), (4096, 9216, 512), (3072, 9216, 512),
+                                   (4096, 6140, 512), (300, 4100, 384)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_packed_a_matches_canonical(mx, oracle_mod, M, N, K, out):
     """mxfp8_gemm_packed: A quantized straight into the packed layout
     (mxfp8_quantize_packed) gives the same bytes as repacking the canonical
     grid, and the GEMM over it is bit-identical to mxfp8_gemm with canonical
-    A, over every tiling the launcher picks (256x128 tiles, 256x256 tiles,
-    the mixed launch 2048x9216: 32 large + 8 small tile columns); the smaller
-    cases also against the oracle."""
+    A, over every kernel the launcher picks: the copying/computing-wave
+    kernel (256x128 tiles, up to three rounds: the first six shapes, and
+    fp32 output wherever N % 4 == 0), and otherwise the 256x256 tiles
+    (3072x9216), the mixed launch (4096x9216: 32 large + 8 small tile
+    columns), the paired launch (4096x6140 bf16: N % 8 != 0) and 256x128
+    tiles (300x4100 bf16); the smaller cases also against the oracle."""
     rng = np.random.default_rng(M * 7 + N + K)
     x = wl.normal_bf16(rng, (M, K))
     w = wl.normal_bf16(rng, (N, K), std=0.02)
