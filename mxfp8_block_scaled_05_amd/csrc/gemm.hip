@@ -1291,9 +1291,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
 // the LDS).  One barrier per step g: before it, the computing waves have
 // finished step g and the copying waves have seen step g+1's copies land;
 // after it, step g+1 is computed and the copies of step g+3 go into the stage
-// step g used.  C leaves straight from the accumulators (8 bytes of bf16 or
-// 16 of fp32 per lane and 16x16 tile, through a descriptor spanning this
-// wave's block of C); the stores drain while the next tile's steps run, since
+// step g used.  C leaves from the accumulators through a descriptor spanning
+// this wave's block of C (bf16: 16-row bands through a 2.3 KB LDS buffer per
+// wave, so every store writes whole 128-byte rows; fp32: 16 bytes per lane
+// and 16x16 tile); the stores drain while the next tile's steps run, since
 // the computing waves never wait on vector memory.
 struct WsLayout {
     static constexpr int BM = 256, BN = 128, NST = 3;
@@ -1302,11 +1303,16 @@ struct WsLayout {
     static constexpr int SB_OFF = SA_OFF + BM * 4;               // 512 B: the B half panel's 8 atoms
     static constexpr int STAGE = SB_OFF + BN * 4;
     static constexpr int FM = 8, FN = 4;                         // 128x64 per computing wave
+    // bf16 C leaves each computing wave 16 rows at a time through a band
+    // buffer of its own after the ring (rows padded by 16 bytes)
+    static constexpr int BAND_ROW = 64 * 2 + 16, BAND = 16 * BAND_ROW, BAND_OFF = NST * STAGE;
 };
+static_assert(WsLayout::BAND_OFF + 4 * WsLayout::BAND <= 160 * 1024, "ring and band buffers fit the LDS");
 
-// Cache policy of the C stores (sc0 | nt: streamed, not kept in the L2 that
-// holds the operands).  Measured against the default policy: the qkv shape
-// 92.6 -> 89.4 us, 2048x4096x4096 34.9 -> 30.6 us, the others within 2%.
+// Cache policy of the bf16 C stores, whole 128-byte rows (sc0 | nt: streamed,
+// not kept in the L2 that holds the operands).  Measured against the default
+// policy: qkv 88.4 -> 85.2 us, 2048x4096x4096 33.7 -> 28.6 us.  (Streamed
+// stores of half rows wrote 1.5x the bytes of C: WRITE_SIZE.)
 constexpr int kStoreStream = 3;
 
 // copy instructions one copying wave (0..3) issues per k-step
@@ -1328,7 +1334,7 @@ __device__ __forceinline__ void ws_tiles(int wg, int nwg, int T, int &first, int
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
     using Lw = WsLayout;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Lw::NST * Lw::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Lw::BAND_OFF + 4 * Lw::BAND];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KS = p.KS;
@@ -1449,24 +1455,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                     for (int i = 0; i < FM; ++i) {
                         const int r = i * 16 + r0;
                         if constexpr (OUT_BF16) {
-                            // tiles 2q and 2q + 1 as 16-byte pieces: lane groups
-                            // 2h and 2h + 1 swap halves, so the even one holds
-                            // columns 8h .. 8h + 7 of tile 2q, the odd one those
-                            // of tile 2q + 1
+                            // the band of 16 rows through this wave's LDS band
+                            // buffer, out as 8 whole 128-byte rows per store
+                            uint8_t *band = smem + Lw::BAND_OFF + w * Lw::BAND;
 #pragma unroll
-                            for (int q = 0; q < FN / 2; ++q) {
-                                const v4f &e = acc[i][2 * q], &o = acc[i][2 * q + 1];
-                                const uint32_t e0 = bf16x2_rne(e[0], e[1]), e1 = bf16x2_rne(e[2], e[3]);
-                                const uint32_t o0 = bf16x2_rne(o[0], o[1]), o1 = bf16x2_rne(o[2], o[3]);
-                                const bool even = (g16 & 1) == 0;
-                                const uint32_t s0 = even ? o0 : e0, s1 = even ? o1 : e1;
-                                const uint32_t x0 = (uint32_t)__shfl_xor((int)s0, 16), x1 = (uint32_t)__shfl_xor((int)s1, 16);
-                                const v4i v = even ? v4i{(int)e0, (int)e1, (int)x0, (int)x1}
-                                                   : v4i{(int)x0, (int)x1, (int)o0, (int)o1};
-                                const int cl = (2 * q + (even ? 0 : 1)) * 16 + (g16 >> 1) * 8;
-                                const uint32_t off = (r < rh && cl < chh) ? (uint32_t)(((int64_t)r * p.N + cl) * ES) : kOOB;
+                            for (int jj = 0; jj < FN; ++jj)
+                                *reinterpret_cast<v2i *>(band + r0 * Lw::BAND_ROW + jj * 32 + g16 * 8) =
+                                    v2i{(int)bf16x2_rne(acc[i][jj][0], acc[i][jj][1]),
+                                        (int)bf16x2_rne(acc[i][jj][2], acc[i][jj][3])};
+                            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const int rr = h * 8 + (lane >> 3), cl = (lane & 7) * 8, row = i * 16 + rr;
+                                const v4i v = *reinterpret_cast<const v4i *>(band + rr * Lw::BAND_ROW + (lane & 7) * 16);
+                                const uint32_t off =
+                                    (row < rh && cl < chh) ? (uint32_t)(((int64_t)row * p.N + cl) * ES) : kOOB;
                                 __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, kStoreStream);
                             }
+                            __builtin_amdgcn_wave_barrier();
                         } else {
 #pragma unroll
                             for (int j = 0; j < FN; ++j) {
@@ -1475,7 +1481,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                                 __builtin_amdgcn_raw_buffer_store_b128(
                                     v4i{(int)float_to_bits(acc[i][j][0]), (int)float_to_bits(acc[i][j][1]),
                                         (int)float_to_bits(acc[i][j][2]), (int)float_to_bits(acc[i][j][3])},
-                                    rc, (int)off, 0, kStoreStream);
+                                    rc, (int)off, 0, 0);
                             }
                         }
                     }

@@ -675,7 +675,7 @@ def test_ws_copies_inside_buffers(M, N, K):
     """The copying waves' descriptors (A panel, B half panel and their scale
     tiles from k-step 0) lie inside the packed buffers, every copy of every
     step lies inside its descriptor, and every LDS target inside its stage."""
-    assert 3 * WS_STAGE <= 160 * 1024
+    assert 3 * WS_STAGE + 4 * 16 * (64 * 2 + 16) <= 160 * 1024     # ring + the computing waves' band buffers
     KS, MP, NP = ceil_div(K, KSTEP), ceil_div(M, PANEL), ceil_div(N, PANEL)
     tiles_m, tiles_n = ceil_div(M, 256), ceil_div(N, 128)
     for L in range(tiles_m * tiles_n):
@@ -708,9 +708,9 @@ def test_ws_copies_inside_buffers(M, N, K):
 @pytest.mark.parametrize("es", [2, 4])
 def test_ws_stores_cover_c_once(M, N, es):
     """Each computing wave's stores through a descriptor spanning its block
-    of C (fp32: one 4-column piece per lane and 16x16 tile; bf16: one
-    8-column piece per lane and pair of tiles): every piece inside the range,
-    every element of C written exactly once."""
+    of C (fp32: one 4-column piece per lane and 16x16 tile; bf16: 16-row
+    bands, one 8-column piece per lane, eight lanes per row): every piece
+    inside the range, every element of C written exactly once."""
     if N % (8 if es == 2 else 4):
         pytest.skip("the launcher takes this kernel only for N % 8 == 0 (bf16) or N % 4 == 0 (fp32)")
     tiles_m, tiles_n = ceil_div(M, 256), ceil_div(N, 128)
@@ -729,13 +729,13 @@ def test_ws_stores_cover_c_once(M, N, es):
             base = (row0 * N + col0) * es
             assert base + rng <= M * N * es and rng < 2 ** 31
             g = lane >> 4
-            if es == 2:        # tiles 2q, 2q + 1: even lane groups tile 2q, odd ones tile 2q + 1
-                pieces = [(q * 32 + (g & 1) * 16 + (g >> 1) * 8, 8) for q in range(2)]
-            else:
-                pieces = [(j * 16 + g * 4, 4) for j in range(4)]
+            if es == 2:        # 16-row bands through LDS: 8 lanes per 128-byte row, two stores per band
+                pieces = [(h * 8 + (lane >> 3), (lane & 7) * 8, 8) for h in range(2)]
+            else:              # 16 bytes per lane and 16x16 tile
+                pieces = [(lane & 15, j * 16 + g * 4, 4) for j in range(4)]
             for i in range(8):
-                for cl, width in pieces:
-                    r = i * 16 + (lane & 15)
+                for rb, cl, width in pieces:
+                    r = i * 16 + rb
                     ok = (r < rh) & (cl < chh)
                     off = (r * N + cl) * es
                     assert np.all(off[ok] + width * es <= rng)
