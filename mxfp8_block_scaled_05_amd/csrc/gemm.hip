@@ -829,6 +829,14 @@ __device__ __forceinline__ void store_tile_scalar(const GemmParams &p, int64_t r
 // vmcnt(count) (vector memory operations complete in issue order), leaving
 // the stores to drain behind its next work.  Returns false (pointer stores,
 // count not exact) when the wave's block spans 4 GiB or more of C.
+// Cache policy of C stores of whole 128-byte rows (sc0 | nt: streamed, not
+// kept in the L2 that holds the operands).  Measured against the default
+// policy: gemm_ws_kernel qkv 88.4 -> 85.2 us, 2048x4096x4096 33.7 -> 28.6 us;
+// the grouped MoE launches gate_up 268 -> 262 us, down 176 -> 166 us; the
+// MLP GEMMs 0-3% faster; the paired launch 2.5% slower, so it keeps the
+// default.  (Streamed stores of half rows wrote 1.5x the bytes of C.)
+constexpr int kStoreStream = 3;
+
 template <int FM, int FN, bool OUT_BF16, int LDS_BYTES, int NW = kWaves>
 struct EpilogueShape {
     static constexpr int ES = OUT_BF16 ? 2 : 4;
@@ -841,7 +849,7 @@ struct EpilogueShape {
     static constexpr int RPI = 64 / LPR;                              // rows per store instruction
     static constexpr int kStores = WTM / RPI;                         // store instructions per wave
 };
-template <int FM, int FN, bool OUT_BF16, int LDS_BYTES, int NW = kWaves>
+template <int FM, int FN, bool OUT_BF16, int LDS_BYTES, int NW = kWaves, int POL = kStoreStream>
 __device__ __forceinline__ bool store_tile_lds(const GemmParams &p, int64_t row0, int64_t col0, int64_t m_end,
                                v4f (*acc)[FN], int lane, int w, uint8_t *smem) {
     using E = EpilogueShape<FM, FN, OUT_BF16, LDS_BYTES, NW>;
@@ -882,7 +890,7 @@ __device__ __forceinline__ bool store_tile_lds(const GemmParams &p, int64_t row0
             const v4i v = *reinterpret_cast<const v4i *>(cw + rl * ROWB + cb);
             if (counted) {
                 const uint32_t off = (uint32_t)(pass * PR + rl) * (uint32_t)(N * ES) + (uint32_t)cb;
-                __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, POL);
             } else {
                 const int64_t row = row0 + pass * PR + rl;
                 uint8_t *dst = static_cast<uint8_t *>(p.c) + (row * N + col0) * ES + cb;
@@ -1245,7 +1253,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
         constexpr int ES = OUT_BF16 ? 2 : 4;
         bool counted = false;
         if (n0 + 256 <= p.N && (p.N * ES) % 16 == 0)
-            counted = store_tile_lds<TB::FM, TB::FN, OUT_BF16, (int)SB>(p, row0, col0, p.M, acc, tb.lane, tb.w,
+            counted = store_tile_lds<TB::FM, TB::FN, OUT_BF16, (int)SB, kWaves, 0>(p, row0, col0, p.M, acc, tb.lane, tb.w,
                                                                         smem + (1 - F) * SB);
         else
             store_tile_scalar<TB::FM, TB::FN, OUT_BF16>(p, row0, col0, p.M, acc, tb.lane);
@@ -1269,7 +1277,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pair_kernel(GemmParams p) {
         constexpr int ES = OUT_BF16 ? 2 : 4;
         if (n2 + 128 <= p.N && (p.N * ES) % 16 == 0) {
             __syncthreads();
-            store_tile_lds<TS::FM, TS::FN, OUT_BF16, 2 * (int)SB>(p, row0, col0, p.M, acc2, ts.lane, ts.w, smem);
+            store_tile_lds<TS::FM, TS::FN, OUT_BF16, 2 * (int)SB, kWaves, 0>(p, row0, col0, p.M, acc2, ts.lane, ts.w, smem);
         } else {
             store_tile_scalar<TS::FM, TS::FN, OUT_BF16>(p, row0, col0, p.M, acc2, ts.lane);
         }
@@ -1308,12 +1316,6 @@ struct WsLayout {
     static constexpr int BAND_ROW = 64 * 2 + 16, BAND = 16 * BAND_ROW, BAND_OFF = NST * STAGE;
 };
 static_assert(WsLayout::BAND_OFF + 4 * WsLayout::BAND <= 160 * 1024, "ring and band buffers fit the LDS");
-
-// Cache policy of the bf16 C stores, whole 128-byte rows (sc0 | nt: streamed,
-// not kept in the L2 that holds the operands).  Measured against the default
-// policy: qkv 88.4 -> 85.2 us, 2048x4096x4096 33.7 -> 28.6 us.  (Streamed
-// stores of half rows wrote 1.5x the bytes of C: WRITE_SIZE.)
-constexpr int kStoreStream = 3;
 
 // copy instructions one copying wave (0..3) issues per k-step
 __device__ __forceinline__ constexpr int ws_copies(int pw) { return 8 + 4 + 1 + (pw < 2 ? 1 : 0); }
