@@ -821,9 +821,10 @@ def bench_sync(args, dev):
 
 def bench_sweep(args, dev):
     """One Qwen3-8B decoder layer's four linears at M tokens, MXFP8 (quantize
-    the input along K + GEMM against packed weights, bf16 out; mxfp8_gemm_splitk
-    with a preallocated workspace, which splits K only for shapes with few
-    output tiles) against BF16
+    the input along K straight into the GEMM's packed operand layout + GEMM
+    against packed weights, bf16 out; mxfp8_gemm_packed_splitk with a
+    preallocated workspace, which splits K only for shapes with few output
+    tiles) against BF16
     (torch.nn.functional.linear -> hipBLASLt).  Fits t = F + c*M per arm, for
     GPU time (events around the four linears) and for host wall time per layer
     call, and reports the break-even M* = dF / dc if it lies in range."""
@@ -844,8 +845,9 @@ def bench_sweep(args, dev):
     rows = []
     for M in Ms:
         xs = [Xall[K][:M] for _, _, K in shapes]
-        qs = [(torch.empty((M, K), dtype=torch.uint8, device=dev),
-               torch.empty((M, K // 32), dtype=torch.uint8, device=dev)) for _, _, K in shapes]
+        qs = [mx.PackedWeight(torch.empty(mx.packed_bytes(1, M, K, 0), dtype=torch.uint8, device=dev),
+                              torch.empty(mx.packed_bytes(1, M, K, 1), dtype=torch.uint8, device=dev), 1, M, K)
+              for _, _, K in shapes]
         ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _, N, _ in shapes]
         # split-K workspaces for the shapes with few output tiles (allocated
         # here, outside the timing; none where the library would not split)
@@ -853,9 +855,9 @@ def bench_sweep(args, dev):
                for _, N, K in shapes]
 
         def mx_layer():
-            for x, (q, sc), w, y, wsp in zip(xs, qs, P, ys, wss):
-                mx.quantize_into(x, 1, q, sc)
-                mx.gemm(q, sc, w, torch.bfloat16, out=y, workspace=wsp)
+            for x, a, w, y, wsp in zip(xs, qs, P, ys, wss):
+                mx.quantize_many_layouts_([(x, a)])
+                mx.gemm_packed(a, w, torch.bfloat16, out=y, workspace=wsp)
 
         def bf_layer():
             for x, W, y in zip(xs, Wb, ys):

@@ -471,6 +471,29 @@ mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s,
 size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * mxfp8_gemm_packed_splitk -- mxfp8_gemm_packed for shapes with few output
+ * tiles (small M: section "Speed: when it pays off", as mxfp8_gemm_splitk).
+ *
+ * Same operands, result and error bound as mxfp8_gemm_packed (A and B in the
+ * mxfp8_repack layout, K % 128 == 0), split as mxfp8_gemm_splitk splits: the
+ * same slices (sized by mxfp8_gemm_splitk_workspace_bytes(M, N, K); with a
+ * smaller workspace, as many slices as fit), the fp32 partial tiles in
+ * `workspace`, summed in slice order.  C is bit-identical to
+ * mxfp8_gemm_splitk over the canonical grids of the same operands (the same
+ * per-slice products in the same order).  workspace: DEVICE memory owned by
+ * the caller, 16-byte aligned, or NULL; contents on entry ignored, on return
+ * unspecified.  No split (too many tiles, fewer than two slices fit, or
+ * N % 4 != 0): the plain mxfp8_gemm_packed path, no workspace touched.
+ * Argument errors as mxfp8_gemm_packed, plus MXFP8_ERR_ALIGN for a workspace
+ * not 16-byte aligned.  Two kernels on `stream`, no allocation, no
+ * synchronization.
+ */
+mxfp8_status mxfp8_gemm_packed_splitk(const uint8_t *a_q_packed, const uint8_t *a_s_packed,
+                                      const uint8_t *b_q_packed, const uint8_t *b_s_packed,
+                                      int64_t M, int64_t N, int64_t K, void *c, mxfp8_dtype c_dtype,
+                                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * mxfp8_gemm_splitk_noalloc -- mxfp8_gemm_splitk with no caller workspace and
  * no allocation, for callers that cannot allocate device memory (code under
  * HIP-graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -72,6 +72,8 @@ def lib():
         L.mxfp8_gemm_accurate.restype = I32
         L.mxfp8_gemm_packed.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P]
         L.mxfp8_gemm_packed.restype = I32
+        L.mxfp8_gemm_packed_splitk.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, ctypes.c_size_t, P]
+        L.mxfp8_gemm_packed_splitk.restype = I32
         L.mxfp8_quantize_many_layouts.argtypes = [P, I64, P]
         L.mxfp8_quantize_many_layouts.restype = I32
         L.mxfp8_gemm_splitk_noalloc.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
@@ -635,10 +637,13 @@ def gemm(a_q: torch.Tensor, a_s: torch.Tensor, b, out_dtype=torch.bfloat16,
 
 
 def gemm_packed(a: PackedWeight, b: PackedWeight, out_dtype=torch.bfloat16,
-                out: torch.Tensor | None = None) -> torch.Tensor:
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                split_k: bool = False) -> torch.Tensor:
     """C[M, N] = A[M, K] B[N, K]^T with both operands in the packed layout
     (mxfp8_gemm_packed): A from quantize_packed / repack of [M, K] (a.N = M),
-    B a packed weight.  K % 128 == 0."""
+    B a packed weight.  K % 128 == 0.  With split_k (or a workspace given)
+    the call is mxfp8_gemm_packed_splitk, its workspace sized as
+    gemm_splitk's (allocated here, through torch, when not given)."""
     for name, w in (("a", a), ("b", b)):
         if not isinstance(w, PackedWeight) or w.batch != 1:
             raise ValueError("%s must be a single packed [rows, K] matrix" % name)
@@ -654,6 +659,17 @@ def gemm_packed(a: PackedWeight, b: PackedWeight, out_dtype=torch.bfloat16,
         _need(out, out_dtype, "out")
         if tuple(out.shape) != (M, N):
             raise ValueError("out must be [M, N]")
+    if split_k or workspace is not None:
+        need = gemm_splitk_workspace_bytes(M, N, K)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=a.q.device)
+        if workspace is not None:
+            _need(workspace, torch.uint8, "workspace")
+        _check(lib().mxfp8_gemm_packed_splitk(_ptr(a.q), _ptr(a.s), _ptr(b.q), _ptr(b.s), M, N, K, _ptr(out), code,
+                                              _ptr(workspace) if workspace is not None else None,
+                                              workspace.numel() if workspace is not None else 0,
+                                              _stream(a.q.device)), "mxfp8_gemm_packed_splitk")
+        return out
     _check(lib().mxfp8_gemm_packed(_ptr(a.q), _ptr(a.s), _ptr(b.q), _ptr(b.s), M, N, K, _ptr(out), code,
                                    _stream(a.q.device)), "mxfp8_gemm_packed")
     return out

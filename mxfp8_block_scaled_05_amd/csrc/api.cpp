@@ -449,6 +449,26 @@ mxfp8_status mxfp8_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b
                               raw(c_dtype) == MXFP8_BF16, stream));
 }
 
+// A split plan cut down to the slices `workspace` holds (fewer than two: no
+// split).
+static SplitPlan fit_split(SplitPlan sp, int64_t M, int64_t N, int64_t K, const void *workspace,
+                           size_t workspace_bytes) {
+    if (sp.splits > 1 && (!workspace || workspace_bytes < (size_t)sp.workspace_bytes)) {
+        const int64_t slice = (M * N + 3) / 4 * 4 * 4;
+        const int64_t fit = workspace ? (int64_t)(workspace_bytes / (size_t)slice) : 0;
+        if (fit >= 2) {
+            const int64_t ks = ceil_div(K, 128);
+            const int64_t steps = ceil_div(ks, fit);
+            sp.split_steps = (int)steps;
+            sp.splits = (int)ceil_div(ks, steps);
+            sp.workspace_bytes = sp.splits * slice;
+        } else {
+            sp.splits = 1;
+        }
+    }
+    return sp;
+}
+
 mxfp8_status mxfp8_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
                                int64_t M, int64_t N, int64_t K, void *c, mxfp8_dtype c_dtype,
                                hipStream_t stream) {
@@ -462,6 +482,29 @@ mxfp8_status mxfp8_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uin
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
     return finish(launch_gemm_packed(a_q, a_s, b_q, b_s, M, N, K, c, raw(c_dtype) == MXFP8_BF16, stream));
+}
+
+mxfp8_status mxfp8_gemm_packed_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                      const uint8_t *b_s, int64_t M, int64_t N, int64_t K, void *c,
+                                      mxfp8_dtype c_dtype, void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    if (!a_q || !a_s || !b_q || !b_s || !c) return MXFP8_ERR_NULL;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K < 128 || K % 128 || K > kMaxK || M >= kMaxDim || N >= kMaxDim)
+        return MXFP8_ERR_SHAPE;
+    if (ceil_div(M, 256) * ceil_div(N, 128) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(b_q) || !aligned16(b_s) || !aligned16(c) ||
+        (workspace && !aligned16(workspace)))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    SplitPlan sp = fit_split(splitk_plan(M, N, K, device_cu_count()), M, N, K, workspace, workspace_bytes);
+    // the split launch stores fp32 partials in 4-column pieces
+    if (N % 4 != 0 || (int64_t)128 * N * 4 >= ((int64_t)1 << 31)) sp.splits = 1;
+    if (sp.splits <= 1)
+        return finish(launch_gemm_packed(a_q, a_s, b_q, b_s, M, N, K, c, raw(c_dtype) == MXFP8_BF16, stream));
+    return finish(launch_gemm_packed_splitk(a_q, a_s, b_q, b_s, M, N, K, c, raw(c_dtype) == MXFP8_BF16, sp,
+                                            static_cast<float *>(workspace), stream));
 }
 
 mxfp8_status mxfp8_gemm_accurate(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
@@ -503,21 +546,7 @@ mxfp8_status mxfp8_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uin
         return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
-    SplitPlan sp = splitk_plan(M, N, K, device_cu_count());
-    if (sp.splits > 1 && (!workspace || workspace_bytes < (size_t)sp.workspace_bytes)) {
-        // fewer slices, as many as the workspace holds
-        const int64_t slice = (M * N + 3) / 4 * 4 * 4;
-        const int64_t fit = workspace ? (int64_t)(workspace_bytes / (size_t)slice) : 0;
-        if (fit >= 2) {
-            const int64_t ks = ceil_div(K, 128);
-            const int64_t steps = ceil_div(ks, fit);
-            sp.split_steps = (int)steps;
-            sp.splits = (int)ceil_div(ks, steps);
-            sp.workspace_bytes = sp.splits * slice;
-        } else {
-            sp.splits = 1;
-        }
-    }
+    const SplitPlan sp = fit_split(splitk_plan(M, N, K, device_cu_count()), M, N, K, workspace, workspace_bytes);
     if (sp.splits <= 1)
         return finish(launch_gemm(a_q, a_s, b_q, b_s, raw(b_layout) == MXFP8_PACKED, M, N, K, c,
                                   raw(c_dtype) == MXFP8_BF16, stream));

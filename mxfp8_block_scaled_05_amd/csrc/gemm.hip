@@ -1340,20 +1340,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KS = p.KS;
-    int first, stride, ntile;
-    ws_tiles(blockIdx.x, gridDim.x, p.tiles_m * p.tiles_n, first, stride, ntile);
-    const int total = ntile * KS;                                // k-steps of this workgroup
+    // work units: tile u % T over K slice u / T (p.splits > 1: the split
+    // launch, fp32 partials of slice s at c + s * c_stride; else one slice)
+    const int T = p.tiles_m * p.tiles_n;
+    const int S = p.splits > 1 ? p.splits : 1, L = p.splits > 1 ? p.split_steps : KS;
+    int first, stride, nunit;
+    ws_tiles(blockIdx.x, gridDim.x, T * S, first, stride, nunit);
+    auto unit_steps = [&](int i, int &k0, int &k1) {
+        k0 = (first + i * stride) / T * L;
+        k1 = min(KS, k0 + L);
+    };
+    int total = 0;                                               // k-steps of this workgroup
+    for (int i = 0; i < nunit; ++i) {
+        int k0, k1;
+        unit_steps(i, k0, k1);
+        total += k1 - k0;
+    }
     const uint32_t lds0 = lds_addr(smem);
 
     if (w >= 4) {
         // ---- copying wave pw: segments pw, pw + 4, ... of each step
         const int pw = w - 4;
         const int nc = ws_copies(pw);
-        int it = 0, ks = 0, st = 0;                              // next step to issue
+        int iu = 0, ks = 0, kend = 0, st = 0;                    // next step to issue
         v4i ra = {}, rsa = {}, rb = {}, rsb = {};
         auto set_tile = [&](int i) {
             int tm, tn;
-            grouped_order(first + i * stride, p.tiles_m, p.tiles_n, tm, tn);
+            grouped_order((first + i * stride) % T, p.tiles_m, p.tiles_n, tm, tn);
             const int64_t pa = tm, pb = ((int64_t)tn * Lw::BN) / kPanelRows, prow = ((int64_t)tn * Lw::BN) % kPanelRows;
             ra = make_srd(p.a_q + pa * KS * kTileBytes, (uint32_t)((int64_t)KS * kTileBytes));
             rsa = make_srd(p.a_s + pa * KS * kScaleStepBytes, (uint32_t)((int64_t)KS * kScaleStepBytes));
@@ -1362,8 +1375,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
             rsb = make_srd(p.b_s + pb * KS * kScaleStepBytes + (prow / 16) * 64,
                            (uint32_t)((int64_t)KS * kScaleStepBytes - (prow / 16) * 64));
         };
+        auto start_unit = [&](int i) {
+            unit_steps(i, ks, kend);
+            set_tile(i);
+        };
+        if (nunit > 0) start_unit(0);
         auto issue_next = [&]() {
-            if (ks == 0) set_tile(it);
             const uint32_t sbase = lds0 + st * Lw::STAGE;
             const uint32_t k0 = (uint32_t)ks * (uint32_t)kTileBytes;
 #pragma unroll
@@ -1380,7 +1397,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
             dma4(rsa, s0, sbase + Lw::SA_OFF + pw * 256);
             if (pw < 2) dma4(rsb, s0, sbase + Lw::SB_OFF + pw * 256);
             st = st == Lw::NST - 1 ? 0 : st + 1;
-            if (++ks == KS) { ks = 0; ++it; }
+            if (++ks == kend && ++iu < nunit) start_unit(iu);
         };
         auto wait_all_but_last = [&]() {
             if (nc == 14) __builtin_amdgcn_s_waitcnt(waitcnt_vm(14));
@@ -1414,8 +1431,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
         for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     __syncthreads();                                             // step 0 has landed
     int st = 0;
-    for (int it = 0; it < ntile; ++it) {
-        for (int ks = 0; ks < KS; ++ks) {
+    for (int iu = 0; iu < nunit; ++iu) {
+        int k0, k1;
+        unit_steps(iu, k0, k1);
+        for (int ks = k0; ks < k1; ++ks) {
             const uint8_t *sp = smem + st * Lw::STAGE;
             const uint8_t *sa = sp + Lw::A_OFF + wm * 128 * 128;
             int sas[FM], sbs[FN];
@@ -1441,17 +1460,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                 __builtin_amdgcn_sched_barrier(0);      // keep the read of row i + 1 ahead of row i's MFMAs
             }
             st = st == Lw::NST - 1 ? 0 : st + 1;
-            if (ks == KS - 1) {
-                // the tile's C: this wave's rows and columns that lie inside C
+            if (ks == k1 - 1) {
+                // the unit's C (or its slice's fp32 partial): this wave's rows
+                // and columns that lie inside C
+                const int u = first + iu * stride;
                 int tm, tn;
-                grouped_order(first + it * stride, p.tiles_m, p.tiles_n, tm, tn);
+                grouped_order(u % T, p.tiles_m, p.tiles_n, tm, tn);
                 const int64_t row0 = (int64_t)tm * Lw::BM + wm * 128, col0 = (int64_t)tn * Lw::BN + wn * 64;
                 const int64_t rows_here = p.M - row0, cols_here = p.N - col0;
+                uint8_t *cbase = static_cast<uint8_t *>(p.c) + (S > 1 ? (int64_t)(u / T) * p.c_stride * 4 : 0);
                 if (rows_here > 0 && cols_here > 0) {
                     const int rh = (int)min(rows_here, (int64_t)128), chh = (int)min(cols_here, (int64_t)64);
                     const uint32_t range = (uint32_t)(((int64_t)(rh - 1) * p.N + chh) * ES);
-                    const __amdgpu_buffer_rsrc_t rc =
-                        make_rsrc(static_cast<uint8_t *>(p.c) + (row0 * p.N + col0) * ES, range);
+                    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cbase + (row0 * p.N + col0) * ES, range);
                     const int r0 = lane & 15;
 #pragma unroll
                     for (int i = 0; i < FM; ++i) {
@@ -1788,6 +1809,42 @@ hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint
     else
         hipLaunchKernelGGL((gemm_kernel<256, 128, 4, true, false, false, true, false, 2, false, false, true>), grid,
                            block, 0, stream, p);
+    return hipGetLastError();
+}
+
+// Packed A and B with K split into slices (the plan of splitk_plan): the
+// copying / computing-wave launch walks (tile, slice) units and writes each
+// slice's fp32 partial tile to `workspace` + slice * c_stride (the layout of
+// gemm_splitk_kernel's partials), then splitk_reduce_kernel sums them in
+// slice order.  Each partial is the same MFMA sequence as in the canonical-A
+// split launch, so C is bit-identical to it.  Needs N % 4 == 0 and
+// 128 * N * 4 < 2^31 (the fp32 partial stores); the caller checks.
+hipError_t launch_gemm_packed_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                     const uint8_t *b_s, int64_t M, int64_t N, int64_t K, void *c,
+                                     bool c_bf16, const SplitPlan &sp, float *workspace, hipStream_t stream) {
+    GemmParams p{};
+    p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = workspace;
+    p.M = M; p.N = N; p.K = K;
+    p.KS = (int)packed_ksteps(K);
+    p.NP = (int)packed_panels(N);
+    p.G = 1;
+    p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
+    p.tiles_m = (int)ceil_div(M, 256);
+    p.tiles_n = (int)ceil_div(N, 128);
+    p.splits = sp.splits;
+    p.split_steps = sp.split_steps;
+    p.c_stride = (M * N + 3) / 4 * 4;
+    const int64_t units = (int64_t)p.tiles_m * p.tiles_n * sp.splits;
+    dim3 grid((unsigned)std::min<int64_t>(units, device_cu_count())), block(kThreads);
+    hipLaunchKernelGGL(gemm_ws_kernel<false>, grid, block, 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = M * N;
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(n / 4, 256), 4096));
+    if (c_bf16) hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                                   workspace, sp.splits, n, p.c_stride, c);
+    else hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                            workspace, sp.splits, n, p.c_stride, c);
     return hipGetLastError();
 }
 

@@ -114,6 +114,9 @@ hipError_t launch_repack(const uint8_t *q, const uint8_t *scales, int64_t batch,
 
 hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
                               int64_t M, int64_t N, int64_t K, void *c, bool c_bf16, hipStream_t stream);
+hipError_t launch_gemm_packed_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                     const uint8_t *b_s, int64_t M, int64_t N, int64_t K, void *c,
+                                     bool c_bf16, const SplitPlan &sp, float *workspace, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                        const uint8_t *b_s, bool b_packed, int64_t M, int64_t N, int64_t K, void *c,
                        bool c_bf16, hipStream_t stream);

@@ -83,6 +83,17 @@ def test_argument_errors_before_any_device_work(libmx):
         args = [p, p, p, p, p]
         args[i] = q
         assert libmx.mxfp8_gemm_packed(args[0], args[1], args[2], args[3], 4, 4, 128, args[4], 0, NULL) == 5, i
+    # ... split over K: the same checks, plus the workspace's alignment
+    sk = libmx.mxfp8_gemm_packed_splitk
+    assert sk(p, p, p, p, 4, 4, 64, p, 0, p, 1024, NULL) == 2                      # K % 128
+    assert sk(p, p, p, p, 4, 0, 128, p, 0, p, 1024, NULL) == 2                     # N
+    assert sk(p, p, p, p, 4, 4, 128, p, 7, p, 1024, NULL) == 4                     # dtype
+    assert sk(p, p, NULL, p, 4, 4, 128, p, 0, p, 1024, NULL) == 1                  # NULL
+    assert sk(p, p, p, p, 4, 4, 128, p, 0, q, 1024, NULL) == 5                     # workspace alignment
+    for i in range(5):
+        args = [p, p, p, p, p]
+        args[i] = q
+        assert sk(args[0], args[1], args[2], args[3], 4, 4, 128, args[4], 0, NULL, 0, NULL) == 5, i
     assert libmx.mxfp8_dequantize(p, p, 4, 32, 1, p, 5, NULL) == 4
     assert libmx.mxfp8_repack(p, p, 1, 4, 40, p, p, NULL) == 2
     # fused quantizers

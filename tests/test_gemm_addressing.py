@@ -743,3 +743,41 @@ def test_ws_stores_cover_c_once(M, N, es):
                     for c in range(width):
                         np.add.at(hits, (row0 + r[ok]) * N + col0 + cl[ok] + c, 1)
     assert np.all(hits == 1), (M, N)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 1024), (300, 4096, 4096), (512, 6144, 4096), (512, 4096, 12288),
+                                   (32, 1000, 2048)])
+def test_ws_split_units_cover_k_and_partials_stay_inside(M, N, K):
+    """The split launch of gemm_ws_kernel: units u = (tile u % T, slice u / T)
+    dealt like tiles; every unit has at least one k-step, each tile's slices
+    tile [0, KS) exactly, and every partial store (the fp32 path, slice s at
+    s * c_stride elements) stays inside the workspace."""
+    S, L = splitk_plan(M, N, K)
+    assert S > 1
+    KS = ceil_div(K, KSTEP)
+    tiles_m, tiles_n = ceil_div(M, 256), ceil_div(N, 128)
+    T = tiles_m * tiles_n
+    c_stride = (M * N + 3) // 4 * 4
+    ws_bytes = S * c_stride * 4
+    covered = {}
+    nwg = min(T * S, 256)
+    for wg in range(nwg):
+        first, stride, count = ws_tiles(wg, nwg, T * S)
+        for i in range(count):
+            u = first + i * stride
+            tile, sl = u % T, u // T
+            k0, k1 = sl * L, min(KS, sl * L + L)
+            assert k0 < k1, (u, k0, k1)
+            covered.setdefault(tile, []).append((k0, k1))
+            tm, tn = grouped_order(tile, tiles_m, tiles_n)
+            for w in range(4):
+                row0, col0 = tm * 256 + (w >> 1) * 128, tn * 128 + (w & 1) * 64
+                if row0 >= M or col0 >= N:
+                    continue
+                rh, chh = min(M - row0, 128), min(N - col0, 64)
+                base = sl * c_stride * 4 + (row0 * N + col0) * 4
+                assert base + ((rh - 1) * N + chh) * 4 <= ws_bytes
+    assert sorted(covered) == list(range(T))
+    for tile, r in covered.items():
+        r.sort()
+        assert r[0][0] == 0 and r[-1][1] == KS and all(a[1] == b[0] for a, b in zip(r, r[1:])), tile

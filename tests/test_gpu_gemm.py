@@ -583,3 +583,49 @@ def test_gemm_splitk_matches_oracle(mx, oracle_mod, M, N, K, out):
     assert ok, worst
     none = torch.empty(0, dtype=torch.uint8, device=a_q.device)
     assert np.array_equal(host(mx.gemm(a_q, a_s, packed, tdt, workspace=none)), host(mx.gemm(a_q, a_s, packed, tdt)))
+
+
+@pytest.mark.parametrize("M,N,K,out", [(64, 256, 1024, "bf16"), (300, 4096, 4096, "f32"), (512, 6144, 4096, "bf16"),
+                                       (512, 4096, 12288, "bf16"), (32, 1000, 2048, "f32"), (512, 1002, 1024, "bf16")])
+def test_gemm_packed_splitk_matches_canonical_split(mx, oracle_mod, M, N, K, out):
+    """mxfp8_gemm_packed_splitk: the copying/computing-wave launch over
+    (tile, K slice) units, fp32 partials summed in slice order.  Bit-identical
+    to mxfp8_gemm_splitk over the canonical grids (the same slices and
+    per-slice products), with the full workspace and with one too small for
+    the full split (fewer slices, the same fitted plan on both sides); N % 4
+    != 0 (512x1002) and no workspace fall back to mxfp8_gemm_packed exactly;
+    the smaller shapes also against the oracle."""
+    import torch
+    _say("gemm packed splitk", M, N, K, out, mx.gemm_splitk_workspace_bytes(M, N, K))
+    rng = np.random.default_rng(M * 3 + N + K)
+    X = wl.normal_bf16(rng, (M, K))
+    W = wl.normal_bf16(rng, (N, K), std=0.02)
+    xq, xs = _quant_pair(oracle_mod, X)
+    wq, ws = _quant_pair(oracle_mod, W)
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    a_q, a_s = to_dev(xq), to_dev(xs)
+    B = mx.repack(to_dev(wq), to_dev(ws))
+    A = mx.repack(a_q, a_s)
+
+    def host(c):
+        torch.cuda.synchronize()
+        return to_host(c.float()) if out == "bf16" else to_host(c)
+
+    need = mx.gemm_splitk_workspace_bytes(M, N, K)
+    assert need > 0
+    full = torch.empty(need, dtype=torch.uint8, device=a_q.device)
+    c1 = host(mx.gemm_packed(A, B, tdt, workspace=full))
+    if N % 4 == 0:
+        assert np.array_equal(c1, host(mx.gemm(a_q, a_s, B, tdt, workspace=full)))
+        half = torch.empty(need // 2 + 16, dtype=torch.uint8, device=a_q.device)
+        assert np.array_equal(host(mx.gemm_packed(A, B, tdt, workspace=half)),
+                              host(mx.gemm(a_q, a_s, B, tdt, workspace=half)))
+    else:
+        assert np.array_equal(c1, host(mx.gemm_packed(A, B, tdt)))
+    none = torch.empty(0, dtype=torch.uint8, device=a_q.device)
+    assert np.array_equal(host(mx.gemm_packed(A, B, tdt, workspace=none)), host(mx.gemm_packed(A, B, tdt)))
+    assert np.array_equal(host(mx.gemm_packed(A, B, tdt, workspace=full)), c1)       # deterministic
+    if M * N * K <= 2 ** 31:
+        ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
+        ok, worst = oracle_mod.gemm_bound_ok(c1, ref, sabs, out)
+        assert ok, worst
