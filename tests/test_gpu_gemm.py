@@ -417,7 +417,8 @@ def _moe_case(oracle_mod, G, N, K, tokens, topk, seed, empty=()):
                                                (16, 512, 768, 1024, 4),
                                                # groups of 256+ rows: the persistent launch, more
                                                # tiles than CUs (K % 512 != 0 and == 0)
-                                               (8, 1024, 768, 8192, 2), (8, 1024, 1024, 8192, 2)])
+                                               (8, 1024, 768, 8192, 2), (8, 1024, 1024, 8192, 2),
+                                               (4, 200, 512, 2048, 2)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_grouped_gemm_small(mx, oracle_mod, G, N, K, tokens, topk, out):
     aq, as_, bq, bs, off, row_token = _moe_case(oracle_mod, G, N, K, tokens, topk, G + N,
@@ -455,6 +456,32 @@ def test_grouped_gemm_untouched_rows_outside_groups(mx, oracle_mod):
     ch = to_host(out)
     inside = grp >= 0
     ok, worst = oracle_mod.gemm_bound_ok(ch[inside], ref[inside], sabs[inside], "f32")
+    assert ok, worst
+    assert np.all(ch[~inside] == -3.0)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_grouped_gemm_persistent_rows_outside_groups(mx, oracle_mod, out):
+    """The 256-row persistent grouped launch (M_total >= 256 G) with rows in
+    no group ([0, 64) and [960, 1024)) and an empty group: those rows
+    untouched, every group row within the bound."""
+    G, N, K = 3, 264, 384
+    rng = np.random.default_rng(35)
+    M = 1024
+    aq, as_ = oracle_mod.quantize(wl.normal_bf16(rng, (M, K)), 1)
+    W = wl.normal_bf16(rng, (G, N, K), std=0.02)
+    bq = np.stack([oracle_mod.quantize(W[g], 1)[0] for g in range(G)])
+    bs = np.stack([oracle_mod.quantize(W[g], 1)[1] for g in range(G)])
+    off = np.array([64, 320, 320, 960], np.int32)
+    ref, sabs, grp = oracle_mod.grouped_gemm(aq, as_, bq, bs, off)
+    w = mx.repack(to_dev(bq), to_dev(bs))
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    res = torch.full((M, N), -3.0, dtype=tdt, device="cuda")
+    _say("grouped persistent untouched rows", out)
+    mx.grouped_gemm(to_dev(aq), to_dev(as_), w, to_dev(off), tdt, out=res)
+    ch = to_host(res.float())
+    inside = grp >= 0
+    ok, worst = oracle_mod.gemm_bound_ok(ch[inside], ref[inside], sabs[inside], out)
     assert ok, worst
     assert np.all(ch[~inside] == -3.0)
 
