@@ -350,7 +350,7 @@ def test_gemm_qkv_full_output(mx, oracle_mod):
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 512), (1000, 96, 1024), (513, 264, 4096),
                                    (2048, 9216, 512), (512, 32768, 256), (4096, 9216, 512), (3072, 9216, 512),
-                                   (4096, 6140, 512), (300, 4100, 384)])
+                                   (4096, 6140, 512), (300, 4100, 384), (1, 8, 128), (33, 4, 128)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_packed_a_matches_canonical(mx, oracle_mod, M, N, K, out):
     """mxfp8_gemm_packed: A quantized straight into the packed layout
@@ -361,7 +361,8 @@ def test_gemm_packed_a_matches_canonical(mx, oracle_mod, M, N, K, out):
     fp32 output wherever N % 4 == 0), and otherwise the 256x256 tiles
     (3072x9216), the mixed launch (4096x9216: 32 large + 8 small tile
     columns), the paired launch (4096x6140 bf16: N % 8 != 0) and 256x128
-    tiles (300x4100 bf16); the smaller cases also against the oracle."""
+    tiles (300x4100 bf16); a single row (1x8) and N = 4 (33x4); the smaller
+    cases also against the oracle."""
     rng = np.random.default_rng(M * 7 + N + K)
     x = wl.normal_bf16(rng, (M, K))
     w = wl.normal_bf16(rng, (N, K), std=0.02)

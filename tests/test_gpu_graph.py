@@ -322,3 +322,77 @@ def test_graph_replay_quantize_many_and_packed_axis0(mx, oracle_mod):
             q0, s0 = oracle_mod.quantize(w, 0)
             qp, sp = oracle_mod.pack(q0.reshape(1, K, N), s0.reshape(1, K, N // 32), 1, K, N)
             assert np.array_equal(to_host(g_buf["wt"].q), qp) and np.array_equal(to_host(g_buf["wt"].s), sp)
+
+
+def test_graph_replay_packed_step_and_packed_split(mx, oracle_mod):
+    """The default bench step's calls (W along K into its canonical grid and X
+    straight into the packed operand layout in one mxfp8_quantize_many_layouts
+    launch, repack of W, mxfp8_gemm_packed) and the packed split-K call
+    (mxfp8_gemm_packed_splitk with its workspace), recorded once and replayed
+    on new inputs: every replay equals the eager calls bit for bit."""
+    import torch
+    M, N, K = 300, 264, 1024
+    Ms = 512                                        # the split case: 2 x 8 tiles, two K slices
+    _say("packed step + packed split", M, N, K, Ms)
+    dev = torch.device("cuda:0")
+    X = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    Xs = torch.empty((Ms, K), dtype=torch.bfloat16, device=dev)
+    W = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    need = mx.gemm_splitk_workspace_bytes(Ms, N, K)
+    assert need > 0
+
+    def pw(rows):
+        return mx.PackedWeight(torch.empty(mx.packed_bytes(1, rows, K, 0), dtype=torch.uint8, device=dev),
+                               torch.empty(mx.packed_bytes(1, rows, K, 1), dtype=torch.uint8, device=dev), 1, rows, K)
+
+    def buffers():
+        return dict(wq=torch.empty((N, K), dtype=torch.uint8, device=dev),
+                    ws=torch.empty((N, K // 32), dtype=torch.uint8, device=dev),
+                    w=pw(N), a=pw(M), a2=pw(Ms),
+                    y=torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                    y2=torch.empty((Ms, N), dtype=torch.float32, device=dev),
+                    wk=torch.empty(need, dtype=torch.uint8, device=dev))
+
+    def step(b):
+        mx.quantize_many_layouts_([(W, (b["wq"], b["ws"])), (X, b["a"]), (Xs, b["a2"])])
+        mx.repack_(b["wq"], b["ws"], b["w"])
+        mx.gemm_packed(b["a"], b["w"], torch.bfloat16, out=b["y"])
+        mx.gemm_packed(b["a2"], b["w"], torch.float32, out=b["y2"], workspace=b["wk"])
+
+    g_buf, e_buf = buffers(), buffers()
+    for t in (X, Xs, W):
+        t.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_buf)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        rng = np.random.default_rng(300 + rep)
+        x = wl.normal_bf16(rng, (M, K), outlier_frac=0.01)
+        xs = wl.normal_bf16(rng, (Ms, K))
+        w = wl.normal_bf16(rng, (N, K), std=0.02)
+        X.copy_(to_dev(x))
+        Xs.copy_(to_dev(xs))
+        W.copy_(to_dev(w))
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_buf)
+        torch.cuda.synchronize()
+        for key in ("wq", "ws", "y", "y2"):
+            assert np.array_equal(to_host(g_buf[key]), to_host(e_buf[key])), (rep, key)
+        for key in ("w", "a", "a2"):
+            assert np.array_equal(to_host(g_buf[key].q), to_host(e_buf[key].q)), (rep, key)
+            assert np.array_equal(to_host(g_buf[key].s), to_host(e_buf[key].s)), (rep, key)
+        if rep == 0:
+            xq, xsc = oracle_mod.quantize(x, 1)
+            wq, wsc = oracle_mod.quantize(w, 1)
+            qp, sp = oracle_mod.pack(xq.reshape(1, M, K), xsc.reshape(1, M, K // 32), 1, M, K)
+            assert np.array_equal(to_host(g_buf["a"].q), qp) and np.array_equal(to_host(g_buf["a"].s), sp)
+            c_ref, c_abs = oracle_mod.gemm(xq, xsc, wq, wsc)
+            ok, worst = oracle_mod.gemm_bound_ok(wl.bf16_bits_to_f32(to_host(g_buf["y"])), c_ref, c_abs, "bf16")
+            assert ok, worst
+            x2q, x2s = oracle_mod.quantize(xs, 1)
+            c2, a2 = oracle_mod.gemm(x2q, x2s, wq, wsc)
+            ok, worst = oracle_mod.gemm_bound_ok(to_host(g_buf["y2"]), c2, a2, "f32")
+            assert ok, worst
