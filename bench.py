@@ -520,10 +520,12 @@ def bench_mlp(args, dev):
 
 def bench_moe(args, dev):
     """Qwen3-30B-A3B MoE layer forward (8192 tokens, 128 experts, Zipf(1.1)
-    top-8, groups padded to 32): quantize the gathered gate_up input, grouped
-    GEMM gate_up -> bf16, quantize the down input, grouped GEMM down -> bf16.
+    top-8, groups padded to 32): quantize the gathered gate_up input straight
+    into the GEMM's packed operand layout, grouped GEMM gate_up -> bf16
+    (mxfp8_grouped_gemm_packed), the same for the down input and GEMM.
     Expert weights are quantized and repacked beforehand (weight sync, timed
-    separately); offsets stay on the device."""
+    separately); offsets stay on the device.  The canonical-A grouped GEMMs
+    over the same inputs are timed in a pass of their own, for reference."""
     import torch
     import mxfp8_block_scaled_05_amd as mx
     import workloads as wl
@@ -551,6 +553,10 @@ def bench_moe(args, dev):
     agu_s = torch.empty((Mt, H // 32), dtype=torch.uint8, device=dev)
     ad_q = torch.empty((Mt, I), dtype=torch.uint8, device=dev)
     ad_s = torch.empty((Mt, I // 32), dtype=torch.uint8, device=dev)
+    agu_p = mx.PackedWeight(torch.empty(mx.packed_bytes(1, Mt, H, 0), dtype=torch.uint8, device=dev),
+                            torch.empty(mx.packed_bytes(1, Mt, H, 1), dtype=torch.uint8, device=dev), 1, Mt, H)
+    ad_p = mx.PackedWeight(torch.empty(mx.packed_bytes(1, Mt, I, 0), dtype=torch.uint8, device=dev),
+                           torch.empty(mx.packed_bytes(1, Mt, I, 1), dtype=torch.uint8, device=dev), 1, Mt, I)
     y_gu = torch.empty((Mt, I2), dtype=torch.bfloat16, device=dev)
     y_d = torch.empty((Mt, H), dtype=torch.bfloat16, device=dev)
     sync_ops = [
@@ -560,14 +566,22 @@ def bench_moe(args, dev):
         ("sync_repack_W_d", lambda: mx.repack_(wd_q.view(G, H, I), wd_s.view(G, H, I // 32), P_d)),
     ]
     ops = [
-        ("quantize_A_gu", lambda: mx.quantize_into(A_gu, 1, agu_q, agu_s)),
-        ("grouped_gemm_gate_up", lambda: mx.grouped_gemm(agu_q, agu_s, P_gu, offs, torch.bfloat16, out=y_gu)),
-        ("quantize_A_d", lambda: mx.quantize_into(A_d, 1, ad_q, ad_s)),
-        ("grouped_gemm_down", lambda: mx.grouped_gemm(ad_q, ad_s, P_d, offs, torch.bfloat16, out=y_d)),
+        ("quantize_A_gu", lambda: mx.quantize_many_layouts_([(A_gu, agu_p)])),
+        ("grouped_gemm_gate_up", lambda: mx.grouped_gemm_packed(agu_p, P_gu, offs, torch.bfloat16, out=y_gu)),
+        ("quantize_A_d", lambda: mx.quantize_many_layouts_([(A_d, ad_p)])),
+        ("grouped_gemm_down", lambda: mx.grouped_gemm_packed(ad_p, P_d, offs, torch.bfloat16, out=y_d)),
+    ]
+    ref_ops = [
+        ("quantize_A_gu_canonical", lambda: mx.quantize_into(A_gu, 1, agu_q, agu_s)),
+        ("grouped_gemm_gate_up_canonical_A", lambda: mx.grouped_gemm(agu_q, agu_s, P_gu, offs, torch.bfloat16,
+                                                                     out=y_gu)),
+        ("quantize_A_d_canonical", lambda: mx.quantize_into(A_d, 1, ad_q, ad_s)),
+        ("grouped_gemm_down_canonical_A", lambda: mx.grouped_gemm(ad_q, ad_s, P_d, offs, torch.bfloat16, out=y_d)),
     ]
     torch.cuda.synchronize()
     sync_ms, sync_avg = run_timed(sync_ops, argparse.Namespace(steps=max(3, args.steps // 10), warmup=1))
     ms, avg = run_timed(ops, args, live=("grouped_gemm_gate_up",))
+    _, ref_avg = run_timed(ref_ops, argparse.Namespace(steps=max(3, args.steps // 2), warmup=1))
     flops_gu = 2.0 * real * I2 * H
     flops_d = 2.0 * real * H * I
     eb = 1 + 1 / 32
@@ -582,6 +596,11 @@ def bench_moe(args, dev):
         kern[key] = {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4),
                      "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                      "roofline_us": round(max(fl / MXFP8_PEAK_TFLOPS / 1e12, by / HBM_PEAK_GBS / 1e9) * 1e6, 1)}
+    for key, fl in (("grouped_gemm_gate_up_canonical_A", flops_gu), ("grouped_gemm_down_canonical_A", flops_d)):
+        tf = fl / (ref_avg[key] * 1e-6) / 1e12
+        kern[key] = {"us": round(ref_avg[key], 2), "TFLOP/s": round(tf, 1),
+                     "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4),
+                     "note": "mxfp8_grouped_gemm over the canonical grid of the same rows, a pass of its own"}
     for key in ("sync_quantize_W_gu", "sync_quantize_W_d"):
         n = G * I2 * H if key.endswith("gu") else G * H * I
         kern[key] = _bw(sync_avg[key], n * Q_BYTES_PER_ELT)
@@ -593,7 +612,8 @@ def bench_moe(args, dev):
                  round((flops_gu + flops_d) / (ms * 1e-3) / 1e12, 2), "TFLOP/s", args, ms,
                  "mxfp8-e4m3/e8m0, fp32 accumulate, bf16 out",
                  {"workload": "qwen3-30b-a3b MoE layer forward, 8192 tokens, 128 experts, Zipf(1.1) top-8, "
-                              "groups padded to 32: quantize + grouped GEMM gate_up, quantize + grouped GEMM down",
+                              "groups padded to 32: quantize (into the packed operand layout) + grouped GEMM "
+                              "gate_up, the same for down",
                   "tokens": 8192, "experts": G, "rows_real": real, "rows_padded": Mt},
                  kernels=kern, flops_basis="unpadded rows (padded FLOPs are %.1f%% more)" % (100.0 * (Mt / real - 1)),
                  roofline={"bound": "mfma", "achieved": top["TFLOP/s"], "peak": MXFP8_PEAK_TFLOPS,

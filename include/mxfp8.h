@@ -545,6 +545,30 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s,
                                 mxfp8_dtype c_dtype, hipStream_t stream);
 
 /*
+ * mxfp8_grouped_gemm_packed -- mxfp8_grouped_gemm with A in the packed layout.
+ *
+ * The expert GEMMs' token rows quantized straight into the kernel layout
+ * (mxfp8_quantize_many_layouts, MXFP8_PACKED, or mxfp8_repack of the
+ * canonical grid), as the dense mxfp8_gemm_packed reads them (section "The
+ * pipeline", sampler paragraph: kernel-specific layouts).
+ *   A : the mxfp8_repack layout of q[M_total][K], s[M_total][K/32]
+ *       (batch 1, N = M_total; mxfp8_packed_bytes(1, M_total, K, 0 / 1)).
+ *   B, d_group_offsets, C, G, M_total, N: as mxfp8_grouped_gemm.
+ * K % 128 == 0 (MXFP8_ERR_SHAPE otherwise).  C is bit-identical to
+ * mxfp8_grouped_gemm over the canonical grid of the same A (the same products
+ * in the same order per element); rows outside [o_0, o_G) are not written.
+ * Each tile's A copies read 8-row segments of its panel rows, so a group
+ * starting inside a panel costs nothing extra; segments past the group's
+ * rows read zeros, never the next group's rows.  No allocation, no
+ * synchronization.
+ */
+mxfp8_status mxfp8_grouped_gemm_packed(const uint8_t *a_q_packed, const uint8_t *a_s_packed,
+                                       const uint8_t *b_q_packed, const uint8_t *b_s_packed,
+                                       const int32_t *d_group_offsets, int64_t G, int64_t M_total,
+                                       int64_t N, int64_t K, void *c, mxfp8_dtype c_dtype,
+                                       hipStream_t stream);
+
+/*
  * mxfp8_grouped_gemm_wgrad -- the experts' weight gradients:
  *   for g in 0..G-1:  C[g] = A[:, o_g : o_{g+1}] * B[:, o_g : o_{g+1}]^T
  *

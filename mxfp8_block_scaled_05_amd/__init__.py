@@ -22,7 +22,7 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["lib", "quantize", "quantize_into", "dequantize", "packed_bytes", "PackedWeight",
-           "repack", "repack_", "quantize_packed_axis0_", "quantize_many_", "quantize_packed_many_", "gemm", "grouped_gemm", "MXFP8Error", "LIB_PATH"]
+           "repack", "repack_", "quantize_packed_axis0_", "quantize_many_", "quantize_packed_many_", "gemm", "grouped_gemm", "grouped_gemm_packed", "MXFP8Error", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
 
@@ -74,6 +74,8 @@ def lib():
         L.mxfp8_gemm_packed.restype = I32
         L.mxfp8_gemm_packed_splitk.argtypes = [P, P, P, P, I64, I64, I64, P, I32, P, ctypes.c_size_t, P]
         L.mxfp8_gemm_packed_splitk.restype = I32
+        L.mxfp8_grouped_gemm_packed.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        L.mxfp8_grouped_gemm_packed.restype = I32
         L.mxfp8_quantize_many_layouts.argtypes = [P, I64, P]
         L.mxfp8_quantize_many_layouts.restype = I32
         L.mxfp8_gemm_splitk_noalloc.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
@@ -699,6 +701,38 @@ def grouped_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, offsets:
     _check(lib().mxfp8_grouped_gemm(_ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s), _ptr(offsets), G,
                                     M_total, w.N, K, _ptr(out), code, _stream(a_q.device)),
            "mxfp8_grouped_gemm")
+    return out
+
+
+def grouped_gemm_packed(a: PackedWeight, w: PackedWeight, offsets: torch.Tensor,
+                        out_dtype=torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """grouped_gemm with A in the packed layout (mxfp8_grouped_gemm_packed):
+    ``a`` is the packed layout of the [M_total, K] rows (batch 1, a.N =
+    M_total), e.g. from quantize_many_layouts_; K % 128 == 0."""
+    for name, t in (("a", a), ("w", w)):
+        if not isinstance(t, PackedWeight):
+            raise ValueError("%s must be a PackedWeight" % name)
+        _need(t.q, torch.uint8, name + ".q")
+        _need(t.s, torch.uint8, name + ".s")
+    if a.batch != 1:
+        raise ValueError("a must be a single packed [M_total, K] matrix")
+    _need(offsets, torch.int32, "offsets")
+    M_total, K = a.N, a.K
+    if w.K != K:
+        raise ValueError("K mismatch")
+    G = w.batch
+    if offsets.numel() != G + 1:
+        raise ValueError("offsets must have G + 1 = %d entries" % (G + 1))
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((M_total, w.N), dtype=out_dtype, device=a.q.device)
+    else:
+        _need(out, out_dtype, "out")
+        if tuple(out.shape) != (M_total, w.N):
+            raise ValueError("out must be [M_total, N]")
+    _check(lib().mxfp8_grouped_gemm_packed(_ptr(a.q), _ptr(a.s), _ptr(w.q), _ptr(w.s), _ptr(offsets), G,
+                                           M_total, w.N, K, _ptr(out), code, _stream(a.q.device)),
+           "mxfp8_grouped_gemm_packed")
     return out
 
 

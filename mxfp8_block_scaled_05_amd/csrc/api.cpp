@@ -599,4 +599,23 @@ mxfp8_status mxfp8_grouped_gemm(const uint8_t *a_q, const uint8_t *a_s, const ui
                                       M_total, N, K, c, raw(c_dtype) == MXFP8_BF16, stream));
 }
 
+mxfp8_status mxfp8_grouped_gemm_packed(const uint8_t *a_q_packed, const uint8_t *a_s_packed,
+                                       const uint8_t *b_q_packed, const uint8_t *b_s_packed,
+                                       const int32_t *d_group_offsets, int64_t G, int64_t M_total, int64_t N,
+                                       int64_t K, void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
+    if (!a_q_packed || !a_s_packed || !b_q_packed || !b_s_packed || !d_group_offsets || !c) return MXFP8_ERR_NULL;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    if (G < 1 || G > 65535 || M_total < 0 || M_total % 32 || M_total >= kMaxDim) return MXFP8_ERR_SHAPE;
+    if (N <= 0 || N >= kMaxDim || K < 128 || K % 128 || K > kMaxK) return MXFP8_ERR_SHAPE;
+    if ((ceil_div(M_total, 256) + G) * ceil_div(N, 256) >= ((int64_t)1 << 31)) return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q_packed) || !aligned16(a_s_packed) || !aligned16(b_q_packed) || !aligned16(b_s_packed) ||
+        !aligned16(c))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    if (M_total == 0) return MXFP8_OK;
+    return finish(launch_grouped_gemm_packed(a_q_packed, a_s_packed, b_q_packed, b_s_packed, d_group_offsets, G,
+                                             M_total, N, K, c, raw(c_dtype) == MXFP8_BF16, stream));
+}
+
 }  // extern "C"

@@ -267,6 +267,7 @@ struct TileOps {
     __amdgpu_buffer_rsrc_t rsa_c, rsb_c;
     int Ki, KBi, lane, w, wm, wn, lrow, lblk;
     int rows_a, rows_b;        // rows of the A and B tiles inside the operands
+    int a_r0, KSa;             // APACK: the tile's first row in its first panel; k-steps per panel
     int lda, lsa, ldb, lsb;    // row strides of canonical operands (bytes)
     uint32_t lds0;
 
@@ -296,11 +297,16 @@ struct TileOps {
         const uint32_t a_bytes = (uint32_t)((rows_a - 1) * p.lda + K);
         const uint32_t as_bytes = (uint32_t)((rows_a - 1) * p.lsa + KB);
         if constexpr (APACK) {
-            // A's panel m0 / 256 from k-step s0 on (m0 % 256 == 0: dense tiles)
-            const int64_t pa = m0 / kPanelRows, s0 = kbase / 128;
-            ra = make_srd(p.a_q + (pa * p.KS + s0) * kTileBytes, (uint32_t)((int64_t)(p.KS - s0) * kTileBytes));
-            rsa = make_srd(p.a_s + (pa * p.KS + s0) * kScaleStepBytes,
-                           (uint32_t)((int64_t)(p.KS - s0) * kScaleStepBytes));
+            // A's panels from m0 / 256 on (K from 0: kbase == 0 for packed A).
+            // Dense tiles start a panel; grouped tiles start at any row of a
+            // group (a multiple of 32) and may run into the next panel, so the
+            // descriptors span two panels where there are two, and each
+            // 8-row copy segment / 16-row scale atom finds its own panel row.
+            const int64_t pa = m0 / kPanelRows, np = min((int64_t)2, (p.M + kPanelRows - 1) / kPanelRows - pa);
+            a_r0 = (int)(m0 % kPanelRows);
+            KSa = p.KS;
+            ra = make_srd(p.a_q + pa * p.KS * kTileBytes, (uint32_t)(np * p.KS * kTileBytes));
+            rsa = make_srd(p.a_s + pa * p.KS * kScaleStepBytes, (uint32_t)(np * p.KS * kScaleStepBytes));
             rsa_c = make_rsrc(p.a_s, 0u);
             (void)a_bytes;
             (void)as_bytes;
@@ -328,6 +334,24 @@ struct TileOps {
         }
     }
 
+    // APACK: offset of this lane's 16 bytes of the tile's 8-row segment seg at
+    // k-step ks (segments past the tile's rows read zeros: in a grouped tile
+    // the panel rows past the group are another group's)
+    __device__ __forceinline__ uint32_t apack_off(int ks, int seg) const {
+        const int row = a_r0 + seg * 8;
+        return seg * 8 < rows_a ? ((uint32_t)((row >> 8) * KSa + ks) * (uint32_t)kTileBytes +
+                                   (uint32_t)((row & 255) * 128 + lane * 16))
+                                : kOOB;
+    }
+    // APACK: this lane's dword of the scale records of atoms 4q .. 4q + 3
+    // (lane l: atom 4q + l / 16, dword l % 16 of its 64-byte record)
+    __device__ __forceinline__ uint32_t apack_scale_off(int ks, int q) const {
+        const int a = q * 4 + (lane >> 4), row = a_r0 + a * 16;
+        return a * 16 < rows_a ? ((uint32_t)((row >> 8) * KSa + ks) * (uint32_t)kScaleStepBytes +
+                                  (uint32_t)(((row & 255) >> 4) * 64 + (lane & 15) * 4))
+                               : kOOB;
+    }
+
     // global -> LDS copies of k-step ks into stage st (this wave's share)
     __device__ __forceinline__ void issue(int ks, int st) const { issue_at(ks, lds0 + st * STAGE); }
     // The copies of a 256-row tile with the two-stage ring are issued by
@@ -347,9 +371,8 @@ struct TileOps {
         for (int i = 0; i < BM / 32; ++i) {
             const int seg = i * 4 + cw;
             uint32_t off;
-            if constexpr (APACK) {
-                off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
-            } else {
+            if constexpr (APACK) off = apack_off(ks, seg);
+            else {
                 const int rr = seg * 8 + (lane >> 3);
                 const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
                 const int kk = ks * 128 + c * 16;
@@ -371,7 +394,7 @@ struct TileOps {
             }
             dma16(rb, off, sbase + BM * 128 + seg * 1024);
         }
-        if constexpr (APACK) dma4(rsa, (uint32_t)(ks * kScaleStepBytes + cw * 256 + lane * 4), sbase + SA_OFF + cw * 256);
+        if constexpr (APACK) dma4(rsa, apack_scale_off(ks, cw), sbase + SA_OFF + cw * 256);
         else if constexpr (SA_LDS) dma4(rsa, (uint32_t)((cw * 64 + lane) * lsa + ks * 4), sbase + SA_OFF + cw * 256);
         if constexpr (SB_LDS) {
             if (cw < BN / 64) {
@@ -393,9 +416,8 @@ struct TileOps {
         for (int i = 0; i < BM / (8 * kWaves); ++i) {
             const int seg = i * kWaves + w;            // 1 KB LDS segment = 8 rows
             uint32_t off;
-            if constexpr (APACK) {
-                off = (uint32_t)ks * (uint32_t)kTileBytes + seg * 1024 + lane * 16;
-            } else {
+            if constexpr (APACK) off = apack_off(ks, seg);
+            else {
                 const int rr = seg * 8 + (lane >> 3);
                 const int c = (lane & 7) ^ (int)swz((uint32_t)rr);
                 const int kk = ks * 128 + c * 16;
@@ -421,7 +443,7 @@ struct TileOps {
         if constexpr (SA_LDS) {
             if (w < BM / 64) {
                 const int rr = w * 64 + lane;
-                if constexpr (APACK) dma4(rsa, (uint32_t)(ks * kScaleStepBytes + w * 256 + lane * 4), sbase + SA_OFF + w * 256);
+                if constexpr (APACK) dma4(rsa, apack_scale_off(ks, w), sbase + SA_OFF + w * 256);
                 else dma4(rsa, (uint32_t)(rr * lsa + ks * 4), sbase + SA_OFF + w * 256);
             }
         }
@@ -1525,10 +1547,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
 // Between two tiles the next tile's first copies (and scale chunk) go into
 // the stage and chunk buffer the finished tile's last step did not read,
 // before its epilogue, which stages C in the other stage only -- the same
-// hand-over as gemm_pair_kernel.  Packed B, K % 128 == 0; SAC: K % 512 == 0.
-template <bool OUT_BF16, bool SAC>
+// hand-over as gemm_pair_kernel.  Packed B, K % 128 == 0; SAC: K % 512 == 0;
+// APACK: A in the packed layout too (the copies of each 8-row segment are one
+// contiguous KB wherever the group's tile starts).
+template <bool OUT_BF16, bool SAC, bool APACK = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_persist_kernel(GemmParams p) {
-    using T = TileOps<256, 256, 2, true, true, SAC>;
+    static_assert(!(SAC && APACK), "packed A carries its scales per step");
+    using T = TileOps<256, 256, 2, true, true, SAC, APACK>;
     constexpr uint32_t SB = T::STAGE, CH = 2 * T::STAGE;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE + (SAC ? 2 * T::CHUNK : 0)];
     const int lane = threadIdx.x & 63;
@@ -1571,7 +1596,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_grouped_persist_kernel(GemmP
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
             for (int jj = 0; jj < T::FN; ++jj) acc[i][jj] = v4f{0.f, 0.f, 0.f, 0.f};
-        pair_loop<256, 256, 2, SAC>(t, KS, smem, st, CH, ch_par, acc);
+        pair_loop<256, 256, 2, SAC, APACK>(t, KS, smem, st, CH, ch_par, acc);
         // the last step read st[(KS-1)&1] and chunk buffer
         // ((KS-1)/8 + ch_par)&1; the other stage and buffer are free
         const uint32_t st_free = st[KS & 1], st_busy = st[(KS - 1) & 1];
@@ -1921,6 +1946,28 @@ hipError_t launch_gemm_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint
                                    workspace, sp.splits, n, p.c_stride, c);
     else hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
                             workspace, sp.splits, n, p.c_stride, c);
+    return hipGetLastError();
+}
+
+// Grouped GEMM with packed A (the mxfp8_repack layout of the [M_total][K]
+// rows): always the persistent 256-row launch (K % 128 == 0), whatever the
+// group sizes; the same products per element as launch_grouped_gemm.
+hipError_t launch_grouped_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                      const uint8_t *b_s, const int32_t *offsets, int64_t G, int64_t M_total,
+                                      int64_t N, int64_t K, void *c, bool c_bf16, hipStream_t stream) {
+    GemmParams p{};
+    p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = c;
+    p.M = M_total; p.N = N; p.K = K;
+    p.KS = (int)packed_ksteps(K);
+    p.NP = (int)packed_panels(N);
+    p.G = (int)G;
+    p.offsets = offsets;
+    p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
+    p.tiles_m = (int)(ceil_div(M_total, 256) + G);
+    p.tiles_n = (int)ceil_div(N, 256);
+    dim3 grid((unsigned)device_cu_count()), block(kThreads);
+    if (c_bf16) hipLaunchKernelGGL((gemm_grouped_persist_kernel<true, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_grouped_persist_kernel<false, false, true>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

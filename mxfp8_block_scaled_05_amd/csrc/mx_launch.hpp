@@ -117,6 +117,9 @@ hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint
 hipError_t launch_gemm_packed_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                                      const uint8_t *b_s, int64_t M, int64_t N, int64_t K, void *c,
                                      bool c_bf16, const SplitPlan &sp, float *workspace, hipStream_t stream);
+hipError_t launch_grouped_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                      const uint8_t *b_s, const int32_t *offsets, int64_t G, int64_t M_total,
+                                      int64_t N, int64_t K, void *c, bool c_bf16, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                        const uint8_t *b_s, bool b_packed, int64_t M, int64_t N, int64_t K, void *c,
                        bool c_bf16, hipStream_t stream);

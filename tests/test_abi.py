@@ -83,6 +83,17 @@ def test_argument_errors_before_any_device_work(libmx):
         args = [p, p, p, p, p]
         args[i] = q
         assert libmx.mxfp8_gemm_packed(args[0], args[1], args[2], args[3], 4, 4, 128, args[4], 0, NULL) == 5, i
+    # grouped GEMM with packed A: K a multiple of 128
+    gp = libmx.mxfp8_grouped_gemm_packed
+    assert gp(p, p, p, p, p, 2, 64, 4, 64, p, 0, NULL) == 2                          # K % 128
+    assert gp(p, p, p, p, p, 2, 48, 4, 128, p, 0, NULL) == 2                         # M_total % 32
+    assert gp(p, p, p, p, p, 0, 64, 4, 128, p, 0, NULL) == 2                         # G
+    assert gp(p, p, p, p, p, 2, 64, 4, 128, p, 3, NULL) == 4                         # dtype
+    assert gp(p, p, p, p, NULL, 2, 64, 4, 128, p, 0, NULL) == 1                      # offsets NULL
+    for i in range(5):
+        args = [p, p, p, p, p]
+        args[i] = q
+        assert gp(args[0], args[1], args[2], args[3], p, 2, 64, 4, 128, args[4], 0, NULL) == 5, i
     # ... split over K: the same checks, plus the workspace's alignment
     sk = libmx.mxfp8_gemm_packed_splitk
     assert sk(p, p, p, p, 4, 4, 64, p, 0, p, 1024, NULL) == 2                      # K % 128

@@ -100,14 +100,28 @@ def descriptors(M, N, K, BM, BN, packed, G=1, m0=0, m_end=None, n0=0, g=0):
 
 
 def packed_a_descriptors(M, K, m0):
-    """mxfp8_gemm_packed's A descriptors for a tile at row m0 (m0 % 256 == 0):
-    panel m0 / 256 from k-step 0, its KS tiles and KS scale tiles."""
+    """The packed-A descriptors of a tile starting at row m0 (a multiple of 8):
+    from panel m0 / 256 on, two panels where there are two (a grouped tile
+    may run into the next panel), all their k-step tiles and scale tiles."""
     KS = ceil_div(K, KSTEP)
     MP = ceil_div(M, PANEL)
-    assert m0 % PANEL == 0
     pa = m0 // PANEL
-    return [("a_q", pa * KS * TILE_BYTES, KS * TILE_BYTES, MP * KS * TILE_BYTES),
-            ("a_s", pa * KS * 1024, KS * 1024, MP * KS * 1024)]
+    n = min(2, MP - pa)
+    return [("a_q", pa * KS * TILE_BYTES, n * KS * TILE_BYTES, MP * KS * TILE_BYTES),
+            ("a_s", pa * KS * 1024, n * KS * 1024, MP * KS * 1024)]
+
+
+def apack_offsets(m0, m_end, K, ks):
+    """Mirror of TileOps::apack_off / apack_scale_off: per 8-row segment the
+    byte offset of lane 0 (None past the tile's rows), per 16-row atom the
+    offset of its 64-byte scale record."""
+    KS = ceil_div(K, KSTEP)
+    r0, rows = m0 % PANEL, min(256, m_end - m0)
+    segs = [None if s * 8 >= rows else ((r0 + s * 8) // 256 * KS + ks) * TILE_BYTES + (r0 + s * 8) % 256 * 128
+            for s in range(32)]
+    atoms = [None if a * 16 >= rows else ((r0 + a * 16) // 256 * KS + ks) * 1024 + (r0 + a * 16) % 256 // 16 * 64
+             for a in range(16)]
+    return segs, atoms
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 512), (1000, 96, 1024), (513, 264, 4096),
@@ -781,3 +795,42 @@ def test_ws_split_units_cover_k_and_partials_stay_inside(M, N, K):
     for tile, r in covered.items():
         r.sort()
         assert r[0][0] == 0 and r[-1][1] == KS and all(a[1] == b[0] for a, b in zip(r, r[1:])), tile
+
+
+@pytest.mark.parametrize("G,N,K,offsets", [
+    (4, 256, 256, [0, 256, 512, 800, 1024]), (3, 136, 384, [0, 32, 544, 1056]),
+    (128, 1536, 2048, None), (128, 2048, 768, None), (3, 256, 256, [-64, 96, 40, 10 ** 6]),
+])
+def test_grouped_packed_a_segments_read_the_tile_rows(G, N, K, offsets):
+    """mxfp8_grouped_gemm_packed: every 8-row segment copy of a group's tile
+    reads exactly its rows' 1 KB of packed bytes inside the two-panel
+    descriptor (the packed row of global row m0 + 8s), every scale atom its
+    rows' 64-byte record, and segments past the group read nothing."""
+    import workloads as wl
+    if offsets is None:
+        rng = np.random.default_rng(G + N)
+        route = wl.zipf_topk_routing(rng, 8192, G, 8)
+        offsets, _, _ = wl.group_layout(route, G)
+    offsets = np.asarray(offsets, np.int64)
+    M_total = max(32, int(min(max(offsets.max(), 0), 10 ** 5)) // 32 * 32)
+    KS = ceil_div(K, KSTEP)
+    for g, m0, m_end in grouped_tiles(offsets, M_total, 256):
+        assert m0 % 8 == 0
+        (_, base, num, size), (_, sbase, snum, ssize) = packed_a_descriptors(M_total, K, m0)
+        assert base + num <= size and sbase + snum <= ssize and num <= 2 ** 31
+        for ks in (0, KS - 1):
+            segs, atoms = apack_offsets(m0, m_end, K, ks)
+            for s_, off in enumerate(segs):
+                row = m0 + s_ * 8
+                if off is None:
+                    assert row >= m_end or s_ * 8 >= 256
+                    continue
+                assert row < m_end and off + 1024 <= num
+                # the packed bytes of global row `row` at k-step ks, as mxfp8_repack lays them out
+                assert base + off == (row // 256 * KS + ks) * TILE_BYTES + row % 256 * 128
+            for a, off in enumerate(atoms):
+                row = m0 + a * 16
+                if off is None:
+                    assert row >= m_end
+                    continue
+                assert off + 64 <= snum and sbase + off == (row // 256 * KS + ks) * 1024 + row % 256 // 16 * 64

@@ -657,3 +657,52 @@ def test_gemm_packed_splitk_matches_canonical_split(mx, oracle_mod, M, N, K, out
         ref, sabs = oracle_mod.gemm(xq, xs, wq, ws)
         ok, worst = oracle_mod.gemm_bound_ok(c1, ref, sabs, out)
         assert ok, worst
+
+
+@pytest.mark.parametrize("G,N,K,tokens,topk", [(8, 256, 256, 300, 2), (16, 512, 768, 1024, 4),
+                                               (8, 1024, 768, 8192, 2), (4, 200, 512, 2048, 2)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_grouped_gemm_packed_a_matches_canonical(mx, oracle_mod, G, N, K, tokens, topk, out):
+    """mxfp8_grouped_gemm_packed: A quantized straight into the packed layout
+    (groups starting anywhere inside a panel, an empty group) gives C
+    bit-identical to mxfp8_grouped_gemm over the canonical grid, and leaves
+    rows past M_total untouched."""
+    aq, as_, bq, bs, off, row_token = _moe_case(oracle_mod, G, N, K, tokens, topk, G + N + 1, empty=(1,))
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+    w = mx.repack(to_dev(bq), to_dev(bs))
+    M = aq.shape[0]
+    _say("grouped packed A", G, N, K, tokens, out)
+    A = mx.repack(to_dev(aq), to_dev(as_))
+    offs = to_dev(off)
+    c0 = mx.grouped_gemm(to_dev(aq), to_dev(as_), w, offs, tdt)
+    sentinel = torch.full((M + 64, N), 7.0, dtype=tdt, device="cuda")
+    c1 = mx.grouped_gemm_packed(A, w, offs, tdt, out=sentinel[:M])
+    torch.cuda.synchronize()
+    iv = torch.int32 if out == "f32" else torch.int16
+    assert torch.equal(c0.view(iv), c1.view(iv))
+    assert bool(torch.all(sentinel[M:] == 7.0))
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+def test_grouped_gemm_packed_a_moe_full_size(mx, oracle_mod, proj):
+    """The Qwen3-30B-A3B expert GEMMs at full size with packed A (the bench's
+    MoE step): every output bit-identical to the canonical-A grouped GEMM."""
+    d = wl.moe(0)
+    A = d["A_gu"] if proj == "gate_up" else d["A_d"]
+    W = d["W_gu"] if proj == "gate_up" else d["W_d"]
+    G, N, K = W.shape
+    _say("grouped packed A full size", proj)
+    Ad = to_dev(A).view(torch.bfloat16)
+    aq, as_ = mx.quantize(Ad, 1)
+    Ap = mx.PackedWeight(torch.empty(mx.packed_bytes(1, A.shape[0], K, 0), dtype=torch.uint8, device="cuda"),
+                         torch.empty(mx.packed_bytes(1, A.shape[0], K, 1), dtype=torch.uint8, device="cuda"),
+                         1, A.shape[0], K)
+    mx.quantize_many_layouts_([(Ad, Ap)])
+    Wd = to_dev(W.reshape(G * N, K)).view(torch.bfloat16)
+    wq, ws = mx.quantize(Wd, 1)
+    w = mx.repack(wq.view(G, N, K), ws.view(G, N, K // 32))
+    offs = torch.from_numpy(d["offsets"]).cuda()
+    c0 = mx.grouped_gemm(aq, as_, w, offs, torch.bfloat16)
+    c1 = mx.grouped_gemm_packed(Ap, w, offs, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.view(torch.int16), c1.view(torch.int16))
