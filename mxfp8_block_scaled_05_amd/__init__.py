@@ -76,6 +76,8 @@ def lib():
         L.mxfp8_gemm_packed_splitk.restype = I32
         L.mxfp8_grouped_gemm_packed.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
         L.mxfp8_grouped_gemm_packed.restype = I32
+        L.mxfp8_quantize_dual_packed.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.mxfp8_quantize_dual_packed.restype = I32
         L.mxfp8_quantize_many_layouts.argtypes = [P, I64, P]
         L.mxfp8_quantize_many_layouts.restype = I32
         L.mxfp8_gemm_splitk_noalloc.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
@@ -276,6 +278,25 @@ def quantize_dual(x: torch.Tensor):
            torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device))
     quantize_dual_into(x, *out)
     return out
+
+
+def quantize_dual_packed_(x: torch.Tensor, row_out: "PackedWeight", col_out: "PackedWeight") -> None:
+    """mxfp8_quantize_dual_packed: BF16 [rows, cols] -> the packed layouts of
+    its axis-1 grid (row_out: PackedWeight(batch 1, N = rows, K = cols)) and
+    of its axis-0 grid (col_out: N = cols, K = rows), from one read of x."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    for t, (n, k), name in ((row_out, (rows, cols), "row_out"), (col_out, (cols, rows), "col_out")):
+        if not isinstance(t, PackedWeight) or (t.batch, t.N, t.K) != (1, n, k):
+            raise ValueError("%s must be PackedWeight(batch 1, N = %d, K = %d)" % (name, n, k))
+        _need(t.q, torch.uint8, name + ".q")
+        _need(t.s, torch.uint8, name + ".s")
+        if t.q.numel() < packed_bytes(1, n, k, 0) or t.s.numel() < packed_bytes(1, n, k, 1):
+            raise ValueError("%s buffers too small" % name)
+    _check(lib().mxfp8_quantize_dual_packed(_ptr(x), rows, cols, _ptr(row_out.q), _ptr(row_out.s), _ptr(col_out.q),
+                                            _ptr(col_out.s), _stream(x.device)), "mxfp8_quantize_dual_packed")
 
 
 def quantize_dual_grouped_into(x: torch.Tensor, src_offsets: torch.Tensor, dst_offsets: torch.Tensor,

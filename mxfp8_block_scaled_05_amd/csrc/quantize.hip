@@ -1044,6 +1044,93 @@ __global__ __launch_bounds__(256) void quantize_axis0_packed_kernel(const uint16
     }
 }
 
+// Both axes straight into the packed layouts: one BF16 read of x[rows][cols]
+// gives what mxfp8_repack writes for the axis-1 grid (q[rows][cols]; N = rows,
+// K = cols) and for the axis-0 grid (q[cols][rows]; N' = cols, K' = rows).  A
+// 128x128 tile is half a panel by one k-step of both layouts; the walk covers
+// every half panel of both (rows and cols rounded up to 256), so tiles and
+// blocks beyond the matrix write the layouts' padding (zero codes, scale code
+// 127).  The axis-1 codes are stored first (each thread's two blocks of a row
+// as four 16-byte chunks at their swizzled slots), then the tile is staged
+// for axis 0 exactly as quantize_axis0_packed_kernel stores it.
+template <bool NT>
+__global__ __launch_bounds__(256) void quantize_dual_packed_kernel(const uint16_t *__restrict__ x,
+                                                                   uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
+                                                                   uint8_t *__restrict__ qc, uint32_t *__restrict__ sc,
+                                                                   int64_t rows, int64_t cols, int64_t ntiles) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kA0Tile * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
+    const int t = threadIdx.x;
+    const int64_t KS1 = (cols + kKStep - 1) / kKStep, KS0 = (rows + kKStep - 1) / kKStep;
+    const int64_t CT = 2 * ((cols + kPanelRows - 1) / kPanelRows);       // column half-panels
+    int64_t idx = blockIdx.x;
+    if (idx >= ntiles) return;
+    int64_t R0 = (idx / CT) * kA0Tile, C0 = (idx % CT) * kA0Tile;
+    v4i v[kA0Loads];
+    load_tile_regs<NT>(x, rows, cols, R0, C0, t, v);
+    for (; idx < ntiles; idx += gridDim.x) {
+        store_tile_regs(tile, t, v);
+        __syncthreads();
+        const int64_t nxt = idx + gridDim.x;
+        int64_t R2 = R0, C2 = C0;
+        if (nxt < ntiles) {
+            R2 = (nxt / CT) * kA0Tile;
+            C2 = (nxt % CT) * kA0Tile;
+            load_tile_regs<NT>(x, rows, cols, R2, C2, t, v);
+        }
+        if (C0 < KS1 * kKStep) {
+            // axis 1: rows R0 .. R0+127 are half (R0 / 128) % 2 of panel R0 / 256
+            // at k-step C0 / 128
+            const int64_t tl = (R0 / kPanelRows) * KS1 + C0 / kKStep;
+            const int half = (int)((R0 / kA0Tile) & 1);
+            uint8_t *qt = qr + tl * kTileBytes + half * (kA0Tile * kKStep);
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int u = u2 * 256 + t, r = u >> 2, bb = u & 3;
+                uint32_t q8[8];
+                uint32_t code = quantize_row_block(tile, r, bb, q8);
+                if (R0 + r >= rows || C0 + 32 * bb >= cols) code = 127u;    // padding (its codes are zero)
+                const int sw = r & 7;
+                *reinterpret_cast<v4i *>(qt + r * kKStep + (((2 * bb) ^ sw) << 4)) =
+                    v4i{(int)q8[0], (int)q8[1], (int)q8[2], (int)q8[3]};
+                *reinterpret_cast<v4i *>(qt + r * kKStep + (((2 * bb + 1) ^ sw) << 4)) =
+                    v4i{(int)q8[4], (int)q8[5], (int)q8[6], (int)q8[7]};
+                const int rp = half * kA0Tile + r;                        // row in the panel
+                sr[tl * kScaleStepBytes + (rp >> 4) * 64 + (rp & 15) + 16 * bb] = (uint8_t)code;
+            }
+        }
+        if (R0 < KS0 * kKStep) {
+            axis0_stage_tile(tile, stile, t);
+            // axis 0: output row o = C0 + col is row o % 256 of panel o / 256 in
+            // k-step R0 / 128 (as quantize_axis0_packed_kernel)
+            const int64_t ks = R0 / kKStep, h = (C0 / kA0Tile) & 1;
+            const int64_t tile_lin = (C0 / kPanelRows) * KS0 + ks;
+            uint8_t *qt = qc + tile_lin * kTileBytes + h * (kA0Tile * kKStep);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = i * 32 + (t >> 3), j = t & 7;
+                *reinterpret_cast<v4i *>(qt + col * kKStep + ((j ^ (col & 7)) << 4)) =
+                    *reinterpret_cast<const v4i *>(tile + col * kA0OutPitch + 16 * j);
+            }
+            if (t < kA0Tile) {
+                const int jb = (t >> 2) & 3;
+                uint32_t o = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int lc = 16 * (t >> 4) + 4 * (t & 3) + i;
+                    const uint32_t code =
+                        (C0 + lc < cols && R0 + 32 * jb < rows) ? (uint32_t)stile[lc * 4 + jb] : 127u;
+                    o |= code << (8 * i);
+                }
+                sc[tile_lin * (kScaleStepBytes / 4) + h * kA0Tile + t] = o;
+            }
+        }
+        __syncthreads();          // every thread's stores have read the tile
+        R0 = R2;
+        C0 = C2;
+    }
+}
+
 // Workgroups of a tile walk: as many per CU as can be resident at once, at
 // most one per tile.  The LDS tile would allow four per CU, but the walks'
 // 130-145 registers per lane leave room for three 256-thread workgroups; with
@@ -1165,6 +1252,23 @@ hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, u
     }
     hipLaunchKernelGGL(quantize_dual_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,
                        s_row, q_col, s_col, rows, cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual_packed(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qr_packed,
+                                       uint8_t *sr_packed, uint8_t *qc_packed, uint8_t *sc_packed,
+                                       hipStream_t stream) {
+    const int64_t tiles = 2 * packed_panels(rows) * 2 * packed_panels(cols);
+    uint32_t *sc = reinterpret_cast<uint32_t *>(sc_packed);
+    if (rows * cols * 2 >= kQuantNontemporalBytes) {
+        const int64_t grid = walk_grid<quantize_dual_packed_kernel<true>>(tiles);
+        hipLaunchKernelGGL(quantize_dual_packed_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                           qr_packed, sr_packed, qc_packed, sc, rows, cols, tiles);
+    } else {
+        const int64_t grid = walk_grid<quantize_dual_packed_kernel<false>>(tiles);
+        hipLaunchKernelGGL(quantize_dual_packed_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, x,
+                           qr_packed, sr_packed, qc_packed, sc, rows, cols, tiles);
+    }
     return hipGetLastError();
 }
 

@@ -220,3 +220,39 @@ def test_quantize_packed_axis0_mlp_weight_full_size(mx):
     ref = mx.repack(q0, s0)
     torch.cuda.synchronize()
     assert torch.equal(pw.q, ref.q) and torch.equal(pw.s, ref.s)
+
+
+@pytest.mark.parametrize("rows,cols", [(32, 32), (96, 160), (288, 416), (512, 384), (64, 4160), (8192, 4096)])
+def test_quantize_dual_packed_matches_pack_of_both_axes(mx, oracle_mod, rows, cols):
+    """mxfp8_quantize_dual_packed equals the oracle's packing of its quantize
+    along each axis (padding rows, blocks and half panels included), on
+    special values; the MLP activation shape (8192 x 4096) against
+    mxfp8_quantize_dual + mxfp8_repack on the device."""
+    import torch
+    _say("dual packed", rows, cols)
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = _specials(wl.normal_bf16(rng, (rows, cols), outlier_frac=0.01), rng)
+    xd = to_dev(x).view(torch.bfloat16)
+    dev = xd.device
+    pr = mx.PackedWeight(torch.full((mx.packed_bytes(1, rows, cols, 0),), 0xEE, dtype=torch.uint8, device=dev),
+                         torch.full((mx.packed_bytes(1, rows, cols, 1),), 0xEE, dtype=torch.uint8, device=dev),
+                         1, rows, cols)
+    pc = mx.PackedWeight(torch.full((mx.packed_bytes(1, cols, rows, 0),), 0xEE, dtype=torch.uint8, device=dev),
+                         torch.full((mx.packed_bytes(1, cols, rows, 1),), 0xEE, dtype=torch.uint8, device=dev),
+                         1, cols, rows)
+    mx.quantize_dual_packed_(xd, pr, pc)
+    torch.cuda.synchronize()
+    if rows * cols <= 1 << 20:
+        q1, s1 = oracle_mod.quantize(x, 1)
+        q0, s0 = oracle_mod.quantize(x, 0)
+        qp1, sp1 = oracle_mod.pack(q1.reshape(1, rows, cols), s1.reshape(1, rows, cols // 32), 1, rows, cols)
+        qp0, sp0 = oracle_mod.pack(q0.reshape(1, cols, rows), s0.reshape(1, cols, rows // 32), 1, cols, rows)
+        assert np.array_equal(to_host(pr.q), qp1) and np.array_equal(to_host(pr.s), sp1)
+        assert np.array_equal(to_host(pc.q), qp0) and np.array_equal(to_host(pc.s), sp0)
+    else:
+        qr, sr, qc, sc = mx.quantize_dual(xd)
+        r1 = mx.repack(qr, sr)
+        r0 = mx.repack(qc, sc)
+        torch.cuda.synchronize()
+        assert torch.equal(pr.q, r1.q) and torch.equal(pr.s, r1.s)
+        assert torch.equal(pc.q, r0.q) and torch.equal(pc.s, r0.s)
