@@ -1336,8 +1336,16 @@ struct WsLayout {
     // bf16 C leaves each computing wave 16 rows at a time through a band
     // buffer of its own after the ring (rows padded by 16 bytes)
     static constexpr int BAND_ROW = 64 * 2 + 16, BAND = 16 * BAND_ROW, BAND_OFF = NST * STAGE;
+    // grouped launch: the coordinates of a workgroup's tiles (at most UNITS),
+    // found once before the first copy
+    static constexpr int UNITS = 64, UNIT_OFF = BAND_OFF + 4 * BAND;
 };
-static_assert(WsLayout::BAND_OFF + 4 * WsLayout::BAND <= 160 * 1024, "ring and band buffers fit the LDS");
+static_assert(WsLayout::UNIT_OFF + WsLayout::UNITS * 16 <= 160 * 1024, "ring, band buffers and tile table fit the LDS");
+
+// a grouped tile: expert, first and end rows (of the padded row space), tile column
+struct WsUnit {
+    int g, m0, m_end, tn;
+};
 
 // copy instructions one copying wave (0..3) issues per k-step
 __device__ __forceinline__ constexpr int ws_copies(int pw) { return 8 + 4 + 1 + (pw < 2 ? 1 : 0); }
@@ -1355,16 +1363,21 @@ __device__ __forceinline__ void ws_tiles(int wg, int nwg, int T, int &first, int
     count = first < hi ? (hi - first + nx - 1) / nx : 0;
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool GROUPED = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
     using Lw = WsLayout;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[Lw::BAND_OFF + 4 * Lw::BAND];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Lw::UNIT_OFF + (GROUPED ? Lw::UNITS * 16 : 0)];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int KS = p.KS;
     // work units: tile u % T over K slice u / T (p.splits > 1: the split
-    // launch, fp32 partials of slice s at c + s * c_stride; else one slice)
-    const int T = p.tiles_m * p.tiles_n;
+    // launch, fp32 partials of slice s at c + s * c_stride; else one slice).
+    // Grouped: the m-tiles are each expert's 256-row tiles in expert order
+    // (clamped offsets, as find_group), the packed A rows those of the
+    // padded row space, the launch never split
+    const int tiles_m =
+        GROUPED ? __builtin_amdgcn_readfirstlane(count_group_tiles<256>(p.offsets, p.G, p.M, lane)) : p.tiles_m;
+    const int T = tiles_m * p.tiles_n;
     const int S = p.splits > 1 ? p.splits : 1, L = p.splits > 1 ? p.split_steps : KS;
     int first, stride, nunit;
     ws_tiles(blockIdx.x, gridDim.x, T * S, first, stride, nunit);
@@ -1372,6 +1385,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
         k0 = (first + i * stride) / T * L;
         k1 = min(KS, k0 + L);
     };
+    WsUnit *units = reinterpret_cast<WsUnit *>(smem + Lw::UNIT_OFF);
+    if constexpr (GROUPED) {
+        // the launcher keeps every workgroup's tile count within UNITS
+        nunit = min(nunit, Lw::UNITS);
+        for (int i = w; i < nunit; i += kWaves) {
+            int tm, tn;
+            grouped_order((first + i * stride) % T, tiles_m, p.tiles_n, tm, tn);
+            int64_t glo = 0, ghi = 0;
+            int tig = 0;
+            const int g = find_group<256>(p.offsets, p.G, p.M, tm, lane, glo, ghi, tig);
+            const int64_t m0 = glo + (int64_t)tig * 256;
+            if (lane == 0) units[i] = g < 0 ? WsUnit{0, 0, 0, tn} : WsUnit{g, (int)m0, (int)ghi, tn};
+        }
+        __syncthreads();
+    }
     int total = 0;                                               // k-steps of this workgroup
     for (int i = 0; i < nunit; ++i) {
         int k0, k1;
@@ -1386,12 +1414,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
         const int nc = ws_copies(pw);
         int iu = 0, ks = 0, kend = 0, st = 0;                    // next step to issue
         v4i ra = {}, rsa = {}, rb = {}, rsb = {};
+        int a_m0 = 0, a_rows = 0;                                // grouped: the tile's rows in A's first panel
         auto set_tile = [&](int i) {
             int tm, tn;
-            grouped_order((first + i * stride) % T, p.tiles_m, p.tiles_n, tm, tn);
-            const int64_t pa = tm, pb = ((int64_t)tn * Lw::BN) / kPanelRows, prow = ((int64_t)tn * Lw::BN) % kPanelRows;
-            ra = make_srd(p.a_q + pa * KS * kTileBytes, (uint32_t)((int64_t)KS * kTileBytes));
-            rsa = make_srd(p.a_s + pa * KS * kScaleStepBytes, (uint32_t)((int64_t)KS * kScaleStepBytes));
+            int64_t pa, bp = 0;
+            if constexpr (GROUPED) {
+                const WsUnit u = units[i];
+                const int g = __builtin_amdgcn_readfirstlane(u.g), m0 = __builtin_amdgcn_readfirstlane(u.m0);
+                a_rows = min(__builtin_amdgcn_readfirstlane(u.m_end) - m0, Lw::BM);
+                tn = __builtin_amdgcn_readfirstlane(u.tn);
+                pa = m0 / kPanelRows;
+                a_m0 = m0 % kPanelRows;
+                bp = (int64_t)g * p.NP;
+            } else {
+                grouped_order((first + i * stride) % T, p.tiles_m, p.tiles_n, tm, tn);
+                pa = tm;
+            }
+            // A: one panel, or (grouped, a tile starting inside a panel) two
+            const int64_t na = GROUPED ? min((int64_t)2, (p.M + kPanelRows - 1) / kPanelRows - pa) : 1;
+            const int64_t pb = bp + ((int64_t)tn * Lw::BN) / kPanelRows, prow = ((int64_t)tn * Lw::BN) % kPanelRows;
+            ra = make_srd(p.a_q + pa * KS * kTileBytes, (uint32_t)(na * KS * kTileBytes));
+            rsa = make_srd(p.a_s + pa * KS * kScaleStepBytes, (uint32_t)(na * KS * kScaleStepBytes));
             rb = make_srd(p.b_q + pb * KS * kTileBytes + prow * 128,
                           (uint32_t)((int64_t)KS * kTileBytes - prow * 128));
             rsb = make_srd(p.b_s + pb * KS * kScaleStepBytes + (prow / 16) * 64,
@@ -1408,7 +1451,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int seg = i * 4 + pw;
-                dma16(ra, k0 + seg * 1024 + lane * 16, sbase + Lw::A_OFF + seg * 1024);
+                uint32_t off = k0 + seg * 1024 + lane * 16;
+                if constexpr (GROUPED) {
+                    // the tile's rows seg*8 .. +7, in the panel they lie in;
+                    // rows past the expert's read zeros
+                    const int r = a_m0 + seg * 8;
+                    off = seg * 8 < a_rows ? (uint32_t)(r / kPanelRows) * (uint32_t)KS * (uint32_t)kTileBytes + k0 +
+                                                 (uint32_t)(r % kPanelRows) * 128u + lane * 16
+                                           : kOOB;
+                }
+                dma16(ra, off, sbase + Lw::A_OFF + seg * 1024);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1416,7 +1468,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                 dma16(rb, k0 + seg * 1024 + lane * 16, sbase + Lw::B_OFF + seg * 1024);
             }
             const uint32_t s0 = (uint32_t)ks * (uint32_t)kScaleStepBytes + pw * 256 + lane * 4;
-            dma4(rsa, s0, sbase + Lw::SA_OFF + pw * 256);
+            uint32_t sa_off = s0;
+            if constexpr (GROUPED) {
+                // this lane's dword: atom pw*4 + lane/16 of the tile (16 rows)
+                const int ra16 = (pw * 4 + (lane >> 4)) * 16, r = a_m0 + ra16;
+                sa_off = ra16 < a_rows ? (uint32_t)(r / kPanelRows) * (uint32_t)KS * (uint32_t)kScaleStepBytes +
+                                             (uint32_t)ks * (uint32_t)kScaleStepBytes +
+                                             (uint32_t)((r % kPanelRows) >> 4) * 64u + (lane & 15) * 4
+                                       : kOOB;
+            }
+            dma4(rsa, sa_off, sbase + Lw::SA_OFF + pw * 256);
             if (pw < 2) dma4(rsb, s0, sbase + Lw::SB_OFF + pw * 256);
             st = st == Lw::NST - 1 ? 0 : st + 1;
             if (++ks == kend && ++iu < nunit) start_unit(iu);
@@ -1487,9 +1548,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                 // and columns that lie inside C
                 const int u = first + iu * stride;
                 int tm, tn;
-                grouped_order(u % T, p.tiles_m, p.tiles_n, tm, tn);
-                const int64_t row0 = (int64_t)tm * Lw::BM + wm * 128, col0 = (int64_t)tn * Lw::BN + wn * 64;
-                const int64_t rows_here = p.M - row0, cols_here = p.N - col0;
+                int64_t row0, row_end;
+                if constexpr (GROUPED) {
+                    const WsUnit un = units[iu];
+                    tn = __builtin_amdgcn_readfirstlane(un.tn);
+                    row0 = (int64_t)__builtin_amdgcn_readfirstlane(un.m0) + wm * 128;
+                    row_end = __builtin_amdgcn_readfirstlane(un.m_end);
+                } else {
+                    grouped_order(u % T, p.tiles_m, p.tiles_n, tm, tn);
+                    row0 = (int64_t)tm * Lw::BM + wm * 128;
+                    row_end = p.M;
+                }
+                const int64_t col0 = (int64_t)tn * Lw::BN + wn * 64;
+                const int64_t rows_here = row_end - row0, cols_here = p.N - col0;
                 uint8_t *cbase = static_cast<uint8_t *>(p.c) + (S > 1 ? (int64_t)(u / T) * p.c_stride * 4 : 0);
                 if (rows_here > 0 && cols_here > 0) {
                     const int rh = (int)min(rows_here, (int64_t)128), chh = (int)min(cols_here, (int64_t)64);
@@ -1964,8 +2035,20 @@ hipError_t launch_grouped_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, co
     p.offsets = offsets;
     p.lda = K; p.lsa = K / 32; p.ldb = K; p.lsb = K / 32;
     p.tiles_m = (int)(ceil_div(M_total, 256) + G);
+    const int cus = device_cu_count();
+    dim3 grid((unsigned)cus), block(kThreads);
+    // the copying / computing-wave launch over 256x128 tiles while every
+    // workgroup's share of the tiles (at most tiles_m x tiles_n of them, the
+    // bound of each expert's ragged last tile) fits its tile table
+    const int64_t ws_cols = ceil_div(N, 128);
+    if (N % (c_bf16 ? 8 : 4) == 0 && (int64_t)128 * N * (c_bf16 ? 2 : 4) < ((int64_t)1 << 31) &&
+        (int64_t)p.tiles_m * ws_cols <= (int64_t)(WsLayout::UNITS - 2) * cus) {
+        p.tiles_n = (int)ws_cols;
+        if (c_bf16) hipLaunchKernelGGL((gemm_ws_kernel<true, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((gemm_ws_kernel<false, true>), grid, block, 0, stream, p);
+        return hipGetLastError();
+    }
     p.tiles_n = (int)ceil_div(N, 256);
-    dim3 grid((unsigned)device_cu_count()), block(kThreads);
     if (c_bf16) hipLaunchKernelGGL((gemm_grouped_persist_kernel<true, false, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((gemm_grouped_persist_kernel<false, false, true>), grid, block, 0, stream, p);
     return hipGetLastError();

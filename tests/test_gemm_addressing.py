@@ -879,3 +879,101 @@ def test_quantize_dual_packed_writes_every_byte_once(rows, cols):
                 np.add.at(s0, (tl * 256 + h * 128 + t[:128]) * 4 + k, 1)
     for a in (q1, s1, q0, s0):
         assert np.all(a == 1), (rows, cols)
+
+
+WS_UNITS = 64
+
+
+@pytest.mark.parametrize("G,N,K,offsets", [
+    (4, 256, 256, [0, 256, 512, 800, 1024]), (3, 136, 384, [0, 32, 544, 1056]),
+    (5, 200, 128, [0, 0, 96, 96, 384, 640]),             # empty groups, a group ending on a panel edge
+    (128, 1536, 2048, None), (128, 2048, 768, None), (3, 256, 256, [-64, 96, 40, 10 ** 6]),
+])
+def test_ws_grouped_copies_and_stores(G, N, K, offsets):
+    """gemm_ws_kernel<.., GROUPED>: with the launcher's bound on the tile
+    count, every workgroup's tiles fit its 64-entry table; each tile's A
+    segment and scale-atom copies read exactly the packed bytes of its own
+    rows (global row m0 + 8s, inside the one- or two-panel descriptor) and
+    nothing past its expert; B comes from the expert's panel; and the
+    computing waves' stores cover each (row of a group, column) once and no
+    row outside the groups."""
+    import workloads as wl
+    if offsets is None:
+        rng = np.random.default_rng(G + N)
+        route = wl.zipf_topk_routing(rng, 8192, G, 8)
+        offsets, _, _ = wl.group_layout(route, G)
+    offsets = np.asarray(offsets, np.int64)
+    M_total = max(32, int(min(max(offsets.max(), 0), 10 ** 5)) // 32 * 32)
+    # a malformed table (offsets off the 32-row grid or decreasing) only has
+    # to keep every descriptor and store inside its buffer
+    wellformed = bool(np.all(offsets % 32 == 0) and np.all(np.diff(offsets) >= 0) and offsets[0] >= 0)
+    KS, NPa, NP = ceil_div(K, KSTEP), ceil_div(M_total, PANEL), ceil_div(N, PANEL)
+    tiles = grouped_tiles(offsets, M_total, 256)
+    tiles_m, tiles_n = len(tiles), ceil_div(N, 128)
+    T = tiles_m * tiles_n
+    bound = (ceil_div(M_total, 256) + G) * tiles_n          # the launcher's tile-count bound
+    assert T <= bound
+    for cus in (256, 80):
+        if bound > (WS_UNITS - 2) * cus:
+            continue
+        counts = [ws_tiles(wg, cus, T)[2] for wg in range(cus)]
+        assert max(counts) <= WS_UNITS, (cus, max(counts))
+    lane = np.arange(64)
+    row_hits = {}
+    for L in range(T):
+        tm, tn = grouped_order(L, tiles_m, tiles_n)
+        g, m0, m_end = tiles[tm]
+        assert 0 <= m0 < m_end <= M_total and (m0 % 32 == 0 or not wellformed)
+        pa, a_m0, a_rows = m0 // PANEL, m0 % PANEL, min(m_end - m0, 256)
+        na = min(2, NPa - pa)
+        abase, anum = pa * KS * TILE_BYTES, na * KS * TILE_BYTES
+        sbase, snum = pa * KS * 1024, na * KS * 1024
+        assert abase + anum <= NPa * KS * TILE_BYTES and sbase + snum <= NPa * KS * 1024 and anum < 2 ** 31
+        for ks in ((0, KS - 1) if wellformed else ()):
+            seen = []
+            for pw in range(4):
+                for i in range(8):
+                    seg = i * 4 + pw
+                    if seg * 8 >= a_rows:
+                        continue                      # kOOB: rows past the expert read zeros
+                    r = a_m0 + seg * 8
+                    off = (r // PANEL) * KS * TILE_BYTES + ks * TILE_BYTES + (r % PANEL) * 128 + lane * 16
+                    assert off.max() + 16 <= anum
+                    row = m0 + seg * 8
+                    assert row + 8 <= m_end
+                    assert abase + off[0] == (row // PANEL * KS + ks) * TILE_BYTES + row % PANEL * 128
+                    seen += list(range(row, row + 8))
+                ra16 = (pw * 4 + (lane >> 4)) * 16
+                ok = ra16 < a_rows
+                r = a_m0 + ra16
+                soff = (r // PANEL) * KS * 1024 + ks * 1024 + ((r % PANEL) >> 4) * 64 + (lane & 15) * 4
+                assert np.all(soff[ok] + 4 <= snum)
+                row = m0 + ra16
+                assert np.all(row[ok] < m_end)
+                assert np.all(sbase + soff[ok] == (row[ok] // PANEL * KS + ks) * 1024 + row[ok] % PANEL // 16 * 64
+                              + (lane[ok] & 15) * 4)
+            assert sorted(seen) == list(range(m0, m0 + a_rows))
+        pb, prow = g * NP + tn * 128 // PANEL, tn * 128 % PANEL
+        bbase, bnum = pb * KS * TILE_BYTES + prow * 128, KS * TILE_BYTES - prow * 128
+        assert bbase + bnum <= G * NP * KS * TILE_BYTES
+        assert (KS - 1) * TILE_BYTES + 15 * 1024 + 1024 <= bnum
+        assert pb * KS * 1024 + prow // 16 * 64 + (KS * 1024 - prow // 16 * 64) <= G * NP * KS * 1024
+        for w in range(4):
+            row0, col0 = m0 + (w >> 1) * 128, tn * 128 + (w & 1) * 64
+            if m_end - row0 <= 0 or N - col0 <= 0:
+                continue
+            rh = min(m_end - row0, 128)
+            assert row0 >= 0 and row0 + rh <= M_total
+            for rr in range(row0, row0 + rh):
+                row_hits[(rr, col0)] = row_hits.get((rr, col0), 0) + 1
+    if not wellformed:
+        return
+    # every row of every group, for every 64-column block, stored exactly once
+    want = set()
+    for g in range(G):
+        lo = min(max(int(offsets[g]), 0), M_total)
+        hi = min(max(int(offsets[g + 1]), lo), M_total)
+        for rr in range(lo, hi):
+            for c0 in range(0, N, 64):
+                want.add((rr, c0))
+    assert set(row_hits) == want and all(v == 1 for v in row_hits.values())
