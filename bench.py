@@ -631,9 +631,9 @@ def bench_moe_train(args, dev):
     """Qwen3-30B-A3B MoE expert layer, one learner micro-batch of 8192 tokens
     (128 experts, Zipf(1.1) top-8, groups padded to 32): forward, data
     gradients and weight gradients of gate_up and down, all in MXFP8.
-      weights (per step): gate_up and down quantized along K into the packed
-        layout, and along N per expert straight into the packed layout of
-        the transposed weights (for dgrad);
+      weights (per step): gate_up and down quantized from one read each along
+        K into the packed layout and along N per expert straight into the
+        packed layout of the transposed weights (for dgrad);
       forward: X gathered by routing + quantized in one pass (the fused
         permute), grouped gate_up; h quantized along both axes, grouped down;
       backward: dY quantized along both axes -> dgrad down (grouped GEMM vs
@@ -693,10 +693,8 @@ def bench_moe_train(args, dev):
     dW_d = torch.empty((G, H, I), dtype=torch.float32, device=dev)
     dW_gu = torch.empty((G, I2, H), dtype=torch.float32, device=dev)
     ops = [
-        ("w_gu_packed", lambda: mx.quantize_packed_(t["W_gu"], P_gu)),
-        ("w_d_packed", lambda: mx.quantize_packed_(t["W_d"], P_d)),
-        ("w_gu_packed_axis0", lambda: mx.quantize_packed_axis0_(t["W_gu"], P_guT)),
-        ("w_d_packed_axis0", lambda: mx.quantize_packed_axis0_(t["W_d"], P_dT)),
+        ("w_gu_dual_packed", lambda: mx.quantize_dual_packed_(t["W_gu"], P_gu, P_guT)),
+        ("w_d_dual_packed", lambda: mx.quantize_dual_packed_(t["W_d"], P_d, P_dT)),
         ("gather_quantize_X", lambda: mx.quantize_gather_into(t["X"], idx, *xq)),
         ("fprop_gate_up", lambda: mx.grouped_gemm(xq[0], xq[1], P_gu, offs, torch.bfloat16, out=y_gu)),
         ("quantize_dual_h", lambda: mx.quantize_dual_grouped_into(t["A_d"], offs, offs128, *h0, *h1)),

@@ -109,18 +109,21 @@ mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols,
  *
  * The learner's activations and output gradients feed three GEMMs each:
  * blocked along K (forward and data gradient) and along tokens, transposed
- * (weight gradient) ("The pipeline", learner paragraph).  One BF16 read of
- * x[rows][cols] (rows % 32 == 0, cols % 32 == 0) writes exactly the bytes
- * mxfp8_repack writes for
- *   q_row_packed / s_row_packed: the axis-1 grid q[rows][cols] (N = rows,
- *     K = cols; mxfp8_packed_bytes(1, rows, cols, 0 / 1) bytes), and
- *   q_col_packed / s_col_packed: the axis-0 grid q[cols][rows] (N = cols,
- *     K = rows; mxfp8_packed_bytes(1, cols, rows, 0 / 1) bytes),
+ * (weight gradient); its weights feed the forward GEMM blocked along K and
+ * the data-gradient GEMM blocked along N ("The pipeline", learner
+ * paragraph).  One BF16 read of x[batch][rows][cols] (rows % 32 == 0,
+ * cols % 32 == 0; 1 <= batch <= 65535, e.g. the experts of an MoE layer)
+ * writes exactly the bytes mxfp8_repack writes for
+ *   q_row_packed / s_row_packed: the axis-1 grids q[b][rows][cols] (N =
+ *     rows, K = cols; mxfp8_packed_bytes(batch, rows, cols, 0 / 1) bytes),
+ *   q_col_packed / s_col_packed: the axis-0 grids q[b][cols][rows] (N =
+ *     cols, K = rows; mxfp8_packed_bytes(batch, cols, rows, 0 / 1) bytes),
  * padding included, so both go to mxfp8_gemm_packed / mxfp8_gemm_packed_splitk
- * as A or B.  The limits of mxfp8_repack apply to both layouts.  Bit-exact,
- * deterministic; no allocation, no synchronization.
+ * (batch 1) or mxfp8_grouped_gemm as A or B.  The limits of mxfp8_repack
+ * apply to both layouts.  Bit-exact, deterministic; no allocation, no
+ * synchronization.
  */
-mxfp8_status mxfp8_quantize_dual_packed(const void *x_bf16, int64_t rows, int64_t cols,
+mxfp8_status mxfp8_quantize_dual_packed(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
                                         uint8_t *q_row_packed, uint8_t *s_row_packed,
                                         uint8_t *q_col_packed, uint8_t *s_col_packed, hipStream_t stream);
 

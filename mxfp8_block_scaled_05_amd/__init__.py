@@ -76,7 +76,7 @@ def lib():
         L.mxfp8_gemm_packed_splitk.restype = I32
         L.mxfp8_grouped_gemm_packed.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
         L.mxfp8_grouped_gemm_packed.restype = I32
-        L.mxfp8_quantize_dual_packed.argtypes = [P, I64, I64, P, P, P, P, P]
+        L.mxfp8_quantize_dual_packed.argtypes = [P, I64, I64, I64, P, P, P, P, P]
         L.mxfp8_quantize_dual_packed.restype = I32
         L.mxfp8_quantize_many_layouts.argtypes = [P, I64, P]
         L.mxfp8_quantize_many_layouts.restype = I32
@@ -281,22 +281,25 @@ def quantize_dual(x: torch.Tensor):
 
 
 def quantize_dual_packed_(x: torch.Tensor, row_out: "PackedWeight", col_out: "PackedWeight") -> None:
-    """mxfp8_quantize_dual_packed: BF16 [rows, cols] -> the packed layouts of
-    its axis-1 grid (row_out: PackedWeight(batch 1, N = rows, K = cols)) and
-    of its axis-0 grid (col_out: N = cols, K = rows), from one read of x."""
+    """mxfp8_quantize_dual_packed: BF16 [(batch,) rows, cols] -> the packed
+    layouts of its axis-1 grids (row_out: PackedWeight(batch, N = rows,
+    K = cols)) and of its axis-0 grids (col_out: N = cols, K = rows), from
+    one read of x."""
     _need(x, torch.bfloat16, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D [rows, cols]")
-    rows, cols = x.shape
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [rows, cols] or [batch, rows, cols]")
+    batch = x.shape[0] if x.dim() == 3 else 1
+    rows, cols = x.shape[-2:]
     for t, (n, k), name in ((row_out, (rows, cols), "row_out"), (col_out, (cols, rows), "col_out")):
-        if not isinstance(t, PackedWeight) or (t.batch, t.N, t.K) != (1, n, k):
-            raise ValueError("%s must be PackedWeight(batch 1, N = %d, K = %d)" % (name, n, k))
+        if not isinstance(t, PackedWeight) or (t.batch, t.N, t.K) != (batch, n, k):
+            raise ValueError("%s must be PackedWeight(batch %d, N = %d, K = %d)" % (name, batch, n, k))
         _need(t.q, torch.uint8, name + ".q")
         _need(t.s, torch.uint8, name + ".s")
-        if t.q.numel() < packed_bytes(1, n, k, 0) or t.s.numel() < packed_bytes(1, n, k, 1):
+        if t.q.numel() < packed_bytes(batch, n, k, 0) or t.s.numel() < packed_bytes(batch, n, k, 1):
             raise ValueError("%s buffers too small" % name)
-    _check(lib().mxfp8_quantize_dual_packed(_ptr(x), rows, cols, _ptr(row_out.q), _ptr(row_out.s), _ptr(col_out.q),
-                                            _ptr(col_out.s), _stream(x.device)), "mxfp8_quantize_dual_packed")
+    _check(lib().mxfp8_quantize_dual_packed(_ptr(x), batch, rows, cols, _ptr(row_out.q), _ptr(row_out.s),
+                                            _ptr(col_out.q), _ptr(col_out.s), _stream(x.device)),
+           "mxfp8_quantize_dual_packed")
 
 
 def quantize_dual_grouped_into(x: torch.Tensor, src_offsets: torch.Tensor, dst_offsets: torch.Tensor,

@@ -205,23 +205,25 @@ mxfp8_status mxfp8_quantize_dual(const void *x_bf16, int64_t rows, int64_t cols,
                                        s_row, q_col, s_col, stream));
 }
 
-mxfp8_status mxfp8_quantize_dual_packed(const void *x_bf16, int64_t rows, int64_t cols, uint8_t *q_row_packed,
-                                        uint8_t *s_row_packed, uint8_t *q_col_packed, uint8_t *s_col_packed,
-                                        hipStream_t stream) {
+mxfp8_status mxfp8_quantize_dual_packed(const void *x_bf16, int64_t batch, int64_t rows, int64_t cols,
+                                        uint8_t *q_row_packed, uint8_t *s_row_packed, uint8_t *q_col_packed,
+                                        uint8_t *s_col_packed, hipStream_t stream) {
     if (!x_bf16 || !q_row_packed || !s_row_packed || !q_col_packed || !s_col_packed) return MXFP8_ERR_NULL;
-    if (rows <= 0 || cols <= 0 || rows % 32 || cols % 32) return MXFP8_ERR_SHAPE;
+    if (batch <= 0 || batch > 65535 || rows <= 0 || cols <= 0 || rows % 32 || cols % 32) return MXFP8_ERR_SHAPE;
     // both packed layouts within mxfp8_repack's limits, and the tile walk's
-    // count (half panels of both) within 2^31
-    if (rows >= kMaxDim || cols >= kMaxDim || rows > kMaxK || cols > kMaxK || !repack_tiles_ok(1, rows, cols) ||
-        !repack_tiles_ok(1, cols, rows) || 4 * packed_panels(rows) * packed_panels(cols) >= ((int64_t)1 << 31))
+    // count (half panels of both, over the batch) within 2^31
+    if (rows >= kMaxDim || cols >= kMaxDim || rows > kMaxK || cols > kMaxK || !repack_tiles_ok(batch, rows, cols) ||
+        !repack_tiles_ok(batch, cols, rows) ||
+        batch * 4 * packed_panels(rows) * packed_panels(cols) >= ((int64_t)1 << 31) ||
+        batch * rows * cols >= ((int64_t)1 << 50))
         return MXFP8_ERR_SHAPE;
     if (!aligned16(x_bf16) || !aligned16(q_row_packed) || !aligned16(s_row_packed) || !aligned16(q_col_packed) ||
         !aligned16(s_col_packed))
         return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
-    return finish(launch_quantize_dual_packed(static_cast<const uint16_t *>(x_bf16), rows, cols, q_row_packed,
-                                              s_row_packed, q_col_packed, s_col_packed, stream));
+    return finish(launch_quantize_dual_packed(static_cast<const uint16_t *>(x_bf16), batch, rows, cols,
+                                              q_row_packed, s_row_packed, q_col_packed, s_col_packed, stream));
 }
 
 mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64_t cols, uint8_t *q_row,

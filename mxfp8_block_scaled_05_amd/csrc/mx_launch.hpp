@@ -51,9 +51,9 @@ hipError_t launch_quantize_gather(const uint16_t *x, int64_t rows_in, int64_t co
 
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
                                 uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream);
-hipError_t launch_quantize_dual_packed(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qr_packed,
-                                       uint8_t *sr_packed, uint8_t *qc_packed, uint8_t *sc_packed,
-                                       hipStream_t stream);
+hipError_t launch_quantize_dual_packed(const uint16_t *x, int64_t batch, int64_t rows, int64_t cols,
+                                       uint8_t *qr_packed, uint8_t *sr_packed, uint8_t *qc_packed,
+                                       uint8_t *sc_packed, hipStream_t stream);
 
 // axis 1 (q_row / s_row may be null) and axis 0 regrouped by token offsets
 // into q_col[cols][rows_out], s_col[cols][rows_out/32], pads zeroed

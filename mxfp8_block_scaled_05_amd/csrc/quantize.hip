@@ -1048,11 +1048,12 @@ __global__ __launch_bounds__(256) void quantize_axis0_packed_kernel(const uint16
 // gives what mxfp8_repack writes for the axis-1 grid (q[rows][cols]; N = rows,
 // K = cols) and for the axis-0 grid (q[cols][rows]; N' = cols, K' = rows).  A
 // 128x128 tile is half a panel by one k-step of both layouts; the walk covers
-// every half panel of both (rows and cols rounded up to 256), so tiles and
-// blocks beyond the matrix write the layouts' padding (zero codes, scale code
-// 127).  The axis-1 codes are stored first (each thread's two blocks of a row
-// as four 16-byte chunks at their swizzled slots), then the tile is staged
-// for axis 0 exactly as quantize_axis0_packed_kernel stores it.
+// every half panel of both (rows and cols rounded up to 256) of every matrix
+// of the batch, so tiles and blocks beyond a matrix write the layouts'
+// padding (zero codes, scale code 127).  The axis-1 codes are stored first
+// (each thread's two blocks of a row as four 16-byte chunks at their swizzled
+// slots), then the tile is staged for axis 0 exactly as
+// quantize_axis0_packed_kernel stores it.
 template <bool NT>
 __global__ __launch_bounds__(256) void quantize_dual_packed_kernel(const uint16_t *__restrict__ x,
                                                                    uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
@@ -1062,26 +1063,35 @@ __global__ __launch_bounds__(256) void quantize_dual_packed_kernel(const uint16_
     __shared__ __attribute__((aligned(16))) uint8_t stile[kA0Tile * 4];
     const int t = threadIdx.x;
     const int64_t KS1 = (cols + kKStep - 1) / kKStep, KS0 = (rows + kKStep - 1) / kKStep;
-    const int64_t CT = 2 * ((cols + kPanelRows - 1) / kPanelRows);       // column half-panels
+    const int64_t NPr = (rows + kPanelRows - 1) / kPanelRows, NPc = (cols + kPanelRows - 1) / kPanelRows;
+    const int64_t CT = 2 * NPc;                                          // column half-panels
+    const int64_t TPM = 2 * NPr * CT;                                    // tiles per matrix
     int64_t idx = blockIdx.x;
     if (idx >= ntiles) return;
-    int64_t R0 = (idx / CT) * kA0Tile, C0 = (idx % CT) * kA0Tile;
+    // tile idx: matrix idx / TPM, its rows R0.. and columns C0..
+    auto tile_of = [&](int64_t i, int64_t &b, int64_t &R, int64_t &C) {
+        b = i / TPM;
+        const int64_t r = i % TPM;
+        R = (r / CT) * kA0Tile;
+        C = (r % CT) * kA0Tile;
+    };
+    int64_t b0, R0, C0;
+    tile_of(idx, b0, R0, C0);
     v4i v[kA0Loads];
-    load_tile_regs<NT>(x, rows, cols, R0, C0, t, v);
+    load_tile_regs<NT>(x + b0 * rows * cols, rows, cols, R0, C0, t, v);
     for (; idx < ntiles; idx += gridDim.x) {
         store_tile_regs(tile, t, v);
         __syncthreads();
         const int64_t nxt = idx + gridDim.x;
-        int64_t R2 = R0, C2 = C0;
+        int64_t b2 = b0, R2 = R0, C2 = C0;
         if (nxt < ntiles) {
-            R2 = (nxt / CT) * kA0Tile;
-            C2 = (nxt % CT) * kA0Tile;
-            load_tile_regs<NT>(x, rows, cols, R2, C2, t, v);
+            tile_of(nxt, b2, R2, C2);
+            load_tile_regs<NT>(x + b2 * rows * cols, rows, cols, R2, C2, t, v);
         }
         if (C0 < KS1 * kKStep) {
             // axis 1: rows R0 .. R0+127 are half (R0 / 128) % 2 of panel R0 / 256
             // at k-step C0 / 128
-            const int64_t tl = (R0 / kPanelRows) * KS1 + C0 / kKStep;
+            const int64_t tl = (b0 * NPr + R0 / kPanelRows) * KS1 + C0 / kKStep;
             const int half = (int)((R0 / kA0Tile) & 1);
             uint8_t *qt = qr + tl * kTileBytes + half * (kA0Tile * kKStep);
 #pragma unroll
@@ -1104,7 +1114,7 @@ __global__ __launch_bounds__(256) void quantize_dual_packed_kernel(const uint16_
             // axis 0: output row o = C0 + col is row o % 256 of panel o / 256 in
             // k-step R0 / 128 (as quantize_axis0_packed_kernel)
             const int64_t ks = R0 / kKStep, h = (C0 / kA0Tile) & 1;
-            const int64_t tile_lin = (C0 / kPanelRows) * KS0 + ks;
+            const int64_t tile_lin = (b0 * NPc + C0 / kPanelRows) * KS0 + ks;
             uint8_t *qt = qc + tile_lin * kTileBytes + h * (kA0Tile * kKStep);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1126,6 +1136,7 @@ __global__ __launch_bounds__(256) void quantize_dual_packed_kernel(const uint16_
             }
         }
         __syncthreads();          // every thread's stores have read the tile
+        b0 = b2;
         R0 = R2;
         C0 = C2;
     }
@@ -1255,12 +1266,12 @@ hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, u
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_dual_packed(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qr_packed,
-                                       uint8_t *sr_packed, uint8_t *qc_packed, uint8_t *sc_packed,
-                                       hipStream_t stream) {
-    const int64_t tiles = 2 * packed_panels(rows) * 2 * packed_panels(cols);
+hipError_t launch_quantize_dual_packed(const uint16_t *x, int64_t batch, int64_t rows, int64_t cols,
+                                       uint8_t *qr_packed, uint8_t *sr_packed, uint8_t *qc_packed,
+                                       uint8_t *sc_packed, hipStream_t stream) {
+    const int64_t tiles = batch * 2 * packed_panels(rows) * 2 * packed_panels(cols);
     uint32_t *sc = reinterpret_cast<uint32_t *>(sc_packed);
-    if (rows * cols * 2 >= kQuantNontemporalBytes) {
+    if (batch * rows * cols * 2 >= kQuantNontemporalBytes) {
         const int64_t grid = walk_grid<quantize_dual_packed_kernel<true>>(tiles);
         hipLaunchKernelGGL(quantize_dual_packed_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
                            qr_packed, sr_packed, qc_packed, sc, rows, cols, tiles);

@@ -85,14 +85,16 @@ def test_argument_errors_before_any_device_work(libmx):
         assert libmx.mxfp8_gemm_packed(args[0], args[1], args[2], args[3], 4, 4, 128, args[4], 0, NULL) == 5, i
     # both axes into the packed layouts
     dp = libmx.mxfp8_quantize_dual_packed
-    assert dp(p, 64, 64, p, p, p, NULL, NULL) == 1                                   # NULL output
-    assert dp(p, 48, 64, p, p, p, p, NULL) == 2                                      # rows % 32
-    assert dp(p, 64, 40, p, p, p, p, NULL) == 2                                      # cols % 32
-    assert dp(p, 64, (1 << 22) + 32, p, p, p, p, NULL) == 2                          # cols beyond the K limit
+    assert dp(p, 1, 64, 64, p, p, p, NULL, NULL) == 1                                # NULL output
+    assert dp(p, 1, 48, 64, p, p, p, p, NULL) == 2                                   # rows % 32
+    assert dp(p, 1, 64, 40, p, p, p, p, NULL) == 2                                   # cols % 32
+    assert dp(p, 1, 64, (1 << 22) + 32, p, p, p, p, NULL) == 2                       # cols beyond the K limit
+    assert dp(p, 0, 64, 64, p, p, p, p, NULL) == 2                                   # batch
+    assert dp(p, 65536, 64, 64, p, p, p, p, NULL) == 2                               # batch beyond 65535
     for i in range(5):
         args = [p, p, p, p, p]
         args[i] = q
-        assert dp(args[0], 64, 64, args[1], args[2], args[3], args[4], NULL) == 5, i
+        assert dp(args[0], 2, 64, 64, args[1], args[2], args[3], args[4], NULL) == 5, i
     # grouped GEMM with packed A: K a multiple of 128
     gp = libmx.mxfp8_grouped_gemm_packed
     assert gp(p, p, p, p, p, 2, 64, 4, 64, p, 0, NULL) == 2                          # K % 128

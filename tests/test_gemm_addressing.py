@@ -836,25 +836,28 @@ def test_grouped_packed_a_segments_read_the_tile_rows(G, N, K, offsets):
                 assert off + 64 <= snum and sbase + off == (row // 256 * KS + ks) * 1024 + row % 256 // 16 * 64
 
 
-@pytest.mark.parametrize("rows,cols", [(32, 32), (96, 160), (256, 256), (288, 416), (512, 384), (8192, 4096)])
-def test_quantize_dual_packed_writes_every_byte_once(rows, cols):
+@pytest.mark.parametrize("batch,rows,cols", [(1, 32, 32), (1, 96, 160), (1, 256, 256), (1, 288, 416),
+                                              (1, 512, 384), (1, 8192, 4096), (3, 96, 160), (2, 288, 416)])
+def test_quantize_dual_packed_writes_every_byte_once(batch, rows, cols):
     """quantize_dual_packed_kernel's walk over the half panels of both
-    layouts: every byte of the axis-1 packed layout (N = rows, K = cols) and
-    of the axis-0 packed layout (N = cols, K = rows) written exactly once,
-    nothing outside them."""
+    layouts of every matrix of the batch: every byte of the axis-1 packed
+    layouts (N = rows, K = cols) and of the axis-0 packed layouts (N = cols,
+    K = rows) written exactly once, nothing outside them."""
     KS1, KS0 = ceil_div(cols, KSTEP), ceil_div(rows, KSTEP)
     NP1, NP0 = ceil_div(rows, PANEL), ceil_div(cols, PANEL)
     CT = 2 * NP0
-    ntiles = 2 * NP1 * CT
-    q1 = np.zeros(NP1 * KS1 * TILE_BYTES, np.int32)
-    s1 = np.zeros(NP1 * KS1 * 1024, np.int32)
-    q0 = np.zeros(NP0 * KS0 * TILE_BYTES, np.int32)
-    s0 = np.zeros(NP0 * KS0 * 1024, np.int32)
+    TPM = 2 * NP1 * CT
+    ntiles = batch * TPM
+    q1 = np.zeros(batch * NP1 * KS1 * TILE_BYTES, np.int32)
+    s1 = np.zeros(batch * NP1 * KS1 * 1024, np.int32)
+    q0 = np.zeros(batch * NP0 * KS0 * TILE_BYTES, np.int32)
+    s0 = np.zeros(batch * NP0 * KS0 * 1024, np.int32)
     t = np.arange(256)
     for idx in range(ntiles):
-        R0, C0 = idx // CT * 128, idx % CT * 128
+        b, rr = idx // TPM, idx % TPM
+        R0, C0 = rr // CT * 128, rr % CT * 128
         if C0 < KS1 * 128:
-            tl = R0 // 256 * KS1 + C0 // 128
+            tl = (b * NP1 + R0 // 256) * KS1 + C0 // 128
             half = R0 // 128 % 2
             base = tl * TILE_BYTES + half * 128 * 128
             for u2 in range(2):
@@ -867,7 +870,7 @@ def test_quantize_dual_packed_writes_every_byte_once(rows, cols):
                 rp = half * 128 + r
                 np.add.at(s1, tl * 1024 + (rp >> 4) * 64 + (rp & 15) + 16 * bb, 1)
         if R0 < KS0 * 128:
-            tl = C0 // 256 * KS0 + R0 // 128
+            tl = (b * NP0 + C0 // 256) * KS0 + R0 // 128
             h = C0 // 128 % 2
             base = tl * TILE_BYTES + h * 128 * 128
             for i in range(4):

@@ -256,3 +256,43 @@ def test_quantize_dual_packed_matches_pack_of_both_axes(mx, oracle_mod, rows, co
         torch.cuda.synchronize()
         assert torch.equal(pr.q, r1.q) and torch.equal(pr.s, r1.s)
         assert torch.equal(pc.q, r0.q) and torch.equal(pc.s, r0.s)
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(3, 96, 160), (2, 288, 416), (128, 1536, 2048)])
+def test_quantize_dual_packed_batched(mx, oracle_mod, batch, rows, cols):
+    """mxfp8_quantize_dual_packed over a batch (the experts of an MoE layer):
+    matrix b's packed bytes of both axes are exactly the oracle's packing of
+    its own quantize (small shapes), and at the Qwen3-30B-A3B gate_up weight
+    shape equal mxfp8_quantize_packed along K and mxfp8_quantize_packed_axis0."""
+    import torch
+    _say("dual packed batched", batch, rows, cols)
+    rng = np.random.default_rng(batch * 31 + rows + cols)
+    x = wl.normal_bf16(rng, (batch, rows, cols), std=0.02, outlier_frac=0.01)
+    if batch * rows * cols <= 1 << 20:
+        x = _specials(x.reshape(batch * rows, cols), rng).reshape(batch, rows, cols)
+    xd = to_dev(x).view(torch.bfloat16)
+    dev = xd.device
+
+    def pw(n, k):
+        return mx.PackedWeight(torch.full((mx.packed_bytes(batch, n, k, 0),), 0xEE, dtype=torch.uint8, device=dev),
+                               torch.full((mx.packed_bytes(batch, n, k, 1),), 0xEE, dtype=torch.uint8, device=dev),
+                               batch, n, k)
+    pr, pc = pw(rows, cols), pw(cols, rows)
+    mx.quantize_dual_packed_(xd, pr, pc)
+    torch.cuda.synchronize()
+    if batch * rows * cols <= 1 << 20:
+        q1, s1 = oracle_mod.quantize(x.reshape(batch * rows, cols), 1)
+        qp1, sp1 = oracle_mod.pack(q1.reshape(batch, rows, cols), s1.reshape(batch, rows, cols // 32),
+                                   batch, rows, cols)
+        qt = np.stack([oracle_mod.quantize(x[b], 0)[0] for b in range(batch)])
+        st = np.stack([oracle_mod.quantize(x[b], 0)[1] for b in range(batch)])
+        qp0, sp0 = oracle_mod.pack(qt, st, batch, cols, rows)
+        assert np.array_equal(to_host(pr.q), qp1) and np.array_equal(to_host(pr.s), sp1)
+        assert np.array_equal(to_host(pc.q), qp0) and np.array_equal(to_host(pc.s), sp0)
+    else:
+        r1, r0 = pw(rows, cols), pw(cols, rows)
+        mx.quantize_packed_(xd, r1)
+        mx.quantize_packed_axis0_(xd, r0)
+        torch.cuda.synchronize()
+        assert torch.equal(pr.q, r1.q) and torch.equal(pr.s, r1.s)
+        assert torch.equal(pc.q, r0.q) and torch.equal(pc.s, r0.s)
