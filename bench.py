@@ -635,14 +635,18 @@ def bench_moe_train(args, dev):
         K into the packed layout and along N per expert straight into the
         packed layout of the transposed weights (for dgrad);
       forward: X gathered by routing + quantized in one pass (the fused
-        permute), grouped gate_up; h quantized along both axes, grouped down;
+        permute) straight into the packed operand layout, grouped gate_up;
+        h quantized along both axes, grouped down;
       backward: dY quantized along both axes -> dgrad down (grouped GEMM vs
         W_d^T), wgrad down (grouped-K GEMM dY^T h); dH quantized along both
         axes -> dgrad gate_up, wgrad gate_up (grouped-K GEMM dH^T X).
-    The token-blocked (axis-0) grids that feed the weight gradients are
-    written regrouped, every expert's tokens starting on a multiple of 128
-    (mxfp8_quantize_dual_grouped), so the weight-gradient GEMMs run aligned;
-    the same GEMMs over the 32-padded grids are timed beside the step.
+    The forward and data-gradient GEMMs read A in the packed layout
+    (mxfp8_grouped_gemm_packed); the token-blocked (axis-0) grids that feed
+    the weight gradients are written regrouped, every expert's tokens
+    starting on a multiple of 128 (mxfp8_quantize_dual_grouped_packed), so
+    the weight-gradient GEMMs run aligned.  Timed beside the step: the
+    weight-gradient GEMMs over the 32-padded grids and the other four with A
+    from the canonical grids.
     The activation function between gate_up and down is outside the MXFP8
     path; h and dH are drawn as N(0,1) and N(0,1)*2^-10 on real rows."""
     import torch
@@ -679,12 +683,13 @@ def bench_moe_train(args, dev):
         return mx.PackedWeight(torch.empty(mx.packed_bytes(G, n, k, 0), **u8),
                                torch.empty(mx.packed_bytes(G, n, k, 1), **u8), G, n, k)
     P_gu, P_d, P_guT, P_dT = packed(I2, H), packed(H, I), packed(H, I2), packed(I, H)
-    xq = (torch.empty((Mt, H), **u8), torch.empty((Mt, H // 32), **u8))
-    h1 = (torch.empty((Mt, I), **u8), torch.empty((Mt, I // 32), **u8))
+
+    def act(k):                                   # a [Mt, k] operand in the packed layout
+        return mx.PackedWeight(torch.empty(mx.packed_bytes(1, Mt, k, 0), **u8),
+                               torch.empty(mx.packed_bytes(1, Mt, k, 1), **u8), 1, Mt, k)
+    xq, h1, dy1, dh1 = act(H), act(I), act(H), act(I2)
     h0 = (torch.empty((I, T128), **u8), torch.empty((I, T128 // 32), **u8))
-    dy1 = (torch.empty((Mt, H), **u8), torch.empty((Mt, H // 32), **u8))
     dy0 = (torch.empty((H, T128), **u8), torch.empty((H, T128 // 32), **u8))
-    dh1 = (torch.empty((Mt, I2), **u8), torch.empty((Mt, I2 // 32), **u8))
     dh0 = (torch.empty((I2, T128), **u8), torch.empty((I2, T128 // 32), **u8))
     x0 = (torch.empty((H, T128), **u8), torch.empty((H, T128 // 32), **u8))
     bf = dict(dtype=torch.bfloat16, device=dev)
@@ -695,16 +700,16 @@ def bench_moe_train(args, dev):
     ops = [
         ("w_gu_dual_packed", lambda: mx.quantize_dual_packed_(t["W_gu"], P_gu, P_guT)),
         ("w_d_dual_packed", lambda: mx.quantize_dual_packed_(t["W_d"], P_d, P_dT)),
-        ("gather_quantize_X", lambda: mx.quantize_gather_into(t["X"], idx, *xq)),
-        ("fprop_gate_up", lambda: mx.grouped_gemm(xq[0], xq[1], P_gu, offs, torch.bfloat16, out=y_gu)),
-        ("quantize_dual_h", lambda: mx.quantize_dual_grouped_into(t["A_d"], offs, offs128, *h0, *h1)),
-        ("fprop_down", lambda: mx.grouped_gemm(h1[0], h1[1], P_d, offs, torch.bfloat16, out=y_d)),
-        ("quantize_dual_dY", lambda: mx.quantize_dual_grouped_into(t["dY"], offs, offs128, *dy0, *dy1)),
-        ("dgrad_down", lambda: mx.grouped_gemm(dy1[0], dy1[1], P_dT, offs, torch.bfloat16, out=g_h)),
+        ("gather_quantize_X", lambda: mx.quantize_gather_packed_(t["X"], idx, xq)),
+        ("fprop_gate_up", lambda: mx.grouped_gemm_packed(xq, P_gu, offs, torch.bfloat16, out=y_gu)),
+        ("quantize_dual_h", lambda: mx.quantize_dual_grouped_packed_(t["A_d"], offs, offs128, *h0, h1)),
+        ("fprop_down", lambda: mx.grouped_gemm_packed(h1, P_d, offs, torch.bfloat16, out=y_d)),
+        ("quantize_dual_dY", lambda: mx.quantize_dual_grouped_packed_(t["dY"], offs, offs128, *dy0, dy1)),
+        ("dgrad_down", lambda: mx.grouped_gemm_packed(dy1, P_dT, offs, torch.bfloat16, out=g_h)),
         ("wgrad_down", lambda: mx.grouped_gemm_wgrad(dy0[0], dy0[1], h0[0], h0[1], offs128, torch.float32,
                                                      out=dW_d)),
-        ("quantize_dual_dH", lambda: mx.quantize_dual_grouped_into(t["dH"], offs, offs128, *dh0, *dh1)),
-        ("dgrad_gate_up", lambda: mx.grouped_gemm(dh1[0], dh1[1], P_guT, offs, torch.bfloat16, out=g_x)),
+        ("quantize_dual_dH", lambda: mx.quantize_dual_grouped_packed_(t["dH"], offs, offs128, *dh0, dh1)),
+        ("dgrad_gate_up", lambda: mx.grouped_gemm_packed(dh1, P_guT, offs, torch.bfloat16, out=g_x)),
         ("quantize_X_axis0", lambda: mx.quantize_dual_grouped_into(t["Xperm"], offs, offs128, *x0)),
         ("wgrad_gate_up", lambda: mx.grouped_gemm_wgrad(dh0[0], dh0[1], x0[0], x0[1], offs128, torch.float32,
                                                         out=dW_gu)),
@@ -720,8 +725,18 @@ def bench_moe_train(args, dev):
     cmp_ops = [("wgrad_down_32", lambda: mx.grouped_gemm_wgrad(*p32["dY"], *p32["h"], offs, torch.float32, out=dW_d)),
                ("wgrad_gate_up_32", lambda: mx.grouped_gemm_wgrad(*p32["dH"], *p32["X"], offs, torch.float32,
                                                                    out=dW_gu))]
+    # the forward and data-gradient grouped GEMMs with A read from the
+    # canonical grids of the same rows (mxfp8_grouped_gemm), for comparison
+    c1 = {}
+    for name, src, w in (("X", None, H), ("h", t["A_d"], I), ("dY", t["dY"], H), ("dH", t["dH"], I2)):
+        c1[name] = (mx.quantize_gather(t["X"], idx) if src is None else mx.quantize(src, 1))
+    cmp_ops += [
+        ("fprop_gate_up_canonical_A", lambda: mx.grouped_gemm(*c1["X"], P_gu, offs, torch.bfloat16, out=y_gu)),
+        ("fprop_down_canonical_A", lambda: mx.grouped_gemm(*c1["h"], P_d, offs, torch.bfloat16, out=y_d)),
+        ("dgrad_down_canonical_A", lambda: mx.grouped_gemm(*c1["dY"], P_dT, offs, torch.bfloat16, out=g_h)),
+        ("dgrad_gate_up_canonical_A", lambda: mx.grouped_gemm(*c1["dH"], P_guT, offs, torch.bfloat16, out=g_x))]
     _, avg32 = run_timed(cmp_ops, argparse.Namespace(steps=max(5, args.steps // 4), warmup=2))
-    del p32
+    del p32, c1
     f_gu = 2.0 * real * I2 * H
     f_d = 2.0 * real * H * I
     flops = {"fprop_gate_up": f_gu, "fprop_down": f_d, "dgrad_down": f_d, "wgrad_down": f_d,
@@ -734,9 +749,11 @@ def bench_moe_train(args, dev):
         else:
             kern[name] = {"us": round(us, 2)}
     for name, us in avg32.items():
-        tf = flops[name[:-3]] / (us * 1e-6) / 1e12
+        base = name[:-3] if name.endswith("_32") else name[:-len("_canonical_A")]
+        tf = flops[base] / (us * 1e-6) / 1e12
         kern[name] = {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4),
-                      "note": "32-padded token grids, not part of the step"}
+                      "note": ("32-padded token grids" if name.endswith("_32") else "A from the canonical grid")
+                      + ", not part of the step"}
     total = sum(flops.values())
     gemm_us = sum(avg[k] for k in flops)
     return _line("MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",

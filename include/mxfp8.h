@@ -165,6 +165,27 @@ mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64
                                          hipStream_t stream);
 
 /*
+ * mxfp8_quantize_dual_grouped_packed -- mxfp8_quantize_dual_grouped with the
+ * axis-1 grid written straight into the GEMM's packed operand layout.
+ *
+ * One BF16 read of the token-sorted x [rows][cols] gives the operand of the
+ * experts' forward or data-gradient GEMM (mxfp8_grouped_gemm_packed's A:
+ * q_row_packed / s_row_packed, exactly what mxfp8_repack writes for
+ * mxfp8_quantize(x, axis=1) with N = rows, K = cols, padding included;
+ * mxfp8_packed_bytes(1, rows, cols, 0 / 1) bytes) and the regrouped
+ * token-blocked grid of their weight gradients (q_col, s_col: exactly as
+ * mxfp8_quantize_dual_grouped).  Arguments, table rules and limits as
+ * mxfp8_quantize_dual_grouped, plus those of mxfp8_repack for the packed
+ * layout; both axis-1 buffers are required.  Bit-exact, deterministic; no
+ * allocation, no synchronization.
+ */
+mxfp8_status mxfp8_quantize_dual_grouped_packed(const void *x_bf16, int64_t rows, int64_t cols,
+                                                uint8_t *q_row_packed, uint8_t *s_row_packed, uint8_t *q_col,
+                                                uint8_t *s_col, const int32_t *src_offsets,
+                                                const int32_t *dst_offsets, int64_t G, int64_t rows_out,
+                                                hipStream_t stream);
+
+/*
  * mxfp8_quantize_packed -- weights BF16 -> MXFP8 straight into the GEMM's
  * packed layout, optionally also the canonical grid.
  *
@@ -334,6 +355,21 @@ mxfp8_status mxfp8_quantize_batched(const void *x_bf16, int64_t batch, int64_t r
 mxfp8_status mxfp8_quantize_gather(const void *x_bf16, int64_t rows_in, int64_t cols,
                                    const int64_t *d_row_index, int64_t rows_out,
                                    uint8_t *q, uint8_t *scales, hipStream_t stream);
+
+/*
+ * mxfp8_quantize_gather_packed -- mxfp8_quantize_gather written straight into
+ * the GEMM's packed operand layout (A of mxfp8_grouped_gemm_packed).
+ *
+ * Same rows as mxfp8_quantize_gather (output row i is input row
+ * d_row_index[i], an index outside [0, rows_in) a zero row), but q_packed /
+ * s_packed receive exactly what mxfp8_repack writes for that grid with
+ * N = rows_out, K = cols (mxfp8_packed_bytes(1, rows_out, cols, 0 / 1)
+ * bytes, padding included).  cols % 32 == 0; the limits of mxfp8_repack
+ * apply.  Bit-exact, deterministic; no allocation, no synchronization.
+ */
+mxfp8_status mxfp8_quantize_gather_packed(const void *x_bf16, int64_t rows_in, int64_t cols,
+                                          const int64_t *d_row_index, int64_t rows_out, uint8_t *q_packed,
+                                          uint8_t *s_packed, hipStream_t stream);
 
 /*
  * mxfp8_dequantize -- MXFP8 -> FP32 or BF16:  out = decode(q) * 2^(code-127).

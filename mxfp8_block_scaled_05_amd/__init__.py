@@ -61,11 +61,15 @@ def lib():
         L.mxfp8_selfcheck.restype = I32
         L.mxfp8_quantize_batched.argtypes = [P, I64, I64, I64, I32, P, P, P]
         L.mxfp8_quantize_gather.argtypes = [P, I64, I64, P, I64, P, P, P]
+        L.mxfp8_quantize_gather_packed.argtypes = [P, I64, I64, P, I64, P, P, P]
+        L.mxfp8_quantize_gather_packed.restype = I32
         L.mxfp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
         for f in ("mxfp8_quantize_batched", "mxfp8_quantize_gather", "mxfp8_grouped_gemm_wgrad"):
             getattr(L, f).restype = I32
         L.mxfp8_quantize_dual.argtypes = [P, I64, I64, P, P, P, P, P]
         L.mxfp8_quantize_dual_grouped.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
+        L.mxfp8_quantize_dual_grouped_packed.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
+        L.mxfp8_quantize_dual_grouped_packed.restype = I32
         L.mxfp8_gemm_splitk.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P, ctypes.c_size_t, P]
         L.mxfp8_gemm_splitk.restype = I32
         L.mxfp8_gemm_accurate.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P]
@@ -238,6 +242,24 @@ def quantize_gather_into(x: torch.Tensor, row_index: torch.Tensor, q: torch.Tens
                                        _ptr(s), _stream(x.device)), "mxfp8_quantize_gather")
 
 
+def quantize_gather_packed_(x: torch.Tensor, row_index: torch.Tensor, out: "PackedWeight") -> None:
+    """mxfp8_quantize_gather_packed: quantize(x[row_index], 1) straight into
+    out = PackedWeight(batch 1, N = rows_out, K = cols); rows whose index is
+    outside [0, rows) zero."""
+    _need(x, torch.bfloat16, "x")
+    _need(row_index, torch.int64, "row_index")
+    rows_in, cols = x.shape
+    rows_out = row_index.numel()
+    if not isinstance(out, PackedWeight) or (out.batch, out.N, out.K) != (1, rows_out, cols):
+        raise ValueError("out must be PackedWeight(batch 1, N = %d, K = %d)" % (rows_out, cols))
+    _need(out.q, torch.uint8, "out.q")
+    _need(out.s, torch.uint8, "out.s")
+    if out.q.numel() < packed_bytes(1, rows_out, cols, 0) or out.s.numel() < packed_bytes(1, rows_out, cols, 1):
+        raise ValueError("out buffers too small")
+    _check(lib().mxfp8_quantize_gather_packed(_ptr(x), rows_in, cols, _ptr(row_index), rows_out, _ptr(out.q),
+                                              _ptr(out.s), _stream(x.device)), "mxfp8_quantize_gather_packed")
+
+
 def quantize_gather(x: torch.Tensor, row_index: torch.Tensor):
     rows_out, cols = row_index.numel(), x.shape[1]
     q = torch.empty((rows_out, cols), dtype=torch.uint8, device=x.device)
@@ -337,6 +359,38 @@ def quantize_dual_grouped_into(x: torch.Tensor, src_offsets: torch.Tensor, dst_o
         _ptr(x), rows, cols, _ptr(q_row) if q_row is not None else None,
         _ptr(s_row) if s_row is not None else None, _ptr(q_col), _ptr(s_col), _ptr(src_offsets),
         _ptr(dst_offsets), G, rows_out, _stream(x.device)), "mxfp8_quantize_dual_grouped")
+
+
+def quantize_dual_grouped_packed_(x: torch.Tensor, src_offsets: torch.Tensor, dst_offsets: torch.Tensor,
+                                  q_col: torch.Tensor, s_col: torch.Tensor, row_out: "PackedWeight") -> None:
+    """mxfp8_quantize_dual_grouped_packed: (q_col, s_col) as
+    quantize_dual_grouped_into, and quantize(x, 1) straight into
+    row_out = PackedWeight(batch 1, N = rows, K = cols)."""
+    _need(x, torch.bfloat16, "x")
+    for t, n in ((q_col, "q_col"), (s_col, "s_col")):
+        _need(t, torch.uint8, n)
+    for t, n in ((src_offsets, "src_offsets"), (dst_offsets, "dst_offsets")):
+        _need(t, torch.int32, n)
+    if x.dim() != 2 or q_col.dim() != 2:
+        raise ValueError("x and q_col must be 2-D")
+    rows, cols = x.shape
+    rows_out = q_col.shape[1]
+    G = src_offsets.numel() - 1
+    if G < 1 or dst_offsets.numel() != G + 1:
+        raise ValueError("src_offsets and dst_offsets must both hold G+1 >= 2 entries")
+    if rows % 32 or cols % 32 or rows_out % 32:
+        raise ValueError("rows, cols and rows_out must be multiples of 32")
+    if tuple(q_col.shape) != (cols, rows_out) or tuple(s_col.shape) != (cols, rows_out // 32):
+        raise ValueError("q_col/s_col must be [cols, rows_out] / [cols, rows_out/32]")
+    if not isinstance(row_out, PackedWeight) or (row_out.batch, row_out.N, row_out.K) != (1, rows, cols):
+        raise ValueError("row_out must be PackedWeight(batch 1, N = %d, K = %d)" % (rows, cols))
+    _need(row_out.q, torch.uint8, "row_out.q")
+    _need(row_out.s, torch.uint8, "row_out.s")
+    if row_out.q.numel() < packed_bytes(1, rows, cols, 0) or row_out.s.numel() < packed_bytes(1, rows, cols, 1):
+        raise ValueError("row_out buffers too small")
+    _check(lib().mxfp8_quantize_dual_grouped_packed(
+        _ptr(x), rows, cols, _ptr(row_out.q), _ptr(row_out.s), _ptr(q_col), _ptr(s_col), _ptr(src_offsets),
+        _ptr(dst_offsets), G, rows_out, _stream(x.device)), "mxfp8_quantize_dual_grouped_packed")
 
 
 def quantize_dual_grouped(x: torch.Tensor, src_offsets: torch.Tensor, dst_offsets: torch.Tensor, rows_out: int,

@@ -172,6 +172,25 @@ mxfp8_status mxfp8_quantize_gather(const void *x_bf16, int64_t rows_in, int64_t 
                                          d_row_index, rows_out, q, scales, stream));
 }
 
+mxfp8_status mxfp8_quantize_gather_packed(const void *x_bf16, int64_t rows_in, int64_t cols,
+                                          const int64_t *d_row_index, int64_t rows_out, uint8_t *q_packed,
+                                          uint8_t *s_packed, hipStream_t stream) {
+    if (!x_bf16 || !d_row_index || !q_packed || !s_packed) return MXFP8_ERR_NULL;
+    if (rows_in <= 0 || rows_out <= 0 || cols <= 0 || cols % 32 || rows_in >= kMaxDim || rows_out >= kMaxDim ||
+        cols > kMaxK)
+        return MXFP8_ERR_SHAPE;
+    // the packed layout within mxfp8_repack's limits; the atom walk's step
+    // count within 2^31
+    if (!repack_tiles_ok(1, rows_out, cols) || packed_panels(rows_out) * 16 * packed_ksteps(cols) >= ((int64_t)1 << 31))
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q_packed) || !aligned16(s_packed) || ((uintptr_t)d_row_index & 7u))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_gather_packed(static_cast<const uint16_t *>(x_bf16), rows_in, cols, d_row_index,
+                                                rows_out, q_packed, s_packed, stream));
+}
+
 mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                                       const uint8_t *b_s, const int32_t *d_group_offsets,
                                       int64_t G, int64_t T, int64_t M, int64_t N, void *c,
@@ -244,6 +263,32 @@ mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64
     if (st != MXFP8_OK) return st;
     return finish(launch_quantize_dual_grouped(static_cast<const uint16_t *>(x_bf16), rows, cols, q_row, s_row,
                                                q_col, s_col, src_offsets, dst_offsets, G, rows_out, stream));
+}
+
+mxfp8_status mxfp8_quantize_dual_grouped_packed(const void *x_bf16, int64_t rows, int64_t cols,
+                                                uint8_t *q_row_packed, uint8_t *s_row_packed, uint8_t *q_col,
+                                                uint8_t *s_col, const int32_t *src_offsets,
+                                                const int32_t *dst_offsets, int64_t G, int64_t rows_out,
+                                                hipStream_t stream) {
+    if (!x_bf16 || !q_row_packed || !s_row_packed || !q_col || !s_col || !src_offsets || !dst_offsets)
+        return MXFP8_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim || cols > kMaxK) return MXFP8_ERR_SHAPE;
+    if (rows % 32 || cols % 32 || !tile128_ok(rows, cols)) return MXFP8_ERR_SHAPE;
+    if (G < 1 || G > 65535 || rows_out <= 0 || rows_out % 32 || rows_out >= kMaxDim ||
+        rows_out / 32 > 0x7FFFFFFF)
+        return MXFP8_ERR_SHAPE;
+    // the packed layout within mxfp8_repack's limits; the walk over whole
+    // panels of rows within 2^31 tiles
+    if (!repack_tiles_ok(1, rows, cols) || 2 * packed_panels(rows) * ((cols + 127) / 128) >= ((int64_t)1 << 31))
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(x_bf16) || !aligned16(q_col) || !aligned16(q_row_packed) || !aligned16(s_row_packed) ||
+        ((uintptr_t)src_offsets & 3u) || ((uintptr_t)dst_offsets & 3u))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_quantize_dual_grouped_packed(static_cast<const uint16_t *>(x_bf16), rows, cols, q_row_packed,
+                                                      s_row_packed, q_col, s_col, src_offsets, dst_offsets, G,
+                                                      rows_out, stream));
 }
 
 mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols,

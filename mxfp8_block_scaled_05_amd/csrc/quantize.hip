@@ -381,6 +381,57 @@ __global__ __launch_bounds__(256) void quantize_gather_kernel(const uint16_t *__
     }
 }
 
+// Gather + axis 1 straight into the packed layout (N = rows_out, K = cols):
+// the atom walk of the list quantizer's packed jobs (a wave-step is 16 rows
+// by one 128-column k-step), each output row read from x[idx[row]] (an index
+// outside [0, rows_in) gives a zero row); atoms and blocks past the matrix
+// write the layout's padding.
+__device__ __forceinline__ void load_step_packed_gather(const uint16_t *__restrict__ x, int64_t rows_in, int64_t cols,
+                                                        const int64_t *__restrict__ idx, int64_t rows_out, int KS,
+                                                        int st, int lane, uint32_t (*d)[4]) {
+    const int atom = st / KS, ks = st - atom * KS;
+    const int bl = lane >> 1, half = lane & 1, i = bl >> 2, kb4 = bl & 3;
+    const int kcol = ks * (int)kKStep + kb4 * 32 + half * 16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t r = (int64_t)atom * 16 + (u >> 1) * 8 + i;
+        const int k = kcol + (u & 1) * 8;
+        const int64_t src = r < rows_out ? idx[r] : -1;
+        if (src >= 0 && src < rows_in && k < cols) {
+            const v4i v = *reinterpret_cast<const v4i *>(x + src * cols + k);
+            d[u][0] = v.x; d[u][1] = v.y; d[u][2] = v.z; d[u][3] = v.w;
+        } else {
+            d[u][0] = d[u][1] = d[u][2] = d[u][3] = 0;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void quantize_gather_packed_kernel(const uint16_t *__restrict__ x,
+                                                                     int64_t rows_in, int64_t cols,
+                                                                     const int64_t *__restrict__ idx,
+                                                                     int64_t rows_out, uint8_t *__restrict__ qp,
+                                                                     uint8_t *__restrict__ sp, int64_t nsteps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int KS = (int)((cols + kKStep - 1) / kKStep);
+    int64_t step = wave;
+    if (step >= nsteps) return;
+    uint32_t cur[4][4], nxt[4][4];
+    load_step_packed_gather(x, rows_in, cols, idx, rows_out, KS, (int)step, lane, cur);
+    for (; step < nsteps; step += nwaves) {
+        const bool more = step + nwaves < nsteps;
+        if (more) load_step_packed_gather(x, rows_in, cols, idx, rows_out, KS, (int)(step + nwaves), lane, nxt);
+        convert_step_packed(qp, sp, rows_out, cols, KS, (int)step, lane, cur);
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) cur[u][k] = nxt[u][k];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- axis 0
 // x[rows][cols] -> q[cols][rows], scales[cols][rows/32].  A workgroup of four
 // waves owns a 128-row x 128-column tile and moves it through LDS twice:
@@ -908,7 +959,7 @@ __global__ __launch_bounds__(256) void quantize_axis0_walk_kernel(const uint16_t
 // blocks found at the top of its iteration; q_row may be null).  Looking the
 // next tile's up beside its loads instead (double-buffered) measured no
 // faster on the MoE learner's tensors.
-template <bool NT, bool GROUPED = false>
+template <bool NT, bool GROUPED = false, bool ROW_PACKED = false>
 __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t *__restrict__ x,
                                                                  uint8_t *__restrict__ q_row,
                                                                  uint8_t *__restrict__ s_row,
@@ -924,8 +975,14 @@ __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t 
     const int t = threadIdx.x;
     int64_t idx = blockIdx.x;
     if (idx >= ntiles) return;
+    // ROW_PACKED: the axis-1 grid goes straight into the packed layout (N =
+    // rows, K = cols), the walk running over the rows of whole panels so that
+    // a half panel past the matrix writes its padding (zero codes, scale code
+    // 127) and nothing of axis 0
+    const int64_t rows_walk = ROW_PACKED ? (rows + kPanelRows - 1) / kPanelRows * kPanelRows : rows;
+    const int64_t KS1 = (cols + kKStep - 1) / kKStep;
     int64_t b_unused, R0, C0;
-    tile_origin_of(idx, rows, cols, b_unused, R0, C0);
+    tile_origin_of(idx, rows_walk, cols, b_unused, R0, C0);
     v4i v[kA0Loads];
     load_tile_regs<NT>(x, rows, cols, R0, C0, t, v);
     const int64_t nb = cols / 32;
@@ -943,10 +1000,30 @@ __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t 
         const int64_t nxt = idx + gridDim.x;
         int64_t R2 = R0, C2 = C0;
         if (nxt < ntiles) {
-            tile_origin_of(nxt, rows, cols, b_unused, R2, C2);
+            tile_origin_of(nxt, rows_walk, cols, b_unused, R2, C2);
             load_tile_regs<NT>(x, rows, cols, R2, C2, t, v);
         }
-        if (!GROUPED || q_row != nullptr) {
+        if constexpr (ROW_PACKED) {
+            // rows R0 .. R0+127 are half (R0 / 128) % 2 of panel R0 / 256 at
+            // k-step C0 / 128 (as quantize_dual_packed_kernel)
+            const int64_t tl = (R0 / kPanelRows) * KS1 + C0 / kKStep;
+            const int half = (int)((R0 / kA0Tile) & 1);
+            uint8_t *qt = q_row + tl * kTileBytes + half * (kA0Tile * kKStep);
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int u = u2 * 256 + t, r = u >> 2, bb = u & 3;
+                uint32_t q8[8];
+                uint32_t code = quantize_row_block(tile, r, bb, q8);
+                if (R0 + r >= rows || C0 + 32 * bb >= cols) code = 127u;    // padding (its codes are zero)
+                const int sw = r & 7;
+                *reinterpret_cast<v4i *>(qt + r * kKStep + (((2 * bb) ^ sw) << 4)) =
+                    v4i{(int)q8[0], (int)q8[1], (int)q8[2], (int)q8[3]};
+                *reinterpret_cast<v4i *>(qt + r * kKStep + (((2 * bb + 1) ^ sw) << 4)) =
+                    v4i{(int)q8[4], (int)q8[5], (int)q8[6], (int)q8[7]};
+                const int rp = half * kA0Tile + r;
+                s_row[tl * kScaleStepBytes + (rp >> 4) * 64 + (rp & 15) + 16 * bb] = (uint8_t)code;
+            }
+        } else if (!GROUPED || q_row != nullptr) {
 #pragma unroll
             for (int u2 = 0; u2 < 2; ++u2) {
                 const int u = u2 * 256 + t, r = u >> 2, bb = u & 3;
@@ -961,10 +1038,12 @@ __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t 
                 }
             }
         }
-        if constexpr (GROUPED)
-            axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t, dstb, rows_out);
-        else
-            axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
+        if (!ROW_PACKED || R0 < rows) {       // (uniform over the workgroup)
+            if constexpr (GROUPED)
+                axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t, dstb, rows_out);
+            else
+                axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
+        }
         __syncthreads();
         R0 = R2;
         C0 = C2;
@@ -1246,6 +1325,19 @@ hipError_t launch_quantize_gather(const uint16_t *x, int64_t rows_in, int64_t co
     return hipGetLastError();
 }
 
+hipError_t launch_quantize_gather_packed(const uint16_t *x, int64_t rows_in, int64_t cols, const int64_t *idx,
+                                         int64_t rows_out, uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream) {
+    const int64_t nsteps = packed_panels(rows_out) * 16 * packed_ksteps(cols);
+    // six 4-wave workgroups per CU, as the list quantizer's packed variant
+    int64_t grid = (nsteps + 3) / 4;
+    const int64_t cap = (int64_t)device_cu_count() * 6;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(quantize_gather_packed_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, rows_in, cols,
+                       idx, rows_out, q_packed, s_packed, nsteps);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_row,
                                 uint8_t *s_row, uint8_t *q_col, uint8_t *s_col, hipStream_t stream) {
     const int64_t tiles = ((rows + kA0Tile - 1) / kA0Tile) * ((cols + kA0Tile - 1) / kA0Tile);
@@ -1310,6 +1402,30 @@ hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t
     }
     hipLaunchKernelGGL(quantize_dual_grouped_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, q_row,
                        s_row, q_col, s_col, rows, cols, src_off, dst_off, (int)G, rows_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual_grouped_packed(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qr_packed,
+                                               uint8_t *sr_packed, uint8_t *q_col, uint8_t *s_col,
+                                               const int32_t *src_off, const int32_t *dst_off, int64_t G,
+                                               int64_t rows_out, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_dst_pads_kernel, dim3((unsigned)(rows_out / 32)), dim3(256), 0, stream, q_col,
+                       s_col, rows, cols, src_off, dst_off, (int)G, rows_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the walk over whole panels of rows (cols % 32 == 0, so rows are
+    // 16-byte aligned for the walk's loads)
+    const int64_t tiles = 2 * packed_panels(rows) * ((cols + kA0Tile - 1) / kA0Tile);
+    if (rows * cols * 2 >= kQuantNontemporalBytes) {
+        const int64_t grid = walk_grid<quantize_dual_walk_kernel<true, true, true>>(tiles);
+        hipLaunchKernelGGL((quantize_dual_walk_kernel<true, true, true>), dim3((unsigned)grid), dim3(256), 0, stream,
+                           x, qr_packed, sr_packed, q_col, s_col, rows, cols, tiles, src_off, dst_off, (int)G,
+                           rows_out);
+        return hipGetLastError();
+    }
+    const int64_t grid = walk_grid<quantize_dual_walk_kernel<false, true, true>>(tiles);
+    hipLaunchKernelGGL((quantize_dual_walk_kernel<false, true, true>), dim3((unsigned)grid), dim3(256), 0, stream, x,
+                       qr_packed, sr_packed, q_col, s_col, rows, cols, tiles, src_off, dst_off, (int)G, rows_out);
     return hipGetLastError();
 }
 

@@ -206,3 +206,28 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, q, p, p, p, 2, 128, NULL) == 5  # alignment
     r = ctypes.c_void_p(p.value + 2)
     assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, p, p, r, p, 2, 128, NULL) == 5  # offsets align
+    # ... with the axis-1 grid into the packed layout (both buffers required)
+    dgp = libmx.mxfp8_quantize_dual_grouped_packed
+    assert dgp(p, 64, 64, NULL, p, p, p, p, p, 2, 128, NULL) == 1                   # packed codes
+    assert dgp(p, 64, 64, p, p, p, p, NULL, p, 2, 128, NULL) == 1                   # offsets
+    assert dgp(p, 48, 64, p, p, p, p, p, p, 2, 128, NULL) == 2                      # rows % 32
+    assert dgp(p, 64, 64, p, p, p, p, p, p, 2, 100, NULL) == 2                      # rows_out % 32
+    assert dgp(p, 64, 64, p, p, p, p, p, p, 0, 128, NULL) == 2                      # G
+    assert dgp(p, 64, (1 << 22) + 32, p, p, p, p, p, p, 2, 128, NULL) == 2          # cols beyond the K limit
+    for i in range(4):                     # x, packed codes and scales, q_col (s_col rows need no alignment)
+        args = [p, p, p, p]
+        args[i] = q
+        assert dgp(args[0], 64, 64, args[1], args[2], args[3], p, p, p, 2, 128, NULL) == 5, i
+    assert dgp(p, 64, 64, p, p, p, p, r, p, 2, 128, NULL) == 5                      # offsets align
+    # gather into the packed layout
+    gpk = libmx.mxfp8_quantize_gather_packed
+    assert gpk(p, 8, 64, NULL, 16, p, p, NULL) == 1                                 # index table
+    assert gpk(p, 8, 64, p, 16, p, NULL, NULL) == 1                                 # packed scales
+    assert gpk(p, 8, 40, p, 16, p, p, NULL) == 2                                    # cols % 32
+    assert gpk(p, 8, 64, p, 0, p, p, NULL) == 2                                     # rows_out
+    assert gpk(p, 8, (1 << 22) + 32, p, 16, p, p, NULL) == 2                        # cols beyond the K limit
+    assert gpk(p, 8, 64, r, 16, p, p, NULL) == 5                                    # index table alignment
+    for i in range(3):
+        args = [p, p, p]
+        args[i] = q
+        assert gpk(args[0], 8, 64, p, 16, args[1], args[2], NULL) == 5, i

@@ -884,6 +884,70 @@ def test_quantize_dual_packed_writes_every_byte_once(batch, rows, cols):
         assert np.all(a == 1), (rows, cols)
 
 
+@pytest.mark.parametrize("rows,cols", [(32, 32), (96, 160), (256, 256), (288, 416), (67744, 768)])
+def test_quantize_dual_grouped_packed_row_grid_written_once(rows, cols):
+    """quantize_dual_walk_kernel<.., ROW_PACKED>: the walk over whole panels
+    of rows (2 NP(rows) x ceil(cols / 128) tiles) writes every byte of the
+    axis-1 packed layout (N = rows, K = cols) exactly once; the tiles past
+    the matrix (R0 >= rows) write only that padding."""
+    KS1, NP1 = ceil_div(cols, KSTEP), ceil_div(rows, PANEL)
+    TC = ceil_div(cols, 128)
+    assert TC == KS1
+    ntiles = 2 * NP1 * TC
+    q1 = np.zeros(NP1 * KS1 * TILE_BYTES // 16, np.int32)
+    s1 = np.zeros(NP1 * KS1 * 1024, np.int32)
+    t = np.arange(256)
+    axis0_tiles = 0
+    for idx in range(ntiles):
+        R0, C0 = idx // TC * 128, idx % TC * 128
+        assert R0 < NP1 * PANEL and C0 < KS1 * 128
+        tl = R0 // 256 * KS1 + C0 // 128
+        half = R0 // 128 % 2
+        base = tl * TILE_BYTES + half * 128 * 128
+        for u2 in range(2):
+            u = u2 * 256 + t
+            r, bb = u >> 2, u & 3
+            for c in (2 * bb, 2 * bb + 1):
+                off = base + r * 128 + ((c ^ (r & 7)) << 4)
+                np.add.at(q1, off // 16, 1)
+            rp = half * 128 + r
+            np.add.at(s1, tl * 1024 + (rp >> 4) * 64 + (rp & 15) + 16 * bb, 1)
+        axis0_tiles += R0 < rows
+    assert np.all(q1 == 1) and np.all(s1 == 1), (rows, cols)
+    assert axis0_tiles == ceil_div(rows, 128) * TC        # the tiles of the plain walk, once each
+
+
+def test_quantize_gather_packed_loads_stay_inside():
+    """quantize_gather_packed_kernel: every 16-byte load reads a row of x
+    named by the index table (inside [0, rows_in)) and columns inside it;
+    rows past rows_out and out-of-range indices load nothing."""
+    rows_in, cols, rows_out = 37, 288, 300
+    rng = np.random.default_rng(5)
+    idx = rng.integers(-3, rows_in + 3, rows_out)
+    KS = ceil_div(cols, KSTEP)
+    lane = np.arange(64)
+    bl, half = lane >> 1, lane & 1
+    i, kb4 = bl >> 2, bl & 3
+    loaded = np.zeros((rows_in, cols), np.int32)
+    for st in range(ceil_div(rows_out, PANEL) * 16 * KS):
+        atom, ks = st // KS, st % KS
+        kcol = ks * 128 + kb4 * 32 + half * 16
+        for u in range(4):
+            r = atom * 16 + (u >> 1) * 8 + i
+            k = kcol + (u & 1) * 8
+            src = np.where(r < rows_out, idx[np.minimum(r, rows_out - 1)], -1)
+            ok = (src >= 0) & (src < rows_in) & (k < cols)
+            assert np.all(k[ok] + 8 <= cols)
+            for e in range(8):
+                np.add.at(loaded, (src[ok], k[ok] + e), 1)
+    # each output row's source elements read exactly once per output row naming it
+    want = np.zeros_like(loaded)
+    for r in range(rows_out):
+        if 0 <= idx[r] < rows_in:
+            want[idx[r]] += 1
+    assert np.array_equal(loaded, want)
+
+
 WS_UNITS = 64
 
 

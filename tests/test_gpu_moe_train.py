@@ -235,3 +235,77 @@ def test_wgrad_aligned_groups_match_oracle(mx, oracle_mod, tokens, experts, topk
     a32, s32 = oracle_mod.quantize(dy, 0)
     b32, t32 = oracle_mod.quantize(h, 0)
     _check_wgrad(oracle_mod, ch, a32, s32, b32, t32, offsets, out, rows=rows)
+
+
+@pytest.mark.parametrize("tokens,experts,topk,hidden", [(64, 8, 2, 64), (512, 16, 4, 288), (8192, 128, 8, 2048)])
+def test_quantize_gather_packed_matches_oracle_pack(mx, oracle_mod, tokens, experts, topk, hidden):
+    """mxfp8_quantize_gather_packed: the packed layout of the gathered,
+    zero-padded rows (out-of-range indices included) is exactly the oracle's
+    pack of its quantize along K (the small cases; padding rows and blocks
+    included, the buffers filled with 0xEE first) and, at the MoE layer's
+    size, exactly mxfp8_repack of mxfp8_quantize_gather's grid."""
+    import torch
+    _say("gather packed", tokens, experts, topk, hidden)
+    rng, offsets, row_token, _ = _routing(tokens + experts + 1, tokens, experts, topk)
+    x = wl.normal_bf16(rng, (tokens, hidden), outlier_frac=0.01)
+    idx = row_token.copy()
+    if idx.size > 8:
+        idx[3] = tokens + 5
+        idx[5] = -7
+    R = idx.size
+    xd, idd = to_dev(x), to_dev(idx)
+    out = mx.PackedWeight(torch.full((mx.packed_bytes(1, R, hidden, 0),), 0xEE, dtype=torch.uint8, device=xd.device),
+                          torch.full((mx.packed_bytes(1, R, hidden, 1),), 0xEE, dtype=torch.uint8, device=xd.device),
+                          1, R, hidden)
+    mx.quantize_gather_packed_(xd, idd, out)
+    torch.cuda.synchronize()
+    if R * hidden <= 1 << 22:
+        gathered = np.zeros((R, hidden), np.uint16)
+        ok = (idx >= 0) & (idx < tokens)
+        gathered[ok] = x[idx[ok]]
+        rq, rs = oracle_mod.quantize(gathered, 1)
+        qp, sp = oracle_mod.pack(rq.reshape(1, R, hidden), rs.reshape(1, R, hidden // 32), 1, R, hidden)
+        assert np.array_equal(to_host(out.q), qp) and np.array_equal(to_host(out.s), sp)
+    else:
+        q, s = mx.quantize_gather(xd, idd)
+        ref = mx.repack(q, s)
+        torch.cuda.synchronize()
+        assert torch.equal(out.q, ref.q) and torch.equal(out.s, ref.s)
+
+
+@pytest.mark.parametrize("tokens,experts,topk,cols", [(64, 8, 2, 64), (512, 16, 4, 288), (8192, 128, 8, 768),
+                                                      (8192, 128, 8, 2048)])
+def test_quantize_dual_grouped_packed_matches(mx, oracle_mod, tokens, experts, topk, cols):
+    """mxfp8_quantize_dual_grouped_packed: the regrouped token-blocked grid is
+    byte for byte mxfp8_quantize_dual_grouped's (pads included; outputs filled
+    first), and the packed row grid is the oracle's pack of quantize(x, 1) on
+    the small cases, mxfp8_repack of the canonical row grid at the MoE
+    learner's sizes (every padding byte written)."""
+    import torch
+    _say("dual grouped packed", tokens, experts, topk, cols)
+    rng, offsets, row_token, _ = _routing(tokens + cols + 3, tokens, experts, topk)
+    T = int(offsets[-1])
+    x = np.zeros((T, cols), np.uint16)
+    real = row_token >= 0
+    x[real] = wl.normal_bf16(rng, (int(real.sum()), cols), outlier_frac=0.01)
+    dst = _pad128(offsets)
+    rows_out = int(dst[-1]) + 64
+    xd, so, do = to_dev(x), to_dev(offsets), to_dev(dst)
+    dev = xd.device
+    q_col = torch.full((cols, rows_out), 0xFF, dtype=torch.uint8, device=dev)
+    s_col = torch.full((cols, rows_out // 32), 0xFF, dtype=torch.uint8, device=dev)
+    pr = mx.PackedWeight(torch.full((mx.packed_bytes(1, T, cols, 0),), 0xEE, dtype=torch.uint8, device=dev),
+                         torch.full((mx.packed_bytes(1, T, cols, 1),), 0xEE, dtype=torch.uint8, device=dev),
+                         1, T, cols)
+    mx.quantize_dual_grouped_packed_(xd, so, do, q_col, s_col, pr)
+    q_row, s_row, q_col2, s_col2 = mx.quantize_dual_grouped(xd, so, do, rows_out)
+    torch.cuda.synchronize()
+    assert torch.equal(q_col, q_col2) and torch.equal(s_col, s_col2)
+    if T * cols <= 1 << 22:
+        rq, rs = oracle_mod.quantize(x, 1)
+        qp, sp = oracle_mod.pack(rq.reshape(1, T, cols), rs.reshape(1, T, cols // 32), 1, T, cols)
+        assert np.array_equal(to_host(pr.q), qp) and np.array_equal(to_host(pr.s), sp)
+    else:
+        ref = mx.repack(q_row, s_row)
+        torch.cuda.synchronize()
+        assert torch.equal(pr.q, ref.q) and torch.equal(pr.s, ref.s)
