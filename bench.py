@@ -645,8 +645,9 @@ def bench_moe_train(args, dev):
     the weight gradients are written regrouped, every expert's tokens
     starting on a multiple of 128 (mxfp8_quantize_dual_grouped_packed), so
     the weight-gradient GEMMs run aligned.  Timed beside the step: the
-    weight-gradient GEMMs over the 32-padded grids and the other four with A
-    from the canonical grids.
+    weight-gradient GEMMs over the 32-padded grids and over the regrouped
+    grids in the packed layout (mxfp8_grouped_gemm_wgrad_packed), and the
+    other four with A from the canonical grids.
     The activation function between gate_up and down is outside the MXFP8
     path; h and dH are drawn as N(0,1) and N(0,1)*2^-10 on real rows."""
     import torch
@@ -688,10 +689,10 @@ def bench_moe_train(args, dev):
         return mx.PackedWeight(torch.empty(mx.packed_bytes(1, Mt, k, 0), **u8),
                                torch.empty(mx.packed_bytes(1, Mt, k, 1), **u8), 1, Mt, k)
     xq, h1, dy1, dh1 = act(H), act(I), act(H), act(I2)
-    h0 = (torch.empty((I, T128), **u8), torch.empty((I, T128 // 32), **u8))
-    dy0 = (torch.empty((H, T128), **u8), torch.empty((H, T128 // 32), **u8))
-    dh0 = (torch.empty((I2, T128), **u8), torch.empty((I2, T128 // 32), **u8))
-    x0 = (torch.empty((H, T128), **u8), torch.empty((H, T128 // 32), **u8))
+
+    def tok(k):                                   # a token-blocked [k, T128] grid, regrouped (canonical)
+        return (torch.empty((k, T128), **u8), torch.empty((k, T128 // 32), **u8))
+    h0, dy0, dh0, x0 = tok(I), tok(H), tok(I2), tok(H)
     bf = dict(dtype=torch.bfloat16, device=dev)
     y_gu, y_d = torch.empty((Mt, I2), **bf), torch.empty((Mt, H), **bf)
     g_h, g_x = torch.empty((Mt, I), **bf), torch.empty((Mt, H), **bf)
@@ -702,29 +703,36 @@ def bench_moe_train(args, dev):
         ("w_d_dual_packed", lambda: mx.quantize_dual_packed_(t["W_d"], P_d, P_dT)),
         ("gather_quantize_X", lambda: mx.quantize_gather_packed_(t["X"], idx, xq)),
         ("fprop_gate_up", lambda: mx.grouped_gemm_packed(xq, P_gu, offs, torch.bfloat16, out=y_gu)),
-        ("quantize_dual_h", lambda: mx.quantize_dual_grouped_packed_(t["A_d"], offs, offs128, *h0, h1)),
+        ("quantize_dual_h", lambda: mx.quantize_dual_grouped_packed_(t["A_d"], offs, offs128, h0, h1)),
         ("fprop_down", lambda: mx.grouped_gemm_packed(h1, P_d, offs, torch.bfloat16, out=y_d)),
-        ("quantize_dual_dY", lambda: mx.quantize_dual_grouped_packed_(t["dY"], offs, offs128, *dy0, dy1)),
+        ("quantize_dual_dY", lambda: mx.quantize_dual_grouped_packed_(t["dY"], offs, offs128, dy0, dy1)),
         ("dgrad_down", lambda: mx.grouped_gemm_packed(dy1, P_dT, offs, torch.bfloat16, out=g_h)),
-        ("wgrad_down", lambda: mx.grouped_gemm_wgrad(dy0[0], dy0[1], h0[0], h0[1], offs128, torch.float32,
-                                                     out=dW_d)),
-        ("quantize_dual_dH", lambda: mx.quantize_dual_grouped_packed_(t["dH"], offs, offs128, *dh0, dh1)),
+        ("wgrad_down", lambda: mx.grouped_gemm_wgrad(*dy0, *h0, offs128, torch.float32, out=dW_d)),
+        ("quantize_dual_dH", lambda: mx.quantize_dual_grouped_packed_(t["dH"], offs, offs128, dh0, dh1)),
         ("dgrad_gate_up", lambda: mx.grouped_gemm_packed(dh1, P_guT, offs, torch.bfloat16, out=g_x)),
         ("quantize_X_axis0", lambda: mx.quantize_dual_grouped_into(t["Xperm"], offs, offs128, *x0)),
-        ("wgrad_gate_up", lambda: mx.grouped_gemm_wgrad(dh0[0], dh0[1], x0[0], x0[1], offs128, torch.float32,
-                                                        out=dW_gu)),
+        ("wgrad_gate_up", lambda: mx.grouped_gemm_wgrad(*dh0, *x0, offs128, torch.float32, out=dW_gu)),
     ]
     torch.cuda.synchronize()
     ms, avg = run_timed(ops, args, live=("wgrad_gate_up",))
-    # the weight-gradient GEMMs over the 32-padded token grids, for comparison
-    # (operands quantized once, outside the timing)
-    p32 = {}
+    # the weight-gradient GEMMs over the 32-padded canonical token grids and
+    # over the regrouped grids in the packed layout
+    # (mxfp8_grouped_gemm_wgrad_packed), for comparison (operands quantized
+    # once, outside the timing)
+    p32, pk = {}, {}
     for name, src, cols in (("dY", t["dY"], H), ("h", t["A_d"], I), ("dH", t["dH"], I2), ("X", t["Xperm"], H)):
         p32[name] = (torch.empty((cols, Mt), **u8), torch.empty((cols, Mt // 32), **u8))
         mx.quantize_into(src, 0, *p32[name])
+        pk[name] = mx.PackedWeight(torch.empty(mx.packed_bytes(1, cols, T128, 0), **u8),
+                                   torch.empty(mx.packed_bytes(1, cols, T128, 1), **u8), 1, cols, T128)
+        mx.quantize_dual_grouped_packed_(src, offs, offs128, pk[name])
     cmp_ops = [("wgrad_down_32", lambda: mx.grouped_gemm_wgrad(*p32["dY"], *p32["h"], offs, torch.float32, out=dW_d)),
                ("wgrad_gate_up_32", lambda: mx.grouped_gemm_wgrad(*p32["dH"], *p32["X"], offs, torch.float32,
-                                                                   out=dW_gu))]
+                                                                   out=dW_gu)),
+               ("wgrad_down_packed", lambda: mx.grouped_gemm_wgrad_packed(pk["dY"], pk["h"], offs128, torch.float32,
+                                                                           out=dW_d)),
+               ("wgrad_gate_up_packed", lambda: mx.grouped_gemm_wgrad_packed(pk["dH"], pk["X"], offs128,
+                                                                              torch.float32, out=dW_gu))]
     # the forward and data-gradient grouped GEMMs with A read from the
     # canonical grids of the same rows (mxfp8_grouped_gemm), for comparison
     c1 = {}
@@ -736,7 +744,7 @@ def bench_moe_train(args, dev):
         ("dgrad_down_canonical_A", lambda: mx.grouped_gemm(*c1["dY"], P_dT, offs, torch.bfloat16, out=g_h)),
         ("dgrad_gate_up_canonical_A", lambda: mx.grouped_gemm(*c1["dH"], P_guT, offs, torch.bfloat16, out=g_x))]
     _, avg32 = run_timed(cmp_ops, argparse.Namespace(steps=max(5, args.steps // 4), warmup=2))
-    del p32, c1
+    del p32, c1, pk
     f_gu = 2.0 * real * I2 * H
     f_d = 2.0 * real * H * I
     flops = {"fprop_gate_up": f_gu, "fprop_down": f_d, "dgrad_down": f_d, "wgrad_down": f_d,
@@ -749,11 +757,12 @@ def bench_moe_train(args, dev):
         else:
             kern[name] = {"us": round(us, 2)}
     for name, us in avg32.items():
-        base = name[:-3] if name.endswith("_32") else name[:-len("_canonical_A")]
+        base, note = ((name[:-3], "32-padded canonical token grids") if name.endswith("_32") else
+                      (name[:-len("_packed")], "regrouped token grids in the packed layout") if name.endswith("_packed")
+                      else (name[:-len("_canonical_A")], "A from the canonical grid"))
         tf = flops[base] / (us * 1e-6) / 1e12
         kern[name] = {"us": round(us, 2), "TFLOP/s": round(tf, 1), "frac_mxfp8_peak": round(tf / MXFP8_PEAK_TFLOPS, 4),
-                      "note": ("32-padded token grids" if name.endswith("_32") else "A from the canonical grid")
-                      + ", not part of the step"}
+                      "note": note + ", not part of the step"}
     total = sum(flops.values())
     gemm_us = sum(avg[k] for k in flops)
     return _line("MXFP8 GEMM TFLOP/s (% MX peak) + quantize GB/s (% HBM) at Qwen3-8B shapes",

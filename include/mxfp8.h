@@ -166,24 +166,32 @@ mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64
 
 /*
  * mxfp8_quantize_dual_grouped_packed -- mxfp8_quantize_dual_grouped with the
- * axis-1 grid written straight into the GEMM's packed operand layout.
+ * row grid written straight into the GEMM's packed operand layout, and the
+ * regrouped token-blocked grid in the layout the caller picks.
  *
- * One BF16 read of the token-sorted x [rows][cols] gives the operand of the
- * experts' forward or data-gradient GEMM (mxfp8_grouped_gemm_packed's A:
- * q_row_packed / s_row_packed, exactly what mxfp8_repack writes for
- * mxfp8_quantize(x, axis=1) with N = rows, K = cols, padding included;
- * mxfp8_packed_bytes(1, rows, cols, 0 / 1) bytes) and the regrouped
- * token-blocked grid of their weight gradients (q_col, s_col: exactly as
- * mxfp8_quantize_dual_grouped).  Arguments, table rules and limits as
- * mxfp8_quantize_dual_grouped, plus those of mxfp8_repack for the packed
- * layout; both axis-1 buffers are required.  Bit-exact, deterministic; no
+ * One BF16 read of the token-sorted x [rows][cols] gives
+ *   q_row_packed / s_row_packed (optional: both NULL or both given): the
+ *     operand of the experts' forward or data-gradient GEMM
+ *     (mxfp8_grouped_gemm_packed's A), exactly what mxfp8_repack writes for
+ *     mxfp8_quantize(x, axis=1) with N = rows, K = cols
+ *     (mxfp8_packed_bytes(1, rows, cols, 0 / 1) bytes, padding included);
+ *   q_col / s_col: the regrouped token-blocked grid of the experts' weight
+ *     gradients -- col_layout MXFP8_CANONICAL: exactly
+ *     mxfp8_quantize_dual_grouped's (q_col, s_col) (for
+ *     mxfp8_grouped_gemm_wgrad); MXFP8_PACKED: exactly what mxfp8_repack
+ *     writes for that grid with N = cols, K = rows_out
+ *     (mxfp8_packed_bytes(1, cols, rows_out, 0 / 1) bytes; pad blocks zero
+ *     codes with scale code 0, the layout's padding scale code 127; for
+ *     mxfp8_grouped_gemm_wgrad_packed).
+ * Arguments, table rules and limits as mxfp8_quantize_dual_grouped, plus
+ * those of mxfp8_repack for the packed layouts.  Bit-exact, deterministic; no
  * allocation, no synchronization.
  */
 mxfp8_status mxfp8_quantize_dual_grouped_packed(const void *x_bf16, int64_t rows, int64_t cols,
-                                                uint8_t *q_row_packed, uint8_t *s_row_packed, uint8_t *q_col,
-                                                uint8_t *s_col, const int32_t *src_offsets,
-                                                const int32_t *dst_offsets, int64_t G, int64_t rows_out,
-                                                hipStream_t stream);
+                                                uint8_t *q_row_packed, uint8_t *s_row_packed,
+                                                uint8_t *q_col, uint8_t *s_col, mxfp8_layout col_layout,
+                                                const int32_t *src_offsets, const int32_t *dst_offsets,
+                                                int64_t G, int64_t rows_out, hipStream_t stream);
 
 /*
  * mxfp8_quantize_packed -- weights BF16 -> MXFP8 straight into the GEMM's
@@ -657,6 +665,33 @@ mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s,
                                       const int32_t *d_group_offsets, int64_t G, int64_t T,
                                       int64_t M, int64_t N, void *c, mxfp8_dtype c_dtype,
                                       hipStream_t stream);
+
+/*
+ * mxfp8_grouped_gemm_wgrad_packed -- mxfp8_grouped_gemm_wgrad with both
+ * operands in the GEMM's packed layout along the token axis.
+ *
+ *   A (a_q_packed, a_s_packed): the packed layout of [M][T] (N = M, K = T;
+ *     mxfp8_packed_bytes(1, M, T, 0 / 1) bytes);
+ *   B (b_q_packed, b_s_packed): the packed layout of [N][T];
+ *   d_group_offsets: DEVICE int32 [G+1] token offsets; expert g reduces over
+ *     the k-steps [o_g / 128, ceil(o_{g+1} / 128)) of the token axis, so
+ *     well-formed tables hold multiples of 128 (as
+ *     mxfp8_quantize_dual_grouped_packed's regrouped grid); offsets are
+ *     clamped into [0, T], so a malformed table can only give wrong sums,
+ *     never address outside the operands;
+ *   C: [G][M][N], FP32 or BF16; an empty group's C[g] is all zeros.
+ * T % 32 == 0, N % 4 == 0 (FP32) or N % 8 == 0 (BF16), the limits of
+ * mxfp8_repack for both operands, G <= 65535.  For 128-aligned groups C is
+ * bit-identical to mxfp8_grouped_gemm_wgrad over the canonical grids (same
+ * products, same order).  Deterministic; no allocation, no synchronization.
+ * Speed: on the Qwen3-30B-A3B learner's weight gradients this launch is
+ * slower than mxfp8_grouped_gemm_wgrad's aligned path (its 256x128 tiles
+ * write FP32 C in half-size pieces); it serves callers that keep one layout.
+ */
+mxfp8_status mxfp8_grouped_gemm_wgrad_packed(const uint8_t *a_q_packed, const uint8_t *a_s_packed,
+                                             const uint8_t *b_q_packed, const uint8_t *b_s_packed,
+                                             const int32_t *d_group_offsets, int64_t G, int64_t T, int64_t M,
+                                             int64_t N, void *c, mxfp8_dtype c_dtype, hipStream_t stream);
 
 /*
  * mxfp8_selfcheck -- post-sync check of one quantized layer's serving path.

@@ -64,11 +64,13 @@ def lib():
         L.mxfp8_quantize_gather_packed.argtypes = [P, I64, I64, P, I64, P, P, P]
         L.mxfp8_quantize_gather_packed.restype = I32
         L.mxfp8_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        L.mxfp8_grouped_gemm_wgrad_packed.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, I32, P]
+        L.mxfp8_grouped_gemm_wgrad_packed.restype = I32
         for f in ("mxfp8_quantize_batched", "mxfp8_quantize_gather", "mxfp8_grouped_gemm_wgrad"):
             getattr(L, f).restype = I32
         L.mxfp8_quantize_dual.argtypes = [P, I64, I64, P, P, P, P, P]
         L.mxfp8_quantize_dual_grouped.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
-        L.mxfp8_quantize_dual_grouped_packed.argtypes = [P, I64, I64, P, P, P, P, P, P, I64, I64, P]
+        L.mxfp8_quantize_dual_grouped_packed.argtypes = [P, I64, I64, P, P, P, P, I32, P, P, I64, I64, P]
         L.mxfp8_quantize_dual_grouped_packed.restype = I32
         L.mxfp8_gemm_splitk.argtypes = [P, P, P, P, I32, I64, I64, I64, P, I32, P, ctypes.c_size_t, P]
         L.mxfp8_gemm_splitk.restype = I32
@@ -362,34 +364,50 @@ def quantize_dual_grouped_into(x: torch.Tensor, src_offsets: torch.Tensor, dst_o
 
 
 def quantize_dual_grouped_packed_(x: torch.Tensor, src_offsets: torch.Tensor, dst_offsets: torch.Tensor,
-                                  q_col: torch.Tensor, s_col: torch.Tensor, row_out: "PackedWeight") -> None:
-    """mxfp8_quantize_dual_grouped_packed: (q_col, s_col) as
-    quantize_dual_grouped_into, and quantize(x, 1) straight into
-    row_out = PackedWeight(batch 1, N = rows, K = cols)."""
+                                  col_out, row_out: "PackedWeight | None" = None) -> None:
+    """mxfp8_quantize_dual_grouped_packed: the regrouped token-blocked grid
+    of quantize_dual_grouped_into into col_out -- a (q_col [cols, rows_out],
+    s_col [cols, rows_out/32]) pair (canonical) or PackedWeight(batch 1,
+    N = cols, K = rows_out) (packed) -- and (if given) quantize(x, 1)
+    straight into row_out = PackedWeight(batch 1, N = rows, K = cols)."""
     _need(x, torch.bfloat16, "x")
-    for t, n in ((q_col, "q_col"), (s_col, "s_col")):
-        _need(t, torch.uint8, n)
     for t, n in ((src_offsets, "src_offsets"), (dst_offsets, "dst_offsets")):
         _need(t, torch.int32, n)
-    if x.dim() != 2 or q_col.dim() != 2:
-        raise ValueError("x and q_col must be 2-D")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
     rows, cols = x.shape
-    rows_out = q_col.shape[1]
     G = src_offsets.numel() - 1
     if G < 1 or dst_offsets.numel() != G + 1:
         raise ValueError("src_offsets and dst_offsets must both hold G+1 >= 2 entries")
+    outs = []
+    if isinstance(col_out, PackedWeight):
+        if col_out.batch != 1 or col_out.N != cols:
+            raise ValueError("col_out must be PackedWeight(batch 1, N = %d, K = rows_out)" % cols)
+        rows_out, layout, qc, sc = col_out.K, MXFP8_PACKED, col_out.q, col_out.s
+        outs.append((col_out, (cols, rows_out), "col_out"))
+    else:
+        qc, sc = col_out
+        _need(qc, torch.uint8, "q_col")
+        _need(sc, torch.uint8, "s_col")
+        if qc.dim() != 2:
+            raise ValueError("q_col must be 2-D")
+        rows_out, layout = qc.shape[1], MXFP8_CANONICAL
+        if tuple(qc.shape) != (cols, rows_out) or tuple(sc.shape) != (cols, rows_out // 32):
+            raise ValueError("q_col/s_col must be [cols, rows_out] / [cols, rows_out/32]")
     if rows % 32 or cols % 32 or rows_out % 32:
         raise ValueError("rows, cols and rows_out must be multiples of 32")
-    if tuple(q_col.shape) != (cols, rows_out) or tuple(s_col.shape) != (cols, rows_out // 32):
-        raise ValueError("q_col/s_col must be [cols, rows_out] / [cols, rows_out/32]")
-    if not isinstance(row_out, PackedWeight) or (row_out.batch, row_out.N, row_out.K) != (1, rows, cols):
-        raise ValueError("row_out must be PackedWeight(batch 1, N = %d, K = %d)" % (rows, cols))
-    _need(row_out.q, torch.uint8, "row_out.q")
-    _need(row_out.s, torch.uint8, "row_out.s")
-    if row_out.q.numel() < packed_bytes(1, rows, cols, 0) or row_out.s.numel() < packed_bytes(1, rows, cols, 1):
-        raise ValueError("row_out buffers too small")
+    if row_out is not None:
+        if not isinstance(row_out, PackedWeight) or (row_out.batch, row_out.N, row_out.K) != (1, rows, cols):
+            raise ValueError("row_out must be PackedWeight(batch 1, N = %d, K = %d)" % (rows, cols))
+        outs.append((row_out, (rows, cols), "row_out"))
+    for t, (n, k), name in outs:
+        _need(t.q, torch.uint8, name + ".q")
+        _need(t.s, torch.uint8, name + ".s")
+        if t.q.numel() < packed_bytes(1, n, k, 0) or t.s.numel() < packed_bytes(1, n, k, 1):
+            raise ValueError("%s buffers too small" % name)
     _check(lib().mxfp8_quantize_dual_grouped_packed(
-        _ptr(x), rows, cols, _ptr(row_out.q), _ptr(row_out.s), _ptr(q_col), _ptr(s_col), _ptr(src_offsets),
+        _ptr(x), rows, cols, _ptr(row_out.q) if row_out is not None else None,
+        _ptr(row_out.s) if row_out is not None else None, _ptr(qc), _ptr(sc), layout, _ptr(src_offsets),
         _ptr(dst_offsets), G, rows_out, _stream(x.device)), "mxfp8_quantize_dual_grouped_packed")
 
 
@@ -837,6 +855,35 @@ def grouped_gemm_wgrad(a_q: torch.Tensor, a_s: torch.Tensor, b_q: torch.Tensor, 
     _check(lib().mxfp8_grouped_gemm_wgrad(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), _ptr(offsets), G,
                                           T, M, N, _ptr(out), code, _stream(a_q.device)),
            "mxfp8_grouped_gemm_wgrad")
+    return out
+
+
+def grouped_gemm_wgrad_packed(a: "PackedWeight", b: "PackedWeight", offsets: torch.Tensor, out_dtype=torch.float32,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+    """mxfp8_grouped_gemm_wgrad_packed: C[g] = A[:, K_g] B[:, K_g]^T with A =
+    PackedWeight(batch 1, N = M, K = T) and B = PackedWeight(batch 1, N, T)
+    (the regrouped token-blocked grids in the packed layout) and device int32
+    token offsets [G+1] (multiples of 128)."""
+    for name, w in (("a", a), ("b", b)):
+        if not isinstance(w, PackedWeight) or w.batch != 1:
+            raise ValueError("%s must be a single packed [rows, T] matrix" % name)
+        _need(w.q, torch.uint8, name + ".q")
+        _need(w.s, torch.uint8, name + ".s")
+    _need(offsets, torch.int32, "offsets")
+    if a.K != b.K:
+        raise ValueError("A and B must share the token axis")
+    M, N, T = a.N, b.N, a.K
+    G = offsets.numel() - 1
+    code = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((G, M, N), dtype=out_dtype, device=a.q.device)
+    else:
+        _need(out, out_dtype, "out")
+        if tuple(out.shape) != (G, M, N):
+            raise ValueError("out must be [G, M, N]")
+    _check(lib().mxfp8_grouped_gemm_wgrad_packed(_ptr(a.q), _ptr(a.s), _ptr(b.q), _ptr(b.s), _ptr(offsets), G, T, M,
+                                                 N, _ptr(out), code, _stream(a.q.device)),
+           "mxfp8_grouped_gemm_wgrad_packed")
     return out
 
 

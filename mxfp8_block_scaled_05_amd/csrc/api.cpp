@@ -191,6 +191,29 @@ mxfp8_status mxfp8_quantize_gather_packed(const void *x_bf16, int64_t rows_in, i
                                                 rows_out, q_packed, s_packed, stream));
 }
 
+mxfp8_status mxfp8_grouped_gemm_wgrad_packed(const uint8_t *a_q_packed, const uint8_t *a_s_packed,
+                                             const uint8_t *b_q_packed, const uint8_t *b_s_packed,
+                                             const int32_t *d_group_offsets, int64_t G, int64_t T, int64_t M,
+                                             int64_t N, void *c, mxfp8_dtype c_dtype, hipStream_t stream) {
+    if (!a_q_packed || !a_s_packed || !b_q_packed || !b_s_packed || !d_group_offsets || !c) return MXFP8_ERR_NULL;
+    if (raw(c_dtype) != MXFP8_F32 && raw(c_dtype) != MXFP8_BF16) return MXFP8_ERR_DTYPE;
+    const bool bf = raw(c_dtype) == MXFP8_BF16;
+    if (G < 1 || G > 65535 || T < 32 || T % 32 || T > kMaxK) return MXFP8_ERR_SHAPE;
+    if (M <= 0 || N <= 0 || M >= kMaxDim || N >= kMaxDim || N % (bf ? 8 : 4)) return MXFP8_ERR_SHAPE;
+    // both packed operands within mxfp8_repack's limits; C's row stores
+    // through 32-bit buffer offsets; the unit count within 2^31
+    if (!repack_tiles_ok(1, M, T) || !repack_tiles_ok(1, N, T) || (int64_t)128 * N * (bf ? 2 : 4) >= ((int64_t)1 << 31) ||
+        G * ((M + 255) / 256) * ((N + 127) / 128) > 0x7FFFFFFF)
+        return MXFP8_ERR_SHAPE;
+    if (!aligned16(a_q_packed) || !aligned16(a_s_packed) || !aligned16(b_q_packed) || !aligned16(b_s_packed) ||
+        !aligned16(c) || ((uintptr_t)d_group_offsets & 3u))
+        return MXFP8_ERR_ALIGN;
+    mxfp8_status st = check_device();
+    if (st != MXFP8_OK) return st;
+    return finish(launch_grouped_gemm_wgrad_packed(a_q_packed, a_s_packed, b_q_packed, b_s_packed, d_group_offsets, G,
+                                                   T, M, N, c, bf, stream));
+}
+
 mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
                                       const uint8_t *b_s, const int32_t *d_group_offsets,
                                       int64_t G, int64_t T, int64_t M, int64_t N, void *c,
@@ -267,28 +290,32 @@ mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64
 
 mxfp8_status mxfp8_quantize_dual_grouped_packed(const void *x_bf16, int64_t rows, int64_t cols,
                                                 uint8_t *q_row_packed, uint8_t *s_row_packed, uint8_t *q_col,
-                                                uint8_t *s_col, const int32_t *src_offsets,
+                                                uint8_t *s_col, mxfp8_layout col_layout, const int32_t *src_offsets,
                                                 const int32_t *dst_offsets, int64_t G, int64_t rows_out,
                                                 hipStream_t stream) {
-    if (!x_bf16 || !q_row_packed || !s_row_packed || !q_col || !s_col || !src_offsets || !dst_offsets)
-        return MXFP8_ERR_NULL;
+    if (!x_bf16 || !q_col || !s_col || !src_offsets || !dst_offsets) return MXFP8_ERR_NULL;
+    if ((q_row_packed == nullptr) != (s_row_packed == nullptr)) return MXFP8_ERR_NULL;
+    if (raw(col_layout) != MXFP8_CANONICAL && raw(col_layout) != MXFP8_PACKED) return MXFP8_ERR_DTYPE;
+    const bool col_packed = raw(col_layout) == MXFP8_PACKED;
     if (rows <= 0 || cols <= 0 || rows >= kMaxDim || cols >= kMaxDim || cols > kMaxK) return MXFP8_ERR_SHAPE;
     if (rows % 32 || cols % 32 || !tile128_ok(rows, cols)) return MXFP8_ERR_SHAPE;
     if (G < 1 || G > 65535 || rows_out <= 0 || rows_out % 32 || rows_out >= kMaxDim ||
-        rows_out / 32 > 0x7FFFFFFF)
+        rows_out / 32 > 0x7FFFFFFF || (col_packed && rows_out > kMaxK))
         return MXFP8_ERR_SHAPE;
-    // the packed layout within mxfp8_repack's limits; the walk over whole
-    // panels of rows within 2^31 tiles
-    if (!repack_tiles_ok(1, rows, cols) || 2 * packed_panels(rows) * ((cols + 127) / 128) >= ((int64_t)1 << 31))
+    // the packed layouts within mxfp8_repack's limits; the walk (over whole
+    // panels of rows with the row grid) within 2^31 tiles
+    if ((col_packed && !repack_tiles_ok(1, cols, rows_out)) || (q_row_packed && !repack_tiles_ok(1, rows, cols)) ||
+        2 * packed_panels(rows) * ((cols + 127) / 128) >= ((int64_t)1 << 31))
         return MXFP8_ERR_SHAPE;
-    if (!aligned16(x_bf16) || !aligned16(q_col) || !aligned16(q_row_packed) || !aligned16(s_row_packed) ||
-        ((uintptr_t)src_offsets & 3u) || ((uintptr_t)dst_offsets & 3u))
+    if (!aligned16(x_bf16) || !aligned16(q_col) || (col_packed && !aligned16(s_col)) ||
+        (q_row_packed && (!aligned16(q_row_packed) || !aligned16(s_row_packed))) || ((uintptr_t)src_offsets & 3u) ||
+        ((uintptr_t)dst_offsets & 3u))
         return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
     return finish(launch_quantize_dual_grouped_packed(static_cast<const uint16_t *>(x_bf16), rows, cols, q_row_packed,
-                                                      s_row_packed, q_col, s_col, src_offsets, dst_offsets, G,
-                                                      rows_out, stream));
+                                                      s_row_packed, q_col, s_col, col_packed, src_offsets, dst_offsets,
+                                                      G, rows_out, stream));
 }
 
 mxfp8_status mxfp8_quantize_packed(const void *w_bf16, int64_t batch, int64_t rows, int64_t cols,

@@ -1363,8 +1363,9 @@ __device__ __forceinline__ void ws_tiles(int wg, int nwg, int T, int &first, int
     count = first < hi ? (hi - first + nx - 1) / nx : 0;
 }
 
-template <bool OUT_BF16, bool GROUPED = false>
+template <bool OUT_BF16, bool GROUPED = false, bool GK = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
+    static_assert(!(GROUPED && GK), "grouped rows or grouped K");
     using Lw = WsLayout;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Lw::UNIT_OFF + (GROUPED ? Lw::UNITS * 16 : 0)];
     const int lane = threadIdx.x & 63;
@@ -1374,16 +1375,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
     // launch, fp32 partials of slice s at c + s * c_stride; else one slice).
     // Grouped: the m-tiles are each expert's 256-row tiles in expert order
     // (clamped offsets, as find_group), the packed A rows those of the
-    // padded row space, the launch never split
+    // padded row space, the launch never split.  GK (the experts' weight
+    // gradients): tile u % T of expert u / T over the expert's k-steps
+    // [offsets[g] / 128, offsets[g+1] / 128) of the packed token axis (ranges
+    // clamped into [0, K]), its C at c + g * c_stride
     const int tiles_m =
         GROUPED ? __builtin_amdgcn_readfirstlane(count_group_tiles<256>(p.offsets, p.G, p.M, lane)) : p.tiles_m;
     const int T = tiles_m * p.tiles_n;
-    const int S = p.splits > 1 ? p.splits : 1, L = p.splits > 1 ? p.split_steps : KS;
+    const int S = GK ? p.G : (p.splits > 1 ? p.splits : 1), L = p.splits > 1 ? p.split_steps : KS;
     int first, stride, nunit;
-    ws_tiles(blockIdx.x, gridDim.x, T * S, first, stride, nunit);
+    if constexpr (GK) {
+        // the experts' tiles in dispatch order, every workgroup taking units
+        // blockIdx, blockIdx + grid, ...: an expert's 1 to ~60 k-steps per
+        // tile vary too much for contiguous per-XCD shares of the units, and
+        // consecutive units (one expert's tiles) land on different workgroups
+        first = blockIdx.x;
+        stride = gridDim.x;
+        nunit = first < T * S ? (T * S - first + stride - 1) / stride : 0;
+    } else {
+        ws_tiles(blockIdx.x, gridDim.x, T * S, first, stride, nunit);
+    }
+    // GK: an expert without tokens runs one step whose copies all read out of
+    // range (zeros), so its C is stored as zeros by the common epilogue
+    auto gk_empty = [&](int i) -> bool {
+        if constexpr (GK) {
+            const int g = (first + i * stride) / T;
+            int64_t lo = p.offsets[g], hi = p.offsets[g + 1];
+            lo = lo < 0 ? 0 : (lo > p.K ? p.K : lo);
+            hi = hi < lo ? lo : (hi > p.K ? p.K : hi);
+            return __builtin_amdgcn_readfirstlane((int)(hi > lo)) == 0;
+        } else {
+            return false;
+        }
+    };
     auto unit_steps = [&](int i, int &k0, int &k1) {
-        k0 = (first + i * stride) / T * L;
-        k1 = min(KS, k0 + L);
+        if constexpr (GK) {
+            const int g = (first + i * stride) / T;
+            int64_t lo = p.offsets[g], hi = p.offsets[g + 1];
+            lo = lo < 0 ? 0 : (lo > p.K ? p.K : lo);
+            hi = hi < lo ? lo : (hi > p.K ? p.K : hi);
+            k0 = __builtin_amdgcn_readfirstlane((int)(lo / 128));
+            k1 = __builtin_amdgcn_readfirstlane((int)((hi + 127) / 128));
+            if (k1 == k0) k1 = k0 + 1;
+        } else {
+            k0 = (first + i * stride) / T * L;
+            k1 = min(KS, k0 + L);
+        }
     };
     WsUnit *units = reinterpret_cast<WsUnit *>(smem + Lw::UNIT_OFF);
     if constexpr (GROUPED) {
@@ -1415,7 +1452,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
         int iu = 0, ks = 0, kend = 0, st = 0;                    // next step to issue
         v4i ra = {}, rsa = {}, rb = {}, rsb = {};
         int a_m0 = 0, a_rows = 0;                                // grouped: the tile's rows in A's first panel
+        uint32_t zero_oob = 0;                                   // GK: kOOB for an expert without tokens
         auto set_tile = [&](int i) {
+            zero_oob = gk_empty(i) ? kOOB : 0u;
             int tm, tn;
             int64_t pa, bp = 0;
             if constexpr (GROUPED) {
@@ -1440,11 +1479,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
             rsb = make_srd(p.b_s + pb * KS * kScaleStepBytes + (prow / 16) * 64,
                            (uint32_t)((int64_t)KS * kScaleStepBytes - (prow / 16) * 64));
         };
+        // the first unit from i on that has steps (GK: past empty experts)
         auto start_unit = [&](int i) {
-            unit_steps(i, ks, kend);
-            set_tile(i);
+            for (iu = i; iu < nunit; ++iu) {
+                unit_steps(iu, ks, kend);
+                if (ks < kend) break;
+            }
+            if (iu < nunit) set_tile(iu);
         };
-        if (nunit > 0) start_unit(0);
+        start_unit(0);
         auto issue_next = [&]() {
             const uint32_t sbase = lds0 + st * Lw::STAGE;
             const uint32_t k0 = (uint32_t)ks * (uint32_t)kTileBytes;
@@ -1460,12 +1503,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                                                  (uint32_t)(r % kPanelRows) * 128u + lane * 16
                                            : kOOB;
                 }
-                dma16(ra, off, sbase + Lw::A_OFF + seg * 1024);
+                dma16(ra, off | zero_oob, sbase + Lw::A_OFF + seg * 1024);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int seg = i * 4 + pw;
-                dma16(rb, k0 + seg * 1024 + lane * 16, sbase + Lw::B_OFF + seg * 1024);
+                dma16(rb, (k0 + seg * 1024 + lane * 16) | zero_oob, sbase + Lw::B_OFF + seg * 1024);
             }
             const uint32_t s0 = (uint32_t)ks * (uint32_t)kScaleStepBytes + pw * 256 + lane * 4;
             uint32_t sa_off = s0;
@@ -1477,10 +1520,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                                              (uint32_t)((r % kPanelRows) >> 4) * 64u + (lane & 15) * 4
                                        : kOOB;
             }
-            dma4(rsa, sa_off, sbase + Lw::SA_OFF + pw * 256);
-            if (pw < 2) dma4(rsb, s0, sbase + Lw::SB_OFF + pw * 256);
+            dma4(rsa, sa_off | zero_oob, sbase + Lw::SA_OFF + pw * 256);
+            if (pw < 2) dma4(rsb, s0 | zero_oob, sbase + Lw::SB_OFF + pw * 256);
             st = st == Lw::NST - 1 ? 0 : st + 1;
-            if (++ks == kend && ++iu < nunit) start_unit(iu);
+            if (++ks == kend) start_unit(iu + 1);
         };
         auto wait_all_but_last = [&]() {
             if (nc == 14) __builtin_amdgcn_s_waitcnt(waitcnt_vm(14));
@@ -1512,6 +1555,72 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // the unit's C (or its slice's fp32 partial) from the accumulators, which
+    // are then cleared
+    auto store_unit = [&](int iu) {
+        // this wave's rows and columns that lie inside C
+        const int u = first + iu * stride;
+        int tm, tn;
+        int64_t row0, row_end;
+        if constexpr (GROUPED) {
+            const WsUnit un = units[iu];
+            tn = __builtin_amdgcn_readfirstlane(un.tn);
+            row0 = (int64_t)__builtin_amdgcn_readfirstlane(un.m0) + wm * 128;
+            row_end = __builtin_amdgcn_readfirstlane(un.m_end);
+        } else {
+            grouped_order(u % T, p.tiles_m, p.tiles_n, tm, tn);
+            row0 = (int64_t)tm * Lw::BM + wm * 128;
+            row_end = p.M;
+        }
+        const int64_t col0 = (int64_t)tn * Lw::BN + wn * 64;
+        const int64_t rows_here = row_end - row0, cols_here = p.N - col0;
+        uint8_t *cbase = static_cast<uint8_t *>(p.c) + (S > 1 ? (int64_t)(u / T) * p.c_stride * ES : 0);
+        if (rows_here > 0 && cols_here > 0) {
+            const int rh = (int)min(rows_here, (int64_t)128), chh = (int)min(cols_here, (int64_t)64);
+            const uint32_t range = (uint32_t)(((int64_t)(rh - 1) * p.N + chh) * ES);
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(cbase + (row0 * p.N + col0) * ES, range);
+            const int r0 = lane & 15;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = i * 16 + r0;
+                if constexpr (OUT_BF16) {
+                    // the band of 16 rows through this wave's LDS band
+                    // buffer, out as 8 whole 128-byte rows per store
+                    uint8_t *band = smem + Lw::BAND_OFF + w * Lw::BAND;
+#pragma unroll
+                    for (int jj = 0; jj < FN; ++jj)
+                        *reinterpret_cast<v2i *>(band + r0 * Lw::BAND_ROW + jj * 32 + g16 * 8) =
+                            v2i{(int)bf16x2_rne(acc[i][jj][0], acc[i][jj][1]),
+                                (int)bf16x2_rne(acc[i][jj][2], acc[i][jj][3])};
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int rr = h * 8 + (lane >> 3), cl = (lane & 7) * 8, row = i * 16 + rr;
+                        const v4i v = *reinterpret_cast<const v4i *>(band + rr * Lw::BAND_ROW + (lane & 7) * 16);
+                        const uint32_t off =
+                            (row < rh && cl < chh) ? (uint32_t)(((int64_t)row * p.N + cl) * ES) : kOOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, kStoreStream);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                } else {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int cl = j * 16 + g16 * 4;
+                        const uint32_t off = (r < rh && cl < chh) ? (uint32_t)(((int64_t)r * p.N + cl) * ES) : kOOB;
+                        // (GK: the experts' gradients are written once, streamed)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v4i{(int)float_to_bits(acc[i][j][0]), (int)float_to_bits(acc[i][j][1]),
+                                (int)float_to_bits(acc[i][j][2]), (int)float_to_bits(acc[i][j][3])},
+                            rc, (int)off, 0, GK ? kStoreStream : 0);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    };
     __syncthreads();                                             // step 0 has landed
     int st = 0;
     for (int iu = 0; iu < nunit; ++iu) {
@@ -1543,70 +1652,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                 __builtin_amdgcn_sched_barrier(0);      // keep the read of row i + 1 ahead of row i's MFMAs
             }
             st = st == Lw::NST - 1 ? 0 : st + 1;
-            if (ks == k1 - 1) {
-                // the unit's C (or its slice's fp32 partial): this wave's rows
-                // and columns that lie inside C
-                const int u = first + iu * stride;
-                int tm, tn;
-                int64_t row0, row_end;
-                if constexpr (GROUPED) {
-                    const WsUnit un = units[iu];
-                    tn = __builtin_amdgcn_readfirstlane(un.tn);
-                    row0 = (int64_t)__builtin_amdgcn_readfirstlane(un.m0) + wm * 128;
-                    row_end = __builtin_amdgcn_readfirstlane(un.m_end);
-                } else {
-                    grouped_order(u % T, p.tiles_m, p.tiles_n, tm, tn);
-                    row0 = (int64_t)tm * Lw::BM + wm * 128;
-                    row_end = p.M;
-                }
-                const int64_t col0 = (int64_t)tn * Lw::BN + wn * 64;
-                const int64_t rows_here = row_end - row0, cols_here = p.N - col0;
-                uint8_t *cbase = static_cast<uint8_t *>(p.c) + (S > 1 ? (int64_t)(u / T) * p.c_stride * 4 : 0);
-                if (rows_here > 0 && cols_here > 0) {
-                    const int rh = (int)min(rows_here, (int64_t)128), chh = (int)min(cols_here, (int64_t)64);
-                    const uint32_t range = (uint32_t)(((int64_t)(rh - 1) * p.N + chh) * ES);
-                    const __amdgpu_buffer_rsrc_t rc = make_rsrc(cbase + (row0 * p.N + col0) * ES, range);
-                    const int r0 = lane & 15;
-#pragma unroll
-                    for (int i = 0; i < FM; ++i) {
-                        const int r = i * 16 + r0;
-                        if constexpr (OUT_BF16) {
-                            // the band of 16 rows through this wave's LDS band
-                            // buffer, out as 8 whole 128-byte rows per store
-                            uint8_t *band = smem + Lw::BAND_OFF + w * Lw::BAND;
-#pragma unroll
-                            for (int jj = 0; jj < FN; ++jj)
-                                *reinterpret_cast<v2i *>(band + r0 * Lw::BAND_ROW + jj * 32 + g16 * 8) =
-                                    v2i{(int)bf16x2_rne(acc[i][jj][0], acc[i][jj][1]),
-                                        (int)bf16x2_rne(acc[i][jj][2], acc[i][jj][3])};
-                            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                const int rr = h * 8 + (lane >> 3), cl = (lane & 7) * 8, row = i * 16 + rr;
-                                const v4i v = *reinterpret_cast<const v4i *>(band + rr * Lw::BAND_ROW + (lane & 7) * 16);
-                                const uint32_t off =
-                                    (row < rh && cl < chh) ? (uint32_t)(((int64_t)row * p.N + cl) * ES) : kOOB;
-                                __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)off, 0, kStoreStream);
-                            }
-                            __builtin_amdgcn_wave_barrier();
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < FN; ++j) {
-                                const int cl = j * 16 + g16 * 4;
-                                const uint32_t off = (r < rh && cl < chh) ? (uint32_t)(((int64_t)r * p.N + cl) * ES) : kOOB;
-                                __builtin_amdgcn_raw_buffer_store_b128(
-                                    v4i{(int)float_to_bits(acc[i][j][0]), (int)float_to_bits(acc[i][j][1]),
-                                        (int)float_to_bits(acc[i][j][2]), (int)float_to_bits(acc[i][j][3])},
-                                    rc, (int)off, 0, 0);
-                            }
-                        }
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-            }
+            if (ks == k1 - 1) store_unit(iu);
             __syncthreads();
         }
     }
@@ -2051,6 +2097,29 @@ hipError_t launch_grouped_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, co
     p.tiles_n = (int)ceil_div(N, 256);
     if (c_bf16) hipLaunchKernelGGL((gemm_grouped_persist_kernel<true, false, true>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((gemm_grouped_persist_kernel<false, false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+// The experts' weight gradients with both operands packed along the token
+// axis (K = T): the copying / computing-wave launch over (expert, tile) units,
+// each over its expert's k-steps; an expert without tokens stores zeros.
+hipError_t launch_grouped_gemm_wgrad_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                            const uint8_t *b_s, const int32_t *offsets, int64_t G, int64_t T,
+                                            int64_t M, int64_t N, void *c, bool c_bf16, hipStream_t stream) {
+    GemmParams p{};
+    p.a_q = a_q; p.a_s = a_s; p.b_q = b_q; p.b_s = b_s; p.c = c;
+    p.M = M; p.N = N; p.K = T;
+    p.KS = (int)packed_ksteps(T);
+    p.NP = (int)packed_panels(N);
+    p.G = (int)G;
+    p.offsets = offsets;
+    p.c_stride = M * N;
+    p.tiles_m = (int)ceil_div(M, 256);
+    p.tiles_n = (int)ceil_div(N, 128);
+    const int64_t units = G * p.tiles_m * p.tiles_n;
+    dim3 grid((unsigned)std::min<int64_t>(units, device_cu_count())), block(kThreads);
+    if (c_bf16) hipLaunchKernelGGL((gemm_ws_kernel<true, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_ws_kernel<false, false, true>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

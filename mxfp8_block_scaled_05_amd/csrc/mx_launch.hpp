@@ -54,9 +54,12 @@ hipError_t launch_quantize_dual(const uint16_t *x, int64_t rows, int64_t cols, u
 hipError_t launch_quantize_gather_packed(const uint16_t *x, int64_t rows_in, int64_t cols, const int64_t *idx,
                                          int64_t rows_out, uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream);
 hipError_t launch_quantize_dual_grouped_packed(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qr_packed,
-                                               uint8_t *sr_packed, uint8_t *q_col, uint8_t *s_col,
+                                               uint8_t *sr_packed, uint8_t *qc, uint8_t *sc, bool col_packed,
                                                const int32_t *src_off, const int32_t *dst_off, int64_t G,
                                                int64_t rows_out, hipStream_t stream);
+hipError_t launch_grouped_gemm_wgrad_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,
+                                            const uint8_t *b_s, const int32_t *offsets, int64_t G, int64_t T,
+                                            int64_t M, int64_t N, void *c, bool c_bf16, hipStream_t stream);
 hipError_t launch_quantize_dual_packed(const uint16_t *x, int64_t batch, int64_t rows, int64_t cols,
                                        uint8_t *qr_packed, uint8_t *sr_packed, uint8_t *qc_packed,
                                        uint8_t *sc_packed, hipStream_t stream);

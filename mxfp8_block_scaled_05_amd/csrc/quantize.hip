@@ -544,6 +544,41 @@ __device__ __forceinline__ void axis0_from_tile(uint8_t *tile, uint8_t *stile, u
     }
 }
 
+// The regrouped axis-0 grid straight into the packed layout of the weight
+// gradient's operand (N = cols, K = rows_out): destination 32-row block d of
+// column f is K-block d % 4 of k-step d / 4 of row f % 256 of panel f / 256,
+// its two 16-byte chunks at slots c ^ (f % 8), its scale byte at the panel
+// row's place in the step's scale tile -- what mxfp8_repack writes for the
+// canonical regrouped grid.
+__device__ __forceinline__ void axis0_from_tile_packed(uint8_t *tile, uint8_t *stile, uint8_t *__restrict__ qp,
+                                                       uint8_t *__restrict__ sp, int64_t cols, int64_t C0, int t,
+                                                       const int *dstb, int64_t KS) {
+    axis0_stage_tile(tile, stile, t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int col = i * 32 + (t >> 3), j = t & 7;
+        const int64_t f = C0 + col;
+        const int d = dstb[j >> 1];
+        if (f < cols && d >= 0) {
+            const int64_t tl = (f / kPanelRows) * KS + d / 4;
+            const int frow = (int)(f % kPanelRows), c = 2 * (d & 3) + (j & 1);
+            *reinterpret_cast<v4i *>(qp + tl * kTileBytes + frow * kKStep + ((c ^ (frow & 7)) << 4)) =
+                *reinterpret_cast<const v4i *>(tile + col * kA0OutPitch + 16 * j);
+        }
+    }
+    if (t < kA0Tile && C0 + t < cols) {
+        const int64_t f = C0 + t;
+        const int frow = (int)(f % kPanelRows);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int d = dstb[b];
+            if (d >= 0)
+                sp[((f / kPanelRows) * KS + d / 4) * kScaleStepBytes + (frow >> 4) * 64 + (frow & 15) + 16 * (d & 3)] =
+                    stile[t * 4 + b];
+        }
+    }
+}
+
 // one workgroup per tile; tiles numbered row-tile-major over a 1-D grid
 // (batched: matrix-major)
 __device__ __forceinline__ void tile_origin_of(int64_t idx, int64_t rows, int64_t cols, int64_t &b, int64_t &R0,
@@ -783,6 +818,65 @@ __global__ __launch_bounds__(256) void zero_dst_pads_kernel(uint8_t *__restrict_
     }
 }
 
+// The same pads in the packed layout of the regrouped grid (N = cols, K =
+// rows_out, KS k-steps): destination block d (one workgroup each, over the
+// KS * 4 blocks of the layout) that no group fills gets zero codes and scale
+// code 0 in every column, as its zero rows quantize; blocks past rows_out and
+// rows past cols are the layout's padding (zero codes, scale code 127).
+__global__ __launch_bounds__(256) void zero_dst_pads_packed_kernel(uint8_t *__restrict__ qp, uint8_t *__restrict__ sp,
+                                                                   int64_t rows, int64_t cols,
+                                                                   const int32_t *__restrict__ src_off,
+                                                                   const int32_t *__restrict__ dst_off, int G,
+                                                                   int64_t rows_out, int64_t KS) {
+    __shared__ int pad;
+    const int t = threadIdx.x;
+    const int64_t d = blockIdx.x, d0 = d * 32;
+    if (t < 64) {
+        int found = -1;
+        int64_t dlo_f = 0, dhi_f = 0, len_f = 0;
+        for (int g0 = 0; g0 < G && found < 0 && d0 < rows_out; g0 += 64) {
+            const int g = g0 + t;
+            int64_t dlo = 0, dhi = 0, lo = 0, hi = 0;
+            if (g < G) {
+                dlo = dst_off[g];
+                dhi = dst_off[g + 1];
+                dlo = dlo < 0 ? 0 : (dlo > rows_out ? rows_out : dlo);
+                dhi = dhi < dlo ? dlo : (dhi > rows_out ? rows_out : dhi);
+                lo = src_off[g];
+                hi = src_off[g + 1];
+                lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
+                hi = hi < lo ? lo : (hi > rows ? rows : hi);
+            }
+            const unsigned long long hit = __ballot(g < G && d0 >= dlo && d0 < dhi);
+            if (hit) {
+                const int src = __ffsll((long long)hit) - 1;
+                found = g0 + src;
+                dlo_f = __shfl(dlo, src);
+                dhi_f = __shfl(dhi, src);
+                len_f = __shfl(hi - lo, src);
+                const int64_t lo_f = __shfl(lo, src);
+                if ((lo_f & 31) || (dlo_f & 31)) len_f = 0;
+            }
+        }
+        if (t == 0) pad = d0 >= rows_out ? 2 : !(found >= 0 && d0 - dlo_f < len_f && d0 + 32 <= dhi_f);
+    }
+    __syncthreads();
+    const int kind = pad;                      // 0: filled by the walk, 1: pad block, 2: past rows_out
+    const int64_t np = (cols + kPanelRows - 1) / kPanelRows, ks = d / 4;
+    const int p = (int)(d & 3);
+    for (int64_t f = t; f < np * kPanelRows; f += 256) {
+        if (kind == 0 && f < cols) continue;
+        const int64_t tl = (f / kPanelRows) * KS + ks;
+        const int frow = (int)(f % kPanelRows);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<v4i *>(qp + tl * kTileBytes + frow * kKStep + (((2 * p + h) ^ (frow & 7)) << 4)) =
+                v4i{0, 0, 0, 0};
+        sp[tl * kScaleStepBytes + (frow >> 4) * 64 + (frow & 15) + 16 * p] =
+            (uint8_t)(kind == 1 && f < cols ? 0u : 127u);
+    }
+}
+
 // ---------------------------------------------------------------- weights -> packed
 // Axis-1 quantization of weights [batch][N][K] written straight into the
 // GEMM's packed layout (and, if q/scales are given, the canonical grid too):
@@ -959,7 +1053,7 @@ __global__ __launch_bounds__(256) void quantize_axis0_walk_kernel(const uint16_t
 // blocks found at the top of its iteration; q_row may be null).  Looking the
 // next tile's up beside its loads instead (double-buffered) measured no
 // faster on the MoE learner's tensors.
-template <bool NT, bool GROUPED = false, bool ROW_PACKED = false>
+template <bool NT, bool GROUPED = false, bool ROW_PACKED = false, bool COL_PACKED = false>
 __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t *__restrict__ x,
                                                                  uint8_t *__restrict__ q_row,
                                                                  uint8_t *__restrict__ s_row,
@@ -1039,7 +1133,11 @@ __global__ __launch_bounds__(256) void quantize_dual_walk_kernel(const uint16_t 
             }
         }
         if (!ROW_PACKED || R0 < rows) {       // (uniform over the workgroup)
-            if constexpr (GROUPED)
+            // COL_PACKED: the regrouped grid in the packed layout (N = cols,
+            // K = rows_out)
+            if constexpr (COL_PACKED)
+                axis0_from_tile_packed(tile, stile, q_col, s_col, cols, C0, t, dstb, (rows_out + kKStep - 1) / kKStep);
+            else if constexpr (GROUPED)
                 axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t, dstb, rows_out);
             else
                 axis0_from_tile(tile, stile, q_col, s_col, rows, cols, R0, C0, t);
@@ -1405,28 +1503,52 @@ hipError_t launch_quantize_dual_grouped(const uint16_t *x, int64_t rows, int64_t
     return hipGetLastError();
 }
 
+template <bool ROWP, bool COLP>
+static hipError_t launch_dual_grouped_packed_walk(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qr,
+                                                  uint8_t *sr, uint8_t *qc, uint8_t *sc, const int32_t *src_off,
+                                                  const int32_t *dst_off, int64_t G, int64_t rows_out,
+                                                  int64_t tiles, hipStream_t stream) {
+    if (rows * cols * 2 >= kQuantNontemporalBytes) {
+        const int64_t grid = walk_grid<quantize_dual_walk_kernel<true, true, ROWP, COLP>>(tiles);
+        hipLaunchKernelGGL((quantize_dual_walk_kernel<true, true, ROWP, COLP>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, x, qr, sr, qc, sc, rows, cols, tiles, src_off, dst_off, (int)G, rows_out);
+    } else {
+        const int64_t grid = walk_grid<quantize_dual_walk_kernel<false, true, ROWP, COLP>>(tiles);
+        hipLaunchKernelGGL((quantize_dual_walk_kernel<false, true, ROWP, COLP>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, x, qr, sr, qc, sc, rows, cols, tiles, src_off, dst_off, (int)G, rows_out);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_dual_grouped_packed(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qr_packed,
-                                               uint8_t *sr_packed, uint8_t *q_col, uint8_t *s_col,
+                                               uint8_t *sr_packed, uint8_t *qc, uint8_t *sc, bool col_packed,
                                                const int32_t *src_off, const int32_t *dst_off, int64_t G,
                                                int64_t rows_out, hipStream_t stream) {
-    hipLaunchKernelGGL(zero_dst_pads_kernel, dim3((unsigned)(rows_out / 32)), dim3(256), 0, stream, q_col,
-                       s_col, rows, cols, src_off, dst_off, (int)G, rows_out);
+    // the regrouped grid's pad blocks (and, packed, the layout's padding)
+    // first: the walk's stores, later on the stream, win wherever a
+    // malformed table overlaps them
+    const int64_t KS = packed_ksteps(rows_out);
+    if (col_packed)
+        hipLaunchKernelGGL(zero_dst_pads_packed_kernel, dim3((unsigned)(KS * 4)), dim3(256), 0, stream, qc, sc, rows,
+                           cols, src_off, dst_off, (int)G, rows_out, KS);
+    else
+        hipLaunchKernelGGL(zero_dst_pads_kernel, dim3((unsigned)(rows_out / 32)), dim3(256), 0, stream, qc, sc, rows,
+                           cols, src_off, dst_off, (int)G, rows_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // the walk over whole panels of rows (cols % 32 == 0, so rows are
-    // 16-byte aligned for the walk's loads)
-    const int64_t tiles = 2 * packed_panels(rows) * ((cols + kA0Tile - 1) / kA0Tile);
-    if (rows * cols * 2 >= kQuantNontemporalBytes) {
-        const int64_t grid = walk_grid<quantize_dual_walk_kernel<true, true, true>>(tiles);
-        hipLaunchKernelGGL((quantize_dual_walk_kernel<true, true, true>), dim3((unsigned)grid), dim3(256), 0, stream,
-                           x, qr_packed, sr_packed, q_col, s_col, rows, cols, tiles, src_off, dst_off, (int)G,
-                           rows_out);
-        return hipGetLastError();
-    }
-    const int64_t grid = walk_grid<quantize_dual_walk_kernel<false, true, true>>(tiles);
-    hipLaunchKernelGGL((quantize_dual_walk_kernel<false, true, true>), dim3((unsigned)grid), dim3(256), 0, stream, x,
-                       qr_packed, sr_packed, q_col, s_col, rows, cols, tiles, src_off, dst_off, (int)G, rows_out);
-    return hipGetLastError();
+    // with the row grid packed, the walk runs over whole panels of rows
+    // (cols % 32 == 0, so rows are 16-byte aligned for the walk's loads)
+    const int64_t tc = (cols + kA0Tile - 1) / kA0Tile;
+    const int64_t tiles_r = 2 * packed_panels(rows) * tc, tiles = ((rows + kA0Tile - 1) / kA0Tile) * tc;
+    if (qr_packed != nullptr)
+        return col_packed ? launch_dual_grouped_packed_walk<true, true>(x, rows, cols, qr_packed, sr_packed, qc, sc,
+                                                                       src_off, dst_off, G, rows_out, tiles_r, stream)
+                          : launch_dual_grouped_packed_walk<true, false>(x, rows, cols, qr_packed, sr_packed, qc, sc,
+                                                                        src_off, dst_off, G, rows_out, tiles_r, stream);
+    return col_packed ? launch_dual_grouped_packed_walk<false, true>(x, rows, cols, nullptr, nullptr, qc, sc, src_off,
+                                                                    dst_off, G, rows_out, tiles, stream)
+                      : launch_dual_grouped_packed_walk<false, false>(x, rows, cols, nullptr, nullptr, qc, sc, src_off,
+                                                                     dst_off, G, rows_out, tiles, stream);
 }
 
 hipError_t launch_quantize_packed_jobs(const PackedJobs &jobs, hipStream_t stream) {

@@ -208,17 +208,34 @@ def test_argument_errors_before_any_device_work(libmx):
     assert libmx.mxfp8_quantize_dual_grouped(p, 64, 64, NULL, NULL, p, p, r, p, 2, 128, NULL) == 5  # offsets align
     # ... with the axis-1 grid into the packed layout (both buffers required)
     dgp = libmx.mxfp8_quantize_dual_grouped_packed
-    assert dgp(p, 64, 64, NULL, p, p, p, p, p, 2, 128, NULL) == 1                   # packed codes
-    assert dgp(p, 64, 64, p, p, p, p, NULL, p, 2, 128, NULL) == 1                   # offsets
-    assert dgp(p, 48, 64, p, p, p, p, p, p, 2, 128, NULL) == 2                      # rows % 32
-    assert dgp(p, 64, 64, p, p, p, p, p, p, 2, 100, NULL) == 2                      # rows_out % 32
-    assert dgp(p, 64, 64, p, p, p, p, p, p, 0, 128, NULL) == 2                      # G
-    assert dgp(p, 64, (1 << 22) + 32, p, p, p, p, p, p, 2, 128, NULL) == 2          # cols beyond the K limit
-    for i in range(4):                     # x, packed codes and scales, q_col (s_col rows need no alignment)
-        args = [p, p, p, p]
+    for lay in (0, 1):                     # regrouped grid canonical / packed
+        assert dgp(p, 64, 64, NULL, p, p, p, lay, p, p, 2, 128, NULL) == 1          # row grid: both or neither
+        assert dgp(p, 64, 64, p, p, p, p, lay, NULL, p, 2, 128, NULL) == 1          # offsets
+        assert dgp(p, 64, 64, NULL, NULL, p, NULL, lay, p, p, 2, 128, NULL) == 1    # regrouped scales
+        assert dgp(p, 48, 64, p, p, p, p, lay, p, p, 2, 128, NULL) == 2             # rows % 32
+        assert dgp(p, 64, 64, p, p, p, p, lay, p, p, 2, 100, NULL) == 2             # rows_out % 32
+        assert dgp(p, 64, 64, p, p, p, p, lay, p, p, 0, 128, NULL) == 2             # G
+        assert dgp(p, 64, (1 << 22) + 32, p, p, p, p, lay, p, p, 2, 128, NULL) == 2  # cols beyond the K limit
+        for i in range(4):                 # x, packed row codes and scales, q_col
+            args = [p, p, p, p]
+            args[i] = q
+            assert dgp(args[0], 64, 64, args[1], args[2], args[3], p, lay, p, p, 2, 128, NULL) == 5, (lay, i)
+        assert dgp(p, 64, 64, p, p, p, p, lay, r, p, 2, 128, NULL) == 5             # offsets align
+    assert dgp(p, 64, 64, p, p, p, q, 1, p, p, 2, 128, NULL) == 5                   # packed regrouped scales align
+    assert dgp(p, 64, 64, p, p, p, p, 7, p, p, 2, 128, NULL) == 4                   # layout
+    # the experts' weight gradients over packed token-blocked operands
+    wgp = libmx.mxfp8_grouped_gemm_wgrad_packed
+    assert wgp(p, p, p, p, NULL, 2, 128, 8, 8, p, 0, NULL) == 1                      # offsets
+    assert wgp(p, p, p, p, p, 0, 128, 8, 8, p, 0, NULL) == 2                         # G
+    assert wgp(p, p, p, p, p, 2, 48, 8, 8, p, 0, NULL) == 2                          # T % 32
+    assert wgp(p, p, p, p, p, 2, 128, 8, 6, p, 0, NULL) == 2                         # N % 4 (fp32)
+    assert wgp(p, p, p, p, p, 2, 128, 8, 12, p, 1, NULL) == 2                        # N % 8 (bf16)
+    assert wgp(p, p, p, p, p, 2, 128, 8, 8, p, 5, NULL) == 4                         # dtype
+    for i in range(5):
+        args = [p, p, p, p, p]
         args[i] = q
-        assert dgp(args[0], 64, 64, args[1], args[2], args[3], p, p, p, 2, 128, NULL) == 5, i
-    assert dgp(p, 64, 64, p, p, p, p, r, p, 2, 128, NULL) == 5                      # offsets align
+        assert wgp(args[0], args[1], args[2], args[3], p, 2, 128, 8, 8, args[4], 0, NULL) == 5, i
+    assert wgp(p, p, p, p, r, 2, 128, 8, 8, p, 0, NULL) == 5                         # offsets align
     # gather into the packed layout
     gpk = libmx.mxfp8_quantize_gather_packed
     assert gpk(p, 8, 64, NULL, 16, p, p, NULL) == 1                                 # index table

@@ -1044,3 +1044,143 @@ def test_ws_grouped_copies_and_stores(G, N, K, offsets):
             for c0 in range(0, N, 64):
                 want.add((rr, c0))
     assert set(row_hits) == want and all(v == 1 for v in row_hits.values())
+
+
+def _dst_block_of(src, dst, rows, rows_out, r):
+    """Mirror of dst_block_of (well-formed tables): destination 32-row block of
+    the source block starting at row r, or -1."""
+    if r >= rows:
+        return -1
+    G = len(src) - 1
+    for g in range(G):
+        lo, hi = min(max(src[g], 0), rows), min(max(src[g + 1], 0), rows)
+        if lo <= r < hi:
+            dlo = min(max(dst[g], 0), rows_out)
+            dhi = min(max(dst[g + 1], dlo), rows_out)
+            if lo % 32 or dlo % 32:
+                return -1
+            d = dlo + (r - lo)
+            return d // 32 if d + 32 <= dhi else -1
+    return -1
+
+
+@pytest.mark.parametrize("tokens,experts,topk,cols,row_grid", [(64, 8, 2, 64, True), (512, 16, 4, 288, False),
+                                                               (8192, 128, 8, 768, True)])
+def test_quantize_dual_grouped_packed_col_grid_written_once(tokens, experts, topk, cols, row_grid):
+    """mxfp8_quantize_dual_grouped_packed's regrouped grid in the packed layout
+    (N = cols, K = rows_out): the walk's stores (destination block d of column
+    f at k-step d / 4, K-block d % 4, chunks 2 (d % 4) + h at slot c ^ (f % 8))
+    and zero_dst_pads_packed_kernel's (pad blocks in every column, the layout's
+    padding rows and blocks) write every byte exactly once, and the pad kernel's
+    scale codes are 0 for pad blocks, 127 for padding."""
+    import workloads as wl
+    rng = np.random.default_rng(tokens + cols)
+    route = wl.zipf_topk_routing(rng, tokens, experts, topk)
+    src, _, _ = wl.group_layout(route, experts)
+    src = [int(v) for v in src]
+    sizes = np.diff(src)
+    dst = [0] + list(np.cumsum(-(-sizes // 128) * 128))
+    dst = [int(v) for v in dst]
+    rows, rows_out = src[-1], dst[-1] + 64               # trailing blocks in no group
+    KS, NP = ceil_div(rows_out, 128), ceil_div(cols, PANEL)
+    q = np.zeros(NP * KS * TILE_BYTES // 16, np.int32)
+    s = np.zeros(NP * KS * 1024, np.int32)
+    scode = np.full(NP * KS * 1024, -1, np.int64)
+    f_all = np.arange(NP * PANEL)
+
+    def mark(f, d, code=None):
+        tl = (f // PANEL) * KS + d // 4
+        frow = f % PANEL
+        for h in range(2):
+            c = 2 * (d % 4) + h
+            np.add.at(q, (tl * TILE_BYTES + frow * 128 + ((c ^ (frow & 7)) << 4)) // 16, 1)
+        si = tl * 1024 + (frow >> 4) * 64 + (frow & 15) + 16 * (d % 4)
+        np.add.at(s, si, 1)
+        if code is not None:
+            scode[si] = code
+    # the walk: source row blocks of the tiles with R0 < rows (both walk shapes cover the same ones)
+    for r in range(0, ceil_div(rows, 128) * 128, 32):
+        d = _dst_block_of(src, dst, rows, rows_out, r)
+        if d >= 0:
+            mark(f_all[:cols], d)
+    # the pad kernel
+    for d in range(KS * 4):
+        d0 = d * 32
+        if d0 >= rows_out:
+            kind = 2
+        else:
+            found = None
+            for g in range(experts):
+                dlo = min(max(dst[g], 0), rows_out)
+                dhi = min(max(dst[g + 1], dlo), rows_out)
+                if dlo <= d0 < dhi:
+                    found = (dlo, dhi, src[g + 1] - src[g])
+                    break
+            kind = 0 if found and d0 - found[0] < found[2] and d0 + 32 <= found[1] else 1
+        fs = f_all if kind else f_all[cols:]
+        if fs.size:
+            mark(fs, d, np.where((kind == 1) & (fs < cols), 0, 127))
+    assert np.all(q == 1) and np.all(s == 1), (tokens, cols)
+    assert set(np.unique(scode)) <= {-1, 0, 127}
+
+
+@pytest.mark.parametrize("G,M,N,sizes", [(4, 256, 320, [128, 0, 384, 256]), (3, 300, 132, [0, 0, 128]),
+                                         (128, 1536, 2048, None), (128, 2048, 768, None)])
+def test_ws_grouped_k_units(G, M, N, sizes):
+    """gemm_ws_kernel<.., GK>: units = (expert, 256x128 tile) dealt in dispatch
+    order (workgroup j: units j, j + grid, ...), each over its expert's k-steps [o_g / 128, ceil(o_{g+1} / 128)) of the
+    packed token axis (an expert without tokens: one step, every copy out of
+    range); the A / B panels' copies stay inside the packed operands and each
+    element of C[g] is stored exactly once, at g * M * N."""
+    import workloads as wl
+    if sizes is None:
+        rng = np.random.default_rng(G + N)
+        route = wl.zipf_topk_routing(rng, 8192, G, 8)
+        off32, _, _ = wl.group_layout(route, G)
+        sz = np.diff(off32)
+        sizes = list(-(-sz // 128) * 128)
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    T = max(int(offs[-1]), 128)
+    KS, NPm, NPn = ceil_div(T, KSTEP), ceil_div(M, PANEL), ceil_div(N, PANEL)
+    tiles_m, tiles_n = ceil_div(M, 256), ceil_div(N, 128)
+    Tt = tiles_m * tiles_n
+    units = G * Tt
+    nwg = min(units, 256)
+    seen = []
+    steps = 0
+    hits = np.zeros(G * M * N if G * M * N <= 1 << 27 else 1, np.int32)
+    for wg in range(nwg):
+        first, stride = wg, nwg                   # dispatch order
+        count = -(-(units - first) // stride) if first < units else 0
+        for i in range(count):
+            u = first + i * stride
+            seen.append(u)
+            g, tile = u // Tt, u % Tt
+            lo, hi = min(max(offs[g], 0), T), min(max(offs[g + 1], offs[g]), T)
+            k0, k1 = lo // 128, -(-hi // 128)
+            empty = k1 == k0
+            if empty:
+                k1 = k0 + 1
+            assert 0 <= k0 < k1 <= max(KS, 1) or (empty and k0 <= KS)
+            steps += k1 - k0
+            tm, tn = grouped_order(tile, tiles_m, tiles_n)
+            pb, prow = tn * 128 // PANEL, tn * 128 % PANEL
+            # descriptors: A panel tm, B half panel, each over all KS k-steps
+            assert (tm + 1) * KS * TILE_BYTES <= NPm * KS * TILE_BYTES
+            assert pb * KS * TILE_BYTES + prow * 128 + (KS * TILE_BYTES - prow * 128) <= NPn * KS * TILE_BYTES
+            if not empty:
+                # the last copy of the unit's last step inside its descriptor
+                assert (k1 - 1) * TILE_BYTES + 31 * 1024 + 1024 <= KS * TILE_BYTES
+                assert (k1 - 1) * TILE_BYTES + 15 * 1024 + 1024 <= KS * TILE_BYTES - prow * 128
+            if hits.size > 1:
+                for w in range(4):
+                    row0, col0 = tm * 256 + (w >> 1) * 128, tn * 128 + (w & 1) * 64
+                    if row0 >= M or col0 >= N:
+                        continue
+                    rh, ch = min(M - row0, 128), min(N - col0, 64)
+                    base = g * M * N + row0 * N + col0
+                    for r in range(rh):
+                        hits[base + r * N: base + r * N + ch] += 1
+    assert sorted(seen) == list(range(units))
+    if hits.size > 1:
+        assert np.all(hits == 1)

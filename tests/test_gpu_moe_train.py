@@ -275,14 +275,17 @@ def test_quantize_gather_packed_matches_oracle_pack(mx, oracle_mod, tokens, expe
 
 @pytest.mark.parametrize("tokens,experts,topk,cols", [(64, 8, 2, 64), (512, 16, 4, 288), (8192, 128, 8, 768),
                                                       (8192, 128, 8, 2048)])
-def test_quantize_dual_grouped_packed_matches(mx, oracle_mod, tokens, experts, topk, cols):
+@pytest.mark.parametrize("row_grid,col_packed", [(True, True), (False, True), (True, False)])
+def test_quantize_dual_grouped_packed_matches(mx, oracle_mod, tokens, experts, topk, cols, row_grid, col_packed):
     """mxfp8_quantize_dual_grouped_packed: the regrouped token-blocked grid is
-    byte for byte mxfp8_quantize_dual_grouped's (pads included; outputs filled
-    first), and the packed row grid is the oracle's pack of quantize(x, 1) on
-    the small cases, mxfp8_repack of the canonical row grid at the MoE
-    learner's sizes (every padding byte written)."""
+    byte for byte mxfp8_quantize_dual_grouped's canonical grid, or in the
+    packed layout mxfp8_repack of it (pad blocks, trailing blocks in no group
+    and the layout's padding included; outputs filled first),
+    and the packed row grid (if asked for) the oracle's pack of quantize(x, 1)
+    on the small cases, mxfp8_repack of the canonical row grid at the MoE
+    learner's sizes."""
     import torch
-    _say("dual grouped packed", tokens, experts, topk, cols)
+    _say("dual grouped packed", tokens, experts, topk, cols, row_grid, col_packed)
     rng, offsets, row_token, _ = _routing(tokens + cols + 3, tokens, experts, topk)
     T = int(offsets[-1])
     x = np.zeros((T, cols), np.uint16)
@@ -292,15 +295,28 @@ def test_quantize_dual_grouped_packed_matches(mx, oracle_mod, tokens, experts, t
     rows_out = int(dst[-1]) + 64
     xd, so, do = to_dev(x), to_dev(offsets), to_dev(dst)
     dev = xd.device
-    q_col = torch.full((cols, rows_out), 0xFF, dtype=torch.uint8, device=dev)
-    s_col = torch.full((cols, rows_out // 32), 0xFF, dtype=torch.uint8, device=dev)
-    pr = mx.PackedWeight(torch.full((mx.packed_bytes(1, T, cols, 0),), 0xEE, dtype=torch.uint8, device=dev),
-                         torch.full((mx.packed_bytes(1, T, cols, 1),), 0xEE, dtype=torch.uint8, device=dev),
-                         1, T, cols)
-    mx.quantize_dual_grouped_packed_(xd, so, do, q_col, s_col, pr)
-    q_row, s_row, q_col2, s_col2 = mx.quantize_dual_grouped(xd, so, do, rows_out)
-    torch.cuda.synchronize()
-    assert torch.equal(q_col, q_col2) and torch.equal(s_col, s_col2)
+
+    def pw(n, k):
+        return mx.PackedWeight(torch.full((mx.packed_bytes(1, n, k, 0),), 0xEE, dtype=torch.uint8, device=dev),
+                               torch.full((mx.packed_bytes(1, n, k, 1),), 0xEE, dtype=torch.uint8, device=dev),
+                               1, n, k)
+    if col_packed:
+        pc = pw(cols, rows_out)
+    else:
+        pc = (torch.full((cols, rows_out), 0xEE, dtype=torch.uint8, device=dev),
+              torch.full((cols, rows_out // 32), 0xEE, dtype=torch.uint8, device=dev))
+    pr = pw(T, cols) if row_grid else None
+    mx.quantize_dual_grouped_packed_(xd, so, do, pc, pr)
+    q_row, s_row, q_col, s_col = mx.quantize_dual_grouped(xd, so, do, rows_out)
+    if col_packed:
+        ref_c = mx.repack(q_col, s_col)
+        torch.cuda.synchronize()
+        assert torch.equal(pc.q, ref_c.q) and torch.equal(pc.s, ref_c.s)
+    else:
+        torch.cuda.synchronize()
+        assert torch.equal(pc[0], q_col) and torch.equal(pc[1], s_col)
+    if not row_grid:
+        return
     if T * cols <= 1 << 22:
         rq, rs = oracle_mod.quantize(x, 1)
         qp, sp = oracle_mod.pack(rq.reshape(1, T, cols), rs.reshape(1, T, cols // 32), 1, T, cols)
@@ -309,3 +325,50 @@ def test_quantize_dual_grouped_packed_matches(mx, oracle_mod, tokens, experts, t
         ref = mx.repack(q_row, s_row)
         torch.cuda.synchronize()
         assert torch.equal(pr.q, ref.q) and torch.equal(pr.s, ref.s)
+
+
+@pytest.mark.parametrize("tokens,experts,topk,M,N,out", [(512, 16, 4, 256, 320, "f32"), (512, 16, 4, 192, 256, "bf16"),
+                                                        (8192, 128, 8, 1536, 2048, "f32"),
+                                                        (8192, 128, 8, 2048, 768, "f32")])
+def test_wgrad_packed_matches_canonical(mx, oracle_mod, tokens, experts, topk, M, N, out):
+    """mxfp8_grouped_gemm_wgrad_packed over the regrouped token-blocked grids
+    in the packed layout equals mxfp8_grouped_gemm_wgrad over the canonical
+    grids bit for bit (every expert, an empty one included: zeros), and on the
+    small cases the oracle per expert within the GEMM bound."""
+    import torch
+    _say("wgrad packed", tokens, experts, topk, M, N, out)
+    rng, offsets, row_token, _ = _routing(tokens + M + N, tokens, experts, topk)
+    offsets = offsets.copy()
+    offsets[2] = offsets[1]                        # expert 1 without tokens (expert 2 takes its rows)
+    Tg = int(offsets[-1])
+    real = row_token >= 0
+    dy = np.zeros((Tg, M), np.uint16)
+    xx = np.zeros((Tg, N), np.uint16)
+    dy[real] = wl.normal_bf16(rng, (int(real.sum()), M), std=2.0 ** -10)
+    xx[real] = wl.normal_bf16(rng, (int(real.sum()), N))     # as the other wgrad oracle checks
+    dst = _pad128(offsets)
+    assert dst[2] == dst[1]
+    T = int(dst[-1])
+    so, do = to_dev(offsets), to_dev(dst)
+    dev = so.device
+    tdt = torch.float32 if out == "f32" else torch.bfloat16
+
+    def pw(n, k):
+        return mx.PackedWeight(torch.empty(mx.packed_bytes(1, n, k, 0), dtype=torch.uint8, device=dev),
+                               torch.empty(mx.packed_bytes(1, n, k, 1), dtype=torch.uint8, device=dev), 1, n, k)
+    pa, pb = pw(M, T), pw(N, T)
+    dyd, xxd = to_dev(dy), to_dev(xx)
+    mx.quantize_dual_grouped_packed_(dyd, so, do, pa)
+    mx.quantize_dual_grouped_packed_(xxd, so, do, pb)
+    _, _, aq, as_ = mx.quantize_dual_grouped(dyd, so, do, T, row_grid=False)
+    _, _, bq, bs = mx.quantize_dual_grouped(xxd, so, do, T, row_grid=False)
+    c_ref = mx.grouped_gemm_wgrad(aq, as_, bq, bs, do, tdt)
+    c = torch.full((experts, M, N), 7.0, dtype=tdt, device=dev)
+    mx.grouped_gemm_wgrad_packed(pa, pb, do, tdt, out=c)
+    torch.cuda.synchronize()
+    iv = torch.int32 if out == "f32" else torch.int16
+    assert torch.equal(c.view(iv), c_ref.view(iv))
+    assert bool(torch.all(c[1] == 0))
+    if tokens <= 512:
+        _check_wgrad(oracle_mod, to_host(c.float()) if out == "bf16" else to_host(c), to_host(aq), to_host(as_),
+                     to_host(bq), to_host(bs), dst, out)
