@@ -550,8 +550,11 @@ size_t mxfp8_gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * mxfp8_gemm_splitk over the canonical grids of the same operands (the same
  * per-slice products in the same order).  workspace: DEVICE memory owned by
  * the caller, 16-byte aligned, or NULL; contents on entry ignored, on return
- * unspecified.  No split (too many tiles, fewer than two slices fit, or
- * N % 4 != 0): the plain mxfp8_gemm_packed path, no workspace touched.
+ * unspecified.  No split (too many tiles, fewer than two slices fit,
+ * N % 4 != 0, or mxfp8_gemm_packed would take its 128-row tiles, those fill
+ * at least half the compute units and K is at most 64 x 128, where the unsplit
+ * launch is the faster): the plain mxfp8_gemm_packed path, no workspace
+ * touched.
  * Argument errors as mxfp8_gemm_packed, plus MXFP8_ERR_ALIGN for a workspace
  * not 16-byte aligned.  Two kernels on `stream`, no allocation, no
  * synchronization.

@@ -591,9 +591,15 @@ mxfp8_status mxfp8_gemm_packed_splitk(const uint8_t *a_q, const uint8_t *a_s, co
         return MXFP8_ERR_ALIGN;
     mxfp8_status st = check_device();
     if (st != MXFP8_OK) return st;
-    SplitPlan sp = fit_split(splitk_plan(M, N, K, device_cu_count()), M, N, K, workspace, workspace_bytes);
+    const int cus = device_cu_count();
+    SplitPlan sp = fit_split(splitk_plan(M, N, K, cus), M, N, K, workspace, workspace_bytes);
     // the split launch stores fp32 partials in 4-column pieces
     if (N % 4 != 0 || (int64_t)128 * N * 4 >= ((int64_t)1 << 31)) sp.splits = 1;
+    // 128-row tiles that keep at least half the CUs busy over at most 64
+    // k-steps: unsplit, without the partial stores and the reduce pass
+    if (packed_tiling(M, N, raw(c_dtype) == MXFP8_BF16, cus) == PackedTiling::kWsHalf &&
+        2 * ceil_div(M, 128) * ceil_div(N, 128) >= cus && ceil_div(K, 128) <= 64)
+        sp.splits = 1;
     if (sp.splits <= 1)
         return finish(launch_gemm_packed(a_q, a_s, b_q, b_s, M, N, K, c, raw(c_dtype) == MXFP8_BF16, stream));
     return finish(launch_gemm_packed_splitk(a_q, a_s, b_q, b_s, M, N, K, c, raw(c_dtype) == MXFP8_BF16, sp,

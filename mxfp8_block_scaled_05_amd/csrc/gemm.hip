@@ -1363,9 +1363,13 @@ __device__ __forceinline__ void ws_tiles(int wg, int nwg, int T, int &first, int
     count = first < hi ? (hi - first + nx - 1) / nx : 0;
 }
 
-template <bool OUT_BF16, bool GROUPED = false, bool GK = false>
+template <bool OUT_BF16, bool GROUPED = false, bool GK = false, bool HALF = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
     static_assert(!(GROUPED && GK), "grouped rows or grouped K");
+    // HALF (dense): 128-row tiles (p.tiles_m counts them), the upper or lower
+    // half of a 256-row panel; only the computing waves of rows 0..127 work
+    // and only those rows' A bytes and scales are copied
+    static_assert(!HALF || (!GROUPED && !GK), "half tiles are dense");
     using Lw = WsLayout;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Lw::UNIT_OFF + (GROUPED ? Lw::UNITS * 16 : 0)];
     const int lane = threadIdx.x & 63;
@@ -1448,7 +1452,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
     if (w >= 4) {
         // ---- copying wave pw: segments pw, pw + 4, ... of each step
         const int pw = w - 4;
-        const int nc = ws_copies(pw);
+        const int nc = ws_copies(pw) - (HALF ? 4 : 0);
         int iu = 0, ks = 0, kend = 0, st = 0;                    // next step to issue
         v4i ra = {}, rsa = {}, rb = {}, rsb = {};
         int a_m0 = 0, a_rows = 0;                                // grouped: the tile's rows in A's first panel
@@ -1467,7 +1471,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                 bp = (int64_t)g * p.NP;
             } else {
                 grouped_order((first + i * stride) % T, p.tiles_m, p.tiles_n, tm, tn);
-                pa = tm;
+                pa = HALF ? tm / 2 : tm;
+                a_m0 = HALF ? (tm % 2) * 128 : 0;
             }
             // A: one panel, or (grouped, a tile starting inside a panel) two
             const int64_t na = GROUPED ? min((int64_t)2, (p.M + kPanelRows - 1) / kPanelRows - pa) : 1;
@@ -1492,9 +1497,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
             const uint32_t sbase = lds0 + st * Lw::STAGE;
             const uint32_t k0 = (uint32_t)ks * (uint32_t)kTileBytes;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < (HALF ? 4 : 8); ++i) {
                 const int seg = i * 4 + pw;
-                uint32_t off = k0 + seg * 1024 + lane * 16;
+                uint32_t off = k0 + (HALF ? (uint32_t)a_m0 * 128u : 0u) + seg * 1024 + lane * 16;
                 if constexpr (GROUPED) {
                     // the tile's rows seg*8 .. +7, in the panel they lie in;
                     // rows past the expert's read zeros
@@ -1520,14 +1525,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
                                              (uint32_t)((r % kPanelRows) >> 4) * 64u + (lane & 15) * 4
                                        : kOOB;
             }
+            if constexpr (HALF) sa_off = pw < 2 ? s0 + (uint32_t)a_m0 * 4u : kOOB;   // the half's 8 atoms
             dma4(rsa, sa_off | zero_oob, sbase + Lw::SA_OFF + pw * 256);
             if (pw < 2) dma4(rsb, s0 | zero_oob, sbase + Lw::SB_OFF + pw * 256);
             st = st == Lw::NST - 1 ? 0 : st + 1;
             if (++ks == kend) start_unit(iu + 1);
         };
         auto wait_all_but_last = [&]() {
-            if (nc == 14) __builtin_amdgcn_s_waitcnt(waitcnt_vm(14));
-            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(13));
+            if constexpr (HALF) {
+                if (nc == 10) __builtin_amdgcn_s_waitcnt(waitcnt_vm(10));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+            } else {
+                if (nc == 14) __builtin_amdgcn_s_waitcnt(waitcnt_vm(14));
+                else __builtin_amdgcn_s_waitcnt(waitcnt_vm(13));
+            }
         };
         if (total > 0) issue_next();
         if (total > 1) { issue_next(); wait_all_but_last(); }
@@ -1567,6 +1578,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
             tn = __builtin_amdgcn_readfirstlane(un.tn);
             row0 = (int64_t)__builtin_amdgcn_readfirstlane(un.m0) + wm * 128;
             row_end = __builtin_amdgcn_readfirstlane(un.m_end);
+        } else if constexpr (HALF) {
+            // rows tm*128 .. +127 (the wm = 1 waves hold none)
+            grouped_order(u % T, p.tiles_m, p.tiles_n, tm, tn);
+            row0 = (int64_t)tm * 128 + wm * 128;
+            row_end = min(p.M, (int64_t)tm * 128 + 128);
         } else {
             grouped_order(u % T, p.tiles_m, p.tiles_n, tm, tn);
             row0 = (int64_t)tm * Lw::BM + wm * 128;
@@ -1629,27 +1645,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ws_kernel(GemmParams p) {
         for (int ks = k0; ks < k1; ++ks) {
             const uint8_t *sp = smem + st * Lw::STAGE;
             const uint8_t *sa = sp + Lw::A_OFF + wm * 128 * 128;
-            int sas[FM], sbs[FN];
-            v8i bf[FN], af[2];
-            // the B fragments and scales, then row 0's A fragment; each later
-            // A fragment is read while the previous row's MFMAs run (with one
-            // computing wave per SIMD nothing else hides the LDS latency)
+            if (!HALF || wm == 0) {
+                int sas[FM], sbs[FN];
+                v8i bf[FN], af[2];
+                // the B fragments and scales, then row 0's A fragment; each later
+                // A fragment is read while the previous row's MFMAs run (with one
+                // computing wave per SIMD nothing else hides the LDS latency)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sp + Lw::B_OFF + (wn * 64 + j * 16) * 128, lane);
+                for (int j = 0; j < FN; ++j) bf[j] = lds_frag(sp + Lw::B_OFF + (wn * 64 + j * 16) * 128, lane);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) sbs[j] = sp[Lw::SB_OFF + (wn * FN + j) * 64 + lane];
+                for (int j = 0; j < FN; ++j) sbs[j] = sp[Lw::SB_OFF + (wn * FN + j) * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) sas[i] = sp[Lw::SA_OFF + (wm * FM + i) * 64 + lane];
-            af[0] = lds_frag(sa, lane);
-            __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < FM; ++i) sas[i] = sp[Lw::SA_OFF + (wm * FM + i) * 64 + lane];
+                af[0] = lds_frag(sa, lane);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                if (i + 1 < FM) af[(i + 1) & 1] = lds_frag(sa + (i + 1) * 16 * 128, lane);
+                for (int i = 0; i < FM; ++i) {
+                    if (i + 1 < FM) af[(i + 1) & 1] = lds_frag(sa + (i + 1) * 16 * 128, lane);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i & 1], acc[i][j], 0, 0,
-                                                                                 0, sbs[j], 0, sas[i]);
-                __builtin_amdgcn_sched_barrier(0);      // keep the read of row i + 1 ahead of row i's MFMAs
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i & 1], acc[i][j], 0, 0,
+                                                                                     0, sbs[j], 0, sas[i]);
+                    __builtin_amdgcn_sched_barrier(0);      // keep the read of row i + 1 ahead of row i's MFMAs
+                }
             }
             st = st == Lw::NST - 1 ? 0 : st + 1;
             if (ks == k1 - 1) store_unit(iu);
@@ -1885,10 +1903,30 @@ hipError_t launch_gemm(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_
     return launch_tile<256, 128, 4, false>(p, b_packed, c_bf16, p.tiles_m * p.tiles_n, stream);
 }
 
+// The tiles of launch_gemm_packed.  Where gemm_ws_kernel's 256x128 tiles
+// make at most three rounds over the CUs (its persistent walk hides each
+// tile's prologue) the choice weighs each candidate's rounds by the time of
+// one of its k-steps, which the copies into LDS set: 1 for 256x128 tiles,
+// ~0.67 for 128x128 ones (two thirds of the bytes), ~1.5 for the two-stage
+// 256x256 tiles (measured 1850-2050 against ~3100 clocks per step).  Beyond
+// three rounds, or where the epilogue's stores cannot take the walk (N not a
+// multiple of 16 bytes of C, or 128 rows of C past 2 GB), launch_gemm's tilings.
+PackedTiling packed_tiling(int64_t M, int64_t N, bool c_bf16, int cus) {
+    const int64_t tm = ceil_div(M, 256), full = tm * ceil_div(N, 128);
+    if (N % (c_bf16 ? 8 : 4) != 0 || (int64_t)128 * N * (c_bf16 ? 2 : 4) >= ((int64_t)1 << 31) ||
+        full > (int64_t)3 * cus)
+        return PackedTiling::kDense;
+    const double t_full = (double)ceil_div(full, (int64_t)cus);
+    const double t_half = 0.67 * (double)ceil_div(ceil_div(M, 128) * ceil_div(N, 128), (int64_t)cus);
+    const double t_big = 1.5 * (double)ceil_div(tm * ceil_div(N, 256), (int64_t)cus);
+    if (t_big < t_full - 1e-9 && t_big < t_half - 1e-9) return PackedTiling::kDense;
+    return t_half < t_full - 1e-9 ? PackedTiling::kWsHalf : PackedTiling::kWs;
+}
+
 // Both operands in the packed layout (A quantized straight into it, or
 // repacked): every copy of a k-step reads one contiguous 1 KB, where a
-// canonical A segment gathers 8 rows K bytes apart.  K % 128 == 0.  The same
-// tilings as launch_gemm.
+// canonical A segment gathers 8 rows K bytes apart.  K % 128 == 0.  The
+// tiles of packed_tiling.
 hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
                               int64_t M, int64_t N, int64_t K, void *c, bool c_bf16, hipStream_t stream) {
     GemmParams p{};
@@ -1902,18 +1940,19 @@ hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint
     const int cus = device_cu_count();
     p.tiles_m = (int)ceil_div(M, 256);
     dim3 block(kThreads);
-    // the copying / computing split of gemm_ws_kernel where its 256x128 tiles
-    // make at most three rounds over the CUs (a persistent walk hides each
-    // tile's prologue; on more rounds the 256x256 tiles' lower copy volume
-    // per output wins)
-    const int64_t ws_cols = ceil_div(N, 128), ws_count = (int64_t)p.tiles_m * ws_cols;
-    if (N % (c_bf16 ? 8 : 4) == 0 && (int64_t)128 * N * (c_bf16 ? 2 : 4) < ((int64_t)1 << 31) &&
-        ws_count <= (int64_t)3 * cus) {
-        p.tiles_n = (int)ws_cols;
-        const int64_t tiles = ws_count;
-        dim3 grid((unsigned)std::min<int64_t>(tiles, cus));
-        if (c_bf16) hipLaunchKernelGGL((gemm_ws_kernel<true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((gemm_ws_kernel<false>), grid, block, 0, stream, p);
+    const PackedTiling pt = packed_tiling(M, N, c_bf16, cus);
+    if (pt == PackedTiling::kWs || pt == PackedTiling::kWsHalf) {
+        const bool half = pt == PackedTiling::kWsHalf;
+        if (half) p.tiles_m = (int)ceil_div(M, 128);
+        p.tiles_n = (int)ceil_div(N, 128);
+        dim3 grid((unsigned)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n, cus));
+        if (half) {
+            if (c_bf16) hipLaunchKernelGGL((gemm_ws_kernel<true, false, false, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_ws_kernel<false, false, false, true>), grid, block, 0, stream, p);
+        } else {
+            if (c_bf16) hipLaunchKernelGGL((gemm_ws_kernel<true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_ws_kernel<false>), grid, block, 0, stream, p);
+        }
         return hipGetLastError();
     }
     const DenseTiling d = dense_tiling(M, N, cus);

@@ -124,6 +124,10 @@ hipError_t launch_dequantize(const uint8_t *q, const uint8_t *scales, int64_t ro
 hipError_t launch_repack(const uint8_t *q, const uint8_t *scales, int64_t batch, int64_t N,
                          int64_t K, uint8_t *q_packed, uint8_t *s_packed, hipStream_t stream);
 
+// the tiles launch_gemm_packed takes: gemm_ws_kernel's 256x128 or 128x128
+// tiles, or launch_gemm's tilings
+enum class PackedTiling { kWs, kWsHalf, kDense };
+PackedTiling packed_tiling(int64_t M, int64_t N, bool c_bf16, int cus);
 hipError_t launch_gemm_packed(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q, const uint8_t *b_s,
                               int64_t M, int64_t N, int64_t K, void *c, bool c_bf16, hipStream_t stream);
 hipError_t launch_gemm_packed_splitk(const uint8_t *a_q, const uint8_t *a_s, const uint8_t *b_q,

@@ -759,6 +759,90 @@ def test_ws_stores_cover_c_once(M, N, es):
     assert np.all(hits == 1), (M, N)
 
 
+def packed_tiling(M, N, es, cus=256):
+    """Mirror of packed_tiling: 'ws' (256x128 tiles), 'half' (128x128) or
+    'dense' (launch_gemm's tilings)."""
+    tm, full = ceil_div(M, 256), ceil_div(M, 256) * ceil_div(N, 128)
+    if N % (8 if es == 2 else 4) or 128 * N * es >= 2 ** 31 or full > 3 * cus:
+        return "dense"
+    t_full = ceil_div(full, cus)
+    t_half = 0.67 * ceil_div(ceil_div(M, 128) * ceil_div(N, 128), cus)
+    t_big = 1.5 * ceil_div(tm * ceil_div(N, 256), cus)
+    if t_big < t_full - 1e-9 and t_big < t_half - 1e-9:
+        return "dense"
+    return "half" if t_half < t_full - 1e-9 else "ws"
+
+
+def test_packed_tiling_choices():
+    """The Qwen3-8B linears: 128-row tiles where 256-row ones leave most CUs
+    idle, 256x256 tiles where 256x128 ones take one and a half rounds."""
+    assert packed_tiling(512, 6144, 2) == "half" and packed_tiling(512, 4096, 2) == "half"
+    assert packed_tiling(512, 24576, 2) == "dense" and packed_tiling(512, 4096, 2, cus=80) == "ws"
+    assert packed_tiling(1024, 6144, 2) == "ws" and packed_tiling(4096, 6144, 2) == "ws"
+    assert packed_tiling(8192, 24576, 2) == "dense" and packed_tiling(512, 6148, 2) == "dense"
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 6144, 4096), (512, 4096, 4096), (100, 264, 512), (384, 136, 256),
+                                   (129, 8, 128), (640, 1024, 1024)])
+@pytest.mark.parametrize("es", [2, 4])
+def test_ws_half_tiles_copy_their_rows_and_store_once(M, N, K, es):
+    """128-row tiles (tm: rows tm*128..+127, the upper or lower half of
+    panel tm/2): the copying waves' four A segments per k-step bring exactly
+    those rows into LDS rows 0..127 (each once, inside the panel's
+    descriptor), waves 0 and 1 copy the half's eight scale atoms into LDS
+    atoms 0..7 (waves 2 and 3 copy nothing: kOOB), and the computing waves of
+    rows 0..127 write every element of C once."""
+    if N % (8 if es == 2 else 4):
+        pytest.skip("the launcher takes this kernel only for N % 8 == 0 (bf16) or N % 4 == 0 (fp32)")
+    KS, MP = ceil_div(K, KSTEP), ceil_div(M, PANEL)
+    tiles_m, tiles_n = ceil_div(M, 128), ceil_div(N, 128)
+    lane = np.arange(64)
+    hits = np.zeros(M * N, np.int32)
+    for L in range(tiles_m * tiles_n):
+        tm, tn = grouped_order(L, tiles_m, tiles_n)
+        pa, a_m0 = tm // 2, (tm % 2) * 128
+        assert pa < MP and pa * KS * TILE_BYTES + KS * TILE_BYTES <= MP * KS * TILE_BYTES
+        for ks in (0, KS - 1):
+            k0 = ks * TILE_BYTES
+            rows = np.zeros(256, np.int32)
+            for pw in range(4):
+                for i in range(4):
+                    seg = i * 4 + pw
+                    off = k0 + a_m0 * 128 + seg * 1024 + lane * 16
+                    assert off.max() + 16 <= KS * TILE_BYTES
+                    lds = seg * 1024 + lane * 16
+                    # a panel row's 128 bytes land on the tile row's 128 bytes
+                    assert np.all((off - k0) // 128 - a_m0 == lds // 128) and np.all(off % 128 == lds % 128)
+                    np.add.at(rows, (off - k0) // 128, 1)
+                if pw < 2:
+                    s_off = ks * 1024 + pw * 256 + lane * 4 + a_m0 * 4
+                    assert s_off.max() + 4 <= KS * 1024
+                    assert np.all(s_off // 64 - ks * 16 - a_m0 // 16 == (pw * 256 + lane * 4) // 64)
+            want = np.zeros(256, np.int32)
+            want[a_m0:a_m0 + 128] = 8           # 8 lanes (16 bytes each) per row
+            assert np.array_equal(rows, want)
+        row0, row_end = tm * 128, min(M, tm * 128 + 128)
+        for wn in range(2):
+            col0 = tn * 128 + wn * 64
+            rh, chh = row_end - row0, min(N - col0, 64)
+            if rh <= 0 or chh <= 0:
+                continue
+            rng = ((rh - 1) * N + chh) * es
+            assert (row0 * N + col0) * es + rng <= M * N * es
+            if es == 2:
+                pieces = [(h * 8 + (lane >> 3), (lane & 7) * 8, 8) for h in range(2)]
+            else:
+                pieces = [(lane & 15, j * 16 + (lane >> 4) * 4, 4) for j in range(4)]
+            for i in range(8):
+                for rb, cl, width in pieces:
+                    r = i * 16 + rb
+                    ok = (r < rh) & (cl < chh)
+                    assert np.all((r[ok] * N + cl[ok]) * es + width * es <= rng)
+                    for c in range(width):
+                        np.add.at(hits, (row0 + r[ok]) * N + col0 + cl[ok] + c, 1)
+    assert np.all(hits == 1), (M, N)
+
+
 @pytest.mark.parametrize("M,N,K", [(64, 256, 1024), (300, 4096, 4096), (512, 6144, 4096), (512, 4096, 12288),
                                    (32, 1000, 2048)])
 def test_ws_split_units_cover_k_and_partials_stay_inside(M, N, K):

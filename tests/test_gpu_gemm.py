@@ -350,19 +350,21 @@ def test_gemm_qkv_full_output(mx, oracle_mod):
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 256), (200, 300, 512), (1000, 96, 1024), (513, 264, 4096),
                                    (2048, 9216, 512), (512, 32768, 256), (4096, 9216, 512), (3072, 9216, 512),
-                                   (4096, 6140, 512), (300, 4100, 384), (1, 8, 128), (33, 4, 128)])
+                                   (4096, 6140, 512), (300, 4100, 384), (1, 8, 128), (33, 4, 128),
+                                   (512, 6144, 4096), (100, 264, 512), (640, 1024, 1024), (129, 8, 128)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_packed_a_matches_canonical(mx, oracle_mod, M, N, K, out):
     """mxfp8_gemm_packed: A quantized straight into the packed layout
     (mxfp8_quantize_packed) gives the same bytes as repacking the canonical
     grid, and the GEMM over it is bit-identical to mxfp8_gemm with canonical
     A, over every kernel the launcher picks: the copying/computing-wave
-    kernel (256x128 tiles, up to three rounds: the first six shapes, and
-    fp32 output wherever N % 4 == 0), and otherwise the 256x256 tiles
-    (3072x9216), the mixed launch (4096x9216: 32 large + 8 small tile
+    kernel with 128-row tiles (the few-tile shapes: 512x6144, 100x264,
+    640x1024, 129x8, 1000x96, 513x264, 64x256, 1x8, 33x4, and 200x300 and
+    300x4100 with fp32 output) or 256x128 tiles (2048x9216), and otherwise
+    the 256x256 tiles (3072x9216, and 512x32768 where 256x128 tiles would
+    take two rounds), the mixed launch (4096x9216: 32 large + 8 small tile
     columns), the paired launch (4096x6140 bf16: N % 8 != 0) and 256x128
-    tiles (300x4100 bf16); a single row (1x8) and N = 4 (33x4); the smaller
-    cases also against the oracle."""
+    tiles (300x4100 bf16); the smaller cases also against the oracle."""
     rng = np.random.default_rng(M * 7 + N + K)
     x = wl.normal_bf16(rng, (M, K))
     w = wl.normal_bf16(rng, (N, K), std=0.02)
@@ -613,6 +615,26 @@ def test_gemm_splitk_matches_oracle(mx, oracle_mod, M, N, K, out):
     assert np.array_equal(host(mx.gemm(a_q, a_s, packed, tdt, workspace=none)), host(mx.gemm(a_q, a_s, packed, tdt)))
 
 
+def _packed_split_declined(M, N, K, out):
+    """Where mxfp8_gemm_packed_splitk keeps the unsplit launch although the
+    split plan has slices: the launcher's 128-row tiles (they take fewer
+    rounds, weighted by a k-step's copy time, than 256x128 or 256x256 tiles)
+    filling at least half the CUs over at most 64 k-steps."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    es = 4 if out == "f32" else 2
+    cd = lambda a, b: -(-a // b)
+    full = cd(M, 256) * cd(N, 128)
+    if N % (8 if es == 2 else 4) or 128 * N * es >= 2 ** 31 or full > 3 * cus:
+        return False
+    t_full = cd(full, cus)
+    t_half = 0.67 * cd(cd(M, 128) * cd(N, 128), cus)
+    t_big = 1.5 * cd(cd(M, 256) * cd(N, 256), cus)
+    if (t_big < t_full - 1e-9 and t_big < t_half - 1e-9) or not t_half < t_full - 1e-9:
+        return False
+    return 2 * cd(M, 128) * cd(N, 128) >= cus and cd(K, 128) <= 64
+
+
 @pytest.mark.parametrize("M,N,K,out", [(64, 256, 1024, "bf16"), (300, 4096, 4096, "f32"), (512, 6144, 4096, "bf16"),
                                        (512, 4096, 12288, "bf16"), (32, 1000, 2048, "f32"), (512, 1002, 1024, "bf16")])
 def test_gemm_packed_splitk_matches_canonical_split(mx, oracle_mod, M, N, K, out):
@@ -643,7 +665,11 @@ def test_gemm_packed_splitk_matches_canonical_split(mx, oracle_mod, M, N, K, out
     assert need > 0
     full = torch.empty(need, dtype=torch.uint8, device=a_q.device)
     c1 = host(mx.gemm_packed(A, B, tdt, workspace=full))
-    if N % 4 == 0:
+    if _packed_split_declined(M, N, K, out):
+        # 128-row tiles filling half the CUs over <= 64 k-steps run unsplit:
+        # bit-identical to the unsplit canonical-A GEMM
+        assert np.array_equal(c1, host(mx.gemm(a_q, a_s, B, tdt)))
+    elif N % 4 == 0:
         assert np.array_equal(c1, host(mx.gemm(a_q, a_s, B, tdt, workspace=full)))
         half = torch.empty(need // 2 + 16, dtype=torch.uint8, device=a_q.device)
         assert np.array_equal(host(mx.gemm_packed(A, B, tdt, workspace=half)),
