@@ -184,8 +184,9 @@ mxfp8_status mxfp8_quantize_dual_grouped(const void *x_bf16, int64_t rows, int64
  *     codes with scale code 0, the layout's padding scale code 127; for
  *     mxfp8_grouped_gemm_wgrad_packed).
  * Arguments, table rules and limits as mxfp8_quantize_dual_grouped, plus
- * those of mxfp8_repack for the packed layouts.  Bit-exact, deterministic; no
- * allocation, no synchronization.
+ * those of mxfp8_repack for the packed layouts (s_col 16-byte aligned only
+ * when packed); MXFP8_ERR_DTYPE for a col_layout other than the two.
+ * Bit-exact, deterministic; no allocation, no synchronization.
  */
 mxfp8_status mxfp8_quantize_dual_grouped_packed(const void *x_bf16, int64_t rows, int64_t cols,
                                                 uint8_t *q_row_packed, uint8_t *s_row_packed,
