@@ -636,7 +636,8 @@ def _packed_split_declined(M, N, K, out):
 
 
 @pytest.mark.parametrize("M,N,K,out", [(64, 256, 1024, "bf16"), (300, 4096, 4096, "f32"), (512, 6144, 4096, "bf16"),
-                                       (512, 4096, 12288, "bf16"), (32, 1000, 2048, "f32"), (512, 1002, 1024, "bf16")])
+                                       (512, 4096, 12288, "bf16"), (32, 1000, 2048, "f32"), (512, 1002, 1024, "bf16"),
+                                       (512, 4096, 4096, "f32"), (384, 4096, 8192, "bf16")])
 def test_gemm_packed_splitk_matches_canonical_split(mx, oracle_mod, M, N, K, out):
     """mxfp8_gemm_packed_splitk: the copying/computing-wave launch over
     (tile, K slice) units, fp32 partials summed in slice order.  Bit-identical
