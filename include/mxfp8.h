@@ -690,7 +690,9 @@ mxfp8_status mxfp8_grouped_gemm_wgrad(const uint8_t *a_q, const uint8_t *a_s,
  * products, same order).  Deterministic; no allocation, no synchronization.
  * Speed: on the Qwen3-30B-A3B learner's weight gradients this launch is
  * slower than mxfp8_grouped_gemm_wgrad's aligned path (its 256x128 tiles
- * write FP32 C in half-size pieces); it serves callers that keep one layout.
+ * copy more operand bytes per output than the aligned path's 256x256 ones,
+ * and four of its eight waves store each tile's FP32 C); it serves callers
+ * that keep one layout.
  */
 mxfp8_status mxfp8_grouped_gemm_wgrad_packed(const uint8_t *a_q_packed, const uint8_t *a_s_packed,
                                              const uint8_t *b_q_packed, const uint8_t *b_s_packed,
